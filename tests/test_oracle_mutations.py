@@ -1,0 +1,148 @@
+"""Planted mistakes in the oracle (on the CPU only): each plausible slip — a
+dropped term, a wrong sign or index, a transposed operand — must make at least
+one of the pins in test_oracle_*.py fail."""
+import numpy as np
+import pytest
+
+import test_oracle_append as T_AP
+import test_oracle_attention as T_A
+import test_oracle_codecs as T_C
+import test_oracle_rope as T_R
+from oracle import append as AP
+from oracle import attention as A
+from oracle import codecs, rope
+
+
+def _fails(fn, *args):
+    with pytest.raises(AssertionError):
+        fn(*args)
+
+
+def test_rope_wrong_sign_is_caught(monkeypatch):
+    def bad(x, pos, theta):
+        x = np.asarray(x, dtype=np.float64)
+        h = x.shape[-1] // 2
+        ang = rope._per_row(rope.rope_angles(pos, theta, x.shape[-1]), x.ndim)
+        c, s = np.cos(ang), np.sin(ang)
+        return np.concatenate([x[..., :h] * c - x[..., h:] * s, x[..., h:] * c - x[..., :h] * s], -1)
+    monkeypatch.setattr(rope, "rope_neox_f64", bad)
+    _fails(T_R.test_pair_norms_preserved)
+
+
+def test_rope_adjacent_pairs_instead_of_split_half_is_caught(monkeypatch):
+    def bad(x, pos, theta):
+        x = np.asarray(x, dtype=np.float64)
+        D = x.shape[-1]
+        ang = rope._per_row(rope.rope_angles(pos, theta, D), x.ndim)
+        c, s = np.cos(ang), np.sin(ang)
+        ev, od = x[..., 0::2], x[..., 1::2]
+        y = np.empty_like(x)
+        y[..., 0::2] = ev * c - od * s
+        y[..., 1::2] = od * c + ev * s
+        return y
+    monkeypatch.setattr(rope, "rope_neox_f64", bad)
+    _fails(T_R.test_split_half_pairing_one_hot)
+
+
+def test_rope_dropped_factor_two_in_frequency_is_caught(monkeypatch):
+    monkeypatch.setattr(rope, "rope_inv_freq",
+                        lambda theta, D: np.power(float(theta), -np.arange(D // 2) / D))
+    _fails(T_R.test_inv_freq_closed_form)
+
+
+def test_attention_dropped_scale_is_caught(monkeypatch):
+    orig = A.attend
+    monkeypatch.setattr(A, "attend", lambda q, K, V, scale: orig(q, K, V, 1.0))
+    _fails(T_A.test_matches_torch_sdpa_fp64_with_gqa)
+
+
+def test_attention_transposed_value_use_is_caught(monkeypatch):
+    def bad(q, K, V, scale):
+        q = np.asarray(q, dtype=np.float64)
+        s = scale * (q @ K.T)
+        p = np.exp(s - s.max(1, keepdims=True))
+        p /= p.sum(1, keepdims=True)
+        out = (p @ K)  # keys used as values
+        return out, np.log(np.exp(s).sum(1)), p
+    monkeypatch.setattr(A, "attend", bad)
+    _fails(T_A.test_golden_tiny_worked_example)
+
+
+def test_interleaved_gqa_head_mapping_is_caught(monkeypatch):
+    def bad(q, k_pool, v_pool, block_tables, context_lens, softmax_scale, *, num_kv_heads, block_size,
+            cache, k_scale=None, v_scale=None, seqs=None):
+        q = np.asarray(q, dtype=np.float64)
+        B, Hq, D = q.shape
+        out = np.zeros((B, Hq, D))
+        lse = np.zeros((B, Hq))
+        for b in range(B):
+            L = int(context_lens[b])
+            for h in range(Hq):
+                g = h % num_kv_heads
+                K = A.gather_kv(k_pool, block_tables, b, L, g, block_size, cache, k_scale)
+                V = A.gather_kv(v_pool, block_tables, b, L, g, block_size, cache, v_scale)
+                o, l, _ = A.attend(q[b, h:h + 1], K, V, softmax_scale)
+                out[b, h], lse[b, h] = o[0], l[0]
+        return out, lse
+    monkeypatch.setattr(A, "paged_decode", bad)
+    _fails(T_A.test_perturbing_one_kv_head_moves_only_its_query_group)
+
+
+def test_off_by_one_block_index_is_caught(monkeypatch):
+    orig = A.gather_kv
+    def bad(pool, block_tables, b, L, g, block_size, cache, scale=None):
+        if L <= 0:
+            return orig(pool, block_tables, b, L, g, block_size, cache, scale)
+        j = np.arange(L)
+        pb = np.asarray(block_tables)[b, (j + 1) // block_size].astype(np.int64)  # slip
+        raw = np.asarray(pool)[pb, j % block_size, g, :]
+        return A.decode_rows(raw, cache, None if scale is None else float(scale[g]))
+    monkeypatch.setattr(A, "gather_kv", bad)
+    _fails(T_A.test_identity_table_matches_dense_attention)
+
+
+def test_merge_without_normalisation_is_caught(monkeypatch):
+    def bad(o_p, lse_p, num_parts=None):
+        o_p, lse_p = np.asarray(o_p), np.asarray(lse_p)
+        M = lse_p.max(axis=2, keepdims=True)
+        w = np.exp(lse_p - M)
+        return (w[..., None] * o_p).sum(2), (M[..., 0] + np.log(w.sum(2)))
+    monkeypatch.setattr(A, "lse_merge", bad)
+    _fails(T_A.test_merge_closed_form_two_partitions)
+
+
+def test_append_at_wrong_position_is_caught(monkeypatch):
+    orig = AP.rope_kv_append
+    def bad(qkv, context_lens, *a, **k):
+        return orig(qkv, np.asarray(context_lens) - 1, *a, **k)  # writes at ctx - 2
+    monkeypatch.setattr(AP, "rope_kv_append", bad)
+    _fails(T_AP.test_only_target_slots_change, "qwen2.5_1.5b_gqa")
+
+
+def test_e4m3_ties_away_from_zero_is_caught(monkeypatch):
+    vals = codecs.e4m3_decode(np.arange(0x7F, dtype=np.uint8))
+    def bad(x):
+        x = np.asarray(x, dtype=np.float64)
+        a = np.minimum(np.abs(x), 448.0)
+        d = np.abs(vals[None, :] - a[:, None])
+        best = np.argmin(d - 1e-12 * np.arange(0x7F)[None, :], axis=1)  # ties go up
+        return (best | np.where(np.signbit(x), 0x80, 0)).astype(np.uint8)
+    monkeypatch.setattr(codecs, "e4m3_encode", bad)
+    _fails(T_C.test_e4m3_golden_cases)
+
+
+def test_e4m3_missing_saturation_is_caught(monkeypatch):
+    orig = codecs.e4m3_encode
+    def bad(x):
+        x = np.asarray(x, dtype=np.float64)
+        return np.where(np.abs(x) > 464, np.uint8(0x7F), orig(x)).astype(np.uint8)
+    monkeypatch.setattr(codecs, "e4m3_encode", bad)
+    _fails(T_C.test_e4m3_saturation_and_signed_zero)
+
+
+def test_bf16_truncation_instead_of_rounding_is_caught(monkeypatch):
+    def bad(x):
+        v = np.asarray(x, dtype=np.float64).astype(np.float32)
+        return (v.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+    monkeypatch.setattr(codecs, "bf16_encode", bad)
+    _fails(T_C.test_bf16_golden_cases)
