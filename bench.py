@@ -1,0 +1,191 @@
+"""Decode-attention benchmark on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama3_8b_gqa]
+
+One step is one pass of the whole hot path over one batch: the fused NeoX
+RoPE + paged-KV append of the new token (lgm_rope_kv_append), then split-K
+paged GQA decode attention with its log-sum-exp merge (lgm_paged_decode_attn),
+all through the C ABI on torch's current stream, inputs resident in HBM.
+
+Printed: one JSON line with the KV bandwidth of the whole step (value, GB/s),
+tokens/s, the roofline of the attention launch (algorithmic KV bytes per
+launch over its average duration, timed with HIP events on its stream) and
+the fp64 CPU oracle timed on the host as a baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode attention KV GB/s (% of HBM peak) + tokens/s, 1 MI355X"
+HBM_PEAK_GBS = 8000.0
+CSRC = os.path.join(ROOT, "paged_gqa_decode_lgm_amd", "csrc")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, name), "rb") as fh:
+            h.update(name.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str, kv_bytes: int):
+    """HBM bytes per attention launch from committed rocprofv3 PMC runs, if they
+    were taken on the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        t = json.load(fh)
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, min_seconds: float = 10.0, max_passes: int = 3):
+    """The fp64 oracle on the whole batch (host copies of the same inputs), one
+    thread; passes repeat until ~min_seconds of work, the median pass is kept."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import workloads as W
+    from oracle import append as OAP
+    from oracle import attention as OA
+
+    c = w.cfg
+    kp, vp = W.storage_bits(w.k_pool), W.storage_bits(w.v_pool)
+    q = OAP.act_to_f64(W.storage_bits(w.qkv)[:, : c.num_q_heads * c.head_dim], c.act).reshape(
+        c.num_seqs, c.num_q_heads, c.head_dim)
+    times = []
+    with threadpool_limits(1):
+        while len(times) < max_passes and (not times or sum(times) < min_seconds):
+            t0 = time.perf_counter()
+            OA.paged_decode(q, kp, vp, w.block_tables.numpy(), w.context_lens.numpy(), c.softmax_scale,
+                            num_kv_heads=c.num_kv_heads, block_size=c.block_size, cache=c.cache,
+                            k_scale=None if w.k_scale is None else w.k_scale.numpy(),
+                            v_scale=None if w.v_scale is None else w.v_scale.numpy())
+            times.append(time.perf_counter() - t0)
+    t = statistics.median(times)
+    return {"value": round(w.kv_bytes() / t / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "tokens_per_s": round(c.num_seqs / t, 3),
+            "sample": f"attention over the whole {c.name} batch ({c.num_seqs} sequences, "
+                      f"{int(w.context_lens.sum())} cached tokens) in fp64 NumPy, 1 thread, median of "
+                      f"{len(times)} passes of {t:.2f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama3_8b_gqa")
+    ap.add_argument("--partition-size", type=int, default=None, help="override the workload's partition size")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (this build has no "
+              "multi-GPU path: the decode step shards by kv heads or sequence blocks, see DESIGN.md).",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    import workloads as W
+    from paged_gqa_decode_lgm_amd import ops
+
+    cfg = W.CONFIGS[args.workload]
+    if args.partition_size is not None:
+        cfg = cfg.with_(partition_size=args.partition_size)
+    w = W.make_workload(cfg)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cu = lambda t: None if t is None else t.to(dev)
+    qkv, k_pool, v_pool = cu(w.qkv), cu(w.k_pool), cu(w.v_pool)
+    bt, ctx, ks, vs = cu(w.block_tables), cu(w.context_lens), cu(w.k_scale), cu(w.v_scale)
+    max_ctx = int(w.context_lens.max())
+    B, Hq, D = cfg.num_seqs, cfg.num_q_heads, cfg.head_dim
+    q = torch.empty((B, Hq, D), dtype=qkv.dtype, device=dev)
+    if not cfg.append:
+        q.copy_(qkv[:, : Hq * D].reshape(B, Hq, D))
+    out = torch.empty((B, Hq, D), dtype=qkv.dtype, device=dev)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    ws_bytes = ops.workspace_bytes(q, k_pool, bt, max_ctx, cfg.partition_size)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    ps = ops.partition_size(q, k_pool, bt, max_ctx, cfg.partition_size)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if cfg.append:
+            if ev:
+                ev[0].record(stream)
+            ops.rope_kv_append(qkv, k_pool, v_pool, bt, ctx, cfg.rope_theta, Hq, ks, vs, q_out=q)
+        if ev:
+            ev[1].record(stream)
+        ops.paged_decode_attn(q, k_pool, v_pool, bt, ctx, max_ctx, softmax_scale=cfg.softmax_scale,
+                              partition_size=cfg.partition_size, k_scale=ks, v_scale=vs, out=out, out_lse=lse,
+                              workspace=ws)
+        if ev:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    attn_ms = [e[1].elapsed_time(e[2]) for e in events]
+    append_ms = [e[0].elapsed_time(e[1]) for e in events] if cfg.append else []
+    ms_per_step = wall * 1e3 / args.steps
+    kv = w.kv_bytes()
+    attn_avg_s = statistics.mean(attn_ms) / 1e3
+    achieved = kv / attn_avg_s / 1e9
+    value = kv / (ms_per_step / 1e3) / 1e9
+    traffic = measured_traffic(cfg.name, kv)
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.cache if cfg.cache != "fp8" else "fp8-e4m3 kv / bf16 act",
+        "data": "synthetic (seeded N(0,1) KV cache, packed QKV and block tables)",
+        "config": {"workload": cfg.name, "global_batch": B, "context": (list(cfg.ctx) if not isinstance(cfg.ctx, int)
+                   else cfg.ctx), "sum_context_tokens": int(w.context_lens.sum()), "num_q_heads": Hq,
+                   "num_kv_heads": cfg.num_kv_heads, "head_dim": D, "block_size": cfg.block_size,
+                   "partition_size": ps, "append": cfg.append, "parallelism": "single GPU"},
+        "tokens_per_s": round(B / (ms_per_step / 1e3), 1),
+        "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "kv_bytes_per_step": kv,
+        "kernel_ms": {"attention_avg": round(attn_avg_s * 1e3, 5),
+                      "attention_median": round(statistics.median(attn_ms), 5),
+                      "append_avg": round(statistics.mean(append_ms), 5) if append_ms else None},
+        "roofline": {"bound": "hbm", "kernel": "lgm_paged_decode_attn (split-K decode + LSE merge launches)",
+                     "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

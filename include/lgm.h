@@ -1,0 +1,228 @@
+/*
+ * lgm.h — paged GQA/MQA single-token decode attention for AMD MI355X (gfx950).
+ *
+ * A C ABI over hand-written HIP kernels.  Sources the operations follow:
+ *   [Loom]     Loom Kernels README (feichai0017/loom-kernels):
+ *              "Supported operator paths" table, rows "Position and KV"
+ *              (NeoX RoPE + native/static-FP8 paged-KV write over packed QKV
+ *              into NHD cache views, static per-tensor/per-head FP8 E4M3
+ *              scales, current-stream execution) and "Attention" (paged
+ *              MQA/GQA decode, local split-K/LSE merge); "Next value program"
+ *              (exact E4M3 cache bytes); "Architecture" (the backend accepts
+ *              the exact contract or returns an error, borrowed pointers and
+ *              the caller's stream).
+ *   [mainarch] mainarch README (MaincodeHQ/mainarch), decode-attention
+ *              section: FlashDecoding split-KV online softmax with a combine
+ *              of partial results, paged KV through a block table, GQA reads
+ *              the cache once per head group, OCP e4m3fn KV, every buffer in
+ *              VRAM (a host-visible scratch buffer pinned the whole pipeline
+ *              at 230 GB/s).
+ *   [microLLM] microLLM-rocm README, "Detailed implementation and experiment
+ *              ledger": split-half RoPE; positions-aware RoPE with mapped KV
+ *              store and per-row-prefix cached attention; bf16 KV storage
+ *              with fp32 accumulation.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * Ownership: the caller owns all memory.  Every pointer is borrowed for the
+ *   duration of the (asynchronous) work; the library allocates nothing, on
+ *   the device or the host, and keeps no pointer after the call returns.
+ * Device pointers: all tensor arguments are device (HBM) pointers.
+ * Stream: `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *   Work is enqueued on it; no call synchronises the host.
+ * Validation: every host-visible argument (pointers for NULL, dims, dtypes,
+ *   strides, partition size, workspace size, address-range aliasing) is
+ *   checked before any HIP call.  On a violation the call returns a nonzero
+ *   lgm_status, enqueues nothing, writes nothing, and lgm_last_error() names
+ *   the function, the argument and what was expected.  Unsupported
+ *   (dtype, head_dim, group, block_size) combinations return
+ *   LGM_ERR_UNSUPPORTED; there is no fallback path.  A failed launch returns
+ *   LGM_ERR_HIP.  Device-side faults surface at the caller's next sync.
+ * Device-resident contents (context lengths, block-table entries) cannot be
+ *   read by the host without a sync and are the caller's contract:
+ *     - context_lens[b] is clamped to [0, max_blocks_per_seq * block_size]
+ *       (and, for attention, to max_context_len); a sequence with length 0
+ *       is inactive;
+ *     - a block-table entry outside [0, num_blocks) is never dereferenced: the
+ *       append skips that write and attention masks those 16 tokens.
+ *   Entries for logical blocks at or beyond ceil(ctx / block_size) are never
+ *   read, so they may hold anything.
+ * Layouts (row-major, innermost last):
+ *   packed QKV  [B][(Hq + 2*Hkv) * D] per row: Q heads, then K heads, then V
+ *               heads, each D contiguous; rows qkv_row_stride elements apart.
+ *   KV caches   NHD: [num_blocks][block_size][Hkv][D], K and V in separate
+ *               pools with identical indexing and dtype.
+ *   block table int32 [B][max_blocks_per_seq]: logical block -> physical.
+ *   context len int32 [B]: tokens in the cache INCLUDING the new token, so
+ *               the new token sits at position ctx - 1.
+ *   q / out     [B][Hq][D]; q rows q_seq_stride elements apart, out dense.
+ * Query head h reads KV head h / (Hq / Hkv) (contiguous groups).
+ */
+#ifndef LGM_H_
+#define LGM_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LGM_ABI_VERSION 1
+
+typedef enum lgm_status {
+  LGM_OK = 0,
+  LGM_ERR_INVALID_ARGUMENT = 1,
+  LGM_ERR_UNSUPPORTED = 2,
+  LGM_ERR_WORKSPACE_TOO_SMALL = 3,
+  LGM_ERR_HIP = 4
+} lgm_status;
+
+/* Element types.  LGM_FP8_E4M3 is OCP e4m3fn ([mainarch]): bias 7, largest
+ * finite 448, 0x7F/0xFF NaN, no infinities. */
+typedef enum lgm_dtype { LGM_F32 = 0, LGM_BF16 = 1, LGM_FP8_E4M3 = 2 } lgm_dtype;
+
+/* Shapes shared by the calls.  num_seqs = B, num_q_heads = Hq,
+ * num_kv_heads = Hkv (Hq % Hkv == 0), head_dim = D, block_size = tokens per
+ * cache block, num_blocks = blocks in each pool, max_blocks_per_seq = block
+ * table row length. */
+typedef struct lgm_paged_dims {
+  int32_t num_seqs;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t block_size;
+  int32_t num_blocks;
+  int32_t max_blocks_per_seq;
+} lgm_paged_dims;
+
+/*
+ * Fused NeoX RoPE + paged-KV append of the new token ([Loom] "Position and
+ * KV"; [microLLM] split-half RoPE, mapped KV store).
+ *
+ * For each sequence b with ctx = context_lens[b] >= 1, pos = ctx - 1:
+ *   every Q head and K head x of qkv row b is rotated split-half:
+ *     pair i < D/2 is (x[i], x[i + D/2]), angle = pos * theta^(-2i/D),
+ *     y[i] = x[i] cos - x[i+D/2] sin,  y[i+D/2] = x[i+D/2] cos + x[i] sin,
+ *   evaluated as: angle, cos and sin in fp64, cos and sin rounded once to
+ *   fp32, then each product and each sum rounded to fp32 (no fused
+ *   multiply-add);
+ *   rotated Q -> q_out[b] (act dtype, round to nearest even);
+ *   rotated K and the unrotated V head g -> slot (pos % block_size) of
+ *   physical block block_tables[b][pos / block_size], kv head g, in the
+ *   cache dtype: f32 as is, bf16 round to nearest even, FP8 E4M3 as
+ *   E4M3(y / scale[g]) with an IEEE fp32 division, round to nearest even,
+ *   magnitudes above 448 saturating to +-448, sign kept for zero.
+ * A sequence with ctx <= 0 writes nothing to the caches and its q_out row is
+ * Q unrotated (angle 0).
+ *
+ *   qkv            [B][row] act dtype, row stride qkv_row_stride >= (Hq+2Hkv)*D
+ *   q_out          [B][Hq][D] act dtype (dense); must not overlap any input
+ *   k_cache,v_cache NHD pools, cache dtype; written only at the B slots
+ *   block_tables   int32 [B][max_blocks_per_seq]
+ *   context_lens   int32 [B]
+ *   k_scale,v_scale fp32 [Hkv] when cache_dtype is LGM_FP8_E4M3, else NULL
+ *   rope_theta     > 0, finite
+ * Supported: (act, cache) in {(F32, F32), (BF16, BF16), (BF16, FP8_E4M3)};
+ * head_dim even, 2..256; block_size >= 1.  Append slots must be distinct
+ * across the batch (the caller's contract; two sequences writing one slot
+ * race).
+ */
+lgm_status lgm_rope_kv_append(const void* qkv, int64_t qkv_row_stride, void* q_out, void* k_cache,
+                              void* v_cache, const int32_t* block_tables,
+                              const int32_t* context_lens, const float* k_scale,
+                              const float* v_scale, float rope_theta, lgm_paged_dims dims,
+                              lgm_dtype act_dtype, lgm_dtype cache_dtype, void* stream);
+
+/*
+ * Partition size the attention call will use.  partition_size 0 lets the
+ * library choose from the shapes alone (deterministic, no device query);
+ * a positive value must be a multiple of block_size and is returned as is.
+ * Returns -1 (and sets lgm_last_error) on invalid arguments.
+ */
+int32_t lgm_paged_decode_partition_size(lgm_paged_dims dims, int32_t max_context_len,
+                                        int32_t partition_size, lgm_dtype cache_dtype);
+
+/*
+ * Bytes of device workspace lgm_paged_decode_attn needs for these
+ * arguments: 0 when every sequence fits one partition, otherwise room for
+ * the split-K records (fp32 partial outputs [B][Hq][P][D] and natural-log
+ * LSEs [B][Hq][P], P = ceil(max_context_len / partition)) plus alignment.
+ * Returns 0 and sets lgm_last_error on invalid arguments (check it when 0 is
+ * unexpected).
+ */
+size_t lgm_paged_decode_workspace_size(lgm_paged_dims dims, int32_t max_context_len,
+                                       int32_t partition_size, lgm_dtype cache_dtype);
+
+/*
+ * Paged GQA/MQA decode attention ([mainarch] decode attention; [Loom]
+ * "Attention").  For each sequence b, query head h, kv head g = h / G,
+ * L = min(context_lens[b], max_context_len):
+ *   s_j = softmax_scale * <q[b][h], K_j>,  j < L, K_j = cache row of token j
+ *         through the block table (FP8: decoded byte * k_scale[g]),
+ *   out[b][h] = sum_j softmax(s)_j V_j   (FP8: V_j = decoded byte * v_scale[g]),
+ *   out_lse[b][h] = log(sum_j exp(s_j))  (natural log; -inf and out = 0 when L = 0).
+ * Arithmetic is fp32 with one final rounding to the act dtype.  Contexts are
+ * cut into partitions of `partition_size` tokens (see
+ * lgm_paged_decode_partition_size) processed in parallel; partial results
+ * are merged by log-sum-exp (as lgm_lse_merge) on the same stream, within
+ * this call.  A sequence that fits one partition is written directly.
+ *
+ *   out            [B][Hq][D] act dtype (dense)
+ *   out_lse        optional fp32 [B][Hq] (NULL = not written)
+ *   q              [B][Hq][D] act dtype, rows q_seq_stride >= Hq*D elements apart;
+ *                  may be the q_out of lgm_rope_kv_append
+ *   k_cache,v_cache NHD pools (cache dtype), read only
+ *   k_scale,v_scale fp32 [Hkv] for LGM_FP8_E4M3 caches, else NULL
+ *   softmax_scale  finite (normally 1/sqrt(D) rounded to fp32)
+ *   partition_size 0 = library chooses; else a positive multiple of
+ *                  block_size; >= max_context_len means no split
+ *   max_context_len upper bound on context_lens, 0..max_blocks_per_seq*block_size
+ *   workspace      device buffer of at least lgm_paged_decode_workspace_size()
+ *                  bytes, 256-byte aligned (NULL allowed when that size is 0);
+ *                  its contents are scratch
+ * Supported: (act, cache) in {(F32, F32), (BF16, BF16), (BF16, FP8_E4M3)},
+ * head_dim in {64, 128}, block_size 16, G = Hq/Hkv in 1..16.
+ * out must not overlap q, the caches or the workspace.
+ */
+lgm_status lgm_paged_decode_attn(void* out, float* out_lse, const void* q, int64_t q_seq_stride,
+                                 const void* k_cache, const void* v_cache,
+                                 const int32_t* block_tables, const int32_t* context_lens,
+                                 const float* k_scale, const float* v_scale, float softmax_scale,
+                                 int32_t partition_size, int32_t max_context_len, void* workspace,
+                                 size_t workspace_bytes, lgm_paged_dims dims, lgm_dtype act_dtype,
+                                 lgm_dtype cache_dtype, void* stream);
+
+/*
+ * Log-sum-exp merge of split-K records ([mainarch] combine of split
+ * partials; [Loom] local split-K/LSE merge).  For each (b, h) with
+ * n = num_partitions[b] (clamped to [0, max_partitions]; NULL = all):
+ *   M = max_p lse_p,  w_p = exp(lse_p - M),
+ *   out[b][h] = sum_p w_p o_p / sum_p w_p,  out_lse[b][h] = M + log(sum_p w_p);
+ * records with lse = -inf weigh 0; n = 0 or all -inf gives out = 0,
+ * out_lse = -inf.  Summation order is fixed (bitwise reproducible).
+ *
+ *   out            [B][H][D] out_dtype (LGM_F32 or LGM_BF16), dense
+ *   out_lse        optional fp32 [B][H]
+ *   partial_out    fp32 [B][H][max_partitions][D], normalised partial outputs
+ *   partial_lse    fp32 [B][H][max_partitions], natural log
+ *   num_partitions optional int32 [B]
+ * Supported: head_dim a multiple of 4, 4..512.
+ */
+lgm_status lgm_lse_merge(void* out, float* out_lse, const float* partial_out,
+                         const float* partial_lse, const int32_t* num_partitions,
+                         int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                         int32_t max_partitions, lgm_dtype out_dtype, void* stream);
+
+/* Message of the last failed lgm_* call on this thread ("" if none).  Valid
+ * until the next lgm_* call on the same thread. */
+const char* lgm_last_error(void);
+
+/* LGM_ABI_VERSION of the loaded library. */
+int32_t lgm_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LGM_H_ */

@@ -1,0 +1,66 @@
+"""Build liblgm.so in-tree with hipcc for gfx950.
+
+    python -m paged_gqa_decode_lgm_amd.build [--verbose]
+
+Each translation unit is compiled separately (the RoPE/append unit with
+-ffp-contract=off so no multiply-add is fused) and linked into
+paged_gqa_decode_lgm_amd/liblgm.so.  Packed-fp32 VALU ops are disabled for all
+device code.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+BUILD = os.path.join(PKG, "_build")
+LIB = os.path.join(PKG, "liblgm.so")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+
+COMMON = [
+    "-O3", f"--offload-arch={ARCH}", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function",
+    "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+]
+UNITS = {
+    "lgm_api.cpp": ["-x", "hip"],
+    "rope_kv_append.hip": ["-ffp-contract=off"],
+    "paged_decode.hip": [],
+    "lse_merge.hip": [],
+}
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError(f"build step failed: {' '.join(cmd)}")
+    return r
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+
+    def compile_one(item):
+        src, extra = item
+        obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+        _run([HIPCC, *COMMON, *extra, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
+        return obj
+
+    with ThreadPoolExecutor(min(len(UNITS), os.cpu_count() or 1)) as ex:
+        objs = list(ex.map(compile_one, UNITS.items()))
+    tmp = LIB + ".tmp"
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="--verbose" in sys.argv))

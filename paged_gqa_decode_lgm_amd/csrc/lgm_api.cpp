@@ -1,0 +1,354 @@
+// C-ABI host layer: validates every host-visible argument before any HIP
+// call, resolves the partition plan, and launches the kernels on the
+// caller's stream.  "Accept the exact contract or return an error" (Loom
+// Kernels README, "Architecture"); error text names the function, the
+// argument and what was expected (the span check of mainarch's VA guard,
+// troubleshooting section, is the model).  Nothing here allocates device or
+// host memory.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <cmath>
+#include <string>
+
+#include "lgm_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+lgm_status fail(lgm_status st, const char* fn, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = std::string(fn) + ": " + buf;
+  return st;
+}
+
+const char* dtype_name(lgm_dtype t) {
+  switch (t) {
+    case LGM_F32: return "LGM_F32";
+    case LGM_BF16: return "LGM_BF16";
+    case LGM_FP8_E4M3: return "LGM_FP8_E4M3";
+  }
+  return "invalid";
+}
+
+bool dtype_valid(int t) { return t == LGM_F32 || t == LGM_BF16 || t == LGM_FP8_E4M3; }
+
+int64_t elem_bytes(lgm_dtype t) { return t == LGM_F32 ? 4 : (t == LGM_BF16 ? 2 : 1); }
+
+struct Span {
+  const char* name;
+  uintptr_t lo;
+  int64_t bytes;
+};
+
+bool overlap(const Span& a, const Span& b) {
+  if (!a.lo || !b.lo || a.bytes <= 0 || b.bytes <= 0) return false;
+  return a.lo < b.lo + (uintptr_t)b.bytes && b.lo < a.lo + (uintptr_t)a.bytes;
+}
+
+// Shared dims checks.  head_dim / block_size support is checked by the caller.
+lgm_status check_dims(const char* fn, const lgm_paged_dims& d) {
+  if (d.num_seqs < 0) return fail(LGM_ERR_INVALID_ARGUMENT, fn, "dims.num_seqs = %d must be >= 0", d.num_seqs);
+  if (d.num_q_heads < 1)
+    return fail(LGM_ERR_INVALID_ARGUMENT, fn, "dims.num_q_heads = %d must be >= 1", d.num_q_heads);
+  if (d.num_kv_heads < 1)
+    return fail(LGM_ERR_INVALID_ARGUMENT, fn, "dims.num_kv_heads = %d must be >= 1", d.num_kv_heads);
+  if (d.num_q_heads % d.num_kv_heads != 0)
+    return fail(LGM_ERR_INVALID_ARGUMENT, fn, "dims.num_q_heads = %d must be a multiple of dims.num_kv_heads = %d",
+                d.num_q_heads, d.num_kv_heads);
+  if (d.head_dim < 2 || d.head_dim % 2 != 0)
+    return fail(LGM_ERR_INVALID_ARGUMENT, fn, "dims.head_dim = %d must be even and >= 2", d.head_dim);
+  if (d.block_size < 1) return fail(LGM_ERR_INVALID_ARGUMENT, fn, "dims.block_size = %d must be >= 1", d.block_size);
+  if (d.num_blocks < 1) return fail(LGM_ERR_INVALID_ARGUMENT, fn, "dims.num_blocks = %d must be >= 1", d.num_blocks);
+  if (d.max_blocks_per_seq < 1)
+    return fail(LGM_ERR_INVALID_ARGUMENT, fn, "dims.max_blocks_per_seq = %d must be >= 1", d.max_blocks_per_seq);
+  if ((int64_t)d.max_blocks_per_seq * d.block_size > INT32_MAX)
+    return fail(LGM_ERR_INVALID_ARGUMENT, fn, "dims.max_blocks_per_seq * dims.block_size = %lld exceeds INT32_MAX",
+                (long long)d.max_blocks_per_seq * d.block_size);
+  return LGM_OK;
+}
+
+int64_t cache_bytes(const lgm_paged_dims& d, lgm_dtype cache) {
+  return (int64_t)d.num_blocks * d.block_size * d.num_kv_heads * d.head_dim * elem_bytes(cache);
+}
+
+lgm_status check_scales(const char* fn, lgm_dtype cache, const float* k_scale, const float* v_scale) {
+  if (cache == LGM_FP8_E4M3) {
+    if (!k_scale) return fail(LGM_ERR_INVALID_ARGUMENT, fn, "k_scale is NULL; LGM_FP8_E4M3 caches need fp32 [num_kv_heads] scales");
+    if (!v_scale) return fail(LGM_ERR_INVALID_ARGUMENT, fn, "v_scale is NULL; LGM_FP8_E4M3 caches need fp32 [num_kv_heads] scales");
+  } else {
+    if (k_scale || v_scale)
+      return fail(LGM_ERR_INVALID_ARGUMENT, fn, "k_scale / v_scale must be NULL for a %s cache", dtype_name(cache));
+  }
+  return LGM_OK;
+}
+
+lgm_status check_no_alias(const char* fn, const Span* outs, int n_out, const Span* ins, int n_in) {
+  for (int i = 0; i < n_out; ++i) {
+    for (int j = i + 1; j < n_out; ++j)
+      if (overlap(outs[i], outs[j]))
+        return fail(LGM_ERR_INVALID_ARGUMENT, fn, "output '%s' overlaps output '%s'", outs[i].name, outs[j].name);
+    for (int j = 0; j < n_in; ++j)
+      if (overlap(outs[i], ins[j]))
+        return fail(LGM_ERR_INVALID_ARGUMENT, fn, "output '%s' overlaps input '%s' (%lld bytes at %p)", outs[i].name,
+                    ins[j].name, (long long)ins[j].bytes, (void*)ins[j].lo);
+  }
+  return LGM_OK;
+}
+
+constexpr int kAutoTargetWorkgroups = 8192;
+constexpr int kMinAutoPartitionBlocks = 4;
+
+// Partition plan: returns the partition size in tokens, or -1 after setting the error.
+int32_t resolve_partition(const char* fn, const lgm_paged_dims& d, int32_t max_ctx, int32_t ps) {
+  if (ps < 0) {
+    fail(LGM_ERR_INVALID_ARGUMENT, fn, "partition_size = %d must be 0 (library chooses) or positive", ps);
+    return -1;
+  }
+  if (ps > 0 && ps % d.block_size != 0) {
+    fail(LGM_ERR_INVALID_ARGUMENT, fn, "partition_size = %d must be a multiple of dims.block_size = %d", ps,
+         d.block_size);
+    return -1;
+  }
+  const int64_t cap = ((int64_t)(max_ctx > 0 ? max_ctx : 1) + d.block_size - 1) / d.block_size * d.block_size;
+  if (ps == 0) {
+    // Enough partitions that the grid holds ~kAutoTargetWorkgroups workgroups
+    // at the longest context, but never fewer than 4 blocks (one per wave).
+    const int64_t units = (int64_t)(d.num_seqs > 0 ? d.num_seqs : 1) * d.num_kv_heads;
+    const int64_t parts = (kAutoTargetWorkgroups + units - 1) / units;
+    int64_t p = (cap + parts - 1) / parts;
+    p = (p + d.block_size - 1) / d.block_size * d.block_size;
+    const int64_t minp = (int64_t)kMinAutoPartitionBlocks * d.block_size;
+    ps = (int32_t)(p < minp ? minp : p);
+  }
+  return (int32_t)(ps < cap ? ps : cap);
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct Workspace {
+  size_t part_out_bytes, part_lse_bytes, total;
+};
+
+Workspace workspace_layout(const lgm_paged_dims& d, int32_t P) {
+  Workspace w{0, 0, 0};
+  if (P <= 1) return w;
+  w.part_out_bytes = align256((size_t)d.num_seqs * d.num_q_heads * P * d.head_dim * sizeof(float));
+  w.part_lse_bytes = align256((size_t)d.num_seqs * d.num_q_heads * P * sizeof(float));
+  w.total = w.part_out_bytes + w.part_lse_bytes;
+  return w;
+}
+
+lgm_status check_decode_common(const char* fn, const lgm_paged_dims& d, int32_t max_ctx, lgm_dtype cache) {
+  lgm_status st = check_dims(fn, d);
+  if (st != LGM_OK) return st;
+  if (!dtype_valid(cache)) return fail(LGM_ERR_INVALID_ARGUMENT, fn, "cache_dtype = %d is not an lgm_dtype", (int)cache);
+  const int64_t cap = (int64_t)d.max_blocks_per_seq * d.block_size;
+  if (max_ctx < 0 || max_ctx > cap)
+    return fail(LGM_ERR_INVALID_ARGUMENT, fn,
+                "max_context_len = %d must be in [0, max_blocks_per_seq * block_size = %lld]", max_ctx, (long long)cap);
+  return LGM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* lgm_last_error(void) { return g_err.c_str(); }
+
+int32_t lgm_abi_version(void) { return LGM_ABI_VERSION; }
+
+lgm_status lgm_rope_kv_append(const void* qkv, int64_t qkv_row_stride, void* q_out, void* k_cache, void* v_cache,
+                              const int32_t* block_tables, const int32_t* context_lens, const float* k_scale,
+                              const float* v_scale, float rope_theta, lgm_paged_dims dims, lgm_dtype act_dtype,
+                              lgm_dtype cache_dtype, void* stream) {
+  const char* fn = "lgm_rope_kv_append";
+  g_err.clear();
+  lgm_status st = check_dims(fn, dims);
+  if (st != LGM_OK) return st;
+  if (dims.head_dim > 256)
+    return fail(LGM_ERR_UNSUPPORTED, fn, "dims.head_dim = %d: supported head_dim is even, 2..256", dims.head_dim);
+  if (!dtype_valid(act_dtype)) return fail(LGM_ERR_INVALID_ARGUMENT, fn, "act_dtype = %d is not an lgm_dtype", (int)act_dtype);
+  if (!dtype_valid(cache_dtype))
+    return fail(LGM_ERR_INVALID_ARGUMENT, fn, "cache_dtype = %d is not an lgm_dtype", (int)cache_dtype);
+  const bool types_ok = (act_dtype == LGM_F32 && cache_dtype == LGM_F32) ||
+                        (act_dtype == LGM_BF16 && cache_dtype == LGM_BF16) ||
+                        (act_dtype == LGM_BF16 && cache_dtype == LGM_FP8_E4M3);
+  if (!types_ok)
+    return fail(LGM_ERR_UNSUPPORTED, fn, "(act_dtype, cache_dtype) = (%s, %s): supported are (F32, F32), "
+                "(BF16, BF16), (BF16, FP8_E4M3)", dtype_name(act_dtype), dtype_name(cache_dtype));
+  if (!(std::isfinite(rope_theta) && rope_theta > 0.f))
+    return fail(LGM_ERR_INVALID_ARGUMENT, fn, "rope_theta = %g must be finite and > 0", (double)rope_theta);
+  const int64_t row = (int64_t)(dims.num_q_heads + 2 * dims.num_kv_heads) * dims.head_dim;
+  if (qkv_row_stride < row)
+    return fail(LGM_ERR_INVALID_ARGUMENT, fn, "qkv_row_stride = %lld must be >= (Hq + 2*Hkv) * D = %lld",
+                (long long)qkv_row_stride, (long long)row);
+  if ((st = check_scales(fn, cache_dtype, k_scale, v_scale)) != LGM_OK) return st;
+  if (dims.num_seqs == 0) return LGM_OK;
+  if (!qkv) return fail(LGM_ERR_INVALID_ARGUMENT, fn, "qkv is NULL");
+  if (!q_out) return fail(LGM_ERR_INVALID_ARGUMENT, fn, "q_out is NULL");
+  if (!k_cache) return fail(LGM_ERR_INVALID_ARGUMENT, fn, "k_cache is NULL");
+  if (!v_cache) return fail(LGM_ERR_INVALID_ARGUMENT, fn, "v_cache is NULL");
+  if (!block_tables) return fail(LGM_ERR_INVALID_ARGUMENT, fn, "block_tables is NULL");
+  if (!context_lens) return fail(LGM_ERR_INVALID_ARGUMENT, fn, "context_lens is NULL");
+
+  const int64_t ea = elem_bytes(act_dtype);
+  const int64_t B = dims.num_seqs;
+  const Span outs[] = {{"q_out", (uintptr_t)q_out, B * dims.num_q_heads * dims.head_dim * ea},
+                       {"k_cache", (uintptr_t)k_cache, cache_bytes(dims, cache_dtype)},
+                       {"v_cache", (uintptr_t)v_cache, cache_bytes(dims, cache_dtype)}};
+  const Span ins[] = {{"qkv", (uintptr_t)qkv, ((B - 1) * qkv_row_stride + row) * ea},
+                      {"block_tables", (uintptr_t)block_tables, B * dims.max_blocks_per_seq * 4},
+                      {"context_lens", (uintptr_t)context_lens, B * 4},
+                      {"k_scale", (uintptr_t)k_scale, k_scale ? (int64_t)dims.num_kv_heads * 4 : 0},
+                      {"v_scale", (uintptr_t)v_scale, v_scale ? (int64_t)dims.num_kv_heads * 4 : 0}};
+  if ((st = check_no_alias(fn, outs, 3, ins, 5)) != LGM_OK) return st;
+
+  lgm::AppendArgs a{qkv, qkv_row_stride, q_out, k_cache, v_cache, block_tables, context_lens,
+                    k_scale, v_scale, rope_theta, dims};
+  const hipError_t e = lgm::launch_rope_kv_append(a, act_dtype, cache_dtype, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(LGM_ERR_HIP, fn, "kernel launch failed: %s", hipGetErrorString(e));
+  return LGM_OK;
+}
+
+int32_t lgm_paged_decode_partition_size(lgm_paged_dims dims, int32_t max_context_len, int32_t partition_size,
+                                        lgm_dtype cache_dtype) {
+  const char* fn = "lgm_paged_decode_partition_size";
+  g_err.clear();
+  if (check_decode_common(fn, dims, max_context_len, cache_dtype) != LGM_OK) return -1;
+  return resolve_partition(fn, dims, max_context_len, partition_size);
+}
+
+size_t lgm_paged_decode_workspace_size(lgm_paged_dims dims, int32_t max_context_len, int32_t partition_size,
+                                       lgm_dtype cache_dtype) {
+  const char* fn = "lgm_paged_decode_workspace_size";
+  g_err.clear();
+  if (check_decode_common(fn, dims, max_context_len, cache_dtype) != LGM_OK) return 0;
+  const int32_t ps = resolve_partition(fn, dims, max_context_len, partition_size);
+  if (ps < 0) return 0;
+  const int32_t P = max_context_len <= 0 ? 1 : (max_context_len + ps - 1) / ps;
+  return workspace_layout(dims, P).total;
+}
+
+lgm_status lgm_paged_decode_attn(void* out, float* out_lse, const void* q, int64_t q_seq_stride, const void* k_cache,
+                                 const void* v_cache, const int32_t* block_tables, const int32_t* context_lens,
+                                 const float* k_scale, const float* v_scale, float softmax_scale,
+                                 int32_t partition_size, int32_t max_context_len, void* workspace,
+                                 size_t workspace_bytes, lgm_paged_dims dims, lgm_dtype act_dtype,
+                                 lgm_dtype cache_dtype, void* stream) {
+  const char* fn = "lgm_paged_decode_attn";
+  g_err.clear();
+  lgm_status st = check_decode_common(fn, dims, max_context_len, cache_dtype);
+  if (st != LGM_OK) return st;
+  if (!dtype_valid(act_dtype)) return fail(LGM_ERR_INVALID_ARGUMENT, fn, "act_dtype = %d is not an lgm_dtype", (int)act_dtype);
+  const int G = dims.num_q_heads / dims.num_kv_heads;
+  if (!lgm::decode_supported(act_dtype, cache_dtype, dims.head_dim, G, dims.block_size))
+    return fail(LGM_ERR_UNSUPPORTED, fn,
+                "(act %s, cache %s, head_dim %d, group %d, block_size %d) unsupported: supported are (F32, F32), "
+                "(BF16, BF16), (BF16, FP8_E4M3) with head_dim 64 or 128, group 1..8, block_size 16",
+                dtype_name(act_dtype), dtype_name(cache_dtype), dims.head_dim, G, dims.block_size);
+  if (dims.num_seqs > 65535 || dims.num_kv_heads > 65535)
+    return fail(LGM_ERR_UNSUPPORTED, fn, "dims.num_seqs = %d / dims.num_kv_heads = %d: at most 65535 each",
+                dims.num_seqs, dims.num_kv_heads);
+  if (!std::isfinite(softmax_scale))
+    return fail(LGM_ERR_INVALID_ARGUMENT, fn, "softmax_scale = %g must be finite", (double)softmax_scale);
+  const int64_t qrow = (int64_t)dims.num_q_heads * dims.head_dim;
+  if (q_seq_stride < qrow)
+    return fail(LGM_ERR_INVALID_ARGUMENT, fn, "q_seq_stride = %lld must be >= num_q_heads * head_dim = %lld",
+                (long long)q_seq_stride, (long long)qrow);
+  if ((st = check_scales(fn, cache_dtype, k_scale, v_scale)) != LGM_OK) return st;
+  const int32_t ps = resolve_partition(fn, dims, max_context_len, partition_size);
+  if (ps < 0) return LGM_ERR_INVALID_ARGUMENT;
+  const int32_t P = max_context_len <= 0 ? 1 : (max_context_len + ps - 1) / ps;
+  const Workspace ws = workspace_layout(dims, P);
+  if (ws.total > 0) {
+    if (!workspace)
+      return fail(LGM_ERR_WORKSPACE_TOO_SMALL, fn, "workspace is NULL but %zu bytes are needed (partition %d, %d partitions)",
+                  ws.total, ps, P);
+    if (workspace_bytes < ws.total)
+      return fail(LGM_ERR_WORKSPACE_TOO_SMALL, fn, "workspace_bytes = %zu < %zu needed (partition %d, %d partitions)",
+                  workspace_bytes, ws.total, ps, P);
+    if ((uintptr_t)workspace % 256 != 0)
+      return fail(LGM_ERR_INVALID_ARGUMENT, fn, "workspace %p must be 256-byte aligned", workspace);
+  }
+  if (dims.num_seqs == 0) return LGM_OK;
+  if (!out) return fail(LGM_ERR_INVALID_ARGUMENT, fn, "out is NULL");
+  if (!q) return fail(LGM_ERR_INVALID_ARGUMENT, fn, "q is NULL");
+  if (!k_cache) return fail(LGM_ERR_INVALID_ARGUMENT, fn, "k_cache is NULL");
+  if (!v_cache) return fail(LGM_ERR_INVALID_ARGUMENT, fn, "v_cache is NULL");
+  if (!block_tables) return fail(LGM_ERR_INVALID_ARGUMENT, fn, "block_tables is NULL");
+  if (!context_lens) return fail(LGM_ERR_INVALID_ARGUMENT, fn, "context_lens is NULL");
+  if ((uintptr_t)k_cache % 16 != 0 || (uintptr_t)v_cache % 16 != 0)
+    return fail(LGM_ERR_INVALID_ARGUMENT, fn, "k_cache (%p) and v_cache (%p) must be 16-byte aligned", k_cache, v_cache);
+
+  const int64_t ea = elem_bytes(act_dtype);
+  const int64_t B = dims.num_seqs;
+  const Span outs[] = {{"out", (uintptr_t)out, B * qrow * ea},
+                       {"out_lse", (uintptr_t)out_lse, out_lse ? B * dims.num_q_heads * 4 : 0},
+                       {"workspace", (uintptr_t)workspace, (int64_t)ws.total}};
+  const Span ins[] = {{"q", (uintptr_t)q, ((B - 1) * q_seq_stride + qrow) * ea},
+                      {"k_cache", (uintptr_t)k_cache, cache_bytes(dims, cache_dtype)},
+                      {"v_cache", (uintptr_t)v_cache, cache_bytes(dims, cache_dtype)},
+                      {"block_tables", (uintptr_t)block_tables, B * dims.max_blocks_per_seq * 4},
+                      {"context_lens", (uintptr_t)context_lens, B * 4},
+                      {"k_scale", (uintptr_t)k_scale, k_scale ? (int64_t)dims.num_kv_heads * 4 : 0},
+                      {"v_scale", (uintptr_t)v_scale, v_scale ? (int64_t)dims.num_kv_heads * 4 : 0}};
+  if ((st = check_no_alias(fn, outs, 3, ins, 7)) != LGM_OK) return st;
+
+  float* part_out = ws.total ? static_cast<float*>(workspace) : nullptr;
+  float* part_lse = ws.total ? reinterpret_cast<float*>(static_cast<char*>(workspace) + ws.part_out_bytes) : nullptr;
+  lgm::DecodeArgs a{out, out_lse, q, q_seq_stride, k_cache, v_cache, block_tables, context_lens, k_scale, v_scale,
+                    part_out, part_lse, softmax_scale, ps, max_context_len, P, dims};
+  hipError_t e = lgm::launch_paged_decode(a, act_dtype, cache_dtype, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(LGM_ERR_HIP, fn, "split kernel launch failed: %s", hipGetErrorString(e));
+  if (P > 1) {
+    lgm::MergeArgs m{out, out_lse, part_out, part_lse, nullptr, context_lens, ps, max_context_len,
+                     dims.num_seqs, dims.num_q_heads, dims.head_dim, P, 1};
+    e = lgm::launch_lse_merge(m, act_dtype, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(LGM_ERR_HIP, fn, "merge kernel launch failed: %s", hipGetErrorString(e));
+  }
+  return LGM_OK;
+}
+
+lgm_status lgm_lse_merge(void* out, float* out_lse, const float* partial_out, const float* partial_lse,
+                         const int32_t* num_partitions, int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                         int32_t max_partitions, lgm_dtype out_dtype, void* stream) {
+  const char* fn = "lgm_lse_merge";
+  g_err.clear();
+  if (num_seqs < 0) return fail(LGM_ERR_INVALID_ARGUMENT, fn, "num_seqs = %d must be >= 0", num_seqs);
+  if (num_q_heads < 1) return fail(LGM_ERR_INVALID_ARGUMENT, fn, "num_q_heads = %d must be >= 1", num_q_heads);
+  if (max_partitions < 1)
+    return fail(LGM_ERR_INVALID_ARGUMENT, fn, "max_partitions = %d must be >= 1", max_partitions);
+  if (!(out_dtype == LGM_F32 || out_dtype == LGM_BF16))
+    return fail(LGM_ERR_UNSUPPORTED, fn, "out_dtype = %d: supported are LGM_F32 and LGM_BF16", (int)out_dtype);
+  if (!lgm::merge_supported(head_dim))
+    return fail(LGM_ERR_UNSUPPORTED, fn, "head_dim = %d: supported are 64 and 128", head_dim);
+  if (num_seqs > 65535)
+    return fail(LGM_ERR_UNSUPPORTED, fn, "num_seqs = %d: at most 65535", num_seqs);
+  if (num_seqs == 0) return LGM_OK;
+  if (!out) return fail(LGM_ERR_INVALID_ARGUMENT, fn, "out is NULL");
+  if (!partial_out) return fail(LGM_ERR_INVALID_ARGUMENT, fn, "partial_out is NULL");
+  if (!partial_lse) return fail(LGM_ERR_INVALID_ARGUMENT, fn, "partial_lse is NULL");
+  if ((uintptr_t)partial_out % 16 != 0)
+    return fail(LGM_ERR_INVALID_ARGUMENT, fn, "partial_out %p must be 16-byte aligned", (const void*)partial_out);
+  const int64_t rows = (int64_t)num_seqs * num_q_heads;
+  const Span outs[] = {{"out", (uintptr_t)out, rows * head_dim * elem_bytes(out_dtype)},
+                       {"out_lse", (uintptr_t)out_lse, out_lse ? rows * 4 : 0}};
+  const Span ins[] = {{"partial_out", (uintptr_t)partial_out, rows * max_partitions * head_dim * 4},
+                      {"partial_lse", (uintptr_t)partial_lse, rows * max_partitions * 4},
+                      {"num_partitions", (uintptr_t)num_partitions, num_partitions ? (int64_t)num_seqs * 4 : 0}};
+  lgm_status st = check_no_alias(fn, outs, 2, ins, 3);
+  if (st != LGM_OK) return st;
+  lgm::MergeArgs m{out, out_lse, partial_out, partial_lse, num_partitions, nullptr, 0, 0,
+                   num_seqs, num_q_heads, head_dim, max_partitions, 0};
+  const hipError_t e = lgm::launch_lse_merge(m, out_dtype, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(LGM_ERR_HIP, fn, "kernel launch failed: %s", hipGetErrorString(e));
+  return LGM_OK;
+}
+
+}  // extern "C"

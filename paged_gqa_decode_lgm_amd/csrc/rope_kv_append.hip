@@ -1,0 +1,141 @@
+// Fused NeoX RoPE + paged-KV append of the new token (Loom Kernels README,
+// "Supported operator paths", row "Position and KV": packed QKV in, rotated
+// Q out, K/V written into NHD cache blocks natively or as static-scaled FP8
+// E4M3; "Next value program": exact E4M3 bytes; microLLM-rocm ledger:
+// split-half RoPE, positions-aware RoPE with a mapped KV store).
+//
+// One workgroup per sequence.  The D/2 rotation factors for the sequence's
+// position are computed once into LDS: angle = pos * theta^(-2i/D) with
+// theta^(-2i/D), the angle, its cosine and sine in fp64, cosine and sine
+// rounded once to fp32.  The rotation itself is fp32 with every product and
+// sum rounded on its own: this translation unit is built with
+// -ffp-contract=off and the pragma below, so no multiply-add is fused.
+#include "device_num.h"
+#include "lgm_internal.h"
+
+#pragma clang fp contract(off)
+
+namespace lgm {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kMaxHalf = 128;
+
+struct ActF32 {
+  using elem_t = float;
+  __device__ static float load(const elem_t* p) { return *p; }
+  __device__ static elem_t store(float x) { return x; }
+};
+struct ActBF16 {
+  using elem_t = uint16_t;
+  __device__ static float load(const elem_t* p) { return bf16_to_f32(*p); }
+  __device__ static elem_t store(float x) { return f32_to_bf16_rne(x); }
+};
+struct CacheF32 {
+  using elem_t = float;
+  __device__ static elem_t store(float x, float) { return x; }
+};
+struct CacheBF16 {
+  using elem_t = uint16_t;
+  __device__ static elem_t store(float x, float) { return f32_to_bf16_rne(x); }
+};
+struct CacheFP8 {
+  using elem_t = uint8_t;
+  __device__ static elem_t store(float x, float scale) { return f32_to_e4m3_rne_sat(__fdiv_rn(x, scale)); }
+};
+
+template <class A, class C>
+__global__ __launch_bounds__(kThreads) void rope_kv_append_kernel(AppendArgs p) {
+#pragma clang fp contract(off)
+  __shared__ float s_cos[kMaxHalf];
+  __shared__ float s_sin[kMaxHalf];
+
+  const int b = blockIdx.x;
+  const int D = p.dims.head_dim;
+  const int half = D / 2;
+  const int Hq = p.dims.num_q_heads;
+  const int Hkv = p.dims.num_kv_heads;
+  const int BS = p.dims.block_size;
+  const int MB = p.dims.max_blocks_per_seq;
+
+  int ctx = p.context_lens[b];
+  const int cap = MB * BS;
+  ctx = ctx > cap ? cap : ctx;
+  const bool active = ctx >= 1;
+  const int pos = active ? ctx - 1 : 0;
+
+  for (int i = threadIdx.x; i < half; i += kThreads) {
+    const double w = pow((double)p.rope_theta, (-2.0 * (double)i) / (double)D);
+    const double ang = (double)pos * w;
+    double sd, cd;
+    sincos(ang, &sd, &cd);
+    s_cos[i] = (float)cd;
+    s_sin[i] = (float)sd;
+  }
+  __syncthreads();
+
+  bool write = false;
+  int64_t slot_base = 0;  // element offset of (block, slot, head 0, 0)
+  if (active) {
+    const int pb = p.block_tables[(int64_t)b * MB + pos / BS];
+    write = (unsigned)pb < (unsigned)p.dims.num_blocks;
+    slot_base = ((int64_t)pb * BS + pos % BS) * (int64_t)Hkv * D;
+  }
+
+  const typename A::elem_t* x = static_cast<const typename A::elem_t*>(p.qkv) + (int64_t)b * p.qkv_row_stride;
+  typename A::elem_t* qo = static_cast<typename A::elem_t*>(p.q_out) + (int64_t)b * Hq * D;
+  typename C::elem_t* kc = static_cast<typename C::elem_t*>(p.k_cache);
+  typename C::elem_t* vc = static_cast<typename C::elem_t*>(p.v_cache);
+
+  // Rotate every Q head and every K head: (Hq + Hkv) * D/2 pairs.
+  const int nrot = (Hq + Hkv) * half;
+  for (int t = threadIdx.x; t < nrot; t += kThreads) {
+    const int hh = t / half;
+    const int i = t - hh * half;
+    const float c = s_cos[i];
+    const float s = s_sin[i];
+    const float x0 = A::load(x + hh * D + i);
+    const float x1 = A::load(x + hh * D + i + half);
+    const float a0 = x0 * c;
+    const float b0 = x1 * s;
+    const float y0 = a0 - b0;
+    const float a1 = x1 * c;
+    const float b1 = x0 * s;
+    const float y1 = a1 + b1;
+    if (hh < Hq) {
+      qo[hh * D + i] = A::store(y0);
+      qo[hh * D + i + half] = A::store(y1);
+    } else if (write) {
+      const int g = hh - Hq;
+      const float sc = p.k_scale ? p.k_scale[g] : 1.f;
+      kc[slot_base + g * D + i] = C::store(y0, sc);
+      kc[slot_base + g * D + i + half] = C::store(y1, sc);
+    }
+  }
+  // V heads are stored unrotated.
+  if (write) {
+    const typename A::elem_t* xv = x + (Hq + Hkv) * D;
+    for (int t = threadIdx.x; t < Hkv * D; t += kThreads) {
+      const int g = t / D;
+      const float sc = p.v_scale ? p.v_scale[g] : 1.f;
+      vc[slot_base + t] = C::store(A::load(xv + t), sc);
+    }
+  }
+}
+
+template <class A, class C>
+hipError_t launch(const AppendArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL((rope_kv_append_kernel<A, C>), dim3(a.dims.num_seqs), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_rope_kv_append(const AppendArgs& a, lgm_dtype act, lgm_dtype cache, hipStream_t s) {
+  if (act == LGM_F32 && cache == LGM_F32) return launch<ActF32, CacheF32>(a, s);
+  if (act == LGM_BF16 && cache == LGM_BF16) return launch<ActBF16, CacheBF16>(a, s);
+  if (act == LGM_BF16 && cache == LGM_FP8_E4M3) return launch<ActBF16, CacheFP8>(a, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace lgm

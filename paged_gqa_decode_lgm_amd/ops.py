@@ -1,0 +1,91 @@
+"""Torch-tensor front end of the C ABI: infers lgm_paged_dims from tensor
+shapes, maps torch dtypes to lgm_dtype and allocates outputs / workspace with
+torch (device memory is torch's job).  Every step of the decode path runs in
+liblgm.so; nothing here computes any of it.
+
+Shapes: qkv [B, (Hq+2Hkv)*D], q [B, Hq, D] (rows may be strided), caches
+[num_blocks, block_size, Hkv, D] (NHD), block_tables int32 [B, MB],
+context_lens int32 [B].
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional, Tuple
+
+import torch
+
+from . import _binding as B
+
+_DTYPES = {torch.float32: B.LGM_F32, torch.bfloat16: B.LGM_BF16, torch.float8_e4m3fn: B.LGM_FP8_E4M3}
+
+
+def lgm_dtype(t: torch.Tensor) -> int:
+    try:
+        return _DTYPES[t.dtype]
+    except KeyError:
+        raise TypeError(f"no lgm_dtype for {t.dtype}") from None
+
+
+def dims_for(num_seqs: int, num_q_heads: int, k_cache: torch.Tensor, block_tables: torch.Tensor) -> B.lgm_paged_dims:
+    nb, bs, hkv, d = k_cache.shape
+    return B.make_dims(num_seqs, num_q_heads, hkv, d, bs, nb, block_tables.shape[1])
+
+
+def rope_kv_append(qkv, k_cache, v_cache, block_tables, context_lens, rope_theta: float, num_q_heads: int,
+                   k_scale=None, v_scale=None, q_out=None, stream=None) -> torch.Tensor:
+    """Rotate Q/K of the new token, append K/V into the paged caches; returns q_out [B, Hq, D]."""
+    bsz = qkv.shape[0]
+    d = k_cache.shape[3]
+    if q_out is None:
+        q_out = torch.empty((bsz, num_q_heads, d), dtype=qkv.dtype, device=qkv.device)
+    dims = dims_for(bsz, num_q_heads, k_cache, block_tables)
+    B.lgm_rope_kv_append(qkv, qkv.stride(0), q_out, k_cache, v_cache, block_tables, context_lens, k_scale, v_scale,
+                         float(rope_theta), dims, lgm_dtype(qkv), lgm_dtype(k_cache), stream)
+    return q_out
+
+
+def workspace_bytes(q, k_cache, block_tables, max_context_len: int, partition_size: int = 0) -> int:
+    dims = dims_for(q.shape[0], q.shape[1], k_cache, block_tables)
+    return B.lgm_paged_decode_workspace_size(dims, max_context_len, partition_size, lgm_dtype(k_cache))
+
+
+def partition_size(q, k_cache, block_tables, max_context_len: int, partition_size: int = 0) -> int:
+    dims = dims_for(q.shape[0], q.shape[1], k_cache, block_tables)
+    return B.lgm_paged_decode_partition_size(dims, max_context_len, partition_size, lgm_dtype(k_cache))
+
+
+def paged_decode_attn(q, k_cache, v_cache, block_tables, context_lens, max_context_len: int,
+                      softmax_scale: Optional[float] = None, partition_size: int = 0, k_scale=None, v_scale=None,
+                      out=None, out_lse=None, workspace=None, want_lse: bool = True,
+                      stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Decode attention of q [B, Hq, D] over the paged caches; returns (out, lse)."""
+    bsz, hq, d = q.shape
+    if q.stride(2) != 1 or q.stride(1) != d:
+        raise ValueError("q must be [B, Hq, D] with heads dense (only the sequence stride may differ)")
+    dims = dims_for(bsz, hq, k_cache, block_tables)
+    if softmax_scale is None:
+        softmax_scale = float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32))
+    if out is None:
+        out = torch.empty((bsz, hq, d), dtype=q.dtype, device=q.device)
+    if out_lse is None and want_lse:
+        out_lse = torch.empty((bsz, hq), dtype=torch.float32, device=q.device)
+    need = B.lgm_paged_decode_workspace_size(dims, max_context_len, partition_size, lgm_dtype(k_cache))
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    B.lgm_paged_decode_attn(out, out_lse, q, q.stride(0), k_cache, v_cache, block_tables, context_lens, k_scale,
+                            v_scale, float(softmax_scale), partition_size, int(max_context_len), workspace, ws_bytes,
+                            dims, lgm_dtype(q), lgm_dtype(k_cache), stream)
+    return out, out_lse
+
+
+def lse_merge(partial_out, partial_lse, num_partitions=None, out_dtype=torch.float32, out=None, out_lse=None,
+              stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Merge records partial_out [B, H, P, D] / partial_lse [B, H, P]."""
+    bsz, h, p, d = partial_out.shape
+    if out is None:
+        out = torch.empty((bsz, h, d), dtype=out_dtype, device=partial_out.device)
+    if out_lse is None:
+        out_lse = torch.empty((bsz, h), dtype=torch.float32, device=partial_out.device)
+    B.lgm_lse_merge(out, out_lse, partial_out, partial_lse, num_partitions, bsz, h, d, p, lgm_dtype(out), stream)
+    return out, out_lse

@@ -1,0 +1,205 @@
+"""C-ABI contract on the CPU: the library loads, exports every function the
+header declares, and rejects every invalid argument with its own status and
+a message naming the function and the argument, before any HIP call (so
+these run without a GPU; fake but aligned addresses are never dereferenced)."""
+import ctypes
+import math
+
+import pytest
+
+import paged_gqa_decode_lgm_amd as L
+from paged_gqa_decode_lgm_amd import _binding as Bn
+
+INV, UNS, WS = L.LGM_ERR_INVALID_ARGUMENT, L.LGM_ERR_UNSUPPORTED, L.LGM_ERR_WORKSPACE_TOO_SMALL
+A = 1 << 32  # fake device addresses, far apart, 256-byte aligned
+
+
+def addr(i):
+    return A * (i + 1)
+
+
+def dims(**kw):
+    d = dict(num_seqs=64, num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16, num_blocks=1000,
+             max_blocks_per_seq=512)
+    d.update(kw)
+    return L.make_dims(**d)
+
+
+def test_library_loads_and_exports_every_header_function():
+    lib = L.lib()
+    names = L.header_functions()
+    assert set(names) == {"lgm_rope_kv_append", "lgm_paged_decode_partition_size", "lgm_paged_decode_workspace_size",
+                          "lgm_paged_decode_attn", "lgm_lse_merge", "lgm_last_error", "lgm_abi_version"}
+    for n in names:
+        assert hasattr(lib, n), n
+    assert L.lgm_abi_version() == 1
+
+
+# ------------------------------------------------------------------ append
+def _append(**over):
+    a = dict(qkv=addr(0), qkv_row_stride=(32 + 16) * 128, q_out=addr(1), k_cache=addr(2), v_cache=addr(3),
+             block_tables=addr(4), context_lens=addr(5), k_scale=None, v_scale=None, rope_theta=5e5, dims=dims(),
+             act_dtype=L.LGM_BF16, cache_dtype=L.LGM_BF16, stream=0)
+    a.update(over)
+    return L.lgm_rope_kv_append(**a)
+
+
+APPEND_BAD = [
+    (dict(dims=dims(num_seqs=-1)), INV, "num_seqs"),
+    (dict(dims=dims(num_q_heads=30)), INV, "num_q_heads"),
+    (dict(dims=dims(num_kv_heads=0)), INV, "num_kv_heads"),
+    (dict(dims=dims(head_dim=127)), INV, "head_dim"),
+    (dict(dims=dims(head_dim=512), qkv_row_stride=48 * 512), UNS, "head_dim"),
+    (dict(dims=dims(block_size=0)), INV, "block_size"),
+    (dict(dims=dims(num_blocks=0)), INV, "num_blocks"),
+    (dict(dims=dims(max_blocks_per_seq=0)), INV, "max_blocks_per_seq"),
+    (dict(act_dtype=L.LGM_F32), UNS, "act_dtype"),
+    (dict(act_dtype=7), INV, "act_dtype"),
+    (dict(cache_dtype=9), INV, "cache_dtype"),
+    (dict(rope_theta=0.0), INV, "rope_theta"),
+    (dict(rope_theta=float("nan")), INV, "rope_theta"),
+    (dict(qkv_row_stride=100), INV, "qkv_row_stride"),
+    (dict(cache_dtype=L.LGM_FP8_E4M3), INV, "k_scale"),
+    (dict(cache_dtype=L.LGM_FP8_E4M3, k_scale=addr(6)), INV, "v_scale"),
+    (dict(k_scale=addr(6), v_scale=addr(7)), INV, "k_scale"),
+    (dict(qkv=None), INV, "qkv"),
+    (dict(q_out=None), INV, "q_out"),
+    (dict(k_cache=None), INV, "k_cache"),
+    (dict(v_cache=None), INV, "v_cache"),
+    (dict(block_tables=None), INV, "block_tables"),
+    (dict(context_lens=None), INV, "context_lens"),
+    (dict(q_out=addr(0) + 256), INV, "q_out"),          # overlaps qkv
+    (dict(v_cache=addr(2) + 1024), INV, "k_cache"),     # pools overlap
+]
+
+
+@pytest.mark.parametrize("over,status,word", APPEND_BAD)
+def test_append_rejects(over, status, word):
+    with pytest.raises(L.LgmError) as e:
+        _append(**over)
+    assert e.value.status == status
+    assert e.value.message.startswith("lgm_rope_kv_append:")
+    assert word in e.value.message
+
+
+def test_append_empty_batch_is_a_noop():
+    _append(dims=dims(num_seqs=0), qkv=None, q_out=None)
+    assert L.lgm_last_error() == ""
+
+
+# ------------------------------------------------------------------ attention
+def _attn(**over):
+    a = dict(out=addr(0), out_lse=addr(1), q=addr(2), q_seq_stride=32 * 128, k_cache=addr(3), v_cache=addr(4),
+             block_tables=addr(5), context_lens=addr(6), k_scale=None, v_scale=None, softmax_scale=0.0883883,
+             partition_size=512, max_context_len=8192, workspace=addr(7), workspace_bytes=1 << 30, dims=dims(),
+             act_dtype=L.LGM_BF16, cache_dtype=L.LGM_BF16, stream=0)
+    a.update(over)
+    return L.lgm_paged_decode_attn(**a)
+
+
+ATTN_BAD = [
+    (dict(dims=dims(head_dim=96)), UNS, "head_dim"),
+    (dict(dims=dims(block_size=32, max_blocks_per_seq=256)), UNS, "block_size"),
+    (dict(dims=dims(num_q_heads=64, num_kv_heads=4)), UNS, "group"),
+    (dict(act_dtype=L.LGM_F32), UNS, "act"),
+    (dict(act_dtype=5), INV, "act_dtype"),
+    (dict(softmax_scale=float("inf")), INV, "softmax_scale"),
+    (dict(q_seq_stride=100), INV, "q_seq_stride"),
+    (dict(max_context_len=8193), INV, "max_context_len"),
+    (dict(max_context_len=-1), INV, "max_context_len"),
+    (dict(partition_size=24), INV, "partition_size"),
+    (dict(partition_size=-16), INV, "partition_size"),
+    (dict(workspace=None), WS, "workspace"),
+    (dict(workspace_bytes=1000), WS, "workspace_bytes"),
+    (dict(workspace=addr(7) + 8), INV, "workspace"),
+    (dict(cache_dtype=L.LGM_FP8_E4M3), INV, "k_scale"),
+    (dict(k_scale=addr(8), v_scale=addr(9)), INV, "k_scale"),
+    (dict(out=None), INV, "out"),
+    (dict(q=None), INV, "q"),
+    (dict(k_cache=None), INV, "k_cache"),
+    (dict(v_cache=None), INV, "v_cache"),
+    (dict(block_tables=None), INV, "block_tables"),
+    (dict(context_lens=None), INV, "context_lens"),
+    (dict(k_cache=addr(3) + 8), INV, "aligned"),
+    (dict(out=addr(2) + 512), INV, "'out' overlaps input 'q'"),
+    (dict(out_lse=addr(0) + 64), INV, "'out' overlaps output 'out_lse'"),
+    (dict(workspace=addr(3)), INV, "workspace"),
+]
+
+
+@pytest.mark.parametrize("over,status,word", ATTN_BAD)
+def test_attention_rejects(over, status, word):
+    with pytest.raises(L.LgmError) as e:
+        _attn(**over)
+    assert e.value.status == status
+    assert e.value.message.startswith("lgm_paged_decode_attn:")
+    assert word in e.value.message
+
+
+def test_attention_empty_batch_is_a_noop():
+    _attn(dims=dims(num_seqs=0), out=None, q=None)
+
+
+# ------------------------------------------------------------------ plan queries
+@pytest.mark.parametrize("d,max_ctx,ps,want", [
+    (dims(), 8192, 0, 512),                                               # Llama-3-8B-shaped, B64
+    (dims(num_seqs=128, max_blocks_per_seq=256), 4096, 0, 512),           # FP8 config, B128
+    (dims(num_seqs=2, num_q_heads=12, num_kv_heads=2, max_blocks_per_seq=128), 2048, 0, 64),
+    (dims(num_seqs=4, max_blocks_per_seq=8192), 131072, 512, 512),         # explicit
+    (dims(num_seqs=1, num_q_heads=4, num_kv_heads=1, head_dim=64, max_blocks_per_seq=16), 256, 256, 256),
+    (dims(), 8192, 16384, 8192),                                          # larger than the context: no split
+    (dims(), 100, 512, 112),                                              # clamped to the rounded-up context
+])
+def test_partition_plan(d, max_ctx, ps, want):
+    assert L.lgm_paged_decode_partition_size(d, max_ctx, ps, L.LGM_BF16) == want
+
+
+def test_workspace_size_formula():
+    d = dims()
+    assert L.lgm_paged_decode_workspace_size(d, 8192, 8192, L.LGM_BF16) == 0     # one partition
+    P = 16
+    out_b = 64 * 32 * P * 128 * 4
+    lse_b = 64 * 32 * P * 4
+    al = lambda x: (x + 255) // 256 * 256
+    assert L.lgm_paged_decode_workspace_size(d, 8192, 512, L.LGM_BF16) == al(out_b) + al(lse_b)
+    assert L.lgm_last_error() == ""
+    with pytest.raises(L.LgmError):
+        L.lgm_paged_decode_workspace_size(d, 8192, 10, L.LGM_BF16)
+
+
+# ------------------------------------------------------------------ merge
+def _merge(**over):
+    a = dict(out=addr(0), out_lse=addr(1), partial_out=addr(2), partial_lse=addr(3), num_partitions=None,
+             num_seqs=4, num_q_heads=32, head_dim=128, max_partitions=256, out_dtype=L.LGM_BF16, stream=0)
+    a.update(over)
+    return L.lgm_lse_merge(**a)
+
+
+MERGE_BAD = [
+    (dict(num_seqs=-2), INV, "num_seqs"),
+    (dict(num_q_heads=0), INV, "num_q_heads"),
+    (dict(max_partitions=0), INV, "max_partitions"),
+    (dict(out_dtype=L.LGM_FP8_E4M3), UNS, "out_dtype"),
+    (dict(head_dim=96), UNS, "head_dim"),
+    (dict(out=None), INV, "out"),
+    (dict(partial_out=None), INV, "partial_out"),
+    (dict(partial_lse=None), INV, "partial_lse"),
+    (dict(partial_out=addr(2) + 4), INV, "aligned"),
+    (dict(out=addr(2) + 64), INV, "overlaps"),
+]
+
+
+@pytest.mark.parametrize("over,status,word", MERGE_BAD)
+def test_merge_rejects(over, status, word):
+    with pytest.raises(L.LgmError) as e:
+        _merge(**over)
+    assert e.value.status == status
+    assert e.value.message.startswith("lgm_lse_merge:")
+    assert word in e.value.message
+
+
+def test_binding_refuses_to_run_without_the_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(Bn, "_lib", None)
+    monkeypatch.setattr(Bn, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        Bn.lib()

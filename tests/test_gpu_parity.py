@@ -1,0 +1,276 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle on the
+same seeded inputs.
+
+Tolerances (the bar):
+  attention outputs   max-abs <= 1e-5 (fp32 activations), <= 2e-2 (bf16 / FP8 paths)
+  appended entries    within 1 bf16 ulp of the exact rotation (ord distance),
+                      fp32 caches within the fp32 rounding bound of the rotation
+  FP8 cache bytes     bit-exact against the oracle's fp32 recipe
+  index handling      bit-exact: every other pool byte unchanged, block-shuffle
+                      and poisoned-slot runs bitwise identical
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from gpu_util import (TOL, act_raw, act_raw_tensor, announce, bf16_ord, gpu_append, gpu_attention, host_bits,
+                      max_abs, oracle_append, oracle_attention, out_values, pool_raw, q_from_qkv, to_device)
+from oracle import attention as OA
+from oracle import codecs
+from paged_gqa_decode_lgm_amd import ops
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs an MI355X")]
+
+# Sizes the oracle finishes in seconds that still span several partitions and a ragged tail.
+PARITY = {
+    "tiny_mqa_f32": {},
+    "qwen2.5_1.5b_gqa": {},
+    "llama3_8b_gqa": dict(num_seqs=8, ctx=(17, 2000)),
+    "long_ctx_splitk": dict(num_seqs=2, ctx=8192),
+    "fp8_kv": dict(num_seqs=8),
+}
+
+
+def _lse_check(g_lse, r_lse, rows=None):
+    g = np.asarray(g_lse, np.float64)
+    r = np.asarray(r_lse, np.float64)
+    if rows is not None:
+        g, r = g[rows], r[rows]
+    assert np.array_equal(np.isneginf(g), np.isneginf(r))
+    fin = np.isfinite(r)
+    if fin.any():
+        assert np.abs(g[fin] - r[fin]).max() <= 1e-4 * max(1.0, np.abs(r[fin]).max())
+
+
+def _check_append(w, d, q_gpu, rec, ex, seqs=None):
+    """q_out and the appended cache slots against the oracle; all other pool bytes unchanged."""
+    c = w.cfg
+    seqs = range(c.num_seqs) if seqs is None else seqs
+    gq = act_raw_tensor(c, q_gpu)
+    gk = pool_raw(w, d.k_pool.cpu())
+    gv = pool_raw(w, d.v_pool.cpu())
+    k0, v0 = pool_raw(w, w.k_pool), pool_raw(w, w.v_pool)
+    slots = {s for s in rec.slots if s is not None}
+    # index exactness: only the target slots moved
+    mask = np.ones(gk.shape[:2], bool)
+    for (pb, off) in slots:
+        mask[pb, off] = False
+    assert np.array_equal(gk[mask], k0[mask]) and np.array_equal(gv[mask], v0[mask])
+    for b in seqs:
+        if c.act == "bf16":
+            assert np.abs(bf16_ord(gq[b]) - bf16_ord(ex.q_out[b])).max() <= 1
+        else:
+            x = w.qkv.numpy()[b, : c.num_q_heads * c.head_dim].astype(np.float64).reshape(c.num_q_heads, -1)
+            h = c.head_dim // 2
+            bound = 4 * 2.0 ** -24 * np.concatenate([np.abs(x[:, :h]) + np.abs(x[:, h:])] * 2, -1)
+            assert (np.abs(gq[b].astype(np.float64) - ex.q_rot[b]) <= bound).all()
+        if rec.slots[b] is None:
+            continue
+        pb, off = rec.slots[b]
+        if c.cache == "fp8":
+            assert np.array_equal(gk[pb, off], rec.k_pool[pb, off]), f"K bytes, seq {b}"
+            assert np.array_equal(gv[pb, off], rec.v_pool[pb, off]), f"V bytes, seq {b}"
+        elif c.cache == "bf16":
+            assert np.abs(bf16_ord(gk[pb, off]) - bf16_ord(ex.k_pool[pb, off])).max() <= 1
+            assert np.abs(bf16_ord(gv[pb, off]) - bf16_ord(ex.v_pool[pb, off])).max() <= 1
+        else:
+            assert np.abs(gk[pb, off] - ex.k_pool[pb, off]).max() <= 4 * 2.0 ** -24 * 8
+            assert np.array_equal(gv[pb, off], ex.v_pool[pb, off])
+
+
+def _run_and_check(cfg, sample=None, partition_size=None):
+    w = W.make_workload(cfg)
+    announce(cfg.name, f"B={cfg.num_seqs}", f"Hq/Hkv={cfg.num_q_heads}/{cfg.num_kv_heads}", f"D={cfg.head_dim}",
+             f"cache={cfg.cache}", f"max_ctx={int(w.context_lens.max())}", f"ps={cfg.partition_size}")
+    d = to_device(w)
+    if cfg.append:
+        q = gpu_append(d)
+    else:
+        q = q_from_qkv(w).cuda()
+    out, lse = gpu_attention(d, q, partition_size)
+    torch.cuda.synchronize()
+    if cfg.append:
+        rec = oracle_append(w, "recipe")
+        ex = oracle_append(w, "exact")
+        _check_append(w, d, q, rec, ex, sample)
+        q_ref, kp, vp = rec.q_out, rec.k_pool, rec.v_pool
+    else:
+        q_ref, kp, vp = act_raw(w, q_from_qkv(w)), pool_raw(w, w.k_pool), pool_raw(w, w.v_pool)
+    r_out, r_lse = oracle_attention(w, q_ref, kp, vp, seqs=sample)
+    rows = slice(None) if sample is None else list(sample)
+    err = max_abs(out_values(cfg, out), r_out, rows)
+    announce(cfg.name, "max-abs", err)
+    assert err <= TOL[cfg.act], err
+    _lse_check(lse.cpu().numpy(), r_lse, rows)
+    return w, d, out, lse
+
+
+@pytest.mark.parametrize("name", list(PARITY))
+def test_config_parity(name):
+    base = W.CONFIGS[name]
+    over = dict(PARITY[name])
+    if over and base.num_blocks is None:
+        over["num_blocks"] = None
+    _run_and_check(base.with_(**over))
+
+
+@pytest.mark.parametrize("name", ["llama3_8b_gqa", "long_ctx_splitk", "fp8_kv"])
+def test_full_size_sampled(name):
+    """Full-size workload in the launch configuration the benchmark times;
+    the oracle checks a sample of sequences (first, shortest, longest, last)."""
+    cfg = W.CONFIGS[name]
+    ctx = W.draw_context_lens(cfg)
+    sample = sorted({0, int(np.argmin(ctx)), int(np.argmax(ctx)), cfg.num_seqs - 1})
+    if name == "long_ctx_splitk":
+        sample = [0, cfg.num_seqs - 1]
+    _run_and_check(cfg, sample=sample)
+
+
+EDGE_CTX = (0, 1, 15, 16, 17, 63, 64, 65, 200, 513)
+
+
+@pytest.mark.parametrize("act,cache,D,G", [
+    ("bf16", "bf16", 128, 4), ("bf16", "bf16", 128, 6), ("bf16", "bf16", 128, 1), ("bf16", "bf16", 64, 8),
+    ("bf16", "fp8", 128, 4), ("bf16", "fp8", 64, 3), ("f32", "f32", 64, 4), ("f32", "f32", 128, 2),
+    ("bf16", "bf16", 128, 8), ("bf16", "fp8", 128, 5),
+])
+@pytest.mark.parametrize("ps", [16, 64, 0, 4096])
+def test_shapes_and_ragged_edges(act, cache, D, G, ps):
+    cfg = W.Config(f"edge_{act}_{cache}_D{D}_G{G}", seed=11, num_seqs=len(EDGE_CTX), num_q_heads=2 * G,
+                   num_kv_heads=2, head_dim=D, block_size=16, act=act, cache=cache, ctx=0, rope_theta=1e4,
+                   partition_size=ps, append=True, ctx_list=EDGE_CTX)
+    _run_and_check(cfg)
+
+
+def _bench_like(name="llama3_8b_gqa", **kw):
+    base = W.CONFIGS[name]
+    return base.with_(**{"num_blocks": None, **kw})
+
+
+def test_block_shuffle_is_bitwise_identical():
+    cfg = _bench_like(num_seqs=6, ctx=(100, 3000), append=False)
+    w = W.make_workload(cfg)
+    w2 = W.shuffled_copy(w, 7)
+    q = q_from_qkv(w).cuda()
+    announce("shuffle", cfg.name)
+    o1, l1 = gpu_attention(to_device(w), q)
+    o2, l2 = gpu_attention(to_device(w2), q)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+
+
+def test_poisoned_unused_slots_and_table_entries_are_bitwise_identical():
+    cfg = _bench_like(num_seqs=6, ctx=(100, 3000), append=False)
+    w = W.make_workload(cfg)
+    q = q_from_qkv(w).cuda()
+    bt = w.block_tables.clone()
+    kp, vp = w.k_pool.clone(), w.v_pool.clone()
+    used = set()
+    for b in range(cfg.num_seqs):
+        L = int(w.context_lens[b])
+        nb = -(-L // 16)
+        used |= set(bt[b, :nb].tolist())
+        bt[b, nb:] = torch.tensor([-5, 1 << 30] * bt.shape[1], dtype=torch.int32)[: bt.shape[1] - nb]
+        last = int(bt[b, nb - 1])
+        kp[last, L - (nb - 1) * 16:] = float("nan")
+        vp[last, L - (nb - 1) * 16:] = float("nan")
+    unused = [i for i in range(kp.shape[0]) if i not in used]
+    kp[unused] = float("nan")
+    vp[unused] = float("inf")
+    w2 = dataclasses.replace(w, block_tables=bt, k_pool=kp, v_pool=vp)
+    announce("poison", cfg.name)
+    o1, l1 = gpu_attention(to_device(w), q)
+    o2, l2 = gpu_attention(to_device(w2), q)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+
+
+def test_repeated_calls_are_bitwise_identical():
+    cfg = _bench_like(num_seqs=16, ctx=(512, 8192), append=False)
+    w = W.make_workload(cfg)
+    d = to_device(w)
+    q = q_from_qkv(w).cuda()
+    announce("determinism x20", cfg.name)
+    o0, l0 = gpu_attention(d, q)
+    for _ in range(19):
+        o, l = gpu_attention(d, q)
+        assert torch.equal(o.view(torch.int16), o0.view(torch.int16)) and torch.equal(l, l0)
+
+
+def test_out_lse_optional_and_strided_q():
+    cfg = _bench_like(num_seqs=3, ctx=(40, 700), append=False)
+    w = W.make_workload(cfg)
+    d = to_device(w)
+    qd = q_from_qkv(w).cuda()
+    padded = torch.zeros((3, 33, 128), dtype=qd.dtype, device="cuda")
+    padded[:, :32] = qd
+    qs = padded[:, :32]  # sequence stride 33*128
+    announce("strided q / no lse", cfg.name)
+    o1, _ = ops.paged_decode_attn(qs, d.k_pool, d.v_pool, d.block_tables, d.context_lens, d.max_ctx,
+                                  softmax_scale=cfg.softmax_scale, want_lse=False)
+    o2, _ = gpu_attention(d, qd)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+
+
+def test_fp8_every_code_decodes_exactly():
+    """V rows hold every finite E4M3 code; equal keys make the output the mean of
+    the decoded V rows, which the oracle computes from the codes' definition."""
+    cfg = W.CONFIGS["fp8_kv"].with_(num_seqs=2, ctx_list=(254, 254), num_blocks=None, append=False)
+    w = W.make_workload(cfg)
+    codes = np.array([c for c in range(256) if c & 0x7F != 0x7F], np.uint8)
+    vb = w.v_pool.view(torch.uint8).clone()
+    kb = torch.full_like(w.k_pool.view(torch.uint8), 0x38)
+    for b in range(2):
+        for j in range(254):
+            pb = int(w.block_tables[b, j // 16])
+            vb[pb, j % 16] = torch.from_numpy(np.roll(codes, j + 3 * b)[:128].copy())
+    w2 = dataclasses.replace(w, k_pool=kb.view(torch.float8_e4m3fn), v_pool=vb.view(torch.float8_e4m3fn))
+    q = q_from_qkv(w2).cuda()
+    announce("fp8 all codes")
+    out, lse = gpu_attention(to_device(w2), q)
+    torch.cuda.synchronize()
+    r_out, r_lse = oracle_attention(w2, act_raw(w2, q_from_qkv(w2)), pool_raw(w2, w2.k_pool), pool_raw(w2, w2.v_pool))
+    assert max_abs(out_values(cfg, out), r_out) <= TOL["bf16"]
+    _lse_check(lse.cpu().numpy(), r_lse)
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_lse_merge_standalone(out_dtype):
+    rng = np.random.default_rng(5)
+    B, H, P, D = 5, 6, 37, 128
+    po = rng.standard_normal((B, H, P, D)).astype(np.float32)
+    pl = (rng.standard_normal((B, H, P)) * 6).astype(np.float32)
+    pl[1, :, 3] = -np.inf
+    pl[2] = -np.inf                     # a sequence whose records are all empty
+    n = np.array([37, 5, 37, 0, 1], np.int32)
+    announce("lse_merge", out_dtype)
+    out, lse = ops.lse_merge(torch.from_numpy(po).cuda(), torch.from_numpy(pl).cuda(),
+                             torch.from_numpy(n).cuda(), out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    r_out, r_lse = OA.lse_merge(po, pl, n)
+    g = out.float().cpu().numpy().astype(np.float64)
+    tol = 1e-5 if out_dtype == torch.float32 else 2e-2
+    assert np.abs(g - r_out).max() <= tol
+    _lse_check(lse.cpu().numpy(), r_lse)
+    # without counts: every record is used
+    out2, _ = ops.lse_merge(torch.from_numpy(po[:2]).cuda(), torch.from_numpy(pl[:2]).cuda(), None, out_dtype=out_dtype)
+    r2, _ = OA.lse_merge(po[:2], pl[:2])
+    assert np.abs(out2.float().cpu().numpy() - r2).max() <= tol
+
+
+def test_inactive_sequence_append_writes_nothing():
+    cfg = W.CONFIGS["qwen2.5_1.5b_gqa"].with_(num_seqs=3, ctx_list=(0, 5, 2048))
+    w = W.make_workload(cfg)
+    d = to_device(w)
+    announce("inactive append")
+    q = gpu_append(d)
+    torch.cuda.synchronize()
+    rec = oracle_append(w, "recipe")
+    ex = oracle_append(w, "exact")
+    _check_append(w, d, q, rec, ex)
+    assert np.array_equal(act_raw_tensor(cfg, q)[0], W.storage_bits(w.qkv)[0, : 12 * 128].reshape(12, 128))

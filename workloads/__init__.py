@@ -60,6 +60,7 @@ class Config:
     outlier_frac: float = 0.0
     outlier_scale: float = 1.0
     calib_tokens: int = 4096
+    ctx_list: Optional[Tuple[int, ...]] = None  # explicit per-sequence lengths (overrides ctx)
     description: str = ""
 
     @property
@@ -68,6 +69,8 @@ class Config:
 
     @property
     def max_ctx(self) -> int:
+        if self.ctx_list is not None:
+            return max(self.ctx_list) if self.ctx_list else 0
         return self.ctx if isinstance(self.ctx, int) else self.ctx[1]
 
     @property
@@ -164,6 +167,10 @@ def _normal_f32(seed: int, stage: int, count: int, threads: int = 0) -> np.ndarr
 
 
 def draw_context_lens(cfg: Config) -> np.ndarray:
+    if cfg.ctx_list is not None:
+        if len(cfg.ctx_list) != cfg.num_seqs:
+            raise ValueError("ctx_list needs one length per sequence")
+        return np.asarray(cfg.ctx_list, dtype=np.int32)
     if isinstance(cfg.ctx, int):
         return np.full(cfg.num_seqs, cfg.ctx, dtype=np.int32)
     rng = np.random.default_rng(_children(cfg.seed, STAGE_CTX, 1)[0])
@@ -176,12 +183,12 @@ def draw_block_tables(cfg: Config, ctx: np.ndarray) -> Tuple[np.ndarray, int]:
     bs = cfg.block_size
     nblk = [-(-int(c) // bs) for c in ctx]
     used = sum(nblk)
-    nb = cfg.num_blocks if cfg.num_blocks is not None else -(-used * 5 // 4)
+    nb = cfg.num_blocks if cfg.num_blocks is not None else max(1, -(-used * 5 // 4))
     if used > nb:
         raise ValueError(f"{cfg.name}: pool of {nb} blocks cannot hold {used}")
     rng = np.random.default_rng(_children(cfg.seed, STAGE_TABLE, 1)[0])
     perm = rng.permutation(nb).astype(np.int32)
-    mb = max(cfg.max_blocks_per_seq, max(nblk) if nblk else 1)
+    mb = max(cfg.max_blocks_per_seq, max(nblk) if nblk else 1, 1)
     bt = np.full((cfg.num_seqs, mb), -1, dtype=np.int32)
     pos = 0
     for b, n in enumerate(nblk):
