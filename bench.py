@@ -119,7 +119,7 @@ def main() -> int:
     out = torch.empty((B, Hq, D), dtype=qkv.dtype, device=dev)
     lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
     ws_bytes = ops.workspace_bytes(q, k_pool, bt, max_ctx, cfg.partition_size)
-    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device=dev)  # zero-filled once, kept zero by the library
     ps = ops.partition_size(q, k_pool, bt, max_ctx, cfg.partition_size)
     stream = torch.cuda.current_stream()
 
@@ -177,7 +177,8 @@ def main() -> int:
         "kernel_ms": {"attention_avg": round(attn_avg_s * 1e3, 5),
                       "attention_median": round(statistics.median(attn_ms), 5),
                       "append_avg": round(statistics.mean(append_ms), 5) if append_ms else None},
-        "roofline": {"bound": "hbm", "kernel": "lgm_paged_decode_attn (split-K decode + LSE merge launches)",
+        "roofline": {"bound": "hbm", "kernel": "lgm_paged_decode_attn (" + ("balanced decode, one launch" if ps == 0
+                     else "split-K decode + LSE merge launches") + ")",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
     }

@@ -135,21 +135,28 @@ lgm_status lgm_rope_kv_append(const void* qkv, int64_t qkv_row_stride, void* q_o
                               lgm_dtype act_dtype, lgm_dtype cache_dtype, void* stream);
 
 /*
- * Partition size the attention call will use.  partition_size 0 lets the
- * library choose from the shapes alone (deterministic, no device query);
- * a positive value must be a multiple of block_size and is returned as is.
- * Returns -1 (and sets lgm_last_error) on invalid arguments.
+ * How the attention call will split the contexts.  A positive
+ * partition_size must be a multiple of block_size and is returned as is
+ * (clamped to the rounded-up max_context_len): fixed partitions of that many
+ * tokens.  partition_size 0 lets the library choose from the shapes alone
+ * (deterministic, no device query): it returns 0 when it uses balanced
+ * ranges (bf16 activations with bf16 / FP8 caches at head_dim 128: the
+ * 32-token tiles of all (sequence, kv head) pairs are cut into as many equal
+ * ranges as the GPU keeps waves resident, so each wave reads the same number
+ * of bytes whatever the mix of context lengths), otherwise the partition size
+ * it picked.  Returns -1 (and sets lgm_last_error) on invalid arguments.
  */
 int32_t lgm_paged_decode_partition_size(lgm_paged_dims dims, int32_t max_context_len,
                                         int32_t partition_size, lgm_dtype cache_dtype);
 
 /*
  * Bytes of device workspace lgm_paged_decode_attn needs for these
- * arguments: 0 when every sequence fits one partition, otherwise room for
- * the split-K records (fp32 partial outputs [B][Hq][P][D] and natural-log
- * LSEs [B][Hq][P], P = ceil(max_context_len / partition)) plus alignment.
- * Returns 0 and sets lgm_last_error on invalid arguments (check it when 0 is
- * unexpected).
+ * arguments.  Fixed partitions: 0 when every sequence fits one partition,
+ * otherwise room for the split-K records (fp32 partial outputs [B][Hq][P][D]
+ * and natural-log LSEs [B][Hq][P], P = ceil(max_context_len / partition)).
+ * Balanced ranges: two records per range plus one int32 arrival counter per
+ * (sequence, kv head).  Returns 0 and sets lgm_last_error on invalid
+ * arguments (check it when 0 is unexpected).
  */
 size_t lgm_paged_decode_workspace_size(lgm_paged_dims dims, int32_t max_context_len,
                                        int32_t partition_size, lgm_dtype cache_dtype);
@@ -179,11 +186,15 @@ size_t lgm_paged_decode_workspace_size(lgm_paged_dims dims, int32_t max_context_
  *                  block_size; >= max_context_len means no split
  *   max_context_len upper bound on context_lens, 0..max_blocks_per_seq*block_size
  *   workspace      device buffer of at least lgm_paged_decode_workspace_size()
- *                  bytes, 256-byte aligned (NULL allowed when that size is 0);
- *                  its contents are scratch
+ *                  bytes, 256-byte aligned (NULL allowed when that size is 0).
+ *                  It must be zero-filled before its first use and again
+ *                  after a call on it failed to complete or the shapes
+ *                  changed; every completed call leaves it as it needs it.
+ *                  Calls sharing a workspace must not overlap in time.
  * Supported: (act, cache) in {(F32, F32), (BF16, BF16), (BF16, FP8_E4M3)},
- * head_dim in {64, 128}, block_size 16, G = Hq/Hkv in 1..16.
- * out must not overlap q, the caches or the workspace.
+ * head_dim in {64, 128}, block_size 16, G = Hq/Hkv in 1..8; with bf16
+ * activations at head_dim 128, G in 1..16 (matrix-core kernel).
+ * out (16-byte aligned) must not overlap q, the caches or the workspace.
  */
 lgm_status lgm_paged_decode_attn(void* out, float* out_lse, const void* q, int64_t q_seq_stride,
                                  const void* k_cache, const void* v_cache,
@@ -207,7 +218,7 @@ lgm_status lgm_paged_decode_attn(void* out, float* out_lse, const void* q, int64
  *   partial_out    fp32 [B][H][max_partitions][D], normalised partial outputs
  *   partial_lse    fp32 [B][H][max_partitions], natural log
  *   num_partitions optional int32 [B]
- * Supported: head_dim a multiple of 4, 4..512.
+ * Supported: head_dim 64 or 128.
  */
 lgm_status lgm_lse_merge(void* out, float* out_lse, const float* partial_out,
                          const float* partial_lse, const int32_t* num_partitions,

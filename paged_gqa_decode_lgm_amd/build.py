@@ -31,6 +31,8 @@ UNITS = {
     "lgm_api.cpp": ["-x", "hip"],
     "rope_kv_append.hip": ["-ffp-contract=off"],
     "paged_decode.hip": [],
+    "paged_decode_mfma.hip": [],
+    "paged_decode_stream.hip": [],
     "lse_merge.hip": [],
 }
 

@@ -122,7 +122,8 @@ int32_t resolve_partition(const char* fn, const lgm_paged_dims& d, int32_t max_c
     const int64_t units = (int64_t)(d.num_seqs > 0 ? d.num_seqs : 1) * d.num_kv_heads;
     const int64_t parts = (kAutoTargetWorkgroups + units - 1) / units;
     int64_t p = (cap + parts - 1) / parts;
-    p = (p + d.block_size - 1) / d.block_size * d.block_size;
+    const int64_t step = 2 * (int64_t)d.block_size;  // whole 32-token tiles of the decode kernels
+    p = (p + step - 1) / step * step;
     const int64_t minp = (int64_t)kMinAutoPartitionBlocks * d.block_size;
     ps = (int32_t)(p < minp ? minp : p);
   }
@@ -131,17 +132,56 @@ int32_t resolve_partition(const char* fn, const lgm_paged_dims& d, int32_t max_c
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-struct Workspace {
-  size_t part_out_bytes, part_lse_bytes, total;
+// Balanced plan: one range per resident wave of the balanced kernel on
+// MI355X's 256 compute units (4 SIMDs each), so every range runs
+// concurrently and they all finish together.
+constexpr int kComputeUnits = 256;
+constexpr int kStreamTileTokens = 32;
+int stream_max_waves(lgm_dtype cache, int group) {
+  return kComputeUnits * 4 * lgm::stream_waves_per_simd(cache == LGM_FP8_E4M3, group);
+}
+
+// Launch plan of one attention call, a function of host-visible arguments only.
+//   balanced: partition_size 0 on a matrix-core shape: W equal tile ranges,
+//             workspace = [W][2] records then [B][Hkv] arrival counters;
+//   fixed:    partitions of `ps` tokens, workspace = partial outputs and LSEs
+//             (none when every sequence fits one partition).
+struct Plan {
+  bool balanced;
+  int32_t ps, P;       // fixed partitions
+  int32_t W, rec_floats;
+  size_t part_out_bytes, part_lse_bytes;
+  size_t records_bytes, counters_bytes;
+  size_t total;
 };
 
-Workspace workspace_layout(const lgm_paged_dims& d, int32_t P) {
-  Workspace w{0, 0, 0};
-  if (P <= 1) return w;
-  w.part_out_bytes = align256((size_t)d.num_seqs * d.num_q_heads * P * d.head_dim * sizeof(float));
-  w.part_lse_bytes = align256((size_t)d.num_seqs * d.num_q_heads * P * sizeof(float));
-  w.total = w.part_out_bytes + w.part_lse_bytes;
-  return w;
+bool plan_decode(const char* fn, const lgm_paged_dims& d, int32_t max_ctx, int32_t ps_arg, lgm_dtype cache, Plan& pl) {
+  pl = Plan{};
+  const int G = d.num_q_heads / d.num_kv_heads;
+  const lgm_dtype act = cache == LGM_F32 ? LGM_F32 : LGM_BF16;  // the only supported pairings
+  if (ps_arg == 0 && lgm::decode_mfma_supported(act, cache, d.head_dim, G, d.block_size)) {
+    pl.balanced = true;
+    const int64_t tiles = (int64_t)(max_ctx + kStreamTileTokens - 1) / kStreamTileTokens;
+    const int64_t n_upper = (int64_t)d.num_seqs * d.num_kv_heads * tiles;
+    int64_t W = (n_upper + 1) / 2;
+    const int64_t wmax = stream_max_waves(cache, G);
+    W = W < 1 ? 1 : (W > wmax ? wmax : W);
+    pl.W = (int32_t)W;
+    pl.rec_floats = lgm::stream_record_floats(G);
+    pl.records_bytes = align256((size_t)W * 2 * pl.rec_floats * sizeof(float));
+    pl.counters_bytes = align256((size_t)d.num_seqs * d.num_kv_heads * sizeof(int32_t));
+    pl.total = pl.records_bytes + pl.counters_bytes;
+    return true;
+  }
+  pl.ps = resolve_partition(fn, d, max_ctx, ps_arg);
+  if (pl.ps < 0) return false;
+  pl.P = max_ctx <= 0 ? 1 : (max_ctx + pl.ps - 1) / pl.ps;
+  if (pl.P > 1) {
+    pl.part_out_bytes = align256((size_t)d.num_seqs * d.num_q_heads * pl.P * d.head_dim * sizeof(float));
+    pl.part_lse_bytes = align256((size_t)d.num_seqs * d.num_q_heads * pl.P * sizeof(float));
+    pl.total = pl.part_out_bytes + pl.part_lse_bytes;
+  }
+  return true;
 }
 
 lgm_status check_decode_common(const char* fn, const lgm_paged_dims& d, int32_t max_ctx, lgm_dtype cache) {
@@ -221,7 +261,9 @@ int32_t lgm_paged_decode_partition_size(lgm_paged_dims dims, int32_t max_context
   const char* fn = "lgm_paged_decode_partition_size";
   g_err.clear();
   if (check_decode_common(fn, dims, max_context_len, cache_dtype) != LGM_OK) return -1;
-  return resolve_partition(fn, dims, max_context_len, partition_size);
+  Plan pl;
+  if (!plan_decode(fn, dims, max_context_len, partition_size, cache_dtype, pl)) return -1;
+  return pl.balanced ? 0 : pl.ps;
 }
 
 size_t lgm_paged_decode_workspace_size(lgm_paged_dims dims, int32_t max_context_len, int32_t partition_size,
@@ -229,10 +271,9 @@ size_t lgm_paged_decode_workspace_size(lgm_paged_dims dims, int32_t max_context_
   const char* fn = "lgm_paged_decode_workspace_size";
   g_err.clear();
   if (check_decode_common(fn, dims, max_context_len, cache_dtype) != LGM_OK) return 0;
-  const int32_t ps = resolve_partition(fn, dims, max_context_len, partition_size);
-  if (ps < 0) return 0;
-  const int32_t P = max_context_len <= 0 ? 1 : (max_context_len + ps - 1) / ps;
-  return workspace_layout(dims, P).total;
+  Plan pl;
+  if (!plan_decode(fn, dims, max_context_len, partition_size, cache_dtype, pl)) return 0;
+  return pl.total;
 }
 
 lgm_status lgm_paged_decode_attn(void* out, float* out_lse, const void* q, int64_t q_seq_stride, const void* k_cache,
@@ -250,7 +291,8 @@ lgm_status lgm_paged_decode_attn(void* out, float* out_lse, const void* q, int64
   if (!lgm::decode_supported(act_dtype, cache_dtype, dims.head_dim, G, dims.block_size))
     return fail(LGM_ERR_UNSUPPORTED, fn,
                 "(act %s, cache %s, head_dim %d, group %d, block_size %d) unsupported: supported are (F32, F32), "
-                "(BF16, BF16), (BF16, FP8_E4M3) with head_dim 64 or 128, group 1..8, block_size 16",
+                "(BF16, BF16), (BF16, FP8_E4M3) with head_dim 64 or 128, block_size 16, group 1..8 "
+                "(1..16 for bf16 activations at head_dim 128)",
                 dtype_name(act_dtype), dtype_name(cache_dtype), dims.head_dim, G, dims.block_size);
   if (dims.num_seqs > 65535 || dims.num_kv_heads > 65535)
     return fail(LGM_ERR_UNSUPPORTED, fn, "dims.num_seqs = %d / dims.num_kv_heads = %d: at most 65535 each",
@@ -262,17 +304,16 @@ lgm_status lgm_paged_decode_attn(void* out, float* out_lse, const void* q, int64
     return fail(LGM_ERR_INVALID_ARGUMENT, fn, "q_seq_stride = %lld must be >= num_q_heads * head_dim = %lld",
                 (long long)q_seq_stride, (long long)qrow);
   if ((st = check_scales(fn, cache_dtype, k_scale, v_scale)) != LGM_OK) return st;
-  const int32_t ps = resolve_partition(fn, dims, max_context_len, partition_size);
-  if (ps < 0) return LGM_ERR_INVALID_ARGUMENT;
-  const int32_t P = max_context_len <= 0 ? 1 : (max_context_len + ps - 1) / ps;
-  const Workspace ws = workspace_layout(dims, P);
+  Plan pl;
+  if (!plan_decode(fn, dims, max_context_len, partition_size, cache_dtype, pl)) return LGM_ERR_INVALID_ARGUMENT;
+  struct {
+    size_t total;
+  } ws{pl.total};
   if (ws.total > 0) {
     if (!workspace)
-      return fail(LGM_ERR_WORKSPACE_TOO_SMALL, fn, "workspace is NULL but %zu bytes are needed (partition %d, %d partitions)",
-                  ws.total, ps, P);
+      return fail(LGM_ERR_WORKSPACE_TOO_SMALL, fn, "workspace is NULL but %zu bytes are needed", ws.total);
     if (workspace_bytes < ws.total)
-      return fail(LGM_ERR_WORKSPACE_TOO_SMALL, fn, "workspace_bytes = %zu < %zu needed (partition %d, %d partitions)",
-                  workspace_bytes, ws.total, ps, P);
+      return fail(LGM_ERR_WORKSPACE_TOO_SMALL, fn, "workspace_bytes = %zu < %zu needed", workspace_bytes, ws.total);
     if ((uintptr_t)workspace % 256 != 0)
       return fail(LGM_ERR_INVALID_ARGUMENT, fn, "workspace %p must be 256-byte aligned", workspace);
   }
@@ -285,6 +326,7 @@ lgm_status lgm_paged_decode_attn(void* out, float* out_lse, const void* q, int64
   if (!context_lens) return fail(LGM_ERR_INVALID_ARGUMENT, fn, "context_lens is NULL");
   if ((uintptr_t)k_cache % 16 != 0 || (uintptr_t)v_cache % 16 != 0)
     return fail(LGM_ERR_INVALID_ARGUMENT, fn, "k_cache (%p) and v_cache (%p) must be 16-byte aligned", k_cache, v_cache);
+  if ((uintptr_t)out % 16 != 0) return fail(LGM_ERR_INVALID_ARGUMENT, fn, "out (%p) must be 16-byte aligned", out);
 
   const int64_t ea = elem_bytes(act_dtype);
   const int64_t B = dims.num_seqs;
@@ -300,15 +342,25 @@ lgm_status lgm_paged_decode_attn(void* out, float* out_lse, const void* q, int64
                       {"v_scale", (uintptr_t)v_scale, v_scale ? (int64_t)dims.num_kv_heads * 4 : 0}};
   if ((st = check_no_alias(fn, outs, 3, ins, 7)) != LGM_OK) return st;
 
-  float* part_out = ws.total ? static_cast<float*>(workspace) : nullptr;
-  float* part_lse = ws.total ? reinterpret_cast<float*>(static_cast<char*>(workspace) + ws.part_out_bytes) : nullptr;
+  char* wsb = static_cast<char*>(workspace);
+  if (pl.balanced) {
+    lgm::DecodeArgs a{out, out_lse, q, q_seq_stride, k_cache, v_cache, block_tables, context_lens, k_scale, v_scale,
+                      nullptr, nullptr, softmax_scale, 0, max_context_len, 0, dims};
+    lgm::StreamArgs x{pl.W, pl.rec_floats, reinterpret_cast<float*>(wsb),
+                      reinterpret_cast<int32_t*>(wsb + pl.records_bytes)};
+    const hipError_t e = lgm::launch_paged_decode_stream(a, x, cache_dtype, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(LGM_ERR_HIP, fn, "decode kernel launch failed: %s", hipGetErrorString(e));
+    return LGM_OK;
+  }
+  float* part_out = pl.total ? reinterpret_cast<float*>(wsb) : nullptr;
+  float* part_lse = pl.total ? reinterpret_cast<float*>(wsb + pl.part_out_bytes) : nullptr;
   lgm::DecodeArgs a{out, out_lse, q, q_seq_stride, k_cache, v_cache, block_tables, context_lens, k_scale, v_scale,
-                    part_out, part_lse, softmax_scale, ps, max_context_len, P, dims};
+                    part_out, part_lse, softmax_scale, pl.ps, max_context_len, pl.P, dims};
   hipError_t e = lgm::launch_paged_decode(a, act_dtype, cache_dtype, (hipStream_t)stream);
   if (e != hipSuccess) return fail(LGM_ERR_HIP, fn, "split kernel launch failed: %s", hipGetErrorString(e));
-  if (P > 1) {
-    lgm::MergeArgs m{out, out_lse, part_out, part_lse, nullptr, context_lens, ps, max_context_len,
-                     dims.num_seqs, dims.num_q_heads, dims.head_dim, P, 1};
+  if (pl.P > 1) {
+    lgm::MergeArgs m{out, out_lse, part_out, part_lse, nullptr, context_lens, pl.ps, max_context_len,
+                     dims.num_seqs, dims.num_q_heads, dims.head_dim, pl.P, 1};
     e = lgm::launch_lse_merge(m, act_dtype, (hipStream_t)stream);
     if (e != hipSuccess) return fail(LGM_ERR_HIP, fn, "merge kernel launch failed: %s", hipGetErrorString(e));
   }

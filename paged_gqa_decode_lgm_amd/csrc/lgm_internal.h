@@ -48,6 +48,14 @@ struct DecodeArgs {
   lgm_paged_dims dims;
 };
 
+// Balanced decode: records of split segments and their arrival counts.
+struct StreamArgs {
+  int32_t num_waves;       // W: the tiles of all segments are cut into W equal ranges
+  int32_t record_floats;   // floats per record (stream_record_floats(G))
+  float* records;          // [W][2][record_floats]
+  int32_t* counters;       // [B][Hkv], zero on entry, left zero on completion
+};
+
 struct MergeArgs {
   void* out;
   float* out_lse;
@@ -69,8 +77,21 @@ hipError_t launch_rope_kv_append(const AppendArgs& a, lgm_dtype act, lgm_dtype c
 hipError_t launch_paged_decode(const DecodeArgs& a, lgm_dtype act, lgm_dtype cache, hipStream_t s);
 hipError_t launch_lse_merge(const MergeArgs& a, lgm_dtype out_dtype, hipStream_t s);
 
+// Matrix-core decode for bf16 activations with bf16 / FP8 caches, head_dim 128.
+hipError_t launch_paged_decode_mfma(const DecodeArgs& a, lgm_dtype cache, hipStream_t s);
+// The same shapes with balanced tile ranges, one launch (partition_size 0).
+hipError_t launch_paged_decode_stream(const DecodeArgs& a, const StreamArgs& x, lgm_dtype cache, hipStream_t s);
+int stream_record_floats(int group);
+
+// Minimum resident waves per SIMD the balanced kernel is compiled for; the
+// host cuts the work into (compute units x 4 x this) ranges so that all of
+// them run at once.
+constexpr int stream_waves_per_simd(bool fp8_cache, int group) { return fp8_cache ? 3 : (group <= 4 ? 3 : 2); }
+
 // Shape support queries used by validation (no HIP calls).
 bool decode_supported(lgm_dtype act, lgm_dtype cache, int head_dim, int group, int block_size);
+bool decode_valu_supported(lgm_dtype act, lgm_dtype cache, int head_dim, int group, int block_size);
+bool decode_mfma_supported(lgm_dtype act, lgm_dtype cache, int head_dim, int group, int block_size);
 bool merge_supported(int head_dim);
 
 }  // namespace lgm

@@ -1,0 +1,314 @@
+// Matrix-core building blocks shared by the decode kernels (gfx950,
+// v_mfma_f32_16x16x32_bf16): cache formats, operand packing and the
+// reductions over the four lanes that hold one head in the score layout.
+//
+// Operand mapping (lane l = 16*kg + n, kg = l / 16, n = l % 16):
+//   scores  S^T[token][head] = K[token][d] * Q^T[d][head]: A = K rows (row n =
+//           token n of a 16-token block; 8 consecutive head_dim values per
+//           lane), B = the G query rows (column n = head n, zero for n >= G).
+//           Output lane (kg, n) holds head n for tokens 4kg..4kg+3.
+//   output  O[head][d] += P[head][token] * V[token][d]: A = the probabilities
+//           exactly as the score MFMAs left them (row n = head n, 8 tokens per
+//           lane: rows 4kg..4kg+3 of the two blocks of a 32-token tile); B = V
+//           with column n of the i-th MFMA meaning head_dim index 8n + i, so a
+//           lane needs V[token][8n .. 8n+7] of its 8 tokens: eight 16-byte
+//           loads that together read whole 256-byte rows, and one byte
+//           permute per operand register instead of a transpose.
+//           Output lane (kg, n) holds O[head 4kg + j][8n + i] in acc[i][j].
+// FP8 rows are converted to bf16 in registers (exact: every E4M3 value is a
+// bf16 value).
+#pragma once
+
+#include "device_num.h"
+#include "lgm_internal.h"
+
+namespace lgm {
+namespace mfma {
+
+typedef short short8 __attribute__((ext_vector_type(8)));
+typedef float float4v __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+
+constexpr int kD = 128;
+constexpr int kBS = 16;
+constexpr int kTile = 32;  // tokens per wave iteration (two blocks)
+constexpr int kNW = kDecodeThreads / kWaveSize;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  bf16x2v v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ short8 words_to_short8(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3) {
+  uint4 u = make_uint4(w0, w1, w2, w3);
+  return __builtin_bit_cast(short8, u);
+}
+// Two FP8 codes (low 16 bits of w) -> two bf16 packed in a dword (exact).
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+}
+__device__ __forceinline__ uint32_t fp8x2_hi_to_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
+}
+// Reductions over the four lanes n, n+16, n+32, n+48 (one head in the score layout).
+__device__ __forceinline__ float max4(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float sum4(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// ---- cache formats ------------------------------------------------------------
+// Per 16-token block a lane holds: K for the score MFMAs (row n) and V for the
+// output MFMAs (rows 4kg .. 4kg+3, head_dim 8n .. 8n+7).
+// K/V reads go through buffer loads with one descriptor per 16-token block
+// (base = the block, size = the block's bytes): offsets stay 32-bit for any
+// pool size, a stray offset reads zeros instead of faulting, and the loads are
+// intrinsic calls, which the compiler keeps where the software pipeline puts
+// them (plain loads carried around the tile loop get merged into a single
+// load at the loop head, right before their use).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const void* pool, int64_t block_bytes, int pb) {
+  return __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<char*>(static_cast<const char*>(pool) + (int64_t)pb * block_bytes), (short)0, (int)block_bytes,
+      0x00020000);
+}
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t span_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+__device__ __forceinline__ int buf_load4(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ uint2 buf_load8(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+
+struct MfmaBF16 {
+  static constexpr bool kFp8 = false;
+  static constexpr int kElemBytes = 2;
+  using elem_t = uint16_t;
+  struct KBlock {
+    uint4 k[4];  // K[n][32c + 8kg .. +8], c = 0..3
+  };
+  struct VBlock {
+    uint4 v[4];  // V[4kg + jj][8n .. +8], jj = 0..3
+  };
+  // Byte offsets inside a block of this lane's first K / V chunk (kv head g,
+  // row stride tok_bytes = Hkv * 128 * 2).
+  __device__ static int k_lane_off(int g, int tok_bytes, int n, int kg) { return n * tok_bytes + g * 256 + 16 * kg; }
+  __device__ static int v_lane_off(int g, int tok_bytes, int n, int kg) {
+    return 4 * kg * tok_bytes + g * 256 + 16 * n;
+  }
+  __device__ static void load_k(KBlock& r, __amdgpu_buffer_rsrc_t rs, int off, int) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) r.k[c] = buf_load16(rs, off + 64 * c);
+  }
+  __device__ static void load_v(VBlock& r, __amdgpu_buffer_rsrc_t rs, int off, int tok_bytes) {
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) r.v[jj] = buf_load16(rs, off + jj * tok_bytes);
+  }
+  // A operand of score MFMA c.
+  __device__ static short8 k_operand(const KBlock& r, int c) { return __builtin_bit_cast(short8, r.k[c]); }
+  // V element i (0..7) of row jj packed with the same element of row jj+1 -> bf16x2.
+  __device__ static uint32_t v_pair(const VBlock& r, int jj, int i) {
+    const uint32_t* a = reinterpret_cast<const uint32_t*>(&r.v[jj]);
+    const uint32_t* b = reinterpret_cast<const uint32_t*>(&r.v[jj + 1]);
+    const uint32_t x = a[i >> 1], y = b[i >> 1];
+    return (i & 1) ? ((y & 0xffff0000u) | (x >> 16)) : ((y << 16) | (x & 0xffffu));
+  }
+  __device__ static void zero_v_row(VBlock& r, int jj) { r.v[jj] = make_uint4(0, 0, 0, 0); }
+};
+
+struct MfmaFP8 {
+  static constexpr bool kFp8 = true;
+  static constexpr int kElemBytes = 1;
+  using elem_t = uint8_t;
+  struct KBlock {
+    uint4 k[2];  // K[n][64u + 16kg .. +16] (16 codes), u = 0..1
+  };
+  struct VBlock {
+    uint2 v[4];  // V[4kg + jj][8n .. +8] (8 codes)
+  };
+  __device__ static int k_lane_off(int g, int tok_bytes, int n, int kg) { return n * tok_bytes + g * 128 + 16 * kg; }
+  __device__ static int v_lane_off(int g, int tok_bytes, int n, int kg) {
+    return 4 * kg * tok_bytes + g * 128 + 8 * n;
+  }
+  __device__ static void load_k(KBlock& r, __amdgpu_buffer_rsrc_t rs, int off, int) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) r.k[u] = buf_load16(rs, off + 64 * u);
+  }
+  __device__ static void load_v(VBlock& r, __amdgpu_buffer_rsrc_t rs, int off, int tok_bytes) {
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) r.v[jj] = buf_load8(rs, off + jj * tok_bytes);
+  }
+  // Score MFMA c = 2u + h uses codes 8h .. 8h+7 of K chunk u: head_dim 64u + 16kg + 8h + j.
+  __device__ static short8 k_operand(const KBlock& r, int c) {
+    const uint4& q = r.k[c >> 1];
+    const uint32_t w0 = (c & 1) ? q.z : q.x;
+    const uint32_t w1 = (c & 1) ? q.w : q.y;
+    return words_to_short8(fp8x2_to_bf16x2(w0), fp8x2_hi_to_bf16x2(w0), fp8x2_to_bf16x2(w1),
+                           fp8x2_hi_to_bf16x2(w1));
+  }
+  __device__ static uint32_t v_pair(const VBlock& r, int jj, int i) {
+    const uint32_t x = (i < 4 ? r.v[jj].x : r.v[jj].y) >> (8 * (i & 3));
+    const uint32_t y = (i < 4 ? r.v[jj + 1].x : r.v[jj + 1].y) >> (8 * (i & 3));
+    return fp8x2_to_bf16x2((x & 0xffu) | ((y & 0xffu) << 8));
+  }
+  __device__ static void zero_v_row(VBlock& r, int jj) { r.v[jj] = make_uint2(0, 0); }
+};
+
+// Head-dim index held by (MFMA c, lane group kg, slot j) in the score operands.
+template <class C>
+__device__ __forceinline__ int score_d(int c, int kg, int j) {
+  if constexpr (C::kFp8)
+    return 64 * (c >> 1) + 16 * kg + 8 * (c & 1) + j;
+  else
+    return 32 * c + 8 * kg + j;
+}
+
+
+// Query rows of a head group as the B operand of the score MFMAs (bf16 bit
+// patterns; zero for n >= G).  qrow points at head 0 of the group; 16-byte
+// loads when the rows are 16-byte aligned, element loads otherwise.
+// Query rows of a head group as the B operand of the score MFMAs (bf16 bit
+// patterns; zero for n >= G).  qrow points at head 0 of the group.  Aligned
+// rows are read with 16-byte buffer loads (the same kind of load as the K/V
+// stream, so the compiler can keep counting outstanding loads exactly);
+// unaligned rows fall back to element loads.
+template <class C, int G>
+__device__ __forceinline__ void load_q_operand(short8 (&qb)[4], const uint16_t* qrow, bool vec, int n, int kg) {
+  const int row = (n < G ? n : 0) * kD;  // rows n >= G read row 0 and are zeroed
+  uint4 raw[4];
+  if (vec) {
+    const __amdgpu_buffer_rsrc_t rs = span_rsrc(qrow, G * kD * 2);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) raw[c] = buf_load16(rs, 2 * (row + score_d<C>(c, kg, 0)));
+  } else {
+    const uint16_t* qp = qrow + row;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      uint32_t w[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        w[j] = (uint32_t)qp[score_d<C>(c, kg, 2 * j)] | ((uint32_t)qp[score_d<C>(c, kg, 2 * j + 1)] << 16);
+      raw[c] = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    if (n >= G) raw[c] = make_uint4(0, 0, 0, 0);
+    qb[c] = __builtin_bit_cast(short8, raw[c]);
+  }
+}
+
+// Online-softmax state of one wave for one (sequence, kv head): running max
+// m of head n (log2 units, the same in its four lanes), this lane's shares of
+// the sums of rounded (lsum) and unrounded (lsum_e) probabilities, and the
+// output accumulator acc[i][j] = O[head 4kg + j][8n + i].
+struct WaveState {
+  float m, lsum, lsum_e;
+  float4v acc[8];
+  __device__ __forceinline__ void reset() {
+    m = -INFINITY;
+    lsum = 0.f;
+    lsum_e = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = (float4v){0.f, 0.f, 0.f, 0.f};
+  }
+};
+
+// Registers of one 32-token tile (blocks x and y).
+template <class C>
+struct TileRegs {
+  typename C::KBlock kx, ky;
+  typename C::VBlock vx, vy;
+};
+
+template <class C>
+__device__ __forceinline__ void tile_scores(const TileRegs<C>& r, const short8 (&qb)[4], float4v& sx, float4v& sy) {
+  sx = (float4v){0.f, 0.f, 0.f, 0.f};
+  sy = (float4v){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    sx = __builtin_amdgcn_mfma_f32_16x16x32_bf16(C::k_operand(r.kx, c), qb[c], sx, 0, 0, 0);
+    sy = __builtin_amdgcn_mfma_f32_16x16x32_bf16(C::k_operand(r.ky, c), qb[c], sy, 0, 0, 0);
+  }
+}
+
+// Softmax update and output MFMAs for one tile whose scores are sx / sy.
+// xval / yval: the blocks are present with valid table entries; tok0: first
+// token of the tile, end: one past the last valid token (same origin).
+// Masked rows get -inf scores and zeroed V rows (V there may hold anything,
+// even NaN, and a zero probability must contribute exactly zero).
+template <class C>
+__device__ __forceinline__ void tile_update(WaveState& st, TileRegs<C>& r, const float4v& sx, const float4v& sy,
+                                            float sscale, bool xval, bool yval, int tok0, int end, int kg) {
+  float s[8];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    s[j] = xval ? sx[j] * sscale : -INFINITY;
+    s[4 + j] = yval ? sy[j] * sscale : -INFINITY;
+  }
+  if (!xval || !yval || tok0 + kTile > end) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (tok0 + 4 * kg + j >= end) s[j] = -INFINITY;
+      if (tok0 + kBS + 4 * kg + j >= end) s[4 + j] = -INFINITY;
+      if (!xval || tok0 + 4 * kg + j >= end) C::zero_v_row(r.vx, j);
+      if (!yval || tok0 + kBS + 4 * kg + j >= end) C::zero_v_row(r.vy, j);
+    }
+  }
+  float tmax = s[0];
+#pragma unroll
+  for (int j = 1; j < 8; ++j) tmax = fmaxf(tmax, s[j]);
+  tmax = max4(tmax);
+  const float mn = fmaxf(st.m, tmax);
+  const float ms = mn == -INFINITY ? 0.f : mn;
+  const float alpha = fast_exp2(st.m - ms);
+  st.m = mn;
+  // Probabilities, rounded to bf16 once for the output MFMAs; the output is
+  // normalised by the sum of those rounded values (an exact convex
+  // combination of V rows) and the log-sum-exp uses the unrounded sum.
+  uint32_t pw[4];
+  float psum = 0.f, psum_e = 0.f;
+#pragma unroll
+  for (int t2 = 0; t2 < 4; ++t2) {
+    const float p0 = fast_exp2(s[2 * t2] - ms);
+    const float p1 = fast_exp2(s[2 * t2 + 1] - ms);
+    pw[t2] = pack_bf16(p0, p1);
+    psum += bf16_lo(pw[t2]) + bf16_hi(pw[t2]);
+    psum_e += p0 + p1;
+  }
+  st.lsum = st.lsum * alpha + psum;
+  st.lsum_e = st.lsum_e * alpha + psum_e;
+  // Rescale the accumulator rows: row j of lane group kg is head 4kg + j,
+  // whose alpha sits in lane 4kg + j.
+  if (__any(alpha != 1.f)) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float aj = __shfl(alpha, 4 * kg + j);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) st.acc[i][j] *= aj;
+    }
+  }
+  // P operand: head n, tokens x rows 4kg..4kg+3 then y rows 4kg..4kg+3.
+  const short8 pa = words_to_short8(pw[0], pw[1], pw[2], pw[3]);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const short8 vb = words_to_short8(C::v_pair(r.vx, 0, i), C::v_pair(r.vx, 2, i), C::v_pair(r.vy, 0, i),
+                                      C::v_pair(r.vy, 2, i));
+    st.acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, st.acc[i], 0, 0, 0);
+  }
+}
+
+}  // namespace mfma
+}  // namespace lgm

@@ -314,14 +314,23 @@ hipError_t dispatch_dim(const DecodeArgs& a, int G, hipStream_t s) {
 
 }  // namespace
 
-bool decode_supported(lgm_dtype act, lgm_dtype cache, int head_dim, int group, int block_size) {
+bool decode_valu_supported(lgm_dtype act, lgm_dtype cache, int head_dim, int group, int block_size) {
   const bool types = (act == LGM_F32 && cache == LGM_F32) || (act == LGM_BF16 && cache == LGM_BF16) ||
                      (act == LGM_BF16 && cache == LGM_FP8_E4M3);
   return types && (head_dim == 64 || head_dim == 128) && group >= 1 && group <= 8 && block_size == kBS;
 }
 
+bool decode_supported(lgm_dtype act, lgm_dtype cache, int head_dim, int group, int block_size) {
+  return decode_mfma_supported(act, cache, head_dim, group, block_size) ||
+         decode_valu_supported(act, cache, head_dim, group, block_size);
+}
+
+// bf16 activations with bf16 / FP8 caches at head_dim 128 run on the matrix
+// cores; every other supported shape runs the vector-ALU kernel above.
 hipError_t launch_paged_decode(const DecodeArgs& a, lgm_dtype act, lgm_dtype cache, hipStream_t s) {
   const int G = a.dims.num_q_heads / a.dims.num_kv_heads;
+  if (decode_mfma_supported(act, cache, a.dims.head_dim, G, a.dims.block_size))
+    return launch_paged_decode_mfma(a, cache, s);
   if (act == LGM_F32 && cache == LGM_F32) return dispatch_dim<CacheF32, ActF32>(a, G, s);
   if (act == LGM_BF16 && cache == LGM_BF16) return dispatch_dim<CacheBF16, ActBF16>(a, G, s);
   if (act == LGM_BF16 && cache == LGM_FP8_E4M3) return dispatch_dim<CacheFP8, ActBF16>(a, G, s);

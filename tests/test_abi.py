@@ -100,7 +100,8 @@ def _attn(**over):
 ATTN_BAD = [
     (dict(dims=dims(head_dim=96)), UNS, "head_dim"),
     (dict(dims=dims(block_size=32, max_blocks_per_seq=256)), UNS, "block_size"),
-    (dict(dims=dims(num_q_heads=64, num_kv_heads=4)), UNS, "group"),
+    (dict(dims=dims(num_q_heads=64, num_kv_heads=2), q_seq_stride=64 * 128), UNS, "group"),
+    (dict(dims=dims(num_q_heads=32, num_kv_heads=2), act_dtype=L.LGM_F32, cache_dtype=L.LGM_F32), UNS, "group"),
     (dict(act_dtype=L.LGM_F32), UNS, "act"),
     (dict(act_dtype=5), INV, "act_dtype"),
     (dict(softmax_scale=float("inf")), INV, "softmax_scale"),
@@ -142,9 +143,11 @@ def test_attention_empty_batch_is_a_noop():
 
 # ------------------------------------------------------------------ plan queries
 @pytest.mark.parametrize("d,max_ctx,ps,want", [
-    (dims(), 8192, 0, 512),                                               # Llama-3-8B-shaped, B64
-    (dims(num_seqs=128, max_blocks_per_seq=256), 4096, 0, 512),           # FP8 config, B128
-    (dims(num_seqs=2, num_q_heads=12, num_kv_heads=2, max_blocks_per_seq=128), 2048, 0, 64),
+    (dims(), 8192, 0, 0),                                                 # Llama-3-8B-shaped: balanced ranges
+    (dims(num_seqs=128, max_blocks_per_seq=256), 4096, 0, 0),             # FP8 config: balanced ranges
+    (dims(num_seqs=2, num_q_heads=12, num_kv_heads=2, max_blocks_per_seq=128), 2048, 0, 0),
+    (dims(head_dim=64), 8192, 0, 512),                                    # vector-ALU shape: fixed partitions
+    (dims(num_seqs=2, num_q_heads=12, num_kv_heads=2, head_dim=64, max_blocks_per_seq=128), 2048, 0, 64),
     (dims(num_seqs=4, max_blocks_per_seq=8192), 131072, 512, 512),         # explicit
     (dims(num_seqs=1, num_q_heads=4, num_kv_heads=1, head_dim=64, max_blocks_per_seq=16), 256, 256, 256),
     (dims(), 8192, 16384, 8192),                                          # larger than the context: no split
@@ -152,6 +155,18 @@ def test_attention_empty_batch_is_a_noop():
 ])
 def test_partition_plan(d, max_ctx, ps, want):
     assert L.lgm_paged_decode_partition_size(d, max_ctx, ps, L.LGM_BF16) == want
+
+
+def test_balanced_workspace_size_formula():
+    al = lambda x: (x + 255) // 256 * 256
+    d = dims()                                     # bf16, G = 4: records of 16 lanes x 32 floats + 48, padded to 576
+    W = 3072                                       # 12 resident waves x 256 CUs (64*8*256 tiles / 2 exceeds it)
+    assert L.lgm_paged_decode_workspace_size(d, 8192, 0, L.LGM_BF16) == al(W * 2 * 576 * 4) + al(64 * 8 * 4)
+    W8 = 3072
+    assert L.lgm_paged_decode_workspace_size(d, 8192, 0, L.LGM_FP8_E4M3) == al(W8 * 2 * 576 * 4) + al(64 * 8 * 4)
+    small = dims(num_seqs=2, num_q_heads=12, num_kv_heads=2, max_blocks_per_seq=128)  # G = 6: 2 lane rows
+    W2 = (2 * 2 * 64 + 1) // 2
+    assert L.lgm_paged_decode_workspace_size(small, 2048, 0, L.LGM_BF16) == al(W2 * 2 * 1088 * 4) + al(2 * 2 * 4)
 
 
 def test_workspace_size_formula():
