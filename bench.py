@@ -51,7 +51,7 @@ def measured_traffic(workload: str, kv_bytes: int):
     return t.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, min_seconds: float = 10.0, max_passes: int = 3):
+def cpu_baseline(w, min_seconds: float = 12.0, max_passes: int = 10):
     """The fp64 oracle on the whole batch (host copies of the same inputs), one
     thread; passes repeat until ~min_seconds of work, the median pass is kept."""
     import numpy as np
@@ -177,8 +177,7 @@ def main() -> int:
         "kernel_ms": {"attention_avg": round(attn_avg_s * 1e3, 5),
                       "attention_median": round(statistics.median(attn_ms), 5),
                       "append_avg": round(statistics.mean(append_ms), 5) if append_ms else None},
-        "roofline": {"bound": "hbm", "kernel": "lgm_paged_decode_attn (" + ("balanced decode, one launch" if ps == 0
-                     else "split-K decode + LSE merge launches") + ")",
+        "roofline": {"bound": "hbm", "kernel": "lgm_paged_decode_attn (split-K decode + LSE merge launches)",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
     }

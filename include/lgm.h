@@ -135,28 +135,31 @@ lgm_status lgm_rope_kv_append(const void* qkv, int64_t qkv_row_stride, void* q_o
                               lgm_dtype act_dtype, lgm_dtype cache_dtype, void* stream);
 
 /*
- * How the attention call will split the contexts.  A positive
- * partition_size must be a multiple of block_size and is returned as is
- * (clamped to the rounded-up max_context_len): fixed partitions of that many
- * tokens.  partition_size 0 lets the library choose from the shapes alone
- * (deterministic, no device query): it returns 0 when it uses balanced
- * ranges (bf16 activations with bf16 / FP8 caches at head_dim 128: the
- * 32-token tiles of all (sequence, kv head) pairs are cut into as many equal
- * ranges as the GPU keeps waves resident, so each wave reads the same number
- * of bytes whatever the mix of context lengths), otherwise the partition size
- * it picked.  Returns -1 (and sets lgm_last_error) on invalid arguments.
+ * The partition size the attention call will use.  A positive partition_size
+ * must be a multiple of block_size and is returned as is (clamped to the
+ * rounded-up max_context_len).  partition_size 0 lets the library choose
+ * from the shapes alone (deterministic, no device query): for the
+ * matrix-core shapes (bf16 activations, bf16 / FP8 caches, head_dim 128) the
+ * largest power of two from 64 to 4096 tokens that still gives 2048
+ * (sequence, partition, kv head) work items at max_context_len; otherwise a
+ * size that gives about 8192 workgroups.  When max_context_len exceeds the
+ * partition size, each context is cut into floor(L / partition) full
+ * partitions followed by partitions of half that size (at least block_size)
+ * over the rest, which are processed last.  Returns -1 (and sets
+ * lgm_last_error) on invalid arguments.
  */
 int32_t lgm_paged_decode_partition_size(lgm_paged_dims dims, int32_t max_context_len,
                                         int32_t partition_size, lgm_dtype cache_dtype);
 
 /*
  * Bytes of device workspace lgm_paged_decode_attn needs for these
- * arguments.  Fixed partitions: 0 when every sequence fits one partition,
- * otherwise room for the split-K records (fp32 partial outputs [B][Hq][P][D]
- * and natural-log LSEs [B][Hq][P], P = ceil(max_context_len / partition)).
- * Balanced ranges: two records per range plus one int32 arrival counter per
- * (sequence, kv head).  Returns 0 and sets lgm_last_error on invalid
- * arguments (check it when 0 is unexpected).
+ * arguments: for the matrix-core shapes first 256 bytes holding two int32
+ * work counters, then, when contexts are split, the split-K records (fp32
+ * partial outputs [B][Hq][P][D] and natural-log LSEs [B][Hq][P], each
+ * 256-byte aligned, P = the most partitions any context up to
+ * max_context_len is cut into).  0 for other shapes without a split.
+ * Returns 0 and sets lgm_last_error on invalid arguments (check it when 0
+ * is unexpected).
  */
 size_t lgm_paged_decode_workspace_size(lgm_paged_dims dims, int32_t max_context_len,
                                        int32_t partition_size, lgm_dtype cache_dtype);
@@ -170,10 +173,12 @@ size_t lgm_paged_decode_workspace_size(lgm_paged_dims dims, int32_t max_context_
  *   out[b][h] = sum_j softmax(s)_j V_j   (FP8: V_j = decoded byte * v_scale[g]),
  *   out_lse[b][h] = log(sum_j exp(s_j))  (natural log; -inf and out = 0 when L = 0).
  * Arithmetic is fp32 with one final rounding to the act dtype.  Contexts are
- * cut into partitions of `partition_size` tokens (see
- * lgm_paged_decode_partition_size) processed in parallel; partial results
- * are merged by log-sum-exp (as lgm_lse_merge) on the same stream, within
- * this call.  A sequence that fits one partition is written directly.
+ * cut into partitions (see lgm_paged_decode_partition_size) processed in
+ * parallel; partial results are merged by log-sum-exp (as lgm_lse_merge) on
+ * the same stream, within this call.  A sequence that fits one partition is
+ * written directly.  The matrix-core kernel runs as many workgroups as the
+ * device keeps resident, each taking (sequence, partition, kv head) items
+ * from the workspace's work counters until none is left.
  *
  *   out            [B][Hq][D] act dtype (dense)
  *   out_lse        optional fp32 [B][Hq] (NULL = not written)
@@ -187,10 +192,11 @@ size_t lgm_paged_decode_workspace_size(lgm_paged_dims dims, int32_t max_context_
  *   max_context_len upper bound on context_lens, 0..max_blocks_per_seq*block_size
  *   workspace      device buffer of at least lgm_paged_decode_workspace_size()
  *                  bytes, 256-byte aligned (NULL allowed when that size is 0).
- *                  It must be zero-filled before its first use and again
- *                  after a call on it failed to complete or the shapes
- *                  changed; every completed call leaves it as it needs it.
- *                  Calls sharing a workspace must not overlap in time.
+ *                  Its first 256 bytes (the work counters, matrix-core
+ *                  shapes) must be zero before the first call on it; every
+ *                  completed call leaves them zero again.  Zero-fill it again
+ *                  after a call on it failed to complete.  Calls sharing a
+ *                  workspace must not overlap in time (one per stream).
  * Supported: (act, cache) in {(F32, F32), (BF16, BF16), (BF16, FP8_E4M3)},
  * head_dim in {64, 128}, block_size 16, G = Hq/Hkv in 1..8; with bf16
  * activations at head_dim 128, G in 1..16 (matrix-core kernel).

@@ -32,7 +32,6 @@ UNITS = {
     "rope_kv_append.hip": ["-ffp-contract=off"],
     "paged_decode.hip": [],
     "paged_decode_mfma.hip": [],
-    "paged_decode_stream.hip": [],
     "lse_merge.hip": [],
 }
 

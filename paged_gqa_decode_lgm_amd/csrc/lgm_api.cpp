@@ -102,10 +102,23 @@ lgm_status check_no_alias(const char* fn, const Span* outs, int n_out, const Spa
 }
 
 constexpr int kAutoTargetWorkgroups = 8192;
+#ifndef LGM_TAIL_DIVISOR
+#define LGM_TAIL_DIVISOR 2
+#endif
+constexpr int kTailDivisor = LGM_TAIL_DIVISOR;
 constexpr int kMinAutoPartitionBlocks = 4;
 
 // Partition plan: returns the partition size in tokens, or -1 after setting the error.
-int32_t resolve_partition(const char* fn, const lgm_paged_dims& d, int32_t max_ctx, int32_t ps) {
+// Auto plan of the persistent matrix-core kernel: the largest power-of-two
+// partition (64 .. 4096 tokens) that still gives at least kAutoMinItems
+// (sequence, partition, kv head) items at the longest context, four per
+// workgroup of its grid on MI355X (256 CUs x 2): large partitions amortise
+// each item's start and merge, enough items keep the drain short.
+constexpr int64_t kAutoMinItems = 2048;
+constexpr int kAutoMaxPartition = 4096;
+constexpr int kAutoMinPartition = 64;
+
+int32_t resolve_partition(const char* fn, const lgm_paged_dims& d, int32_t max_ctx, int32_t ps, bool persistent) {
   if (ps < 0) {
     fail(LGM_ERR_INVALID_ARGUMENT, fn, "partition_size = %d must be 0 (library chooses) or positive", ps);
     return -1;
@@ -116,7 +129,16 @@ int32_t resolve_partition(const char* fn, const lgm_paged_dims& d, int32_t max_c
     return -1;
   }
   const int64_t cap = ((int64_t)(max_ctx > 0 ? max_ctx : 1) + d.block_size - 1) / d.block_size * d.block_size;
-  if (ps == 0) {
+  if (ps == 0 && persistent) {
+    const int64_t units = (int64_t)(d.num_seqs > 0 ? d.num_seqs : 1) * d.num_kv_heads;
+    ps = kAutoMinPartition;
+    for (int64_t p = kAutoMaxPartition; p > kAutoMinPartition; p /= 2) {
+      if (units * ((cap + p - 1) / p) >= kAutoMinItems) {
+        ps = (int32_t)p;
+        break;
+      }
+    }
+  } else if (ps == 0) {
     // Enough partitions that the grid holds ~kAutoTargetWorkgroups workgroups
     // at the longest context, but never fewer than 4 blocks (one per wave).
     const int64_t units = (int64_t)(d.num_seqs > 0 ? d.num_seqs : 1) * d.num_kv_heads;
@@ -132,56 +154,49 @@ int32_t resolve_partition(const char* fn, const lgm_paged_dims& d, int32_t max_c
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Balanced plan: one range per resident wave of the balanced kernel on
-// MI355X's 256 compute units (4 SIMDs each), so every range runs
-// concurrently and they all finish together.
-constexpr int kComputeUnits = 256;
-constexpr int kStreamTileTokens = 32;
-int stream_max_waves(lgm_dtype cache, int group) {
-  return kComputeUnits * 4 * lgm::stream_waves_per_simd(cache == LGM_FP8_E4M3, group);
-}
-
-// Launch plan of one attention call, a function of host-visible arguments only.
-//   balanced: partition_size 0 on a matrix-core shape: W equal tile ranges,
-//             workspace = [W][2] records then [B][Hkv] arrival counters;
-//   fixed:    partitions of `ps` tokens, workspace = partial outputs and LSEs
-//             (none when every sequence fits one partition).
+// Launch plan of one attention call, a function of host-visible arguments only:
+// partitions of `ps` tokens; workspace = the persistent kernel's two work
+// counters (matrix-core shapes, one 256-byte slot), then the partial outputs
+// and LSEs (none when every sequence fits one partition).
 struct Plan {
-  bool balanced;
-  int32_t ps, P;       // fixed partitions
-  int32_t W, rec_floats;
-  size_t part_out_bytes, part_lse_bytes;
-  size_t records_bytes, counters_bytes;
+  lgm::PartitionPlan parts;
+  int32_t ps, P;
+  size_t counters_bytes, part_out_bytes, part_lse_bytes;
   size_t total;
 };
 
-bool plan_decode(const char* fn, const lgm_paged_dims& d, int32_t max_ctx, int32_t ps_arg, lgm_dtype cache, Plan& pl) {
+lgm_status plan_decode(const char* fn, const lgm_paged_dims& d, int32_t max_ctx, int32_t ps_arg, lgm_dtype cache,
+                       Plan& pl) {
   pl = Plan{};
   const int G = d.num_q_heads / d.num_kv_heads;
   const lgm_dtype act = cache == LGM_F32 ? LGM_F32 : LGM_BF16;  // the only supported pairings
-  if (ps_arg == 0 && lgm::decode_mfma_supported(act, cache, d.head_dim, G, d.block_size)) {
-    pl.balanced = true;
-    const int64_t tiles = (int64_t)(max_ctx + kStreamTileTokens - 1) / kStreamTileTokens;
-    const int64_t n_upper = (int64_t)d.num_seqs * d.num_kv_heads * tiles;
-    int64_t W = (n_upper + 1) / 2;
-    const int64_t wmax = stream_max_waves(cache, G);
-    W = W < 1 ? 1 : (W > wmax ? wmax : W);
-    pl.W = (int32_t)W;
-    pl.rec_floats = lgm::stream_record_floats(G);
-    pl.records_bytes = align256((size_t)W * 2 * pl.rec_floats * sizeof(float));
-    pl.counters_bytes = align256((size_t)d.num_seqs * d.num_kv_heads * sizeof(int32_t));
-    pl.total = pl.records_bytes + pl.counters_bytes;
-    return true;
+  const bool persistent = lgm::decode_mfma_supported(act, cache, d.head_dim, G, d.block_size);
+  pl.ps = resolve_partition(fn, d, max_ctx, ps_arg, persistent);
+  if (pl.ps < 0) return LGM_ERR_INVALID_ARGUMENT;
+  // When contexts are split, the tokens past a context's last full partition
+  // go to partitions of half the size, which the kernels take last: the work
+  // drains on short items instead of ending on long ones.
+  pl.parts = lgm::PartitionPlan{pl.ps, pl.ps};
+  if (max_ctx > pl.ps) {
+    const int32_t q = pl.ps / kTailDivisor / d.block_size * d.block_size;
+    pl.parts.tps = q < d.block_size ? d.block_size : q;
   }
-  pl.ps = resolve_partition(fn, d, max_ctx, ps_arg);
-  if (pl.ps < 0) return false;
-  pl.P = max_ctx <= 0 ? 1 : (max_ctx + pl.ps - 1) / pl.ps;
+  pl.P = pl.parts.max_count(max_ctx);
+  if (pl.P > 65535)  // the partition index is a grid dimension of the vector-ALU kernel
+    return fail(LGM_ERR_UNSUPPORTED, fn, "max_context_len = %d / partition_size = %d gives %d partitions: at most 65535",
+                max_ctx, pl.ps, pl.P);
+  // Work item numbers of the persistent kernel are 32-bit, with room for one
+  // overshooting fetch per workgroup.
+  if (persistent && (int64_t)d.num_seqs * d.num_kv_heads * pl.P > (int64_t)INT32_MAX - (1 << 20))
+    return fail(LGM_ERR_UNSUPPORTED, fn, "num_seqs * num_kv_heads * partitions = %lld work items: too many",
+                (long long)d.num_seqs * d.num_kv_heads * pl.P);
+  if (persistent) pl.counters_bytes = 256;
   if (pl.P > 1) {
     pl.part_out_bytes = align256((size_t)d.num_seqs * d.num_q_heads * pl.P * d.head_dim * sizeof(float));
     pl.part_lse_bytes = align256((size_t)d.num_seqs * d.num_q_heads * pl.P * sizeof(float));
-    pl.total = pl.part_out_bytes + pl.part_lse_bytes;
   }
-  return true;
+  pl.total = pl.counters_bytes + pl.part_out_bytes + pl.part_lse_bytes;
+  return LGM_OK;
 }
 
 lgm_status check_decode_common(const char* fn, const lgm_paged_dims& d, int32_t max_ctx, lgm_dtype cache) {
@@ -262,8 +277,8 @@ int32_t lgm_paged_decode_partition_size(lgm_paged_dims dims, int32_t max_context
   g_err.clear();
   if (check_decode_common(fn, dims, max_context_len, cache_dtype) != LGM_OK) return -1;
   Plan pl;
-  if (!plan_decode(fn, dims, max_context_len, partition_size, cache_dtype, pl)) return -1;
-  return pl.balanced ? 0 : pl.ps;
+  if (plan_decode(fn, dims, max_context_len, partition_size, cache_dtype, pl) != LGM_OK) return -1;
+  return pl.ps;
 }
 
 size_t lgm_paged_decode_workspace_size(lgm_paged_dims dims, int32_t max_context_len, int32_t partition_size,
@@ -272,7 +287,7 @@ size_t lgm_paged_decode_workspace_size(lgm_paged_dims dims, int32_t max_context_
   g_err.clear();
   if (check_decode_common(fn, dims, max_context_len, cache_dtype) != LGM_OK) return 0;
   Plan pl;
-  if (!plan_decode(fn, dims, max_context_len, partition_size, cache_dtype, pl)) return 0;
+  if (plan_decode(fn, dims, max_context_len, partition_size, cache_dtype, pl) != LGM_OK) return 0;
   return pl.total;
 }
 
@@ -305,7 +320,7 @@ lgm_status lgm_paged_decode_attn(void* out, float* out_lse, const void* q, int64
                 (long long)q_seq_stride, (long long)qrow);
   if ((st = check_scales(fn, cache_dtype, k_scale, v_scale)) != LGM_OK) return st;
   Plan pl;
-  if (!plan_decode(fn, dims, max_context_len, partition_size, cache_dtype, pl)) return LGM_ERR_INVALID_ARGUMENT;
+  if ((st = plan_decode(fn, dims, max_context_len, partition_size, cache_dtype, pl)) != LGM_OK) return st;
   struct {
     size_t total;
   } ws{pl.total};
@@ -343,23 +358,15 @@ lgm_status lgm_paged_decode_attn(void* out, float* out_lse, const void* q, int64
   if ((st = check_no_alias(fn, outs, 3, ins, 7)) != LGM_OK) return st;
 
   char* wsb = static_cast<char*>(workspace);
-  if (pl.balanced) {
-    lgm::DecodeArgs a{out, out_lse, q, q_seq_stride, k_cache, v_cache, block_tables, context_lens, k_scale, v_scale,
-                      nullptr, nullptr, softmax_scale, 0, max_context_len, 0, dims};
-    lgm::StreamArgs x{pl.W, pl.rec_floats, reinterpret_cast<float*>(wsb),
-                      reinterpret_cast<int32_t*>(wsb + pl.records_bytes)};
-    const hipError_t e = lgm::launch_paged_decode_stream(a, x, cache_dtype, (hipStream_t)stream);
-    if (e != hipSuccess) return fail(LGM_ERR_HIP, fn, "decode kernel launch failed: %s", hipGetErrorString(e));
-    return LGM_OK;
-  }
-  float* part_out = pl.total ? reinterpret_cast<float*>(wsb) : nullptr;
-  float* part_lse = pl.total ? reinterpret_cast<float*>(wsb + pl.part_out_bytes) : nullptr;
+  int32_t* counters = pl.counters_bytes ? reinterpret_cast<int32_t*>(wsb) : nullptr;
+  float* part_out = pl.P > 1 ? reinterpret_cast<float*>(wsb + pl.counters_bytes) : nullptr;
+  float* part_lse = pl.P > 1 ? reinterpret_cast<float*>(wsb + pl.counters_bytes + pl.part_out_bytes) : nullptr;
   lgm::DecodeArgs a{out, out_lse, q, q_seq_stride, k_cache, v_cache, block_tables, context_lens, k_scale, v_scale,
-                    part_out, part_lse, softmax_scale, pl.ps, max_context_len, pl.P, dims};
+                    part_out, part_lse, counters, softmax_scale, pl.parts, max_context_len, pl.P, dims};
   hipError_t e = lgm::launch_paged_decode(a, act_dtype, cache_dtype, (hipStream_t)stream);
   if (e != hipSuccess) return fail(LGM_ERR_HIP, fn, "split kernel launch failed: %s", hipGetErrorString(e));
   if (pl.P > 1) {
-    lgm::MergeArgs m{out, out_lse, part_out, part_lse, nullptr, context_lens, pl.ps, max_context_len,
+    lgm::MergeArgs m{out, out_lse, part_out, part_lse, nullptr, context_lens, pl.parts, max_context_len,
                      dims.num_seqs, dims.num_q_heads, dims.head_dim, pl.P, 1};
     e = lgm::launch_lse_merge(m, act_dtype, (hipStream_t)stream);
     if (e != hipSuccess) return fail(LGM_ERR_HIP, fn, "merge kernel launch failed: %s", hipGetErrorString(e));
@@ -396,7 +403,7 @@ lgm_status lgm_lse_merge(void* out, float* out_lse, const float* partial_out, co
                       {"num_partitions", (uintptr_t)num_partitions, num_partitions ? (int64_t)num_seqs * 4 : 0}};
   lgm_status st = check_no_alias(fn, outs, 2, ins, 3);
   if (st != LGM_OK) return st;
-  lgm::MergeArgs m{out, out_lse, partial_out, partial_lse, num_partitions, nullptr, 0, 0,
+  lgm::MergeArgs m{out, out_lse, partial_out, partial_lse, num_partitions, nullptr, lgm::PartitionPlan{1, 1}, 0,
                    num_seqs, num_q_heads, head_dim, max_partitions, 0};
   const hipError_t e = lgm::launch_lse_merge(m, out_dtype, (hipStream_t)stream);
   if (e != hipSuccess) return fail(LGM_ERR_HIP, fn, "kernel launch failed: %s", hipGetErrorString(e));

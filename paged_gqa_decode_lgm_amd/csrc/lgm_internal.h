@@ -28,6 +28,41 @@ struct AppendArgs {
   lgm_paged_dims dims;
 };
 
+// How one context of ctx tokens is cut into split-K partitions: the first
+// nfull(ctx) = floor(ctx / ps) partitions hold ps tokens each, the rest of
+// the context follows in partitions of tps <= ps tokens; an empty context has
+// one (empty) partition.  {ps, ps} gives the plain ceil(ctx / ps) partitions.
+struct PartitionPlan {
+  int32_t ps, tps;
+  __host__ __device__ int nfull(int ctx) const { return ctx / ps; }
+  __host__ __device__ int count(int ctx) const {
+    if (ctx <= 0) return 1;
+    const int nf = nfull(ctx);
+    return nf + (ctx - nf * ps + tps - 1) / tps;
+  }
+  __host__ __device__ void range(int ctx, int part, int& start, int& end) const {
+    const int nf = nfull(ctx);
+    if (part < nf) {
+      start = part * ps;
+      end = start + ps;
+    } else {
+      start = nf * ps + (part - nf) * tps;
+      end = start + tps < ctx ? start + tps : ctx;
+    }
+  }
+  // Largest count over contexts 0..max_ctx: count grows with ctx between
+  // multiples of ps and drops at each multiple, so it peaks at max_ctx or
+  // just below the largest multiple of ps not above it.
+  __host__ __device__ int max_count(int max_ctx) const {
+    int m = count(max_ctx);
+    if (max_ctx >= ps) {
+      const int below = count(max_ctx / ps * ps - 1);
+      m = below > m ? below : m;
+    }
+    return m;
+  }
+};
+
 struct DecodeArgs {
   void* out;
   float* out_lse;
@@ -41,19 +76,12 @@ struct DecodeArgs {
   const float* v_scale;
   float* part_out;   // [B][Hq][P][D] fp32, NULL when P == 1
   float* part_lse;   // [B][Hq][P] fp32
+  int32_t* work_counters;  // matrix-core kernel: 2 ints, zero on entry, left zero on completion
   float softmax_scale;
-  int32_t partition_size;
+  PartitionPlan parts;
   int32_t max_context_len;
   int32_t max_partitions;
   lgm_paged_dims dims;
-};
-
-// Balanced decode: records of split segments and their arrival counts.
-struct StreamArgs {
-  int32_t num_waves;       // W: the tiles of all segments are cut into W equal ranges
-  int32_t record_floats;   // floats per record (stream_record_floats(G))
-  float* records;          // [W][2][record_floats]
-  int32_t* counters;       // [B][Hkv], zero on entry, left zero on completion
 };
 
 struct MergeArgs {
@@ -62,8 +90,8 @@ struct MergeArgs {
   const float* part_out;
   const float* part_lse;
   const int32_t* num_partitions;  // per sequence, or NULL
-  const int32_t* context_lens;    // alternative source of the count (with partition_size)
-  int32_t partition_size;
+  const int32_t* context_lens;    // alternative source of the count (parts.count)
+  PartitionPlan parts;
   int32_t max_context_len;
   int32_t num_seqs;
   int32_t num_heads;
@@ -79,14 +107,12 @@ hipError_t launch_lse_merge(const MergeArgs& a, lgm_dtype out_dtype, hipStream_t
 
 // Matrix-core decode for bf16 activations with bf16 / FP8 caches, head_dim 128.
 hipError_t launch_paged_decode_mfma(const DecodeArgs& a, lgm_dtype cache, hipStream_t s);
-// The same shapes with balanced tile ranges, one launch (partition_size 0).
-hipError_t launch_paged_decode_stream(const DecodeArgs& a, const StreamArgs& x, lgm_dtype cache, hipStream_t s);
-int stream_record_floats(int group);
-
-// Minimum resident waves per SIMD the balanced kernel is compiled for; the
-// host cuts the work into (compute units x 4 x this) ranges so that all of
-// them run at once.
-constexpr int stream_waves_per_simd(bool fp8_cache, int group) { return fp8_cache ? 3 : (group <= 4 ? 3 : 2); }
+// Upper bound on the persistent matrix-core kernel's workgroups per compute
+// unit (the grid is compute units x min(this, resident capacity)).
+#ifndef LGM_PERSISTENT_MAX_PER_CU
+#define LGM_PERSISTENT_MAX_PER_CU 2
+#endif
+constexpr int kPersistentMaxPerCU = LGM_PERSISTENT_MAX_PER_CU;
 
 // Shape support queries used by validation (no HIP calls).
 bool decode_supported(lgm_dtype act, lgm_dtype cache, int head_dim, int group, int block_size);

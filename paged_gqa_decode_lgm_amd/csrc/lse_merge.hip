@@ -60,7 +60,7 @@ __global__ __launch_bounds__(kThreads) void lse_merge_kernel(MergeArgs p) {
   } else if (p.context_lens) {
     int ctx = p.context_lens[b];
     ctx = ctx < 0 ? 0 : (ctx > p.max_context_len ? p.max_context_len : ctx);
-    n = ctx == 0 ? 1 : (ctx + p.partition_size - 1) / p.partition_size;
+    n = p.parts.count(ctx);
     n = n > P ? P : n;
   } else {
     n = P;

@@ -95,20 +95,22 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_split_kernel(Deco
   __shared__ float s_m[kNW][G];
   __shared__ float s_l[kNW][G];
 
-  const int part = blockIdx.x;
-  const int g = blockIdx.y;
-  const int b = blockIdx.z;
+  // Partition index slowest: workgroups are dealt to the 8 XCDs by linear id,
+  // and with the partition fastest an XCD would own fixed partition indices,
+  // of which the high ones exist only for the longest sequences.
+  const int g = blockIdx.x;
+  const int b = blockIdx.y;
+  const int part = blockIdx.z;
   const int Hq = p.dims.num_q_heads;
   const int Hkv = p.dims.num_kv_heads;
   const int MB = p.dims.max_blocks_per_seq;
-  const int PS = p.partition_size;
 
   int ctx = p.context_lens[b];
   ctx = ctx < 0 ? 0 : (ctx > p.max_context_len ? p.max_context_len : ctx);
-  const int nparts = ctx == 0 ? 1 : (ctx + PS - 1) / PS;
+  const int nparts = p.parts.count(ctx);
   if (part >= nparts) return;
-  const int start = part * PS;
-  const int end = min(start + PS, ctx);
+  int start, end;
+  p.parts.range(ctx, part, start, end);
 
   const int lane = threadIdx.x & (kWaveSize - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWaveSize);
@@ -283,7 +285,7 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_split_kernel(Deco
 
 template <class C, class A, int D>
 hipError_t dispatch_group(const DecodeArgs& a, int G, hipStream_t s) {
-  const dim3 grid(a.max_partitions, a.dims.num_kv_heads, a.dims.num_seqs);
+  const dim3 grid(a.dims.num_kv_heads, a.dims.num_seqs, a.max_partitions);
   const dim3 block(kDecodeThreads);
 #define LGM_CASE(GV)                                                                    \
   case GV:                                                                              \

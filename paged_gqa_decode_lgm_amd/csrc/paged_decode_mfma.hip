@@ -3,17 +3,28 @@
 //
 // The method is the one of paged_decode.hip (mainarch README, decode-attention
 // section; Loom Kernels README, "Attention" row): partitions of the context
-// processed by independent workgroups with an online softmax, merged by
-// log-sum-exp, each KV row read once for its G query heads.  What changes is
-// how a wave spends its instructions: with G query heads sharing a KV head,
-// the scores of a 16-token block and the probability-weighted sum of V rows
-// are small dense contractions, so both go to v_mfma_f32_16x16x32_bf16 and
-// the vector ALU only runs the softmax bookkeeping.
+// processed independently with an online softmax, merged by log-sum-exp, each
+// KV row read once for its G query heads.  Two things change on this chip.
 //
-// Operand layouts and the per-tile update are in mfma_common.h.  The
-// probabilities enter the MFMA rounded to bf16 and the output is normalised by
-// the sum of those same rounded values, so it is an exact convex combination
-// of V rows up to fp32 accumulation; the log-sum-exp uses the unrounded sum.
+// Arithmetic: with G query heads sharing a KV head, the scores of a 16-token
+// block and the probability-weighted sum of V rows are small dense
+// contractions, so both go to v_mfma_f32_16x16x32_bf16 and the vector ALU only
+// runs the softmax bookkeeping (operand layouts and the per-tile update are in
+// mfma_common.h).  The probabilities enter the MFMA rounded to bf16 and the
+// output is normalised by the sum of those same rounded values, so it is an
+// exact convex combination of V rows up to fp32 accumulation; the log-sum-exp
+// uses the unrounded sum.
+//
+// Scheduling: a grid of one workgroup per (partition, kv head, sequence)
+// dispatches in order, so with ragged batches the empty partitions of short
+// sequences sit between live ones and hold up dispatch, and the workgroups
+// that land on one XCD are fixed in advance even though XCDs do not stream
+// all kv heads at the same speed.  Instead a persistent grid (the resident
+// capacity of the chip) pulls work items from an atomic counter.  The items
+// are the live (sequence, partition, kv head) triples only, the full-size
+// partitions first and the shorter tail partitions last; every workgroup
+// walks the context lengths 64 sequences at a time with a wave prefix sum to
+// turn an item number into its triple.
 #include "mfma_common.h"
 
 namespace lgm {
@@ -21,31 +32,114 @@ namespace {
 
 using namespace mfma;
 
-template <class C, int G>
-__global__ __launch_bounds__(kDecodeThreads, 3) void paged_decode_mfma_kernel(DecodeArgs p) {
-  static_assert(G >= 1 && G <= 16, "group size");
-  __shared__ float s_acc[kNW][G][kD];
-  __shared__ float s_m[kNW][G];
-  __shared__ float s_l[kNW][G];   // sums of the bf16-rounded probabilities (normalise the output)
-  __shared__ float s_le[kNW][G];  // sums of the fp32 probabilities (the log-sum-exp)
+// Item number -> (sequence, partition, kv head).  First come the full
+// partitions of every sequence (phase 0), then the shorter tail partitions
+// that cover the rest of each context (phase 1), so the queue drains on short
+// items.  Within a phase the items of sequence b are consecutive numbers,
+// partition-major, kv head fastest (the kv heads of one partition read the
+// same blocks at about the same time).  Wave 0 walks the context lengths 64
+// sequences at a time with a wave prefix sum; the walk only moves forward (a
+// workgroup's item numbers increase) and its state stays in LDS between
+// items, so none of it occupies registers during the tile loop.
+struct CursorSmem {
+  int incl[kWaveSize];  // inclusive item counts of the chunk's sequences
+  int ctx[kWaveSize];   // their clamped context lengths
+  int phase, base_b, base_item, total;
+};
+struct ItemSlot {
+  int b, part, g, ctx;  // b < 0: no item left
+};
 
-  const int part = blockIdx.x;
-  const int g = blockIdx.y;
-  const int b = blockIdx.z;
+// Loads the chunk of sequences base_b .. base_b + 63 for `phase`; returns its item count.
+__device__ __forceinline__ int cursor_load(const DecodeArgs& p, CursorSmem& cs, int phase, int base_b, int lane) {
+  const int bb = base_b + lane;
+  int c = 0, items = 0;
+  if (bb < p.dims.num_seqs) {
+    c = p.context_lens[bb];
+    c = c < 0 ? 0 : (c > p.max_context_len ? p.max_context_len : c);
+    const int nfull = p.parts.nfull(c);
+    items = (phase == 0 ? nfull : p.parts.count(c) - nfull) * p.dims.num_kv_heads;
+  }
+#pragma unroll
+  for (int o = 1; o < kWaveSize; o <<= 1) {
+    const int t = __shfl_up(items, o);
+    if (lane >= o) items += t;
+  }
+  cs.incl[lane] = items;
+  cs.ctx[lane] = c;
+  return __builtin_amdgcn_readlane(items, kWaveSize - 1);
+}
+
+// Wave 0 only: the triple of `item` into `out`.
+__device__ __forceinline__ void cursor_locate(const DecodeArgs& p, CursorSmem& cs, int item, int lane,
+                                              ItemSlot& out) {
+  int phase = __builtin_amdgcn_readfirstlane(cs.phase);
+  int base_b = __builtin_amdgcn_readfirstlane(cs.base_b);
+  int base_item = __builtin_amdgcn_readfirstlane(cs.base_item);
+  int total = __builtin_amdgcn_readfirstlane(cs.total);
+  bool found = true;
+  while (item >= base_item + total) {
+    base_item += total;
+    if (base_b + kWaveSize < p.dims.num_seqs) {
+      base_b += kWaveSize;
+    } else if (phase == 0) {
+      phase = 1;
+      base_b = 0;
+    } else {
+      total = 0;
+      found = false;
+      break;
+    }
+    total = cursor_load(p, cs, phase, base_b, lane);
+  }
+  int b = -1, part = 0, g = 0, ctx = 0;
+  if (found) {
+    const uint64_t above = __ballot(base_item + cs.incl[lane] > item);
+    const int j = __builtin_ctzll(above);
+    const int excl = j == 0 ? 0 : cs.incl[j - 1];
+    const int r = item - base_item - excl;
+    const int within = r / p.dims.num_kv_heads;
+    g = r - within * p.dims.num_kv_heads;
+    b = base_b + j;
+    ctx = cs.ctx[j];
+    part = phase == 0 ? within : p.parts.nfull(ctx) + within;
+  }
+  if (lane == 0) {
+    cs.phase = phase;
+    cs.base_b = base_b;
+    cs.base_item = base_item;
+    cs.total = total;
+    out.b = b;
+    out.part = part;
+    out.g = g;
+    out.ctx = ctx;
+  }
+}
+
+template <int G>
+struct DecodeSmem {
+  float acc[kNW][G][kD];
+  float m[kNW][G];
+  float l[kNW][G];   // sums of the bf16-rounded probabilities (normalise the output)
+  float le[kNW][G];  // sums of the fp32 probabilities (the log-sum-exp)
+  ItemSlot slot[2];  // the current and the next item, by item parity
+  CursorSmem cursor;
+};
+
+// One item: partition `part` of sequence b (context length ctx) for kv head g.
+// The four waves take the partition's 32-token tiles round-robin, then merge
+// their states through LDS; returns with the results written and sm.acc read
+// by this thread (the caller synchronises before sm is written again), and
+// in thread 0's `next` the number of the workgroup's next item.
+template <class C, int G>
+__device__ __forceinline__ void decode_item(const DecodeArgs& p, DecodeSmem<G>& sm, int b, int g, int part, int ctx,
+                                            int lane, int wave, int tid, int& next) {
   const int Hq = p.dims.num_q_heads;
   const int Hkv = p.dims.num_kv_heads;
   const int MB = p.dims.max_blocks_per_seq;
-  const int PS = p.partition_size;
-
-  int ctx = p.context_lens[b];
-  ctx = ctx < 0 ? 0 : (ctx > p.max_context_len ? p.max_context_len : ctx);
-  const int nparts = ctx == 0 ? 1 : (ctx + PS - 1) / PS;
-  if (part >= nparts) return;
-  const int start = part * PS;
-  const int end = min(start + PS, ctx);
-
-  const int lane = threadIdx.x & (kWaveSize - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWaveSize);
+  const int nparts = p.parts.count(ctx);
+  int start, end;
+  p.parts.range(ctx, part, start, end);
   const int n = lane & 15;
   const int kg = lane >> 4;
 
@@ -132,39 +226,44 @@ __global__ __launch_bounds__(kDecodeThreads, 3) void paged_decode_mfma_kernel(De
     }
   }
 
+  // The next item is taken only now, when this one's loads are all issued:
+  // taken earlier, late items would be claimed long before they start and
+  // the full partitions would no longer all run ahead of the tail ones.
+  if (tid == 0) next = (int)gridDim.x + atomicAdd(p.work_counters, 1);
+
   // Wave epilogue: complete the denominators and publish this wave's state.
   const float lsum = sum4(st.lsum);
   const float lsum_e = sum4(st.lsum_e);
   if (kg == 0 && n < G) {
-    s_m[wave][n] = st.m;
-    s_l[wave][n] = lsum;
-    s_le[wave][n] = lsum_e;
+    sm.m[wave][n] = st.m;
+    sm.l[wave][n] = lsum;
+    sm.le[wave][n] = lsum_e;
   }
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int h = 4 * kg + j;
     if (h < G) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) s_acc[wave][h][8 * n + i] = st.acc[i][j];
+      for (int i = 0; i < 8; ++i) sm.acc[wave][h][8 * n + i] = st.acc[i][j];
     }
   }
   __syncthreads();
 
   const float vscale = C::kFp8 ? p.v_scale[g] : 1.f;
-  for (int idx = threadIdx.x; idx < G * kD; idx += kDecodeThreads) {
+  for (int idx = tid; idx < G * kD; idx += kDecodeThreads) {
     const int h = idx / kD;
     const int d = idx % kD;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kNW; ++w) M = fmaxf(M, s_m[w][h]);
+    for (int w = 0; w < kNW; ++w) M = fmaxf(M, sm.m[w][h]);
     const float ms = M == -INFINITY ? 0.f : M;
     float L = 0.f, Le = 0.f, o = 0.f;
 #pragma unroll
     for (int w = 0; w < kNW; ++w) {
-      const float f = fast_exp2(s_m[w][h] - ms);
-      L += s_l[w][h] * f;
-      Le += s_le[w][h] * f;
-      o += s_acc[w][h][d] * f;
+      const float f = fast_exp2(sm.m[w][h] - ms);
+      L += sm.l[w][h] * f;
+      Le += sm.le[w][h] * f;
+      o += sm.acc[w][h][d] * f;
     }
     o = L > 0.f ? o / L : 0.f;
     o *= vscale;
@@ -180,20 +279,108 @@ __global__ __launch_bounds__(kDecodeThreads, 3) void paged_decode_mfma_kernel(De
   }
 }
 
+// Persistent workgroup: items blockIdx.x, then gridDim.x + (counter value) for
+// every further item.  counters[0] hands out items, counters[1] counts
+// workgroups that have run out of items; the last one to run out puts both
+// back to zero, so the next launch finds them zero.  A workgroup increments
+// counters[1] only after its final fetch from counters[0] has returned (its
+// exit depends on the fetched value), so no fetch follows the reset.
+template <class C, int G>
+__global__ __launch_bounds__(kDecodeThreads, 3) void paged_decode_mfma_kernel(DecodeArgs p) {
+  static_assert(G >= 1 && G <= 16, "group size");
+  __shared__ DecodeSmem<G> sm;
+  const int lane = threadIdx.x & (kWaveSize - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWaveSize);
+  int32_t* counters = p.work_counters;
+
+  if (wave == 0) {
+    const int total = cursor_load(p, sm.cursor, 0, 0, lane);
+    if (lane == 0) {
+      sm.cursor.phase = 0;
+      sm.cursor.base_b = 0;
+      sm.cursor.base_item = 0;
+      sm.cursor.total = total;
+    }
+    cursor_locate(p, sm.cursor, blockIdx.x, lane, sm.slot[0]);
+  }
+  __syncthreads();
+  for (int k = 0;; ++k) {
+    const ItemSlot& sl = sm.slot[k & 1];
+    const int b = __builtin_amdgcn_readfirstlane(sl.b);
+    if (b < 0) break;
+    const int part = __builtin_amdgcn_readfirstlane(sl.part);
+    const int g = __builtin_amdgcn_readfirstlane(sl.g);
+    const int ctx = __builtin_amdgcn_readfirstlane(sl.ctx);
+    int next = 0;
+    // Lane-derived addresses are loop-invariant; recomputing them per item
+    // (instead of keeping them live across every tile) keeps the tile loop
+    // within the registers of three resident workgroups per CU.
+    int lane_i = lane, tid_i = threadIdx.x;
+    asm volatile("" : "+v"(lane_i), "+v"(tid_i));
+    decode_item<C, G>(p, sm, b, g, part, ctx, lane_i, wave, tid_i, next);
+    if (wave == 0) cursor_locate(p, sm.cursor, __builtin_amdgcn_readlane(next, 0), lane_i, sm.slot[(k + 1) & 1]);
+    __syncthreads();
+  }
+  if (threadIdx.x == 0 && atomicAdd(counters + 1, 1) == (int)gridDim.x - 1) {
+    atomicExch(counters, 0);
+    atomicExch(counters + 1, 0);
+  }
+}
+
+// Resident workgroups per compute unit of each instantiation, queried once.
+template <class C, int G>
+int resident_per_cu() {
+  static const int occ = [] {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, paged_decode_mfma_kernel<C, G>, kDecodeThreads, 0) !=
+            hipSuccess ||
+        n < 1)
+      n = 1;
+    return n;
+  }();
+  return occ;
+}
+
+template <class C, int G>
+hipError_t launch_persistent(const DecodeArgs& a, int compute_units, hipStream_t s) {
+  const int64_t per_cu = resident_per_cu<C, G>();
+  const int64_t upper = (int64_t)a.dims.num_seqs * a.dims.num_kv_heads * a.max_partitions;
+  int64_t grid = compute_units * (per_cu < kPersistentMaxPerCU ? per_cu : kPersistentMaxPerCU);
+  if (grid > upper) grid = upper;
+  if (grid < 1) grid = 1;
+  hipLaunchKernelGGL((paged_decode_mfma_kernel<C, G>), dim3((unsigned)grid), dim3(kDecodeThreads), 0, s, a);
+  return hipGetLastError();
+}
+
 template <class C>
-hipError_t dispatch(const DecodeArgs& a, int G, hipStream_t s) {
-  const dim3 grid(a.max_partitions, a.dims.num_kv_heads, a.dims.num_seqs);
-  const dim3 block(kDecodeThreads);
+hipError_t dispatch(const DecodeArgs& a, int G, int compute_units, hipStream_t s) {
   switch (G) {
 #define LGM_CASE(GV) \
-  case GV: hipLaunchKernelGGL((paged_decode_mfma_kernel<C, GV>), grid, block, 0, s, a); break;
+  case GV:           \
+    return launch_persistent<C, GV>(a, compute_units, s);
     LGM_CASE(1) LGM_CASE(2) LGM_CASE(3) LGM_CASE(4) LGM_CASE(5) LGM_CASE(6) LGM_CASE(7) LGM_CASE(8)
     LGM_CASE(9) LGM_CASE(10) LGM_CASE(11) LGM_CASE(12) LGM_CASE(13) LGM_CASE(14) LGM_CASE(15) LGM_CASE(16)
 #undef LGM_CASE
     default:
       return hipErrorInvalidValue;
   }
-  return hipGetLastError();
+}
+
+// Compute units of the device a stream runs on, queried once per device.
+int compute_units_of(hipStream_t s) {
+  constexpr int kMaxDevices = 64;
+  static int cache[kMaxDevices] = {};
+  int dev = 0;
+  if (s == nullptr || hipStreamGetDevice(s, &dev) != hipSuccess) {
+    if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  }
+  if (dev < 0 || dev >= kMaxDevices) dev = 0;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) n = 1;
+    cache[dev] = n;
+  }
+  return cache[dev];
 }
 
 }  // namespace
@@ -205,8 +392,9 @@ bool decode_mfma_supported(lgm_dtype act, lgm_dtype cache, int head_dim, int gro
 
 hipError_t launch_paged_decode_mfma(const DecodeArgs& a, lgm_dtype cache, hipStream_t s) {
   const int G = a.dims.num_q_heads / a.dims.num_kv_heads;
-  if (cache == LGM_BF16) return dispatch<MfmaBF16>(a, G, s);
-  if (cache == LGM_FP8_E4M3) return dispatch<MfmaFP8>(a, G, s);
+  const int cus = compute_units_of(s);
+  if (cache == LGM_BF16) return dispatch<MfmaBF16>(a, G, cus, s);
+  if (cache == LGM_FP8_E4M3) return dispatch<MfmaFP8>(a, G, cus, s);
   return hipErrorInvalidValue;
 }
 

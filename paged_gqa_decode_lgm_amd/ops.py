@@ -71,7 +71,7 @@ def paged_decode_attn(q, k_cache, v_cache, block_tables, context_lens, max_conte
         out_lse = torch.empty((bsz, hq), dtype=torch.float32, device=q.device)
     need = B.lgm_paged_decode_workspace_size(dims, max_context_len, partition_size, lgm_dtype(k_cache))
     if workspace is None and need:
-        # zero-filled: the balanced plan keeps arrival counters in it
+        # zero-filled: the matrix-core kernel keeps its work counters at its start
         workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     B.lgm_paged_decode_attn(out, out_lse, q, q.stride(0), k_cache, v_cache, block_tables, context_lens, k_scale,

@@ -143,10 +143,12 @@ def test_attention_empty_batch_is_a_noop():
 
 # ------------------------------------------------------------------ plan queries
 @pytest.mark.parametrize("d,max_ctx,ps,want", [
-    (dims(), 8192, 0, 0),                                                 # Llama-3-8B-shaped: balanced ranges
-    (dims(num_seqs=128, max_blocks_per_seq=256), 4096, 0, 0),             # FP8 config: balanced ranges
-    (dims(num_seqs=2, num_q_heads=12, num_kv_heads=2, max_blocks_per_seq=128), 2048, 0, 0),
-    (dims(head_dim=64), 8192, 0, 512),                                    # vector-ALU shape: fixed partitions
+    (dims(), 8192, 0, 2048),                                              # Llama-3-8B-shaped batch
+    (dims(num_seqs=128, max_blocks_per_seq=256), 4096, 0, 2048),          # FP8-cache batch
+    (dims(num_seqs=4, max_blocks_per_seq=8192), 131072, 0, 2048),         # long contexts
+    (dims(num_seqs=256), 8192, 0, 4096),
+    (dims(num_seqs=2, num_q_heads=12, num_kv_heads=2, max_blocks_per_seq=128), 2048, 0, 64),
+    (dims(head_dim=64), 8192, 0, 512),                                    # vector-ALU shape
     (dims(num_seqs=2, num_q_heads=12, num_kv_heads=2, head_dim=64, max_blocks_per_seq=128), 2048, 0, 64),
     (dims(num_seqs=4, max_blocks_per_seq=8192), 131072, 512, 512),         # explicit
     (dims(num_seqs=1, num_q_heads=4, num_kv_heads=1, head_dim=64, max_blocks_per_seq=16), 256, 256, 256),
@@ -157,29 +159,47 @@ def test_partition_plan(d, max_ctx, ps, want):
     assert L.lgm_paged_decode_partition_size(d, max_ctx, ps, L.LGM_BF16) == want
 
 
-def test_balanced_workspace_size_formula():
-    al = lambda x: (x + 255) // 256 * 256
-    d = dims()                                     # bf16, G = 4: records of 16 lanes x 32 floats + 48, padded to 576
-    W = 3072                                       # 12 resident waves x 256 CUs (64*8*256 tiles / 2 exceeds it)
-    assert L.lgm_paged_decode_workspace_size(d, 8192, 0, L.LGM_BF16) == al(W * 2 * 576 * 4) + al(64 * 8 * 4)
-    W8 = 3072
-    assert L.lgm_paged_decode_workspace_size(d, 8192, 0, L.LGM_FP8_E4M3) == al(W8 * 2 * 576 * 4) + al(64 * 8 * 4)
-    small = dims(num_seqs=2, num_q_heads=12, num_kv_heads=2, max_blocks_per_seq=128)  # G = 6: 2 lane rows
-    W2 = (2 * 2 * 64 + 1) // 2
-    assert L.lgm_paged_decode_workspace_size(small, 2048, 0, L.LGM_BF16) == al(W2 * 2 * 1088 * 4) + al(2 * 2 * 4)
+def partitions_brute_force(max_ctx, ps, tps):
+    """Most partitions any context 0..max_ctx is cut into: its full partitions
+    of ps tokens plus the rest in partitions of tps tokens (one if empty)."""
+    return max(1 if c == 0 else c // ps + -(-(c % ps) // tps) for c in range(max_ctx + 1))
 
 
 def test_workspace_size_formula():
-    d = dims()
-    assert L.lgm_paged_decode_workspace_size(d, 8192, 8192, L.LGM_BF16) == 0     # one partition
-    P = 16
+    al = lambda x: (x + 255) // 256 * 256
+    d = dims()                                     # matrix-core shape: 256 bytes of work counters first
+    assert L.lgm_paged_decode_workspace_size(d, 8192, 8192, L.LGM_BF16) == 256     # one partition
+    assert L.lgm_paged_decode_workspace_size(d, 8192, 8192, L.LGM_FP8_E4M3) == 256
+    P = partitions_brute_force(8192, 512, 256)     # tails in half partitions
+    assert P == 17
     out_b = 64 * 32 * P * 128 * 4
     lse_b = 64 * 32 * P * 4
+    assert L.lgm_paged_decode_workspace_size(d, 8192, 512, L.LGM_BF16) == 256 + al(out_b) + al(lse_b)
+    v = dims(head_dim=64)                          # vector-ALU shape: partials only
+    assert L.lgm_paged_decode_workspace_size(v, 8192, 8192, L.LGM_BF16) == 0
+    assert L.lgm_paged_decode_workspace_size(v, 8192, 512, L.LGM_BF16) == al(64 * 32 * P * 64 * 4) + al(lse_b)
+
+
+@pytest.mark.parametrize("max_ctx,ps", [(100, 16), (100, 64), (1000, 96), (3000, 512), (4096, 1024), (17, 16),
+                                        (5000, 4096), (2048, 2048)])
+def test_partition_count_bound(max_ctx, ps):
+    """The library's partition count bound equals the brute-force maximum."""
+    tps = ps if max_ctx <= ps else max(16, ps // 2 // 16 * 16)
+    P = partitions_brute_force(max_ctx, ps, tps)
+    d = dims(head_dim=64, max_blocks_per_seq=(max_ctx + 15) // 16)
     al = lambda x: (x + 255) // 256 * 256
-    assert L.lgm_paged_decode_workspace_size(d, 8192, 512, L.LGM_BF16) == al(out_b) + al(lse_b)
+    want = 0 if P == 1 else al(64 * 32 * P * 64 * 4) + al(64 * 32 * P * 4)
+    assert L.lgm_paged_decode_workspace_size(d, max_ctx, ps, L.LGM_BF16) == want
     assert L.lgm_last_error() == ""
     with pytest.raises(L.LgmError):
         L.lgm_paged_decode_workspace_size(d, 8192, 10, L.LGM_BF16)
+
+
+def test_too_many_partitions_is_unsupported():
+    d = dims(num_seqs=1, max_blocks_per_seq=1 << 17)
+    with pytest.raises(L.LgmError) as e:
+        L.lgm_paged_decode_workspace_size(d, 1 << 21, 16, L.LGM_BF16)
+    assert "partitions: at most 65535" in e.value.message
 
 
 # ------------------------------------------------------------------ merge

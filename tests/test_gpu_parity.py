@@ -277,40 +277,42 @@ def test_inactive_sequence_append_writes_nothing():
 
 
 @pytest.mark.parametrize("name", ["llama3_8b_gqa", "fp8_kv"])
-def test_balanced_workspace_is_reusable_and_left_zeroed(name):
-    """Balanced ranges keep arrival counters in the workspace: a zero-filled
-    workspace reused by consecutive calls must give identical results and be
-    left with every counter back at zero."""
+@pytest.mark.parametrize("ps", [0, 64])
+def test_persistent_workspace_is_reusable_and_left_zeroed(name, ps):
+    """The matrix-core kernel hands out work items from two counters at the
+    start of the workspace: a zero-filled workspace reused by consecutive calls
+    must give identical results and be left with both counters back at zero."""
     cfg = W.CONFIGS[name].with_(num_seqs=12, ctx=(1, 3000), num_blocks=None, append=False)
     w = W.make_workload(cfg)
     d = to_device(w)
     q = q_from_qkv(w).cuda()
     mc = d.max_ctx
-    assert ops.partition_size(q, d.k_pool, d.block_tables, mc, 0) == 0
-    nbytes = ops.workspace_bytes(q, d.k_pool, d.block_tables, mc, 0)
+    nbytes = ops.workspace_bytes(q, d.k_pool, d.block_tables, mc, ps)
     ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
-    announce("balanced workspace reuse", name, nbytes)
+    announce("persistent workspace reuse", name, ps, nbytes)
     outs = []
     for _ in range(3):
         o, l = ops.paged_decode_attn(q, d.k_pool, d.v_pool, d.block_tables, d.context_lens, mc,
-                                     softmax_scale=cfg.softmax_scale, partition_size=0, k_scale=d.k_scale,
+                                     softmax_scale=cfg.softmax_scale, partition_size=ps, k_scale=d.k_scale,
                                      v_scale=d.v_scale, workspace=ws)
         outs.append((o.clone(), l.clone()))
     torch.cuda.synchronize()
     for o, l in outs[1:]:
         assert torch.equal(o.view(torch.int16), outs[0][0].view(torch.int16)) and torch.equal(l, outs[0][1])
-    counters = ws[nbytes - ((cfg.num_seqs * cfg.num_kv_heads * 4 + 255) // 256 * 256):].view(torch.int32)
-    assert int(counters.abs().sum()) == 0
+    assert int(ws[:256].view(torch.int32).abs().sum()) == 0
     r_out, r_lse = oracle_attention(w, act_raw(w, q_from_qkv(w)), pool_raw(w, w.k_pool), pool_raw(w, w.v_pool))
     assert max_abs(out_values(cfg, outs[0][0]), r_out) <= TOL["bf16"]
     _lse_check(outs[0][1].cpu().numpy(), r_lse)
 
 
-def test_balanced_many_short_sequences_and_empty_ones():
-    """Many segments per range (short contexts), zero-length sequences mixed in,
-    more ranges than tiles for the smallest batch."""
-    ctx = tuple([0, 1, 5, 31, 32, 33, 0, 64, 100, 17] * 7)
-    cfg = W.CONFIGS["llama3_8b_gqa"].with_(num_seqs=len(ctx), ctx_list=ctx, num_blocks=None, append=False)
+@pytest.mark.parametrize("ps", [0, 16, 32])
+def test_persistent_many_short_sequences_and_empty_ones(ps):
+    """Short and zero-length contexts across more than three 64-sequence chunks
+    of the work-item walk, with one to several items per sequence; and a
+    batch with fewer work items than workgroups."""
+    ctx = tuple([0, 1, 5, 31, 32, 33, 0, 64, 100, 17] * 21)
+    cfg = W.CONFIGS["llama3_8b_gqa"].with_(num_seqs=len(ctx), ctx_list=ctx, num_blocks=None, append=False,
+                                           partition_size=ps)
     _run_and_check(cfg)
     cfg1 = W.CONFIGS["qwen2.5_1.5b_gqa"].with_(num_seqs=1, ctx_list=(40,), num_blocks=None, append=False)
     _run_and_check(cfg1)
