@@ -118,175 +118,199 @@ __device__ __forceinline__ void cursor_locate(const DecodeArgs& p, CursorSmem& c
 
 template <int G>
 struct DecodeSmem {
-  float acc[kNW][G][kD];
-  float m[kNW][G];
-  float l[kNW][G];   // sums of the bf16-rounded probabilities (normalise the output)
-  float le[kNW][G];  // sums of the fp32 probabilities (the log-sum-exp)
-  ItemSlot slot[2];  // the current and the next item, by item parity
+  // Wave states of an item, double-buffered by item parity: the next item's
+  // waves write one buffer while the other still holds this item's states.
+  float acc[2][kNW][G][kD];
+  float m[2][kNW][G];
+  float l[2][kNW][G];   // sums of the bf16-rounded probabilities (normalise the output)
+  float le[2][kNW][G];  // sums of the fp32 probabilities (the log-sum-exp)
+  ItemSlot slot[2];     // the current and the next item, by item parity
   CursorSmem cursor;
 };
 
-// One item: partition `part` of sequence b (context length ctx) for kv head g.
-// The four waves take the partition's 32-token tiles round-robin, then merge
-// their states through LDS; returns with the results written and sm.acc read
-// by this thread (the caller synchronises before sm is written again), and
-// in thread 0's `next` the number of the workgroup's next item.
-template <class C, int G>
-__device__ __forceinline__ void decode_item(const DecodeArgs& p, DecodeSmem<G>& sm, int b, int g, int part, int ctx,
-                                            int lane, int wave, int tid, int& next) {
-  const int Hq = p.dims.num_q_heads;
-  const int Hkv = p.dims.num_kv_heads;
+// One item's values, uniform across the workgroup.
+struct Item {
+  int b, g, part, nparts, start, end, ntiles;
+};
+
+__device__ __forceinline__ Item read_item(const DecodeArgs& p, const ItemSlot& sl) {
+  Item it;
+  it.b = __builtin_amdgcn_readfirstlane(sl.b);
+  it.g = __builtin_amdgcn_readfirstlane(sl.g);
+  it.part = __builtin_amdgcn_readfirstlane(sl.part);
+  const int ctx = __builtin_amdgcn_readfirstlane(sl.ctx);
+  it.nparts = p.parts.count(ctx);
+  p.parts.range(ctx, it.part, it.start, it.end);
+  it.ntiles = (it.end - it.start + kTile - 1) / kTile;
+  return it;
+}
+
+// Tiles of the item this wave takes: wave, wave + 4, ...
+__device__ __forceinline__ int wave_tiles(const Item& it, int wave) {
+  return it.ntiles > wave ? (it.ntiles - wave + kNW - 1) / kNW : 0;
+}
+
+// Block ids of this wave's tiles k0 .. k0 + 31 of the item, one per lane
+// (lane 2k + h holds block h of the wave's tile k0 + k), read back with
+// readlane so no table load sits between a tile and its K/V loads.  -1 marks
+// an absent block (past the end) or an out-of-range table entry.
+__device__ __forceinline__ int preload_ids(const DecodeArgs& p, const Item& it, int k0, int lane, int wave) {
   const int MB = p.dims.max_blocks_per_seq;
-  const int nparts = p.parts.count(ctx);
-  int start, end;
-  p.parts.range(ctx, part, start, end);
-  const int n = lane & 15;
-  const int kg = lane >> 4;
+  const __amdgpu_buffer_rsrc_t bt_rs = span_rsrc(p.block_tables + (int64_t)it.b * MB, MB * 4);
+  const int t = wave + kNW * (k0 + (lane >> 1));
+  const int lb = it.start / kBS + 2 * t + (lane & 1);
+  const int lb_end = (it.end + kBS - 1) / kBS;
+  const int id = buf_load4(bt_rs, 4 * (lb < MB ? lb : 0));
+  return (t < it.ntiles && lb < lb_end && (unsigned)id < (unsigned)p.dims.num_blocks) ? id : -1;
+}
 
-  // Query rows as the B operand of the score MFMAs (bf16 bit patterns).
-  short8 qb[4];
-  {
-    const bool qvec = ((uintptr_t)p.q % 16 == 0) && (p.q_seq_stride % 8 == 0);
-    const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + (int64_t)b * p.q_seq_stride + (int64_t)g * G * kD;
-    load_q_operand<C, G>(qb, qrow, qvec, n, kg);
-  }
-  float sscale = p.softmax_scale * kLog2e;
-  if constexpr (C::kFp8) sscale *= p.k_scale[g];
-
-  WaveState st;
-  st.reset();
-
-  const int32_t* bt = p.block_tables + (int64_t)b * MB;
-  const int tok_bytes = Hkv * kD * C::kElemBytes;
+// Every tile issues the same loads: an absent or invalid block reads the
+// tile's other block (or block 0) instead and is masked, so the load count
+// per tile is fixed and the compiler can wait for K without waiting for V.
+template <class C>
+__device__ __forceinline__ void load_tile_k(const DecodeArgs& p, int g, int px, int py, int lane, TileRegs<C>& tr) {
+  const int tok_bytes = p.dims.num_kv_heads * kD * C::kElemBytes;
   const int64_t block_bytes = (int64_t)kBS * tok_bytes;
-  const int k_off = C::k_lane_off(g, tok_bytes, n, kg);
-  const int v_off = C::v_lane_off(g, tok_bytes, n, kg);
-  const unsigned nblocks = (unsigned)p.dims.num_blocks;
-  const int lb_end = (end + kBS - 1) / kBS;
+  const int off = C::k_lane_off(g, tok_bytes, lane & 15, lane >> 4);
+  const int ex = px >= 0 ? px : 0, ey = py >= 0 ? py : ex;
+  C::load_k(tr.kx, block_rsrc(p.k_cache, block_bytes, ex), off, tok_bytes);
+  C::load_k(tr.ky, block_rsrc(p.k_cache, block_bytes, ey), off, tok_bytes);
+}
+template <class C>
+__device__ __forceinline__ void load_tile_v(const DecodeArgs& p, int g, int px, int py, int lane, TileRegs<C>& tr) {
+  const int tok_bytes = p.dims.num_kv_heads * kD * C::kElemBytes;
+  const int64_t block_bytes = (int64_t)kBS * tok_bytes;
+  const int off = C::v_lane_off(g, tok_bytes, lane & 15, lane >> 4);
+  const int ex = px >= 0 ? px : 0, ey = py >= 0 ? py : ex;
+  C::load_v(tr.vx, block_rsrc(p.v_cache, block_bytes, ex), off, tok_bytes);
+  C::load_v(tr.vy, block_rsrc(p.v_cache, block_bytes, ey), off, tok_bytes);
+}
 
-  const int lb0 = start / kBS;
-  const int ntiles = (end - start + kTile - 1) / kTile;
-  // Block ids of this wave's tiles, preloaded 32 tiles at a time into one
-  // register (lane 2k + h holds block h of the wave's k-th tile) and read back
-  // with readlane: no table load sits between a tile and its K/V loads.
-  // -1 marks an absent block (past the end) or an out-of-range table entry.
-  const __amdgpu_buffer_rsrc_t bt_rs = span_rsrc(bt, MB * 4);
-  auto preload_ids = [&](int k0) -> int {
-    const int t = wave + kNW * (k0 + (lane >> 1));
-    const int lb = lb0 + 2 * t + (lane & 1);
-    const int id = buf_load4(bt_rs, 4 * (lb < MB ? lb : 0));
-    return (t < ntiles && lb < lb_end && (unsigned)id < nblocks) ? id : -1;
-  };
-  // Every tile issues the same loads: an absent or invalid block reads the
-  // tile's other block (or block 0) instead and is masked, so the load count
-  // per tile is fixed and the compiler can wait for K without waiting for V.
-  auto tile_ids = [&](int ids, int k, int& px, int& py) {
-    px = __builtin_amdgcn_readlane(ids, 2 * (k & 31));
-    py = __builtin_amdgcn_readlane(ids, 2 * (k & 31) + 1);
-  };
-
-  // One register set per operand: the next tile's K loads are issued as soon
-  // as the score MFMAs have consumed the current K, and its V loads as soon as
-  // the output MFMAs have consumed the current V, so loads stay in flight
-  // through all of a tile's arithmetic.
-  TileRegs<C> tr;
-  const int my_tiles = ntiles > wave ? (ntiles - wave + kNW - 1) / kNW : 0;
-  if (my_tiles > 0) {
-    int ids = preload_ids(0);
-    int px, py;
-    tile_ids(ids, 0, px, py);
-    int ex = px >= 0 ? px : 0, ey = py >= 0 ? py : ex;
-    C::load_k(tr.kx, block_rsrc(p.k_cache, block_bytes, ex), k_off, tok_bytes);
-    C::load_k(tr.ky, block_rsrc(p.k_cache, block_bytes, ey), k_off, tok_bytes);
-    __builtin_amdgcn_sched_barrier(0);  // K before V, as inside the loop
-    C::load_v(tr.vx, block_rsrc(p.v_cache, block_bytes, ex), v_off, tok_bytes);
-    C::load_v(tr.vy, block_rsrc(p.v_cache, block_bytes, ey), v_off, tok_bytes);
-    for (int k = 0; k < my_tiles; ++k) {
-      const int t = wave + kNW * k;
-      float4v sx, sy;
-      tile_scores<C>(tr, qb, sx, sy);
-      // Next tile's K.  After the last tile the current blocks are read again
-      // (cache hits, results unused) so that every iteration issues the same
-      // loads in the same order and the compiler can wait for K alone.
-      const bool more = k + 1 < my_tiles;
-      int nx = px, ny = py;
-      if (more) {
-        if (((k + 1) & 31) == 0) ids = preload_ids(k + 1);
-        tile_ids(ids, k + 1, nx, ny);
-        ex = nx >= 0 ? nx : 0;
-        ey = ny >= 0 ? ny : ex;
-      }
-      C::load_k(tr.kx, block_rsrc(p.k_cache, block_bytes, ex), k_off, tok_bytes);
-      C::load_k(tr.ky, block_rsrc(p.k_cache, block_bytes, ey), k_off, tok_bytes);
-      tile_update<C>(st, tr, sx, sy, sscale, px >= 0, py >= 0, start + kTile * t, end, kg);
-      C::load_v(tr.vx, block_rsrc(p.v_cache, block_bytes, ex), v_off, tok_bytes);
-      C::load_v(tr.vy, block_rsrc(p.v_cache, block_bytes, ey), v_off, tok_bytes);
-      px = nx;
-      py = ny;
-    }
+// Starts an item for this wave: the query operand, the block ids of its
+// first 32 tiles and the K/V loads of its first tile are issued here, so
+// that they are in flight while the previous item is merged and stored.
+template <class C, int G>
+__device__ __forceinline__ void begin_item(const DecodeArgs& p, const Item& it, int lane, int wave, short8 (&qb)[4],
+                                           int& ids, int& px, int& py, TileRegs<C>& tr) {
+  const bool qvec = ((uintptr_t)p.q % 16 == 0) && (p.q_seq_stride % 8 == 0);
+  const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + (int64_t)it.b * p.q_seq_stride + (int64_t)it.g * G * kD;
+  load_q_operand<C, G>(qb, qrow, qvec, lane & 15, lane >> 4);
+  if (wave_tiles(it, wave) > 0) {
+    ids = preload_ids(p, it, 0, lane, wave);
+    px = __builtin_amdgcn_readlane(ids, 0);
+    py = __builtin_amdgcn_readlane(ids, 1);
+    load_tile_k<C>(p, it.g, px, py, lane, tr);
+    __builtin_amdgcn_sched_barrier(0);  // K before V, as inside the tile loop
+    load_tile_v<C>(p, it.g, px, py, lane, tr);
   }
+}
 
-  // The next item is taken only now, when this one's loads are all issued:
-  // taken earlier, late items would be claimed long before they start and
-  // the full partitions would no longer all run ahead of the tail ones.
-  if (tid == 0) next = (int)gridDim.x + atomicAdd(p.work_counters, 1);
+// The wave's tiles of an item into st.  One register set per operand: the
+// next tile's K loads are issued as soon as the score MFMAs have consumed the
+// current K, and its V loads as soon as the output MFMAs have consumed the
+// current V, so loads stay in flight through all of a tile's arithmetic.
+// Wave 0's lane 0 claims the workgroup's next item two tiles before the end
+// (into `next`): late enough that items are claimed in about the order they
+// start, early enough that the claim is back before the merge needs it.
+template <class C, int G>
+__device__ __forceinline__ void run_tiles(const DecodeArgs& p, const Item& it, int lane, int wave,
+                                          const short8 (&qb)[4], int ids, int px, int py, TileRegs<C>& tr,
+                                          WaveState& st, int& next) {
+  float sscale = p.softmax_scale * kLog2e;
+  if constexpr (C::kFp8) sscale *= p.k_scale[it.g];
+  const int my_tiles = wave_tiles(it, wave);
+  const int claim_at = my_tiles > 2 ? my_tiles - 2 : 0;
+  const bool claimer = wave == 0;
+  if (claimer && my_tiles == 0 && lane == 0) next = (int)gridDim.x + atomicAdd(p.work_counters, 1);
+  for (int k = 0; k < my_tiles; ++k) {
+    if (claimer && k == claim_at && lane == 0) next = (int)gridDim.x + atomicAdd(p.work_counters, 1);
+    const int t = wave + kNW * k;
+    float4v sx, sy;
+    tile_scores<C>(tr, qb, sx, sy);
+    // Next tile's K.  After the last tile the current blocks are read again
+    // (cache hits, results unused) so that every iteration issues the same
+    // loads in the same order and the compiler can wait for K alone.
+    int nx = px, ny = py;
+    if (k + 1 < my_tiles) {
+      if (((k + 1) & 31) == 0) ids = preload_ids(p, it, k + 1, lane, wave);
+      nx = __builtin_amdgcn_readlane(ids, 2 * ((k + 1) & 31));
+      ny = __builtin_amdgcn_readlane(ids, 2 * ((k + 1) & 31) + 1);
+    }
+    load_tile_k<C>(p, it.g, nx, ny, lane, tr);
+    tile_update<C>(st, tr, sx, sy, sscale, px >= 0, py >= 0, it.start + kTile * t, it.end, lane >> 4);
+    load_tile_v<C>(p, it.g, nx, ny, lane, tr);
+    px = nx;
+    py = ny;
+  }
+}
 
-  // Wave epilogue: complete the denominators and publish this wave's state.
+// Wave epilogue: complete the denominators and publish this wave's state.
+template <int G>
+__device__ __forceinline__ void publish_state(DecodeSmem<G>& sm, int buf, const WaveState& st, int lane, int wave) {
+  const int n = lane & 15, kg = lane >> 4;
   const float lsum = sum4(st.lsum);
   const float lsum_e = sum4(st.lsum_e);
   if (kg == 0 && n < G) {
-    sm.m[wave][n] = st.m;
-    sm.l[wave][n] = lsum;
-    sm.le[wave][n] = lsum_e;
+    sm.m[buf][wave][n] = st.m;
+    sm.l[buf][wave][n] = lsum;
+    sm.le[buf][wave][n] = lsum_e;
   }
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int h = 4 * kg + j;
     if (h < G) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) sm.acc[wave][h][8 * n + i] = st.acc[i][j];
+      for (int i = 0; i < 8; ++i) sm.acc[buf][wave][h][8 * n + i] = st.acc[i][j];
     }
   }
-  __syncthreads();
+}
 
-  const float vscale = C::kFp8 ? p.v_scale[g] : 1.f;
+// Merges the four wave states of an item and writes the final output (one
+// partition) or the partition's record.
+template <class C, int G>
+__device__ __forceinline__ void merge_and_store(const DecodeArgs& p, const DecodeSmem<G>& sm, int buf, const Item& it,
+                                                int tid) {
+  const float vscale = C::kFp8 ? p.v_scale[it.g] : 1.f;
   for (int idx = tid; idx < G * kD; idx += kDecodeThreads) {
     const int h = idx / kD;
     const int d = idx % kD;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kNW; ++w) M = fmaxf(M, sm.m[w][h]);
+    for (int w = 0; w < kNW; ++w) M = fmaxf(M, sm.m[buf][w][h]);
     const float ms = M == -INFINITY ? 0.f : M;
     float L = 0.f, Le = 0.f, o = 0.f;
 #pragma unroll
     for (int w = 0; w < kNW; ++w) {
-      const float f = fast_exp2(sm.m[w][h] - ms);
-      L += sm.l[w][h] * f;
-      Le += sm.le[w][h] * f;
-      o += sm.acc[w][h][d] * f;
+      const float f = fast_exp2(sm.m[buf][w][h] - ms);
+      L += sm.l[buf][w][h] * f;
+      Le += sm.le[buf][w][h] * f;
+      o += sm.acc[buf][w][h][d] * f;
     }
     o = L > 0.f ? o / L : 0.f;
     o *= vscale;
     const float lse = Le > 0.f ? (ms + fast_log2(Le)) * kLn2 : -INFINITY;
-    const int64_t row = (int64_t)b * Hq + g * G + h;
-    if (nparts == 1) {
+    const int64_t row = (int64_t)it.b * p.dims.num_q_heads + it.g * G + h;
+    if (it.nparts == 1) {
       static_cast<uint16_t*>(p.out)[row * kD + d] = f32_to_bf16_rne(o);
       if (d == 0 && p.out_lse) p.out_lse[row] = lse;
     } else {
-      p.part_out[(row * p.max_partitions + part) * kD + d] = o;
-      if (d == 0) p.part_lse[row * p.max_partitions + part] = lse;
+      p.part_out[(row * p.max_partitions + it.part) * kD + d] = o;
+      if (d == 0) p.part_lse[row * p.max_partitions + it.part] = lse;
     }
   }
 }
 
 // Persistent workgroup: items blockIdx.x, then gridDim.x + (counter value) for
-// every further item.  counters[0] hands out items, counters[1] counts
+// every further item.  Per item the four waves run their tiles, publish their
+// states and meet at one barrier, behind which wave 0 has placed the next
+// item; each wave then starts the next item's loads before merging and
+// storing this one.  counters[0] hands out items, counters[1] counts
 // workgroups that have run out of items; the last one to run out puts both
 // back to zero, so the next launch finds them zero.  A workgroup increments
 // counters[1] only after its final fetch from counters[0] has returned (its
 // exit depends on the fetched value), so no fetch follows the reset.
 template <class C, int G>
-__global__ __launch_bounds__(kDecodeThreads, 3) void paged_decode_mfma_kernel(DecodeArgs p) {
+__global__ __launch_bounds__(kDecodeThreads, 2) void paged_decode_mfma_kernel(DecodeArgs p) {
   static_assert(G >= 1 && G <= 16, "group size");
   __shared__ DecodeSmem<G> sm;
   const int lane = threadIdx.x & (kWaveSize - 1);
@@ -304,22 +328,28 @@ __global__ __launch_bounds__(kDecodeThreads, 3) void paged_decode_mfma_kernel(De
     cursor_locate(p, sm.cursor, blockIdx.x, lane, sm.slot[0]);
   }
   __syncthreads();
-  for (int k = 0;; ++k) {
-    const ItemSlot& sl = sm.slot[k & 1];
-    const int b = __builtin_amdgcn_readfirstlane(sl.b);
-    if (b < 0) break;
-    const int part = __builtin_amdgcn_readfirstlane(sl.part);
-    const int g = __builtin_amdgcn_readfirstlane(sl.g);
-    const int ctx = __builtin_amdgcn_readfirstlane(sl.ctx);
-    int next = 0;
+  Item it = read_item(p, sm.slot[0]);
+  short8 qb[4];
+  TileRegs<C> tr;
+  int ids = 0, px = -1, py = -1;
+  if (it.b >= 0) begin_item<C, G>(p, it, lane, wave, qb, ids, px, py, tr);
+  for (int k = 0; it.b >= 0; ++k) {
     // Lane-derived addresses are loop-invariant; recomputing them per item
     // (instead of keeping them live across every tile) keeps the tile loop
-    // within the registers of three resident workgroups per CU.
+    // within its register budget.
     int lane_i = lane, tid_i = threadIdx.x;
     asm volatile("" : "+v"(lane_i), "+v"(tid_i));
-    decode_item<C, G>(p, sm, b, g, part, ctx, lane_i, wave, tid_i, next);
+    WaveState st;
+    st.reset();
+    int next = 0;
+    run_tiles<C, G>(p, it, lane_i, wave, qb, ids, px, py, tr, st, next);
+    publish_state<G>(sm, k & 1, st, lane_i, wave);
     if (wave == 0) cursor_locate(p, sm.cursor, __builtin_amdgcn_readlane(next, 0), lane_i, sm.slot[(k + 1) & 1]);
     __syncthreads();
+    const Item nx = read_item(p, sm.slot[(k + 1) & 1]);
+    if (nx.b >= 0) begin_item<C, G>(p, nx, lane_i, wave, qb, ids, px, py, tr);
+    merge_and_store<C, G>(p, sm, k & 1, it, tid_i);
+    it = nx;
   }
   if (threadIdx.x == 0 && atomicAdd(counters + 1, 1) == (int)gridDim.x - 1) {
     atomicExch(counters, 0);
