@@ -135,29 +135,41 @@ lgm_status lgm_rope_kv_append(const void* qkv, int64_t qkv_row_stride, void* q_o
                               lgm_dtype act_dtype, lgm_dtype cache_dtype, void* stream);
 
 /*
- * The partition size the attention call will use.  A positive partition_size
- * must be a multiple of block_size and is returned as is (clamped to the
- * rounded-up max_context_len).  partition_size 0 lets the library choose
- * from the shapes alone (deterministic, no device query): for the
- * matrix-core shapes (bf16 activations, bf16 / FP8 caches, head_dim 128) the
- * largest power of two from 64 to 4096 tokens that still gives 2048
- * (sequence, partition, kv head) work items at max_context_len; otherwise a
- * size that gives about 8192 workgroups.  When max_context_len exceeds the
- * partition size, each context is cut into floor(L / partition) full
- * partitions followed by partitions of half that size (at least block_size)
- * over the rest, which are processed last.  Returns -1 (and sets
- * lgm_last_error) on invalid arguments.
+ * The partition size the attention call will use, or 0 for equal ranges.
+ * A positive partition_size must be a multiple of block_size and is returned
+ * as is (clamped to the rounded-up max_context_len).  partition_size 0 lets
+ * the library choose from the shapes alone (deterministic, no device query):
+ *  - matrix-core shapes (bf16 activations, bf16 / FP8 caches, head_dim 128)
+ *    with num_kv_heads divisible by 4: returns 0.  The 32-token tiles of all
+ *    contexts (per group of 8, or 4, kv heads) are cut into equal ranges, one
+ *    per compute unit (256, fewer when a range would hold under 8 tiles);
+ *    each workgroup reads whole KV rows of its head group, and contexts split
+ *    between ranges are merged by log-sum-exp;
+ *  - other matrix-core shapes: the largest power of two from 64 to 4096
+ *    tokens that still gives 2048 (sequence, partition, kv head) work items
+ *    at max_context_len;
+ *  - other shapes: a size that gives about 8192 workgroups.
+ * With partitions, when max_context_len exceeds the partition size each
+ * context is cut into floor(L / partition) full partitions followed by
+ * partitions of half that size (at least block_size) over the rest, which
+ * are processed last.  Returns -1 (and sets lgm_last_error) on invalid
+ * arguments.
  */
 int32_t lgm_paged_decode_partition_size(lgm_paged_dims dims, int32_t max_context_len,
                                         int32_t partition_size, lgm_dtype cache_dtype);
 
 /*
  * Bytes of device workspace lgm_paged_decode_attn needs for these
- * arguments: for the matrix-core shapes first 256 bytes holding two int32
- * work counters, then, when contexts are split, the split-K records (fp32
- * partial outputs [B][Hq][P][D] and natural-log LSEs [B][Hq][P], each
- * 256-byte aligned, P = the most partitions any context up to
- * max_context_len is cut into).  0 for other shapes without a split.
+ * arguments (each region 256-byte aligned):
+ *  - equal ranges (see lgm_paged_decode_partition_size): two records per
+ *    range (fp32 outputs of the head group's Hq * 8 / Hkv or Hq * 4 / Hkv
+ *    query heads, D each, and their natural-log LSEs), then int32 range
+ *    and context bookkeeping (one per range, two per context and head group);
+ *  - partitions on the matrix-core shapes: 256 bytes holding two int32 work
+ *    counters, then, when contexts are split, fp32 partial outputs
+ *    [B][Hq][P][D] and LSEs [B][Hq][P], P = the most partitions any context
+ *    up to max_context_len is cut into;
+ *  - partitions on other shapes: the partials only (0 without a split).
  * Returns 0 and sets lgm_last_error on invalid arguments (check it when 0
  * is unexpected).
  */
@@ -192,11 +204,12 @@ size_t lgm_paged_decode_workspace_size(lgm_paged_dims dims, int32_t max_context_
  *   max_context_len upper bound on context_lens, 0..max_blocks_per_seq*block_size
  *   workspace      device buffer of at least lgm_paged_decode_workspace_size()
  *                  bytes, 256-byte aligned (NULL allowed when that size is 0).
- *                  Its first 256 bytes (the work counters, matrix-core
- *                  shapes) must be zero before the first call on it; every
- *                  completed call leaves them zero again.  Zero-fill it again
- *                  after a call on it failed to complete.  Calls sharing a
- *                  workspace must not overlap in time (one per stream).
+ *                  With partitions on the matrix-core shapes its first 256
+ *                  bytes (the work counters) must be zero before the first
+ *                  call on it; every completed call leaves them zero again.
+ *                  Zero-fill it again after a call on it failed to complete.
+ *                  Calls sharing a workspace must not overlap in time (one
+ *                  per stream).
  * Supported: (act, cache) in {(F32, F32), (BF16, BF16), (BF16, FP8_E4M3)},
  * head_dim in {64, 128}, block_size 16, G = Hq/Hkv in 1..8; with bf16
  * activations at head_dim 128, G in 1..16 (matrix-core kernel).

@@ -32,6 +32,7 @@ UNITS = {
     "rope_kv_append.hip": ["-ffp-contract=off"],
     "paged_decode.hip": [],
     "paged_decode_mfma.hip": [],
+    "paged_decode_rows.hip": [],
     "lse_merge.hip": [],
 }
 

@@ -159,11 +159,24 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // counters (matrix-core shapes, one 256-byte slot), then the partial outputs
 // and LSEs (none when every sequence fits one partition).
 struct Plan {
+  bool rows;  // whole-row kernel over equal tile ranges (partition_size 0, Hkv % 4 == 0)
   lgm::PartitionPlan parts;
   int32_t ps, P;
   size_t counters_bytes, part_out_bytes, part_lse_bytes;
+  int32_t W, HG;  // rows: workgroups (ranges), kv heads per workgroup
+  size_t rec_out_bytes, rec_lse_bytes, first_bytes, stream_bytes;
   size_t total;
 };
+
+// Whole-row plan: one range per compute unit of MI355X (256 CUs, one
+// workgroup each, so no range runs beside another that the CU favours),
+// fewer for small batches so that a range holds at least kRowsMinTiles tiles.
+#ifndef LGM_ROWS_WORKGROUPS
+#define LGM_ROWS_WORKGROUPS 256
+#endif
+constexpr int64_t kRowsWorkgroups = LGM_ROWS_WORKGROUPS;
+constexpr int64_t kRowsMinTiles = 8;
+constexpr int64_t kRowsTile = 32;
 
 lgm_status plan_decode(const char* fn, const lgm_paged_dims& d, int32_t max_ctx, int32_t ps_arg, lgm_dtype cache,
                        Plan& pl) {
@@ -171,6 +184,24 @@ lgm_status plan_decode(const char* fn, const lgm_paged_dims& d, int32_t max_ctx,
   const int G = d.num_q_heads / d.num_kv_heads;
   const lgm_dtype act = cache == LGM_F32 ? LGM_F32 : LGM_BF16;  // the only supported pairings
   const bool persistent = lgm::decode_mfma_supported(act, cache, d.head_dim, G, d.block_size);
+  if (ps_arg == 0 && lgm::decode_rows_supported(act, cache, d.head_dim, d.num_kv_heads, G, d.block_size)) {
+    pl.rows = true;
+    pl.HG = d.num_kv_heads % 8 == 0 ? 8 : 4;
+    const int64_t streams = (int64_t)d.num_seqs * (d.num_kv_heads / pl.HG);
+    const int64_t tiles = streams * ((max_ctx + kRowsTile - 1) / kRowsTile);
+    if (tiles > (int64_t)INT32_MAX)
+      return fail(LGM_ERR_UNSUPPORTED, fn, "num_seqs * head groups * tiles = %lld: too many", (long long)tiles);
+    int64_t W = (tiles + kRowsMinTiles - 1) / kRowsMinTiles;
+    W = W < 1 ? 1 : (W > kRowsWorkgroups ? kRowsWorkgroups : W);
+    pl.W = (int32_t)W;
+    const size_t rows_per_rec = (size_t)pl.HG * G;
+    pl.rec_out_bytes = align256((size_t)W * 2 * rows_per_rec * d.head_dim * sizeof(float));
+    pl.rec_lse_bytes = align256((size_t)W * 2 * rows_per_rec * sizeof(float));
+    pl.first_bytes = align256((size_t)W * sizeof(int32_t));
+    pl.stream_bytes = align256((size_t)streams * sizeof(int32_t));
+    pl.total = pl.rec_out_bytes + pl.rec_lse_bytes + pl.first_bytes + 2 * pl.stream_bytes;
+    return LGM_OK;
+  }
   pl.ps = resolve_partition(fn, d, max_ctx, ps_arg, persistent);
   if (pl.ps < 0) return LGM_ERR_INVALID_ARGUMENT;
   // When contexts are split, the tokens past a context's last full partition
@@ -278,7 +309,7 @@ int32_t lgm_paged_decode_partition_size(lgm_paged_dims dims, int32_t max_context
   if (check_decode_common(fn, dims, max_context_len, cache_dtype) != LGM_OK) return -1;
   Plan pl;
   if (plan_decode(fn, dims, max_context_len, partition_size, cache_dtype, pl) != LGM_OK) return -1;
-  return pl.ps;
+  return pl.rows ? 0 : pl.ps;
 }
 
 size_t lgm_paged_decode_workspace_size(lgm_paged_dims dims, int32_t max_context_len, int32_t partition_size,
@@ -358,6 +389,26 @@ lgm_status lgm_paged_decode_attn(void* out, float* out_lse, const void* q, int64
   if ((st = check_no_alias(fn, outs, 3, ins, 7)) != LGM_OK) return st;
 
   char* wsb = static_cast<char*>(workspace);
+  if (pl.rows) {
+    lgm::DecodeArgs a{out, out_lse, q, q_seq_stride, k_cache, v_cache, block_tables, context_lens, k_scale, v_scale,
+                      nullptr, nullptr, nullptr, softmax_scale, lgm::PartitionPlan{1, 1}, max_context_len, 0, dims};
+    char* w = wsb;
+    lgm::RowsArgs r{};
+    r.num_wg = pl.W;
+    r.head_group = pl.HG;
+    r.rec_out = reinterpret_cast<float*>(w);
+    w += pl.rec_out_bytes;
+    r.rec_lse = reinterpret_cast<float*>(w);
+    w += pl.rec_lse_bytes;
+    r.first_stream = reinterpret_cast<int32_t*>(w);
+    w += pl.first_bytes;
+    r.wg_first = reinterpret_cast<int32_t*>(w);
+    w += pl.stream_bytes;
+    r.wg_last = reinterpret_cast<int32_t*>(w);
+    const hipError_t e = lgm::launch_paged_decode_rows(a, r, cache_dtype, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(LGM_ERR_HIP, fn, "row kernel launch failed: %s", hipGetErrorString(e));
+    return LGM_OK;
+  }
   int32_t* counters = pl.counters_bytes ? reinterpret_cast<int32_t*>(wsb) : nullptr;
   float* part_out = pl.P > 1 ? reinterpret_cast<float*>(wsb + pl.counters_bytes) : nullptr;
   float* part_lse = pl.P > 1 ? reinterpret_cast<float*>(wsb + pl.counters_bytes + pl.part_out_bytes) : nullptr;

@@ -107,6 +107,21 @@ hipError_t launch_lse_merge(const MergeArgs& a, lgm_dtype out_dtype, hipStream_t
 
 // Matrix-core decode for bf16 activations with bf16 / FP8 caches, head_dim 128.
 hipError_t launch_paged_decode_mfma(const DecodeArgs& a, lgm_dtype cache, hipStream_t s);
+// Whole-row decode (matrix-core shapes with num_kv_heads % 4 == 0): equal
+// static tile ranges, one per workgroup, then a merge of the split streams.
+struct RowsArgs {
+  int32_t num_wg;         // W: workgroups, one range each
+  int32_t head_group;     // HG: kv heads per workgroup (8, or 4)
+  float* rec_out;         // [W][2][HG * G][D] normalised partial outputs
+  float* rec_lse;         // [W][2][HG * G] natural-log LSEs
+  int32_t* first_stream;  // [W] stream each range starts in, -1 for an empty range
+  int32_t* wg_first;      // [B * Hkv / HG] workgroup holding the stream's first tile
+  int32_t* wg_last;       // [B * Hkv / HG] workgroup holding its last tile
+};
+hipError_t launch_paged_decode_rows(const DecodeArgs& a, const RowsArgs& r, lgm_dtype cache, hipStream_t s);
+bool decode_rows_supported(lgm_dtype act, lgm_dtype cache, int head_dim, int num_kv_heads, int group,
+                           int block_size);
+
 // Upper bound on the persistent matrix-core kernel's workgroups per compute
 // unit (the grid is compute units x min(this, resident capacity)).
 #ifndef LGM_PERSISTENT_MAX_PER_CU

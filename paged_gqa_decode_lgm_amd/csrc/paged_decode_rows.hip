@@ -1,0 +1,434 @@
+// Paged GQA decode attention over whole KV token rows, for gfx950 matrix
+// cores: bf16 activations, bf16 or FP8 E4M3 caches, head_dim 128, block_size
+// 16, a kv head count divisible by 4.
+//
+// The split-K method of paged_decode.hip (mainarch README, decode-attention
+// section; Loom Kernels README, "Attention" row) with the work laid out for
+// how HBM serves a paged NHD cache.  A token row holds all kv heads side by
+// side (Hkv x 256 bytes for bf16), and a 16-token block is one contiguous
+// run of rows.  Workgroups that each read one kv head's 256-byte slice of
+// every row leave the rest of each DRAM page to other workgroups at other
+// times; here one workgroup covers a group of HG = 8 (or 4) kv heads, its four
+// waves taking 2 (or 1) heads each, so the workgroup reads whole rows and
+// whole blocks.
+//
+// The work is the flattened list of 32-token tiles of all streams (a stream
+// is one sequence's tiles for one head group), cut into as many equal ranges
+// as workgroups run at once: every workgroup reads the same number of bytes
+// whatever the mix of context lengths, and there is no queue.  A range covers
+// the end of one stream, whole streams, and the start of another; a stream
+// that lies inside one range is written directly, the pieces of a split
+// stream go to two record slots per workgroup and are merged by log-sum-exp
+// afterwards (rows_merge_kernel).  Since each wave owns its heads for the
+// whole range, no wave ever waits for another.
+//
+// Per tile a wave computes scores S^T = K Q^T and O += P V on
+// v_mfma_f32_16x16x32_bf16 exactly as the partition kernel does (operand
+// layouts and the softmax update in mfma_common.h), alternating between its
+// two heads with one tile of loads in flight.
+#include "mfma_common.h"
+
+namespace lgm {
+namespace {
+
+using namespace mfma;
+
+constexpr int kChunk = 4 * kDecodeThreads;  // sequences per scan step
+
+struct RowsSmem {
+  int pre[kChunk + 1];  // tiles of the streams of sequences b0 .. b0 + j - 1
+  int wave_sum[kNW];
+};
+
+__device__ __forceinline__ int clamped_ctx(const DecodeArgs& p, int b) {
+  const int c = p.context_lens[b];
+  return c < 0 ? 0 : (c > p.max_context_len ? p.max_context_len : c);
+}
+
+// Fills sm.pre for sequences b0 .. b0 + kChunk - 1 (nhg streams of
+// ceil(ctx / 32) tiles per sequence) and returns the chunk's tile total.
+// Called by every thread of the workgroup (it synchronises).
+__device__ int scan_chunk(const DecodeArgs& p, RowsSmem& sm, int b0, int nhg) {
+  const int tid = threadIdx.x, lane = tid & (kWaveSize - 1), wave = tid / kWaveSize;
+  int t[4], s = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int b = b0 + 4 * tid + k;
+    t[k] = b < p.dims.num_seqs ? (clamped_ctx(p, b) + kTile - 1) / kTile * nhg : 0;
+    s += t[k];
+  }
+  int incl = s;
+#pragma unroll
+  for (int o = 1; o < kWaveSize; o <<= 1) {
+    const int x = __shfl_up(incl, o);
+    if (lane >= o) incl += x;
+  }
+  __syncthreads();  // earlier readers of sm.pre are done
+  if (lane == kWaveSize - 1) sm.wave_sum[wave] = incl;
+  __syncthreads();
+  int run = incl - s;
+  for (int w = 0; w < wave; ++w) run += sm.wave_sum[w];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    sm.pre[4 * tid + k] = run;
+    run += t[k];
+  }
+  if (tid == kDecodeThreads - 1) sm.pre[kChunk] = run;
+  __syncthreads();
+  return __builtin_amdgcn_readfirstlane(sm.pre[kChunk]);
+}
+
+// Block ids of tiles k0 .. k0 + 31 of a segment starting at tile lt of
+// sequence b, one per lane (lane 2k + h: block h of tile k0 + k); -1 marks a
+// block past the segment or the context (lb_end blocks) or an out-of-range
+// table entry.
+__device__ __forceinline__ int preload_row_ids(const DecodeArgs& p, int b, int lt, int et, int lb_end, int k0,
+                                               int lane) {
+  const int MB = p.dims.max_blocks_per_seq;
+  const __amdgpu_buffer_rsrc_t rs = span_rsrc(p.block_tables + (int64_t)b * MB, MB * 4);
+  const int tile = lt + k0 + (lane >> 1);
+  const int lb = 2 * tile + (lane & 1);
+  const int id = buf_load4(rs, 4 * (lb < MB ? lb : 0));
+  return (tile < et && lb < lb_end && (unsigned)id < (unsigned)p.dims.num_blocks) ? id : -1;
+}
+
+template <class C>
+__device__ __forceinline__ void row_load_k(const DecodeArgs& p, int g, int px, int py, int lane, TileRegs<C>& tr) {
+  const int tok_bytes = p.dims.num_kv_heads * kD * C::kElemBytes;
+  const int64_t block_bytes = (int64_t)kBS * tok_bytes;
+  const int off = C::k_lane_off(g, tok_bytes, lane & 15, lane >> 4);
+  const int ex = px >= 0 ? px : 0, ey = py >= 0 ? py : ex;
+  C::load_k(tr.kx, block_rsrc(p.k_cache, block_bytes, ex), off, tok_bytes);
+  C::load_k(tr.ky, block_rsrc(p.k_cache, block_bytes, ey), off, tok_bytes);
+}
+template <class C>
+__device__ __forceinline__ void row_load_v(const DecodeArgs& p, int g, int px, int py, int lane, TileRegs<C>& tr) {
+  const int tok_bytes = p.dims.num_kv_heads * kD * C::kElemBytes;
+  const int64_t block_bytes = (int64_t)kBS * tok_bytes;
+  const int off = C::v_lane_off(g, tok_bytes, lane & 15, lane >> 4);
+  const int ex = px >= 0 ? px : 0, ey = py >= 0 ? py : ex;
+  C::load_v(tr.vx, block_rsrc(p.v_cache, block_bytes, ex), off, tok_bytes);
+  C::load_v(tr.vy, block_rsrc(p.v_cache, block_bytes, ey), off, tok_bytes);
+}
+
+// Writes one head's result of a segment: the final output (bf16, normalised)
+// when the segment is the whole stream, else a record (fp32 normalised output
+// and natural-log LSE).  acc[i][j] holds O[row 4kg + j][8n + i]; the row's
+// max and sums sit in lane `row` of the score layout.
+template <class C, int G>
+__device__ __forceinline__ void write_head(const DecodeArgs& p, const RowsArgs& r, const WaveState& st, int b, int g,
+                                           bool whole, int rec, int lane) {
+  const int n = lane & 15, kg = lane >> 4;
+  const float lsum = sum4(st.lsum);
+  const float lsum_e = sum4(st.lsum_e);
+  const float vscale = C::kFp8 ? p.v_scale[g] : 1.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int row = 4 * kg + j;
+    const float L = __shfl(lsum, row);
+    const float Le = __shfl(lsum_e, row);
+    const float m = __shfl(st.m, row);
+    if (row < G) {
+      const float inv = L > 0.f ? vscale / L : 0.f;
+      const float lse = Le > 0.f ? (m + fast_log2(Le)) * kLn2 : -INFINITY;
+      const int64_t orow = (int64_t)b * p.dims.num_q_heads + g * G + row;
+      if (whole) {
+        uint32_t w[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          w[i] = (uint32_t)f32_to_bf16_rne(st.acc[2 * i][j] * inv) |
+                 ((uint32_t)f32_to_bf16_rne(st.acc[2 * i + 1][j] * inv) << 16);
+        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.out) + orow * kD + 8 * n) = make_uint4(w[0], w[1], w[2], w[3]);
+        if (n == 0 && p.out_lse) p.out_lse[orow] = lse;
+      } else {
+        const int hrow = (g % r.head_group) * G + row;  // row inside the head group
+        float* dst = r.rec_out + ((int64_t)rec * r.head_group * G + hrow) * kD + 8 * n;
+        *reinterpret_cast<float4*>(dst) =
+            make_float4(st.acc[0][j] * inv, st.acc[1][j] * inv, st.acc[2][j] * inv, st.acc[3][j] * inv);
+        *reinterpret_cast<float4*>(dst + 4) =
+            make_float4(st.acc[4][j] * inv, st.acc[5][j] * inv, st.acc[6][j] * inv, st.acc[7][j] * inv);
+        if (n == 0) r.rec_lse[(int64_t)rec * r.head_group * G + hrow] = lse;
+      }
+    }
+  }
+}
+
+// One segment for this wave: tiles lt .. et - 1 of sequence b (context ctx)
+// for kv heads g0 .. g0 + HPW - 1.  The wave streams through steps (a tile
+// for one head) with two register sets, A and B: with two heads A always
+// holds the first head's tile and B the second's; with one head A holds the
+// even tiles and B the odd ones.  A set's next tile is loaded as soon as its
+// current step's MFMAs have consumed the registers (K after the scores, V
+// after P V), so while one set is computed the other set's loads and the
+// first set's next loads are in flight: two steps of loads per wave, which
+// with one wave per SIMD keeps HBM busy.  Steps past the segment (and the
+// dummy loads after the last one) use absent blocks: they read block 0 and
+// are masked, so every iteration issues the same loads in the same order.
+template <class C, int G, int HPW>
+__device__ __forceinline__ void run_segment(const DecodeArgs& p, const RowsArgs& r, int b, int ctx, int lt, int et,
+                                            int g0, bool whole, int rec, int lane) {
+  short8 qb[HPW][4];
+  WaveState st[HPW];
+  const bool qvec = ((uintptr_t)p.q % 16 == 0) && (p.q_seq_stride % 8 == 0);
+#pragma unroll
+  for (int hh = 0; hh < HPW; ++hh) {
+    const uint16_t* qrow =
+        static_cast<const uint16_t*>(p.q) + (int64_t)b * p.q_seq_stride + (int64_t)(g0 + hh) * G * kD;
+    load_q_operand<C, G>(qb[hh], qrow, qvec, lane & 15, lane >> 4);
+    st[hh].reset();
+  }
+  float sscale[HPW];
+#pragma unroll
+  for (int hh = 0; hh < HPW; ++hh) {
+    sscale[hh] = p.softmax_scale * kLog2e;
+    if constexpr (C::kFp8) sscale[hh] *= p.k_scale[g0 + hh];
+  }
+
+  const int lb_end = (ctx + kBS - 1) / kBS;
+  int win = 0;
+  int ids = preload_row_ids(p, b, lt, et, lb_end, 0, lane);
+  // Block ids of tile lt + k (-1 when absent), from the 32-tile window of ids.
+  auto tile_id = [&](int k, int& x, int& y) {
+    if ((k >> 5) != win) {
+      win = k >> 5;
+      ids = preload_row_ids(p, b, lt, et, lb_end, 32 * win, lane);
+    }
+    x = __builtin_amdgcn_readlane(ids, 2 * (k & 31));
+    y = __builtin_amdgcn_readlane(ids, 2 * (k & 31) + 1);
+  };
+  constexpr int kAdvance = HPW == 2 ? 1 : 2;  // tiles a set moves per iteration
+  const int gA = g0, gB = HPW == 2 ? g0 + 1 : g0;
+  TileRegs<C> ta, tb;
+  int ax, ay, bx, by;
+  tile_id(0, ax, ay);
+  if (HPW == 2) {
+    bx = ax;
+    by = ay;
+  } else {
+    tile_id(1, bx, by);
+  }
+  row_load_k<C>(p, gA, ax, ay, lane, ta);
+  __builtin_amdgcn_sched_barrier(0);  // the loop's load order: K A, V A, K B, V B
+  row_load_v<C>(p, gA, ax, ay, lane, ta);
+  __builtin_amdgcn_sched_barrier(0);
+  row_load_k<C>(p, gB, bx, by, lane, tb);
+  __builtin_amdgcn_sched_barrier(0);
+  row_load_v<C>(p, gB, bx, by, lane, tb);
+  const int ntiles = et - lt;
+  const int iters = HPW == 2 ? ntiles : (ntiles + 1) / 2;
+  for (int it = 0; it < iters; ++it) {
+    const int ka = HPW == 2 ? it : 2 * it;
+    const int kb = HPW == 2 ? it : 2 * it + 1;
+    int nax, nay, nbx, nby;
+    tile_id(ka + kAdvance, nax, nay);
+    if (HPW == 2) {
+      nbx = nax;
+      nby = nay;
+    } else {
+      tile_id(kb + kAdvance, nbx, nby);
+    }
+    float4v sx, sy;
+    tile_scores<C>(ta, qb[0], sx, sy);
+    row_load_k<C>(p, gA, nax, nay, lane, ta);
+    tile_update<C>(st[0], ta, sx, sy, sscale[0], ax >= 0, ay >= 0, kTile * (lt + ka), ctx, lane >> 4);
+    row_load_v<C>(p, gA, nax, nay, lane, ta);
+    tile_scores<C>(tb, qb[HPW - 1], sx, sy);
+    row_load_k<C>(p, gB, nbx, nby, lane, tb);
+    tile_update<C>(st[HPW - 1], tb, sx, sy, sscale[HPW - 1], bx >= 0, by >= 0, kTile * (lt + kb), ctx, lane >> 4);
+    row_load_v<C>(p, gB, nbx, nby, lane, tb);
+    ax = nax;
+    ay = nay;
+    bx = nbx;
+    by = nby;
+  }
+#pragma unroll
+  for (int hh = 0; hh < HPW; ++hh) write_head<C, G>(p, r, st[hh], b, g0 + hh, whole, rec, lane);
+}
+
+// One workgroup per equal range of the flattened tile list.  Metadata for the
+// merge: first_stream[w] = the stream the range starts in (-1 if empty),
+// wg_first[u] / wg_last[u] = the workgroups holding stream u's first and
+// last tiles.  Record slot 2w holds the range's first stream when split,
+// slot 2w + 1 its last one (when that is another stream).
+template <class C, int G, int HPW>
+__global__ __launch_bounds__(kDecodeThreads, 1) void paged_decode_rows_kernel(DecodeArgs p, RowsArgs r) {
+  __shared__ RowsSmem sm;
+  constexpr int HG = kNW * HPW;
+  const int lane = threadIdx.x & (kWaveSize - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWaveSize);
+  const int B = p.dims.num_seqs;
+  const int nhg = p.dims.num_kv_heads / HG;
+  const int W = gridDim.x;
+  const int wg = blockIdx.x;
+
+  int total = scan_chunk(p, sm, 0, nhg);
+  for (int c0 = kChunk; c0 < B; c0 += kChunk) total += scan_chunk(p, sm, c0, nhg);
+  const int t_lo = (int)((int64_t)wg * total / W);
+  const int t_hi = (int)((int64_t)(wg + 1) * total / W);
+  int b0 = 0, base = 0;
+  if (B > kChunk) scan_chunk(p, sm, 0, nhg);  // back to the first chunk
+
+  int pos = t_lo;
+  bool first = true;
+  if (threadIdx.x == 0 && t_lo >= t_hi) r.first_stream[wg] = -1;
+  while (pos < t_hi) {
+    int rel = pos - base;
+    while (rel >= __builtin_amdgcn_readfirstlane(sm.pre[kChunk])) {  // uniform: every thread moves on together
+      base += __builtin_amdgcn_readfirstlane(sm.pre[kChunk]);
+      b0 += kChunk;
+      scan_chunk(p, sm, b0, nhg);
+      rel = pos - base;
+    }
+    int lo = 0, hi = kChunk;  // sm.pre[lo] <= rel < sm.pre[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (__builtin_amdgcn_readfirstlane(sm.pre[mid]) <= rel) lo = mid;
+      else hi = mid;
+    }
+    const int b = b0 + lo;
+    const int ctx = __builtin_amdgcn_readfirstlane(clamped_ctx(p, b));
+    const int ntb = (ctx + kTile - 1) / kTile;
+    const int off = rel - __builtin_amdgcn_readfirstlane(sm.pre[lo]);
+    const int hg = off / ntb;
+    const int lt = off - hg * ntb;
+    const int et = min(ntb, lt + (t_hi - pos));
+    const int u = b * nhg + hg;
+    const bool whole = lt == 0 && et == ntb;
+    if (threadIdx.x == 0) {
+      if (first) r.first_stream[wg] = u;
+      if (lt == 0) r.wg_first[u] = wg;
+      if (et == ntb) r.wg_last[u] = wg;
+    }
+    run_segment<C, G, HPW>(p, r, b, ctx, lt, et, hg * HG + wave * HPW, whole, 2 * wg + (first ? 0 : 1), lane);
+    pos += et - lt;
+    first = false;
+  }
+}
+
+// Log-sum-exp merge of the records of split streams (the combine step of the
+// split-K method; [mainarch] decode attention, [Loom] local split-K/LSE
+// merge).  One workgroup per (sequence, query head); streams written whole
+// by the decode kernel are skipped, empty contexts get out = 0, lse = -inf.
+constexpr int kMergeThreads = 256;
+constexpr int kMergeGroups = kMergeThreads / (kD / 4);  // records in flight per pass
+
+template <int G>
+__global__ __launch_bounds__(kMergeThreads) void rows_merge_kernel(DecodeArgs p, RowsArgs r) {
+  __shared__ float red[kMergeThreads];
+  __shared__ float s_acc[kMergeGroups][kD];
+  const int h = blockIdx.x;
+  const int b = blockIdx.y;
+  const int g = h / G;
+  const int HG = r.head_group;
+  const int nhg = p.dims.num_kv_heads / HG;
+  const int u = b * nhg + g / HG;
+  const int64_t orow = (int64_t)b * p.dims.num_q_heads + h;
+  if (clamped_ctx(p, b) == 0) {
+    if (threadIdx.x < kD) static_cast<uint16_t*>(p.out)[orow * kD + threadIdx.x] = 0;
+    if (threadIdx.x == 0 && p.out_lse) p.out_lse[orow] = -INFINITY;
+    return;
+  }
+  const int i0 = r.wg_first[u], i1 = r.wg_last[u];
+  if (i0 == i1) return;
+  const int n = i1 - i0 + 1;
+  const int hrow = (g % HG) * G + h % G;
+  // Record of the k-th workgroup from i0, or -1 for a workgroup whose range
+  // is empty (there are more workgroups than tiles).
+  auto rec_of = [&](int k) -> int64_t {
+    const int w = i0 + k;
+    const int f = r.first_stream[w];
+    return f < 0 ? -1 : 2 * (int64_t)w + (f == u ? 0 : 1);
+  };
+  auto lse_of = [&](int64_t rec) -> float { return rec < 0 ? -INFINITY : r.rec_lse[rec * HG * G + hrow]; };
+
+  float mx = -INFINITY;
+  for (int k = threadIdx.x; k < n; k += kMergeThreads) mx = fmaxf(mx, lse_of(rec_of(k)));
+  red[threadIdx.x] = mx;
+  __syncthreads();
+  for (int s = kMergeThreads / 2; s > 0; s >>= 1) {
+    if (threadIdx.x < s) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + s]);
+    __syncthreads();
+  }
+  const float M = red[0];
+  const float ms = M == -INFINITY ? 0.f : M;
+  __syncthreads();
+  float sw = 0.f;
+  for (int k = threadIdx.x; k < n; k += kMergeThreads) sw += expf(lse_of(rec_of(k)) - ms);
+  red[threadIdx.x] = sw;
+  __syncthreads();
+  for (int s = kMergeThreads / 2; s > 0; s >>= 1) {
+    if (threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
+    __syncthreads();
+  }
+  const float S = red[0];
+
+  const int td = threadIdx.x % (kD / 4);
+  const int pg = threadIdx.x / (kD / 4);
+  float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int k = pg; k < n; k += kMergeGroups) {
+    const int64_t rec = rec_of(k);
+    if (rec < 0) continue;
+    const float w = expf(r.rec_lse[rec * HG * G + hrow] - ms);
+    const float4 v = reinterpret_cast<const float4*>(r.rec_out + (rec * HG * G + hrow) * kD)[td];
+    a.x = fmaf(w, v.x, a.x);
+    a.y = fmaf(w, v.y, a.y);
+    a.z = fmaf(w, v.z, a.z);
+    a.w = fmaf(w, v.w, a.w);
+  }
+  s_acc[pg][4 * td + 0] = a.x;
+  s_acc[pg][4 * td + 1] = a.y;
+  s_acc[pg][4 * td + 2] = a.z;
+  s_acc[pg][4 * td + 3] = a.w;
+  __syncthreads();
+  if (threadIdx.x < kD) {
+    float o = 0.f;
+#pragma unroll
+    for (int k = 0; k < kMergeGroups; ++k) o += s_acc[k][threadIdx.x];
+    o = S > 0.f ? o / S : 0.f;
+    static_cast<uint16_t*>(p.out)[orow * kD + threadIdx.x] = f32_to_bf16_rne(o);
+  }
+  if (threadIdx.x == 0 && p.out_lse) p.out_lse[orow] = S > 0.f ? M + logf(S) : -INFINITY;
+}
+
+template <class C, int G>
+hipError_t launch_group(const DecodeArgs& a, const RowsArgs& r, hipStream_t s) {
+  if (r.head_group == 8)
+    hipLaunchKernelGGL((paged_decode_rows_kernel<C, G, 2>), dim3(r.num_wg), dim3(kDecodeThreads), 0, s, a, r);
+  else
+    hipLaunchKernelGGL((paged_decode_rows_kernel<C, G, 1>), dim3(r.num_wg), dim3(kDecodeThreads), 0, s, a, r);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((rows_merge_kernel<G>), dim3(a.dims.num_q_heads, a.dims.num_seqs), dim3(kMergeThreads), 0, s, a,
+                     r);
+  return hipGetLastError();
+}
+
+template <class C>
+hipError_t dispatch(const DecodeArgs& a, const RowsArgs& r, int G, hipStream_t s) {
+  switch (G) {
+#define LGM_CASE(GV) \
+  case GV:           \
+    return launch_group<C, GV>(a, r, s);
+    LGM_CASE(1) LGM_CASE(2) LGM_CASE(3) LGM_CASE(4) LGM_CASE(5) LGM_CASE(6) LGM_CASE(7) LGM_CASE(8)
+    LGM_CASE(9) LGM_CASE(10) LGM_CASE(11) LGM_CASE(12) LGM_CASE(13) LGM_CASE(14) LGM_CASE(15) LGM_CASE(16)
+#undef LGM_CASE
+    default:
+      return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+bool decode_rows_supported(lgm_dtype act, lgm_dtype cache, int head_dim, int num_kv_heads, int group,
+                           int block_size) {
+  return decode_mfma_supported(act, cache, head_dim, group, block_size) && num_kv_heads % 4 == 0;
+}
+
+hipError_t launch_paged_decode_rows(const DecodeArgs& a, const RowsArgs& r, lgm_dtype cache, hipStream_t s) {
+  const int G = a.dims.num_q_heads / a.dims.num_kv_heads;
+  if (cache == LGM_BF16) return dispatch<MfmaBF16>(a, r, G, s);
+  if (cache == LGM_FP8_E4M3) return dispatch<MfmaFP8>(a, r, G, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace lgm

@@ -143,10 +143,12 @@ def test_attention_empty_batch_is_a_noop():
 
 # ------------------------------------------------------------------ plan queries
 @pytest.mark.parametrize("d,max_ctx,ps,want", [
-    (dims(), 8192, 0, 2048),                                              # Llama-3-8B-shaped batch
-    (dims(num_seqs=128, max_blocks_per_seq=256), 4096, 0, 2048),          # FP8-cache batch
-    (dims(num_seqs=4, max_blocks_per_seq=8192), 131072, 0, 2048),         # long contexts
-    (dims(num_seqs=256), 8192, 0, 4096),
+    (dims(), 8192, 0, 0),                                                 # whole-row ranges (Hkv % 4 == 0)
+    (dims(num_seqs=128, max_blocks_per_seq=256), 4096, 0, 0),
+    (dims(num_seqs=4, max_blocks_per_seq=8192), 131072, 0, 0),
+    (dims(num_q_heads=16, num_kv_heads=2), 8192, 0, 512),                 # work queue: >= 2048 items
+    (dims(num_q_heads=24, num_kv_heads=6), 8192, 0, 1024),
+    (dims(num_seqs=256, num_q_heads=16, num_kv_heads=2), 8192, 0, 2048),
     (dims(num_seqs=2, num_q_heads=12, num_kv_heads=2, max_blocks_per_seq=128), 2048, 0, 64),
     (dims(head_dim=64), 8192, 0, 512),                                    # vector-ALU shape
     (dims(num_seqs=2, num_q_heads=12, num_kv_heads=2, head_dim=64, max_blocks_per_seq=128), 2048, 0, 64),
@@ -193,6 +195,19 @@ def test_partition_count_bound(max_ctx, ps):
     assert L.lgm_last_error() == ""
     with pytest.raises(L.LgmError):
         L.lgm_paged_decode_workspace_size(d, 8192, 10, L.LGM_BF16)
+
+
+def test_row_plan_workspace_formula():
+    al = lambda x: (x + 255) // 256 * 256
+    d = dims()                                     # 8 kv heads per workgroup, 64 streams of 256 tiles
+    W, rows = 256, 8 * 4
+    want = al(W * 2 * rows * 128 * 4) + al(W * 2 * rows * 4) + al(W * 4) + 2 * al(64 * 4)
+    assert L.lgm_paged_decode_workspace_size(d, 8192, 0, L.LGM_BF16) == want
+    assert L.lgm_paged_decode_workspace_size(d, 8192, 0, L.LGM_FP8_E4M3) == want
+    small = dims(num_seqs=2, num_q_heads=16, num_kv_heads=4, max_blocks_per_seq=8)  # 2 x 4 tiles: one range
+    W, rows = 1, 4 * 4
+    assert L.lgm_paged_decode_workspace_size(small, 100, 0, L.LGM_BF16) == (
+        al(W * 2 * rows * 128 * 4) + al(W * 2 * rows * 4) + al(W * 4) + 2 * al(2 * 4))
 
 
 def test_too_many_partitions_is_unsupported():

@@ -46,6 +46,26 @@ def _lse_check(g_lse, r_lse, rows=None):
         assert np.abs(g[fin] - r[fin]).max() <= 1e-4 * max(1.0, np.abs(r[fin]).max())
 
 
+def _pair_abs(x):
+    """|x_i| + |x_{i+D/2}| for every element of rows x [.., D] (both halves)."""
+    h = x.shape[-1] // 2
+    a = np.abs(x[..., :h]) + np.abs(x[..., h:])
+    return np.concatenate([a, a], -1)
+
+
+def _check_bf16_rotation(g_bits, rec_bits, exact, pair_abs):
+    """Rotated bf16 values: within 1 ord of the fp32-recipe mirror, and within
+    one bf16 ulp plus the fp32 recipe's rounding bound (4 * 2^-24 * (|x_i| +
+    |x_i+D/2|), |cos|, |sin| <= 1) of the exact rotation.  Under cancellation
+    (x_i cos ~ x_i+D/2 sin) that bound exceeds one bf16 ulp of the tiny
+    result, and no fp32 evaluation can do better."""
+    assert np.abs(bf16_ord(g_bits) - bf16_ord(rec_bits)).max() <= 1
+    g = codecs.bf16_decode(np.asarray(g_bits, np.uint16)).astype(np.float64)
+    _, e = np.frexp(g)
+    ulp = np.where(g == 0, 2.0 ** -133, np.ldexp(1.0, e - 8))
+    assert (np.abs(g - exact) <= ulp + 4 * 2.0 ** -24 * pair_abs).all()
+
+
 def _check_append(w, d, q_gpu, rec, ex, seqs=None):
     """q_out and the appended cache slots against the oracle; all other pool bytes unchanged."""
     c = w.cfg
@@ -60,9 +80,15 @@ def _check_append(w, d, q_gpu, rec, ex, seqs=None):
     for (pb, off) in slots:
         mask[pb, off] = False
     assert np.array_equal(gk[mask], k0[mask]) and np.array_equal(gv[mask], v0[mask])
+    xq = xk = None
+    if c.act == "bf16":
+        x = codecs.bf16_decode(W.storage_bits(w.qkv)).astype(np.float64)
+        Hq, Hkv, D = c.num_q_heads, c.num_kv_heads, c.head_dim
+        xq = x[:, : Hq * D].reshape(-1, Hq, D)
+        xk = x[:, Hq * D:(Hq + Hkv) * D].reshape(-1, Hkv, D)
     for b in seqs:
         if c.act == "bf16":
-            assert np.abs(bf16_ord(gq[b]) - bf16_ord(ex.q_out[b])).max() <= 1
+            _check_bf16_rotation(gq[b], rec.q_out[b], ex.q_rot[b], _pair_abs(xq[b]))
         else:
             x = w.qkv.numpy()[b, : c.num_q_heads * c.head_dim].astype(np.float64).reshape(c.num_q_heads, -1)
             h = c.head_dim // 2
@@ -75,7 +101,7 @@ def _check_append(w, d, q_gpu, rec, ex, seqs=None):
             assert np.array_equal(gk[pb, off], rec.k_pool[pb, off]), f"K bytes, seq {b}"
             assert np.array_equal(gv[pb, off], rec.v_pool[pb, off]), f"V bytes, seq {b}"
         elif c.cache == "bf16":
-            assert np.abs(bf16_ord(gk[pb, off]) - bf16_ord(ex.k_pool[pb, off])).max() <= 1
+            _check_bf16_rotation(gk[pb, off], rec.k_pool[pb, off], ex.k_rot[b], _pair_abs(xk[b]))
             assert np.abs(bf16_ord(gv[pb, off]) - bf16_ord(ex.v_pool[pb, off])).max() <= 1
         else:
             assert np.abs(gk[pb, off] - ex.k_pool[pb, off]).max() <= 4 * 2.0 ** -24 * 8
@@ -277,7 +303,7 @@ def test_inactive_sequence_append_writes_nothing():
 
 
 @pytest.mark.parametrize("name", ["llama3_8b_gqa", "fp8_kv"])
-@pytest.mark.parametrize("ps", [0, 64])
+@pytest.mark.parametrize("ps", [64, 512])
 def test_persistent_workspace_is_reusable_and_left_zeroed(name, ps):
     """The matrix-core kernel hands out work items from two counters at the
     start of the workspace: a zero-filled workspace reused by consecutive calls
@@ -306,7 +332,7 @@ def test_persistent_workspace_is_reusable_and_left_zeroed(name, ps):
 
 
 @pytest.mark.parametrize("ps", [0, 16, 32])
-def test_persistent_many_short_sequences_and_empty_ones(ps):
+def test_many_short_sequences_and_empty_ones(ps):
     """Short and zero-length contexts across more than three 64-sequence chunks
     of the work-item walk, with one to several items per sequence; and a
     batch with fewer work items than workgroups."""
@@ -316,3 +342,54 @@ def test_persistent_many_short_sequences_and_empty_ones(ps):
     _run_and_check(cfg)
     cfg1 = W.CONFIGS["qwen2.5_1.5b_gqa"].with_(num_seqs=1, ctx_list=(40,), num_blocks=None, append=False)
     _run_and_check(cfg1)
+
+
+@pytest.mark.parametrize("cache", ["bf16", "fp8"])
+@pytest.mark.parametrize("hkv,G", [(4, 1), (4, 4), (8, 4), (8, 5), (16, 2), (8, 16)])
+def test_row_plan_ragged_edges(cache, hkv, G):
+    """Whole-row ranges (partition_size 0, kv heads divisible by 4): head
+    groups of 4 and 8, empty and one-token contexts, block and tile edges."""
+    cfg = W.Config(f"rows_{cache}_H{hkv}_G{G}", seed=12, num_seqs=len(EDGE_CTX), num_q_heads=hkv * G,
+                   num_kv_heads=hkv, head_dim=128, block_size=16, act="bf16", cache=cache, ctx=0, rope_theta=1e4,
+                   partition_size=0, append=True, ctx_list=EDGE_CTX)
+    _run_and_check(cfg)
+
+
+def test_row_plan_more_workgroups_than_tiles():
+    """The range count follows the longest context, so one long sequence among
+    many one-token ones leaves most ranges empty, between non-empty ones."""
+    ctx = (8192,) + (1,) * 40 + (0, 33, 17) + (1,) * 20
+    cfg = _bench_like(num_seqs=len(ctx), ctx_list=ctx, append=False, partition_size=0)
+    _run_and_check(cfg)
+
+
+def test_row_plan_many_sequences_scan_chunks():
+    """More sequences than one scan step of the range walk (1024)."""
+    ctx = tuple((i * 37) % 97 for i in range(1100))
+    cfg = W.Config("rows_many", seed=13, num_seqs=len(ctx), num_q_heads=8, num_kv_heads=4, head_dim=128,
+                   block_size=16, act="bf16", cache="bf16", ctx=0, rope_theta=1e4, partition_size=0, append=False,
+                   ctx_list=ctx)
+    _run_and_check(cfg)
+
+
+def test_row_plan_workspace_reuse():
+    """The row plan needs no zeroed workspace (every entry it reads is written
+    earlier in the same call): a reused, non-zero one gives identical results."""
+    cfg = W.CONFIGS["llama3_8b_gqa"].with_(num_seqs=12, ctx=(1, 3000), num_blocks=None, append=False)
+    w = W.make_workload(cfg)
+    d = to_device(w)
+    q = q_from_qkv(w).cuda()
+    nbytes = ops.workspace_bytes(q, d.k_pool, d.block_tables, d.max_ctx, 0)
+    ws = torch.full((nbytes,), 0x7F, dtype=torch.uint8, device="cuda")
+    announce("row workspace reuse", nbytes)
+    outs = []
+    for _ in range(3):
+        o, l = ops.paged_decode_attn(q, d.k_pool, d.v_pool, d.block_tables, d.context_lens, d.max_ctx,
+                                     softmax_scale=cfg.softmax_scale, partition_size=0, workspace=ws)
+        outs.append((o.clone(), l.clone()))
+    torch.cuda.synchronize()
+    for o, l in outs[1:]:
+        assert torch.equal(o.view(torch.int16), outs[0][0].view(torch.int16)) and torch.equal(l, outs[0][1])
+    r_out, r_lse = oracle_attention(w, act_raw(w, q_from_qkv(w)), pool_raw(w, w.k_pool), pool_raw(w, w.v_pool))
+    assert max_abs(out_values(cfg, outs[0][0]), r_out) <= TOL["bf16"]
+    _lse_check(outs[0][1].cpu().numpy(), r_lse)
