@@ -82,6 +82,63 @@ def cpu_baseline(w, min_seconds: float = 12.0, max_passes: int = 10):
                       f"{len(times)} passes of {t:.2f} s"}
 
 
+ATTN_KERNELS = ("paged_decode", "merge")  # the launches of one lgm_paged_decode_attn call
+
+
+def copy_probe(nbytes: int, reps: int) -> int:
+    """A plain device copy of nbytes, reps times: the known-size kernel that
+    scales rocprofv3's FETCH_SIZE / WRITE_SIZE readings to bytes."""
+    import torch
+
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": nbytes, "reps": reps}), flush=True)
+    return 0
+
+
+def _counter_means(path: str, counter: str):
+    """Mean counter value (KiB) per dispatch for each kernel name in a rocprofv3 counter_collection.csv."""
+    import csv
+    import collections
+
+    acc = collections.defaultdict(list)
+    with open(path) as fh:
+        for r in csv.DictReader(fh):
+            if r["Counter_Name"] == counter:
+                acc[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in acc.items()}
+
+
+def traffic_summary(workload: str, fetch_csv: str, write_csv: str, copy_fetch_csv: str, copy_write_csv: str,
+                    copy_bytes: int, commands: list) -> int:
+    """HBM bytes per attention call from two rocprofv3 --pmc runs of the bench (FETCH_SIZE, WRITE_SIZE),
+    each scaled by the same counter's reading for the copy probe; writes profiles/traffic_<workload>.json."""
+    cf = max(_counter_means(copy_fetch_csv, "FETCH_SIZE").items(), key=lambda kv: kv[1])
+    cw = max(_counter_means(copy_write_csv, "WRITE_SIZE").items(), key=lambda kv: kv[1])
+    f_fetch = copy_bytes / (cf[1] * 1024.0)
+    f_write = copy_bytes / (cw[1] * 1024.0)
+    fetch = _counter_means(fetch_csv, "FETCH_SIZE")
+    write = _counter_means(write_csv, "WRITE_SIZE")
+    kernels = {}
+    for name in fetch:
+        if any(k in name for k in ATTN_KERNELS):
+            kernels[name] = {"fetch_bytes": fetch[name] * 1024.0 * f_fetch,
+                             "write_bytes": write.get(name, 0.0) * 1024.0 * f_write}
+    total = sum(v["fetch_bytes"] + v["write_bytes"] for v in kernels.values())
+    rec = {"workload": workload, "kernel_source_hash": kernel_source_hash(), "hbm_bytes_per_launch": total,
+           "copy_probe": {"bytes": copy_bytes, "kernel": cf[0], "fetch_kib": cf[1], "write_kib": cw[1],
+                          "fetch_scale": f_fetch, "write_scale": f_write},
+           "kernels": kernels, "commands": commands}
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(os.path.join(ROOT, "profiles", f"traffic_{workload}.json"), "w") as fh:
+        json.dump(rec, fh, indent=1)
+    print(json.dumps(rec, indent=1))
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -90,7 +147,18 @@ def main() -> int:
     ap.add_argument("--workload", default="llama3_8b_gqa")
     ap.add_argument("--partition-size", type=int, default=None, help="override the workload's partition size")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=None, metavar="BYTES",
+                    help="only run a plain device copy of BYTES (counter calibration)")
+    ap.add_argument("--traffic-summary", nargs=5, default=None,
+                    metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV", "COPY_BYTES"),
+                    help="write profiles/traffic_<workload>.json from rocprofv3 counter_collection.csv files")
+    ap.add_argument("--commands", nargs="*", default=[], help="the profiling command lines, recorded with the summary")
     args = ap.parse_args()
+    if args.traffic_summary:
+        f, w_, cf, cw, cb = args.traffic_summary
+        return traffic_summary(args.workload, f, w_, cf, cw, int(cb), args.commands)
+    if args.copy_probe:
+        return copy_probe(args.copy_probe, max(args.steps, 1))
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (this build has no "
               "multi-GPU path: the decode step shards by kv heads or sequence blocks, see DESIGN.md).",
@@ -177,7 +245,9 @@ def main() -> int:
         "kernel_ms": {"attention_avg": round(attn_avg_s * 1e3, 5),
                       "attention_median": round(statistics.median(attn_ms), 5),
                       "append_avg": round(statistics.mean(append_ms), 5) if append_ms else None},
-        "roofline": {"bound": "hbm", "kernel": "lgm_paged_decode_attn (split-K decode + LSE merge launches)",
+        "roofline": {"bound": "hbm", "kernel": "lgm_paged_decode_attn (" + (
+                     "whole-row decode over equal tile ranges + LSE merge" if ps == 0 else
+                     "split-K partition decode + LSE merge") + ", one call: two launches)",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
     }

@@ -393,3 +393,33 @@ def test_row_plan_workspace_reuse():
     r_out, r_lse = oracle_attention(w, act_raw(w, q_from_qkv(w)), pool_raw(w, w.k_pool), pool_raw(w, w.v_pool))
     assert max_abs(out_values(cfg, outs[0][0]), r_out) <= TOL["bf16"]
     _lse_check(outs[0][1].cpu().numpy(), r_lse)
+
+
+@pytest.mark.parametrize("name", ["llama3_8b_gqa", "long_ctx_splitk"])
+def test_row_plan_back_to_back_different_inputs(name):
+    """Calls with different queries and caches on one workspace, no host sync
+    between them: each must see its own split records, not the previous
+    call's."""
+    over = dict(num_seqs=10, ctx=(1, 6000)) if name == "llama3_8b_gqa" else dict(num_seqs=2, ctx=20000)
+    cfgs = [W.CONFIGS[name].with_(seed=40 + i, num_blocks=None, append=False, partition_size=0, **over)
+            for i in range(3)]
+    ws_list = [W.make_workload(c) for c in cfgs]
+    devs = [to_device(w) for w in ws_list]
+    qs = [q_from_qkv(w).cuda() for w in ws_list]
+    mc = max(d.max_ctx for d in devs)
+    nbytes = max(ops.workspace_bytes(q, d.k_pool, d.block_tables, mc, 0) for q, d in zip(qs, devs))
+    ws = torch.zeros((nbytes,), dtype=torch.uint8, device="cuda")
+    announce("row plan back-to-back", name, nbytes)
+    outs = []
+    for rep in range(2):
+        for q, d, c in zip(qs, devs, cfgs):
+            o, l = ops.paged_decode_attn(q, d.k_pool, d.v_pool, d.block_tables, d.context_lens, mc,
+                                         softmax_scale=c.softmax_scale, partition_size=0, workspace=ws)
+            outs.append((o, l))
+    torch.cuda.synchronize()
+    for i, (w, c) in enumerate(zip(ws_list, cfgs)):
+        r_out, r_lse = oracle_attention(w, act_raw(w, q_from_qkv(w)), pool_raw(w, w.k_pool), pool_raw(w, w.v_pool))
+        for rep in range(2):
+            o, l = outs[rep * len(cfgs) + i]
+            assert max_abs(out_values(c, o), r_out) <= TOL["bf16"]
+            _lse_check(l.cpu().numpy(), r_lse)
