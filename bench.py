@@ -147,6 +147,7 @@ def main() -> int:
     ap.add_argument("--workload", default="llama3_8b_gqa")
     ap.add_argument("--partition-size", type=int, default=None, help="override the workload's partition size")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold", type=int, default=10, help="extra attention calls timed after a cache-evicting write")
     ap.add_argument("--copy-probe", type=int, default=None, metavar="BYTES",
                     help="only run a plain device copy of BYTES (counter calibration)")
     ap.add_argument("--traffic-summary", nargs=5, default=None,
@@ -214,6 +215,22 @@ def main() -> int:
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
+    # Cold calls: a 1 GiB write between calls (outside the event pair) evicts
+    # the previous call's lines from L2 and the 256 MB Infinity Cache.
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    cold_ms = []
+    for _ in range(args.cold):
+        scratch.fill_(1)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        ops.paged_decode_attn(q, k_pool, v_pool, bt, ctx, max_ctx, softmax_scale=cfg.softmax_scale,
+                              partition_size=cfg.partition_size, k_scale=ks, v_scale=vs, out=out, out_lse=lse,
+                              workspace=ws)
+        b.record(stream)
+        b.synchronize()
+        cold_ms.append(a.elapsed_time(b))
+    del scratch
+
     attn_ms = [e[1].elapsed_time(e[2]) for e in events]
     append_ms = [e[0].elapsed_time(e[1]) for e in events] if cfg.append else []
     ms_per_step = wall * 1e3 / args.steps
@@ -244,7 +261,8 @@ def main() -> int:
         "kv_bytes_per_step": kv,
         "kernel_ms": {"attention_avg": round(attn_avg_s * 1e3, 5),
                       "attention_median": round(statistics.median(attn_ms), 5),
-                      "append_avg": round(statistics.mean(append_ms), 5) if append_ms else None},
+                      "append_avg": round(statistics.mean(append_ms), 5) if append_ms else None,
+                      "attention_cold_avg": round(statistics.mean(cold_ms), 5) if cold_ms else None},
         "roofline": {"bound": "hbm", "kernel": "lgm_paged_decode_attn (" + (
                      "whole-row decode over equal tile ranges + LSE merge" if ps == 0 else
                      "split-K partition decode + LSE merge") + ", one call: two launches)",

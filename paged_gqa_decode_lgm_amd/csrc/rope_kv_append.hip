@@ -10,6 +10,8 @@
 // rounded once to fp32.  The rotation itself is fp32 with every product and
 // sum rounded on its own: this translation unit is built with
 // -ffp-contract=off and the pragma below, so no multiply-add is fused.
+// Rows move as eight-element vectors whenever the pointers and the QKV row
+// stride allow it.
 #include "device_num.h"
 #include "lgm_internal.h"
 
@@ -20,6 +22,12 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kMaxHalf = 128;
+
+// Eight consecutive elements of a dtype (one 16-byte load for bf16, two for fp32).
+template <class T>
+struct alignas(8 * sizeof(T)) Vec8 {
+  T v[8];
+};
 
 struct ActF32 {
   using elem_t = float;
@@ -64,6 +72,15 @@ __global__ __launch_bounds__(kThreads) void rope_kv_append_kernel(AppendArgs p) 
   const bool active = ctx >= 1;
   const int pos = active ? ctx - 1 : 0;
 
+  // The slot's table entry is read before the rotation factors are computed,
+  // so its latency overlaps theirs.
+  bool write = false;
+  int64_t slot_base = 0;  // element offset of (block, slot, head 0, 0)
+  if (active) {
+    const int pb = p.block_tables[(int64_t)b * MB + pos / BS];
+    write = (unsigned)pb < (unsigned)p.dims.num_blocks;
+    slot_base = ((int64_t)pb * BS + pos % BS) * (int64_t)Hkv * D;
+  }
   for (int i = threadIdx.x; i < half; i += kThreads) {
     const double w = pow((double)p.rope_theta, (-2.0 * (double)i) / (double)D);
     const double ang = (double)pos * w;
@@ -74,18 +91,80 @@ __global__ __launch_bounds__(kThreads) void rope_kv_append_kernel(AppendArgs p) 
   }
   __syncthreads();
 
-  bool write = false;
-  int64_t slot_base = 0;  // element offset of (block, slot, head 0, 0)
-  if (active) {
-    const int pb = p.block_tables[(int64_t)b * MB + pos / BS];
-    write = (unsigned)pb < (unsigned)p.dims.num_blocks;
-    slot_base = ((int64_t)pb * BS + pos % BS) * (int64_t)Hkv * D;
-  }
-
   const typename A::elem_t* x = static_cast<const typename A::elem_t*>(p.qkv) + (int64_t)b * p.qkv_row_stride;
   typename A::elem_t* qo = static_cast<typename A::elem_t*>(p.q_out) + (int64_t)b * Hq * D;
   typename C::elem_t* kc = static_cast<typename C::elem_t*>(p.k_cache);
   typename C::elem_t* vc = static_cast<typename C::elem_t*>(p.v_cache);
+
+  // Eight-element vectors when every row and pointer allows them (the usual
+  // case: dense packed QKV); element by element otherwise.  The arithmetic is
+  // the same either way.
+  const bool vec = ((uintptr_t)p.qkv % (8 * sizeof(typename A::elem_t)) == 0) &&
+                   ((p.qkv_row_stride * (int64_t)sizeof(typename A::elem_t)) % (8 * sizeof(typename A::elem_t)) == 0) &&
+                   ((uintptr_t)p.q_out % (8 * sizeof(typename A::elem_t)) == 0) &&
+                   ((uintptr_t)p.k_cache % (8 * sizeof(typename C::elem_t)) == 0) &&
+                   ((uintptr_t)p.v_cache % (8 * sizeof(typename C::elem_t)) == 0);
+  if (vec) {
+    using AV = Vec8<typename A::elem_t>;
+    using CV = Vec8<typename C::elem_t>;
+    const int nchunk = half / 8;
+    // Rotate every Q head and every K head: (Hq + Hkv) * D/16 chunks of 8 pairs.
+    for (int t = threadIdx.x; t < (Hq + Hkv) * nchunk; t += kThreads) {
+      const int hh = t / nchunk;
+      const int i0 = 8 * (t - hh * nchunk);
+      const AV lo = *reinterpret_cast<const AV*>(x + hh * D + i0);
+      const AV hi = *reinterpret_cast<const AV*>(x + hh * D + i0 + half);
+      float y0[8], y1[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float c = s_cos[i0 + k];
+        const float sn = s_sin[i0 + k];
+        const float x0 = A::load(&lo.v[k]);
+        const float x1 = A::load(&hi.v[k]);
+        const float a0 = x0 * c;
+        const float b0 = x1 * sn;
+        y0[k] = a0 - b0;
+        const float a1 = x1 * c;
+        const float b1 = x0 * sn;
+        y1[k] = a1 + b1;
+      }
+      if (hh < Hq) {
+        AV o0, o1;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          o0.v[k] = A::store(y0[k]);
+          o1.v[k] = A::store(y1[k]);
+        }
+        *reinterpret_cast<AV*>(qo + hh * D + i0) = o0;
+        *reinterpret_cast<AV*>(qo + hh * D + i0 + half) = o1;
+      } else if (write) {
+        const int g = hh - Hq;
+        const float sc = p.k_scale ? p.k_scale[g] : 1.f;
+        CV o0, o1;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          o0.v[k] = C::store(y0[k], sc);
+          o1.v[k] = C::store(y1[k], sc);
+        }
+        *reinterpret_cast<CV*>(kc + slot_base + g * D + i0) = o0;
+        *reinterpret_cast<CV*>(kc + slot_base + g * D + i0 + half) = o1;
+      }
+    }
+    // V heads are stored unrotated.
+    if (write) {
+      const typename A::elem_t* xv = x + (Hq + Hkv) * D;
+      for (int t = threadIdx.x; t < Hkv * D / 8; t += kThreads) {
+        const int g = (8 * t) / D;
+        const float sc = p.v_scale ? p.v_scale[g] : 1.f;
+        const AV in = *reinterpret_cast<const AV*>(xv + 8 * t);
+        CV o;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) o.v[k] = C::store(A::load(&in.v[k]), sc);
+        *reinterpret_cast<CV*>(vc + slot_base + 8 * t) = o;
+      }
+    }
+    return;
+  }
 
   // Rotate every Q head and every K head: (Hq + Hkv) * D/2 pairs.
   const int nrot = (Hq + Hkv) * half;
