@@ -215,12 +215,15 @@ def main() -> int:
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    # Cold calls: a 1 GiB write between calls (outside the event pair) evicts
-    # the previous call's lines from L2 and the 256 MB Infinity Cache.
-    scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    # Cold calls: reading 1 GiB between calls (outside the event pair) evicts
+    # the previous call's lines from L2 and the 256 MB Infinity Cache.  A read,
+    # not a write: evicting a write's dirty lines would charge the next call
+    # with someone else's write-back traffic.
+    scratch = torch.zeros(1 << 27, dtype=torch.int64, device=dev)
+    torch.sum(scratch)
     cold_ms = []
     for _ in range(args.cold):
-        scratch.fill_(1)
+        torch.sum(scratch)
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(stream)
         ops.paged_decode_attn(q, k_pool, v_pool, bt, ctx, max_ctx, softmax_scale=cfg.softmax_scale,
