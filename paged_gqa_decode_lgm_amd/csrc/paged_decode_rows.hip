@@ -98,8 +98,8 @@ __device__ __forceinline__ void row_load_k(const DecodeArgs& p, int g, int px, i
   const int64_t block_bytes = (int64_t)kBS * tok_bytes;
   const int off = C::k_lane_off(g, tok_bytes, lane & 15, lane >> 4);
   const int ex = px >= 0 ? px : 0, ey = py >= 0 ? py : ex;
-  C::load_k(tr.kx, block_rsrc(p.k_cache, block_bytes, ex), off, tok_bytes);
-  C::load_k(tr.ky, block_rsrc(p.k_cache, block_bytes, ey), off, tok_bytes);
+  C::template load_k<kStreamPolicy>(tr.kx, block_rsrc(p.k_cache, block_bytes, ex), off, tok_bytes);
+  C::template load_k<kStreamPolicy>(tr.ky, block_rsrc(p.k_cache, block_bytes, ey), off, tok_bytes);
 }
 template <class C>
 __device__ __forceinline__ void row_load_v(const DecodeArgs& p, int g, int px, int py, int lane, TileRegs<C>& tr) {
@@ -107,8 +107,8 @@ __device__ __forceinline__ void row_load_v(const DecodeArgs& p, int g, int px, i
   const int64_t block_bytes = (int64_t)kBS * tok_bytes;
   const int off = C::v_lane_off(g, tok_bytes, lane & 15, lane >> 4);
   const int ex = px >= 0 ? px : 0, ey = py >= 0 ? py : ex;
-  C::load_v(tr.vx, block_rsrc(p.v_cache, block_bytes, ex), off, tok_bytes);
-  C::load_v(tr.vy, block_rsrc(p.v_cache, block_bytes, ey), off, tok_bytes);
+  C::template load_v<kStreamPolicy>(tr.vx, block_rsrc(p.v_cache, block_bytes, ex), off, tok_bytes);
+  C::template load_v<kStreamPolicy>(tr.vy, block_rsrc(p.v_cache, block_bytes, ey), off, tok_bytes);
 }
 
 // Writes one head's result of a segment: the final output (bf16, normalised)
