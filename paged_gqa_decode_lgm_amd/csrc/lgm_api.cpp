@@ -191,6 +191,9 @@ lgm_status plan_decode(const char* fn, const lgm_paged_dims& d, int32_t max_ctx,
     const int64_t tiles = streams * ((max_ctx + kRowsTile - 1) / kRowsTile);
     if (tiles > (int64_t)INT32_MAX)
       return fail(LGM_ERR_UNSUPPORTED, fn, "num_seqs * head groups * tiles = %lld: too many", (long long)tiles);
+    if ((int64_t)d.num_seqs * d.num_q_heads > (int64_t)INT32_MAX - 1024)  // merge rows are int-indexed
+      return fail(LGM_ERR_UNSUPPORTED, fn, "num_seqs * num_q_heads = %lld: too many",
+                  (long long)d.num_seqs * d.num_q_heads);
     int64_t W = (tiles + kRowsMinTiles - 1) / kRowsMinTiles;
     W = W < 1 ? 1 : (W > kRowsWorkgroups ? kRowsWorkgroups : W);
     pl.W = (int32_t)W;

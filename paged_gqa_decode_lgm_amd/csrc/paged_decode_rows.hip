@@ -310,84 +310,108 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void paged_decode_rows_kernel(De
 // merge).  One workgroup per (sequence, query head); streams written whole
 // by the decode kernel are skipped, empty contexts get out = 0, lse = -inf.
 constexpr int kMergeThreads = 256;
-constexpr int kMergeGroups = kMergeThreads / (kD / 4);  // records in flight per pass
+constexpr int kMergeRows = kMergeThreads / kWaveSize;  // one wave per (sequence, query head) row
+constexpr int kMergeLanes = kD / 8;                    // lanes per record row: eight columns each
+constexpr int kMergeGroups = kWaveSize / kMergeLanes;  // records in flight per wave
 
-template <int G>
+// Merge of the records of one output row.  Lane k first holds the record of
+// the k-th workgroup of the stream (64 at a time) and its weight
+// exp(lse - max); the wave then works as four groups of 16 lanes, each group
+// folding every fourth record into eight columns per lane, and the groups are
+// summed by lane shuffles at the end: no LDS, no barrier.
 __global__ __launch_bounds__(kMergeThreads) void rows_merge_kernel(DecodeArgs p, RowsArgs r) {
-  __shared__ float red[kMergeThreads];
-  __shared__ float s_acc[kMergeGroups][kD];
-  const int h = blockIdx.x;
-  const int b = blockIdx.y;
+  const int lane = threadIdx.x % kWaveSize;
+  const int Hq = p.dims.num_q_heads;
+  const int orow = blockIdx.x * kMergeRows + threadIdx.x / kWaveSize;
+  if (orow >= p.dims.num_seqs * Hq) return;
+  const int b = orow / Hq;
+  const int h = orow - b * Hq;
+  const int G = Hq / p.dims.num_kv_heads;
   const int g = h / G;
   const int HG = r.head_group;
   const int nhg = p.dims.num_kv_heads / HG;
   const int u = b * nhg + g / HG;
-  const int64_t orow = (int64_t)b * p.dims.num_q_heads + h;
-  if (clamped_ctx(p, b) == 0) {
-    if (threadIdx.x < kD) static_cast<uint16_t*>(p.out)[orow * kD + threadIdx.x] = 0;
-    if (threadIdx.x == 0 && p.out_lse) p.out_lse[orow] = -INFINITY;
+  // The context length and the stream's workgroup span do not depend on
+  // each other: both loads are issued before either is used.
+  const int ctx = clamped_ctx(p, b);
+  const int i0 = r.wg_first[u];
+  const int i1 = r.wg_last[u];
+  uint16_t* out = static_cast<uint16_t*>(p.out) + (int64_t)orow * kD;
+  const int grp = lane / kMergeLanes;
+  const int c = lane % kMergeLanes;
+  if (ctx == 0) {
+    if (grp == 0) *reinterpret_cast<uint4*>(out + 8 * c) = make_uint4(0, 0, 0, 0);
+    if (lane == 0 && p.out_lse) p.out_lse[orow] = -INFINITY;
     return;
   }
-  const int i0 = r.wg_first[u], i1 = r.wg_last[u];
-  if (i0 == i1) return;
+  if (i0 == i1) return;  // the only workgroup of the stream wrote the row itself
   const int n = i1 - i0 + 1;
+  const int64_t rec_rows = (int64_t)HG * G;
   const int hrow = (g % HG) * G + h % G;
   // Record of the k-th workgroup from i0, or -1 for a workgroup whose range
   // is empty (there are more workgroups than tiles).
-  auto rec_of = [&](int k) -> int64_t {
+  auto rec_of = [&](int k) -> int {
     const int w = i0 + k;
     const int f = r.first_stream[w];
-    return f < 0 ? -1 : 2 * (int64_t)w + (f == u ? 0 : 1);
+    return f < 0 ? -1 : 2 * w + (f == u ? 0 : 1);
   };
-  auto lse_of = [&](int64_t rec) -> float { return rec < 0 ? -INFINITY : r.rec_lse[rec * HG * G + hrow]; };
+  auto lse_of = [&](int rec) -> float { return rec < 0 ? -INFINITY : r.rec_lse[rec * rec_rows + hrow]; };
 
-  float mx = -INFINITY;
-  for (int k = threadIdx.x; k < n; k += kMergeThreads) mx = fmaxf(mx, lse_of(rec_of(k)));
-  red[threadIdx.x] = mx;
-  __syncthreads();
-  for (int s = kMergeThreads / 2; s > 0; s >>= 1) {
-    if (threadIdx.x < s) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + s]);
-    __syncthreads();
-  }
-  const float M = red[0];
-  const float ms = M == -INFINITY ? 0.f : M;
-  __syncthreads();
-  float sw = 0.f;
-  for (int k = threadIdx.x; k < n; k += kMergeThreads) sw += expf(lse_of(rec_of(k)) - ms);
-  red[threadIdx.x] = sw;
-  __syncthreads();
-  for (int s = kMergeThreads / 2; s > 0; s >>= 1) {
-    if (threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
-    __syncthreads();
-  }
-  const float S = red[0];
-
-  const int td = threadIdx.x % (kD / 4);
-  const int pg = threadIdx.x / (kD / 4);
-  float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int k = pg; k < n; k += kMergeGroups) {
-    const int64_t rec = rec_of(k);
-    if (rec < 0) continue;
-    const float w = expf(r.rec_lse[rec * HG * G + hrow] - ms);
-    const float4 v = reinterpret_cast<const float4*>(r.rec_out + (rec * HG * G + hrow) * kD)[td];
-    a.x = fmaf(w, v.x, a.x);
-    a.y = fmaf(w, v.y, a.y);
-    a.z = fmaf(w, v.z, a.z);
-    a.w = fmaf(w, v.w, a.w);
-  }
-  s_acc[pg][4 * td + 0] = a.x;
-  s_acc[pg][4 * td + 1] = a.y;
-  s_acc[pg][4 * td + 2] = a.z;
-  s_acc[pg][4 * td + 3] = a.w;
-  __syncthreads();
-  if (threadIdx.x < kD) {
-    float o = 0.f;
+  // The first 64 records stay in registers; longer spans reload the rest.
+  const int rc0 = lane < n ? rec_of(lane) : -1;
+  const float ls0 = lse_of(rc0);
+  float mx = ls0;
+  for (int k = lane + kWaveSize; k < n; k += kWaveSize) mx = fmaxf(mx, lse_of(rec_of(k)));
 #pragma unroll
-    for (int k = 0; k < kMergeGroups; ++k) o += s_acc[k][threadIdx.x];
-    o = S > 0.f ? o / S : 0.f;
-    static_cast<uint16_t*>(p.out)[orow * kD + threadIdx.x] = f32_to_bf16_rne(o);
+  for (int o = 1; o < kWaveSize; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+  const float ms = mx == -INFINITY ? 0.f : mx;
+  const float w0 = rc0 < 0 ? 0.f : expf(ls0 - ms);
+  float sw = w0;
+  for (int k = lane + kWaveSize; k < n; k += kWaveSize) {
+    const int rc = rec_of(k);
+    sw += rc < 0 ? 0.f : expf(lse_of(rc) - ms);
   }
-  if (threadIdx.x == 0 && p.out_lse) p.out_lse[orow] = S > 0.f ? M + logf(S) : -INFINITY;
+  const float S = group_sum<kWaveSize>(sw);
+
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  // A record that is absent reads record 0 (always in the workspace) and is
+  // dropped by a select, so unwritten workspace bytes never reach the sum.
+  auto fold = [&](int rk, float wk) {
+    const bool ok = rk >= 0;
+    const float4* src = reinterpret_cast<const float4*>(r.rec_out + ((ok ? rk : 0) * rec_rows + hrow) * kD) + 2 * c;
+    const float4 v0 = src[0];
+    const float4 v1 = src[1];
+    const float x[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = fmaf(wk, ok ? x[e] : 0.f, acc[e]);
+  };
+  const int n0 = n < kWaveSize ? n : kWaveSize;
+#pragma unroll 4
+  for (int k0 = 0; k0 < n0; k0 += kMergeGroups) {
+    const int k = k0 + grp;  // below 64; lanes at or past n hold record -1
+    fold(__shfl(rc0, k), __shfl(w0, k));
+  }
+  for (int k0 = kWaveSize; k0 < n; k0 += kMergeGroups) {
+    const int k = k0 + grp;
+    const int rk = k < n ? rec_of(k) : -1;
+    fold(rk, rk < 0 ? 0.f : expf(lse_of(rk) - ms));
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    acc[e] += __shfl_xor(acc[e], kMergeLanes);
+    acc[e] += __shfl_xor(acc[e], 2 * kMergeLanes);
+  }
+  if (grp == 0) {
+    uint32_t o[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float a = S > 0.f ? acc[2 * e] / S : 0.f;
+      const float bb = S > 0.f ? acc[2 * e + 1] / S : 0.f;
+      o[e] = (uint32_t)f32_to_bf16_rne(a) | ((uint32_t)f32_to_bf16_rne(bb) << 16);
+    }
+    *reinterpret_cast<uint4*>(out + 8 * c) = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+  if (lane == 0 && p.out_lse) p.out_lse[orow] = S > 0.f ? mx + logf(S) : -INFINITY;
 }
 
 template <class C, int G>
@@ -398,7 +422,8 @@ hipError_t launch_group(const DecodeArgs& a, const RowsArgs& r, hipStream_t s) {
     hipLaunchKernelGGL((paged_decode_rows_kernel<C, G, 1>), dim3(r.num_wg), dim3(kDecodeThreads), 0, s, a, r);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((rows_merge_kernel<G>), dim3(a.dims.num_q_heads, a.dims.num_seqs), dim3(kMergeThreads), 0, s, a,
+  const int merge_rows = a.dims.num_seqs * a.dims.num_q_heads;
+  hipLaunchKernelGGL(rows_merge_kernel, dim3((merge_rows + kMergeRows - 1) / kMergeRows), dim3(kMergeThreads), 0, s, a,
                      r);
   return hipGetLastError();
 }
