@@ -51,10 +51,9 @@ def measured_traffic(workload: str, kv_bytes: int):
     return t.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, min_seconds: float = 12.0, max_passes: int = 10):
-    """The fp64 oracle on the whole batch (host copies of the same inputs), one
-    thread; passes repeat until ~min_seconds of work, the median pass is kept."""
-    import numpy as np
+def _oracle_passes(w, threads: int, min_seconds: float, max_passes: int):
+    """Times the fp64 oracle over the whole batch under a BLAS/OpenMP thread
+    limit; passes repeat until ~min_seconds of work.  Returns the pass times."""
     from threadpoolctl import threadpool_limits
 
     import workloads as W
@@ -66,7 +65,7 @@ def cpu_baseline(w, min_seconds: float = 12.0, max_passes: int = 10):
     q = OAP.act_to_f64(W.storage_bits(w.qkv)[:, : c.num_q_heads * c.head_dim], c.act).reshape(
         c.num_seqs, c.num_q_heads, c.head_dim)
     times = []
-    with threadpool_limits(1):
+    with threadpool_limits(threads):
         while len(times) < max_passes and (not times or sum(times) < min_seconds):
             t0 = time.perf_counter()
             OA.paged_decode(q, kp, vp, w.block_tables.numpy(), w.context_lens.numpy(), c.softmax_scale,
@@ -74,12 +73,75 @@ def cpu_baseline(w, min_seconds: float = 12.0, max_passes: int = 10):
                             k_scale=None if w.k_scale is None else w.k_scale.numpy(),
                             v_scale=None if w.v_scale is None else w.v_scale.numpy())
             times.append(time.perf_counter() - t0)
+    return times
+
+
+def host_threads() -> int:
+    """Cores this process may use: its CPU affinity, capped by OMP_NUM_THREADS when that is set."""
+    n = len(os.sched_getaffinity(0))
+    try:
+        n = min(n, int(os.environ.get("OMP_NUM_THREADS", n)))
+    except ValueError:
+        pass
+    return max(n, 1)
+
+
+def cpu_baseline(w, min_seconds: float = 12.0, max_passes: int = 10):
+    """The fp64 oracle on the whole batch (host copies of the same inputs),
+    one thread; the median pass is kept.  The same run with the BLAS/OpenMP
+    pools at every available core is reported beside it."""
+    c = w.cfg
+    times = _oracle_passes(w, 1, min_seconds, max_passes)
     t = statistics.median(times)
+    n = host_threads()
+    times_n = _oracle_passes(w, n, min_seconds / 2, max_passes)
+    tn = statistics.median(times_n)
     return {"value": round(w.kv_bytes() / t / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "tokens_per_s": round(c.num_seqs / t, 3),
             "sample": f"attention over the whole {c.name} batch ({c.num_seqs} sequences, "
                       f"{int(w.context_lens.sum())} cached tokens) in fp64 NumPy, 1 thread, median of "
-                      f"{len(times)} passes of {t:.2f} s"}
+                      f"{len(times)} passes of {t:.2f} s",
+            "all_cores": {"value": round(w.kv_bytes() / tn / 1e9, 4), "unit": "GB/s", "cores": n,
+                          "tokens_per_s": round(c.num_seqs / tn, 3),
+                          "sample": f"the same, BLAS/OpenMP pools limited to {n} threads, median of "
+                                    f"{len(times_n)} passes of {tn:.2f} s"}}
+
+
+def read_ceiling(torch, nbytes: int = 4 << 30, reps: int = 10):
+    """The measured streaming ceiling: lgm_stream_read_probe over an nbytes
+    buffer, for a few workgroup counts with and without the non-temporal
+    hint; the fastest median is the ceiling."""
+    from paged_gqa_decode_lgm_amd import _binding as Bn
+
+    dev = torch.device("cuda:0")
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    best = None
+    for nwg in (1024, 2048, 4096):
+        for nt in (1, 0):
+            call = lambda: Bn.lgm_stream_read_probe(buf, nbytes, nwg, nt, sink)
+            call()
+            ms = []
+            for _ in range(reps):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                call()
+                b.record(stream)
+                b.synchronize()
+                ms.append(a.elapsed_time(b))
+            gbs = nbytes / (statistics.median(ms) / 1e3) / 1e9
+            if best is None or gbs > best["gbs"]:
+                best = {"gbs": round(gbs, 1), "workgroups": nwg, "nontemporal": bool(nt)}
+    del buf
+    best.update({"probe": f"read-only stream of {nbytes >> 30} GiB, 16-byte loads, median of {reps}",
+                 "pct_of_hbm_peak": round(100.0 * best["gbs"] / HBM_PEAK_GBS, 2)})
+    return best
+
+
+def _quantile(xs, q: float) -> float:
+    ys = sorted(xs)
+    return ys[min(len(ys) - 1, int(q * len(ys)))]
 
 
 ATTN_KERNELS = ("paged_decode", "merge")  # the launches of one lgm_paged_decode_attn call
@@ -147,6 +209,7 @@ def main() -> int:
     ap.add_argument("--workload", default="llama3_8b_gqa")
     ap.add_argument("--partition-size", type=int, default=None, help="override the workload's partition size")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the read-only streaming ceiling probe")
     ap.add_argument("--cold", type=int, default=10, help="extra attention calls timed after a cache-evicting write")
     ap.add_argument("--copy-probe", type=int, default=None, metavar="BYTES",
                     help="only run a plain device copy of BYTES (counter calibration)")
@@ -264,6 +327,8 @@ def main() -> int:
         "kv_bytes_per_step": kv,
         "kernel_ms": {"attention_avg": round(attn_avg_s * 1e3, 5),
                       "attention_median": round(statistics.median(attn_ms), 5),
+                      "attention_p10": round(_quantile(attn_ms, 0.1), 5),
+                      "attention_p90": round(_quantile(attn_ms, 0.9), 5),
                       "append_avg": round(statistics.mean(append_ms), 5) if append_ms else None,
                       "attention_cold_avg": round(statistics.mean(cold_ms), 5) if cold_ms else None},
         "roofline": {"bound": "hbm", "kernel": "lgm_paged_decode_attn (" + (
@@ -272,6 +337,10 @@ def main() -> int:
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
     }
+    if not args.no_ceiling:
+        ceil = read_ceiling(torch)
+        ceil["attention_pct_of_ceiling"] = round(100.0 * achieved / ceil["gbs"], 2)
+        rec["ceiling"] = ceil
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(rec), flush=True)

@@ -14,7 +14,8 @@ import os
 import re
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblgm.so")
-HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "lgm.h")
+INCLUDE = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+HEADER = os.path.join(INCLUDE, "lgm.h")
 
 LGM_OK, LGM_ERR_INVALID_ARGUMENT, LGM_ERR_UNSUPPORTED, LGM_ERR_WORKSPACE_TOO_SMALL, LGM_ERR_HIP = range(5)
 LGM_F32, LGM_BF16, LGM_FP8_E4M3 = 0, 1, 2
@@ -64,15 +65,22 @@ def lib() -> ctypes.CDLL:
         L.lgm_last_error.restype = ctypes.c_char_p
         L.lgm_abi_version.argtypes = []
         L.lgm_abi_version.restype = i32
+        L.lgm_stream_read_probe.argtypes = [vp, sz, i32, i32, vp, vp]
+        L.lgm_stream_read_probe.restype = i32
         _lib = L
     return _lib
 
 
 def header_functions() -> list:
-    """Names of the functions include/lgm.h declares."""
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s+(lgm_[a-z_0-9]+)\s*\(", text, flags=re.M)
+    """Names of the functions the headers under include/ declare."""
+    names = []
+    for h in sorted(os.listdir(INCLUDE)):
+        if not h.endswith(".h"):
+            continue
+        text = open(os.path.join(INCLUDE, h)).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names += re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s+(lgm_[a-z_0-9]+)\s*\(", text, flags=re.M)
+    return names
 
 
 def _ptr(x):
@@ -144,3 +152,7 @@ def lgm_last_error() -> str:
 
 def lgm_abi_version() -> int:
     return lib().lgm_abi_version()
+
+
+def lgm_stream_read_probe(src, nbytes, num_workgroups, nontemporal, sink, stream=None):
+    _check(lib().lgm_stream_read_probe(_ptr(src), nbytes, num_workgroups, nontemporal, _ptr(sink), _stream(stream)))

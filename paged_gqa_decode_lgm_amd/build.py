@@ -34,6 +34,7 @@ UNITS = {
     "paged_decode_mfma.hip": [],
     "paged_decode_rows.hip": [],
     "lse_merge.hip": [],
+    "stream_probe.hip": [],
 }
 
 

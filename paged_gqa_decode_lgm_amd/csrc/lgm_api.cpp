@@ -12,6 +12,7 @@
 #include <string>
 
 #include "lgm_internal.h"
+#include "lgm_probe.h"
 
 namespace {
 
@@ -460,6 +461,32 @@ lgm_status lgm_lse_merge(void* out, float* out_lse, const float* partial_out, co
   lgm::MergeArgs m{out, out_lse, partial_out, partial_lse, num_partitions, nullptr, lgm::PartitionPlan{1, 1}, 0,
                    num_seqs, num_q_heads, head_dim, max_partitions, 0};
   const hipError_t e = lgm::launch_lse_merge(m, out_dtype, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(LGM_ERR_HIP, fn, "kernel launch failed: %s", hipGetErrorString(e));
+  return LGM_OK;
+}
+
+lgm_status lgm_stream_read_probe(const void* src, size_t bytes, int32_t num_workgroups, int32_t nontemporal,
+                                 uint32_t* sink, void* stream) {
+  const char* fn = "lgm_stream_read_probe";
+  g_err.clear();
+  if (!src) return fail(LGM_ERR_INVALID_ARGUMENT, fn, "src is NULL");
+  if (!sink) return fail(LGM_ERR_INVALID_ARGUMENT, fn, "sink is NULL");
+  if ((uintptr_t)src % 16 != 0) return fail(LGM_ERR_INVALID_ARGUMENT, fn, "src %p must be 16-byte aligned", src);
+  if (num_workgroups < 1 || num_workgroups > 65536)
+    return fail(LGM_ERR_INVALID_ARGUMENT, fn, "num_workgroups = %d must be in [1, 65536]", num_workgroups);
+  const uint64_t unit = (uint64_t)num_workgroups * lgm::stream_probe_granule();
+  if (bytes == 0 || bytes % unit != 0)
+    return fail(LGM_ERR_INVALID_ARGUMENT, fn, "bytes = %zu must be a positive multiple of num_workgroups * %d = %llu",
+                bytes, lgm::stream_probe_granule(), (unsigned long long)unit);
+  if (bytes / num_workgroups > (uint64_t)INT32_MAX)
+    return fail(LGM_ERR_INVALID_ARGUMENT, fn, "bytes / num_workgroups = %llu exceeds INT32_MAX",
+                (unsigned long long)(bytes / num_workgroups));
+  const Span outs[] = {{"sink", (uintptr_t)sink, 4}};
+  const Span ins[] = {{"src", (uintptr_t)src, (int64_t)bytes}};
+  lgm_status st = check_no_alias(fn, outs, 1, ins, 1);
+  if (st != LGM_OK) return st;
+  const hipError_t e =
+      lgm::launch_stream_read_probe(src, (int64_t)bytes, num_workgroups, nontemporal != 0, sink, (hipStream_t)stream);
   if (e != hipSuccess) return fail(LGM_ERR_HIP, fn, "kernel launch failed: %s", hipGetErrorString(e));
   return LGM_OK;
 }

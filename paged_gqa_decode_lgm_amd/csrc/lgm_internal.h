@@ -102,6 +102,11 @@ struct MergeArgs {
 
 // Each returns hipSuccess or the launch error.
 hipError_t launch_rope_kv_append(const AppendArgs& a, lgm_dtype act, lgm_dtype cache, hipStream_t s);
+// Read-only streaming probe: bytes must be a multiple of num_wg *
+// stream_probe_granule(), and bytes / num_wg must fit in an int.
+int stream_probe_granule();
+hipError_t launch_stream_read_probe(const void* src, int64_t bytes, int num_wg, bool nontemporal, uint32_t* sink,
+                                    hipStream_t s);
 hipError_t launch_paged_decode(const DecodeArgs& a, lgm_dtype act, lgm_dtype cache, hipStream_t s);
 hipError_t launch_lse_merge(const MergeArgs& a, lgm_dtype out_dtype, hipStream_t s);
 

@@ -29,7 +29,8 @@ def test_library_loads_and_exports_every_header_function():
     lib = L.lib()
     names = L.header_functions()
     assert set(names) == {"lgm_rope_kv_append", "lgm_paged_decode_partition_size", "lgm_paged_decode_workspace_size",
-                          "lgm_paged_decode_attn", "lgm_lse_merge", "lgm_last_error", "lgm_abi_version"}
+                          "lgm_paged_decode_attn", "lgm_lse_merge", "lgm_last_error", "lgm_abi_version",
+                          "lgm_stream_read_probe"}
     for n in names:
         assert hasattr(lib, n), n
     assert L.lgm_abi_version() == 1
@@ -253,3 +254,24 @@ def test_binding_refuses_to_run_without_the_library(monkeypatch, tmp_path):
     monkeypatch.setattr(Bn, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="missing"):
         Bn.lib()
+
+
+# ------------------------------------------------------------------ streaming probe
+@pytest.mark.parametrize("kw, msg", [
+    (dict(src=None), "src is NULL"),
+    (dict(sink=None), "sink is NULL"),
+    (dict(src=addr(0) + 8), "16-byte aligned"),
+    (dict(num_workgroups=0), "num_workgroups"),
+    (dict(num_workgroups=65537), "num_workgroups"),
+    (dict(nbytes=0), "positive multiple"),
+    (dict(nbytes=4 * 16384 + 16), "positive multiple"),
+    (dict(nbytes=(1 << 31) * 4, num_workgroups=2), "INT32_MAX"),
+    (dict(sink=addr(0) + 64), "overlap"),
+])
+def test_stream_probe_rejects_before_launch(kw, msg):
+    a = dict(src=addr(0), nbytes=4 * 16384, num_workgroups=4, nontemporal=1, sink=addr(1), stream=0)
+    a.update(kw)
+    with pytest.raises(L.LgmError) as e:
+        Bn.lgm_stream_read_probe(**a)
+    assert e.value.status == L.LGM_ERR_INVALID_ARGUMENT
+    assert msg in e.value.message

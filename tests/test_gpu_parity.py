@@ -423,3 +423,19 @@ def test_row_plan_back_to_back_different_inputs(name):
             o, l = outs[rep * len(cfgs) + i]
             assert max_abs(out_values(c, o), r_out) <= TOL["bf16"]
             _lse_check(l.cpu().numpy(), r_lse)
+
+
+@pytest.mark.gpu
+def test_stream_read_probe_reads_without_writing():
+    """The streaming-ceiling probe only reads: its sink is left alone for a
+    buffer whose words XOR to zero, and the buffer is unchanged."""
+    from paged_gqa_decode_lgm_amd import _binding as Bn
+    nbytes = 8 * 16384 * 4
+    announce("stream read probe", nbytes)
+    buf = torch.full((nbytes,), 7, dtype=torch.uint8, device="cuda")
+    sink = torch.full((1,), -5, dtype=torch.int32, device="cuda")
+    for nt in (0, 1):
+        Bn.lgm_stream_read_probe(buf, nbytes, 8, nt, sink)
+    torch.cuda.synchronize()
+    assert int(sink.item()) == -5
+    assert bool((buf == 7).all())
