@@ -15,11 +15,18 @@ details open; the readings taken here are:
   activation dtype;
 * FP8: code = E4M3(y / scale[g]) with an fp32 division, rounded to nearest
   even, saturating (codecs.e4m3_encode);
+* FP4 (mainarch README, decode-attention section: E2M1 KV with E8M0 block
+  scales): each 32-element block of the row is quantised with the MX rule of
+  codecs.mx_fp4_quantize (scale exponent floor(log2 amax) - 2, codes rounded
+  to nearest even and saturating at 6); the division by a power-of-two scale
+  is exact, so the recipe needs no fp32 step of its own.  Codes go to the
+  block's code area and the scale bytes to its scale area (codecs.fp4_block_views);
 * a sequence with ctx <= 0 is inactive: nothing is written to the caches and
   its q_out row is its Q rotated by angle zero, i.e. copied.
 
 Storage arrays: act 'f32' -> float32 values, 'bf16' -> uint16 bits;
-cache 'f32' -> float32, 'bf16' -> uint16 bits, 'fp8' -> uint8 codes.
+cache 'f32' -> float32, 'bf16' -> uint16 bits, 'fp8' -> uint8 codes,
+'fp4' -> uint8 blocks [num_blocks, block_bytes] (codes, then scales).
 
 Two modes:
   mode="recipe"  the fp32 evaluation recipe (rope.rope_neox_f32_recipe, fp32
@@ -106,6 +113,10 @@ def rope_kv_append(qkv, context_lens, block_tables, k_pool, v_pool, *, num_q_hea
     q_out = f64_to_act(q_rot, act)
     k_new = np.array(k_pool, copy=True)
     v_new_pool = np.array(v_pool, copy=True)
+    if cache == "fp4":
+        k_parts = codecs.fp4_block_views(k_new, bs, Hkv, D)
+        v_parts = codecs.fp4_block_views(v_new_pool, bs, Hkv, D)
+        assert all(np.shares_memory(a, base) for a, base in ((k_parts[0], k_new), (v_parts[1], v_new_pool)))
     slots = []
     bt = np.asarray(block_tables)
     for b in range(B):
@@ -114,7 +125,13 @@ def rope_kv_append(qkv, context_lens, block_tables, k_pool, v_pool, *, num_q_hea
             continue
         p = int(ctx[b] - 1)
         pb, off = int(bt[b, p // bs]), p % bs
-        k_new[pb, off] = f64_to_cache(k_rot[b], cache, k_scale, fp32_div=(mode == "recipe"))
-        v_new_pool[pb, off] = f64_to_cache(v_in[b], cache, v_scale, fp32_div=(mode == "recipe"))
+        if cache == "fp4":
+            for parts, rows in ((k_parts, k_rot[b]), (v_parts, v_in[b])):
+                codes, scale_bytes = codecs.mx_fp4_quantize(rows)
+                parts[0][pb, off] = codecs.fp4_pack(codes)
+                parts[1][pb, off] = scale_bytes
+        else:
+            k_new[pb, off] = f64_to_cache(k_rot[b], cache, k_scale, fp32_div=(mode == "recipe"))
+            v_new_pool[pb, off] = f64_to_cache(v_in[b], cache, v_scale, fp32_div=(mode == "recipe"))
         slots.append((pb, off))
     return AppendResult(q_out, k_new, v_new_pool, q_rot, k_rot, v_in, slots)

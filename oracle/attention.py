@@ -15,7 +15,9 @@ G = Hq / Hkv query heads; the pages only say that a group of query heads
 shares one KV head) and L = context_lens[b]:
     K_j, V_j = cache rows of token j < L, found through the block table:
                physical block block_tables[b, j // bs], slot j % bs
-               (FP8 rows are decoded and multiplied by the head's scale)
+               (FP8 rows are decoded and multiplied by the head's scale;
+               FP4 rows are E2M1 codes times their 32-element blocks' E8M0
+               scales, oracle.codecs)
     s_j   = scale * <q_h, K_j>
     p     = softmax(s)
     out_h = sum_j p_j V_j,   lse_h = log sum_j exp(s_j)   (natural log)
@@ -38,23 +40,40 @@ from . import codecs
 
 
 def decode_rows(raw, cache: str, scale_g: Optional[float] = None) -> np.ndarray:
-    """Cache storage -> float64 values (FP8: decoded byte times the scale)."""
+    """Cache storage -> float64 values (FP8: decoded byte times the scale;
+    FP4: raw is (packed codes, scale bytes) of the rows)."""
     if cache == "f32":
         return np.asarray(raw, dtype=np.float32).astype(np.float64)
     if cache == "bf16":
         return codecs.bf16_decode(raw)
     if cache == "fp8":
         return codecs.e4m3_decode(raw) * np.float64(np.float32(scale_g))
+    if cache == "fp4":
+        return codecs.mx_fp4_dequantize(*raw)
     raise ValueError(cache)
+
+
+def kv_source(pool, cache: str, block_size: int, num_kv_heads: int, head_dim: int):
+    """A pool as gather_kv indexes it: [NB, bs, Hkv, D] storage, or for FP4
+    (uint8 [NB, block_bytes] blocks of codes then scales) the pair of views
+    (codes [NB, bs, Hkv, D/2], scales [NB, bs, Hkv, D/32])."""
+    if cache == "fp4":
+        return codecs.fp4_block_views(pool, block_size, num_kv_heads, head_dim)
+    return np.asarray(pool)
 
 
 def gather_kv(pool, block_tables, b: int, L: int, g: int, block_size: int, cache: str,
               scale=None) -> np.ndarray:
-    """Rows j < L of kv head g for sequence b, through the block table: [L, D]."""
+    """Rows j < L of kv head g for sequence b, through the block table: [L, D].
+    ``pool`` as kv_source returns it."""
     if L <= 0:
-        return np.zeros((0, pool.shape[-1]), dtype=np.float64)
+        D = 2 * pool[0].shape[-1] if cache == "fp4" else pool.shape[-1]
+        return np.zeros((0, D), dtype=np.float64)
     j = np.arange(L)
     pb = np.asarray(block_tables)[b, j // block_size].astype(np.int64)
+    if cache == "fp4":
+        codes, scales = pool
+        return decode_rows((codes[pb, j % block_size, g, :], scales[pb, j % block_size, g, :]), cache)
     raw = np.asarray(pool)[pb, j % block_size, g, :]
     sg = None if scale is None else float(np.asarray(scale)[g])
     return decode_rows(raw, cache, sg)
@@ -87,6 +106,8 @@ def paged_decode(q, k_pool, v_pool, block_tables, context_lens, softmax_scale: f
     out = np.full((B, Hq, D), np.nan)
     lse = np.full((B, Hq), np.nan)
     ctx = np.asarray(context_lens, dtype=np.int64)
+    k_pool = kv_source(k_pool, cache, block_size, num_kv_heads, D)
+    v_pool = kv_source(v_pool, cache, block_size, num_kv_heads, D)
     for b in (range(B) if seqs is None else seqs):
         L = max(int(ctx[b]), 0)
         for g in range(num_kv_heads):
@@ -117,6 +138,8 @@ def paged_decode_partials(q, k_pool, v_pool, block_tables, context_lens, softmax
     o_p = np.zeros((B, Hq, Pmax, D))
     lse_p = np.full((B, Hq, Pmax), -np.inf)
     ctx = np.asarray(context_lens, dtype=np.int64)
+    k_pool = kv_source(k_pool, cache, block_size, num_kv_heads, D)
+    v_pool = kv_source(v_pool, cache, block_size, num_kv_heads, D)
     for b in range(B):
         L = max(int(ctx[b]), 0)
         for g in range(num_kv_heads):

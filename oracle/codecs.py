@@ -101,3 +101,133 @@ def e4m3_encode(x) -> np.ndarray:
     code = code | np.where(neg, np.uint8(0x80), np.uint8(0)).astype(np.uint8)
     code = np.where(np.isnan(a), np.uint8(E4M3_NAN), code).astype(np.uint8)
     return code
+
+
+# ----------------------------------------------------------------- MX FP4: E2M1 codes with E8M0 block scales
+# mainarch's decode-attention section stores KV as 4-bit E2M1 values with
+# E8M0 block scales (dequantised through the hardware's scaled FP4
+# conversion).  The pages give neither the block size nor the scale rule; the
+# oracle takes the OCP Microscaling (MX) v1.0 definitions, where those names
+# come from:
+#   E2M1: 1 sign bit, 2 exponent bits (bias 1), 1 mantissa bit, no infinities
+#         and no NaN: E == 0 -> M * 0.5 (subnormal), else (1 + M/2) * 2**(E-1);
+#         the magnitudes are 0, 0.5, 1, 1.5, 2, 3, 4, 6.
+#   E8M0: an unbiased-exponent byte, value 2**(byte - 127); 0xFF is NaN.
+#   Block: 32 consecutive elements share one scale X = 2**(floor(log2(amax)) - 2),
+#         2 being the exponent of E2M1's largest normal (6 = 1.5 * 2**2);
+#         elements are V_i / X rounded to nearest E2M1, ties to the even
+#         mantissa, magnitudes above 6 saturating to 6.
+# Readings where MX leaves a choice: an all-zero block takes the smallest
+# scale (byte 0x00); the exponent is clamped to E8M0's [-127, 127]; values
+# that round to zero keep their sign (code 0x8 for negative ones), as for FP8.
+# Packing: element 2i sits in the low nibble of byte i, element 2i+1 in the
+# high nibble.
+
+MX_BLOCK = 32
+E2M1_MAX = 6.0
+E2M1_EMAX = 2
+E8M0_BIAS = 127
+E8M0_NAN = 0xFF
+
+
+def e2m1_decode(codes) -> np.ndarray:
+    """E2M1 code (low 4 bits) -> float64, from the field definition."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64) & 0xF
+    sign = np.where(c & 0x8, -1.0, 1.0)
+    E = (c >> 1) & 0x3
+    M = c & 0x1
+    mag = np.where(E == 0, M * 0.5, (1.0 + M / 2.0) * np.power(2.0, E - 1))
+    return sign * mag
+
+
+def e8m0_decode(b) -> np.ndarray:
+    """E8M0 byte -> float64 scale 2**(b - 127); 0xFF is NaN."""
+    b = np.asarray(b, dtype=np.uint8).astype(np.int64)
+    return np.where(b == E8M0_NAN, np.nan, np.ldexp(1.0, (b - E8M0_BIAS).astype(np.int32)))
+
+
+def e2m1_encode(x) -> np.ndarray:
+    """float (already divided by the block scale) -> E2M1 code.
+
+    Rounds |x| in its own binade: the spacing is 0.5 below 2 (E2M1's subnormal
+    step and the first normal binade share it), 1 in [2, 4) and 2 in [4, 8);
+    |x| / spacing goes to the nearest integer with ties to even, which is the
+    even mantissa.  Magnitudes that round above 6 saturate to 6."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    if np.isnan(a).any():
+        raise ValueError("E2M1 has no NaN")
+    spacing = np.where(a < 2.0, 0.5, np.where(a < 4.0, 1.0, 2.0))
+    r = np.minimum(np.rint(a / spacing) * spacing, E2M1_MAX)  # rint: ties to even multiple of the spacing
+    # value -> code: exponent field and mantissa bit of the rounded magnitude
+    E = np.where(r < 1.0, 0, np.floor(np.log2(np.maximum(r, 1.0))).astype(np.int64) + 1)
+    M = np.where(E == 0, (r / 0.5).astype(np.int64), (r / np.ldexp(1.0, (E - 1).astype(np.int32)) - 1.0) * 2.0)
+    code = (E.astype(np.int64) << 1) | M.astype(np.int64)
+    code = code | np.where(np.signbit(x), 0x8, 0)
+    return code.astype(np.uint8)
+
+
+def mx_block_exponent(amax) -> np.ndarray:
+    """Shared exponent of blocks with absolute maxima amax: floor(log2 amax) - 2,
+    clamped to [-127, 127]; an all-zero block gets -127."""
+    amax = np.asarray(amax, dtype=np.float64)
+    _, e2 = np.frexp(np.where(amax > 0, amax, 1.0))  # amax = m * 2**e2, 0.5 <= m < 1
+    e = e2.astype(np.int64) - 1 - E2M1_EMAX
+    e = np.where(amax > 0, e, -E8M0_BIAS)
+    return np.clip(e, -E8M0_BIAS, E8M0_BIAS)
+
+
+def mx_fp4_quantize(x):
+    """Rows x [..., D] (D a multiple of 32) -> (codes uint8 [..., D], one code
+    per element, and scale bytes uint8 [..., D/32])."""
+    x = np.asarray(x, dtype=np.float64)
+    D = x.shape[-1]
+    if D % MX_BLOCK:
+        raise ValueError("row length must be a multiple of 32")
+    blocks = x.reshape(x.shape[:-1] + (D // MX_BLOCK, MX_BLOCK))
+    e = mx_block_exponent(np.abs(blocks).max(axis=-1))
+    scaled = blocks / np.ldexp(1.0, e.astype(np.int32))[..., None]  # a power of two: exact
+    codes = e2m1_encode(scaled).reshape(x.shape)
+    return codes, (e + E8M0_BIAS).astype(np.uint8)
+
+
+def fp4_pack(codes) -> np.ndarray:
+    """Codes [..., D] -> bytes [..., D/2]: element 2i low nibble, 2i+1 high nibble."""
+    c = np.asarray(codes, dtype=np.uint8)
+    return (c[..., 0::2] & 0xF) | ((c[..., 1::2] & 0xF) << 4)
+
+
+def fp4_unpack(packed) -> np.ndarray:
+    p = np.asarray(packed, dtype=np.uint8)
+    out = np.empty(p.shape[:-1] + (2 * p.shape[-1],), dtype=np.uint8)
+    out[..., 0::2] = p & 0xF
+    out[..., 1::2] = p >> 4
+    return out
+
+
+def mx_fp4_dequantize(packed, scales) -> np.ndarray:
+    """Packed codes [..., D/2] and scale bytes [..., D/32] -> float64 [..., D] (exact)."""
+    v = e2m1_decode(fp4_unpack(packed))
+    s = e8m0_decode(scales)
+    D = v.shape[-1]
+    return (v.reshape(v.shape[:-1] + (D // MX_BLOCK, MX_BLOCK)) * s[..., None]).reshape(v.shape)
+
+
+def fp4_block_views(pool, block_size: int, num_kv_heads: int, head_dim: int):
+    """An FP4 cache pool, uint8 [num_blocks, block_bytes], as its two parts.
+
+    Each block holds its codes, NHD [block_size][num_kv_heads][head_dim/2]
+    bytes, followed by its scales, [block_size][num_kv_heads][head_dim/32]
+    bytes.  Returns (codes [NB, bs, Hkv, D/2], scales [NB, bs, Hkv, D/32])."""
+    p = np.asarray(pool, dtype=np.uint8)
+    nb = p.shape[0]
+    nc = block_size * num_kv_heads * head_dim // 2
+    ns = block_size * num_kv_heads * head_dim // MX_BLOCK
+    if p.shape[1] != nc + ns:
+        raise ValueError(f"FP4 block holds {nc + ns} bytes, pool rows have {p.shape[1]}")
+    return (p[:, :nc].reshape(nb, block_size, num_kv_heads, head_dim // 2),
+            p[:, nc:].reshape(nb, block_size, num_kv_heads, head_dim // MX_BLOCK))
+
+
+def fp4_block_bytes(block_size: int, num_kv_heads: int, head_dim: int) -> int:
+    return block_size * num_kv_heads * (head_dim // 2 + head_dim // MX_BLOCK)

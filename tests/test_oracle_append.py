@@ -126,3 +126,35 @@ def test_inactive_sequence_writes_nothing_and_copies_q():
     k0 = workloads.storage_bits(w.k_pool)
     changed = np.argwhere((r.k_pool != k0).any(axis=(2, 3)))
     assert [tuple(x) for x in changed.tolist()] == [(pb, off)]
+
+
+def test_fp4_append_writes_mx_codes_of_the_recipe_and_nothing_else():
+    """Each active sequence's new K row (fp32 recipe rotation) and V row are
+    written as MX FP4: codes at (slot * Hkv + g) * D/2 of the block, scale
+    bytes at bs * Hkv * D/2 + (slot * Hkv + g) * D/32; every other byte of
+    both pools is unchanged."""
+    w = _wl("fp4_kv", num_seqs=12, ctx=(1, 200), num_blocks=None)
+    c = w.cfg
+    w.context_lens[3] = 0
+    r = _append(w, "recipe")
+    hkv, d, bs = c.num_kv_heads, c.head_dim, c.block_size
+    nc = bs * hkv * d // 2
+    x = codecs.bf16_decode(workloads.storage_bits(w.qkv)).reshape(c.num_seqs, -1, d)
+    k_expect = workloads.storage_bits(w.k_pool).copy()
+    v_expect = workloads.storage_bits(w.v_pool).copy()
+    for b in range(c.num_seqs):
+        if r.slots[b] is None:
+            assert int(w.context_lens[b]) <= 0
+            continue
+        pb, off = r.slots[b]
+        pos = int(w.context_lens[b]) - 1
+        assert (pb, off) == (int(w.block_tables[b, pos // bs]), pos % bs)
+        k32 = rope.rope_neox_f32_recipe(x[b, 32:40].astype(np.float32), pos, c.rope_theta)
+        for expect, rows in ((k_expect, k32.astype(np.float64)), (v_expect, x[b, 40:48])):
+            codes, sc = codecs.mx_fp4_quantize(rows)
+            packed = codecs.fp4_pack(codes)
+            for g in range(hkv):
+                expect[pb, (off * hkv + g) * d // 2:(off * hkv + g + 1) * d // 2] = packed[g]
+                expect[pb, nc + (off * hkv + g) * d // 32:nc + (off * hkv + g + 1) * d // 32] = sc[g]
+    assert np.array_equal(r.k_pool, k_expect)
+    assert np.array_equal(r.v_pool, v_expect)

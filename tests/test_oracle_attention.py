@@ -264,3 +264,45 @@ def test_fp8_dequant_applies_per_head_scales():
     for h in range(32):
         assert np.allclose(out[:, h], 2.0 * vs[h // 4], rtol=0, atol=1e-15)
     assert codecs.e4m3_decode(np.array([0x40], np.uint8))[0] == 2.0
+
+
+def _fp4_pool_to_f32_by_offsets(pool, bs, hkv, d):
+    """Decode an FP4 pool byte by byte from the stated layout (codes of (t, g)
+    at (t*Hkv + g)*D/2, two per byte, low nibble first; scales after all
+    codes, one per 32 elements), without the oracle's views or dequantiser."""
+    mag = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    nb = pool.shape[0]
+    nc = bs * hkv * d // 2
+    out = np.zeros((nb, bs, hkv, d), dtype=np.float32)
+    for blk in range(nb):
+        row = pool[blk]
+        for t in range(bs):
+            for g in range(hkv):
+                base = (t * hkv + g) * d // 2
+                sbase = nc + (t * hkv + g) * d // 32
+                for e in range(d):
+                    byte = int(row[base + e // 2])
+                    code = byte & 0xF if e % 2 == 0 else byte >> 4
+                    v = mag[code & 7] * (-1.0 if code & 8 else 1.0)
+                    out[blk, t, g, e] = math.ldexp(v, int(row[sbase + e // 32]) - 127)
+    return out
+
+
+def test_fp4_cache_equals_f32_cache_of_its_decoded_values():
+    """Attention over an FP4 pool equals attention over an fp32 pool holding
+    the same values (every E2M1 value times a power of two is an fp32 value),
+    decoded here from the layout's byte offsets alone."""
+    w = _small("fp4_kv", num_seqs=2, ctx=(1, 90))
+    c = w.cfg
+    kp, vp = w.k_pool.numpy(), w.v_pool.numpy()
+    kf = _fp4_pool_to_f32_by_offsets(kp, c.block_size, c.num_kv_heads, c.head_dim)
+    vf = _fp4_pool_to_f32_by_offsets(vp, c.block_size, c.num_kv_heads, c.head_dim)
+    q = _q(w, 21)
+    args = (w.block_tables.numpy(), w.context_lens.numpy(), c.softmax_scale)
+    kw = dict(num_kv_heads=c.num_kv_heads, block_size=c.block_size)
+    o4, l4 = A.paged_decode(q, kp, vp, *args, cache="fp4", **kw)
+    o32, l32 = A.paged_decode(q, kf, vf, *args, cache="f32", **kw)
+    assert np.array_equal(o4, o32) and np.array_equal(l4, l32)
+    p4 = A.paged_decode_partials(q, kp, vp, *args, 32, cache="fp4", **kw)
+    p32 = A.paged_decode_partials(q, kf, vf, *args, 32, cache="f32", **kw)
+    assert all(np.array_equal(a, b) for a, b in zip(p4, p32))

@@ -146,3 +146,51 @@ def test_bf16_truncation_instead_of_rounding_is_caught(monkeypatch):
         return (v.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
     monkeypatch.setattr(codecs, "bf16_encode", bad)
     _fails(T_C.test_bf16_golden_cases)
+
+
+def test_e2m1_ties_away_from_zero_is_caught(monkeypatch):
+    orig = codecs.e2m1_encode
+    def bad(x):
+        x = np.asarray(x, dtype=np.float64)
+        a = np.abs(x)
+        spacing = np.where(a < 2.0, 0.5, np.where(a < 4.0, 1.0, 2.0))
+        up = np.floor(a / spacing + 0.5) * spacing  # ties away from zero
+        return orig(np.copysign(np.minimum(up, 6.0), x))
+    monkeypatch.setattr(codecs, "e2m1_encode", bad)
+    _fails(T_C.test_e2m1_golden_cases)
+
+
+def test_mx_scale_exponent_off_by_one_is_caught(monkeypatch):
+    orig = codecs.mx_block_exponent
+    monkeypatch.setattr(codecs, "mx_block_exponent", lambda amax: orig(amax) + 1)
+    _fails(T_C.test_mx_golden_blocks)
+    _fails(T_C.test_mx_scale_rule_invariants)
+
+
+def test_fp4_swapped_nibbles_are_caught(monkeypatch):
+    def bad(codes):
+        c = np.asarray(codes, dtype=np.uint8)
+        return (c[..., 1::2] & 0xF) | ((c[..., 0::2] & 0xF) << 4)
+    monkeypatch.setattr(codecs, "fp4_pack", bad)
+    _fails(T_C.test_mx_golden_blocks)
+
+
+def test_fp4_scales_before_codes_is_caught(monkeypatch):
+    def bad(pool, block_size, num_kv_heads, head_dim):
+        p = np.asarray(pool, dtype=np.uint8)
+        ns = block_size * num_kv_heads * head_dim // 32
+        return (p[:, ns:].reshape(p.shape[0], block_size, num_kv_heads, head_dim // 2),
+                p[:, :ns].reshape(p.shape[0], block_size, num_kv_heads, head_dim // 32))
+    monkeypatch.setattr(codecs, "fp4_block_views", bad)
+    _fails(T_C.test_fp4_block_views_address_the_stated_bytes)
+    _fails(T_A.test_fp4_cache_equals_f32_cache_of_its_decoded_values)
+
+
+def test_fp4_scale_per_16_elements_is_caught(monkeypatch):
+    def bad(packed, scales):
+        v = codecs.e2m1_decode(codecs.fp4_unpack(packed))
+        s = codecs.e8m0_decode(scales)
+        idx = (np.arange(v.shape[-1]) // 16) % s.shape[-1]
+        return v * s[..., idx]
+    monkeypatch.setattr(codecs, "mx_fp4_dequantize", bad)
+    _fails(T_A.test_fp4_cache_equals_f32_cache_of_its_decoded_values)

@@ -30,8 +30,15 @@ def test_shapes_dtypes_and_tables(name):
                      num_blocks=full.num_blocks if name != "long_ctx_splitk" else None)
     w = W.make_workload(cfg)
     B, Hq, Hkv, D, bs = cfg.num_seqs, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim, cfg.block_size
-    assert w.k_pool.dtype == W.TORCH_STORAGE[cfg.cache] and w.v_pool.dtype == w.k_pool.dtype
-    assert w.k_pool.shape == (w.num_blocks, bs, Hkv, D)
+    if cfg.cache == "fp4":
+        assert w.k_pool.dtype == torch.uint8 and w.v_pool.dtype == torch.uint8
+        assert w.k_pool.shape == (w.num_blocks, W.fp4_block_bytes(bs, Hkv, D)) == w.v_pool.shape
+        nc = bs * Hkv * D // 2
+        assert set(torch.unique(w.k_pool[:, nc:]).tolist()) <= set(W.FP4_SCALE_BYTES)
+        assert w.k_scale is None and w.v_scale is None
+    else:
+        assert w.k_pool.dtype == W.TORCH_STORAGE[cfg.cache] and w.v_pool.dtype == w.k_pool.dtype
+        assert w.k_pool.shape == (w.num_blocks, bs, Hkv, D)
     assert w.qkv.shape == (B, (Hq + 2 * Hkv) * D) and w.qkv.dtype == W.TORCH_STORAGE[cfg.act]
     ctx = w.context_lens.numpy()
     lo, hi = (cfg.ctx, cfg.ctx) if isinstance(cfg.ctx, int) else cfg.ctx

@@ -1,7 +1,10 @@
 """Seeded synthetic inputs for paged GQA/MQA decode attention.
 
 This module only *draws inputs*: context lengths, block tables, cache pools,
-packed QKV rows and static FP8 scales.  It holds none of the decode method's
+packed QKV rows and static FP8 scales.  FP4 pools are drawn directly as
+bytes (uniform E2M1 codes, E8M0 scale bytes spread over the binades that
+N(0,1) blocks of 32 land in), since turning drawn values into FP4 would be
+the method's own quantisation.  It holds none of the decode method's
 arithmetic (no RoPE, no attention, no merge, no quantised append).  Casts of
 the drawn N(0,1) values into the storage dtypes use torch's own conversions
 (round-to-nearest-even), so neither the oracle nor the HIP library lends it
@@ -33,8 +36,10 @@ import torch
 STAGE_CTX, STAGE_TABLE, STAGE_K, STAGE_V, STAGE_QKV, STAGE_OUTLIER, STAGE_CALIB = range(7)
 _CHUNK = 1 << 22  # values per RNG chunk
 
-DTYPE_F32, DTYPE_BF16, DTYPE_FP8 = "f32", "bf16", "fp8"
+DTYPE_F32, DTYPE_BF16, DTYPE_FP8, DTYPE_FP4 = "f32", "bf16", "fp8", "fp4"
 ELEM_BYTES = {DTYPE_F32: 4, DTYPE_BF16: 2, DTYPE_FP8: 1}
+FP4_SCALE_BLOCK = 32              # elements per E8M0 scale
+FP4_SCALE_BYTES = (125, 126)  # drawn scale bytes 2**-2, 2**-1: |values| <= 3, rms ~1.2
 TORCH_STORAGE = {DTYPE_F32: torch.float32, DTYPE_BF16: torch.bfloat16, DTYPE_FP8: torch.float8_e4m3fn}
 E4M3_MAX = 448.0
 
@@ -113,14 +118,33 @@ CONFIGS = {
         block_size=16, act=DTYPE_BF16, cache=DTYPE_FP8, ctx=(1024, 4096), rope_theta=5e5,
         partition_size=0,
         description="32/8, D128, FP8 E4M3 cache with static per-head scales, B128, ctx U[1024,4096]"),
+    "fp4_kv": Config(
+        "fp4_kv", seed=6, num_seqs=128, num_q_heads=32, num_kv_heads=8, head_dim=128,
+        block_size=16, act=DTYPE_BF16, cache=DTYPE_FP4, ctx=(1024, 4096), rope_theta=5e5,
+        partition_size=0,
+        description="32/8, D128, FP4 E2M1 cache with E8M0 scales per 32 elements, B128, ctx U[1024,4096]"),
 }
+
+
+def fp4_block_bytes(block_size: int, num_kv_heads: int, head_dim: int) -> int:
+    """Bytes of one FP4 cache block: NHD codes (two per byte), then one scale
+    byte per 32 elements of each (token, kv head) row."""
+    return block_size * num_kv_heads * (head_dim // 2 + head_dim // FP4_SCALE_BLOCK)
+
+
+def row_bytes(cache: str, head_dim: int) -> int:
+    """Bytes of one (token, kv head) row of a cache, scales included."""
+    if cache == DTYPE_FP4:
+        return head_dim // 2 + head_dim // FP4_SCALE_BLOCK
+    return head_dim * ELEM_BYTES[cache]
 
 
 @dataclasses.dataclass
 class Workload:
     """Host-side inputs.  Storage tensors hold the exact bytes the GPU sees.
 
-    k_pool / v_pool: [num_blocks, block_size, Hkv, D] in the cache storage dtype.
+    k_pool / v_pool: [num_blocks, block_size, Hkv, D] in the cache storage dtype
+    (FP4: uint8 [num_blocks, fp4_block_bytes]).
     qkv: [B, (Hq + 2*Hkv) * D] in the activation dtype; per row Q heads, then
     K heads, then V heads, each head_dim-contiguous.
     """
@@ -141,7 +165,7 @@ class Workload:
     def kv_bytes(self) -> int:
         """Algorithmic KV bytes one attention call reads: each (token, kv-head) row once."""
         c = self.cfg
-        return int(self.context_lens.clamp(min=0).sum()) * 2 * c.num_kv_heads * c.head_dim * ELEM_BYTES[c.cache]
+        return int(self.context_lens.clamp(min=0).sum()) * 2 * c.num_kv_heads * row_bytes(c.cache, c.head_dim)
 
 
 def _children(seed: int, stage: int, n: int):
@@ -220,10 +244,31 @@ def draw_calibration_scales(cfg: Config) -> Tuple[np.ndarray, np.ndarray]:
     return scales[0].copy(), scales[1].copy()
 
 
+def draw_fp4_pool(cfg: Config, stage: int, nb: int) -> torch.Tensor:
+    """uint8 [nb, block_bytes]: each block's code bytes uniform over all 256
+    (two uniform E2M1 codes), then its scale bytes uniform over FP4_SCALE_BYTES."""
+    hkv, d, bs = cfg.num_kv_heads, cfg.head_dim, cfg.block_size
+    nc = bs * hkv * d // 2
+    ns = bs * hkv * d // FP4_SCALE_BLOCK
+    kid_codes, kid_scales = _children(cfg.seed, stage, 2)
+    pool = np.empty((nb, nc + ns), dtype=np.uint8)
+    pool[:, :nc] = np.random.default_rng(kid_codes).integers(0, 256, size=(nb, nc), dtype=np.uint8)
+    choice = np.random.default_rng(kid_scales).integers(0, len(FP4_SCALE_BYTES), size=(nb, ns))
+    pool[:, nc:] = np.asarray(FP4_SCALE_BYTES, dtype=np.uint8)[choice]
+    return torch.from_numpy(pool)
+
+
 def make_workload(cfg: Config) -> Workload:
     ctx = draw_context_lens(cfg)
     bt, nb = draw_block_tables(cfg, ctx)
     hkv, d, bs = cfg.num_kv_heads, cfg.head_dim, cfg.block_size
+    if cfg.cache == DTYPE_FP4:
+        if cfg.outlier_frac > 0.0:
+            raise ValueError("FP4 pools are drawn as bytes; outlier rows do not apply")
+        row = (cfg.num_q_heads + 2 * hkv) * d
+        qkv_f = _normal_f32(cfg.seed, STAGE_QKV, cfg.num_seqs * row).reshape(cfg.num_seqs, row)
+        return Workload(cfg, torch.from_numpy(ctx), torch.from_numpy(bt), draw_fp4_pool(cfg, STAGE_K, nb),
+                        draw_fp4_pool(cfg, STAGE_V, nb), _to_storage(qkv_f, cfg.act), None, None)
     pool_shape = (nb, bs, hkv, d)
     kf = _normal_f32(cfg.seed, STAGE_K, int(np.prod(pool_shape))).reshape(pool_shape)
     vf = _normal_f32(cfg.seed, STAGE_V, int(np.prod(pool_shape))).reshape(pool_shape)
