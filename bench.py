@@ -242,6 +242,9 @@ def main() -> int:
     torch.cuda.set_device(dev)
     cu = lambda t: None if t is None else t.to(dev)
     qkv, k_pool, v_pool = cu(w.qkv), cu(w.k_pool), cu(w.v_pool)
+    if cfg.cache == W.DTYPE_FP4:
+        k_pool = ops.FP4Pool(k_pool, cfg.block_size, cfg.num_kv_heads, cfg.head_dim)
+        v_pool = ops.FP4Pool(v_pool, cfg.block_size, cfg.num_kv_heads, cfg.head_dim)
     bt, ctx, ks, vs = cu(w.block_tables), cu(w.context_lens), cu(w.k_scale), cu(w.v_scale)
     max_ctx = int(w.context_lens.max())
     B, Hq, D = cfg.num_seqs, cfg.num_q_heads, cfg.head_dim
@@ -316,8 +319,10 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": cfg.cache if cfg.cache != "fp8" else "fp8-e4m3 kv / bf16 act",
-        "data": "synthetic (seeded N(0,1) KV cache, packed QKV and block tables)",
+        "dtype": {"fp8": "fp8-e4m3 kv / bf16 act", "fp4": "fp4-e2m1 (e8m0 per 32) kv / bf16 act"}.get(
+            cfg.cache, cfg.cache),
+        "data": ("synthetic (seeded uniform E2M1 code bytes and E8M0 scale bytes, N(0,1) packed QKV, block tables)"
+                 if cfg.cache == W.DTYPE_FP4 else "synthetic (seeded N(0,1) KV cache, packed QKV and block tables)"),
         "config": {"workload": cfg.name, "global_batch": B, "context": (list(cfg.ctx) if not isinstance(cfg.ctx, int)
                    else cfg.ctx), "sum_context_tokens": int(w.context_lens.sum()), "num_q_heads": Hq,
                    "num_kv_heads": cfg.num_kv_heads, "head_dim": D, "block_size": cfg.block_size,

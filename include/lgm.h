@@ -52,6 +52,13 @@
  *               heads, each D contiguous; rows qkv_row_stride elements apart.
  *   KV caches   NHD: [num_blocks][block_size][Hkv][D], K and V in separate
  *               pools with identical indexing and dtype.
+ *   FP4 cache blocks (LGM_FP4_E2M1): block i of a pool is the byte range
+ *               [i * S, (i + 1) * S), S = block_size * Hkv * (D/2 + D/32):
+ *               first the codes, NHD [block_size][Hkv][D/2] bytes (element
+ *               2k in the low nibble of byte k, 2k+1 in the high nibble),
+ *               then the scales, [block_size][Hkv][D/32] E8M0 bytes (scale s
+ *               of a row covers its elements 32s .. 32s+31).  The scales
+ *               travel with their block, so no scale pointer is passed.
  *   block table int32 [B][max_blocks_per_seq]: logical block -> physical.
  *   context len int32 [B]: tokens in the cache INCLUDING the new token, so
  *               the new token sits at position ctx - 1.
@@ -68,7 +75,7 @@
 extern "C" {
 #endif
 
-#define LGM_ABI_VERSION 1
+#define LGM_ABI_VERSION 2
 
 typedef enum lgm_status {
   LGM_OK = 0,
@@ -79,8 +86,12 @@ typedef enum lgm_status {
 } lgm_status;
 
 /* Element types.  LGM_FP8_E4M3 is OCP e4m3fn ([mainarch]): bias 7, largest
- * finite 448, 0x7F/0xFF NaN, no infinities. */
-typedef enum lgm_dtype { LGM_F32 = 0, LGM_BF16 = 1, LGM_FP8_E4M3 = 2 } lgm_dtype;
+ * finite 448, 0x7F/0xFF NaN, no infinities.  LGM_FP4_E2M1 is a cache type
+ * only ([mainarch]: 4-bit E2M1 KV with E8M0 block scales), in the OCP
+ * Microscaling form: E2M1 codes (magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6), one
+ * E8M0 scale byte 2^(byte - 127) per 32 consecutive head_dim elements of a
+ * (token, kv head) row; see "FP4 cache blocks" above. */
+typedef enum lgm_dtype { LGM_F32 = 0, LGM_BF16 = 1, LGM_FP8_E4M3 = 2, LGM_FP4_E2M1 = 3 } lgm_dtype;
 
 /* Shapes shared by the calls.  num_seqs = B, num_q_heads = Hq,
  * num_kv_heads = Hkv (Hq % Hkv == 0), head_dim = D, block_size = tokens per
@@ -112,7 +123,12 @@ typedef struct lgm_paged_dims {
  *   physical block block_tables[b][pos / block_size], kv head g, in the
  *   cache dtype: f32 as is, bf16 round to nearest even, FP8 E4M3 as
  *   E4M3(y / scale[g]) with an IEEE fp32 division, round to nearest even,
- *   magnitudes above 448 saturating to +-448, sign kept for zero.
+ *   magnitudes above 448 saturating to +-448, sign kept for zero.  FP4:
+ *   each 32-element block of the row gets the scale exponent
+ *   X = floor(log2(max |y|)) - 2 clamped to [-127, 127] (byte X + 127; an
+ *   all-zero block gets byte 0), and each element the E2M1 code of
+ *   y / 2^X (exact), rounded to nearest with ties to the even mantissa,
+ *   magnitudes above 6 saturating to 6, sign kept for zero.
  * A sequence with ctx <= 0 writes nothing to the caches and its q_out row is
  * Q unrotated (angle 0).
  *
@@ -123,8 +139,9 @@ typedef struct lgm_paged_dims {
  *   context_lens   int32 [B]
  *   k_scale,v_scale fp32 [Hkv] when cache_dtype is LGM_FP8_E4M3, else NULL
  *   rope_theta     > 0, finite
- * Supported: (act, cache) in {(F32, F32), (BF16, BF16), (BF16, FP8_E4M3)};
- * head_dim even, 2..256; block_size >= 1.  Append slots must be distinct
+ * Supported: (act, cache) in {(F32, F32), (BF16, BF16), (BF16, FP8_E4M3),
+ * (BF16, FP4_E2M1)}; head_dim even, 2..256 (a multiple of 32 for FP4);
+ * block_size >= 1.  Append slots must be distinct
  * across the batch (the caller's contract; two sequences writing one slot
  * race).
  */
@@ -139,7 +156,7 @@ lgm_status lgm_rope_kv_append(const void* qkv, int64_t qkv_row_stride, void* q_o
  * A positive partition_size must be a multiple of block_size and is returned
  * as is (clamped to the rounded-up max_context_len).  partition_size 0 lets
  * the library choose from the shapes alone (deterministic, no device query):
- *  - matrix-core shapes (bf16 activations, bf16 / FP8 caches, head_dim 128)
+ *  - matrix-core shapes (bf16 activations, bf16 / FP8 / FP4 caches, head_dim 128)
  *    with num_kv_heads divisible by 4: returns 0.  The 32-token tiles of all
  *    contexts (per group of 8, or 4, kv heads) are cut into equal ranges, one
  *    per compute unit (256, fewer when a range would hold under 8 tiles);
@@ -181,7 +198,8 @@ size_t lgm_paged_decode_workspace_size(lgm_paged_dims dims, int32_t max_context_
  * "Attention").  For each sequence b, query head h, kv head g = h / G,
  * L = min(context_lens[b], max_context_len):
  *   s_j = softmax_scale * <q[b][h], K_j>,  j < L, K_j = cache row of token j
- *         through the block table (FP8: decoded byte * k_scale[g]),
+ *         through the block table (FP8: decoded byte * k_scale[g]; FP4:
+ *         each E2M1 code times its block's E8M0 scale),
  *   out[b][h] = sum_j softmax(s)_j V_j   (FP8: V_j = decoded byte * v_scale[g]),
  *   out_lse[b][h] = log(sum_j exp(s_j))  (natural log; -inf and out = 0 when L = 0).
  * Arithmetic is fp32 with one final rounding to the act dtype.  Contexts are
@@ -212,7 +230,9 @@ size_t lgm_paged_decode_workspace_size(lgm_paged_dims dims, int32_t max_context_
  *                  per stream).
  * Supported: (act, cache) in {(F32, F32), (BF16, BF16), (BF16, FP8_E4M3)},
  * head_dim in {64, 128}, block_size 16, G = Hq/Hkv in 1..8; with bf16
- * activations at head_dim 128, G in 1..16 (matrix-core kernel).
+ * activations at head_dim 128, G in 1..16 (matrix-core kernel); and
+ * (BF16, FP4_E2M1) at head_dim 128, block_size 16, G in 1..16.  FP4 codes
+ * and scales decode exactly; a scale byte 0xFF is NaN, as E8M0 defines.
  * out (16-byte aligned) must not overlap q, the caches or the workspace.
  */
 lgm_status lgm_paged_decode_attn(void* out, float* out_lse, const void* q, int64_t q_seq_stride,

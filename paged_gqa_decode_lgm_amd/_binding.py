@@ -18,7 +18,7 @@ INCLUDE = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__)
 HEADER = os.path.join(INCLUDE, "lgm.h")
 
 LGM_OK, LGM_ERR_INVALID_ARGUMENT, LGM_ERR_UNSUPPORTED, LGM_ERR_WORKSPACE_TOO_SMALL, LGM_ERR_HIP = range(5)
-LGM_F32, LGM_BF16, LGM_FP8_E4M3 = 0, 1, 2
+LGM_F32, LGM_BF16, LGM_FP8_E4M3, LGM_FP4_E2M1 = 0, 1, 2, 3
 STATUS_NAMES = {0: "LGM_OK", 1: "LGM_ERR_INVALID_ARGUMENT", 2: "LGM_ERR_UNSUPPORTED",
                 3: "LGM_ERR_WORKSPACE_TOO_SMALL", 4: "LGM_ERR_HIP"}
 

@@ -33,11 +33,12 @@ const char* dtype_name(lgm_dtype t) {
     case LGM_F32: return "LGM_F32";
     case LGM_BF16: return "LGM_BF16";
     case LGM_FP8_E4M3: return "LGM_FP8_E4M3";
+    case LGM_FP4_E2M1: return "LGM_FP4_E2M1";
   }
   return "invalid";
 }
 
-bool dtype_valid(int t) { return t == LGM_F32 || t == LGM_BF16 || t == LGM_FP8_E4M3; }
+bool dtype_valid(int t) { return t == LGM_F32 || t == LGM_BF16 || t == LGM_FP8_E4M3 || t == LGM_FP4_E2M1; }
 
 int64_t elem_bytes(lgm_dtype t) { return t == LGM_F32 ? 4 : (t == LGM_BF16 ? 2 : 1); }
 
@@ -74,8 +75,12 @@ lgm_status check_dims(const char* fn, const lgm_paged_dims& d) {
   return LGM_OK;
 }
 
+// Bytes of one cache pool.  FP4 blocks hold their codes (D/2 bytes per
+// token and kv head) and then their E8M0 scales (D/32 bytes).
 int64_t cache_bytes(const lgm_paged_dims& d, lgm_dtype cache) {
-  return (int64_t)d.num_blocks * d.block_size * d.num_kv_heads * d.head_dim * elem_bytes(cache);
+  const int64_t rows = (int64_t)d.num_blocks * d.block_size * d.num_kv_heads;
+  if (cache == LGM_FP4_E2M1) return rows * (d.head_dim / 2 + d.head_dim / 32);
+  return rows * d.head_dim * elem_bytes(cache);
 }
 
 lgm_status check_scales(const char* fn, lgm_dtype cache, const float* k_scale, const float* v_scale) {
@@ -268,10 +273,14 @@ lgm_status lgm_rope_kv_append(const void* qkv, int64_t qkv_row_stride, void* q_o
     return fail(LGM_ERR_INVALID_ARGUMENT, fn, "cache_dtype = %d is not an lgm_dtype", (int)cache_dtype);
   const bool types_ok = (act_dtype == LGM_F32 && cache_dtype == LGM_F32) ||
                         (act_dtype == LGM_BF16 && cache_dtype == LGM_BF16) ||
-                        (act_dtype == LGM_BF16 && cache_dtype == LGM_FP8_E4M3);
+                        (act_dtype == LGM_BF16 && cache_dtype == LGM_FP8_E4M3) ||
+                        (act_dtype == LGM_BF16 && cache_dtype == LGM_FP4_E2M1);
   if (!types_ok)
     return fail(LGM_ERR_UNSUPPORTED, fn, "(act_dtype, cache_dtype) = (%s, %s): supported are (F32, F32), "
-                "(BF16, BF16), (BF16, FP8_E4M3)", dtype_name(act_dtype), dtype_name(cache_dtype));
+                "(BF16, BF16), (BF16, FP8_E4M3), (BF16, FP4_E2M1)", dtype_name(act_dtype), dtype_name(cache_dtype));
+  if (cache_dtype == LGM_FP4_E2M1 && dims.head_dim % 32 != 0)
+    return fail(LGM_ERR_UNSUPPORTED, fn, "dims.head_dim = %d: FP4 caches need a multiple of 32 (one scale per 32)",
+                dims.head_dim);
   if (!(std::isfinite(rope_theta) && rope_theta > 0.f))
     return fail(LGM_ERR_INVALID_ARGUMENT, fn, "rope_theta = %g must be finite and > 0", (double)rope_theta);
   const int64_t row = (int64_t)(dims.num_q_heads + 2 * dims.num_kv_heads) * dims.head_dim;
@@ -342,7 +351,8 @@ lgm_status lgm_paged_decode_attn(void* out, float* out_lse, const void* q, int64
     return fail(LGM_ERR_UNSUPPORTED, fn,
                 "(act %s, cache %s, head_dim %d, group %d, block_size %d) unsupported: supported are (F32, F32), "
                 "(BF16, BF16), (BF16, FP8_E4M3) with head_dim 64 or 128, block_size 16, group 1..8 "
-                "(1..16 for bf16 activations at head_dim 128)",
+                "(1..16 for bf16 activations at head_dim 128), and (BF16, FP4_E2M1) with head_dim 128, "
+                "block_size 16, group 1..16",
                 dtype_name(act_dtype), dtype_name(cache_dtype), dims.head_dim, G, dims.block_size);
   if (dims.num_seqs > 65535 || dims.num_kv_heads > 65535)
     return fail(LGM_ERR_UNSUPPORTED, fn, "dims.num_seqs = %d / dims.num_kv_heads = %d: at most 65535 each",

@@ -16,7 +16,10 @@
 //           permute per operand register instead of a transpose.
 //           Output lane (kg, n) holds O[head 4kg + j][8n + i] in acc[i][j].
 // FP8 rows are converted to bf16 in registers (exact: every E4M3 value is a
-// bf16 value).
+// bf16 value).  FP4 rows (E2M1 codes, one E8M0 scale per 32 head-dim
+// elements, stored after the block's codes) are converted to bf16 with their
+// scale folded in by the scaled conversion (exact: an E2M1 value times a
+// power of two has at most two significant bits).
 #pragma once
 
 #include "device_num.h"
@@ -108,11 +111,32 @@ template <int POL>
 __device__ __forceinline__ uint2 kv_load8(__amdgpu_buffer_rsrc_t r, int off) {
   return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, POL));
 }
+template <int POL>
+__device__ __forceinline__ uint32_t kv_load4(__amdgpu_buffer_rsrc_t r, int off) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, POL);
+}
+template <int POL>
+__device__ __forceinline__ uint32_t kv_load1(__amdgpu_buffer_rsrc_t r, int off) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, off, 0, POL);
+}
+// E8M0 byte -> the fp32 scale 2^(b - 127): the byte is the fp32 exponent
+// field, except 0 (2^-127, an fp32 subnormal) and 0xFF (NaN).
+__device__ __forceinline__ float e8m0_to_f32(uint32_t b) {
+  return __uint_as_float(b == 0 ? 0x00400000u : (b == 0xFFu ? 0x7FC00000u : b << 23));
+}
+// Two E2M1 codes (byte SEL of w, low nibble first) times scale -> two bf16 packed in a dword.
+template <int SEL>
+__device__ __forceinline__ uint32_t fp4x2_to_bf16x2(uint32_t w, float scale) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, SEL));
+}
 
 struct MfmaBF16 {
   static constexpr bool kFp8 = false;
-  static constexpr int kElemBytes = 2;
   using elem_t = uint16_t;
+  // Bytes of one token row (all kv heads) and of one 16-token block.
+  __device__ static int tok_bytes(int hkv) { return hkv * kD * 2; }
+  __device__ static int64_t block_bytes(int hkv) { return (int64_t)kBS * tok_bytes(hkv); }
+  __device__ static int score_d(int c, int kg, int j) { return 32 * c + 8 * kg + j; }
   struct KBlock {
     uint4 k[4];  // K[n][32c + 8kg .. +8], c = 0..3
   };
@@ -125,13 +149,15 @@ struct MfmaBF16 {
   __device__ static int v_lane_off(int g, int tok_bytes, int n, int kg) {
     return 4 * kg * tok_bytes + g * 256 + 16 * n;
   }
+  __device__ static int k_scale_off(int, int, int, int) { return 0; }
+  __device__ static int v_scale_off(int, int, int, int) { return 0; }
   template <int POL = kDefaultPolicy>
-  __device__ static void load_k(KBlock& r, __amdgpu_buffer_rsrc_t rs, int off, int) {
+  __device__ static void load_k(KBlock& r, __amdgpu_buffer_rsrc_t rs, int off, int, int) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) r.k[c] = kv_load16<POL>(rs, off + 64 * c);
   }
   template <int POL = kDefaultPolicy>
-  __device__ static void load_v(VBlock& r, __amdgpu_buffer_rsrc_t rs, int off, int tok_bytes) {
+  __device__ static void load_v(VBlock& r, __amdgpu_buffer_rsrc_t rs, int off, int tok_bytes, int) {
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) r.v[jj] = kv_load16<POL>(rs, off + jj * tok_bytes);
   }
@@ -149,8 +175,11 @@ struct MfmaBF16 {
 
 struct MfmaFP8 {
   static constexpr bool kFp8 = true;
-  static constexpr int kElemBytes = 1;
   using elem_t = uint8_t;
+  __device__ static int tok_bytes(int hkv) { return hkv * kD; }
+  __device__ static int64_t block_bytes(int hkv) { return (int64_t)kBS * tok_bytes(hkv); }
+  // Score MFMA c = 2u + h uses codes 8h .. 8h+7 of K chunk u.
+  __device__ static int score_d(int c, int kg, int j) { return 64 * (c >> 1) + 16 * kg + 8 * (c & 1) + j; }
   struct KBlock {
     uint4 k[2];  // K[n][64u + 16kg .. +16] (16 codes), u = 0..1
   };
@@ -161,13 +190,15 @@ struct MfmaFP8 {
   __device__ static int v_lane_off(int g, int tok_bytes, int n, int kg) {
     return 4 * kg * tok_bytes + g * 128 + 8 * n;
   }
+  __device__ static int k_scale_off(int, int, int, int) { return 0; }
+  __device__ static int v_scale_off(int, int, int, int) { return 0; }
   template <int POL = kDefaultPolicy>
-  __device__ static void load_k(KBlock& r, __amdgpu_buffer_rsrc_t rs, int off, int) {
+  __device__ static void load_k(KBlock& r, __amdgpu_buffer_rsrc_t rs, int off, int, int) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) r.k[u] = kv_load16<POL>(rs, off + 64 * u);
   }
   template <int POL = kDefaultPolicy>
-  __device__ static void load_v(VBlock& r, __amdgpu_buffer_rsrc_t rs, int off, int tok_bytes) {
+  __device__ static void load_v(VBlock& r, __amdgpu_buffer_rsrc_t rs, int off, int tok_bytes, int) {
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) r.v[jj] = kv_load8<POL>(rs, off + jj * tok_bytes);
   }
@@ -187,13 +218,78 @@ struct MfmaFP8 {
   __device__ static void zero_v_row(VBlock& r, int jj) { r.v[jj] = make_uint2(0, 0); }
 };
 
+// FP4 blocks: codes [16][Hkv][64 bytes] (two E2M1 codes a byte, low nibble
+// first), then scales [16][Hkv][4 bytes] (E8M0, one per 32 head-dim elements).
+struct MfmaFP4 {
+  static constexpr bool kFp8 = false;
+  using elem_t = uint8_t;
+  __device__ static int tok_bytes(int hkv) { return hkv * kD / 2; }  // code bytes of a token row
+  __device__ static int64_t block_bytes(int hkv) { return (int64_t)kBS * hkv * (kD / 2 + kD / 32); }
+  // Lane kg holds head-dim 32kg .. 32kg+31 of its K row (one scale block);
+  // score MFMA c takes eight of them.
+  __device__ static int score_d(int c, int kg, int j) { return 32 * kg + 8 * c + j; }
+  struct KBlock {
+    uint4 k;     // codes of K[n][32kg .. 32kg+31]
+    uint32_t s;  // their scale byte
+  };
+  struct VBlock {
+    uint32_t v[4];  // codes of V[4kg + jj][8n .. 8n+7]
+    uint32_t s[4];  // their scale bytes
+  };
+  __device__ static int k_lane_off(int g, int tok_bytes, int n, int kg) { return n * tok_bytes + g * 64 + 16 * kg; }
+  __device__ static int v_lane_off(int g, int tok_bytes, int n, int kg) { return 4 * kg * tok_bytes + g * 64 + 4 * n; }
+  // Scale bytes: the scale area starts after the block's 16 code rows; the
+  // (token t, head g) row's four scales sit at (t * Hkv + g) * 4 in it
+  // (tok_bytes / 16 = Hkv * 4 bytes per token).
+  __device__ static int k_scale_off(int g, int tok_bytes, int n, int kg) {
+    return kBS * tok_bytes + n * (tok_bytes / 16) + 4 * g + kg;
+  }
+  __device__ static int v_scale_off(int g, int tok_bytes, int n, int kg) {
+    return kBS * tok_bytes + 4 * kg * (tok_bytes / 16) + 4 * g + (n >> 2);
+  }
+  template <int POL = kDefaultPolicy>
+  __device__ static void load_k(KBlock& r, __amdgpu_buffer_rsrc_t rs, int off, int, int soff) {
+    r.k = kv_load16<POL>(rs, off);
+    r.s = kv_load1<POL>(rs, soff);
+  }
+  template <int POL = kDefaultPolicy>
+  __device__ static void load_v(VBlock& r, __amdgpu_buffer_rsrc_t rs, int off, int tok_bytes, int soff) {
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) r.v[jj] = kv_load4<POL>(rs, off + jj * tok_bytes);
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) r.s[jj] = kv_load1<POL>(rs, soff + jj * (tok_bytes / 16));
+  }
+  __device__ static short8 k_operand(const KBlock& r, int c) {
+    const uint32_t w = c == 0 ? r.k.x : (c == 1 ? r.k.y : (c == 2 ? r.k.z : r.k.w));
+    const float sc = e8m0_to_f32(r.s);
+    return words_to_short8(fp4x2_to_bf16x2<0>(w, sc), fp4x2_to_bf16x2<1>(w, sc), fp4x2_to_bf16x2<2>(w, sc),
+                           fp4x2_to_bf16x2<3>(w, sc));
+  }
+  // Rows jj and jj+1, element i: convert the byte holding element i of each
+  // row with the row's own scale, then pair the two halves.
+  __device__ static uint32_t v_pair(const VBlock& r, int jj, int i) {
+    uint32_t x, y;
+    const float sx = e8m0_to_f32(r.s[jj]), sy = e8m0_to_f32(r.s[jj + 1]);
+    switch (i >> 1) {
+      case 0: x = fp4x2_to_bf16x2<0>(r.v[jj], sx); y = fp4x2_to_bf16x2<0>(r.v[jj + 1], sy); break;
+      case 1: x = fp4x2_to_bf16x2<1>(r.v[jj], sx); y = fp4x2_to_bf16x2<1>(r.v[jj + 1], sy); break;
+      case 2: x = fp4x2_to_bf16x2<2>(r.v[jj], sx); y = fp4x2_to_bf16x2<2>(r.v[jj + 1], sy); break;
+      default: x = fp4x2_to_bf16x2<3>(r.v[jj], sx); y = fp4x2_to_bf16x2<3>(r.v[jj + 1], sy); break;
+    }
+    return (i & 1) ? ((y & 0xffff0000u) | (x >> 16)) : ((y << 16) | (x & 0xffffu));
+  }
+  // A masked row: zero codes and a finite scale, so the row contributes
+  // exactly zero whatever its stored scale byte held.
+  __device__ static void zero_v_row(VBlock& r, int jj) {
+    r.v[jj] = 0;
+    r.s[jj] = 127;
+  }
+};
+
 // Head-dim index held by (MFMA c, lane group kg, slot j) in the score operands.
 template <class C>
 __device__ __forceinline__ int score_d(int c, int kg, int j) {
-  if constexpr (C::kFp8)
-    return 64 * (c >> 1) + 16 * kg + 8 * (c & 1) + j;
-  else
-    return 32 * c + 8 * kg + j;
+  return C::score_d(c, kg, j);
 }
 
 

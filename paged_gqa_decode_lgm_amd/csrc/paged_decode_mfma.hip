@@ -169,21 +169,23 @@ __device__ __forceinline__ int preload_ids(const DecodeArgs& p, const Item& it, 
 // per tile is fixed and the compiler can wait for K without waiting for V.
 template <class C>
 __device__ __forceinline__ void load_tile_k(const DecodeArgs& p, int g, int px, int py, int lane, TileRegs<C>& tr) {
-  const int tok_bytes = p.dims.num_kv_heads * kD * C::kElemBytes;
-  const int64_t block_bytes = (int64_t)kBS * tok_bytes;
+  const int tok_bytes = C::tok_bytes(p.dims.num_kv_heads);
+  const int64_t block_bytes = C::block_bytes(p.dims.num_kv_heads);
   const int off = C::k_lane_off(g, tok_bytes, lane & 15, lane >> 4);
+  const int soff = C::k_scale_off(g, tok_bytes, lane & 15, lane >> 4);
   const int ex = px >= 0 ? px : 0, ey = py >= 0 ? py : ex;
-  C::load_k(tr.kx, block_rsrc(p.k_cache, block_bytes, ex), off, tok_bytes);
-  C::load_k(tr.ky, block_rsrc(p.k_cache, block_bytes, ey), off, tok_bytes);
+  C::load_k(tr.kx, block_rsrc(p.k_cache, block_bytes, ex), off, tok_bytes, soff);
+  C::load_k(tr.ky, block_rsrc(p.k_cache, block_bytes, ey), off, tok_bytes, soff);
 }
 template <class C>
 __device__ __forceinline__ void load_tile_v(const DecodeArgs& p, int g, int px, int py, int lane, TileRegs<C>& tr) {
-  const int tok_bytes = p.dims.num_kv_heads * kD * C::kElemBytes;
-  const int64_t block_bytes = (int64_t)kBS * tok_bytes;
+  const int tok_bytes = C::tok_bytes(p.dims.num_kv_heads);
+  const int64_t block_bytes = C::block_bytes(p.dims.num_kv_heads);
   const int off = C::v_lane_off(g, tok_bytes, lane & 15, lane >> 4);
+  const int soff = C::v_scale_off(g, tok_bytes, lane & 15, lane >> 4);
   const int ex = px >= 0 ? px : 0, ey = py >= 0 ? py : ex;
-  C::load_v(tr.vx, block_rsrc(p.v_cache, block_bytes, ex), off, tok_bytes);
-  C::load_v(tr.vy, block_rsrc(p.v_cache, block_bytes, ey), off, tok_bytes);
+  C::load_v(tr.vx, block_rsrc(p.v_cache, block_bytes, ex), off, tok_bytes, soff);
+  C::load_v(tr.vy, block_rsrc(p.v_cache, block_bytes, ey), off, tok_bytes, soff);
 }
 
 // Starts an item for this wave: the query operand, the block ids of its
@@ -416,8 +418,8 @@ int compute_units_of(hipStream_t s) {
 }  // namespace
 
 bool decode_mfma_supported(lgm_dtype act, lgm_dtype cache, int head_dim, int group, int block_size) {
-  return act == LGM_BF16 && (cache == LGM_BF16 || cache == LGM_FP8_E4M3) && head_dim == kD && group >= 1 &&
-         group <= 16 && block_size == kBS;
+  return act == LGM_BF16 && (cache == LGM_BF16 || cache == LGM_FP8_E4M3 || cache == LGM_FP4_E2M1) &&
+         head_dim == kD && group >= 1 && group <= 16 && block_size == kBS;
 }
 
 hipError_t launch_paged_decode_mfma(const DecodeArgs& a, lgm_dtype cache, hipStream_t s) {
@@ -425,6 +427,7 @@ hipError_t launch_paged_decode_mfma(const DecodeArgs& a, lgm_dtype cache, hipStr
   const int cus = compute_units_of(s);
   if (cache == LGM_BF16) return dispatch<MfmaBF16>(a, G, cus, s);
   if (cache == LGM_FP8_E4M3) return dispatch<MfmaFP8>(a, G, cus, s);
+  if (cache == LGM_FP4_E2M1) return dispatch<MfmaFP4>(a, G, cus, s);
   return hipErrorInvalidValue;
 }
 

@@ -1,6 +1,6 @@
 // Paged GQA decode attention over whole KV token rows, for gfx950 matrix
-// cores: bf16 activations, bf16 or FP8 E4M3 caches, head_dim 128, block_size
-// 16, a kv head count divisible by 4.
+// cores: bf16 activations, bf16, FP8 E4M3 or FP4 E2M1 (E8M0 block scales)
+// caches, head_dim 128, block_size 16, a kv head count divisible by 4.
 //
 // The split-K method of paged_decode.hip (mainarch README, decode-attention
 // section; Loom Kernels README, "Attention" row) with the work laid out for
@@ -26,6 +26,8 @@
 // v_mfma_f32_16x16x32_bf16 exactly as the partition kernel does (operand
 // layouts and the softmax update in mfma_common.h), alternating between its
 // two heads with one tile of loads in flight.
+#include <type_traits>
+
 #include "mfma_common.h"
 
 namespace lgm {
@@ -33,11 +35,12 @@ namespace {
 
 using namespace mfma;
 
-constexpr int kChunk = 4 * kDecodeThreads;  // sequences per scan step
+constexpr int kChunk = 1024;       // sequences per scan step
+constexpr int kMaxRowWaves = 8;    // waves of the widest row workgroup
 
 struct RowsSmem {
   int pre[kChunk + 1];  // tiles of the streams of sequences b0 .. b0 + j - 1
-  int wave_sum[kNW];
+  int wave_sum[kMaxRowWaves];
 };
 
 __device__ __forceinline__ int clamped_ctx(const DecodeArgs& p, int b) {
@@ -47,13 +50,16 @@ __device__ __forceinline__ int clamped_ctx(const DecodeArgs& p, int b) {
 
 // Fills sm.pre for sequences b0 .. b0 + kChunk - 1 (nhg streams of
 // ceil(ctx / 32) tiles per sequence) and returns the chunk's tile total.
-// Called by every thread of the workgroup (it synchronises).
+// Called by every thread of the NT-thread workgroup (it synchronises).
+template <int NT>
 __device__ int scan_chunk(const DecodeArgs& p, RowsSmem& sm, int b0, int nhg) {
+  constexpr int SPT = kChunk / NT;  // sequences per thread
+  static_assert(SPT * NT == kChunk && NT / kWaveSize <= kMaxRowWaves, "scan layout");
   const int tid = threadIdx.x, lane = tid & (kWaveSize - 1), wave = tid / kWaveSize;
-  int t[4], s = 0;
+  int t[SPT], s = 0;
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int b = b0 + 4 * tid + k;
+  for (int k = 0; k < SPT; ++k) {
+    const int b = b0 + SPT * tid + k;
     t[k] = b < p.dims.num_seqs ? (clamped_ctx(p, b) + kTile - 1) / kTile * nhg : 0;
     s += t[k];
   }
@@ -69,11 +75,11 @@ __device__ int scan_chunk(const DecodeArgs& p, RowsSmem& sm, int b0, int nhg) {
   int run = incl - s;
   for (int w = 0; w < wave; ++w) run += sm.wave_sum[w];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    sm.pre[4 * tid + k] = run;
+  for (int k = 0; k < SPT; ++k) {
+    sm.pre[SPT * tid + k] = run;
     run += t[k];
   }
-  if (tid == kDecodeThreads - 1) sm.pre[kChunk] = run;
+  if (tid == NT - 1) sm.pre[kChunk] = run;
   __syncthreads();
   return __builtin_amdgcn_readfirstlane(sm.pre[kChunk]);
 }
@@ -92,23 +98,36 @@ __device__ __forceinline__ int preload_row_ids(const DecodeArgs& p, int b, int l
   return (tile < et && lb < lb_end && (unsigned)id < (unsigned)p.dims.num_blocks) ? id : -1;
 }
 
+// K/V load cache policy.  bf16 and FP8 head rows are whole 128-byte lines
+// (or pairs of them) that one wave reads once, and the non-temporal hint lifts
+// them to the streaming ceiling.  An FP4 head row is 64 bytes, so two heads
+// share each line, and one line of scales serves four tokens of all heads:
+// with the hint those shared lines were evicted between their readers (HBM
+// fetches 1.68x the cache bytes, measured), with the default policy 1.09x.
+template <class C>
+constexpr int row_policy() {
+  return std::is_same<C, MfmaFP4>::value ? kDefaultPolicy : kStreamPolicy;
+}
+
 template <class C>
 __device__ __forceinline__ void row_load_k(const DecodeArgs& p, int g, int px, int py, int lane, TileRegs<C>& tr) {
-  const int tok_bytes = p.dims.num_kv_heads * kD * C::kElemBytes;
-  const int64_t block_bytes = (int64_t)kBS * tok_bytes;
+  const int tok_bytes = C::tok_bytes(p.dims.num_kv_heads);
+  const int64_t block_bytes = C::block_bytes(p.dims.num_kv_heads);
   const int off = C::k_lane_off(g, tok_bytes, lane & 15, lane >> 4);
+  const int soff = C::k_scale_off(g, tok_bytes, lane & 15, lane >> 4);
   const int ex = px >= 0 ? px : 0, ey = py >= 0 ? py : ex;
-  C::template load_k<kStreamPolicy>(tr.kx, block_rsrc(p.k_cache, block_bytes, ex), off, tok_bytes);
-  C::template load_k<kStreamPolicy>(tr.ky, block_rsrc(p.k_cache, block_bytes, ey), off, tok_bytes);
+  C::template load_k<row_policy<C>()>(tr.kx, block_rsrc(p.k_cache, block_bytes, ex), off, tok_bytes, soff);
+  C::template load_k<row_policy<C>()>(tr.ky, block_rsrc(p.k_cache, block_bytes, ey), off, tok_bytes, soff);
 }
 template <class C>
 __device__ __forceinline__ void row_load_v(const DecodeArgs& p, int g, int px, int py, int lane, TileRegs<C>& tr) {
-  const int tok_bytes = p.dims.num_kv_heads * kD * C::kElemBytes;
-  const int64_t block_bytes = (int64_t)kBS * tok_bytes;
+  const int tok_bytes = C::tok_bytes(p.dims.num_kv_heads);
+  const int64_t block_bytes = C::block_bytes(p.dims.num_kv_heads);
   const int off = C::v_lane_off(g, tok_bytes, lane & 15, lane >> 4);
+  const int soff = C::v_scale_off(g, tok_bytes, lane & 15, lane >> 4);
   const int ex = px >= 0 ? px : 0, ey = py >= 0 ? py : ex;
-  C::template load_v<kStreamPolicy>(tr.vx, block_rsrc(p.v_cache, block_bytes, ex), off, tok_bytes);
-  C::template load_v<kStreamPolicy>(tr.vy, block_rsrc(p.v_cache, block_bytes, ey), off, tok_bytes);
+  C::template load_v<row_policy<C>()>(tr.vx, block_rsrc(p.v_cache, block_bytes, ex), off, tok_bytes, soff);
+  C::template load_v<row_policy<C>()>(tr.vy, block_rsrc(p.v_cache, block_bytes, ey), off, tok_bytes, soff);
 }
 
 // Writes one head's result of a segment: the final output (bf16, normalised)
@@ -153,20 +172,30 @@ __device__ __forceinline__ void write_head(const DecodeArgs& p, const RowsArgs& 
   }
 }
 
+// Register sets per wave: how many (tile, head) steps of loads a wave keeps
+// in flight.  Two cover HBM latency at one wave per SIMD for bf16 tiles
+// (16 KB per kv head).  The FP8 and FP4 tiles are smaller, but four or six
+// sets made those kernels slower (more register traffic, no more bandwidth:
+// they are bound by their per-tile instruction stream, not by loads in
+// flight), so every format uses two.
+constexpr int kRowSets = 2;
+
 // One segment for this wave: tiles lt .. et - 1 of sequence b (context ctx)
-// for kv heads g0 .. g0 + HPW - 1.  The wave streams through steps (a tile
-// for one head) with two register sets, A and B: with two heads A always
-// holds the first head's tile and B the second's; with one head A holds the
-// even tiles and B the odd ones.  A set's next tile is loaded as soon as its
-// current step's MFMAs have consumed the registers (K after the scores, V
-// after P V), so while one set is computed the other set's loads and the
-// first set's next loads are in flight: two steps of loads per wave, which
-// with one wave per SIMD keeps HBM busy.  Steps past the segment (and the
-// dummy loads after the last one) use absent blocks: they read block 0 and
-// are masked, so every iteration issues the same loads in the same order.
+// for kv heads g0 .. g0 + HPW - 1.  The wave walks steps s = (tile s / HPW,
+// head s % HPW) with NS register sets: set j always holds steps j, j + NS,
+// j + 2NS, ... (one head, every NS/HPW-th tile).  A set's next step is loaded
+// as soon as its current step's MFMAs have consumed the registers (K after
+// the scores, V after P V), so while one set is computed the other sets'
+// loads and this set's next loads are in flight: NS steps of loads per wave,
+// which with one wave per SIMD keeps HBM busy.  Steps past the segment (and
+// the dummy loads after the last one) use absent blocks: they read block 0
+// and are masked, so every iteration issues the same loads in the same order.
 template <class C, int G, int HPW>
 __device__ __forceinline__ void run_segment(const DecodeArgs& p, const RowsArgs& r, int b, int ctx, int lt, int et,
                                             int g0, bool whole, int rec, int lane) {
+  constexpr int NS = kRowSets;
+  static_assert(NS % HPW == 0, "each set must stay on one head");
+  constexpr int kAdvance = NS / HPW;  // tiles a set moves per iteration
   short8 qb[HPW][4];
   WaveState st[HPW];
   const bool qvec = ((uintptr_t)p.q % 16 == 0) && (p.q_seq_stride % 8 == 0);
@@ -196,50 +225,46 @@ __device__ __forceinline__ void run_segment(const DecodeArgs& p, const RowsArgs&
     x = __builtin_amdgcn_readlane(ids, 2 * (k & 31));
     y = __builtin_amdgcn_readlane(ids, 2 * (k & 31) + 1);
   };
-  constexpr int kAdvance = HPW == 2 ? 1 : 2;  // tiles a set moves per iteration
-  const int gA = g0, gB = HPW == 2 ? g0 + 1 : g0;
-  TileRegs<C> ta, tb;
-  int ax, ay, bx, by;
-  tile_id(0, ax, ay);
-  if (HPW == 2) {
-    bx = ax;
-    by = ay;
-  } else {
-    tile_id(1, bx, by);
-  }
-  row_load_k<C>(p, gA, ax, ay, lane, ta);
-  __builtin_amdgcn_sched_barrier(0);  // the loop's load order: K A, V A, K B, V B
-  row_load_v<C>(p, gA, ax, ay, lane, ta);
-  __builtin_amdgcn_sched_barrier(0);
-  row_load_k<C>(p, gB, bx, by, lane, tb);
-  __builtin_amdgcn_sched_barrier(0);
-  row_load_v<C>(p, gB, bx, by, lane, tb);
-  const int ntiles = et - lt;
-  const int iters = HPW == 2 ? ntiles : (ntiles + 1) / 2;
-  for (int it = 0; it < iters; ++it) {
-    const int ka = HPW == 2 ? it : 2 * it;
-    const int kb = HPW == 2 ? it : 2 * it + 1;
-    int nax, nay, nbx, nby;
-    tile_id(ka + kAdvance, nax, nay);
-    if (HPW == 2) {
-      nbx = nax;
-      nby = nay;
+  TileRegs<C> ts[NS];
+  int px[NS], py[NS];
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
+    if (j % HPW == 0) {
+      tile_id(j / HPW, px[j], py[j]);
     } else {
-      tile_id(kb + kAdvance, nbx, nby);
+      px[j] = px[j - j % HPW];
+      py[j] = py[j - j % HPW];
     }
-    float4v sx, sy;
-    tile_scores<C>(ta, qb[0], sx, sy);
-    row_load_k<C>(p, gA, nax, nay, lane, ta);
-    tile_update<C>(st[0], ta, sx, sy, sscale[0], ax >= 0, ay >= 0, kTile * (lt + ka), ctx, lane >> 4);
-    row_load_v<C>(p, gA, nax, nay, lane, ta);
-    tile_scores<C>(tb, qb[HPW - 1], sx, sy);
-    row_load_k<C>(p, gB, nbx, nby, lane, tb);
-    tile_update<C>(st[HPW - 1], tb, sx, sy, sscale[HPW - 1], bx >= 0, by >= 0, kTile * (lt + kb), ctx, lane >> 4);
-    row_load_v<C>(p, gB, nbx, nby, lane, tb);
-    ax = nax;
-    ay = nay;
-    bx = nbx;
-    by = nby;
+  }
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {  // the loop's load order: K, V of each set in turn
+    row_load_k<C>(p, g0 + j % HPW, px[j], py[j], lane, ts[j]);
+    __builtin_amdgcn_sched_barrier(0);
+    row_load_v<C>(p, g0 + j % HPW, px[j], py[j], lane, ts[j]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  const int ntiles = et - lt;
+  const int iters = (ntiles + kAdvance - 1) / kAdvance;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      const int h = j % HPW;
+      const int k = it * kAdvance + j / HPW;  // this set's tile
+      int nx, ny;
+      if (h == 0) {
+        tile_id(k + kAdvance, nx, ny);
+      } else {
+        nx = px[j - h];  // the head-0 set of the same tile has just looked it up
+        ny = py[j - h];
+      }
+      float4v sx, sy;
+      tile_scores<C>(ts[j], qb[h], sx, sy);
+      row_load_k<C>(p, g0 + h, nx, ny, lane, ts[j]);
+      tile_update<C>(st[h], ts[j], sx, sy, sscale[h], px[j] >= 0, py[j] >= 0, kTile * (lt + k), ctx, lane >> 4);
+      row_load_v<C>(p, g0 + h, nx, ny, lane, ts[j]);
+      px[j] = nx;
+      py[j] = ny;
+    }
   }
 #pragma unroll
   for (int hh = 0; hh < HPW; ++hh) write_head<C, G>(p, r, st[hh], b, g0 + hh, whole, rec, lane);
@@ -250,10 +275,10 @@ __device__ __forceinline__ void run_segment(const DecodeArgs& p, const RowsArgs&
 // wg_first[u] / wg_last[u] = the workgroups holding stream u's first and
 // last tiles.  Record slot 2w holds the range's first stream when split,
 // slot 2w + 1 its last one (when that is another stream).
-template <class C, int G, int HPW>
-__global__ __launch_bounds__(kDecodeThreads, 1) void paged_decode_rows_kernel(DecodeArgs p, RowsArgs r) {
+template <class C, int G, int HPW, int NT>
+__global__ __launch_bounds__(NT, 1) void paged_decode_rows_kernel(DecodeArgs p, RowsArgs r) {
   __shared__ RowsSmem sm;
-  constexpr int HG = kNW * HPW;
+  constexpr int HG = NT / kWaveSize * HPW;
   const int lane = threadIdx.x & (kWaveSize - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWaveSize);
   const int B = p.dims.num_seqs;
@@ -261,12 +286,12 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void paged_decode_rows_kernel(De
   const int W = gridDim.x;
   const int wg = blockIdx.x;
 
-  int total = scan_chunk(p, sm, 0, nhg);
-  for (int c0 = kChunk; c0 < B; c0 += kChunk) total += scan_chunk(p, sm, c0, nhg);
+  int total = scan_chunk<NT>(p, sm, 0, nhg);
+  for (int c0 = kChunk; c0 < B; c0 += kChunk) total += scan_chunk<NT>(p, sm, c0, nhg);
   const int t_lo = (int)((int64_t)wg * total / W);
   const int t_hi = (int)((int64_t)(wg + 1) * total / W);
   int b0 = 0, base = 0;
-  if (B > kChunk) scan_chunk(p, sm, 0, nhg);  // back to the first chunk
+  if (B > kChunk) scan_chunk<NT>(p, sm, 0, nhg);  // back to the first chunk
 
   int pos = t_lo;
   bool first = true;
@@ -276,7 +301,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void paged_decode_rows_kernel(De
     while (rel >= __builtin_amdgcn_readfirstlane(sm.pre[kChunk])) {  // uniform: every thread moves on together
       base += __builtin_amdgcn_readfirstlane(sm.pre[kChunk]);
       b0 += kChunk;
-      scan_chunk(p, sm, b0, nhg);
+      scan_chunk<NT>(p, sm, b0, nhg);
       rel = pos - base;
     }
     int lo = 0, hi = kChunk;  // sm.pre[lo] <= rel < sm.pre[hi]
@@ -414,12 +439,28 @@ __global__ __launch_bounds__(kMergeThreads) void rows_merge_kernel(DecodeArgs p,
   if (lane == 0 && p.out_lse) p.out_lse[orow] = S > 0.f ? mx + logf(S) : -INFINITY;
 }
 
+// Workgroup shape for a head group of 8: four waves of two heads (one wave
+// per SIMD), except for FP4, which runs eight waves of one head, two per SIMD,
+// each within half the register file.  FP4 moves the fewest bytes per
+// instruction; with one wave per SIMD its dependency stalls were exposed, and
+// eight waves made it ~10% faster, while FP8 was ~2% slower with eight.
+template <class C>
+constexpr bool two_waves_per_simd() {
+  return std::is_same<C, MfmaFP4>::value;
+}
+
 template <class C, int G>
 hipError_t launch_group(const DecodeArgs& a, const RowsArgs& r, hipStream_t s) {
-  if (r.head_group == 8)
-    hipLaunchKernelGGL((paged_decode_rows_kernel<C, G, 2>), dim3(r.num_wg), dim3(kDecodeThreads), 0, s, a, r);
-  else
-    hipLaunchKernelGGL((paged_decode_rows_kernel<C, G, 1>), dim3(r.num_wg), dim3(kDecodeThreads), 0, s, a, r);
+  if (r.head_group == 8) {
+    if constexpr (two_waves_per_simd<C>())
+      hipLaunchKernelGGL((paged_decode_rows_kernel<C, G, 1, 2 * kDecodeThreads>), dim3(r.num_wg),
+                         dim3(2 * kDecodeThreads), 0, s, a, r);
+    else
+      hipLaunchKernelGGL((paged_decode_rows_kernel<C, G, 2, kDecodeThreads>), dim3(r.num_wg), dim3(kDecodeThreads),
+                         0, s, a, r);
+  } else
+    hipLaunchKernelGGL((paged_decode_rows_kernel<C, G, 1, kDecodeThreads>), dim3(r.num_wg), dim3(kDecodeThreads), 0,
+                       s, a, r);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int merge_rows = a.dims.num_seqs * a.dims.num_q_heads;
@@ -453,6 +494,7 @@ hipError_t launch_paged_decode_rows(const DecodeArgs& a, const RowsArgs& r, lgm_
   const int G = a.dims.num_q_heads / a.dims.num_kv_heads;
   if (cache == LGM_BF16) return dispatch<MfmaBF16>(a, r, G, s);
   if (cache == LGM_FP8_E4M3) return dispatch<MfmaFP8>(a, r, G, s);
+  if (cache == LGM_FP4_E2M1) return dispatch<MfmaFP4>(a, r, G, s);
   return hipErrorInvalidValue;
 }
 

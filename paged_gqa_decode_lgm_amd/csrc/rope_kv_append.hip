@@ -12,6 +12,15 @@
 // -ffp-contract=off and the pragma below, so no multiply-add is fused.
 // Rows move as eight-element vectors whenever the pointers and the QKV row
 // stride allow it.
+//
+// FP4 caches (mainarch README, decode-attention section: E2M1 KV with E8M0
+// block scales; OCP MX block rule, as the library header states): one thread
+// per 32-element block of a new K or V row.  It evaluates its block's rotated
+// values with the same fp32 operations as the Q path, takes the block's
+// largest magnitude, the scale exponent X = floor(log2 amax) - 2 (exact, from
+// ilogbf), multiplies by 2^-X (exact: a power of two), and rounds each value
+// to E2M1 by comparing its magnitude with the midpoints of the code values
+// (ties go to the even mantissa, magnitudes above 5 go to 6).
 #include "device_num.h"
 #include "lgm_internal.h"
 
@@ -40,17 +49,106 @@ struct ActBF16 {
   __device__ static elem_t store(float x) { return f32_to_bf16_rne(x); }
 };
 struct CacheF32 {
+  static constexpr bool kFp4 = false;
   using elem_t = float;
   __device__ static elem_t store(float x, float) { return x; }
 };
 struct CacheBF16 {
+  static constexpr bool kFp4 = false;
   using elem_t = uint16_t;
   __device__ static elem_t store(float x, float) { return f32_to_bf16_rne(x); }
 };
 struct CacheFP8 {
+  static constexpr bool kFp4 = false;
   using elem_t = uint8_t;
   __device__ static elem_t store(float x, float scale) { return f32_to_e4m3_rne_sat(__fdiv_rn(x, scale)); }
 };
+// FP4 rows are written by fp4_append_blocks, not element by element.
+struct CacheFP4 {
+  static constexpr bool kFp4 = true;
+  using elem_t = uint8_t;
+  __device__ static elem_t store(float, float) { return 0; }
+};
+
+constexpr int kMxBlock = 32;
+
+// E2M1 code of a value already divided by its block scale: nearest of
+// 0, 0.5, 1, 1.5, 2, 3, 4, 6, ties to the even mantissa, saturating at 6;
+// the sign bit is kept, so values that round to zero keep their sign.
+__device__ __forceinline__ uint32_t e2m1_code(float q) {
+  const float a = fabsf(q);
+  uint32_t c = a <= 0.25f ? 0u : a < 0.75f ? 1u : a <= 1.25f ? 2u : a < 1.75f ? 3u
+             : a <= 2.5f ? 4u : a < 3.5f ? 5u : a <= 5.0f ? 6u : 7u;
+  return c | ((__float_as_uint(q) >> 28) & 0x8u);
+}
+
+// Quantises this sequence's new K (rotated) and V rows, one 32-element
+// block per thread: codes to the block's code area at (slot, head), the scale
+// byte to its scale area.  cb_* are the byte addresses of the slot's rows.
+template <class A>
+__device__ void fp4_append_blocks(const AppendArgs& p, const typename A::elem_t* x, const float* s_cos,
+                                  const float* s_sin, uint8_t* kblock, uint8_t* vblock, int slot) {
+#pragma clang fp contract(off)
+  const int D = p.dims.head_dim;
+  const int half = D / 2;
+  const int Hq = p.dims.num_q_heads;
+  const int Hkv = p.dims.num_kv_heads;
+  const int BS = p.dims.block_size;
+  const int nblk = D / kMxBlock;
+  const int64_t codes_bytes = (int64_t)BS * Hkv * (D / 2);
+  for (int t = threadIdx.x; t < 2 * Hkv * nblk; t += kThreads) {
+    const bool is_v = t >= Hkv * nblk;
+    const int u = is_v ? t - Hkv * nblk : t;
+    const int g = u / nblk;
+    const int blk = u - g * nblk;
+    const typename A::elem_t* row = x + (int64_t)(Hq + (is_v ? Hkv : 0) + g) * D;
+    float y[kMxBlock];
+    float amax = 0.f;
+#pragma unroll
+    for (int k = 0; k < kMxBlock; ++k) {
+      const int i = blk * kMxBlock + k;
+      float v;
+      if (is_v) {
+        v = A::load(row + i);
+      } else {
+        // the Q path's operations for pair (i0, i0 + D/2)
+        const int i0 = i < half ? i : i - half;
+        const float c = s_cos[i0];
+        const float sn = s_sin[i0];
+        const float x0 = A::load(row + i0);
+        const float x1 = A::load(row + i0 + half);
+        if (i < half) {
+          const float a0 = x0 * c;
+          const float b0 = x1 * sn;
+          v = a0 - b0;
+        } else {
+          const float a1 = x1 * c;
+          const float b1 = x0 * sn;
+          v = a1 + b1;
+        }
+      }
+      y[k] = v;
+      amax = fmaxf(amax, fabsf(v));
+    }
+    int X = amax > 0.f ? ilogbf(amax) - 2 : -127;
+    X = X < -127 ? -127 : (X > 127 ? 127 : X);
+    // 2^-X as an fp32 bit pattern: X <= 125 for any finite amax (ilogbf <= 127),
+    // so the biased exponent 127 - X lies in [2, 254], a normal float.
+    const float mul = __uint_as_float((uint32_t)(127 - X) << 23);
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int k = 0; k < kMxBlock; ++k) w[k / 8] |= e2m1_code(y[k] * mul) << (4 * (k % 8));
+    uint8_t* base = (is_v ? vblock : kblock);
+    uint8_t* dst = base + (int64_t)(slot * Hkv + g) * (D / 2) + blk * (kMxBlock / 2);
+    if ((uintptr_t)dst % 16 == 0) {
+      *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) dst[k] = (uint8_t)(w[k / 4] >> (8 * (k % 4)));
+    }
+    base[codes_bytes + (int64_t)(slot * Hkv + g) * nblk + blk] = (uint8_t)(X + 127);
+  }
+}
 
 template <class A, class C>
 __global__ __launch_bounds__(kThreads) void rope_kv_append_kernel(AppendArgs p) {
@@ -75,12 +173,16 @@ __global__ __launch_bounds__(kThreads) void rope_kv_append_kernel(AppendArgs p) 
   // The slot's table entry is read before the rotation factors are computed,
   // so its latency overlaps theirs.
   bool write = false;
+  int pb = 0;
   int64_t slot_base = 0;  // element offset of (block, slot, head 0, 0)
   if (active) {
-    const int pb = p.block_tables[(int64_t)b * MB + pos / BS];
+    pb = p.block_tables[(int64_t)b * MB + pos / BS];
     write = (unsigned)pb < (unsigned)p.dims.num_blocks;
     slot_base = ((int64_t)pb * BS + pos % BS) * (int64_t)Hkv * D;
   }
+  // Heads rotated by the element paths: Q and K, or only Q for FP4 caches,
+  // whose K rows are rotated block by block in fp4_append_blocks.
+  const int nrot_heads = Hq + (C::kFp4 ? 0 : Hkv);
   for (int i = threadIdx.x; i < half; i += kThreads) {
     const double w = pow((double)p.rope_theta, (-2.0 * (double)i) / (double)D);
     const double ang = (double)pos * w;
@@ -99,7 +201,7 @@ __global__ __launch_bounds__(kThreads) void rope_kv_append_kernel(AppendArgs p) 
   // Eight-element vectors when every row and pointer allows them (the usual
   // case: dense packed QKV); element by element otherwise.  The arithmetic is
   // the same either way.
-  const bool vec = ((uintptr_t)p.qkv % (8 * sizeof(typename A::elem_t)) == 0) &&
+  const bool vec = (half % 8 == 0) && ((uintptr_t)p.qkv % (8 * sizeof(typename A::elem_t)) == 0) &&
                    ((p.qkv_row_stride * (int64_t)sizeof(typename A::elem_t)) % (8 * sizeof(typename A::elem_t)) == 0) &&
                    ((uintptr_t)p.q_out % (8 * sizeof(typename A::elem_t)) == 0) &&
                    ((uintptr_t)p.k_cache % (8 * sizeof(typename C::elem_t)) == 0) &&
@@ -109,7 +211,7 @@ __global__ __launch_bounds__(kThreads) void rope_kv_append_kernel(AppendArgs p) 
     using CV = Vec8<typename C::elem_t>;
     const int nchunk = half / 8;
     // Rotate every Q head and every K head: (Hq + Hkv) * D/16 chunks of 8 pairs.
-    for (int t = threadIdx.x; t < (Hq + Hkv) * nchunk; t += kThreads) {
+    for (int t = threadIdx.x; t < nrot_heads * nchunk; t += kThreads) {
       const int hh = t / nchunk;
       const int i0 = 8 * (t - hh * nchunk);
       const AV lo = *reinterpret_cast<const AV*>(x + hh * D + i0);
@@ -151,7 +253,7 @@ __global__ __launch_bounds__(kThreads) void rope_kv_append_kernel(AppendArgs p) 
       }
     }
     // V heads are stored unrotated.
-    if (write) {
+    if (write && !C::kFp4) {
       const typename A::elem_t* xv = x + (Hq + Hkv) * D;
       for (int t = threadIdx.x; t < Hkv * D / 8; t += kThreads) {
         const int g = (8 * t) / D;
@@ -163,44 +265,51 @@ __global__ __launch_bounds__(kThreads) void rope_kv_append_kernel(AppendArgs p) 
         *reinterpret_cast<CV*>(vc + slot_base + 8 * t) = o;
       }
     }
-    return;
-  }
-
-  // Rotate every Q head and every K head: (Hq + Hkv) * D/2 pairs.
-  const int nrot = (Hq + Hkv) * half;
-  for (int t = threadIdx.x; t < nrot; t += kThreads) {
-    const int hh = t / half;
-    const int i = t - hh * half;
-    const float c = s_cos[i];
-    const float s = s_sin[i];
-    const float x0 = A::load(x + hh * D + i);
-    const float x1 = A::load(x + hh * D + i + half);
-    const float a0 = x0 * c;
-    const float b0 = x1 * s;
-    const float y0 = a0 - b0;
-    const float a1 = x1 * c;
-    const float b1 = x0 * s;
-    const float y1 = a1 + b1;
-    if (hh < Hq) {
-      qo[hh * D + i] = A::store(y0);
-      qo[hh * D + i + half] = A::store(y1);
-    } else if (write) {
-      const int g = hh - Hq;
-      const float sc = p.k_scale ? p.k_scale[g] : 1.f;
-      kc[slot_base + g * D + i] = C::store(y0, sc);
-      kc[slot_base + g * D + i + half] = C::store(y1, sc);
+  } else {
+    // Rotate every Q head and every K head: (Hq + Hkv) * D/2 pairs.
+    const int nrot = nrot_heads * half;
+    for (int t = threadIdx.x; t < nrot; t += kThreads) {
+      const int hh = t / half;
+      const int i = t - hh * half;
+      const float c = s_cos[i];
+      const float s = s_sin[i];
+      const float x0 = A::load(x + hh * D + i);
+      const float x1 = A::load(x + hh * D + i + half);
+      const float a0 = x0 * c;
+      const float b0 = x1 * s;
+      const float y0 = a0 - b0;
+      const float a1 = x1 * c;
+      const float b1 = x0 * s;
+      const float y1 = a1 + b1;
+      if (hh < Hq) {
+        qo[hh * D + i] = A::store(y0);
+        qo[hh * D + i + half] = A::store(y1);
+      } else if (write) {
+        const int g = hh - Hq;
+        const float sc = p.k_scale ? p.k_scale[g] : 1.f;
+        kc[slot_base + g * D + i] = C::store(y0, sc);
+        kc[slot_base + g * D + i + half] = C::store(y1, sc);
+      }
+    }
+    // V heads are stored unrotated.
+    if (write && !C::kFp4) {
+      const typename A::elem_t* xv = x + (Hq + Hkv) * D;
+      for (int t = threadIdx.x; t < Hkv * D; t += kThreads) {
+        const int g = t / D;
+        const float sc = p.v_scale ? p.v_scale[g] : 1.f;
+        vc[slot_base + t] = C::store(A::load(xv + t), sc);
+      }
     }
   }
-  // V heads are stored unrotated.
-  if (write) {
-    const typename A::elem_t* xv = x + (Hq + Hkv) * D;
-    for (int t = threadIdx.x; t < Hkv * D; t += kThreads) {
-      const int g = t / D;
-      const float sc = p.v_scale ? p.v_scale[g] : 1.f;
-      vc[slot_base + t] = C::store(A::load(xv + t), sc);
+  if constexpr (C::kFp4) {
+    if (write) {
+      const int64_t block_bytes = (int64_t)BS * Hkv * (D / 2 + D / kMxBlock);
+      fp4_append_blocks<A>(p, x, s_cos, s_sin, static_cast<uint8_t*>(p.k_cache) + (int64_t)pb * block_bytes,
+                           static_cast<uint8_t*>(p.v_cache) + (int64_t)pb * block_bytes, pos % BS);
     }
   }
 }
+
 
 template <class A, class C>
 hipError_t launch(const AppendArgs& a, hipStream_t s) {
@@ -214,6 +323,7 @@ hipError_t launch_rope_kv_append(const AppendArgs& a, lgm_dtype act, lgm_dtype c
   if (act == LGM_F32 && cache == LGM_F32) return launch<ActF32, CacheF32>(a, s);
   if (act == LGM_BF16 && cache == LGM_BF16) return launch<ActBF16, CacheBF16>(a, s);
   if (act == LGM_BF16 && cache == LGM_FP8_E4M3) return launch<ActBF16, CacheFP8>(a, s);
+  if (act == LGM_BF16 && cache == LGM_FP4_E2M1) return launch<ActBF16, CacheFP4>(a, s);
   return hipErrorInvalidValue;
 }
 

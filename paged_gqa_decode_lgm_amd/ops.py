@@ -4,8 +4,8 @@ torch (device memory is torch's job).  Every step of the decode path runs in
 liblgm.so; nothing here computes any of it.
 
 Shapes: qkv [B, (Hq+2Hkv)*D], q [B, Hq, D] (rows may be strided), caches
-[num_blocks, block_size, Hkv, D] (NHD), block_tables int32 [B, MB],
-context_lens int32 [B].
+[num_blocks, block_size, Hkv, D] (NHD) or FP4Pool, block_tables int32
+[B, MB], context_lens int32 [B].
 """
 from __future__ import annotations
 
@@ -19,7 +19,33 @@ from . import _binding as B
 _DTYPES = {torch.float32: B.LGM_F32, torch.bfloat16: B.LGM_BF16, torch.float8_e4m3fn: B.LGM_FP8_E4M3}
 
 
-def lgm_dtype(t: torch.Tensor) -> int:
+class FP4Pool:
+    """An FP4 cache pool (LGM_FP4_E2M1): ``data`` is uint8 [num_blocks,
+    block_bytes], each block its NHD E2M1 codes [block_size][Hkv][D/2] (two
+    per byte, low nibble first) followed by its E8M0 scales
+    [block_size][Hkv][D/32].  ``shape`` is the logical (num_blocks,
+    block_size, Hkv, D)."""
+
+    def __init__(self, data: torch.Tensor, block_size: int, num_kv_heads: int, head_dim: int):
+        if head_dim % 32:
+            raise ValueError("FP4 pools need head_dim a multiple of 32")
+        nbytes = block_size * num_kv_heads * (head_dim // 2 + head_dim // 32)
+        if data.dtype != torch.uint8 or data.dim() != 2 or data.shape[1] != nbytes or not data.is_contiguous():
+            raise ValueError(f"FP4 pool data must be contiguous uint8 [num_blocks, {nbytes}]")
+        self.data = data
+        self.shape = (data.shape[0], block_size, num_kv_heads, head_dim)
+
+    @property
+    def device(self):
+        return self.data.device
+
+    def data_ptr(self) -> int:
+        return self.data.data_ptr()
+
+
+def lgm_dtype(t) -> int:
+    if isinstance(t, FP4Pool):
+        return B.LGM_FP4_E2M1
     try:
         return _DTYPES[t.dtype]
     except KeyError:

@@ -45,7 +45,12 @@ class Dev:
 
 def to_device(w: W.Workload) -> Dev:
     cu = lambda t: None if t is None else t.to("cuda")
-    return Dev(w, cu(w.qkv), cu(w.k_pool), cu(w.v_pool), cu(w.block_tables), cu(w.context_lens),
+    c = w.cfg
+    if c.cache == "fp4":
+        pool = lambda t: ops.FP4Pool(t.to("cuda"), c.block_size, c.num_kv_heads, c.head_dim)
+    else:
+        pool = cu
+    return Dev(w, cu(w.qkv), pool(w.k_pool), pool(w.v_pool), cu(w.block_tables), cu(w.context_lens),
                cu(w.k_scale), cu(w.v_scale))
 
 

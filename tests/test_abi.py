@@ -33,7 +33,7 @@ def test_library_loads_and_exports_every_header_function():
                           "lgm_stream_read_probe"}
     for n in names:
         assert hasattr(lib, n), n
-    assert L.lgm_abi_version() == 1
+    assert L.lgm_abi_version() == 2
 
 
 # ------------------------------------------------------------------ append
@@ -63,6 +63,11 @@ APPEND_BAD = [
     (dict(cache_dtype=L.LGM_FP8_E4M3), INV, "k_scale"),
     (dict(cache_dtype=L.LGM_FP8_E4M3, k_scale=addr(6)), INV, "v_scale"),
     (dict(k_scale=addr(6), v_scale=addr(7)), INV, "k_scale"),
+    (dict(cache_dtype=L.LGM_FP4_E2M1, k_scale=addr(6), v_scale=addr(7)), INV, "k_scale"),
+    (dict(cache_dtype=L.LGM_FP4_E2M1, dims=dims(head_dim=48), qkv_row_stride=48 * 48), UNS, "multiple of 32"),
+    (dict(cache_dtype=L.LGM_FP4_E2M1, act_dtype=L.LGM_F32), UNS, "FP4_E2M1"),
+    # an FP4 pool is num_blocks * block_size * Hkv * (D/2 + D/32) bytes = 1000 * 16 * 8 * 68
+    (dict(cache_dtype=L.LGM_FP4_E2M1, v_cache=addr(2) + 1000 * 16 * 8 * 68 - 16), INV, "k_cache"),
     (dict(qkv=None), INV, "qkv"),
     (dict(q_out=None), INV, "q_out"),
     (dict(k_cache=None), INV, "k_cache"),
@@ -116,6 +121,10 @@ ATTN_BAD = [
     (dict(workspace=addr(7) + 8), INV, "workspace"),
     (dict(cache_dtype=L.LGM_FP8_E4M3), INV, "k_scale"),
     (dict(k_scale=addr(8), v_scale=addr(9)), INV, "k_scale"),
+    (dict(cache_dtype=L.LGM_FP4_E2M1, k_scale=addr(8), v_scale=addr(9)), INV, "k_scale"),
+    (dict(cache_dtype=L.LGM_FP4_E2M1, dims=dims(head_dim=64), q_seq_stride=32 * 64), UNS, "FP4_E2M1"),
+    (dict(cache_dtype=L.LGM_FP4_E2M1, act_dtype=L.LGM_FP4_E2M1), UNS, "act"),
+    (dict(cache_dtype=L.LGM_FP4_E2M1, workspace=addr(3) + 1000 * 16 * 8 * 68 - 256), INV, "workspace"),
     (dict(out=None), INV, "out"),
     (dict(q=None), INV, "q"),
     (dict(k_cache=None), INV, "k_cache"),
@@ -205,6 +214,7 @@ def test_row_plan_workspace_formula():
     want = al(W * 2 * rows * 128 * 4) + al(W * 2 * rows * 4) + al(W * 4) + 2 * al(64 * 4)
     assert L.lgm_paged_decode_workspace_size(d, 8192, 0, L.LGM_BF16) == want
     assert L.lgm_paged_decode_workspace_size(d, 8192, 0, L.LGM_FP8_E4M3) == want
+    assert L.lgm_paged_decode_workspace_size(d, 8192, 0, L.LGM_FP4_E2M1) == want
     small = dims(num_seqs=2, num_q_heads=16, num_kv_heads=4, max_blocks_per_seq=8)  # 2 x 4 tiles: one range
     W, rows = 1, 4 * 4
     assert L.lgm_paged_decode_workspace_size(small, 100, 0, L.LGM_BF16) == (

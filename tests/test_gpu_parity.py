@@ -32,7 +32,13 @@ PARITY = {
     "llama3_8b_gqa": dict(num_seqs=8, ctx=(17, 2000)),
     "long_ctx_splitk": dict(num_seqs=2, ctx=8192),
     "fp8_kv": dict(num_seqs=8),
+    "fp4_kv": dict(num_seqs=8),
 }
+
+
+def _host_pool(pool):
+    """A device pool back on the host (FP4 pools are wrapped)."""
+    return (pool.data if isinstance(pool, ops.FP4Pool) else pool).cpu()
 
 
 def _lse_check(g_lse, r_lse, rows=None):
@@ -71,15 +77,21 @@ def _check_append(w, d, q_gpu, rec, ex, seqs=None):
     c = w.cfg
     seqs = range(c.num_seqs) if seqs is None else seqs
     gq = act_raw_tensor(c, q_gpu)
-    gk = pool_raw(w, d.k_pool.cpu())
-    gv = pool_raw(w, d.v_pool.cpu())
+    gk = pool_raw(w, _host_pool(d.k_pool))
+    gv = pool_raw(w, _host_pool(d.v_pool))
     k0, v0 = pool_raw(w, w.k_pool), pool_raw(w, w.v_pool)
     slots = {s for s in rec.slots if s is not None}
-    # index exactness: only the target slots moved
-    mask = np.ones(gk.shape[:2], bool)
-    for (pb, off) in slots:
-        mask[pb, off] = False
-    assert np.array_equal(gk[mask], k0[mask]) and np.array_equal(gv[mask], v0[mask])
+    if c.cache == "fp4":
+        # every byte of both pools: the MX codes and scale bytes of the recipe
+        # at the target slots, everything else unchanged
+        assert np.array_equal(gk, rec.k_pool), "FP4 K pool bytes"
+        assert np.array_equal(gv, rec.v_pool), "FP4 V pool bytes"
+    else:
+        # index exactness: only the target slots moved
+        mask = np.ones(gk.shape[:2], bool)
+        for (pb, off) in slots:
+            mask[pb, off] = False
+        assert np.array_equal(gk[mask], k0[mask]) and np.array_equal(gv[mask], v0[mask])
     xq = xk = None
     if c.act == "bf16":
         x = codecs.bf16_decode(W.storage_bits(w.qkv)).astype(np.float64)
@@ -94,7 +106,7 @@ def _check_append(w, d, q_gpu, rec, ex, seqs=None):
             h = c.head_dim // 2
             bound = 4 * 2.0 ** -24 * np.concatenate([np.abs(x[:, :h]) + np.abs(x[:, h:])] * 2, -1)
             assert (np.abs(gq[b].astype(np.float64) - ex.q_rot[b]) <= bound).all()
-        if rec.slots[b] is None:
+        if rec.slots[b] is None or c.cache == "fp4":
             continue
         pb, off = rec.slots[b]
         if c.cache == "fp8":
@@ -144,7 +156,7 @@ def test_config_parity(name):
     _run_and_check(base.with_(**over))
 
 
-@pytest.mark.parametrize("name", ["llama3_8b_gqa", "long_ctx_splitk", "fp8_kv"])
+@pytest.mark.parametrize("name", ["llama3_8b_gqa", "long_ctx_splitk", "fp8_kv", "fp4_kv"])
 def test_full_size_sampled(name):
     """Full-size workload in the launch configuration the benchmark times;
     the oracle checks a sample of sequences (first, shortest, longest, last)."""
@@ -162,7 +174,7 @@ EDGE_CTX = (0, 1, 15, 16, 17, 63, 64, 65, 200, 513)
 @pytest.mark.parametrize("act,cache,D,G", [
     ("bf16", "bf16", 128, 4), ("bf16", "bf16", 128, 6), ("bf16", "bf16", 128, 1), ("bf16", "bf16", 64, 8),
     ("bf16", "fp8", 128, 4), ("bf16", "fp8", 64, 3), ("f32", "f32", 64, 4), ("f32", "f32", 128, 2),
-    ("bf16", "bf16", 128, 8), ("bf16", "fp8", 128, 5),
+    ("bf16", "bf16", 128, 8), ("bf16", "fp8", 128, 5), ("bf16", "fp4", 128, 4), ("bf16", "fp4", 128, 7),
 ])
 @pytest.mark.parametrize("ps", [16, 64, 0, 4096])
 def test_shapes_and_ragged_edges(act, cache, D, G, ps):
@@ -302,7 +314,7 @@ def test_inactive_sequence_append_writes_nothing():
     assert np.array_equal(act_raw_tensor(cfg, q)[0], W.storage_bits(w.qkv)[0, : 12 * 128].reshape(12, 128))
 
 
-@pytest.mark.parametrize("name", ["llama3_8b_gqa", "fp8_kv"])
+@pytest.mark.parametrize("name", ["llama3_8b_gqa", "fp8_kv", "fp4_kv"])
 @pytest.mark.parametrize("ps", [64, 512])
 def test_persistent_workspace_is_reusable_and_left_zeroed(name, ps):
     """The matrix-core kernel hands out work items from two counters at the
@@ -344,7 +356,7 @@ def test_many_short_sequences_and_empty_ones(ps):
     _run_and_check(cfg1)
 
 
-@pytest.mark.parametrize("cache", ["bf16", "fp8"])
+@pytest.mark.parametrize("cache", ["bf16", "fp8", "fp4"])
 @pytest.mark.parametrize("hkv,G", [(4, 1), (4, 4), (8, 4), (8, 5), (16, 2), (8, 16)])
 def test_row_plan_ragged_edges(cache, hkv, G):
     """Whole-row ranges (partition_size 0, kv heads divisible by 4): head
@@ -439,3 +451,111 @@ def test_stream_read_probe_reads_without_writing():
     torch.cuda.synchronize()
     assert int(sink.item()) == -5
     assert bool((buf == 7).all())
+
+
+# ------------------------------------------------------------------ FP4 caches
+def _fp4_parts(pool: torch.Tensor, cfg):
+    """Code and scale views of an FP4 pool tensor [NB, block_bytes] (host or device)."""
+    bs, hkv, d = cfg.block_size, cfg.num_kv_heads, cfg.head_dim
+    nc = bs * hkv * d // 2
+    return pool[:, :nc].view(-1, bs, hkv, d // 2), pool[:, nc:].view(-1, bs, hkv, d // 32)
+
+
+@pytest.mark.parametrize("ps", [0, 64])
+def test_fp4_poisoned_unused_slots_and_blocks_are_bitwise_identical(ps):
+    """Slots past each context and blocks no table uses hold code bytes 0xFF
+    and NaN scale bytes (0xFF); table entries past the context are out of
+    range.  None of it may reach the output."""
+    cfg = W.CONFIGS["fp4_kv"].with_(num_seqs=6, ctx=(100, 3000), num_blocks=None, append=False,
+                                    partition_size=ps)
+    w = W.make_workload(cfg)
+    q = q_from_qkv(w).cuda()
+    bt = w.block_tables.clone()
+    kp, vp = w.k_pool.clone(), w.v_pool.clone()
+    used = set()
+    for pool in (kp, vp):
+        codes, scales = _fp4_parts(pool, cfg)
+        for b in range(cfg.num_seqs):
+            L = int(w.context_lens[b])
+            nb = -(-L // 16)
+            used |= set(w.block_tables[b, :nb].tolist())
+            last = int(w.block_tables[b, nb - 1])
+            codes[last, L - (nb - 1) * 16:] = 0xFF
+            scales[last, L - (nb - 1) * 16:] = 0xFF
+    for b in range(cfg.num_seqs):
+        nb = -(-int(w.context_lens[b]) // 16)
+        bt[b, nb:] = torch.tensor([-5, 1 << 30] * bt.shape[1], dtype=torch.int32)[: bt.shape[1] - nb]
+    unused = [i for i in range(kp.shape[0]) if i not in used]
+    kp[unused] = 0xFF
+    vp[unused] = 0xFF
+    w2 = dataclasses.replace(w, block_tables=bt, k_pool=kp, v_pool=vp)
+    announce("fp4 poison", ps)
+    o1, l1 = gpu_attention(to_device(w), q, ps)
+    o2, l2 = gpu_attention(to_device(w2), q, ps)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+    r_out, r_lse = oracle_attention(w, act_raw(w, q_from_qkv(w)), pool_raw(w, w.k_pool), pool_raw(w, w.v_pool))
+    assert max_abs(out_values(cfg, o1), r_out) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("ps", [0, 64])
+def test_fp4_every_code_and_scale_position_decodes_exactly(ps):
+    """K rows all decode to 1.0 (code 0x2, scale byte 127), so every key is
+    equal and the output is the mean of the V rows.  V rows cycle through all
+    16 codes in every nibble position with scale bytes 0x00 (2^-127) and
+    120..127 in every scale position; the oracle decodes them from the
+    format's definition."""
+    cfg = W.CONFIGS["fp4_kv"].with_(num_seqs=2, ctx_list=(254, 254), num_blocks=None, append=False,
+                                    partition_size=ps)
+    w = W.make_workload(cfg)
+    kp, vp = w.k_pool.clone(), w.v_pool.clone()
+    kc, ks = _fp4_parts(kp, cfg)
+    kc[:] = 0x22
+    ks[:] = 127
+    vc, vs = _fp4_parts(vp, cfg)
+    rng = np.random.default_rng(17)
+    for b in range(2):
+        for j in range(254):
+            pb, off = int(w.block_tables[b, j // 16]), j % 16
+            lo = (np.arange(64) + j + 5 * b) % 16
+            hi = (np.arange(64) * 7 + 3 * j + b) % 16
+            vc[pb, off] = torch.from_numpy((lo | (hi << 4)).astype(np.uint8)).view(1, 64).expand(cfg.num_kv_heads, 64)
+            vs[pb, off] = torch.from_numpy(rng.choice([0, 120, 121, 122, 123, 124, 125, 126, 127],
+                                                      size=(cfg.num_kv_heads, 4)).astype(np.uint8))
+    w2 = dataclasses.replace(w, k_pool=kp, v_pool=vp)
+    q = q_from_qkv(w2).cuda()
+    announce("fp4 all codes", ps)
+    out, lse = gpu_attention(to_device(w2), q, ps)
+    torch.cuda.synchronize()
+    r_out, r_lse = oracle_attention(w2, act_raw(w2, q_from_qkv(w2)), pool_raw(w2, w2.k_pool), pool_raw(w2, w2.v_pool))
+    assert max_abs(out_values(cfg, out), r_out) <= TOL["bf16"]
+    _lse_check(lse.cpu().numpy(), r_lse)
+
+
+def test_fp4_append_quantises_edge_blocks_exactly():
+    """New K/V rows whose 32-element blocks hit the rounding edges: exact
+    midpoints between codes, values above 6 * scale, an all-zero block and a
+    block of negative values that round to zero; the bytes must equal the
+    oracle's."""
+    cfg = W.CONFIGS["fp4_kv"].with_(num_seqs=4, ctx_list=(1, 17, 300, 16), num_blocks=None)
+    w = W.make_workload(cfg)
+    Hq, Hkv, D = cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim
+    qkv = w.qkv.float().numpy().reshape(cfg.num_seqs, Hq + 2 * Hkv, D)
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 7.0, -0.25, -0.75, -5.0, -7.5, 6.0, 4.0, 0.5, 0.0])
+    for b in range(cfg.num_seqs):
+        for g in range(Hkv):
+            v = qkv[b, Hq + Hkv + g]
+            v[0:16] = mids * 2.0 ** (g - 3)         # block 0: midpoints at scale 2^(g-3) (largest 7.5 -> X = g - 3)
+            v[16:32] = mids[::-1] * 2.0 ** (g - 3)
+            v[32:64] = 0.0                          # block 1: all zero
+            v[64:96] = -(2.0 ** -12)                # block 2: tiny negatives (round to -0 against a big value)
+            v[96] = 3.0
+    qb = torch.from_numpy(qkv.reshape(cfg.num_seqs, -1)).to(torch.bfloat16)
+    w2 = dataclasses.replace(w, qkv=qb)
+    d = to_device(w2)
+    announce("fp4 append edges")
+    q = gpu_append(d)
+    torch.cuda.synchronize()
+    rec = oracle_append(w2, "recipe")
+    ex = oracle_append(w2, "exact")
+    _check_append(w2, d, q, rec, ex)
