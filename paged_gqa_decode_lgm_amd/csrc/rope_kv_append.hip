@@ -87,7 +87,7 @@ __device__ __forceinline__ uint32_t e2m1_code(float q) {
 // byte to its scale area.  cb_* are the byte addresses of the slot's rows.
 template <class A>
 __device__ void fp4_append_blocks(const AppendArgs& p, const typename A::elem_t* x, const float* s_cos,
-                                  const float* s_sin, uint8_t* kblock, uint8_t* vblock, int slot) {
+                                  const float* s_sin, uint8_t* kblock, uint8_t* vblock, int slot, bool vec) {
 #pragma clang fp contract(off)
   const int D = p.dims.head_dim;
   const int half = D / 2;
@@ -102,22 +102,47 @@ __device__ void fp4_append_blocks(const AppendArgs& p, const typename A::elem_t*
     const int g = u / nblk;
     const int blk = u - g * nblk;
     const typename A::elem_t* row = x + (int64_t)(Hq + (is_v ? Hkv : 0) + g) * D;
+    // The block's own values and, for K, their rotation partners: elements
+    // blk*32 .. +31 and the same range shifted by D/2 (a block lies within one
+    // half, since D/2 is a multiple of 32).
+    const int i_first = blk * kMxBlock;
+    const int lo_first = i_first < half ? i_first : i_first - half;  // first element of the low half used
+    typename A::elem_t xs[kMxBlock], xp[kMxBlock];  // x[i0 + k] and x[i0 + D/2 + k], i0 = lo_first
+    if (vec) {
+      using AV = Vec8<typename A::elem_t>;
+#pragma unroll
+      for (int c = 0; c < kMxBlock / 8; ++c) {
+        const AV a = *reinterpret_cast<const AV*>(row + (is_v ? i_first : lo_first) + 8 * c);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) xs[8 * c + k] = a.v[k];
+        if (!is_v) {
+          const AV b = *reinterpret_cast<const AV*>(row + lo_first + half + 8 * c);
+#pragma unroll
+          for (int k = 0; k < 8; ++k) xp[8 * c + k] = b.v[k];
+        }
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < kMxBlock; ++k) {
+        xs[k] = row[(is_v ? i_first : lo_first) + k];
+        if (!is_v) xp[k] = row[lo_first + half + k];
+      }
+    }
     float y[kMxBlock];
     float amax = 0.f;
 #pragma unroll
     for (int k = 0; k < kMxBlock; ++k) {
-      const int i = blk * kMxBlock + k;
       float v;
       if (is_v) {
-        v = A::load(row + i);
+        v = A::load(&xs[k]);
       } else {
         // the Q path's operations for pair (i0, i0 + D/2)
-        const int i0 = i < half ? i : i - half;
+        const int i0 = lo_first + k;
         const float c = s_cos[i0];
         const float sn = s_sin[i0];
-        const float x0 = A::load(row + i0);
-        const float x1 = A::load(row + i0 + half);
-        if (i < half) {
+        const float x0 = A::load(&xs[k]);
+        const float x1 = A::load(&xp[k]);
+        if (i_first < half) {
           const float a0 = x0 * c;
           const float b0 = x1 * sn;
           v = a0 - b0;
@@ -305,7 +330,7 @@ __global__ __launch_bounds__(kThreads) void rope_kv_append_kernel(AppendArgs p) 
     if (write) {
       const int64_t block_bytes = (int64_t)BS * Hkv * (D / 2 + D / kMxBlock);
       fp4_append_blocks<A>(p, x, s_cos, s_sin, static_cast<uint8_t*>(p.k_cache) + (int64_t)pb * block_bytes,
-                           static_cast<uint8_t*>(p.v_cache) + (int64_t)pb * block_bytes, pos % BS);
+                           static_cast<uint8_t*>(p.v_cache) + (int64_t)pb * block_bytes, pos % BS, vec);
     }
   }
 }

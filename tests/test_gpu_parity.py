@@ -559,3 +559,20 @@ def test_fp4_append_quantises_edge_blocks_exactly():
     rec = oracle_append(w2, "recipe")
     ex = oracle_append(w2, "exact")
     _check_append(w2, d, q, rec, ex)
+
+
+@pytest.mark.parametrize("D", [8, 24, 40, 96])
+@pytest.mark.parametrize("act,cache", [("bf16", "bf16"), ("f32", "f32"), ("bf16", "fp8")])
+def test_append_small_and_odd_head_dims(D, act, cache):
+    """Head dims whose half is not a multiple of 8 take the element-wise path
+    even with aligned buffers; every rotated value and appended slot must
+    still match the oracle (the append supports any even D up to 256)."""
+    cfg = W.Config(f"append_D{D}_{cache}", seed=21, num_seqs=5, num_q_heads=6, num_kv_heads=2, head_dim=D,
+                   block_size=16, act=act, cache=cache, ctx=0, rope_theta=1e4, partition_size=0, append=True,
+                   ctx_list=(1, 16, 17, 40, 0))
+    w = W.make_workload(cfg)
+    d = to_device(w)
+    announce("append", cfg.name)
+    q = gpu_append(d)
+    torch.cuda.synchronize()
+    _check_append(w, d, q, oracle_append(w, "recipe"), oracle_append(w, "exact"))
