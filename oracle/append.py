@@ -22,14 +22,21 @@ details open; the readings taken here are:
   is exact, so the recipe needs no fp32 step of its own.  Codes go to the
   block's code area and the scale bytes to its scale area (codecs.fp4_block_views);
 * a sequence with ctx <= 0 is inactive: nothing is written to the caches and
-  its q_out row is its Q rotated by angle zero, i.e. copied.
+  its q_out row is its Q rotated by angle zero, i.e. copied;
+* contract variants (Loom's "Position and KV" row: NeoX/interleaved RoPE,
+  NHD/HND cache views, static per-tensor/per-head FP8 scales):
+  rope_style="interleaved" rotates adjacent pairs (rope.rope_interleaved_*);
+  layout="hnd" stores the pools as [num_blocks][Hkv][block_size][D] (FP4:
+  codes [Hkv][block_size][D/2], then scales [Hkv][block_size][D/32] per
+  block); a scale array of one element is a per-tensor scale, used for every
+  kv head.
 
 Storage arrays: act 'f32' -> float32 values, 'bf16' -> uint16 bits;
 cache 'f32' -> float32, 'bf16' -> uint16 bits, 'fp8' -> uint8 codes,
 'fp4' -> uint8 blocks [num_blocks, block_bytes] (codes, then scales).
 
 Two modes:
-  mode="recipe"  the fp32 evaluation recipe (rope.rope_neox_f32_recipe, fp32
+  mode="recipe"  the fp32 evaluation recipe (rope.rope_f32_recipe, fp32
                  division by the scale) then rounding to storage: this is what
                  must match the device bit for bit;
   mode="exact"   the fp64 rotation rounded once to storage (the mathematical
@@ -90,9 +97,24 @@ class AppendResult:
     slots: list              # per sequence: (physical block, slot) written, or None
 
 
+def pool_view(pool, cache: str, block_size: int, num_kv_heads: int, head_dim: int, layout: str = "nhd"):
+    """A pool as [NB, block_size, Hkv, ...] views (for FP4 the pair (codes,
+    scales)); for HND the block and head axes of the stored array are swapped,
+    so writes through the view land in the stored layout."""
+    p = np.asarray(pool)
+    if cache == "fp4":
+        return codecs.fp4_block_views(p, block_size, num_kv_heads, head_dim, layout)
+    if layout == "hnd":
+        return np.swapaxes(p, 1, 2)
+    if layout != "nhd":
+        raise ValueError(layout)
+    return p
+
+
 def rope_kv_append(qkv, context_lens, block_tables, k_pool, v_pool, *, num_q_heads: int,
                    num_kv_heads: int, head_dim: int, block_size: int, act: str, cache: str,
-                   rope_theta: float, k_scale=None, v_scale=None, mode: str = "recipe") -> AppendResult:
+                   rope_theta: float, k_scale=None, v_scale=None, mode: str = "recipe",
+                   rope_style: str = "neox", layout: str = "nhd") -> AppendResult:
     Hq, Hkv, D, bs = num_q_heads, num_kv_heads, head_dim, block_size
     qkv = np.asarray(qkv)
     B = qkv.shape[0]
@@ -102,21 +124,24 @@ def rope_kv_append(qkv, context_lens, block_tables, k_pool, v_pool, *, num_q_hea
 
     q_in, k_in, v_in = x[:, :Hq], x[:, Hq:Hq + Hkv], x[:, Hq + Hkv:]
     if mode == "recipe":
-        q_rot = rope.rope_neox_f32_recipe(q_in.astype(np.float32), pos, rope_theta).astype(np.float64)
-        k_rot = rope.rope_neox_f32_recipe(k_in.astype(np.float32), pos, rope_theta).astype(np.float64)
+        q_rot = rope.rope_f32_recipe(q_in.astype(np.float32), pos, rope_theta, rope_style).astype(np.float64)
+        k_rot = rope.rope_f32_recipe(k_in.astype(np.float32), pos, rope_theta, rope_style).astype(np.float64)
     elif mode == "exact":
-        q_rot = rope.rope_neox_f64(q_in, pos, rope_theta)
-        k_rot = rope.rope_neox_f64(k_in, pos, rope_theta)
+        q_rot = rope.rope_f64(q_in, pos, rope_theta, rope_style)
+        k_rot = rope.rope_f64(k_in, pos, rope_theta, rope_style)
     else:
         raise ValueError(mode)
 
     q_out = f64_to_act(q_rot, act)
     k_new = np.array(k_pool, copy=True)
     v_new_pool = np.array(v_pool, copy=True)
+    kview = pool_view(k_new, cache, bs, Hkv, D, layout)
+    vview = pool_view(v_new_pool, cache, bs, Hkv, D, layout)
     if cache == "fp4":
-        k_parts = codecs.fp4_block_views(k_new, bs, Hkv, D)
-        v_parts = codecs.fp4_block_views(v_new_pool, bs, Hkv, D)
+        k_parts, v_parts = kview, vview
         assert all(np.shares_memory(a, base) for a, base in ((k_parts[0], k_new), (v_parts[1], v_new_pool)))
+    else:
+        assert np.shares_memory(kview, k_new) and np.shares_memory(vview, v_new_pool)
     slots = []
     bt = np.asarray(block_tables)
     for b in range(B):
@@ -131,7 +156,7 @@ def rope_kv_append(qkv, context_lens, block_tables, k_pool, v_pool, *, num_q_hea
                 parts[0][pb, off] = codecs.fp4_pack(codes)
                 parts[1][pb, off] = scale_bytes
         else:
-            k_new[pb, off] = f64_to_cache(k_rot[b], cache, k_scale, fp32_div=(mode == "recipe"))
-            v_new_pool[pb, off] = f64_to_cache(v_in[b], cache, v_scale, fp32_div=(mode == "recipe"))
+            kview[pb, off] = f64_to_cache(k_rot[b], cache, k_scale, fp32_div=(mode == "recipe"))
+            vview[pb, off] = f64_to_cache(v_in[b], cache, v_scale, fp32_div=(mode == "recipe"))
         slots.append((pb, off))
     return AppendResult(q_out, k_new, v_new_pool, q_rot, k_rot, v_in, slots)

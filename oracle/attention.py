@@ -15,13 +15,15 @@ G = Hq / Hkv query heads; the pages only say that a group of query heads
 shares one KV head) and L = context_lens[b]:
     K_j, V_j = cache rows of token j < L, found through the block table:
                physical block block_tables[b, j // bs], slot j % bs
-               (FP8 rows are decoded and multiplied by the head's scale;
+               (FP8 rows are decoded and multiplied by the head's scale, or
+               the single per-tensor scale;
                FP4 rows are E2M1 codes times their 32-element blocks' E8M0
                scales, oracle.codecs)
     s_j   = scale * <q_h, K_j>
     p     = softmax(s)
     out_h = sum_j p_j V_j,   lse_h = log sum_j exp(s_j)   (natural log)
-L = 0 gives out = 0 and lse = -inf.
+L = 0 gives out = 0 and lse = -inf.  The pools are NHD ([NB][bs][Hkv][D]) or,
+with layout="hnd", [NB][Hkv][bs][D] (Loom's "NHD/HND cache views").
 
 Split-K (the reading taken of "split-K partitions merged by log-sum-exp"):
 partition p covers tokens [p*PS, min((p+1)*PS, L)), P_b = ceil(L / PS);
@@ -53,13 +55,20 @@ def decode_rows(raw, cache: str, scale_g: Optional[float] = None) -> np.ndarray:
     raise ValueError(cache)
 
 
-def kv_source(pool, cache: str, block_size: int, num_kv_heads: int, head_dim: int):
+def kv_source(pool, cache: str, block_size: int, num_kv_heads: int, head_dim: int, layout: str = "nhd"):
     """A pool as gather_kv indexes it: [NB, bs, Hkv, D] storage, or for FP4
     (uint8 [NB, block_bytes] blocks of codes then scales) the pair of views
-    (codes [NB, bs, Hkv, D/2], scales [NB, bs, Hkv, D/32])."""
+    (codes [NB, bs, Hkv, D/2], scales [NB, bs, Hkv, D/32]).  An HND pool
+    ([NB, Hkv, bs, D]; FP4: each part head-major) is viewed with the block
+    and head axes swapped, so the gather is the same for both layouts."""
     if cache == "fp4":
-        return codecs.fp4_block_views(pool, block_size, num_kv_heads, head_dim)
-    return np.asarray(pool)
+        return codecs.fp4_block_views(pool, block_size, num_kv_heads, head_dim, layout)
+    p = np.asarray(pool)
+    if layout == "hnd":
+        return np.swapaxes(p, 1, 2)
+    if layout != "nhd":
+        raise ValueError(layout)
+    return p
 
 
 def gather_kv(pool, block_tables, b: int, L: int, g: int, block_size: int, cache: str,
@@ -75,7 +84,8 @@ def gather_kv(pool, block_tables, b: int, L: int, g: int, block_size: int, cache
         codes, scales = pool
         return decode_rows((codes[pb, j % block_size, g, :], scales[pb, j % block_size, g, :]), cache)
     raw = np.asarray(pool)[pb, j % block_size, g, :]
-    sg = None if scale is None else float(np.asarray(scale)[g])
+    sc = None if scale is None else np.asarray(scale).reshape(-1)
+    sg = None if sc is None else float(sc[g] if sc.size > 1 else sc[0])  # one element: a per-tensor scale
     return decode_rows(raw, cache, sg)
 
 
@@ -97,7 +107,7 @@ def attend(q, K, V, scale: float):
 
 def paged_decode(q, k_pool, v_pool, block_tables, context_lens, softmax_scale: float, *,
                  num_kv_heads: int, block_size: int, cache: str, k_scale=None, v_scale=None,
-                 seqs: Optional[Iterable[int]] = None):
+                 seqs: Optional[Iterable[int]] = None, layout: str = "nhd"):
     """out [B, Hq, D] and lse [B, Hq] in fp64.  q: [B, Hq, D] (float64 values).
     ``seqs`` restricts the work to some sequences (others are NaN)."""
     q = np.asarray(q, dtype=np.float64)
@@ -106,8 +116,8 @@ def paged_decode(q, k_pool, v_pool, block_tables, context_lens, softmax_scale: f
     out = np.full((B, Hq, D), np.nan)
     lse = np.full((B, Hq), np.nan)
     ctx = np.asarray(context_lens, dtype=np.int64)
-    k_pool = kv_source(k_pool, cache, block_size, num_kv_heads, D)
-    v_pool = kv_source(v_pool, cache, block_size, num_kv_heads, D)
+    k_pool = kv_source(k_pool, cache, block_size, num_kv_heads, D, layout)
+    v_pool = kv_source(v_pool, cache, block_size, num_kv_heads, D, layout)
     for b in (range(B) if seqs is None else seqs):
         L = max(int(ctx[b]), 0)
         for g in range(num_kv_heads):
@@ -126,7 +136,7 @@ def num_partitions(context_lens, partition_size: int) -> np.ndarray:
 
 def paged_decode_partials(q, k_pool, v_pool, block_tables, context_lens, softmax_scale: float,
                           partition_size: int, *, num_kv_heads: int, block_size: int, cache: str,
-                          k_scale=None, v_scale=None):
+                          k_scale=None, v_scale=None, layout: str = "nhd"):
     """Per-partition records: o_p [B, Hq, Pmax, D] (normalised), lse_p
     [B, Hq, Pmax] and P_b [B].  Records at p >= P_b are zeros / -inf."""
     q = np.asarray(q, dtype=np.float64)
@@ -138,8 +148,8 @@ def paged_decode_partials(q, k_pool, v_pool, block_tables, context_lens, softmax
     o_p = np.zeros((B, Hq, Pmax, D))
     lse_p = np.full((B, Hq, Pmax), -np.inf)
     ctx = np.asarray(context_lens, dtype=np.int64)
-    k_pool = kv_source(k_pool, cache, block_size, num_kv_heads, D)
-    v_pool = kv_source(v_pool, cache, block_size, num_kv_heads, D)
+    k_pool = kv_source(k_pool, cache, block_size, num_kv_heads, D, layout)
+    v_pool = kv_source(v_pool, cache, block_size, num_kv_heads, D, layout)
     for b in range(B):
         L = max(int(ctx[b]), 0)
         for g in range(num_kv_heads):

@@ -213,20 +213,27 @@ def mx_fp4_dequantize(packed, scales) -> np.ndarray:
     return (v.reshape(v.shape[:-1] + (D // MX_BLOCK, MX_BLOCK)) * s[..., None]).reshape(v.shape)
 
 
-def fp4_block_views(pool, block_size: int, num_kv_heads: int, head_dim: int):
+def fp4_block_views(pool, block_size: int, num_kv_heads: int, head_dim: int, layout: str = "nhd"):
     """An FP4 cache pool, uint8 [num_blocks, block_bytes], as its two parts.
 
     Each block holds its codes, NHD [block_size][num_kv_heads][head_dim/2]
-    bytes, followed by its scales, [block_size][num_kv_heads][head_dim/32]
-    bytes.  Returns (codes [NB, bs, Hkv, D/2], scales [NB, bs, Hkv, D/32])."""
+    bytes (HND: [num_kv_heads][block_size][head_dim/2]), followed by its
+    scales in the same order with head_dim/32 bytes per row.  Returns
+    (codes [NB, bs, Hkv, D/2], scales [NB, bs, Hkv, D/32]), views into the
+    pool whatever the stored order."""
     p = np.asarray(pool, dtype=np.uint8)
     nb = p.shape[0]
     nc = block_size * num_kv_heads * head_dim // 2
     ns = block_size * num_kv_heads * head_dim // MX_BLOCK
     if p.shape[1] != nc + ns:
         raise ValueError(f"FP4 block holds {nc + ns} bytes, pool rows have {p.shape[1]}")
-    return (p[:, :nc].reshape(nb, block_size, num_kv_heads, head_dim // 2),
-            p[:, nc:].reshape(nb, block_size, num_kv_heads, head_dim // MX_BLOCK))
+    if layout == "nhd":
+        return (p[:, :nc].reshape(nb, block_size, num_kv_heads, head_dim // 2),
+                p[:, nc:].reshape(nb, block_size, num_kv_heads, head_dim // MX_BLOCK))
+    if layout == "hnd":
+        return (np.swapaxes(p[:, :nc].reshape(nb, num_kv_heads, block_size, head_dim // 2), 1, 2),
+                np.swapaxes(p[:, nc:].reshape(nb, num_kv_heads, block_size, head_dim // MX_BLOCK), 1, 2))
+    raise ValueError(layout)
 
 
 def fp4_block_bytes(block_size: int, num_kv_heads: int, head_dim: int) -> int:

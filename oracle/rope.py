@@ -1,4 +1,4 @@
-"""NeoX (split-half) rotary position embedding (oracle only).
+"""NeoX (split-half) and interleaved rotary position embedding (oracle only).
 
 The pages name the operation but print no formula: Loom Kernels lists
 "NeoX/interleaved RoPE + native/static-FP8 paged-KV write" among its
@@ -10,7 +10,14 @@ rotated by the angle pos * w_i with w_i = theta ** (-2i/D):
     y[i]       = x[i] * cos - x[i + D/2] * sin
     y[i + D/2] = x[i + D/2] * cos + x[i] * sin
 
-Two evaluations are provided:
+The interleaved form (the GPT-J layout; Loom's "interleaved RoPE") pairs
+adjacent elements instead: pair i is (x[2i], x[2i + 1]) with the same angle
+pos * w_i:
+
+    y[2i]     = x[2i] * cos - x[2i + 1] * sin
+    y[2i + 1] = x[2i + 1] * cos + x[2i] * sin
+
+Two evaluations are provided for each:
   rope_neox_f64        the exact rotation in fp64 (the mathematical result);
   rope_neox_f32_recipe the rotation as a device evaluates it in fp32: the
                        angle and its cosine/sine in fp64, each rounded once to
@@ -73,3 +80,49 @@ def rope_neox_f32_recipe(x, pos, theta: float) -> np.ndarray:
     y_lo = np.subtract(np.multiply(lo, c, dtype=f32), np.multiply(hi, s, dtype=f32), dtype=f32)
     y_hi = np.add(np.multiply(hi, c, dtype=f32), np.multiply(lo, s, dtype=f32), dtype=f32)
     return np.concatenate([y_lo, y_hi], axis=-1)
+
+
+def rope_interleaved_f64(x, pos, theta: float) -> np.ndarray:
+    """Exact adjacent-pair rotation of x[..., D] (fp64)."""
+    x = np.asarray(x, dtype=np.float64)
+    D = x.shape[-1]
+    ang = _per_row(rope_angles(pos, theta, D), x.ndim)
+    c, s = np.cos(ang), np.sin(ang)
+    ev, od = x[..., 0::2], x[..., 1::2]
+    y = np.empty_like(x)
+    y[..., 0::2] = ev * c - od * s
+    y[..., 1::2] = od * c + ev * s
+    return y
+
+
+def rope_interleaved_f32_recipe(x, pos, theta: float) -> np.ndarray:
+    """The fp32 evaluation recipe of the adjacent-pair rotation."""
+    x = np.asarray(x, dtype=np.float32)
+    D = x.shape[-1]
+    c, s = rope_cos_sin_f32(pos, theta, D)
+    c, s = _per_row(c, x.ndim), _per_row(s, x.ndim)
+    ev, od = x[..., 0::2], x[..., 1::2]
+    f32 = np.float32
+    y = np.empty_like(x)
+    y[..., 0::2] = np.subtract(np.multiply(ev, c, dtype=f32), np.multiply(od, s, dtype=f32), dtype=f32)
+    y[..., 1::2] = np.add(np.multiply(od, c, dtype=f32), np.multiply(ev, s, dtype=f32), dtype=f32)
+    return y
+
+
+ROPE_STYLES = ("neox", "interleaved")
+
+
+def rope_f64(x, pos, theta: float, style: str = "neox") -> np.ndarray:
+    if style == "neox":
+        return rope_neox_f64(x, pos, theta)
+    if style == "interleaved":
+        return rope_interleaved_f64(x, pos, theta)
+    raise ValueError(style)
+
+
+def rope_f32_recipe(x, pos, theta: float, style: str = "neox") -> np.ndarray:
+    if style == "neox":
+        return rope_neox_f32_recipe(x, pos, theta)
+    if style == "interleaved":
+        return rope_interleaved_f32_recipe(x, pos, theta)
+    raise ValueError(style)

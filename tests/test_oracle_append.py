@@ -158,3 +158,67 @@ def test_fp4_append_writes_mx_codes_of_the_recipe_and_nothing_else():
                 expect[pb, nc + (off * hkv + g) * d // 32:nc + (off * hkv + g + 1) * d // 32] = sc[g]
     assert np.array_equal(r.k_pool, k_expect)
     assert np.array_equal(r.v_pool, v_expect)
+
+
+# ------------------------------------------------------------------ contract variants
+def _append_raw(w, mode, **kw):
+    c = w.cfg
+    raw = (lambda t: t.numpy()) if c.cache == "f32" else workloads.storage_bits
+    qkv = w.qkv.numpy() if c.act == "f32" else workloads.storage_bits(w.qkv)
+    return AP.rope_kv_append(
+        qkv, w.context_lens.numpy(), w.block_tables.numpy(), kw.pop("k_pool", raw(w.k_pool)),
+        kw.pop("v_pool", raw(w.v_pool)), num_q_heads=c.num_q_heads, num_kv_heads=c.num_kv_heads,
+        head_dim=c.head_dim, block_size=c.block_size, act=c.act, cache=c.cache, rope_theta=c.rope_theta,
+        k_scale=kw.pop("k_scale", None if w.k_scale is None else w.k_scale.numpy()),
+        v_scale=kw.pop("v_scale", None if w.v_scale is None else w.v_scale.numpy()), mode=mode, **kw)
+
+
+@pytest.mark.parametrize("mode", ["recipe", "exact"])
+def test_interleaved_append_is_neox_append_of_even_odd_split_rows(mode):
+    """Permuting each Q and K head's elements (evens first, then odds) and
+    running the NeoX append gives, after undoing the permutation, exactly the
+    interleaved append: q_out and the appended K rows bit for bit, V as is."""
+    w = _wl("qwen2.5_1.5b_gqa", num_seqs=3, ctx=(1, 300), num_blocks=None)
+    c = w.cfg
+    D, Hq, Hkv = c.head_dim, c.num_q_heads, c.num_kv_heads
+    perm = np.concatenate([np.arange(0, D, 2), np.arange(1, D, 2)])
+    inv = np.argsort(perm)
+    qkv = workloads.storage_bits(w.qkv).reshape(c.num_seqs, Hq + 2 * Hkv, D).copy()
+    qkv_p = qkv.copy()
+    qkv_p[:, :Hq + Hkv] = qkv[:, :Hq + Hkv][..., perm]
+    w_p = workloads.Workload(c, w.context_lens, w.block_tables, w.k_pool, w.v_pool,
+                             torch.from_numpy(qkv_p.reshape(c.num_seqs, -1)).view(torch.bfloat16), None, None)
+    r_int = _append_raw(w, mode, rope_style="interleaved")
+    r_neo = _append_raw(w_p, mode)
+    assert np.array_equal(r_int.q_out, r_neo.q_out[..., inv])
+    for b in range(c.num_seqs):
+        pb, off = r_int.slots[b]
+        assert np.array_equal(r_int.k_pool[pb, off], r_neo.k_pool[pb, off][..., inv])
+        assert np.array_equal(r_int.v_pool[pb, off], r_neo.v_pool[pb, off])
+
+
+@pytest.mark.parametrize("name", ["qwen2.5_1.5b_gqa", "fp8_kv", "fp4_kv", "tiny_mqa_f32"])
+def test_hnd_append_writes_the_same_rows_head_major(name):
+    """Appending into HND pools equals appending into NHD pools and then
+    moving every block's rows head-major (the conversion is written out in
+    test_oracle_attention)."""
+    import test_oracle_attention as T_A
+    over = dict(num_seqs=6, ctx=(1, 200), num_blocks=None) if name != "tiny_mqa_f32" else {}
+    w = _wl(name, **over)
+    c = w.cfg
+    raw = (lambda t: t.numpy()) if c.cache == "f32" else workloads.storage_bits
+    if c.cache == "fp4":
+        conv = lambda p: T_A._fp4_to_hnd(p, c.block_size, c.num_kv_heads, c.head_dim)
+    else:
+        conv = T_A._to_hnd
+    r_nhd = _append_raw(w, "recipe")
+    r_hnd = _append_raw(w, "recipe", k_pool=conv(raw(w.k_pool)), v_pool=conv(raw(w.v_pool)), layout="hnd")
+    assert np.array_equal(r_hnd.q_out, r_nhd.q_out)
+    assert np.array_equal(r_hnd.k_pool, conv(r_nhd.k_pool)) and np.array_equal(r_hnd.v_pool, conv(r_nhd.v_pool))
+
+
+def test_per_tensor_fp8_append_uses_the_one_scale_for_every_head():
+    w = _wl("fp8_kv", num_seqs=8, num_blocks=None)
+    one = _append_raw(w, "recipe", k_scale=np.array([0.0123], np.float32), v_scale=np.array([0.0234], np.float32))
+    each = _append_raw(w, "recipe", k_scale=np.full(8, 0.0123, np.float32), v_scale=np.full(8, 0.0234, np.float32))
+    assert np.array_equal(one.k_pool, each.k_pool) and np.array_equal(one.v_pool, each.v_pool)

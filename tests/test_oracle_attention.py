@@ -306,3 +306,71 @@ def test_fp4_cache_equals_f32_cache_of_its_decoded_values():
     p4 = A.paged_decode_partials(q, kp, vp, *args, 32, cache="fp4", **kw)
     p32 = A.paged_decode_partials(q, kf, vf, *args, 32, cache="f32", **kw)
     assert all(np.array_equal(a, b) for a, b in zip(p4, p32))
+
+
+# ------------------------------------------------------------------ cache views and scale granularity
+def _to_hnd(pool):
+    """NHD [NB, bs, Hkv, D] -> HND [NB, Hkv, bs, D], element by element."""
+    nb, bs, hkv, d = pool.shape
+    out = np.empty((nb, hkv, bs, d), dtype=pool.dtype)
+    for blk in range(nb):
+        for t in range(bs):
+            for g in range(hkv):
+                out[blk, g, t] = pool[blk, t, g]
+    return out
+
+
+def _fp4_to_hnd(pool, bs, hkv, d):
+    """FP4 blocks with NHD parts -> the same blocks with head-major parts,
+    byte by byte from the stated offsets."""
+    nc = bs * hkv * d // 2
+    out = np.empty_like(pool)
+    for blk in range(pool.shape[0]):
+        for t in range(bs):
+            for g in range(hkv):
+                src, dst = (t * hkv + g) * d // 2, (g * bs + t) * d // 2
+                out[blk, dst:dst + d // 2] = pool[blk, src:src + d // 2]
+                src, dst = nc + (t * hkv + g) * d // 32, nc + (g * bs + t) * d // 32
+                out[blk, dst:dst + d // 32] = pool[blk, src:src + d // 32]
+    return out
+
+
+@pytest.mark.parametrize("name", ["llama3_8b_gqa", "fp8_kv", "fp4_kv"])
+def test_hnd_pool_equals_nhd_pool(name):
+    """The same cache stored head-major inside each block gives bitwise the
+    same attention, split or not."""
+    w = _small(name, num_seqs=2, ctx=(1, 120))
+    c = w.cfg
+    kp, vp = _pools(w)
+    if c.cache == "fp4":
+        kh = _fp4_to_hnd(kp, c.block_size, c.num_kv_heads, c.head_dim)
+        vh = _fp4_to_hnd(vp, c.block_size, c.num_kv_heads, c.head_dim)
+    else:
+        kh, vh = _to_hnd(kp), _to_hnd(vp)
+    q = _q(w, 3)
+    ks = None if w.k_scale is None else w.k_scale.numpy()
+    vs = None if w.v_scale is None else w.v_scale.numpy()
+    kw = dict(num_kv_heads=c.num_kv_heads, block_size=c.block_size, cache=c.cache, k_scale=ks, v_scale=vs)
+    args = (w.block_tables.numpy(), w.context_lens.numpy(), c.softmax_scale)
+    a = A.paged_decode(q, kp, vp, *args, **kw)
+    b = A.paged_decode(q, kh, vh, *args, layout="hnd", **kw)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    pa = A.paged_decode_partials(q, kp, vp, *args, 32, **kw)
+    pb = A.paged_decode_partials(q, kh, vh, *args, 32, layout="hnd", **kw)
+    assert all(np.array_equal(x, y) for x, y in zip(pa, pb))
+
+
+def test_per_tensor_fp8_scale_is_every_heads_scale():
+    """A one-element scale array scales every kv head: the same as a per-head
+    array holding that value for each head."""
+    w = _small("fp8_kv", num_seqs=2, ctx=(5, 90))
+    c = w.cfg
+    kp, vp = _pools(w)
+    q = _q(w, 4)
+    args = (w.block_tables.numpy(), w.context_lens.numpy(), c.softmax_scale)
+    kw = dict(num_kv_heads=c.num_kv_heads, block_size=c.block_size, cache="fp8")
+    one = A.paged_decode(q, kp, vp, *args, k_scale=np.array([0.013], np.float32),
+                         v_scale=np.array([0.021], np.float32), **kw)
+    each = A.paged_decode(q, kp, vp, *args, k_scale=np.full(8, 0.013, np.float32),
+                          v_scale=np.full(8, 0.021, np.float32), **kw)
+    assert np.array_equal(one[0], each[0]) and np.array_equal(one[1], each[1])

@@ -176,7 +176,7 @@ def test_fp4_swapped_nibbles_are_caught(monkeypatch):
 
 
 def test_fp4_scales_before_codes_is_caught(monkeypatch):
-    def bad(pool, block_size, num_kv_heads, head_dim):
+    def bad(pool, block_size, num_kv_heads, head_dim, layout="nhd"):
         p = np.asarray(pool, dtype=np.uint8)
         ns = block_size * num_kv_heads * head_dim // 32
         return (p[:, ns:].reshape(p.shape[0], block_size, num_kv_heads, head_dim // 2),
@@ -194,3 +194,44 @@ def test_fp4_scale_per_16_elements_is_caught(monkeypatch):
         return v * s[..., idx]
     monkeypatch.setattr(codecs, "mx_fp4_dequantize", bad)
     _fails(T_A.test_fp4_cache_equals_f32_cache_of_its_decoded_values)
+
+
+def test_interleaved_with_split_half_pairs_is_caught(monkeypatch):
+    monkeypatch.setattr(rope, "rope_interleaved_f64", rope.rope_neox_f64)
+    _fails(T_R.test_interleaved_is_neox_of_the_even_odd_split)
+    _fails(T_R.test_interleaved_first_pair_and_identity)
+
+
+def test_interleaved_with_doubled_frequency_index_is_caught(monkeypatch):
+    def bad(x, pos, theta):
+        x = np.asarray(x, dtype=np.float64)
+        D = x.shape[-1]
+        ang = rope._per_row(np.asarray(pos, np.float64)[..., None] * np.power(theta, -4.0 * np.arange(D // 2) / D),
+                            x.ndim)
+        c, s = np.cos(ang), np.sin(ang)
+        y = np.empty_like(x)
+        y[..., 0::2] = x[..., 0::2] * c - x[..., 1::2] * s
+        y[..., 1::2] = x[..., 1::2] * c + x[..., 0::2] * s
+        return y
+    monkeypatch.setattr(rope, "rope_interleaved_f64", bad)
+    _fails(T_R.test_interleaved_is_neox_of_the_even_odd_split)
+
+
+def test_hnd_view_without_the_axis_swap_is_caught(monkeypatch):
+    orig = A.kv_source
+    def bad(pool, cache, block_size, num_kv_heads, head_dim, layout="nhd"):
+        if layout == "hnd" and cache != "fp4":
+            return np.asarray(pool).reshape(pool.shape[0], block_size, num_kv_heads, head_dim)
+        return orig(pool, cache, block_size, num_kv_heads, head_dim, layout)
+    monkeypatch.setattr(A, "kv_source", bad)
+    _fails(T_A.test_hnd_pool_equals_nhd_pool, "llama3_8b_gqa")
+
+
+def test_per_tensor_scale_read_as_one_is_caught(monkeypatch):
+    orig = A.gather_kv
+    def bad(pool, block_tables, b, L, g, block_size, cache, scale=None):
+        if scale is not None and np.asarray(scale).size == 1:
+            scale = np.ones(64, np.float32)  # the one-element array taken as "no scale"
+        return orig(pool, block_tables, b, L, g, block_size, cache, scale)
+    monkeypatch.setattr(A, "gather_kv", bad)
+    _fails(T_A.test_per_tensor_fp8_scale_is_every_heads_scale)

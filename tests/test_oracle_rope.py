@@ -110,3 +110,43 @@ def test_f32_recipe_exact_values_small_case():
                       np.float32(np.float32(-0.25 * c) + np.float32(1.5 * s))]], np.float32)
     got = rope.rope_neox_f32_recipe(x, 1, 1e4)
     assert np.array_equal(got, want)
+
+
+# ------------------------------------------------------------------ interleaved (GPT-J) pairs
+def test_interleaved_is_neox_of_the_even_odd_split():
+    """Moving the even elements to the first half and the odd ones to the
+    second turns adjacent pairs (2i, 2i+1) into split-half pairs (i, i+D/2)
+    with the same frequency index: both rotations must agree bit for bit."""
+    x = _x((3, 4, D), 7)
+    perm = np.concatenate([np.arange(0, D, 2), np.arange(1, D, 2)])
+    inv = np.argsort(perm)
+    pos = np.array([0, 9, 4097])
+    for theta in (1e4, 5e5):
+        a = rope.rope_interleaved_f64(x, pos, theta)
+        b = rope.rope_neox_f64(x[..., perm], pos, theta)[..., inv]
+        assert np.array_equal(a, b)
+        x32 = x.astype(np.float32)
+        a32 = rope.rope_interleaved_f32_recipe(x32, pos, theta)
+        b32 = rope.rope_neox_f32_recipe(x32[..., perm], pos, theta)[..., inv]
+        assert np.array_equal(a32, b32)
+
+
+def test_interleaved_first_pair_and_identity():
+    x = np.zeros(D)
+    x[0] = 1.0
+    for pos in (1, 7, 255):
+        y = rope.rope_interleaved_f64(x, pos, 1e6)
+        assert math.isclose(y[0], math.cos(pos), abs_tol=1e-15)
+        assert math.isclose(y[1], math.sin(pos), abs_tol=1e-15)
+        assert np.count_nonzero(y) == 2
+    z = _x((2, D))
+    assert np.array_equal(rope.rope_interleaved_f64(z, 0, 1e4), z)
+
+
+def test_interleaved_relative_position():
+    """<R(p) q, R(p') k> depends only on p - p'."""
+    q, k = _x(D, 1), _x(D, 2)
+    ref = rope.rope_interleaved_f64(q, 40, 1e4) @ rope.rope_interleaved_f64(k, 30, 1e4)
+    for p in (10, 1000, 77777):
+        v = rope.rope_interleaved_f64(q, p + 10, 1e4) @ rope.rope_interleaved_f64(k, p, 1e4)
+        assert math.isclose(v, ref, rel_tol=1e-9, abs_tol=1e-9)

@@ -67,6 +67,10 @@ class Config:
     calib_tokens: int = 4096
     ctx_list: Optional[Tuple[int, ...]] = None  # explicit per-sequence lengths (overrides ctx)
     description: str = ""
+    # contract variants (Loom's "Position and KV" row)
+    rope_style: str = "neox"        # or "interleaved" (adjacent pairs)
+    cache_layout: str = "nhd"       # or "hnd": [num_blocks][Hkv][block_size][D]
+    scale_per_tensor: bool = False  # FP8: one K and one V scale for all kv heads
 
     @property
     def group(self) -> int:
@@ -144,7 +148,9 @@ class Workload:
     """Host-side inputs.  Storage tensors hold the exact bytes the GPU sees.
 
     k_pool / v_pool: [num_blocks, block_size, Hkv, D] in the cache storage dtype
-    (FP4: uint8 [num_blocks, fp4_block_bytes]).
+    ([num_blocks, Hkv, block_size, D] for the HND layout; FP4: uint8
+    [num_blocks, fp4_block_bytes], whose bytes are drawn uniformly, so the
+    same draw serves either layout).
     qkv: [B, (Hq + 2*Hkv) * D] in the activation dtype; per row Q heads, then
     K heads, then V heads, each head_dim-contiguous.
     """
@@ -235,11 +241,14 @@ def _to_storage(x_f32: np.ndarray, dtype: str, scale: Optional[np.ndarray] = Non
 
 
 def draw_calibration_scales(cfg: Config) -> Tuple[np.ndarray, np.ndarray]:
-    """Static per-head FP8 scales: absmax / 448 of a seeded calibration draw
-    of ``calib_tokens`` x D values per KV head, separately for K and V."""
+    """Static FP8 scales: absmax / 448 of a seeded calibration draw of
+    ``calib_tokens`` x D values per KV head, separately for K and V; per
+    tensor, the absmax is taken over all heads and one scale is returned."""
     n = cfg.calib_tokens * cfg.head_dim
     x = _normal_f32(cfg.seed, STAGE_CALIB, 2 * cfg.num_kv_heads * n).reshape(2, cfg.num_kv_heads, n)
     amax = np.abs(x).max(axis=2).astype(np.float32)
+    if cfg.scale_per_tensor:
+        amax = amax.max(axis=1, keepdims=True)
     scales = (amax / np.float32(E4M3_MAX)).astype(np.float32)
     return scales[0].copy(), scales[1].copy()
 
@@ -302,6 +311,11 @@ def make_workload(cfg: Config) -> Workload:
         k_pool = _to_storage(kf, cfg.cache)
         v_pool = _to_storage(vf, cfg.cache)
     del kf, vf
+    if cfg.cache_layout == "hnd":
+        k_pool = k_pool.transpose(1, 2).contiguous()
+        v_pool = v_pool.transpose(1, 2).contiguous()
+    elif cfg.cache_layout != "nhd":
+        raise ValueError(cfg.cache_layout)
     qkv = _to_storage(qkv_f, cfg.act)
     return Workload(cfg, torch.from_numpy(ctx), torch.from_numpy(bt), k_pool, v_pool, qkv, k_scale, v_scale)
 
