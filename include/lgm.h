@@ -51,13 +51,15 @@
  *   packed QKV  [B][(Hq + 2*Hkv) * D] per row: Q heads, then K heads, then V
  *               heads, each D contiguous; rows qkv_row_stride elements apart.
  *   KV caches   NHD: [num_blocks][block_size][Hkv][D], K and V in separate
- *               pools with identical indexing and dtype.
+ *               pools with identical indexing and dtype.  With LGM_CACHE_HND
+ *               the pools are [num_blocks][Hkv][block_size][D] instead.
  *   FP4 cache blocks (LGM_FP4_E2M1): block i of a pool is the byte range
  *               [i * S, (i + 1) * S), S = block_size * Hkv * (D/2 + D/32):
  *               first the codes, NHD [block_size][Hkv][D/2] bytes (element
  *               2k in the low nibble of byte k, 2k+1 in the high nibble),
  *               then the scales, [block_size][Hkv][D/32] E8M0 bytes (scale s
- *               of a row covers its elements 32s .. 32s+31).  The scales
+ *               of a row covers its elements 32s .. 32s+31).  With
+ *               LGM_CACHE_HND both parts are head-major: [Hkv][block_size][..].  The scales
  *               travel with their block, so no scale pointer is passed.
  *   block table int32 [B][max_blocks_per_seq]: logical block -> physical.
  *   context len int32 [B]: tokens in the cache INCLUDING the new token, so
@@ -75,7 +77,7 @@
 extern "C" {
 #endif
 
-#define LGM_ABI_VERSION 2
+#define LGM_ABI_VERSION 3
 
 typedef enum lgm_status {
   LGM_OK = 0,
@@ -93,6 +95,14 @@ typedef enum lgm_status {
  * (token, kv head) row; see "FP4 cache blocks" above. */
 typedef enum lgm_dtype { LGM_F32 = 0, LGM_BF16 = 1, LGM_FP8_E4M3 = 2, LGM_FP4_E2M1 = 3 } lgm_dtype;
 
+/* Contract-variant flags ([Loom] "Position and KV": NeoX/interleaved RoPE,
+ * NHD/HND cache views, static per-tensor/per-head FP8 scales), OR-ed into
+ * the `flags` argument; 0 selects NeoX RoPE, NHD caches and per-head scales.
+ * Each call rejects bits it does not document with LGM_ERR_INVALID_ARGUMENT. */
+#define LGM_ROPE_INTERLEAVED 0x1u /* append: rotate adjacent pairs (x[2i], x[2i+1]) */
+#define LGM_CACHE_HND 0x2u        /* append and attention: caches stored head-major, see Layouts */
+#define LGM_SCALE_PER_TENSOR 0x4u /* append and attention, FP8 caches: one K and one V scale */
+
 /* Shapes shared by the calls.  num_seqs = B, num_q_heads = Hq,
  * num_kv_heads = Hkv (Hq % Hkv == 0), head_dim = D, block_size = tokens per
  * cache block, num_blocks = blocks in each pool, max_blocks_per_seq = block
@@ -108,13 +118,15 @@ typedef struct lgm_paged_dims {
 } lgm_paged_dims;
 
 /*
- * Fused NeoX RoPE + paged-KV append of the new token ([Loom] "Position and
- * KV"; [microLLM] split-half RoPE, mapped KV store).
+ * Fused NeoX (or interleaved) RoPE + paged-KV append of the new token
+ * ([Loom] "Position and KV"; [microLLM] split-half RoPE, mapped KV store).
  *
  * For each sequence b with ctx = context_lens[b] >= 1, pos = ctx - 1:
  *   every Q head and K head x of qkv row b is rotated split-half:
  *     pair i < D/2 is (x[i], x[i + D/2]), angle = pos * theta^(-2i/D),
  *     y[i] = x[i] cos - x[i+D/2] sin,  y[i+D/2] = x[i+D/2] cos + x[i] sin,
+ *   (with LGM_ROPE_INTERLEAVED: pair i is (x[2i], x[2i+1]), same angle,
+ *     y[2i] = x[2i] cos - x[2i+1] sin,  y[2i+1] = x[2i+1] cos + x[2i] sin),
  *   evaluated as: angle, cos and sin in fp64, cos and sin rounded once to
  *   fp32, then each product and each sum rounded to fp32 (no fused
  *   multiply-add);
@@ -134,11 +146,14 @@ typedef struct lgm_paged_dims {
  *
  *   qkv            [B][row] act dtype, row stride qkv_row_stride >= (Hq+2Hkv)*D
  *   q_out          [B][Hq][D] act dtype (dense); must not overlap any input
- *   k_cache,v_cache NHD pools, cache dtype; written only at the B slots
+ *   k_cache,v_cache NHD (or HND) pools, cache dtype; written only at the B slots
  *   block_tables   int32 [B][max_blocks_per_seq]
  *   context_lens   int32 [B]
- *   k_scale,v_scale fp32 [Hkv] when cache_dtype is LGM_FP8_E4M3, else NULL
+ *   k_scale,v_scale fp32 [Hkv] when cache_dtype is LGM_FP8_E4M3 ([1] with
+ *                  LGM_SCALE_PER_TENSOR), else NULL
  *   rope_theta     > 0, finite
+ *   flags          LGM_ROPE_INTERLEAVED | LGM_CACHE_HND | LGM_SCALE_PER_TENSOR
+ *                  (the last for FP8 caches only)
  * Supported: (act, cache) in {(F32, F32), (BF16, BF16), (BF16, FP8_E4M3),
  * (BF16, FP4_E2M1)}; head_dim even, 2..256 (a multiple of 32 for FP4);
  * block_size >= 1.  Append slots must be distinct
@@ -149,7 +164,8 @@ lgm_status lgm_rope_kv_append(const void* qkv, int64_t qkv_row_stride, void* q_o
                               void* v_cache, const int32_t* block_tables,
                               const int32_t* context_lens, const float* k_scale,
                               const float* v_scale, float rope_theta, lgm_paged_dims dims,
-                              lgm_dtype act_dtype, lgm_dtype cache_dtype, void* stream);
+                              lgm_dtype act_dtype, lgm_dtype cache_dtype, uint32_t flags,
+                              void* stream);
 
 /*
  * The partition size the attention call will use, or 0 for equal ranges.
@@ -214,8 +230,9 @@ size_t lgm_paged_decode_workspace_size(lgm_paged_dims dims, int32_t max_context_
  *   out_lse        optional fp32 [B][Hq] (NULL = not written)
  *   q              [B][Hq][D] act dtype, rows q_seq_stride >= Hq*D elements apart;
  *                  may be the q_out of lgm_rope_kv_append
- *   k_cache,v_cache NHD pools (cache dtype), read only
- *   k_scale,v_scale fp32 [Hkv] for LGM_FP8_E4M3 caches, else NULL
+ *   k_cache,v_cache NHD (or HND) pools (cache dtype), read only
+ *   k_scale,v_scale fp32 [Hkv] for LGM_FP8_E4M3 caches ([1] with
+ *                  LGM_SCALE_PER_TENSOR), else NULL
  *   softmax_scale  finite (normally 1/sqrt(D) rounded to fp32)
  *   partition_size 0 = library chooses; else a positive multiple of
  *                  block_size; >= max_context_len means no split
@@ -228,6 +245,8 @@ size_t lgm_paged_decode_workspace_size(lgm_paged_dims dims, int32_t max_context_
  *                  Zero-fill it again after a call on it failed to complete.
  *                  Calls sharing a workspace must not overlap in time (one
  *                  per stream).
+ *   flags          LGM_CACHE_HND | LGM_SCALE_PER_TENSOR (the latter for FP8
+ *                  caches only); LGM_ROPE_INTERLEAVED is rejected here
  * Supported: (act, cache) in {(F32, F32), (BF16, BF16), (BF16, FP8_E4M3)},
  * head_dim in {64, 128}, block_size 16, G = Hq/Hkv in 1..8; with bf16
  * activations at head_dim 128, G in 1..16 (matrix-core kernel); and
@@ -241,7 +260,7 @@ lgm_status lgm_paged_decode_attn(void* out, float* out_lse, const void* q, int64
                                  const float* k_scale, const float* v_scale, float softmax_scale,
                                  int32_t partition_size, int32_t max_context_len, void* workspace,
                                  size_t workspace_bytes, lgm_paged_dims dims, lgm_dtype act_dtype,
-                                 lgm_dtype cache_dtype, void* stream);
+                                 lgm_dtype cache_dtype, uint32_t flags, void* stream);
 
 /*
  * Log-sum-exp merge of split-K records ([mainarch] combine of split

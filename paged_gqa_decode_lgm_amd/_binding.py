@@ -19,6 +19,7 @@ HEADER = os.path.join(INCLUDE, "lgm.h")
 
 LGM_OK, LGM_ERR_INVALID_ARGUMENT, LGM_ERR_UNSUPPORTED, LGM_ERR_WORKSPACE_TOO_SMALL, LGM_ERR_HIP = range(5)
 LGM_F32, LGM_BF16, LGM_FP8_E4M3, LGM_FP4_E2M1 = 0, 1, 2, 3
+LGM_ROPE_INTERLEAVED, LGM_CACHE_HND, LGM_SCALE_PER_TENSOR = 0x1, 0x2, 0x4
 STATUS_NAMES = {0: "LGM_OK", 1: "LGM_ERR_INVALID_ARGUMENT", 2: "LGM_ERR_UNSUPPORTED",
                 3: "LGM_ERR_WORKSPACE_TOO_SMALL", 4: "LGM_ERR_HIP"}
 
@@ -50,14 +51,15 @@ def lib() -> ctypes.CDLL:
             raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m paged_gqa_decode_lgm_amd.build`")
         L = ctypes.CDLL(LIB_PATH)
         vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
-        L.lgm_rope_kv_append.argtypes = [vp, i64, vp, vp, vp, vp, vp, vp, vp, f32, lgm_paged_dims, i32, i32, vp]
+        u32 = ctypes.c_uint32
+        L.lgm_rope_kv_append.argtypes = [vp, i64, vp, vp, vp, vp, vp, vp, vp, f32, lgm_paged_dims, i32, i32, u32, vp]
         L.lgm_rope_kv_append.restype = i32
         L.lgm_paged_decode_partition_size.argtypes = [lgm_paged_dims, i32, i32, i32]
         L.lgm_paged_decode_partition_size.restype = i32
         L.lgm_paged_decode_workspace_size.argtypes = [lgm_paged_dims, i32, i32, i32]
         L.lgm_paged_decode_workspace_size.restype = sz
         L.lgm_paged_decode_attn.argtypes = [vp, vp, vp, i64, vp, vp, vp, vp, vp, vp, f32, i32, i32, vp, sz,
-                                            lgm_paged_dims, i32, i32, vp]
+                                            lgm_paged_dims, i32, i32, u32, vp]
         L.lgm_paged_decode_attn.restype = i32
         L.lgm_lse_merge.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
         L.lgm_lse_merge.restype = i32
@@ -108,10 +110,10 @@ def make_dims(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blo
 
 
 def lgm_rope_kv_append(qkv, qkv_row_stride, q_out, k_cache, v_cache, block_tables, context_lens, k_scale, v_scale,
-                       rope_theta, dims, act_dtype, cache_dtype, stream=None):
+                       rope_theta, dims, act_dtype, cache_dtype, flags=0, stream=None):
     _check(lib().lgm_rope_kv_append(_ptr(qkv), qkv_row_stride, _ptr(q_out), _ptr(k_cache), _ptr(v_cache),
                                     _ptr(block_tables), _ptr(context_lens), _ptr(k_scale), _ptr(v_scale),
-                                    rope_theta, dims, act_dtype, cache_dtype, _stream(stream)))
+                                    rope_theta, dims, act_dtype, cache_dtype, flags, _stream(stream)))
 
 
 def lgm_paged_decode_partition_size(dims, max_context_len, partition_size, cache_dtype) -> int:
@@ -131,11 +133,11 @@ def lgm_paged_decode_workspace_size(dims, max_context_len, partition_size, cache
 
 def lgm_paged_decode_attn(out, out_lse, q, q_seq_stride, k_cache, v_cache, block_tables, context_lens, k_scale,
                           v_scale, softmax_scale, partition_size, max_context_len, workspace, workspace_bytes, dims,
-                          act_dtype, cache_dtype, stream=None):
+                          act_dtype, cache_dtype, flags=0, stream=None):
     _check(lib().lgm_paged_decode_attn(_ptr(out), _ptr(out_lse), _ptr(q), q_seq_stride, _ptr(k_cache),
                                        _ptr(v_cache), _ptr(block_tables), _ptr(context_lens), _ptr(k_scale),
                                        _ptr(v_scale), softmax_scale, partition_size, max_context_len,
-                                       _ptr(workspace), workspace_bytes, dims, act_dtype, cache_dtype,
+                                       _ptr(workspace), workspace_bytes, dims, act_dtype, cache_dtype, flags,
                                        _stream(stream)))
 
 

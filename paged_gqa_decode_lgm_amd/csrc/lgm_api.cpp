@@ -94,6 +94,25 @@ lgm_status check_scales(const char* fn, lgm_dtype cache, const float* k_scale, c
   return LGM_OK;
 }
 
+// Contract-variant flags: only the bits a call documents, and the per-tensor
+// scale only for FP8 caches.
+lgm_status check_flags(const char* fn, uint32_t flags, uint32_t allowed, lgm_dtype cache) {
+  if (flags & ~allowed)
+    return fail(LGM_ERR_INVALID_ARGUMENT, fn, "flags = 0x%x: only 0x%x (%s) are defined for this call", flags,
+                allowed, allowed & LGM_ROPE_INTERLEAVED
+                             ? "LGM_ROPE_INTERLEAVED | LGM_CACHE_HND | LGM_SCALE_PER_TENSOR"
+                             : "LGM_CACHE_HND | LGM_SCALE_PER_TENSOR");
+  if ((flags & LGM_SCALE_PER_TENSOR) && cache != LGM_FP8_E4M3)
+    return fail(LGM_ERR_INVALID_ARGUMENT, fn, "flags: LGM_SCALE_PER_TENSOR needs an LGM_FP8_E4M3 cache, not %s",
+                dtype_name(cache));
+  return LGM_OK;
+}
+
+// Bytes of the k_scale / v_scale arrays a call reads.
+int64_t scale_bytes(const float* s, const lgm_paged_dims& d, uint32_t flags) {
+  return s ? ((flags & LGM_SCALE_PER_TENSOR) ? 4 : (int64_t)d.num_kv_heads * 4) : 0;
+}
+
 lgm_status check_no_alias(const char* fn, const Span* outs, int n_out, const Span* ins, int n_in) {
   for (int i = 0; i < n_out; ++i) {
     for (int j = i + 1; j < n_out; ++j)
@@ -261,7 +280,7 @@ int32_t lgm_abi_version(void) { return LGM_ABI_VERSION; }
 lgm_status lgm_rope_kv_append(const void* qkv, int64_t qkv_row_stride, void* q_out, void* k_cache, void* v_cache,
                               const int32_t* block_tables, const int32_t* context_lens, const float* k_scale,
                               const float* v_scale, float rope_theta, lgm_paged_dims dims, lgm_dtype act_dtype,
-                              lgm_dtype cache_dtype, void* stream) {
+                              lgm_dtype cache_dtype, uint32_t flags, void* stream) {
   const char* fn = "lgm_rope_kv_append";
   g_err.clear();
   lgm_status st = check_dims(fn, dims);
@@ -288,6 +307,9 @@ lgm_status lgm_rope_kv_append(const void* qkv, int64_t qkv_row_stride, void* q_o
     return fail(LGM_ERR_INVALID_ARGUMENT, fn, "qkv_row_stride = %lld must be >= (Hq + 2*Hkv) * D = %lld",
                 (long long)qkv_row_stride, (long long)row);
   if ((st = check_scales(fn, cache_dtype, k_scale, v_scale)) != LGM_OK) return st;
+  if ((st = check_flags(fn, flags, LGM_ROPE_INTERLEAVED | LGM_CACHE_HND | LGM_SCALE_PER_TENSOR, cache_dtype)) !=
+      LGM_OK)
+    return st;
   if (dims.num_seqs == 0) return LGM_OK;
   if (!qkv) return fail(LGM_ERR_INVALID_ARGUMENT, fn, "qkv is NULL");
   if (!q_out) return fail(LGM_ERR_INVALID_ARGUMENT, fn, "q_out is NULL");
@@ -304,12 +326,12 @@ lgm_status lgm_rope_kv_append(const void* qkv, int64_t qkv_row_stride, void* q_o
   const Span ins[] = {{"qkv", (uintptr_t)qkv, ((B - 1) * qkv_row_stride + row) * ea},
                       {"block_tables", (uintptr_t)block_tables, B * dims.max_blocks_per_seq * 4},
                       {"context_lens", (uintptr_t)context_lens, B * 4},
-                      {"k_scale", (uintptr_t)k_scale, k_scale ? (int64_t)dims.num_kv_heads * 4 : 0},
-                      {"v_scale", (uintptr_t)v_scale, v_scale ? (int64_t)dims.num_kv_heads * 4 : 0}};
+                      {"k_scale", (uintptr_t)k_scale, scale_bytes(k_scale, dims, flags)},
+                      {"v_scale", (uintptr_t)v_scale, scale_bytes(v_scale, dims, flags)}};
   if ((st = check_no_alias(fn, outs, 3, ins, 5)) != LGM_OK) return st;
 
   lgm::AppendArgs a{qkv, qkv_row_stride, q_out, k_cache, v_cache, block_tables, context_lens,
-                    k_scale, v_scale, rope_theta, dims};
+                    k_scale, v_scale, rope_theta, dims, flags};
   const hipError_t e = lgm::launch_rope_kv_append(a, act_dtype, cache_dtype, (hipStream_t)stream);
   if (e != hipSuccess) return fail(LGM_ERR_HIP, fn, "kernel launch failed: %s", hipGetErrorString(e));
   return LGM_OK;
@@ -340,7 +362,7 @@ lgm_status lgm_paged_decode_attn(void* out, float* out_lse, const void* q, int64
                                  const float* k_scale, const float* v_scale, float softmax_scale,
                                  int32_t partition_size, int32_t max_context_len, void* workspace,
                                  size_t workspace_bytes, lgm_paged_dims dims, lgm_dtype act_dtype,
-                                 lgm_dtype cache_dtype, void* stream) {
+                                 lgm_dtype cache_dtype, uint32_t flags, void* stream) {
   const char* fn = "lgm_paged_decode_attn";
   g_err.clear();
   lgm_status st = check_decode_common(fn, dims, max_context_len, cache_dtype);
@@ -364,6 +386,7 @@ lgm_status lgm_paged_decode_attn(void* out, float* out_lse, const void* q, int64
     return fail(LGM_ERR_INVALID_ARGUMENT, fn, "q_seq_stride = %lld must be >= num_q_heads * head_dim = %lld",
                 (long long)q_seq_stride, (long long)qrow);
   if ((st = check_scales(fn, cache_dtype, k_scale, v_scale)) != LGM_OK) return st;
+  if ((st = check_flags(fn, flags, LGM_CACHE_HND | LGM_SCALE_PER_TENSOR, cache_dtype)) != LGM_OK) return st;
   Plan pl;
   if ((st = plan_decode(fn, dims, max_context_len, partition_size, cache_dtype, pl)) != LGM_OK) return st;
   struct {
@@ -398,14 +421,15 @@ lgm_status lgm_paged_decode_attn(void* out, float* out_lse, const void* q, int64
                       {"v_cache", (uintptr_t)v_cache, cache_bytes(dims, cache_dtype)},
                       {"block_tables", (uintptr_t)block_tables, B * dims.max_blocks_per_seq * 4},
                       {"context_lens", (uintptr_t)context_lens, B * 4},
-                      {"k_scale", (uintptr_t)k_scale, k_scale ? (int64_t)dims.num_kv_heads * 4 : 0},
-                      {"v_scale", (uintptr_t)v_scale, v_scale ? (int64_t)dims.num_kv_heads * 4 : 0}};
+                      {"k_scale", (uintptr_t)k_scale, scale_bytes(k_scale, dims, flags)},
+                      {"v_scale", (uintptr_t)v_scale, scale_bytes(v_scale, dims, flags)}};
   if ((st = check_no_alias(fn, outs, 3, ins, 7)) != LGM_OK) return st;
 
   char* wsb = static_cast<char*>(workspace);
   if (pl.rows) {
     lgm::DecodeArgs a{out, out_lse, q, q_seq_stride, k_cache, v_cache, block_tables, context_lens, k_scale, v_scale,
-                      nullptr, nullptr, nullptr, softmax_scale, lgm::PartitionPlan{1, 1}, max_context_len, 0, dims};
+                      nullptr, nullptr, nullptr, softmax_scale, lgm::PartitionPlan{1, 1}, max_context_len, 0, dims,
+                      flags};
     char* w = wsb;
     lgm::RowsArgs r{};
     r.num_wg = pl.W;
@@ -427,7 +451,7 @@ lgm_status lgm_paged_decode_attn(void* out, float* out_lse, const void* q, int64
   float* part_out = pl.P > 1 ? reinterpret_cast<float*>(wsb + pl.counters_bytes) : nullptr;
   float* part_lse = pl.P > 1 ? reinterpret_cast<float*>(wsb + pl.counters_bytes + pl.part_out_bytes) : nullptr;
   lgm::DecodeArgs a{out, out_lse, q, q_seq_stride, k_cache, v_cache, block_tables, context_lens, k_scale, v_scale,
-                    part_out, part_lse, counters, softmax_scale, pl.parts, max_context_len, pl.P, dims};
+                    part_out, part_lse, counters, softmax_scale, pl.parts, max_context_len, pl.P, dims, flags};
   hipError_t e = lgm::launch_paged_decode(a, act_dtype, cache_dtype, (hipStream_t)stream);
   if (e != hipSuccess) return fail(LGM_ERR_HIP, fn, "split kernel launch failed: %s", hipGetErrorString(e));
   if (pl.P > 1) {

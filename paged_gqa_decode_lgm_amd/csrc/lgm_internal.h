@@ -26,6 +26,7 @@ struct AppendArgs {
   const float* v_scale;
   float rope_theta;
   lgm_paged_dims dims;
+  uint32_t flags;  // LGM_ROPE_INTERLEAVED | LGM_CACHE_HND | LGM_SCALE_PER_TENSOR
 };
 
 // How one context of ctx tokens is cut into split-K partitions: the first
@@ -82,7 +83,26 @@ struct DecodeArgs {
   int32_t max_context_len;
   int32_t max_partitions;
   lgm_paged_dims dims;
+  uint32_t flags;  // LGM_CACHE_HND | LGM_SCALE_PER_TENSOR
 };
+
+// Strides, in storage units, of a cache pool whose (token, kv head) rows are
+// `row` units long: NHD blocks are [block_size][Hkv][row], HND blocks
+// [Hkv][block_size][row].
+struct CacheStrides {
+  int64_t block;  // between blocks
+  int tok;        // between the rows of consecutive tokens of one head
+  int head;       // between the rows of consecutive heads of one token
+};
+__host__ __device__ inline CacheStrides cache_strides(uint32_t flags, int block_size, int num_kv_heads, int row) {
+  const int64_t block = (int64_t)block_size * num_kv_heads * row;
+  return (flags & LGM_CACHE_HND) ? CacheStrides{block, row, block_size * row}
+                                 : CacheStrides{block, num_kv_heads * row, row};
+}
+// The FP8 scale of kv head g: per head, or the one per-tensor value.
+__host__ __device__ inline float kv_scale(const float* s, uint32_t flags, int g) {
+  return s[(flags & LGM_SCALE_PER_TENSOR) ? 0 : g];
+}
 
 struct MergeArgs {
   void* out;

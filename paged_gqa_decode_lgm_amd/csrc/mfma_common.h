@@ -124,6 +124,23 @@ __device__ __forceinline__ uint32_t kv_load1(__amdgpu_buffer_rsrc_t r, int off) 
 __device__ __forceinline__ float e8m0_to_f32(uint32_t b) {
   return __uint_as_float(b == 0 ? 0x00400000u : (b == 0xFFu ? 0x7FC00000u : b << 23));
 }
+// Byte strides of one pool for the loads below: K/V rows of kRowBytes per
+// (token, kv head), NHD or HND (CacheStrides), and for FP4 the scale area
+// that follows the block's codes, laid out the same way with 4 bytes a row.
+struct KVLayout {
+  int64_t block;  // bytes per block
+  int tok;        // between consecutive tokens' rows of one head
+  int head;       // between consecutive heads' rows of one token
+  int sbase;      // FP4: first byte of the block's scale area
+  int stok, shead;  // FP4: scale-row strides, as tok / head
+};
+template <class C>
+__device__ __forceinline__ KVLayout kv_layout(uint32_t flags, int hkv) {
+  const CacheStrides c = cache_strides(flags, kBS, hkv, C::kRowBytes);
+  const CacheStrides sc = cache_strides(flags, kBS, hkv, C::kScaleRowBytes);
+  return KVLayout{c.block + sc.block, c.tok, c.head, (int)c.block, sc.tok, sc.head};
+}
+
 // Two E2M1 codes (byte SEL of w, low nibble first) times scale -> two bf16 packed in a dword.
 template <int SEL>
 __device__ __forceinline__ uint32_t fp4x2_to_bf16x2(uint32_t w, float scale) {
@@ -133,9 +150,8 @@ __device__ __forceinline__ uint32_t fp4x2_to_bf16x2(uint32_t w, float scale) {
 struct MfmaBF16 {
   static constexpr bool kFp8 = false;
   using elem_t = uint16_t;
-  // Bytes of one token row (all kv heads) and of one 16-token block.
-  __device__ static int tok_bytes(int hkv) { return hkv * kD * 2; }
-  __device__ static int64_t block_bytes(int hkv) { return (int64_t)kBS * tok_bytes(hkv); }
+  static constexpr int kRowBytes = kD * 2;  // one (token, kv head) row
+  static constexpr int kScaleRowBytes = 0;
   __device__ static int score_d(int c, int kg, int j) { return 32 * c + 8 * kg + j; }
   struct KBlock {
     uint4 k[4];  // K[n][32c + 8kg .. +8], c = 0..3
@@ -143,23 +159,22 @@ struct MfmaBF16 {
   struct VBlock {
     uint4 v[4];  // V[4kg + jj][8n .. +8], jj = 0..3
   };
-  // Byte offsets inside a block of this lane's first K / V chunk (kv head g,
-  // row stride tok_bytes = Hkv * 128 * 2).
-  __device__ static int k_lane_off(int g, int tok_bytes, int n, int kg) { return n * tok_bytes + g * 256 + 16 * kg; }
-  __device__ static int v_lane_off(int g, int tok_bytes, int n, int kg) {
-    return 4 * kg * tok_bytes + g * 256 + 16 * n;
+  // Byte offsets inside a block of this lane's first K / V chunk (kv head g).
+  __device__ static int k_lane_off(const KVLayout& L, int g, int n, int kg) { return n * L.tok + g * L.head + 16 * kg; }
+  __device__ static int v_lane_off(const KVLayout& L, int g, int n, int kg) {
+    return 4 * kg * L.tok + g * L.head + 16 * n;
   }
-  __device__ static int k_scale_off(int, int, int, int) { return 0; }
-  __device__ static int v_scale_off(int, int, int, int) { return 0; }
+  __device__ static int k_scale_off(const KVLayout&, int, int, int) { return 0; }
+  __device__ static int v_scale_off(const KVLayout&, int, int, int) { return 0; }
   template <int POL = kDefaultPolicy>
-  __device__ static void load_k(KBlock& r, __amdgpu_buffer_rsrc_t rs, int off, int, int) {
+  __device__ static void load_k(KBlock& r, __amdgpu_buffer_rsrc_t rs, int off, const KVLayout&, int) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) r.k[c] = kv_load16<POL>(rs, off + 64 * c);
   }
   template <int POL = kDefaultPolicy>
-  __device__ static void load_v(VBlock& r, __amdgpu_buffer_rsrc_t rs, int off, int tok_bytes, int) {
+  __device__ static void load_v(VBlock& r, __amdgpu_buffer_rsrc_t rs, int off, const KVLayout& L, int) {
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) r.v[jj] = kv_load16<POL>(rs, off + jj * tok_bytes);
+    for (int jj = 0; jj < 4; ++jj) r.v[jj] = kv_load16<POL>(rs, off + jj * L.tok);
   }
   // A operand of score MFMA c.
   __device__ static short8 k_operand(const KBlock& r, int c) { return __builtin_bit_cast(short8, r.k[c]); }
@@ -176,8 +191,8 @@ struct MfmaBF16 {
 struct MfmaFP8 {
   static constexpr bool kFp8 = true;
   using elem_t = uint8_t;
-  __device__ static int tok_bytes(int hkv) { return hkv * kD; }
-  __device__ static int64_t block_bytes(int hkv) { return (int64_t)kBS * tok_bytes(hkv); }
+  static constexpr int kRowBytes = kD;
+  static constexpr int kScaleRowBytes = 0;
   // Score MFMA c = 2u + h uses codes 8h .. 8h+7 of K chunk u.
   __device__ static int score_d(int c, int kg, int j) { return 64 * (c >> 1) + 16 * kg + 8 * (c & 1) + j; }
   struct KBlock {
@@ -186,21 +201,21 @@ struct MfmaFP8 {
   struct VBlock {
     uint2 v[4];  // V[4kg + jj][8n .. +8] (8 codes)
   };
-  __device__ static int k_lane_off(int g, int tok_bytes, int n, int kg) { return n * tok_bytes + g * 128 + 16 * kg; }
-  __device__ static int v_lane_off(int g, int tok_bytes, int n, int kg) {
-    return 4 * kg * tok_bytes + g * 128 + 8 * n;
+  __device__ static int k_lane_off(const KVLayout& L, int g, int n, int kg) { return n * L.tok + g * L.head + 16 * kg; }
+  __device__ static int v_lane_off(const KVLayout& L, int g, int n, int kg) {
+    return 4 * kg * L.tok + g * L.head + 8 * n;
   }
-  __device__ static int k_scale_off(int, int, int, int) { return 0; }
-  __device__ static int v_scale_off(int, int, int, int) { return 0; }
+  __device__ static int k_scale_off(const KVLayout&, int, int, int) { return 0; }
+  __device__ static int v_scale_off(const KVLayout&, int, int, int) { return 0; }
   template <int POL = kDefaultPolicy>
-  __device__ static void load_k(KBlock& r, __amdgpu_buffer_rsrc_t rs, int off, int, int) {
+  __device__ static void load_k(KBlock& r, __amdgpu_buffer_rsrc_t rs, int off, const KVLayout&, int) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) r.k[u] = kv_load16<POL>(rs, off + 64 * u);
   }
   template <int POL = kDefaultPolicy>
-  __device__ static void load_v(VBlock& r, __amdgpu_buffer_rsrc_t rs, int off, int tok_bytes, int) {
+  __device__ static void load_v(VBlock& r, __amdgpu_buffer_rsrc_t rs, int off, const KVLayout& L, int) {
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) r.v[jj] = kv_load8<POL>(rs, off + jj * tok_bytes);
+    for (int jj = 0; jj < 4; ++jj) r.v[jj] = kv_load8<POL>(rs, off + jj * L.tok);
   }
   // Score MFMA c = 2u + h uses codes 8h .. 8h+7 of K chunk u: head_dim 64u + 16kg + 8h + j.
   __device__ static short8 k_operand(const KBlock& r, int c) {
@@ -223,8 +238,8 @@ struct MfmaFP8 {
 struct MfmaFP4 {
   static constexpr bool kFp8 = false;
   using elem_t = uint8_t;
-  __device__ static int tok_bytes(int hkv) { return hkv * kD / 2; }  // code bytes of a token row
-  __device__ static int64_t block_bytes(int hkv) { return (int64_t)kBS * hkv * (kD / 2 + kD / 32); }
+  static constexpr int kRowBytes = kD / 2;        // codes of one (token, kv head) row
+  static constexpr int kScaleRowBytes = kD / 32;  // its scales
   // Lane kg holds head-dim 32kg .. 32kg+31 of its K row (one scale block);
   // score MFMA c takes eight of them.
   __device__ static int score_d(int c, int kg, int j) { return 32 * kg + 8 * c + j; }
@@ -236,28 +251,29 @@ struct MfmaFP4 {
     uint32_t v[4];  // codes of V[4kg + jj][8n .. 8n+7]
     uint32_t s[4];  // their scale bytes
   };
-  __device__ static int k_lane_off(int g, int tok_bytes, int n, int kg) { return n * tok_bytes + g * 64 + 16 * kg; }
-  __device__ static int v_lane_off(int g, int tok_bytes, int n, int kg) { return 4 * kg * tok_bytes + g * 64 + 4 * n; }
-  // Scale bytes: the scale area starts after the block's 16 code rows; the
-  // (token t, head g) row's four scales sit at (t * Hkv + g) * 4 in it
-  // (tok_bytes / 16 = Hkv * 4 bytes per token).
-  __device__ static int k_scale_off(int g, int tok_bytes, int n, int kg) {
-    return kBS * tok_bytes + n * (tok_bytes / 16) + 4 * g + kg;
+  __device__ static int k_lane_off(const KVLayout& L, int g, int n, int kg) { return n * L.tok + g * L.head + 16 * kg; }
+  __device__ static int v_lane_off(const KVLayout& L, int g, int n, int kg) {
+    return 4 * kg * L.tok + g * L.head + 4 * n;
   }
-  __device__ static int v_scale_off(int g, int tok_bytes, int n, int kg) {
-    return kBS * tok_bytes + 4 * kg * (tok_bytes / 16) + 4 * g + (n >> 2);
+  // Scale bytes: the (token t, head g) row's four scales sit at
+  // sbase + t * stok + g * shead; byte s covers head-dim 32s .. 32s+31.
+  __device__ static int k_scale_off(const KVLayout& L, int g, int n, int kg) {
+    return L.sbase + n * L.stok + g * L.shead + kg;
+  }
+  __device__ static int v_scale_off(const KVLayout& L, int g, int n, int kg) {
+    return L.sbase + 4 * kg * L.stok + g * L.shead + (n >> 2);
   }
   template <int POL = kDefaultPolicy>
-  __device__ static void load_k(KBlock& r, __amdgpu_buffer_rsrc_t rs, int off, int, int soff) {
+  __device__ static void load_k(KBlock& r, __amdgpu_buffer_rsrc_t rs, int off, const KVLayout&, int soff) {
     r.k = kv_load16<POL>(rs, off);
     r.s = kv_load1<POL>(rs, soff);
   }
   template <int POL = kDefaultPolicy>
-  __device__ static void load_v(VBlock& r, __amdgpu_buffer_rsrc_t rs, int off, int tok_bytes, int soff) {
+  __device__ static void load_v(VBlock& r, __amdgpu_buffer_rsrc_t rs, int off, const KVLayout& L, int soff) {
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) r.v[jj] = kv_load4<POL>(rs, off + jj * tok_bytes);
+    for (int jj = 0; jj < 4; ++jj) r.v[jj] = kv_load4<POL>(rs, off + jj * L.tok);
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) r.s[jj] = kv_load1<POL>(rs, soff + jj * (tok_bytes / 16));
+    for (int jj = 0; jj < 4; ++jj) r.s[jj] = kv_load1<POL>(rs, soff + jj * L.stok);
   }
   __device__ static short8 k_operand(const KBlock& r, int c) {
     const uint32_t w = c == 0 ? r.k.x : (c == 1 ? r.k.y : (c == 2 ? r.k.z : r.k.w));

@@ -119,7 +119,7 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_split_kernel(Deco
 
   // q rows of the group, pre-scaled to log2 units (FP8: K's scale folded in).
   float qscale = p.softmax_scale * kLog2e;
-  if constexpr (C::kFp8) qscale *= p.k_scale[g];
+  if constexpr (C::kFp8) qscale *= kv_scale(p.k_scale, p.flags, g);
   float q[G][VEC];
   {
     const typename A::elem_t* qp = static_cast<const typename A::elem_t*>(p.q) +
@@ -142,8 +142,8 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_split_kernel(Deco
   const int32_t* bt = p.block_tables + (int64_t)b * MB;
   const typename C::elem_t* kc = static_cast<const typename C::elem_t*>(p.k_cache);
   const typename C::elem_t* vc = static_cast<const typename C::elem_t*>(p.v_cache);
-  const int64_t tok_stride = (int64_t)Hkv * D;
-  const int64_t lane_off = (int64_t)g * D + chunk * VEC;
+  const CacheStrides cs = cache_strides(p.flags, kBS, Hkv, D);  // in elements
+  const int64_t lane_off = (int64_t)g * cs.head + chunk * VEC;
   const unsigned nblocks = (unsigned)p.dims.num_blocks;
 
   auto load_block = [&](int lb, BlockRegs<C, U>& r) {
@@ -154,7 +154,7 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_split_kernel(Deco
       const int tib = u * TPI + slot;
       const int t = lb * kBS + tib;
       r.ok[u] = blk_ok && t < end;
-      const int64_t off = ((int64_t)pb * kBS + tib) * tok_stride + lane_off;
+      const int64_t off = (int64_t)pb * cs.block + (int64_t)tib * cs.tok + lane_off;
       raw_t zk{}, zv{};
       if (r.ok[u]) {
         zk = *reinterpret_cast<const raw_t*>(kc + off);
@@ -254,7 +254,7 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_split_kernel(Deco
   __syncthreads();
 
   // Merge the waves and write either the final row or this partition's record.
-  const float vscale = C::kFp8 ? p.v_scale[g] : 1.f;
+  const float vscale = C::kFp8 ? kv_scale(p.v_scale, p.flags, g) : 1.f;
   for (int idx = threadIdx.x; idx < G * D; idx += kDecodeThreads) {
     const int h = idx / D;
     const int d = idx % D;

@@ -169,23 +169,21 @@ __device__ __forceinline__ int preload_ids(const DecodeArgs& p, const Item& it, 
 // per tile is fixed and the compiler can wait for K without waiting for V.
 template <class C>
 __device__ __forceinline__ void load_tile_k(const DecodeArgs& p, int g, int px, int py, int lane, TileRegs<C>& tr) {
-  const int tok_bytes = C::tok_bytes(p.dims.num_kv_heads);
-  const int64_t block_bytes = C::block_bytes(p.dims.num_kv_heads);
-  const int off = C::k_lane_off(g, tok_bytes, lane & 15, lane >> 4);
-  const int soff = C::k_scale_off(g, tok_bytes, lane & 15, lane >> 4);
+  const KVLayout L = kv_layout<C>(p.flags, p.dims.num_kv_heads);
+  const int off = C::k_lane_off(L, g, lane & 15, lane >> 4);
+  const int soff = C::k_scale_off(L, g, lane & 15, lane >> 4);
   const int ex = px >= 0 ? px : 0, ey = py >= 0 ? py : ex;
-  C::load_k(tr.kx, block_rsrc(p.k_cache, block_bytes, ex), off, tok_bytes, soff);
-  C::load_k(tr.ky, block_rsrc(p.k_cache, block_bytes, ey), off, tok_bytes, soff);
+  C::load_k(tr.kx, block_rsrc(p.k_cache, L.block, ex), off, L, soff);
+  C::load_k(tr.ky, block_rsrc(p.k_cache, L.block, ey), off, L, soff);
 }
 template <class C>
 __device__ __forceinline__ void load_tile_v(const DecodeArgs& p, int g, int px, int py, int lane, TileRegs<C>& tr) {
-  const int tok_bytes = C::tok_bytes(p.dims.num_kv_heads);
-  const int64_t block_bytes = C::block_bytes(p.dims.num_kv_heads);
-  const int off = C::v_lane_off(g, tok_bytes, lane & 15, lane >> 4);
-  const int soff = C::v_scale_off(g, tok_bytes, lane & 15, lane >> 4);
+  const KVLayout L = kv_layout<C>(p.flags, p.dims.num_kv_heads);
+  const int off = C::v_lane_off(L, g, lane & 15, lane >> 4);
+  const int soff = C::v_scale_off(L, g, lane & 15, lane >> 4);
   const int ex = px >= 0 ? px : 0, ey = py >= 0 ? py : ex;
-  C::load_v(tr.vx, block_rsrc(p.v_cache, block_bytes, ex), off, tok_bytes, soff);
-  C::load_v(tr.vy, block_rsrc(p.v_cache, block_bytes, ey), off, tok_bytes, soff);
+  C::load_v(tr.vx, block_rsrc(p.v_cache, L.block, ex), off, L, soff);
+  C::load_v(tr.vy, block_rsrc(p.v_cache, L.block, ey), off, L, soff);
 }
 
 // Starts an item for this wave: the query operand, the block ids of its
@@ -219,7 +217,7 @@ __device__ __forceinline__ void run_tiles(const DecodeArgs& p, const Item& it, i
                                           const short8 (&qb)[4], int ids, int px, int py, TileRegs<C>& tr,
                                           WaveState& st, int& next) {
   float sscale = p.softmax_scale * kLog2e;
-  if constexpr (C::kFp8) sscale *= p.k_scale[it.g];
+  if constexpr (C::kFp8) sscale *= kv_scale(p.k_scale, p.flags, it.g);
   const int my_tiles = wave_tiles(it, wave);
   const int claim_at = my_tiles > 2 ? my_tiles - 2 : 0;
   const bool claimer = wave == 0;
@@ -272,7 +270,7 @@ __device__ __forceinline__ void publish_state(DecodeSmem<G>& sm, int buf, const 
 template <class C, int G>
 __device__ __forceinline__ void merge_and_store(const DecodeArgs& p, const DecodeSmem<G>& sm, int buf, const Item& it,
                                                 int tid) {
-  const float vscale = C::kFp8 ? p.v_scale[it.g] : 1.f;
+  const float vscale = C::kFp8 ? kv_scale(p.v_scale, p.flags, it.g) : 1.f;
   for (int idx = tid; idx < G * kD; idx += kDecodeThreads) {
     const int h = idx / kD;
     const int d = idx % kD;

@@ -111,23 +111,21 @@ constexpr int row_policy() {
 
 template <class C>
 __device__ __forceinline__ void row_load_k(const DecodeArgs& p, int g, int px, int py, int lane, TileRegs<C>& tr) {
-  const int tok_bytes = C::tok_bytes(p.dims.num_kv_heads);
-  const int64_t block_bytes = C::block_bytes(p.dims.num_kv_heads);
-  const int off = C::k_lane_off(g, tok_bytes, lane & 15, lane >> 4);
-  const int soff = C::k_scale_off(g, tok_bytes, lane & 15, lane >> 4);
+  const KVLayout L = kv_layout<C>(p.flags, p.dims.num_kv_heads);
+  const int off = C::k_lane_off(L, g, lane & 15, lane >> 4);
+  const int soff = C::k_scale_off(L, g, lane & 15, lane >> 4);
   const int ex = px >= 0 ? px : 0, ey = py >= 0 ? py : ex;
-  C::template load_k<row_policy<C>()>(tr.kx, block_rsrc(p.k_cache, block_bytes, ex), off, tok_bytes, soff);
-  C::template load_k<row_policy<C>()>(tr.ky, block_rsrc(p.k_cache, block_bytes, ey), off, tok_bytes, soff);
+  C::template load_k<row_policy<C>()>(tr.kx, block_rsrc(p.k_cache, L.block, ex), off, L, soff);
+  C::template load_k<row_policy<C>()>(tr.ky, block_rsrc(p.k_cache, L.block, ey), off, L, soff);
 }
 template <class C>
 __device__ __forceinline__ void row_load_v(const DecodeArgs& p, int g, int px, int py, int lane, TileRegs<C>& tr) {
-  const int tok_bytes = C::tok_bytes(p.dims.num_kv_heads);
-  const int64_t block_bytes = C::block_bytes(p.dims.num_kv_heads);
-  const int off = C::v_lane_off(g, tok_bytes, lane & 15, lane >> 4);
-  const int soff = C::v_scale_off(g, tok_bytes, lane & 15, lane >> 4);
+  const KVLayout L = kv_layout<C>(p.flags, p.dims.num_kv_heads);
+  const int off = C::v_lane_off(L, g, lane & 15, lane >> 4);
+  const int soff = C::v_scale_off(L, g, lane & 15, lane >> 4);
   const int ex = px >= 0 ? px : 0, ey = py >= 0 ? py : ex;
-  C::template load_v<row_policy<C>()>(tr.vx, block_rsrc(p.v_cache, block_bytes, ex), off, tok_bytes, soff);
-  C::template load_v<row_policy<C>()>(tr.vy, block_rsrc(p.v_cache, block_bytes, ey), off, tok_bytes, soff);
+  C::template load_v<row_policy<C>()>(tr.vx, block_rsrc(p.v_cache, L.block, ex), off, L, soff);
+  C::template load_v<row_policy<C>()>(tr.vy, block_rsrc(p.v_cache, L.block, ey), off, L, soff);
 }
 
 // Writes one head's result of a segment: the final output (bf16, normalised)
@@ -140,7 +138,7 @@ __device__ __forceinline__ void write_head(const DecodeArgs& p, const RowsArgs& 
   const int n = lane & 15, kg = lane >> 4;
   const float lsum = sum4(st.lsum);
   const float lsum_e = sum4(st.lsum_e);
-  const float vscale = C::kFp8 ? p.v_scale[g] : 1.f;
+  const float vscale = C::kFp8 ? kv_scale(p.v_scale, p.flags, g) : 1.f;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int row = 4 * kg + j;
@@ -210,7 +208,7 @@ __device__ __forceinline__ void run_segment(const DecodeArgs& p, const RowsArgs&
 #pragma unroll
   for (int hh = 0; hh < HPW; ++hh) {
     sscale[hh] = p.softmax_scale * kLog2e;
-    if constexpr (C::kFp8) sscale[hh] *= p.k_scale[g0 + hh];
+    if constexpr (C::kFp8) sscale[hh] *= kv_scale(p.k_scale, p.flags, g0 + hh);
   }
 
   const int lb_end = (ctx + kBS - 1) / kBS;

@@ -11,7 +11,10 @@
 // sum rounded on its own: this translation unit is built with
 // -ffp-contract=off and the pragma below, so no multiply-add is fused.
 // Rows move as eight-element vectors whenever the pointers and the QKV row
-// stride allow it.
+// stride allow it.  Contract variants (Loom, "Position and KV" row):
+// LGM_ROPE_INTERLEAVED rotates adjacent pairs (x[2i], x[2i+1]) with the same
+// angles and the same fp32 operations; LGM_CACHE_HND stores each block
+// head-major; LGM_SCALE_PER_TENSOR uses one FP8 scale for every kv head.
 //
 // FP4 caches (mainarch README, decode-attention section: E2M1 KV with E8M0
 // block scales; OCP MX block rule, as the library header states): one thread
@@ -95,27 +98,31 @@ __device__ void fp4_append_blocks(const AppendArgs& p, const typename A::elem_t*
   const int Hkv = p.dims.num_kv_heads;
   const int BS = p.dims.block_size;
   const int nblk = D / kMxBlock;
-  const int64_t codes_bytes = (int64_t)BS * Hkv * (D / 2);
+  const bool il = p.flags & LGM_ROPE_INTERLEAVED;
+  const CacheStrides cc = cache_strides(p.flags, BS, Hkv, D / 2);         // code bytes
+  const CacheStrides cs = cache_strides(p.flags, BS, Hkv, D / kMxBlock);  // scale bytes
+  const int64_t codes_bytes = cc.block;
   for (int t = threadIdx.x; t < 2 * Hkv * nblk; t += kThreads) {
     const bool is_v = t >= Hkv * nblk;
     const int u = is_v ? t - Hkv * nblk : t;
     const int g = u / nblk;
     const int blk = u - g * nblk;
     const typename A::elem_t* row = x + (int64_t)(Hq + (is_v ? Hkv : 0) + g) * D;
-    // The block's own values and, for K, their rotation partners: elements
-    // blk*32 .. +31 and the same range shifted by D/2 (a block lies within one
-    // half, since D/2 is a multiple of 32).
+    // The block's own values and, for split-half K, their rotation partners:
+    // elements blk*32 .. +31 and the same range shifted by D/2 (a block lies
+    // within one half, since D/2 is a multiple of 32).  Interleaved pairs lie
+    // inside the block.
     const int i_first = blk * kMxBlock;
-    const int lo_first = i_first < half ? i_first : i_first - half;  // first element of the low half used
+    const int lo_first = (is_v || il) ? i_first : (i_first < half ? i_first : i_first - half);
     typename A::elem_t xs[kMxBlock], xp[kMxBlock];  // x[i0 + k] and x[i0 + D/2 + k], i0 = lo_first
     if (vec) {
       using AV = Vec8<typename A::elem_t>;
 #pragma unroll
       for (int c = 0; c < kMxBlock / 8; ++c) {
-        const AV a = *reinterpret_cast<const AV*>(row + (is_v ? i_first : lo_first) + 8 * c);
+        const AV a = *reinterpret_cast<const AV*>(row + lo_first + 8 * c);
 #pragma unroll
         for (int k = 0; k < 8; ++k) xs[8 * c + k] = a.v[k];
-        if (!is_v) {
+        if (!is_v && !il) {
           const AV b = *reinterpret_cast<const AV*>(row + lo_first + half + 8 * c);
 #pragma unroll
           for (int k = 0; k < 8; ++k) xp[8 * c + k] = b.v[k];
@@ -124,8 +131,8 @@ __device__ void fp4_append_blocks(const AppendArgs& p, const typename A::elem_t*
     } else {
 #pragma unroll
       for (int k = 0; k < kMxBlock; ++k) {
-        xs[k] = row[(is_v ? i_first : lo_first) + k];
-        if (!is_v) xp[k] = row[lo_first + half + k];
+        xs[k] = row[lo_first + k];
+        if (!is_v && !il) xp[k] = row[lo_first + half + k];
       }
     }
     float y[kMxBlock];
@@ -135,6 +142,22 @@ __device__ void fp4_append_blocks(const AppendArgs& p, const typename A::elem_t*
       float v;
       if (is_v) {
         v = A::load(&xs[k]);
+      } else if (il) {
+        // the Q path's operations for pair (2i, 2i+1), i = (i_first + k) / 2
+        const int i = (i_first + k) >> 1;
+        const float c = s_cos[i];
+        const float sn = s_sin[i];
+        const float x0 = A::load(&xs[k & ~1]);
+        const float x1 = A::load(&xs[k | 1]);
+        if ((k & 1) == 0) {
+          const float a0 = x0 * c;
+          const float b0 = x1 * sn;
+          v = a0 - b0;
+        } else {
+          const float a1 = x1 * c;
+          const float b1 = x0 * sn;
+          v = a1 + b1;
+        }
       } else {
         // the Q path's operations for pair (i0, i0 + D/2)
         const int i0 = lo_first + k;
@@ -164,14 +187,14 @@ __device__ void fp4_append_blocks(const AppendArgs& p, const typename A::elem_t*
 #pragma unroll
     for (int k = 0; k < kMxBlock; ++k) w[k / 8] |= e2m1_code(y[k] * mul) << (4 * (k % 8));
     uint8_t* base = (is_v ? vblock : kblock);
-    uint8_t* dst = base + (int64_t)(slot * Hkv + g) * (D / 2) + blk * (kMxBlock / 2);
+    uint8_t* dst = base + (int64_t)slot * cc.tok + (int64_t)g * cc.head + blk * (kMxBlock / 2);
     if ((uintptr_t)dst % 16 == 0) {
       *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
     } else {
 #pragma unroll
       for (int k = 0; k < 16; ++k) dst[k] = (uint8_t)(w[k / 4] >> (8 * (k % 4)));
     }
-    base[codes_bytes + (int64_t)(slot * Hkv + g) * nblk + blk] = (uint8_t)(X + 127);
+    base[codes_bytes + (int64_t)slot * cs.tok + (int64_t)g * cs.head + blk] = (uint8_t)(X + 127);
   }
 }
 
@@ -199,12 +222,14 @@ __global__ __launch_bounds__(kThreads) void rope_kv_append_kernel(AppendArgs p) 
   // so its latency overlaps theirs.
   bool write = false;
   int pb = 0;
-  int64_t slot_base = 0;  // element offset of (block, slot, head 0, 0)
+  const CacheStrides cs = cache_strides(p.flags, BS, Hkv, D);  // in elements
+  int64_t slot_base = 0;  // element offset of (block, slot, head 0, 0); head g adds g * cs.head
   if (active) {
     pb = p.block_tables[(int64_t)b * MB + pos / BS];
     write = (unsigned)pb < (unsigned)p.dims.num_blocks;
-    slot_base = ((int64_t)pb * BS + pos % BS) * (int64_t)Hkv * D;
+    slot_base = (int64_t)pb * cs.block + (int64_t)(pos % BS) * cs.tok;
   }
+  const bool il = p.flags & LGM_ROPE_INTERLEAVED;
   // Heads rotated by the element paths: Q and K, or only Q for FP4 caches,
   // whose K rows are rotated block by block in fp4_append_blocks.
   const int nrot_heads = Hq + (C::kFp4 ? 0 : Hkv);
@@ -231,29 +256,57 @@ __global__ __launch_bounds__(kThreads) void rope_kv_append_kernel(AppendArgs p) 
                    ((uintptr_t)p.q_out % (8 * sizeof(typename A::elem_t)) == 0) &&
                    ((uintptr_t)p.k_cache % (8 * sizeof(typename C::elem_t)) == 0) &&
                    ((uintptr_t)p.v_cache % (8 * sizeof(typename C::elem_t)) == 0);
+  // Stores rotated head hh (Q, or K head hh - Hq) element e.
+  auto store_rot = [&](int hh, int e, float y) {
+    if (hh < Hq) {
+      qo[hh * D + e] = A::store(y);
+    } else if (write) {
+      const int g = hh - Hq;
+      kc[slot_base + (int64_t)g * cs.head + e] = C::store(y, p.k_scale ? kv_scale(p.k_scale, p.flags, g) : 1.f);
+    }
+  };
   if (vec) {
     using AV = Vec8<typename A::elem_t>;
     using CV = Vec8<typename C::elem_t>;
     const int nchunk = half / 8;
-    // Rotate every Q head and every K head: (Hq + Hkv) * D/16 chunks of 8 pairs.
+    // Rotate every Q head (and K head): nrot_heads * D/16 chunks of 8 pairs,
+    // (i0 .. i0+7, i0+D/2 .. i0+D/2+7) split-half or (2i0 .. 2i0+15) interleaved.
     for (int t = threadIdx.x; t < nrot_heads * nchunk; t += kThreads) {
       const int hh = t / nchunk;
       const int i0 = 8 * (t - hh * nchunk);
-      const AV lo = *reinterpret_cast<const AV*>(x + hh * D + i0);
-      const AV hi = *reinterpret_cast<const AV*>(x + hh * D + i0 + half);
-      float y0[8], y1[8];
+      const int e_lo = il ? 2 * i0 : i0;          // first element of each 8-element vector
+      const int e_hi = il ? 2 * i0 + 8 : i0 + half;
+      const AV lo = *reinterpret_cast<const AV*>(x + hh * D + e_lo);
+      const AV hi = *reinterpret_cast<const AV*>(x + hh * D + e_hi);
+      float y0[8], y1[8];  // split-half: y[i0+k], y[i0+D/2+k]; interleaved: y[2i0+k], y[2i0+8+k]
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const float c = s_cos[i0 + k];
-        const float sn = s_sin[i0 + k];
-        const float x0 = A::load(&lo.v[k]);
-        const float x1 = A::load(&hi.v[k]);
+        // pair k: split-half (lo[k], hi[k]); interleaved (e[2k], e[2k+1]) of lo|hi
+        const int ic = i0 + k;
+        const float c = s_cos[ic];
+        const float sn = s_sin[ic];
+        float x0, x1;
+        if (il) {
+          x0 = A::load(k < 4 ? &lo.v[2 * k] : &hi.v[2 * k - 8]);
+          x1 = A::load(k < 4 ? &lo.v[2 * k + 1] : &hi.v[2 * k - 7]);
+        } else {
+          x0 = A::load(&lo.v[k]);
+          x1 = A::load(&hi.v[k]);
+        }
         const float a0 = x0 * c;
         const float b0 = x1 * sn;
-        y0[k] = a0 - b0;
+        const float r0 = a0 - b0;
         const float a1 = x1 * c;
         const float b1 = x0 * sn;
-        y1[k] = a1 + b1;
+        const float r1 = a1 + b1;
+        if (il) {
+          float* dst = k < 4 ? y0 : y1;
+          dst[(2 * k) & 7] = r0;
+          dst[(2 * k + 1) & 7] = r1;
+        } else {
+          y0[k] = r0;
+          y1[k] = r1;
+        }
       }
       if (hh < Hq) {
         AV o0, o1;
@@ -262,19 +315,20 @@ __global__ __launch_bounds__(kThreads) void rope_kv_append_kernel(AppendArgs p) 
           o0.v[k] = A::store(y0[k]);
           o1.v[k] = A::store(y1[k]);
         }
-        *reinterpret_cast<AV*>(qo + hh * D + i0) = o0;
-        *reinterpret_cast<AV*>(qo + hh * D + i0 + half) = o1;
+        *reinterpret_cast<AV*>(qo + hh * D + e_lo) = o0;
+        *reinterpret_cast<AV*>(qo + hh * D + e_hi) = o1;
       } else if (write) {
         const int g = hh - Hq;
-        const float sc = p.k_scale ? p.k_scale[g] : 1.f;
+        const float sc = p.k_scale ? kv_scale(p.k_scale, p.flags, g) : 1.f;
         CV o0, o1;
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
           o0.v[k] = C::store(y0[k], sc);
           o1.v[k] = C::store(y1[k], sc);
         }
-        *reinterpret_cast<CV*>(kc + slot_base + g * D + i0) = o0;
-        *reinterpret_cast<CV*>(kc + slot_base + g * D + i0 + half) = o1;
+        typename C::elem_t* kh = kc + slot_base + (int64_t)g * cs.head;
+        *reinterpret_cast<CV*>(kh + e_lo) = o0;
+        *reinterpret_cast<CV*>(kh + e_hi) = o1;
       }
     }
     // V heads are stored unrotated.
@@ -282,47 +336,42 @@ __global__ __launch_bounds__(kThreads) void rope_kv_append_kernel(AppendArgs p) 
       const typename A::elem_t* xv = x + (Hq + Hkv) * D;
       for (int t = threadIdx.x; t < Hkv * D / 8; t += kThreads) {
         const int g = (8 * t) / D;
-        const float sc = p.v_scale ? p.v_scale[g] : 1.f;
+        const float sc = p.v_scale ? kv_scale(p.v_scale, p.flags, g) : 1.f;
         const AV in = *reinterpret_cast<const AV*>(xv + 8 * t);
         CV o;
 #pragma unroll
         for (int k = 0; k < 8; ++k) o.v[k] = C::store(A::load(&in.v[k]), sc);
-        *reinterpret_cast<CV*>(vc + slot_base + 8 * t) = o;
+        *reinterpret_cast<CV*>(vc + slot_base + (int64_t)g * cs.head + (8 * t - g * D)) = o;
       }
     }
   } else {
-    // Rotate every Q head and every K head: (Hq + Hkv) * D/2 pairs.
+    // Rotate every Q head (and K head): nrot_heads * D/2 pairs.
     const int nrot = nrot_heads * half;
     for (int t = threadIdx.x; t < nrot; t += kThreads) {
       const int hh = t / half;
       const int i = t - hh * half;
       const float c = s_cos[i];
       const float s = s_sin[i];
-      const float x0 = A::load(x + hh * D + i);
-      const float x1 = A::load(x + hh * D + i + half);
+      const int e0 = il ? 2 * i : i;          // the pair's elements
+      const int e1 = il ? 2 * i + 1 : i + half;
+      const float x0 = A::load(x + hh * D + e0);
+      const float x1 = A::load(x + hh * D + e1);
       const float a0 = x0 * c;
       const float b0 = x1 * s;
       const float y0 = a0 - b0;
       const float a1 = x1 * c;
       const float b1 = x0 * s;
       const float y1 = a1 + b1;
-      if (hh < Hq) {
-        qo[hh * D + i] = A::store(y0);
-        qo[hh * D + i + half] = A::store(y1);
-      } else if (write) {
-        const int g = hh - Hq;
-        const float sc = p.k_scale ? p.k_scale[g] : 1.f;
-        kc[slot_base + g * D + i] = C::store(y0, sc);
-        kc[slot_base + g * D + i + half] = C::store(y1, sc);
-      }
+      store_rot(hh, e0, y0);
+      store_rot(hh, e1, y1);
     }
     // V heads are stored unrotated.
     if (write && !C::kFp4) {
       const typename A::elem_t* xv = x + (Hq + Hkv) * D;
       for (int t = threadIdx.x; t < Hkv * D; t += kThreads) {
         const int g = t / D;
-        const float sc = p.v_scale ? p.v_scale[g] : 1.f;
-        vc[slot_base + t] = C::store(A::load(xv + t), sc);
+        const float sc = p.v_scale ? kv_scale(p.v_scale, p.flags, g) : 1.f;
+        vc[slot_base + (int64_t)g * cs.head + (t - g * D)] = C::store(A::load(xv + t), sc);
       }
     }
   }

@@ -52,43 +52,66 @@ def lgm_dtype(t) -> int:
         raise TypeError(f"no lgm_dtype for {t.dtype}") from None
 
 
-def dims_for(num_seqs: int, num_q_heads: int, k_cache: torch.Tensor, block_tables: torch.Tensor) -> B.lgm_paged_dims:
-    nb, bs, hkv, d = k_cache.shape
+def dims_for(num_seqs: int, num_q_heads: int, k_cache, block_tables: torch.Tensor,
+             layout: str = "nhd") -> B.lgm_paged_dims:
+    """Dims from a cache's shape: [NB, bs, Hkv, D] (NHD), [NB, Hkv, bs, D]
+    (HND tensors) or an FP4Pool's logical shape (always (NB, bs, Hkv, D))."""
+    if layout == "hnd" and not isinstance(k_cache, FP4Pool):
+        nb, hkv, bs, d = k_cache.shape
+    else:
+        nb, bs, hkv, d = k_cache.shape
     return B.make_dims(num_seqs, num_q_heads, hkv, d, bs, nb, block_tables.shape[1])
 
 
+def variant_flags(layout: str = "nhd", rope_style: str = "neox", k_scale=None, num_kv_heads: int = 1) -> int:
+    """lgm flags for a cache layout ("nhd" / "hnd"), a RoPE style ("neox" /
+    "interleaved") and FP8 scales given as one value for all kv heads."""
+    if layout not in ("nhd", "hnd") or rope_style not in ("neox", "interleaved"):
+        raise ValueError(f"layout {layout!r} / rope_style {rope_style!r}")
+    f = B.LGM_CACHE_HND if layout == "hnd" else 0
+    f |= B.LGM_ROPE_INTERLEAVED if rope_style == "interleaved" else 0
+    if k_scale is not None and k_scale.numel() == 1 and num_kv_heads > 1:
+        f |= B.LGM_SCALE_PER_TENSOR
+    return f
+
+
 def rope_kv_append(qkv, k_cache, v_cache, block_tables, context_lens, rope_theta: float, num_q_heads: int,
-                   k_scale=None, v_scale=None, q_out=None, stream=None) -> torch.Tensor:
+                   k_scale=None, v_scale=None, q_out=None, stream=None, layout: str = "nhd",
+                   rope_style: str = "neox") -> torch.Tensor:
     """Rotate Q/K of the new token, append K/V into the paged caches; returns q_out [B, Hq, D]."""
     bsz = qkv.shape[0]
     d = k_cache.shape[3]
     if q_out is None:
         q_out = torch.empty((bsz, num_q_heads, d), dtype=qkv.dtype, device=qkv.device)
-    dims = dims_for(bsz, num_q_heads, k_cache, block_tables)
+    dims = dims_for(bsz, num_q_heads, k_cache, block_tables, layout)
+    flags = variant_flags(layout, rope_style, k_scale, dims.num_kv_heads)
     B.lgm_rope_kv_append(qkv, qkv.stride(0), q_out, k_cache, v_cache, block_tables, context_lens, k_scale, v_scale,
-                         float(rope_theta), dims, lgm_dtype(qkv), lgm_dtype(k_cache), stream)
+                         float(rope_theta), dims, lgm_dtype(qkv), lgm_dtype(k_cache), flags=flags, stream=stream)
     return q_out
 
 
-def workspace_bytes(q, k_cache, block_tables, max_context_len: int, partition_size: int = 0) -> int:
-    dims = dims_for(q.shape[0], q.shape[1], k_cache, block_tables)
+def workspace_bytes(q, k_cache, block_tables, max_context_len: int, partition_size: int = 0,
+                    layout: str = "nhd") -> int:
+    dims = dims_for(q.shape[0], q.shape[1], k_cache, block_tables, layout)
     return B.lgm_paged_decode_workspace_size(dims, max_context_len, partition_size, lgm_dtype(k_cache))
 
 
-def partition_size(q, k_cache, block_tables, max_context_len: int, partition_size: int = 0) -> int:
-    dims = dims_for(q.shape[0], q.shape[1], k_cache, block_tables)
+def partition_size(q, k_cache, block_tables, max_context_len: int, partition_size: int = 0,
+                   layout: str = "nhd") -> int:
+    dims = dims_for(q.shape[0], q.shape[1], k_cache, block_tables, layout)
     return B.lgm_paged_decode_partition_size(dims, max_context_len, partition_size, lgm_dtype(k_cache))
 
 
 def paged_decode_attn(q, k_cache, v_cache, block_tables, context_lens, max_context_len: int,
                       softmax_scale: Optional[float] = None, partition_size: int = 0, k_scale=None, v_scale=None,
                       out=None, out_lse=None, workspace=None, want_lse: bool = True,
-                      stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+                      stream=None, layout: str = "nhd") -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Decode attention of q [B, Hq, D] over the paged caches; returns (out, lse)."""
     bsz, hq, d = q.shape
     if q.stride(2) != 1 or q.stride(1) != d:
         raise ValueError("q must be [B, Hq, D] with heads dense (only the sequence stride may differ)")
-    dims = dims_for(bsz, hq, k_cache, block_tables)
+    dims = dims_for(bsz, hq, k_cache, block_tables, layout)
+    flags = variant_flags(layout, "neox", k_scale, dims.num_kv_heads)
     if softmax_scale is None:
         softmax_scale = float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32))
     if out is None:
@@ -102,7 +125,7 @@ def paged_decode_attn(q, k_cache, v_cache, block_tables, context_lens, max_conte
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     B.lgm_paged_decode_attn(out, out_lse, q, q.stride(0), k_cache, v_cache, block_tables, context_lens, k_scale,
                             v_scale, float(softmax_scale), partition_size, int(max_context_len), workspace, ws_bytes,
-                            dims, lgm_dtype(q), lgm_dtype(k_cache), stream)
+                            dims, lgm_dtype(q), lgm_dtype(k_cache), flags=flags, stream=stream)
     return out, out_lse
 
 

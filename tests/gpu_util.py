@@ -57,7 +57,7 @@ def to_device(w: W.Workload) -> Dev:
 def gpu_append(d: Dev) -> torch.Tensor:
     c = d.cfg
     return ops.rope_kv_append(d.qkv, d.k_pool, d.v_pool, d.block_tables, d.context_lens, c.rope_theta,
-                              c.num_q_heads, d.k_scale, d.v_scale)
+                              c.num_q_heads, d.k_scale, d.v_scale, layout=c.cache_layout, rope_style=c.rope_style)
 
 
 def gpu_attention(d: Dev, q: torch.Tensor, partition_size: Optional[int] = None, max_ctx: Optional[int] = None):
@@ -66,7 +66,7 @@ def gpu_attention(d: Dev, q: torch.Tensor, partition_size: Optional[int] = None,
     mc = d.max_ctx if max_ctx is None else max_ctx
     return ops.paged_decode_attn(q, d.k_pool, d.v_pool, d.block_tables, d.context_lens, mc,
                                  softmax_scale=c.softmax_scale, partition_size=ps,
-                                 k_scale=d.k_scale, v_scale=d.v_scale)
+                                 k_scale=d.k_scale, v_scale=d.v_scale, layout=c.cache_layout)
 
 
 # ------------------------------------------------------------------ host views
@@ -94,7 +94,8 @@ def oracle_append(w: W.Workload, mode: str):
         pool_raw(w, w.v_pool), num_q_heads=c.num_q_heads, num_kv_heads=c.num_kv_heads, head_dim=c.head_dim,
         block_size=c.block_size, act=c.act, cache=c.cache, rope_theta=c.rope_theta,
         k_scale=None if w.k_scale is None else w.k_scale.numpy(),
-        v_scale=None if w.v_scale is None else w.v_scale.numpy(), mode=mode)
+        v_scale=None if w.v_scale is None else w.v_scale.numpy(), mode=mode, rope_style=c.rope_style,
+        layout=c.cache_layout)
 
 
 def oracle_attention(w: W.Workload, q_raw: np.ndarray, k_pool_raw, v_pool_raw, seqs=None, ctx=None):
@@ -104,7 +105,8 @@ def oracle_attention(w: W.Workload, q_raw: np.ndarray, k_pool_raw, v_pool_raw, s
                            w.context_lens.numpy() if ctx is None else ctx, c.softmax_scale,
                            num_kv_heads=c.num_kv_heads, block_size=c.block_size, cache=c.cache,
                            k_scale=None if w.k_scale is None else w.k_scale.numpy(),
-                           v_scale=None if w.v_scale is None else w.v_scale.numpy(), seqs=seqs)
+                           v_scale=None if w.v_scale is None else w.v_scale.numpy(), seqs=seqs,
+                           layout=c.cache_layout)
 
 
 def q_from_qkv(w: W.Workload) -> torch.Tensor:

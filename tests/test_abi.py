@@ -33,7 +33,7 @@ def test_library_loads_and_exports_every_header_function():
                           "lgm_stream_read_probe"}
     for n in names:
         assert hasattr(lib, n), n
-    assert L.lgm_abi_version() == 2
+    assert L.lgm_abi_version() == 3
 
 
 # ------------------------------------------------------------------ append
@@ -64,6 +64,10 @@ APPEND_BAD = [
     (dict(cache_dtype=L.LGM_FP8_E4M3, k_scale=addr(6)), INV, "v_scale"),
     (dict(k_scale=addr(6), v_scale=addr(7)), INV, "k_scale"),
     (dict(cache_dtype=L.LGM_FP4_E2M1, k_scale=addr(6), v_scale=addr(7)), INV, "k_scale"),
+    (dict(flags=0x8), INV, "flags"),
+    (dict(flags=L.LGM_SCALE_PER_TENSOR), INV, "LGM_SCALE_PER_TENSOR"),
+    # a per-tensor scale is 4 bytes: v_scale 4 bytes after k_scale is fine, inside the per-head span is not
+    (dict(cache_dtype=L.LGM_FP8_E4M3, k_scale=addr(6), v_scale=addr(6) + 16, q_out=addr(6) + 8), INV, "q_out"),
     (dict(cache_dtype=L.LGM_FP4_E2M1, dims=dims(head_dim=48), qkv_row_stride=48 * 48), UNS, "multiple of 32"),
     (dict(cache_dtype=L.LGM_FP4_E2M1, act_dtype=L.LGM_F32), UNS, "FP4_E2M1"),
     # an FP4 pool is num_blocks * block_size * Hkv * (D/2 + D/32) bytes = 1000 * 16 * 8 * 68
@@ -122,6 +126,9 @@ ATTN_BAD = [
     (dict(cache_dtype=L.LGM_FP8_E4M3), INV, "k_scale"),
     (dict(k_scale=addr(8), v_scale=addr(9)), INV, "k_scale"),
     (dict(cache_dtype=L.LGM_FP4_E2M1, k_scale=addr(8), v_scale=addr(9)), INV, "k_scale"),
+    (dict(flags=L.LGM_ROPE_INTERLEAVED), INV, "flags"),
+    (dict(flags=0x10), INV, "flags"),
+    (dict(flags=L.LGM_SCALE_PER_TENSOR), INV, "LGM_SCALE_PER_TENSOR"),
     (dict(cache_dtype=L.LGM_FP4_E2M1, dims=dims(head_dim=64), q_seq_stride=32 * 64), UNS, "FP4_E2M1"),
     (dict(cache_dtype=L.LGM_FP4_E2M1, act_dtype=L.LGM_FP4_E2M1), UNS, "act"),
     (dict(cache_dtype=L.LGM_FP4_E2M1, workspace=addr(3) + 1000 * 16 * 8 * 68 - 256), INV, "workspace"),
@@ -285,3 +292,4 @@ def test_stream_probe_rejects_before_launch(kw, msg):
         Bn.lgm_stream_read_probe(**a)
     assert e.value.status == L.LGM_ERR_INVALID_ARGUMENT
     assert msg in e.value.message
+

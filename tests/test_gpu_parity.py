@@ -59,6 +59,12 @@ def _pair_abs(x):
     return np.concatenate([a, a], -1)
 
 
+def _pair_abs_interleaved(x):
+    """|x_2i| + |x_2i+1| for both elements of every adjacent pair."""
+    a = np.abs(x[..., 0::2]) + np.abs(x[..., 1::2])
+    return np.repeat(a, 2, axis=-1)
+
+
 def _check_bf16_rotation(g_bits, rec_bits, exact, pair_abs):
     """Rotated bf16 values: within 1 ord of the fp32-recipe mirror, and within
     one bf16 ulp plus the fp32 recipe's rounding bound (4 * 2^-24 * (|x_i| +
@@ -81,6 +87,12 @@ def _check_append(w, d, q_gpu, rec, ex, seqs=None):
     gv = pool_raw(w, _host_pool(d.v_pool))
     k0, v0 = pool_raw(w, w.k_pool), pool_raw(w, w.v_pool)
     slots = {s for s in rec.slots if s is not None}
+    if c.cache != "fp4" and c.cache_layout == "hnd":
+        # compare through [NB, bs, Hkv, D] views of the head-major pools
+        sw = lambda a: np.swapaxes(a, 1, 2)
+        gk, gv, k0, v0 = sw(gk), sw(gv), sw(k0), sw(v0)
+        rec = dataclasses.replace(rec, k_pool=sw(rec.k_pool), v_pool=sw(rec.v_pool))
+        ex = dataclasses.replace(ex, k_pool=sw(ex.k_pool), v_pool=sw(ex.v_pool))
     if c.cache == "fp4":
         # every byte of both pools: the MX codes and scale bytes of the recipe
         # at the target slots, everything else unchanged
@@ -98,13 +110,13 @@ def _check_append(w, d, q_gpu, rec, ex, seqs=None):
         Hq, Hkv, D = c.num_q_heads, c.num_kv_heads, c.head_dim
         xq = x[:, : Hq * D].reshape(-1, Hq, D)
         xk = x[:, Hq * D:(Hq + Hkv) * D].reshape(-1, Hkv, D)
+    pair_abs = _pair_abs if c.rope_style == "neox" else _pair_abs_interleaved
     for b in seqs:
         if c.act == "bf16":
-            _check_bf16_rotation(gq[b], rec.q_out[b], ex.q_rot[b], _pair_abs(xq[b]))
+            _check_bf16_rotation(gq[b], rec.q_out[b], ex.q_rot[b], pair_abs(xq[b]))
         else:
             x = w.qkv.numpy()[b, : c.num_q_heads * c.head_dim].astype(np.float64).reshape(c.num_q_heads, -1)
-            h = c.head_dim // 2
-            bound = 4 * 2.0 ** -24 * np.concatenate([np.abs(x[:, :h]) + np.abs(x[:, h:])] * 2, -1)
+            bound = 4 * 2.0 ** -24 * pair_abs(x)
             assert (np.abs(gq[b].astype(np.float64) - ex.q_rot[b]) <= bound).all()
         if rec.slots[b] is None or c.cache == "fp4":
             continue
@@ -113,7 +125,7 @@ def _check_append(w, d, q_gpu, rec, ex, seqs=None):
             assert np.array_equal(gk[pb, off], rec.k_pool[pb, off]), f"K bytes, seq {b}"
             assert np.array_equal(gv[pb, off], rec.v_pool[pb, off]), f"V bytes, seq {b}"
         elif c.cache == "bf16":
-            _check_bf16_rotation(gk[pb, off], rec.k_pool[pb, off], ex.k_rot[b], _pair_abs(xk[b]))
+            _check_bf16_rotation(gk[pb, off], rec.k_pool[pb, off], ex.k_rot[b], pair_abs(xk[b]))
             assert np.abs(bf16_ord(gv[pb, off]) - bf16_ord(ex.v_pool[pb, off])).max() <= 1
         else:
             assert np.abs(gk[pb, off] - ex.k_pool[pb, off]).max() <= 4 * 2.0 ** -24 * 8
@@ -576,3 +588,31 @@ def test_append_small_and_odd_head_dims(D, act, cache):
     q = gpu_append(d)
     torch.cuda.synchronize()
     _check_append(w, d, q, oracle_append(w, "recipe"), oracle_append(w, "exact"))
+
+
+# ------------------------------------------------------------------ contract variants
+VARIANTS = [
+    # (cache, layout, rope_style, per_tensor, partition_size, hkv, G)
+    ("bf16", "hnd", "neox", False, 0, 8, 4),          # whole-row plan, head-major blocks
+    ("bf16", "hnd", "interleaved", False, 64, 2, 6),  # work-queue plan
+    ("bf16", "nhd", "interleaved", False, 0, 4, 4),
+    ("fp8", "hnd", "neox", True, 0, 8, 4),
+    ("fp8", "nhd", "interleaved", True, 64, 2, 5),
+    ("fp8", "hnd", "interleaved", False, 32, 4, 1),   # MHA sibling (G = 1)
+    ("fp4", "hnd", "neox", False, 0, 8, 4),           # eight-wave FP4 row plan
+    ("fp4", "hnd", "interleaved", False, 64, 2, 4),
+    ("f32", "hnd", "interleaved", False, 64, 1, 4),   # vector-ALU plan, D = 64
+]
+
+
+@pytest.mark.parametrize("cache,layout,rope_style,per_tensor,ps,hkv,G", VARIANTS)
+def test_contract_variants(cache, layout, rope_style, per_tensor, ps, hkv, G):
+    """Interleaved RoPE, head-major (HND) blocks and per-tensor FP8 scales,
+    append then attention, over the plans and cache dtypes, ragged contexts."""
+    D = 64 if cache == "f32" else 128
+    cfg = W.Config(f"variant_{cache}_{layout}_{rope_style}_{'pt' if per_tensor else 'ph'}", seed=31,
+                   num_seqs=len(EDGE_CTX), num_q_heads=hkv * G, num_kv_heads=hkv, head_dim=D, block_size=16,
+                   act="f32" if cache == "f32" else "bf16", cache=cache, ctx=0, rope_theta=1e4, partition_size=ps,
+                   append=True, ctx_list=EDGE_CTX, rope_style=rope_style, cache_layout=layout,
+                   scale_per_tensor=per_tensor)
+    _run_and_check(cfg)
