@@ -338,7 +338,9 @@ def main() -> int:
                       "attention_cold_avg": round(statistics.mean(cold_ms), 5) if cold_ms else None},
         "roofline": {"bound": "hbm", "kernel": "lgm_paged_decode_attn (" + (
                      "whole-row decode over equal tile ranges + LSE merge" if ps == 0 else
-                     "split-K partition decode + LSE merge") + ", one call: two launches)",
+                     f"split-K decode in {ps}-token partitions + LSE merge; whole-row kernel over equal runs of "
+                     "whole partitions when contexts are long, else the work-queue kernel") +
+                     ", one call: two launches)",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
     }

@@ -184,7 +184,8 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // counters (matrix-core shapes, one 256-byte slot), then the partial outputs
 // and LSEs (none when every sequence fits one partition).
 struct Plan {
-  bool rows;  // whole-row kernel over equal tile ranges (partition_size 0, Hkv % 4 == 0)
+  bool rows;        // whole-row kernel (Hkv % 4 == 0): equal tile ranges (partition_size 0) ...
+  bool rows_parts;  // ... or equal runs of whole partitions (an explicit partition_size of whole tiles)
   lgm::PartitionPlan parts;
   int32_t ps, P;
   size_t counters_bytes, part_out_bytes, part_lse_bytes;
@@ -202,6 +203,19 @@ struct Plan {
 constexpr int64_t kRowsWorkgroups = LGM_ROWS_WORKGROUPS;
 constexpr int64_t kRowsMinTiles = 8;
 constexpr int64_t kRowsTile = 32;
+// Whole-row partition plan: explicit partition sizes of at least this many
+// tokens (and whole 32-token tiles), when the longest context holds at least
+// kRowsMinPartitions of them and the batch at least one unit per range.  The
+// ranges hold whole partitions in equal numbers, which balances long
+// contexts; with only a few partitions per range, ragged contexts leave the
+// ranges unequal by up to a partition, and the work-queue kernel is faster
+// (measured: 131072-token contexts, partitions of 512: 386 vs 406 us; 64
+// contexts of 512..8192 tokens, partitions of 512: 263 vs 239 us).
+#ifndef LGM_ROWS_MIN_PARTITION
+#define LGM_ROWS_MIN_PARTITION 256
+#endif
+constexpr int32_t kRowsMinPartition = LGM_ROWS_MIN_PARTITION;
+constexpr int32_t kRowsMinPartitions = 64;
 
 lgm_status plan_decode(const char* fn, const lgm_paged_dims& d, int32_t max_ctx, int32_t ps_arg, lgm_dtype cache,
                        Plan& pl) {
@@ -232,6 +246,28 @@ lgm_status plan_decode(const char* fn, const lgm_paged_dims& d, int32_t max_ctx,
   }
   pl.ps = resolve_partition(fn, d, max_ctx, ps_arg, persistent);
   if (pl.ps < 0) return LGM_ERR_INVALID_ARGUMENT;
+  const int32_t most_parts = (int32_t)(((int64_t)max_ctx + pl.ps - 1) / pl.ps);
+  const int64_t est_units = (int64_t)d.num_seqs * (d.num_kv_heads / (d.num_kv_heads % 8 == 0 ? 8 : 4)) * most_parts;
+  if (ps_arg > 0 && pl.ps >= kRowsMinPartition && pl.ps % kRowsTile == 0 && most_parts >= kRowsMinPartitions &&
+      est_units >= kRowsWorkgroups &&
+      lgm::decode_rows_supported(act, cache, d.head_dim, d.num_kv_heads, G, d.block_size)) {
+    // Whole-row kernel over equal runs of whole partitions, plain
+    // ceil(L / ps) partitions (the ranges already balance the work).
+    pl.rows = pl.rows_parts = true;
+    pl.HG = d.num_kv_heads % 8 == 0 ? 8 : 4;
+    pl.parts = lgm::PartitionPlan{pl.ps, pl.ps};
+    pl.P = pl.parts.max_count(max_ctx);
+    const int64_t units = (int64_t)d.num_seqs * (d.num_kv_heads / pl.HG) * pl.P;
+    if (units > (int64_t)INT32_MAX || (int64_t)d.num_seqs * d.num_q_heads > (int64_t)INT32_MAX - 1024)
+      return fail(LGM_ERR_UNSUPPORTED, fn, "num_seqs * head groups * partitions = %lld: too many", (long long)units);
+    pl.W = (int32_t)(units < 1 ? 1 : (units > kRowsWorkgroups ? kRowsWorkgroups : units));
+    if (pl.P > 1) {
+      pl.part_out_bytes = align256((size_t)d.num_seqs * d.num_q_heads * pl.P * d.head_dim * sizeof(float));
+      pl.part_lse_bytes = align256((size_t)d.num_seqs * d.num_q_heads * pl.P * sizeof(float));
+    }
+    pl.total = pl.part_out_bytes + pl.part_lse_bytes;
+    return LGM_OK;
+  }
   // When contexts are split, the tokens past a context's last full partition
   // go to partitions of half the size, which the kernels take last: the work
   // drains on short items instead of ending on long ones.
@@ -344,7 +380,7 @@ int32_t lgm_paged_decode_partition_size(lgm_paged_dims dims, int32_t max_context
   if (check_decode_common(fn, dims, max_context_len, cache_dtype) != LGM_OK) return -1;
   Plan pl;
   if (plan_decode(fn, dims, max_context_len, partition_size, cache_dtype, pl) != LGM_OK) return -1;
-  return pl.rows ? 0 : pl.ps;
+  return pl.rows && !pl.rows_parts ? 0 : pl.ps;
 }
 
 size_t lgm_paged_decode_workspace_size(lgm_paged_dims dims, int32_t max_context_len, int32_t partition_size,
@@ -426,6 +462,25 @@ lgm_status lgm_paged_decode_attn(void* out, float* out_lse, const void* q, int64
   if ((st = check_no_alias(fn, outs, 3, ins, 7)) != LGM_OK) return st;
 
   char* wsb = static_cast<char*>(workspace);
+  if (pl.rows_parts) {
+    float* part_out = pl.P > 1 ? reinterpret_cast<float*>(wsb) : nullptr;
+    float* part_lse = pl.P > 1 ? reinterpret_cast<float*>(wsb + pl.part_out_bytes) : nullptr;
+    lgm::DecodeArgs a{out, out_lse, q, q_seq_stride, k_cache, v_cache, block_tables, context_lens, k_scale, v_scale,
+                      part_out, part_lse, nullptr, softmax_scale, pl.parts, max_context_len, pl.P, dims, flags};
+    lgm::RowsArgs r{};
+    r.num_wg = pl.W;
+    r.head_group = pl.HG;
+    r.part_tiles = pl.ps / (int32_t)kRowsTile;
+    hipError_t e = lgm::launch_paged_decode_rows(a, r, cache_dtype, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(LGM_ERR_HIP, fn, "row kernel launch failed: %s", hipGetErrorString(e));
+    if (pl.P > 1) {
+      lgm::MergeArgs m{out, out_lse, part_out, part_lse, nullptr, context_lens, pl.parts, max_context_len,
+                       dims.num_seqs, dims.num_q_heads, dims.head_dim, pl.P, 1};
+      e = lgm::launch_lse_merge(m, act_dtype, (hipStream_t)stream);
+      if (e != hipSuccess) return fail(LGM_ERR_HIP, fn, "merge kernel launch failed: %s", hipGetErrorString(e));
+    }
+    return LGM_OK;
+  }
   if (pl.rows) {
     lgm::DecodeArgs a{out, out_lse, q, q_seq_stride, k_cache, v_cache, block_tables, context_lens, k_scale, v_scale,
                       nullptr, nullptr, nullptr, softmax_scale, lgm::PartitionPlan{1, 1}, max_context_len, 0, dims,

@@ -142,6 +142,10 @@ struct RowsArgs {
   int32_t* first_stream;  // [W] stream each range starts in, -1 for an empty range
   int32_t* wg_first;      // [B * Hkv / HG] workgroup holding the stream's first tile
   int32_t* wg_last;       // [B * Hkv / HG] workgroup holding its last tile
+  // > 0: the ranges are cut into split-K partitions of this many 32-token
+  // tiles instead (whole partitions per workgroup); each partition's record
+  // goes to DecodeArgs::part_out / part_lse and lse_merge combines them.
+  int32_t part_tiles;
 };
 hipError_t launch_paged_decode_rows(const DecodeArgs& a, const RowsArgs& r, lgm_dtype cache, hipStream_t s);
 bool decode_rows_supported(lgm_dtype act, lgm_dtype cache, int head_dim, int num_kv_heads, int group,

@@ -3,12 +3,14 @@
 // than by one workgroup grinding through them; Loom Kernels README, row
 // "Attention": local split-K/LSE merge).
 //
-// One workgroup per (sequence, head).  The partition LSEs are reduced to
-// their maximum M and to S = sum exp(lse_p - M) with fixed-shape tree
-// reductions in LDS; the partial rows are then read with 16-byte loads,
-// PG partitions at a time (D/4 lanes per row), weighted by exp(lse_p - M)
-// and summed, and the PG partial sums are added in a fixed order.  The
-// result is bitwise reproducible.
+// One workgroup per (sequence, head) or, when there are few rows (long
+// contexts, many partitions each), per (sequence, head, 32-element slice of
+// the head dim), so that a row's partitions are read by D/32 workgroups side
+// by side.  Each reduces the partition LSEs to their maximum M and to
+// S = sum exp(lse_p - M) with fixed-shape tree reductions in LDS; its slice
+// of the partial rows is then read with 16-byte loads, 256 / (SL/4) records
+// at a time, weighted by exp(lse_p - M) and summed, and the partial sums are
+// added in a fixed order.  The result is bitwise reproducible.
 #include "device_num.h"
 #include "lgm_internal.h"
 
@@ -43,15 +45,19 @@ __device__ float block_reduce(float x, float* red) {
   return r;
 }
 
-template <class O, int D>
+constexpr int kNarrowSlice = 32;     // head-dim elements per workgroup when rows are few
+constexpr int64_t kFewRows = 1024;   // below this many (sequence, head) rows, slice the head dim
+
+template <class O, int D, int SL>
 __global__ __launch_bounds__(kThreads) void lse_merge_kernel(MergeArgs p) {
-  constexpr int TD = D / 4;          // lanes per partial row (float4 each)
-  constexpr int PG = kThreads / TD;  // rows in flight per pass
+  constexpr int TD = SL / 4;         // lanes per record slice (float4 each)
+  constexpr int PG = kThreads / TD;  // records in flight per pass
   __shared__ float red[kThreads];
-  __shared__ float s_acc[PG][D];
+  __shared__ float s_acc[PG][SL];
 
   const int h = blockIdx.x;
   const int b = blockIdx.y;
+  const int z = blockIdx.z;  // which slice of the head dim
   const int P = p.max_partitions;
   int n;
   if (p.num_partitions) {
@@ -69,7 +75,7 @@ __global__ __launch_bounds__(kThreads) void lse_merge_kernel(MergeArgs p) {
 
   const int64_t row = (int64_t)b * p.num_heads + h;
   const float* lse = p.part_lse + row * P;
-  const float* po = p.part_out + row * P * D;
+  const float* po = p.part_out + row * P * D + z * SL;
 
   float mx = -INFINITY;
   for (int i = threadIdx.x; i < n; i += kThreads) mx = fmaxf(mx, lse[i]);
@@ -82,6 +88,7 @@ __global__ __launch_bounds__(kThreads) void lse_merge_kernel(MergeArgs p) {
   const int td = threadIdx.x % TD;
   const int pg = threadIdx.x / TD;
   float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 4
   for (int i = pg; i < n; i += PG) {
     const float w = expf(lse[i] - ms);
     const float4 v = reinterpret_cast<const float4*>(po + (int64_t)i * D)[td];
@@ -95,23 +102,31 @@ __global__ __launch_bounds__(kThreads) void lse_merge_kernel(MergeArgs p) {
   s_acc[pg][td * 4 + 2] = a.z;
   s_acc[pg][td * 4 + 3] = a.w;
   __syncthreads();
-  for (int d = threadIdx.x; d < D; d += kThreads) {
+  for (int d = threadIdx.x; d < SL; d += kThreads) {
     float o = 0.f;
 #pragma unroll
     for (int k = 0; k < PG; ++k) o += s_acc[k][d];
     o = S > 0.f ? o / S : 0.f;
-    static_cast<typename O::elem_t*>(p.out)[row * D + d] = O::from_f32(o);
+    static_cast<typename O::elem_t*>(p.out)[row * D + z * SL + d] = O::from_f32(o);
   }
-  if (threadIdx.x == 0 && p.out_lse) p.out_lse[row] = S > 0.f ? M + logf(S) : -INFINITY;
+  if (z == 0 && threadIdx.x == 0 && p.out_lse) p.out_lse[row] = S > 0.f ? M + logf(S) : -INFINITY;
+}
+
+template <class O, int D>
+void launch_dim(const MergeArgs& a, hipStream_t s) {
+  if ((int64_t)a.num_seqs * a.num_heads < kFewRows)
+    hipLaunchKernelGGL((lse_merge_kernel<O, D, kNarrowSlice>), dim3(a.num_heads, a.num_seqs, D / kNarrowSlice),
+                       dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((lse_merge_kernel<O, D, D>), dim3(a.num_heads, a.num_seqs, 1), dim3(kThreads), 0, s, a);
 }
 
 template <class O>
 hipError_t dispatch(const MergeArgs& a, hipStream_t s) {
-  const dim3 grid(a.num_heads, a.num_seqs);
   if (a.head_dim == 64)
-    hipLaunchKernelGGL((lse_merge_kernel<O, 64>), grid, dim3(kThreads), 0, s, a);
+    launch_dim<O, 64>(a, s);
   else if (a.head_dim == 128)
-    hipLaunchKernelGGL((lse_merge_kernel<O, 128>), grid, dim3(kThreads), 0, s, a);
+    launch_dim<O, 128>(a, s);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

@@ -49,10 +49,11 @@ __device__ __forceinline__ int clamped_ctx(const DecodeArgs& p, int b) {
 }
 
 // Fills sm.pre for sequences b0 .. b0 + kChunk - 1 (nhg streams of
-// ceil(ctx / 32) tiles per sequence) and returns the chunk's tile total.
+// ceil(ctx / unit) work units per sequence: 32-token tiles, or partitions,
+// where an empty context still counts one) and returns the chunk's total.
 // Called by every thread of the NT-thread workgroup (it synchronises).
 template <int NT>
-__device__ int scan_chunk(const DecodeArgs& p, RowsSmem& sm, int b0, int nhg) {
+__device__ int scan_chunk(const DecodeArgs& p, RowsSmem& sm, int b0, int nhg, int unit, int min_units) {
   constexpr int SPT = kChunk / NT;  // sequences per thread
   static_assert(SPT * NT == kChunk && NT / kWaveSize <= kMaxRowWaves, "scan layout");
   const int tid = threadIdx.x, lane = tid & (kWaveSize - 1), wave = tid / kWaveSize;
@@ -60,7 +61,7 @@ __device__ int scan_chunk(const DecodeArgs& p, RowsSmem& sm, int b0, int nhg) {
 #pragma unroll
   for (int k = 0; k < SPT; ++k) {
     const int b = b0 + SPT * tid + k;
-    t[k] = b < p.dims.num_seqs ? (clamped_ctx(p, b) + kTile - 1) / kTile * nhg : 0;
+    t[k] = b < p.dims.num_seqs ? max((clamped_ctx(p, b) + unit - 1) / unit, min_units) * nhg : 0;
     s += t[k];
   }
   int incl = s;
@@ -157,6 +158,15 @@ __device__ __forceinline__ void write_head(const DecodeArgs& p, const RowsArgs& 
                  ((uint32_t)f32_to_bf16_rne(st.acc[2 * i + 1][j] * inv) << 16);
         *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.out) + orow * kD + 8 * n) = make_uint4(w[0], w[1], w[2], w[3]);
         if (n == 0 && p.out_lse) p.out_lse[orow] = lse;
+      } else if (r.part_tiles > 0) {
+        // split-K record of partition `rec`: [B][Hq][P][D] and [B][Hq][P]
+        const int64_t prow = orow * p.max_partitions + rec;
+        float* dst = p.part_out + prow * kD + 8 * n;
+        *reinterpret_cast<float4*>(dst) =
+            make_float4(st.acc[0][j] * inv, st.acc[1][j] * inv, st.acc[2][j] * inv, st.acc[3][j] * inv);
+        *reinterpret_cast<float4*>(dst + 4) =
+            make_float4(st.acc[4][j] * inv, st.acc[5][j] * inv, st.acc[6][j] * inv, st.acc[7][j] * inv);
+        if (n == 0) p.part_lse[prow] = lse;
       } else {
         const int hrow = (g % r.head_group) * G + row;  // row inside the head group
         float* dst = r.rec_out + ((int64_t)rec * r.head_group * G + hrow) * kD + 8 * n;
@@ -268,11 +278,14 @@ __device__ __forceinline__ void run_segment(const DecodeArgs& p, const RowsArgs&
   for (int hh = 0; hh < HPW; ++hh) write_head<C, G>(p, r, st[hh], b, g0 + hh, whole, rec, lane);
 }
 
-// One workgroup per equal range of the flattened tile list.  Metadata for the
-// merge: first_stream[w] = the stream the range starts in (-1 if empty),
-// wg_first[u] / wg_last[u] = the workgroups holding stream u's first and
-// last tiles.  Record slot 2w holds the range's first stream when split,
-// slot 2w + 1 its last one (when that is another stream).
+// One workgroup per equal range of the flattened list of work units: the
+// 32-token tiles of all streams, or (partition mode) their split-K
+// partitions, so that a range holds whole partitions.  Metadata for the
+// range merge: first_stream[w] = the stream the range starts in (-1 if
+// empty), wg_first[u] / wg_last[u] = the workgroups holding stream u's first
+// and last tiles.  Record slot 2w holds the range's first stream when split,
+// slot 2w + 1 its last one (when that is another stream).  In partition mode
+// every partition of a split context writes its own record, at its index.
 template <class C, int G, int HPW, int NT>
 __global__ __launch_bounds__(NT, 1) void paged_decode_rows_kernel(DecodeArgs p, RowsArgs r) {
   __shared__ RowsSmem sm;
@@ -283,23 +296,27 @@ __global__ __launch_bounds__(NT, 1) void paged_decode_rows_kernel(DecodeArgs p, 
   const int nhg = p.dims.num_kv_heads / HG;
   const int W = gridDim.x;
   const int wg = blockIdx.x;
+  const bool parts = r.part_tiles > 0;
+  const int upt = parts ? r.part_tiles : 1;   // tiles per unit
+  const int unit = kTile * upt;               // tokens per unit
+  const int min_units = parts ? 1 : 0;        // an empty context still writes out = 0, lse = -inf
 
-  int total = scan_chunk<NT>(p, sm, 0, nhg);
-  for (int c0 = kChunk; c0 < B; c0 += kChunk) total += scan_chunk<NT>(p, sm, c0, nhg);
+  int total = scan_chunk<NT>(p, sm, 0, nhg, unit, min_units);
+  for (int c0 = kChunk; c0 < B; c0 += kChunk) total += scan_chunk<NT>(p, sm, c0, nhg, unit, min_units);
   const int t_lo = (int)((int64_t)wg * total / W);
   const int t_hi = (int)((int64_t)(wg + 1) * total / W);
   int b0 = 0, base = 0;
-  if (B > kChunk) scan_chunk<NT>(p, sm, 0, nhg);  // back to the first chunk
+  if (B > kChunk) scan_chunk<NT>(p, sm, 0, nhg, unit, min_units);  // back to the first chunk
 
   int pos = t_lo;
   bool first = true;
-  if (threadIdx.x == 0 && t_lo >= t_hi) r.first_stream[wg] = -1;
+  if (!parts && threadIdx.x == 0 && t_lo >= t_hi) r.first_stream[wg] = -1;
   while (pos < t_hi) {
     int rel = pos - base;
     while (rel >= __builtin_amdgcn_readfirstlane(sm.pre[kChunk])) {  // uniform: every thread moves on together
       base += __builtin_amdgcn_readfirstlane(sm.pre[kChunk]);
       b0 += kChunk;
-      scan_chunk<NT>(p, sm, b0, nhg);
+      scan_chunk<NT>(p, sm, b0, nhg, unit, min_units);
       rel = pos - base;
     }
     int lo = 0, hi = kChunk;  // sm.pre[lo] <= rel < sm.pre[hi]
@@ -310,20 +327,24 @@ __global__ __launch_bounds__(NT, 1) void paged_decode_rows_kernel(DecodeArgs p, 
     }
     const int b = b0 + lo;
     const int ctx = __builtin_amdgcn_readfirstlane(clamped_ctx(p, b));
-    const int ntb = (ctx + kTile - 1) / kTile;
+    const int ntb = (ctx + kTile - 1) / kTile;                      // tiles of the stream
+    const int ntu = max((ctx + unit - 1) / unit, min_units);        // units of the stream
     const int off = rel - __builtin_amdgcn_readfirstlane(sm.pre[lo]);
-    const int hg = off / ntb;
-    const int lt = off - hg * ntb;
-    const int et = min(ntb, lt + (t_hi - pos));
+    const int hg = off / ntu;
+    const int lu = off - hg * ntu;
+    const int eu = parts ? lu + 1 : min(ntu, lu + (t_hi - pos));
+    const int lt = lu * upt;
+    const int et = min(ntb, eu * upt);
     const int u = b * nhg + hg;
-    const bool whole = lt == 0 && et == ntb;
-    if (threadIdx.x == 0) {
+    const bool whole = parts ? ntu == 1 : (lu == 0 && eu == ntu);
+    if (!parts && threadIdx.x == 0) {
       if (first) r.first_stream[wg] = u;
       if (lt == 0) r.wg_first[u] = wg;
       if (et == ntb) r.wg_last[u] = wg;
     }
-    run_segment<C, G, HPW>(p, r, b, ctx, lt, et, hg * HG + wave * HPW, whole, 2 * wg + (first ? 0 : 1), lane);
-    pos += et - lt;
+    run_segment<C, G, HPW>(p, r, b, ctx, lt, et, hg * HG + wave * HPW, whole,
+                           parts ? lu : 2 * wg + (first ? 0 : 1), lane);
+    pos += eu - lu;
     first = false;
   }
 }
@@ -460,7 +481,7 @@ hipError_t launch_group(const DecodeArgs& a, const RowsArgs& r, hipStream_t s) {
     hipLaunchKernelGGL((paged_decode_rows_kernel<C, G, 1, kDecodeThreads>), dim3(r.num_wg), dim3(kDecodeThreads), 0,
                        s, a, r);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || r.part_tiles > 0) return e;  // partition records are merged by lse_merge
   const int merge_rows = a.dims.num_seqs * a.dims.num_q_heads;
   hipLaunchKernelGGL(rows_merge_kernel, dim3((merge_rows + kMergeRows - 1) / kMergeRows), dim3(kMergeThreads), 0, s, a,
                      r);

@@ -186,14 +186,28 @@ def partitions_brute_force(max_ctx, ps, tps):
 
 def test_workspace_size_formula():
     al = lambda x: (x + 255) // 256 * 256
-    d = dims()                                     # matrix-core shape: 256 bytes of work counters first
+    # whole-row partition plan: Hkv % 4 == 0, whole-tile partitions of >= 256 tokens, >= 64 of them at the
+    # longest context and >= 256 units in the batch; plain ceil(L / ps) partitions, no counters
+    long = dims(num_seqs=4, max_blocks_per_seq=8192)
+    assert L.lgm_paged_decode_workspace_size(long, 131072, 512, L.LGM_BF16) == (
+        al(4 * 32 * 256 * 128 * 4) + al(4 * 32 * 256 * 4))
+    assert L.lgm_paged_decode_workspace_size(long, 131072, 2048, L.LGM_FP8_E4M3) == (
+        al(4 * 32 * 64 * 128 * 4) + al(4 * 32 * 64 * 4))
+    d = dims()                                     # 16 partitions at the longest context: work-queue kernel
     assert L.lgm_paged_decode_workspace_size(d, 8192, 8192, L.LGM_BF16) == 256     # one partition
     assert L.lgm_paged_decode_workspace_size(d, 8192, 8192, L.LGM_FP8_E4M3) == 256
+    d2 = dims(num_q_heads=16, num_kv_heads=2)      # work-queue shape: 256 bytes of work counters first
+    assert L.lgm_paged_decode_workspace_size(d2, 8192, 8192, L.LGM_BF16) == 256    # one partition
     P = partitions_brute_force(8192, 512, 256)     # tails in half partitions
     assert P == 17
-    out_b = 64 * 32 * P * 128 * 4
+    out_b = 64 * 16 * P * 128 * 4
+    lse_b = 64 * 16 * P * 4
+    assert L.lgm_paged_decode_workspace_size(d2, 8192, 512, L.LGM_BF16) == 256 + al(out_b) + al(lse_b)
+    # below the whole-row partition minimum: the work-queue kernel, tails included
+    P64 = partitions_brute_force(8192, 64, 32)
+    assert L.lgm_paged_decode_workspace_size(d, 8192, 64, L.LGM_BF16) == (
+        256 + al(64 * 32 * P64 * 128 * 4) + al(64 * 32 * P64 * 4))
     lse_b = 64 * 32 * P * 4
-    assert L.lgm_paged_decode_workspace_size(d, 8192, 512, L.LGM_BF16) == 256 + al(out_b) + al(lse_b)
     v = dims(head_dim=64)                          # vector-ALU shape: partials only
     assert L.lgm_paged_decode_workspace_size(v, 8192, 8192, L.LGM_BF16) == 0
     assert L.lgm_paged_decode_workspace_size(v, 8192, 512, L.LGM_BF16) == al(64 * 32 * P * 64 * 4) + al(lse_b)

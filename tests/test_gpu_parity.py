@@ -327,7 +327,7 @@ def test_inactive_sequence_append_writes_nothing():
 
 
 @pytest.mark.parametrize("name", ["llama3_8b_gqa", "fp8_kv", "fp4_kv"])
-@pytest.mark.parametrize("ps", [64, 512])
+@pytest.mark.parametrize("ps", [64, 128])
 def test_persistent_workspace_is_reusable_and_left_zeroed(name, ps):
     """The matrix-core kernel hands out work items from two counters at the
     start of the workspace: a zero-filled workspace reused by consecutive calls
@@ -616,3 +616,48 @@ def test_contract_variants(cache, layout, rope_style, per_tensor, ps, hkv, G):
                    append=True, ctx_list=EDGE_CTX, rope_style=rope_style, cache_layout=layout,
                    scale_per_tensor=per_tensor)
     _run_and_check(cfg)
+
+
+# ------------------------------------------------------------------ whole-row partition plan
+@pytest.mark.parametrize("cache", ["bf16", "fp8", "fp4"])
+@pytest.mark.parametrize("hkv,G,ps", [(8, 4, 256), (4, 4, 256), (16, 2, 512)])
+def test_row_partition_plan_ragged_edges(cache, hkv, G, ps):
+    """Explicit partition sizes of whole tiles (>= 256 tokens) on whole-row
+    shapes with a long context (>= 64 partitions) in the batch: equal runs of
+    whole partitions, a record per partition of a split context, merged by
+    lse_merge; empty, one-token and tile-edge contexts and contexts that are a
+    partition plus one token."""
+    ctx = EDGE_CTX + (ps + 1, 2 * ps, 3 * ps - 17, 64 * ps + 5) + (ps // 2,) * 20
+    cfg = W.Config(f"rowparts_{cache}_H{hkv}_G{G}_ps{ps}", seed=14, num_seqs=len(ctx), num_q_heads=hkv * G,
+                   num_kv_heads=hkv, head_dim=128, block_size=16, act="bf16", cache=cache, ctx=0, rope_theta=1e4,
+                   partition_size=ps, append=True, ctx_list=ctx)
+    _run_and_check(cfg)
+
+
+def test_row_partition_plan_needs_no_zeroed_workspace_and_many_sequences():
+    """The partition plan reads only records written earlier in the same call
+    (a 0x7F-filled workspace gives identical results on repeated calls), and
+    walks more sequences than one scan step (1024)."""
+    ctx = tuple((i * 131) % 1500 for i in range(1099)) + (16400,)   # one context of 65 partitions
+    cfg = W.Config("rowparts_many", seed=15, num_seqs=len(ctx), num_q_heads=8, num_kv_heads=4, head_dim=128,
+                   block_size=16, act="bf16", cache="bf16", ctx=0, rope_theta=1e4, partition_size=256, append=False,
+                   ctx_list=ctx)
+    w = W.make_workload(cfg)
+    d = to_device(w)
+    q = q_from_qkv(w).cuda()
+    assert ops.partition_size(q, d.k_pool, d.block_tables, d.max_ctx, 256) == 256
+    nbytes = ops.workspace_bytes(q, d.k_pool, d.block_tables, d.max_ctx, 256)
+    ws = torch.full((nbytes,), 0x7F, dtype=torch.uint8, device="cuda")
+    announce("row partition plan, 1100 sequences", nbytes)
+    outs = []
+    for _ in range(2):
+        o, l = ops.paged_decode_attn(q, d.k_pool, d.v_pool, d.block_tables, d.context_lens, d.max_ctx,
+                                     softmax_scale=cfg.softmax_scale, partition_size=256, workspace=ws)
+        outs.append((o.clone(), l.clone()))
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0][0].view(torch.int16), outs[1][0].view(torch.int16)) and torch.equal(outs[0][1], outs[1][1])
+    sample = list(range(0, 1100, 37)) + [1099]
+    r_out, r_lse = oracle_attention(w, act_raw(w, q_from_qkv(w)), pool_raw(w, w.k_pool), pool_raw(w, w.v_pool),
+                                    seqs=sample)
+    assert max_abs(out_values(cfg, outs[0][0]), r_out, sample) <= TOL["bf16"]
+    _lse_check(outs[0][1].cpu().numpy(), r_lse, sample)
