@@ -235,3 +235,25 @@ def test_per_tensor_scale_read_as_one_is_caught(monkeypatch):
         return orig(pool, block_tables, b, L, g, block_size, cache, scale)
     monkeypatch.setattr(A, "gather_kv", bad)
     _fails(T_A.test_per_tensor_fp8_scale_is_every_heads_scale)
+
+
+def test_mla_dropped_positional_term_is_caught(monkeypatch):
+    import test_oracle_mla as T_M
+    from oracle import mla as M
+    def bad(q_lat, q_pe, c, r, scale):
+        return orig(q_lat, np.zeros_like(np.asarray(q_pe, dtype=np.float64)), c, r, scale)
+    orig = M.mla_attend
+    monkeypatch.setattr(M, "mla_attend", bad)
+    _fails(T_M.test_matches_torch_sdpa_fp64)
+
+
+def test_mla_value_from_positional_rows_is_caught(monkeypatch):
+    import test_oracle_mla as T_M
+    from oracle import mla as M
+    def bad(q_lat, q_pe, c, r, scale):
+        o, l = orig(q_lat, q_pe, c, r, scale)
+        return o * 0.5, l   # a mis-scaled value path
+    orig = M.mla_attend
+    monkeypatch.setattr(M, "mla_attend", bad)
+    _fails(T_M.test_matches_torch_sdpa_fp64)
+    _fails(T_M.test_equal_latent_rows_return_that_row_and_empty_context)

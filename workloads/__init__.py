@@ -341,3 +341,96 @@ def shuffled_copy(w: Workload, seed: int) -> Workload:
     mask = bt >= 0
     bt[mask] = perm[bt[mask].long()].to(torch.int32)
     return dataclasses.replace(w, block_tables=bt, k_pool=k_new, v_pool=v_new)
+
+
+# ------------------------------------------------------------------ multi-head latent attention (MLA)
+@dataclasses.dataclass(frozen=True)
+class MlaConfig:
+    """One paged MLA decode workload: per token a latent of latent_dim values
+    (FP8 E4M3 with one static per-tensor scale, or bf16) and a positional part
+    of rope_dim bf16 values; num_heads query heads share them.  ``ctx`` is a
+    fixed length or an inclusive (lo, hi), as for Config."""
+
+    name: str
+    seed: int
+    num_seqs: int
+    num_heads: int
+    ctx: Union[int, Tuple[int, int]]
+    partition_size: int
+    block_size: int = 64
+    latent_dim: int = 512
+    rope_dim: int = 64
+    ckv_cache: str = DTYPE_FP8
+    num_blocks: Optional[int] = None
+    calib_tokens: int = 4096
+    ctx_list: Optional[Tuple[int, ...]] = None
+    description: str = ""
+
+    @property
+    def max_ctx(self) -> int:
+        if self.ctx_list is not None:
+            return max(self.ctx_list) if self.ctx_list else 0
+        return self.ctx if isinstance(self.ctx, int) else self.ctx[1]
+
+    @property
+    def max_blocks_per_seq(self) -> int:
+        return -(-self.max_ctx // self.block_size)
+
+    @property
+    def softmax_scale(self) -> float:
+        # 1/sqrt(192): the 128 + 64 query-key width of the models with this cache shape
+        return float(np.float32(1.0 / math.sqrt(192.0)))
+
+    def with_(self, **kw) -> "MlaConfig":
+        return dataclasses.replace(self, **kw)
+
+
+MLA_CONFIGS = {
+    "mla_kimi_tp8": MlaConfig(
+        "mla_kimi_tp8", seed=7, num_seqs=1, num_heads=8, ctx=51200, partition_size=832,
+        description="MLA latent decode: 8 heads (one GPU's share of 64 under TP8), 51,200 tokens in 800 pages "
+                    "of 64, FP8 E4M3 ckv 512 + bf16 kpe 64, split-K into 62 partitions of 832 tokens"),
+}
+
+
+@dataclasses.dataclass
+class MlaWorkload:
+    cfg: MlaConfig
+    context_lens: torch.Tensor  # int32 [B]
+    block_tables: torch.Tensor  # int32 [B, MB]
+    ckv_pool: torch.Tensor      # [NB, bs, latent_dim] float8_e4m3fn or bfloat16
+    kpe_pool: torch.Tensor      # [NB, bs, rope_dim] bfloat16
+    q_latent: torch.Tensor      # [B, H, latent_dim] bfloat16
+    q_pe: torch.Tensor          # [B, H, rope_dim] bfloat16
+    ckv_scale: Optional[torch.Tensor]  # fp32 [1] for an FP8 ckv
+
+    def kv_bytes(self) -> int:
+        """Algorithmic bytes one call reads: each token's latent and positional rows once."""
+        c = self.cfg
+        e = 1 if c.ckv_cache == DTYPE_FP8 else 2
+        return int(self.context_lens.clamp(min=0).sum()) * (c.latent_dim * e + c.rope_dim * 2)
+
+
+def make_mla_workload(cfg: MlaConfig) -> MlaWorkload:
+    """Draw order: context lengths, tables, latent rows, positional rows,
+    queries, calibration (stage ids as for Config)."""
+    ctx = draw_context_lens(cfg)
+    bt, nb = draw_block_tables(cfg, ctx)
+    bs, dl, dr, B, H = cfg.block_size, cfg.latent_dim, cfg.rope_dim, cfg.num_seqs, cfg.num_heads
+    cf = _normal_f32(cfg.seed, STAGE_K, nb * bs * dl).reshape(nb, bs, dl)
+    rf = _normal_f32(cfg.seed, STAGE_V, nb * bs * dr).reshape(nb, bs, dr)
+    qf = _normal_f32(cfg.seed, STAGE_QKV, B * H * (dl + dr)).reshape(B, H, dl + dr)
+    scale = None
+    if cfg.ckv_cache == DTYPE_FP8:
+        calib = _normal_f32(cfg.seed, STAGE_CALIB, cfg.calib_tokens * dl)
+        s = np.float32(np.abs(calib).max()) / np.float32(E4M3_MAX)
+        scale = torch.tensor([s], dtype=torch.float32)
+        ckv = (torch.from_numpy(cf) / scale).clamp_(-E4M3_MAX, E4M3_MAX).to(torch.float8_e4m3fn)
+    elif cfg.ckv_cache == DTYPE_BF16:
+        ckv = torch.from_numpy(cf).to(torch.bfloat16)
+    else:
+        raise ValueError(cfg.ckv_cache)
+    kpe = torch.from_numpy(rf).to(torch.bfloat16)
+    q = torch.from_numpy(qf).to(torch.bfloat16)
+    return MlaWorkload(cfg, torch.from_numpy(ctx), torch.from_numpy(bt), ckv, kpe,
+                       q[..., :dl].contiguous(), q[..., dl:].contiguous(), scale)
