@@ -77,7 +77,7 @@
 extern "C" {
 #endif
 
-#define LGM_ABI_VERSION 3
+#define LGM_ABI_VERSION 4
 
 typedef enum lgm_status {
   LGM_OK = 0,
@@ -276,7 +276,7 @@ lgm_status lgm_paged_decode_attn(void* out, float* out_lse, const void* q, int64
  *   partial_out    fp32 [B][H][max_partitions][D], normalised partial outputs
  *   partial_lse    fp32 [B][H][max_partitions], natural log
  *   num_partitions optional int32 [B]
- * Supported: head_dim 64 or 128.
+ * Supported: head_dim 64, 128 or 512 (the MLA latent).
  */
 lgm_status lgm_lse_merge(void* out, float* out_lse, const float* partial_out,
                          const float* partial_lse, const int32_t* num_partitions,

@@ -1,4 +1,4 @@
-"""ctypes binding of liblgm.so (include/lgm.h): argument marshalling only.
+"""ctypes binding of liblgm.so (include/*.h): argument marshalling only.
 
 Each function has the name and argument order of its C entry point.  Tensor
 arguments may be torch tensors (their data_ptr() is passed), raw integer
@@ -40,6 +40,14 @@ class lgm_paged_dims(ctypes.Structure):
         return "lgm_paged_dims(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")"
 
 
+class lgm_mla_dims(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "num_seqs", "num_heads", "latent_dim", "rope_dim", "block_size", "num_blocks", "max_blocks_per_seq")]
+
+    def __repr__(self):
+        return "lgm_mla_dims(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")"
+
+
 _lib = None
 
 
@@ -67,6 +75,13 @@ def lib() -> ctypes.CDLL:
         L.lgm_last_error.restype = ctypes.c_char_p
         L.lgm_abi_version.argtypes = []
         L.lgm_abi_version.restype = i32
+        L.lgm_paged_mla_partition_size.argtypes = [lgm_mla_dims, i32, i32]
+        L.lgm_paged_mla_partition_size.restype = i32
+        L.lgm_paged_mla_workspace_size.argtypes = [lgm_mla_dims, i32, i32]
+        L.lgm_paged_mla_workspace_size.restype = sz
+        L.lgm_paged_mla_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, f32, i32, i32, vp, sz, lgm_mla_dims,
+                                           i32, vp]
+        L.lgm_paged_mla_decode.restype = i32
         L.lgm_stream_read_probe.argtypes = [vp, sz, i32, i32, vp, vp]
         L.lgm_stream_read_probe.restype = i32
         _lib = L
@@ -146,6 +161,34 @@ def lgm_lse_merge(out, out_lse, partial_out, partial_lse, num_partitions, num_se
     _check(lib().lgm_lse_merge(_ptr(out), _ptr(out_lse), _ptr(partial_out), _ptr(partial_lse),
                                _ptr(num_partitions), num_seqs, num_q_heads, head_dim, max_partitions, out_dtype,
                                _stream(stream)))
+
+
+def make_mla_dims(num_seqs, num_heads, latent_dim, rope_dim, block_size, num_blocks, max_blocks_per_seq):
+    return lgm_mla_dims(num_seqs, num_heads, latent_dim, rope_dim, block_size, num_blocks, max_blocks_per_seq)
+
+
+def lgm_paged_mla_partition_size(dims, max_context_len, partition_size) -> int:
+    r = lib().lgm_paged_mla_partition_size(dims, max_context_len, partition_size)
+    if r < 0:
+        raise LgmError(LGM_ERR_INVALID_ARGUMENT, lib().lgm_last_error().decode())
+    return r
+
+
+def lgm_paged_mla_workspace_size(dims, max_context_len, partition_size) -> int:
+    r = lib().lgm_paged_mla_workspace_size(dims, max_context_len, partition_size)
+    err = lib().lgm_last_error().decode()
+    if r == 0 and err:
+        raise LgmError(LGM_ERR_INVALID_ARGUMENT, err)
+    return r
+
+
+def lgm_paged_mla_decode(out, out_lse, q_latent, q_pe, ckv_cache, kpe_cache, block_tables, context_lens, ckv_scale,
+                         softmax_scale, partition_size, max_context_len, workspace, workspace_bytes, dims, ckv_dtype,
+                         stream=None):
+    _check(lib().lgm_paged_mla_decode(_ptr(out), _ptr(out_lse), _ptr(q_latent), _ptr(q_pe), _ptr(ckv_cache),
+                                      _ptr(kpe_cache), _ptr(block_tables), _ptr(context_lens), _ptr(ckv_scale),
+                                      softmax_scale, partition_size, max_context_len, _ptr(workspace),
+                                      workspace_bytes, dims, ckv_dtype, _stream(stream)))
 
 
 def lgm_last_error() -> str:

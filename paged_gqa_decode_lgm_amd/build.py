@@ -35,6 +35,7 @@ UNITS = {
     "paged_decode_rows.hip": [],
     "lse_merge.hip": [],
     "stream_probe.hip": [],
+    "paged_mla.hip": [],
 }
 
 

@@ -12,6 +12,7 @@
 #include <string>
 
 #include "lgm_internal.h"
+#include "lgm_mla.h"
 #include "lgm_probe.h"
 
 namespace {
@@ -305,6 +306,72 @@ lgm_status check_decode_common(const char* fn, const lgm_paged_dims& d, int32_t 
   return LGM_OK;
 }
 
+// ---- paged MLA ------------------------------------------------------------------
+// Auto partition of the MLA kernel: about one workgroup (a partition of one
+// sequence, its four waves taking turns over the 32-token tiles) per compute
+// unit of MI355X at max_context_len, and at least one tile per wave.
+constexpr int64_t kMlaTargetWorkgroups = 256;
+constexpr int32_t kMlaTile = 32;
+constexpr int32_t kMlaMinAutoPartition = 128;
+
+lgm_status check_mla_dims(const char* fn, const lgm_mla_dims& d, int32_t max_ctx) {
+  if (d.num_seqs < 0) return fail(LGM_ERR_INVALID_ARGUMENT, fn, "dims.num_seqs = %d must be >= 0", d.num_seqs);
+  if (d.num_heads < 1) return fail(LGM_ERR_INVALID_ARGUMENT, fn, "dims.num_heads = %d must be >= 1", d.num_heads);
+  if (d.latent_dim < 1 || d.rope_dim < 1)
+    return fail(LGM_ERR_INVALID_ARGUMENT, fn, "dims.latent_dim = %d and dims.rope_dim = %d must be >= 1",
+                d.latent_dim, d.rope_dim);
+  if (d.block_size < 1) return fail(LGM_ERR_INVALID_ARGUMENT, fn, "dims.block_size = %d must be >= 1", d.block_size);
+  if (d.num_blocks < 1) return fail(LGM_ERR_INVALID_ARGUMENT, fn, "dims.num_blocks = %d must be >= 1", d.num_blocks);
+  if (d.max_blocks_per_seq < 1)
+    return fail(LGM_ERR_INVALID_ARGUMENT, fn, "dims.max_blocks_per_seq = %d must be >= 1", d.max_blocks_per_seq);
+  const int64_t cap = (int64_t)d.max_blocks_per_seq * d.block_size;
+  if (cap > INT32_MAX)
+    return fail(LGM_ERR_INVALID_ARGUMENT, fn, "dims.max_blocks_per_seq * dims.block_size = %lld exceeds INT32_MAX",
+                (long long)cap);
+  if (max_ctx < 0 || max_ctx > cap)
+    return fail(LGM_ERR_INVALID_ARGUMENT, fn,
+                "max_context_len = %d must be in [0, max_blocks_per_seq * block_size = %lld]", max_ctx, (long long)cap);
+  if (!lgm::mla_supported(LGM_FP8_E4M3, d.latent_dim, d.rope_dim, d.num_heads, d.block_size))
+    return fail(LGM_ERR_UNSUPPORTED, fn,
+                "(latent_dim %d, rope_dim %d, num_heads %d, block_size %d) unsupported: supported are latent_dim "
+                "512, rope_dim 64, num_heads 1..16, block_size a multiple of 16",
+                d.latent_dim, d.rope_dim, d.num_heads, d.block_size);
+  if (d.num_seqs > 65535) return fail(LGM_ERR_UNSUPPORTED, fn, "dims.num_seqs = %d: at most 65535", d.num_seqs);
+  if ((int64_t)d.num_seqs * d.num_heads > (int64_t)INT32_MAX - 1024)  // merge rows are int-indexed
+    return fail(LGM_ERR_UNSUPPORTED, fn, "num_seqs * num_heads = %lld: too many",
+                (long long)d.num_seqs * d.num_heads);
+  return LGM_OK;
+}
+
+struct MlaPlan {
+  int32_t ps, P;
+  size_t part_out_bytes, part_lse_bytes, total;
+};
+
+lgm_status plan_mla(const char* fn, const lgm_mla_dims& d, int32_t max_ctx, int32_t ps, MlaPlan& pl) {
+  pl = MlaPlan{};
+  if (ps < 0 || ps % kMlaTile != 0)
+    return fail(LGM_ERR_INVALID_ARGUMENT, fn, "partition_size = %d must be 0 (library chooses) or a positive "
+                "multiple of %d", ps, kMlaTile);
+  const int64_t cap = ((int64_t)(max_ctx > 0 ? max_ctx : 1) + kMlaTile - 1) / kMlaTile * kMlaTile;
+  int64_t p = ps;
+  if (p == 0) {
+    const int64_t tokens = (int64_t)(d.num_seqs > 0 ? d.num_seqs : 1) * max_ctx;
+    p = (tokens + kMlaTargetWorkgroups - 1) / kMlaTargetWorkgroups;
+    p = (p + kMlaTile - 1) / kMlaTile * kMlaTile;
+    p = p < kMlaMinAutoPartition ? kMlaMinAutoPartition : p;
+  }
+  pl.ps = (int32_t)(p < cap ? p : cap);
+  pl.P = (int32_t)(((int64_t)max_ctx + pl.ps - 1) / pl.ps);
+  pl.P = pl.P < 1 ? 1 : pl.P;
+  if (pl.P > 1) {
+    pl.part_out_bytes = align256((size_t)d.num_seqs * d.num_heads * pl.P * d.latent_dim * sizeof(float));
+    pl.part_lse_bytes = align256((size_t)d.num_seqs * d.num_heads * pl.P * sizeof(float));
+  }
+  pl.total = pl.part_out_bytes + pl.part_lse_bytes;
+  return LGM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -530,7 +597,7 @@ lgm_status lgm_lse_merge(void* out, float* out_lse, const float* partial_out, co
   if (!(out_dtype == LGM_F32 || out_dtype == LGM_BF16))
     return fail(LGM_ERR_UNSUPPORTED, fn, "out_dtype = %d: supported are LGM_F32 and LGM_BF16", (int)out_dtype);
   if (!lgm::merge_supported(head_dim))
-    return fail(LGM_ERR_UNSUPPORTED, fn, "head_dim = %d: supported are 64 and 128", head_dim);
+    return fail(LGM_ERR_UNSUPPORTED, fn, "head_dim = %d: supported are 64, 128 and 512", head_dim);
   if (num_seqs > 65535)
     return fail(LGM_ERR_UNSUPPORTED, fn, "num_seqs = %d: at most 65535", num_seqs);
   if (num_seqs == 0) return LGM_OK;
@@ -551,6 +618,93 @@ lgm_status lgm_lse_merge(void* out, float* out_lse, const float* partial_out, co
                    num_seqs, num_q_heads, head_dim, max_partitions, 0};
   const hipError_t e = lgm::launch_lse_merge(m, out_dtype, (hipStream_t)stream);
   if (e != hipSuccess) return fail(LGM_ERR_HIP, fn, "kernel launch failed: %s", hipGetErrorString(e));
+  return LGM_OK;
+}
+
+int32_t lgm_paged_mla_partition_size(lgm_mla_dims dims, int32_t max_context_len, int32_t partition_size) {
+  const char* fn = "lgm_paged_mla_partition_size";
+  g_err.clear();
+  if (check_mla_dims(fn, dims, max_context_len) != LGM_OK) return -1;
+  MlaPlan pl;
+  if (plan_mla(fn, dims, max_context_len, partition_size, pl) != LGM_OK) return -1;
+  return pl.ps;
+}
+
+size_t lgm_paged_mla_workspace_size(lgm_mla_dims dims, int32_t max_context_len, int32_t partition_size) {
+  const char* fn = "lgm_paged_mla_workspace_size";
+  g_err.clear();
+  if (check_mla_dims(fn, dims, max_context_len) != LGM_OK) return 0;
+  MlaPlan pl;
+  if (plan_mla(fn, dims, max_context_len, partition_size, pl) != LGM_OK) return 0;
+  return pl.total;
+}
+
+lgm_status lgm_paged_mla_decode(void* out, float* out_lse, const void* q_latent, const void* q_pe,
+                                const void* ckv_cache, const void* kpe_cache, const int32_t* block_tables,
+                                const int32_t* context_lens, const float* ckv_scale, float softmax_scale,
+                                int32_t partition_size, int32_t max_context_len, void* workspace,
+                                size_t workspace_bytes, lgm_mla_dims dims, lgm_dtype ckv_dtype, void* stream) {
+  const char* fn = "lgm_paged_mla_decode";
+  g_err.clear();
+  lgm_status st = check_mla_dims(fn, dims, max_context_len);
+  if (st != LGM_OK) return st;
+  if (!dtype_valid(ckv_dtype)) return fail(LGM_ERR_INVALID_ARGUMENT, fn, "ckv_dtype = %d is not an lgm_dtype", (int)ckv_dtype);
+  if (ckv_dtype != LGM_FP8_E4M3)
+    return fail(LGM_ERR_UNSUPPORTED, fn, "ckv_dtype = %s: supported is LGM_FP8_E4M3", dtype_name(ckv_dtype));
+  if (!std::isfinite(softmax_scale))
+    return fail(LGM_ERR_INVALID_ARGUMENT, fn, "softmax_scale = %g must be finite", (double)softmax_scale);
+  MlaPlan pl;
+  if ((st = plan_mla(fn, dims, max_context_len, partition_size, pl)) != LGM_OK) return st;
+  if (pl.total > 0) {
+    if (!workspace)
+      return fail(LGM_ERR_WORKSPACE_TOO_SMALL, fn, "workspace is NULL but %zu bytes are needed", pl.total);
+    if (workspace_bytes < pl.total)
+      return fail(LGM_ERR_WORKSPACE_TOO_SMALL, fn, "workspace_bytes = %zu < %zu needed", workspace_bytes, pl.total);
+    if ((uintptr_t)workspace % 256 != 0)
+      return fail(LGM_ERR_INVALID_ARGUMENT, fn, "workspace %p must be 256-byte aligned", workspace);
+  }
+  if (!ckv_scale) return fail(LGM_ERR_INVALID_ARGUMENT, fn, "ckv_scale is NULL; an FP8 ckv cache needs its fp32 [1] scale");
+  if (dims.num_seqs == 0) return LGM_OK;
+  if (!out) return fail(LGM_ERR_INVALID_ARGUMENT, fn, "out is NULL");
+  if (!q_latent) return fail(LGM_ERR_INVALID_ARGUMENT, fn, "q_latent is NULL");
+  if (!q_pe) return fail(LGM_ERR_INVALID_ARGUMENT, fn, "q_pe is NULL");
+  if (!ckv_cache) return fail(LGM_ERR_INVALID_ARGUMENT, fn, "ckv_cache is NULL");
+  if (!kpe_cache) return fail(LGM_ERR_INVALID_ARGUMENT, fn, "kpe_cache is NULL");
+  if (!block_tables) return fail(LGM_ERR_INVALID_ARGUMENT, fn, "block_tables is NULL");
+  if (!context_lens) return fail(LGM_ERR_INVALID_ARGUMENT, fn, "context_lens is NULL");
+  const void* aligned[] = {out, q_latent, q_pe, ckv_cache, kpe_cache};
+  const char* aligned_names[] = {"out", "q_latent", "q_pe", "ckv_cache", "kpe_cache"};
+  for (int i = 0; i < 5; ++i)
+    if ((uintptr_t)aligned[i] % 16 != 0)
+      return fail(LGM_ERR_INVALID_ARGUMENT, fn, "%s (%p) must be 16-byte aligned", aligned_names[i], aligned[i]);
+
+  const int64_t B = dims.num_seqs, H = dims.num_heads;
+  const int64_t pool_rows = (int64_t)dims.num_blocks * dims.block_size;
+  const Span outs[] = {{"out", (uintptr_t)out, B * H * dims.latent_dim * 2},
+                       {"out_lse", (uintptr_t)out_lse, out_lse ? B * H * 4 : 0},
+                       {"workspace", (uintptr_t)workspace, (int64_t)pl.total}};
+  const Span ins[] = {{"q_latent", (uintptr_t)q_latent, B * H * dims.latent_dim * 2},
+                      {"q_pe", (uintptr_t)q_pe, B * H * dims.rope_dim * 2},
+                      {"ckv_cache", (uintptr_t)ckv_cache, pool_rows * dims.latent_dim},
+                      {"kpe_cache", (uintptr_t)kpe_cache, pool_rows * dims.rope_dim * 2},
+                      {"block_tables", (uintptr_t)block_tables, B * dims.max_blocks_per_seq * 4},
+                      {"context_lens", (uintptr_t)context_lens, B * 4},
+                      {"ckv_scale", (uintptr_t)ckv_scale, 4}};
+  if ((st = check_no_alias(fn, outs, 3, ins, 7)) != LGM_OK) return st;
+
+  char* wsb = static_cast<char*>(workspace);
+  float* part_out = pl.P > 1 ? reinterpret_cast<float*>(wsb) : nullptr;
+  float* part_lse = pl.P > 1 ? reinterpret_cast<float*>(wsb + pl.part_out_bytes) : nullptr;
+  lgm::MlaArgs a{out, out_lse, q_latent, q_pe, ckv_cache, kpe_cache, block_tables, context_lens, ckv_scale,
+                 part_out, part_lse, softmax_scale, pl.ps, max_context_len, pl.P, dims};
+  hipError_t e = lgm::launch_paged_mla(a, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(LGM_ERR_HIP, fn, "MLA kernel launch failed: %s", hipGetErrorString(e));
+  if (pl.P > 1) {
+    lgm::MergeArgs m{out, out_lse, part_out, part_lse, nullptr, context_lens, lgm::PartitionPlan{pl.ps, pl.ps},
+                     max_context_len, dims.num_seqs, dims.num_heads, dims.latent_dim, pl.P, 1};
+    e = lgm::launch_lse_merge(m, LGM_BF16, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(LGM_ERR_HIP, fn, "merge kernel launch failed: %s", hipGetErrorString(e));
+  }
   return LGM_OK;
 }
 

@@ -8,6 +8,7 @@
 #include <stdint.h>
 
 #include "lgm.h"
+#include "lgm_mla.h"
 
 namespace lgm {
 
@@ -157,6 +158,29 @@ bool decode_rows_supported(lgm_dtype act, lgm_dtype cache, int head_dim, int num
 #define LGM_PERSISTENT_MAX_PER_CU 2
 #endif
 constexpr int kPersistentMaxPerCU = LGM_PERSISTENT_MAX_PER_CU;
+
+// Paged MLA decode: one workgroup per (sequence, partition), grid
+// (max_partitions, num_seqs).
+struct MlaArgs {
+  void* out;                // [B][H][512] bf16
+  float* out_lse;           // [B][H] or NULL
+  const void* q_latent;     // [B][H][512] bf16
+  const void* q_pe;         // [B][H][64] bf16
+  const void* ckv;          // [NB][bs][512] FP8 codes
+  const void* kpe;          // [NB][bs][64] bf16
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  const float* ckv_scale;   // [1]
+  float* part_out;          // [B][H][P][512] fp32, NULL when P == 1
+  float* part_lse;          // [B][H][P]
+  float softmax_scale;
+  int32_t partition_size;   // multiple of 32
+  int32_t max_context_len;
+  int32_t max_partitions;   // P
+  lgm_mla_dims dims;
+};
+hipError_t launch_paged_mla(const MlaArgs& a, hipStream_t s);
+bool mla_supported(lgm_dtype ckv, int latent_dim, int rope_dim, int num_heads, int block_size);
 
 // Shape support queries used by validation (no HIP calls).
 bool decode_supported(lgm_dtype act, lgm_dtype cache, int head_dim, int group, int block_size);

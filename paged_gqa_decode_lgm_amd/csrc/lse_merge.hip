@@ -127,6 +127,8 @@ hipError_t dispatch(const MergeArgs& a, hipStream_t s) {
     launch_dim<O, 64>(a, s);
   else if (a.head_dim == 128)
     launch_dim<O, 128>(a, s);
+  else if (a.head_dim == 512)  // the MLA latent
+    launch_dim<O, 512>(a, s);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
@@ -134,7 +136,7 @@ hipError_t dispatch(const MergeArgs& a, hipStream_t s) {
 
 }  // namespace
 
-bool merge_supported(int head_dim) { return head_dim == 64 || head_dim == 128; }
+bool merge_supported(int head_dim) { return head_dim == 64 || head_dim == 128 || head_dim == 512; }
 
 hipError_t launch_lse_merge(const MergeArgs& a, lgm_dtype out_dtype, hipStream_t s) {
   if (out_dtype == LGM_F32) return dispatch<OutF32>(a, s);

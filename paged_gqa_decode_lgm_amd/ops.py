@@ -139,3 +139,47 @@ def lse_merge(partial_out, partial_lse, num_partitions=None, out_dtype=torch.flo
         out_lse = torch.empty((bsz, h), dtype=torch.float32, device=partial_out.device)
     B.lgm_lse_merge(out, out_lse, partial_out, partial_lse, num_partitions, bsz, h, d, p, lgm_dtype(out), stream)
     return out, out_lse
+
+
+# ---- paged MLA (include/lgm_mla.h) -----------------------------------------------------
+def mla_dims_for(q_latent, q_pe, ckv_cache, block_tables) -> B.lgm_mla_dims:
+    """Dims from q_latent [B, H, 512], q_pe [B, H, 64], ckv [NB, bs, 512]."""
+    bsz, h, dl = q_latent.shape
+    nb, bs, _ = ckv_cache.shape
+    return B.make_mla_dims(bsz, h, dl, q_pe.shape[2], bs, nb, block_tables.shape[1])
+
+
+def mla_partition_size(q_latent, q_pe, ckv_cache, block_tables, max_context_len: int, partition_size: int = 0) -> int:
+    dims = mla_dims_for(q_latent, q_pe, ckv_cache, block_tables)
+    return B.lgm_paged_mla_partition_size(dims, int(max_context_len), partition_size)
+
+
+def mla_workspace_bytes(q_latent, q_pe, ckv_cache, block_tables, max_context_len: int,
+                        partition_size: int = 0) -> int:
+    dims = mla_dims_for(q_latent, q_pe, ckv_cache, block_tables)
+    return B.lgm_paged_mla_workspace_size(dims, int(max_context_len), partition_size)
+
+
+def paged_mla_decode(q_latent, q_pe, ckv_cache, kpe_cache, block_tables, context_lens, max_context_len: int,
+                     softmax_scale: float, ckv_scale, partition_size: int = 0, out=None, out_lse=None,
+                     workspace=None, want_lse: bool = True, stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Paged MLA decode of q_latent [B, H, 512] / q_pe [B, H, 64] (bf16,
+    dense) over ckv [NB, bs, 512] (float8_e4m3fn) and kpe [NB, bs, 64]
+    (bf16); returns (out [B, H, 512] bf16, lse [B, H] or None)."""
+    for name, t in (("q_latent", q_latent), ("q_pe", q_pe), ("ckv_cache", ckv_cache), ("kpe_cache", kpe_cache)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    dims = mla_dims_for(q_latent, q_pe, ckv_cache, block_tables)
+    bsz, h, dl = q_latent.shape
+    if out is None:
+        out = torch.empty((bsz, h, dl), dtype=torch.bfloat16, device=q_latent.device)
+    if out_lse is None and want_lse:
+        out_lse = torch.empty((bsz, h), dtype=torch.float32, device=q_latent.device)
+    need = B.lgm_paged_mla_workspace_size(dims, int(max_context_len), partition_size)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q_latent.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    B.lgm_paged_mla_decode(out, out_lse, q_latent, q_pe, ckv_cache, kpe_cache, block_tables, context_lens, ckv_scale,
+                           float(softmax_scale), partition_size, int(max_context_len), workspace, ws_bytes, dims,
+                           lgm_dtype(ckv_cache), stream=stream)
+    return out, out_lse

@@ -30,10 +30,11 @@ def test_library_loads_and_exports_every_header_function():
     names = L.header_functions()
     assert set(names) == {"lgm_rope_kv_append", "lgm_paged_decode_partition_size", "lgm_paged_decode_workspace_size",
                           "lgm_paged_decode_attn", "lgm_lse_merge", "lgm_last_error", "lgm_abi_version",
-                          "lgm_stream_read_probe"}
+                          "lgm_stream_read_probe", "lgm_paged_mla_partition_size", "lgm_paged_mla_workspace_size",
+                          "lgm_paged_mla_decode"}
     for n in names:
         assert hasattr(lib, n), n
-    assert L.lgm_abi_version() == 3
+    assert L.lgm_abi_version() == 4
 
 
 # ------------------------------------------------------------------ append
@@ -307,3 +308,99 @@ def test_stream_probe_rejects_before_launch(kw, msg):
     assert e.value.status == L.LGM_ERR_INVALID_ARGUMENT
     assert msg in e.value.message
 
+
+
+# ------------------------------------------------------------------ paged MLA
+def mla_dims(**kw):
+    d = dict(num_seqs=1, num_heads=8, latent_dim=512, rope_dim=64, block_size=64, num_blocks=1000,
+             max_blocks_per_seq=800)
+    d.update(kw)
+    return L.make_mla_dims(**d)
+
+
+def _mla(**over):
+    a = dict(out=addr(0), out_lse=addr(1), q_latent=addr(2), q_pe=addr(3), ckv_cache=addr(4), kpe_cache=addr(5),
+             block_tables=addr(6), context_lens=addr(7), ckv_scale=addr(8), softmax_scale=0.0722,
+             partition_size=832, max_context_len=51200, workspace=addr(9), workspace_bytes=1 << 30,
+             dims=mla_dims(), ckv_dtype=L.LGM_FP8_E4M3, stream=0)
+    a.update(over)
+    return L.lgm_paged_mla_decode(**a)
+
+
+MLA_BAD = [
+    (dict(dims=mla_dims(latent_dim=256)), UNS, "latent_dim"),
+    (dict(dims=mla_dims(rope_dim=32)), UNS, "rope_dim"),
+    (dict(dims=mla_dims(num_heads=17)), UNS, "num_heads"),
+    (dict(dims=mla_dims(num_heads=0)), INV, "num_heads"),
+    (dict(dims=mla_dims(block_size=8, max_blocks_per_seq=6400)), UNS, "block_size"),
+    (dict(dims=mla_dims(block_size=24, max_blocks_per_seq=3000)), UNS, "block_size"),
+    (dict(dims=mla_dims(num_seqs=-1)), INV, "num_seqs"),
+    (dict(dims=mla_dims(num_seqs=70000)), UNS, "num_seqs"),
+    (dict(dims=mla_dims(num_blocks=0)), INV, "num_blocks"),
+    (dict(ckv_dtype=L.LGM_BF16), UNS, "ckv_dtype"),
+    (dict(ckv_dtype=9), INV, "ckv_dtype"),
+    (dict(softmax_scale=float("nan")), INV, "softmax_scale"),
+    (dict(max_context_len=51201), INV, "max_context_len"),
+    (dict(partition_size=48), INV, "partition_size"),
+    (dict(partition_size=-32), INV, "partition_size"),
+    (dict(workspace=None), WS, "workspace"),
+    (dict(workspace_bytes=4096), WS, "workspace_bytes"),
+    (dict(workspace=addr(9) + 16), INV, "workspace"),
+    (dict(ckv_scale=None), INV, "ckv_scale"),
+    (dict(out=None), INV, "out"),
+    (dict(q_latent=None), INV, "q_latent"),
+    (dict(q_pe=None), INV, "q_pe"),
+    (dict(ckv_cache=None), INV, "ckv_cache"),
+    (dict(kpe_cache=None), INV, "kpe_cache"),
+    (dict(block_tables=None), INV, "block_tables"),
+    (dict(context_lens=None), INV, "context_lens"),
+    (dict(q_pe=addr(3) + 8), INV, "aligned"),
+    (dict(out=addr(0) + 2), INV, "aligned"),
+    (dict(out=addr(2) + 1024), INV, "'out' overlaps input 'q_latent'"),
+    (dict(workspace=addr(4) + 256), INV, "overlaps input 'ckv_cache'"),
+]
+
+
+@pytest.mark.parametrize("over,status,word", MLA_BAD)
+def test_mla_rejects(over, status, word):
+    with pytest.raises(L.LgmError) as e:
+        _mla(**over)
+    assert e.value.status == status
+    assert e.value.message.startswith("lgm_paged_mla_decode:")
+    assert word in e.value.message
+
+
+def test_mla_empty_batch_is_a_noop():
+    _mla(dims=mla_dims(num_seqs=0), out=None, q_latent=None, workspace=None, workspace_bytes=0)
+
+
+@pytest.mark.parametrize("B,max_ctx,ps,want", [
+    (1, 51200, 832, 832),      # explicit: kept
+    (1, 51200, 0, 224),        # ceil(51200 / 256) = 200 -> 224 (whole tiles)
+    (64, 4096, 0, 1024),       # 64 * 4096 / 256
+    (1, 1000, 0, 128),         # at least one tile per wave
+    (1, 100, 0, 128),          # capped to the context rounded up to 32
+    (1, 100, 4096, 128),
+    (1, 0, 0, 32),
+    (3, 70, 64, 64),
+])
+def test_mla_partition_plan(B, max_ctx, ps, want):
+    assert L.lgm_paged_mla_partition_size(mla_dims(num_seqs=B), max_ctx, ps) == want
+
+
+@pytest.mark.parametrize("B,H,max_ctx,ps", [(1, 8, 51200, 832), (1, 8, 51200, 0), (4, 16, 3000, 96),
+                                            (2, 1, 100, 0), (5, 8, 64, 64)])
+def test_mla_workspace_formula(B, H, max_ctx, ps):
+    d = mla_dims(num_seqs=B, num_heads=H)
+    p = L.lgm_paged_mla_partition_size(d, max_ctx, ps)
+    P = max(1, -(-max_ctx // p))
+    al = lambda x: -(-x // 256) * 256
+    want = 0 if P == 1 else al(B * H * P * 512 * 4) + al(B * H * P * 4)
+    assert L.lgm_paged_mla_workspace_size(d, max_ctx, ps) == want
+
+
+def test_merge_accepts_the_latent_width():
+    # rejected only for its NULL output, after the head_dim check passed
+    with pytest.raises(L.LgmError) as e:
+        _merge(head_dim=512, out=None)
+    assert "out is NULL" in e.value.message
