@@ -97,7 +97,7 @@ size_t lgm_paged_mla_workspace_size(lgm_mla_dims dims, int32_t max_context_len, 
  *                  256-byte aligned (NULL allowed when that size is 0)
  *   ckv_dtype      LGM_FP8_E4M3
  * Supported: latent_dim 512, rope_dim 64, num_heads 1..16, block_size a
- * multiple of 16, num_seqs <= 65535.
+ * power of two, num_seqs <= 65535.
  */
 lgm_status lgm_paged_mla_decode(void* out, float* out_lse, const void* q_latent, const void* q_pe,
                                 const void* ckv_cache, const void* kpe_cache, const int32_t* block_tables,

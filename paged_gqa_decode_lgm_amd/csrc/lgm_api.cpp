@@ -334,7 +334,7 @@ lgm_status check_mla_dims(const char* fn, const lgm_mla_dims& d, int32_t max_ctx
   if (!lgm::mla_supported(LGM_FP8_E4M3, d.latent_dim, d.rope_dim, d.num_heads, d.block_size))
     return fail(LGM_ERR_UNSUPPORTED, fn,
                 "(latent_dim %d, rope_dim %d, num_heads %d, block_size %d) unsupported: supported are latent_dim "
-                "512, rope_dim 64, num_heads 1..16, block_size a multiple of 16",
+                "512, rope_dim 64, num_heads 1..16, block_size a power of two",
                 d.latent_dim, d.rope_dim, d.num_heads, d.block_size);
   if (d.num_seqs > 65535) return fail(LGM_ERR_UNSUPPORTED, fn, "dims.num_seqs = %d: at most 65535", d.num_seqs);
   if ((int64_t)d.num_seqs * d.num_heads > (int64_t)INT32_MAX - 1024)  // merge rows are int-indexed

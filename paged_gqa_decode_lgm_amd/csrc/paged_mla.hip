@@ -4,29 +4,35 @@
 // exported LSE, softmax-weighted latent output tiles, split-K across the
 // sequence with a stage-2 merge of the partial records).
 //
-// Every query head attends to the same latent rows, so one wave takes all
-// heads (up to 16) of a sequence at once: they are the 16 columns of the
-// score MFMA and the 16 rows of the output MFMA (v_mfma_f32_16x16x32_bf16,
-// lane l = 16 kg + n).
-//   scores  S^T[token][head] = K[token][576] Q^T: 16 MFMAs over the latent
-//           (FP8 codes converted to bf16, exactly) and 2 over the positional
-//           part, in two accumulators, so that s = scale * (s_ckv * <q_lat,
-//           code> + <q_pe, kpe>); lane (kg, n) reads 16 latent codes per
-//           64-byte chunk and 8 positional values per 32 of token n.
-//   output  O[head][512] += P[head][token] V[token][512], V = the latent
-//           codes: 32 MFMAs per 32-token tile, column n of MFMA i meaning
-//           latent element 32n + i, so a lane reads 32 contiguous bytes of
-//           each of its 8 token rows; s_ckv is applied at the end.
-// The latent bytes are therefore read twice per tile in the two operand
-// layouts (once from HBM, once from cache).
-//
-// Work split: one workgroup per (sequence, partition); its four waves take
-// the partition's 32-token tiles in turn (wave w: tiles w, w + 4, ...), each
-// with its own running max and sums, and combine through LDS at the end, so
-// a partition of ps tokens leaves one record however small ps / 4 is.  The
-// record (normalised fp32 output and natural-log LSE) goes to the partial
-// buffers when the sequence has several partitions (lse_merge combines
-// them), else the output is written directly.
+// Every query head attends to the same latent rows.  One workgroup takes one
+// (sequence, partition) and walks it in 64-token tiles held in LDS.  Its
+// eight waves have two roles:
+//   load waves (4..7) gather the tiles through the block table into
+//           registers and store them into one of three LDS tile buffers,
+//           two tiles ahead of the compute waves, so that HBM reads overlap
+//           the matrix work; invalid rows (past the partition, or behind an
+//           out-of-range table entry) are stored as zeros and masked.
+//   compute waves (0..3), v_mfma_f32_16x16x32_bf16, lane l = 16 kg + n:
+//     scores  wave w scores tokens 16w .. 16w+15 for all heads (up to 16,
+//             the MFMA columns): S^T[token][head] = K[token][576] Q^T, 16
+//             MFMAs over the latent (FP8 codes converted to bf16, exactly)
+//             and 2 over the positional part in separate accumulators, so
+//             that s = scale * (s_ckv * <q_lat, code> + <q_pe, kpe>);
+//     softmax the waves exchange their tile maxima through LDS, so every
+//             wave holds the same running reference max, and write their
+//             probabilities (bf16) into a shared [head][token] tile;
+//     output  wave w owns latent columns 128w .. 128w+127: O[head][col] +=
+//             P[head][token] V[token][col], V = the latent codes, 8 MFMAs
+//             per 32 tokens with column n of MFMA i meaning latent
+//             128w + 8n + i, so a lane reads 8 contiguous codes of each of
+//             its 8 token rows; s_ckv is applied at the end.
+// Each latent byte is read from HBM once and converted twice (once per
+// operand layout).  Two barriers per tile order the roles: B1 (tile maxima
+// written) and B2 (probabilities written; the load waves then refill the
+// buffer the previous tile used).  A partition's record (normalised fp32
+// output and natural-log LSE) goes to the partial buffers when its sequence
+// has several partitions (lse_merge combines them), else the output is
+// written directly.
 #include "mfma_common.h"
 
 namespace lgm {
@@ -36,303 +42,328 @@ using namespace mfma;
 
 constexpr int kDL = 512;  // latent elements
 constexpr int kDR = 64;   // positional elements
-constexpr int kDQ = kDL + kDR;
-constexpr int kMlaWaves = kDecodeThreads / kWaveSize;
+constexpr int kMlaThreads = 512;
+constexpr int kComputeWaves = 4;
 constexpr int kMlaHeads = 16;
-constexpr int kMergePad = 36;
-constexpr float kRescaleSlack = 8.f;  // floats per 32-element slice in the merge buffer (bank spread)
+constexpr int kT = 64;               // tokens per tile
+constexpr int kBufs = 3;             // LDS tile buffers
+constexpr int kRowC = kDL + 16;      // LDS bytes per latent row (padded: bank spread)
+constexpr int kRowP = 2 * kDR + 16;  // LDS bytes per positional row
+constexpr int kRowPr = 2 * kT + 16;  // LDS bytes per probability row
+constexpr float kRescaleSlack = 8.f;
 
-struct MlaMerge {
-  float acc[kMlaWaves][kMlaHeads][16][kMergePad];  // [wave][head][n][i]: O[head][32n + i]
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+struct MlaTileBuf {
+  alignas(16) uint8_t ckv[kT * kRowC];
+  alignas(16) uint8_t kpe[kT * kRowP];
+  alignas(16) int32_t valid[kT];
 };
-constexpr int kQRow = kDQ + 8;  // padded query row (bank spread of the operand reads)
-union MlaSmem {
-  uint16_t q[kMlaHeads][kQRow];  // query rows (bf16 bits), rows past num_heads zero
-  MlaMerge m;                    // used once every wave has left its tile loop
+struct MlaSmem {
+  MlaTileBuf tile[kBufs];
+  alignas(16) uint8_t prob[kMlaHeads * kRowPr];  // bf16 P[head][token] of the current tile
+  float red[kComputeWaves][kMlaHeads];           // per-wave tile maxima, then final sums
+  float red2[kComputeWaves][kMlaHeads];
 };
 
-// One 16-token half tile of one lane: K operands of token n (latent bytes
-// 64u + 16kg .. +16, u < 8; positional elements 32c + 8kg .. +8, c < 2) and
-// V operands of tokens 4kg + jj (latent bytes 32n .. 32n + 31).
-struct MlaHalf {
-  uint4 ck[8];
-  uint4 kp[2];
-  uint4 v[4][2];
+// A load wave's share of a tile (load wave v = 0..3), in whole cache lines
+// per load: latent load k (0..7) covers rows 8k + 2v and 8k + 2v + 1 (lane
+// l: row 8k + 2v + l/32, bytes 16 (l % 32) .. +16); positional load k
+// (0..1) covers rows 32k + 8v .. +8 (lane l: row 32k + 8v + l/8, bytes
+// 16 (l % 8)).
+struct MlaStage {
+  u32x4 c[8];
+  u32x4 r[2];
+  int ok;  // bit k: latent row k valid; bit 8 + k: positional row k valid
+};
+struct MlaRows {
+  int e[10];  // table entries of those rows (latent 0..7, positional 8..9)
 };
 
-__device__ __forceinline__ void load_k_half(const MlaArgs& p, int pb, int off, int lane, MlaHalf& h) {
-  const int bs = p.dims.block_size;
-  const int n = lane & 15, kg = lane >> 4;
-  const __amdgpu_buffer_rsrc_t rc = block_rsrc(p.ckv, (int64_t)bs * kDL, pb);
-  const __amdgpu_buffer_rsrc_t rp = block_rsrc(p.kpe, (int64_t)bs * kDR * 2, pb);
-#pragma unroll
-  for (int u = 0; u < 8; ++u) h.ck[u] = kv_load16<kStreamPolicy>(rc, (off + n) * kDL + 64 * u + 16 * kg);
-#pragma unroll
-  for (int c = 0; c < 2; ++c) h.kp[c] = kv_load16<kStreamPolicy>(rp, (off + n) * kDR * 2 + 64 * c + 16 * kg);
+__device__ __forceinline__ int lat_row(int k, int v, int lane) { return 8 * k + 2 * v + (lane >> 5); }
+__device__ __forceinline__ int pos_row(int k, int v, int lane) { return 32 * k + 8 * v + (lane >> 3); }
+
+__device__ __forceinline__ u32x4 ld_nt(const uint8_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
-__device__ __forceinline__ void load_v_half(const MlaArgs& p, int pb, int off, int lane, MlaHalf& h) {
-  const int bs = p.dims.block_size;
-  const int n = lane & 15, kg = lane >> 4;
-  const __amdgpu_buffer_rsrc_t rc = block_rsrc(p.ckv, (int64_t)bs * kDL, pb);
+
+// Table entries of this lane's rows of the tile starting at token ts.
+// Reads are clamped to the partition's last token (t1 - 1), so they stay
+// within the entries of the context; the values are first used by the tile's
+// loads, one tile later.
+__device__ __forceinline__ void load_entries(const int32_t* bt, int ts, int t1, int bs_log2, int v, int lane,
+                                             MlaRows& e) {
 #pragma unroll
-  for (int jj = 0; jj < 4; ++jj) {
-    h.v[jj][0] = kv_load16<kDefaultPolicy>(rc, (off + 4 * kg + jj) * kDL + 32 * n);
-    h.v[jj][1] = kv_load16<kDefaultPolicy>(rc, (off + 4 * kg + jj) * kDL + 32 * n + 16);
+  for (int k = 0; k < 8; ++k) e.e[k] = bt[min(ts + lat_row(k, v, lane), t1 - 1) >> bs_log2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) e.e[8 + k] = bt[min(ts + pos_row(k, v, lane), t1 - 1) >> bs_log2];
+}
+
+// Loads of this lane's share of the tile starting at ts; a row past the
+// partition end t1 or behind an out-of-range entry reads block 0, row 0.
+__device__ __forceinline__ void stage_load(const MlaArgs& p, int ts, int t1, int bs_log2, const MlaRows& e, int v,
+                                           int lane, MlaStage& st) {
+  const unsigned nb = (unsigned)p.dims.num_blocks;
+  const uint8_t* ckv = static_cast<const uint8_t*>(p.ckv);
+  const uint8_t* kpe = static_cast<const uint8_t*>(p.kpe);
+  int ok = 0;
+#pragma unroll
+  for (int k = 0; k < 10; ++k) {
+    const int tok = ts + (k < 8 ? lat_row(k, v, lane) : pos_row(k - 8, v, lane));
+    const bool good = tok < t1 && (unsigned)e.e[k] < nb;
+    const int64_t row = good ? ((int64_t)e.e[k] << bs_log2) + (tok & ((1 << bs_log2) - 1)) : 0;
+    if (k < 8)
+      st.c[k] = ld_nt(ckv + row * kDL + 16 * (lane & 31));
+    else
+      st.r[k - 8] = ld_nt(kpe + row * (2 * kDR) + 16 * (lane & 7));
+    ok |= (int)good << k;
   }
+  st.ok = ok;
 }
 
-// Latent score MFMA c (0..15): codes 8(c & 1) .. +7 of chunk c >> 1.
-__device__ __forceinline__ short8 latent_operand(const MlaHalf& h, int c) {
-  const uint4& q = h.ck[c >> 1];
-  const uint32_t w0 = (c & 1) ? q.z : q.x;
-  const uint32_t w1 = (c & 1) ? q.w : q.y;
+__device__ __forceinline__ void stage_store(const MlaStage& st, MlaTileBuf& tb, int v, int lane) {
+  const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const bool good = (st.ok >> k) & 1;
+    const int r = lat_row(k, v, lane);
+    *reinterpret_cast<u32x4*>(&tb.ckv[r * kRowC + 16 * (lane & 31)]) = good ? st.c[k] : z;
+    if ((lane & 31) == 0) tb.valid[r] = good;
+  }
+#pragma unroll
+  for (int k = 0; k < 2; ++k)
+    *reinterpret_cast<u32x4*>(&tb.kpe[pos_row(k, v, lane) * kRowP + 16 * (lane & 7)]) =
+        ((st.ok >> (8 + k)) & 1) ? st.r[k] : z;
+}
+
+__device__ __forceinline__ short8 fp8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
   return words_to_short8(fp8x2_to_bf16x2(w0), fp8x2_hi_to_bf16x2(w0), fp8x2_to_bf16x2(w1), fp8x2_hi_to_bf16x2(w1));
 }
 
-__device__ __forceinline__ uint32_t word_of(const uint4& q, int w) {
-  return w == 0 ? q.x : (w == 1 ? q.y : (w == 2 ? q.z : q.w));
-}
-// Codes i and i + 1 (i even) of rows jj and jj + 1, interleaved as
-// (row jj: i, row jj+1: i, row jj: i+1, row jj+1: i+1) by one byte permute.
-__device__ __forceinline__ uint32_t code_pairs(const MlaHalf& h, int jj, int i) {
-  const int s = i >> 4, w = (i >> 2) & 3;
-  const uint32_t sel = (i & 2) ? 0x07030602u : 0x05010400u;
-  return __builtin_amdgcn_perm(word_of(h.v[jj + 1][s], w), word_of(h.v[jj][s], w), sel);
+// Load waves: tiles 0 and 1 before the first barrier, then after each
+// tile's B2 the tile two ahead into the buffer the previous tile used (its
+// readers finished before this tile's B1) and a new load four ahead.  Tile
+// k sits in stage sa for even k, sb for odd k; entries run one tile ahead of
+// the loads that use them (ea even tiles, eb odd).  Tile starts past the
+// partition are clamped to its last token (their rows are invalid and read
+// block 0, row 0), so every load is unconditional and the memory counters
+// carried around the loop are exact.
+__device__ __forceinline__ void load_role(const MlaArgs& p, MlaSmem& sm, const int32_t* bt, int t0, int t1, int ntiles,
+                                          int bsl, int v, int lane) {
+  auto tile_start = [&](int k) { return min(t0 + k * kT, t1 - 1); };
+  MlaStage sa, sb;
+  MlaRows ea, eb;
+  load_entries(bt, tile_start(0), t1, bsl, v, lane, ea);
+  load_entries(bt, tile_start(1), t1, bsl, v, lane, eb);
+  stage_load(p, tile_start(0), t1, bsl, ea, v, lane, sa);
+  load_entries(bt, tile_start(2), t1, bsl, v, lane, ea);
+  __builtin_amdgcn_sched_barrier(0);
+  stage_load(p, tile_start(1), t1, bsl, eb, v, lane, sb);
+  load_entries(bt, tile_start(3), t1, bsl, v, lane, eb);
+  __builtin_amdgcn_sched_barrier(0);
+  stage_store(sa, sm.tile[0], v, lane);
+  stage_load(p, tile_start(2), t1, bsl, ea, v, lane, sa);
+  load_entries(bt, tile_start(4), t1, bsl, v, lane, ea);
+  __builtin_amdgcn_sched_barrier(0);
+  stage_store(sb, sm.tile[1], v, lane);
+  stage_load(p, tile_start(3), t1, bsl, eb, v, lane, sb);
+  load_entries(bt, tile_start(5), t1, bsl, v, lane, eb);
+  __syncthreads();  // tiles 0 and 1 in LDS
+
+  auto step = [&](int tau, MlaStage& st, MlaRows& et) {
+    __syncthreads();  // B1
+    __syncthreads();  // B2
+    stage_store(st, sm.tile[(tau + 2) % kBufs], v, lane);
+    MlaRows cur = et;
+    load_entries(bt, tile_start(tau + 6), t1, bsl, v, lane, et);
+    __builtin_amdgcn_sched_barrier(0);  // entry loads ahead of the tile loads (counter order)
+    stage_load(p, tile_start(tau + 4), t1, bsl, cur, v, lane, st);
+  };
+  int tau = 0;
+  for (; tau + 1 < ntiles; tau += 2) {
+    step(tau, sa, ea);
+    step(tau + 1, sb, eb);
+  }
+  if (tau < ntiles) step(tau, sa, ea);
+  __syncthreads();  // final sums
+  __builtin_amdgcn_s_waitcnt(0);  // drain the prefetches past the end before leaving
 }
 
-// Query operands come from LDS at each use: held in registers they would
-// push the tile's loads out of the register file.
-__device__ __forceinline__ void half_scores(const MlaHalf& h, const uint16_t* qrow, int kg, float4v& s_lat,
-                                            float4v& s_pe) {
-  s_lat = (float4v){0.f, 0.f, 0.f, 0.f};
-  s_pe = (float4v){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int c = 0; c < 16; ++c) {
-    const short8 qb = *reinterpret_cast<const short8*>(qrow + 64 * (c >> 1) + 16 * kg + 8 * (c & 1));
-    s_lat = __builtin_amdgcn_mfma_f32_16x16x32_bf16(latent_operand(h, c), qb, s_lat, 0, 0, 0);
-  }
-#pragma unroll
-  for (int c = 0; c < 2; ++c) {
-    const short8 qb = *reinterpret_cast<const short8*>(qrow + kDL + 32 * c + 8 * kg);
-    s_pe = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(short8, h.kp[c]), qb, s_pe, 0, 0, 0);
-  }
-}
-
-__global__ __launch_bounds__(kDecodeThreads, 1) void paged_mla_kernel(MlaArgs p) {
+__global__ __launch_bounds__(kMlaThreads, 1) void paged_mla_kernel(MlaArgs p) {
   __shared__ MlaSmem sm;
-  __shared__ float s_m[kMlaWaves][kMlaHeads], s_l[kMlaWaves][kMlaHeads], s_le[kMlaWaves][kMlaHeads];
   const int b = blockIdx.y;
   const int part = blockIdx.x;
   const int lane = threadIdx.x & (kWaveSize - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWaveSize);
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWaveSize);
+  const int n = lane & 15, kg = lane >> 4;
   const int H = p.dims.num_heads;
-  const int bs = p.dims.block_size;
+  const int bsl = __builtin_ctz(p.dims.block_size);  // block_size is a power of two
   int ctx = p.context_lens[b];
   ctx = ctx < 0 ? 0 : (ctx > p.max_context_len ? p.max_context_len : ctx);
   ctx = __builtin_amdgcn_readfirstlane(ctx);
   const int PS = p.partition_size;
   const int nparts = ctx == 0 ? 1 : (ctx + PS - 1) / PS;
   if (part >= nparts) return;  // whole workgroup, before any barrier
-
-  const float s_ckv = p.ckv_scale ? p.ckv_scale[0] : 1.f;
-  const float sl2 = p.softmax_scale * kLog2e;
   const int t0 = part * PS;
   const int t1 = min(ctx, t0 + PS);
-  const int32_t* bt = p.block_tables + (int64_t)b * p.dims.max_blocks_per_seq;
-  const unsigned nb = (unsigned)p.dims.num_blocks;
-  // Block and in-block offset of the half tile starting at token t; block -1
-  // when t is past the partition or the table entry is out of range (the
-  // loads then read block 0 and the tokens are masked).
-  auto half_at = [&](int t, int& pb, int& off) {
-    off = t % bs;
-    pb = -1;
-    if (t < t1) {
-      const int id = __builtin_amdgcn_readfirstlane(bt[t / bs]);
-      pb = (unsigned)id < nb ? id : -1;
-    }
-  };
-  constexpr int kStride = kMlaWaves * kTile;
-  MlaHalf hx, hy;
-  int px, ox, py, oy;
-  const int tw = t0 + wave * kTile;
-  half_at(tw, px, ox);
-  half_at(tw + 16, py, oy);
-  // The sequence's query rows (latent then positional) into LDS, loaded
-  // ahead of the first tile's K/V loads (which overlap the staging).
-  {
-    constexpr int kChunks = kMlaHeads * kDQ / 8;
-    constexpr int kPer = (kChunks + kDecodeThreads - 1) / kDecodeThreads;
-    const uint16_t* ql = static_cast<const uint16_t*>(p.q_latent) + (int64_t)b * H * kDL;
-    const uint16_t* qp = static_cast<const uint16_t*>(p.q_pe) + (int64_t)b * H * kDR;
-    uint4 v[kPer];
+  const int ntiles = t1 > t0 ? (t1 - t0 + kT - 1) / kT : 0;
+  if (ntiles == 0) {  // an empty context (its one partition): zeros, LSE -inf
+    if (w < kComputeWaves) {
 #pragma unroll
-    for (int k = 0; k < kPer; ++k) {  // unconditional loads (clamped rows), zeroed after
-      const int i = min(threadIdx.x + k * kDecodeThreads, kChunks - 1);
-      const int row = i / (kDQ / 8);
-      const int col = 8 * (i - row * (kDQ / 8));
-      const int r = min(row, H - 1);
-      v[k] = col < kDL ? *reinterpret_cast<const uint4*>(ql + r * kDL + col)
-                       : *reinterpret_cast<const uint4*>(qp + r * kDR + (col - kDL));
+      for (int j = 0; j < 4; ++j) {
+        const int h = 4 * kg + j;
+        if (h < H) {
+          const int64_t orow = (int64_t)b * H + h;
+          *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.out) + orow * kDL + 128 * w + 8 * n) =
+              make_uint4(0, 0, 0, 0);
+          if (w == 0 && n == 0 && p.out_lse) p.out_lse[orow] = -INFINITY;
+        }
+      }
     }
-    // The first tile's loads follow, unconditionally (a wave with no tile
-    // reads block 0 and never uses it), so that storing the query rows waits
-    // for the query loads alone.
-    __builtin_amdgcn_sched_barrier(0);
-    load_k_half(p, px < 0 ? 0 : px, px < 0 ? 0 : ox, lane, hx);
-    load_k_half(p, py < 0 ? 0 : py, py < 0 ? 0 : oy, lane, hy);
-    load_v_half(p, px < 0 ? 0 : px, px < 0 ? 0 : ox, lane, hx);
-    load_v_half(p, py < 0 ? 0 : py, py < 0 ? 0 : oy, lane, hy);
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-      const int i = threadIdx.x + k * kDecodeThreads;
-      const int row = i / (kDQ / 8);
-      const int col = 8 * (i - row * (kDQ / 8));
-      if (i < kChunks) *reinterpret_cast<uint4*>(&sm.q[row][col]) = row < H ? v[k] : make_uint4(0, 0, 0, 0);
-    }
+    return;
   }
-  __syncthreads();
-  const int n = lane & 15, kg = lane >> 4;
-  const uint16_t* qrow = &sm.q[n][0];
+  const int32_t* bt = p.block_tables + (int64_t)b * p.dims.max_blocks_per_seq;
+  if (w >= kComputeWaves) {
+    load_role(p, sm, bt, t0, t1, ntiles, bsl, w - kComputeWaves, lane);
+    return;
+  }
 
+  // ---- compute waves ----
+  const float s_ckv = p.ckv_scale ? p.ckv_scale[0] : 1.f;
+  const float sl2 = p.softmax_scale * kLog2e;
+  // Query operands of head n: latent MFMA c reads elements 64(c>>1) + 16kg
+  // + 8(c&1) .. +8, positional MFMA c 32c + 8kg .. +8.  Columns n >= H repeat
+  // the last head (finite values whose rows are never written out).
+  short8 qb[18];
+  {
+    const int hq = min(n, H - 1);
+    const uint16_t* ql = static_cast<const uint16_t*>(p.q_latent) + ((int64_t)b * H + hq) * kDL;
+    const uint16_t* qp = static_cast<const uint16_t*>(p.q_pe) + ((int64_t)b * H + hq) * kDR;
+#pragma unroll
+    for (int c = 0; c < 16; ++c) qb[c] = *reinterpret_cast<const short8*>(ql + 64 * (c >> 1) + 16 * kg + 8 * (c & 1));
+#pragma unroll
+    for (int c = 0; c < 2; ++c) qb[16 + c] = *reinterpret_cast<const short8*>(qp + 32 * c + 8 * kg);
+  }
   float m = -INFINITY, lsum = 0.f, lsum_e = 0.f;
-  float4v acc[32];
+  float4v acc[8];
 #pragma unroll
-  for (int i = 0; i < 32; ++i) acc[i] = (float4v){0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < 8; ++i) acc[i] = (float4v){0.f, 0.f, 0.f, 0.f};
+  __syncthreads();  // tiles 0 and 1 in LDS
 
-  for (int t = tw; t < t1; t += kStride) {
-    float4v lx, ex, ly, ey;
-    half_scores(hx, qrow, kg, lx, ex);
-    half_scores(hy, qrow, kg, ly, ey);
-    const bool xval = px >= 0, yval = py >= 0;
-    int nx, nox, ny, noy;
-    half_at(t + kStride, nx, nox);
-    half_at(t + kStride + 16, ny, noy);
-    const bool more = t + kStride < t1;
-    if (more) {  // next tile's K operands while this tile finishes
-      load_k_half(p, nx < 0 ? 0 : nx, nx < 0 ? 0 : nox, lane, hx);
-      load_k_half(p, ny < 0 ? 0 : ny, ny < 0 ? 0 : noy, lane, hy);
-    }
-    float s[8];
+  for (int tau = 0; tau < ntiles; ++tau) {
+    const MlaTileBuf& tb = sm.tile[tau % kBufs];
+    float4v sl = {0.f, 0.f, 0.f, 0.f}, se = {0.f, 0.f, 0.f, 0.f};
+    {
+      const uint8_t* krow = &tb.ckv[(16 * w + n) * kRowC + 16 * kg];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      s[j] = (xval && t + 4 * kg + j < t1) ? sl2 * fmaf(s_ckv, lx[j], ex[j]) : -INFINITY;
-      s[4 + j] = (yval && t + 16 + 4 * kg + j < t1) ? sl2 * fmaf(s_ckv, ly[j], ey[j]) : -INFINITY;
-    }
+      for (int u = 0; u < 8; ++u) {
+        const u32x4 k = *reinterpret_cast<const u32x4*>(krow + 64 * u);
+        sl = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16x8(k.x, k.y), qb[2 * u], sl, 0, 0, 0);
+        sl = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16x8(k.z, k.w), qb[2 * u + 1], sl, 0, 0, 0);
+      }
+      const uint8_t* prow = &tb.kpe[(16 * w + n) * kRowP + 16 * kg];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {  // masked rows may hold any bytes (NaN codes)
-      if (s[j] == -INFINITY) hx.v[j][0] = hx.v[j][1] = make_uint4(0, 0, 0, 0);
-      if (s[4 + j] == -INFINITY) hy.v[j][0] = hy.v[j][1] = make_uint4(0, 0, 0, 0);
+      for (int c = 0; c < 2; ++c)
+        se = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const short8*>(prow + 64 * c), qb[16 + c], se,
+                                                     0, 0, 0);
     }
-    // Running reference max, moved only when a score passes it by more than
-    // kRescaleSlack (log2 units): probabilities stay <= 2^kRescaleSlack, and
-    // the accumulators are rescaled only on such a jump (any reference gives
-    // the same normalised result and LSE).
-    float tmax = s[0];
-#pragma unroll
-    for (int j = 1; j < 8; ++j) tmax = fmaxf(tmax, s[j]);
-    tmax = max4(tmax);
+    const int4 ok = *reinterpret_cast<const int4*>(&tb.valid[16 * w + 4 * kg]);
+    float s[4];
+    s[0] = ok.x ? sl2 * fmaf(s_ckv, sl[0], se[0]) : -INFINITY;
+    s[1] = ok.y ? sl2 * fmaf(s_ckv, sl[1], se[1]) : -INFINITY;
+    s[2] = ok.z ? sl2 * fmaf(s_ckv, sl[2], se[2]) : -INFINITY;
+    s[3] = ok.w ? sl2 * fmaf(s_ckv, sl[3], se[3]) : -INFINITY;
+    const float wmax = max4(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])));
+    if (kg == 0) sm.red[w][n] = wmax;
+    __syncthreads();  // B1
+    // Shared reference max (the same in every wave), moved only when a score
+    // passes it by more than kRescaleSlack (log2 units): probabilities stay
+    // <= 2^kRescaleSlack and the accumulators are rescaled only on a jump.
+    const float tmax = fmaxf(fmaxf(sm.red[0][n], sm.red[1][n]), fmaxf(sm.red[2][n], sm.red[3][n]));
     const float mn = tmax > m + kRescaleSlack ? tmax : m;
     const float ms = mn == -INFINITY ? 0.f : mn;
     const float alpha = fast_exp2(m - ms);
     const bool rescale = m != -INFINITY && mn != m;
     m = mn;
-    uint32_t pw[4];
-    float psum = 0.f, psum_e = 0.f;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const float p0 = fast_exp2(s[2 * k] - ms);
-      const float p1 = fast_exp2(s[2 * k + 1] - ms);
-      pw[k] = pack_bf16(p0, p1);
-      psum += bf16_lo(pw[k]) + bf16_hi(pw[k]);
-      psum_e += p0 + p1;
-    }
-    lsum = lsum * alpha + psum;
-    lsum_e = lsum_e * alpha + psum_e;
+    const float p0 = fast_exp2(s[0] - ms), p1 = fast_exp2(s[1] - ms);
+    const float p2 = fast_exp2(s[2] - ms), p3 = fast_exp2(s[3] - ms);
+    const uint32_t pw0 = pack_bf16(p0, p1), pw1 = pack_bf16(p2, p3);
+    *reinterpret_cast<uint2*>(&sm.prob[n * kRowPr + (16 * w + 4 * kg) * 2]) = make_uint2(pw0, pw1);
+    lsum = lsum * alpha + ((bf16_lo(pw0) + bf16_hi(pw0)) + (bf16_lo(pw1) + bf16_hi(pw1)));
+    lsum_e = lsum_e * alpha + ((p0 + p1) + (p2 + p3));
     if (__any(rescale)) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const float aj = __shfl(alpha, 4 * kg + j);
 #pragma unroll
-        for (int i = 0; i < 32; ++i) acc[i][j] *= aj;
+        for (int i = 0; i < 8; ++i) acc[i][j] *= aj;
       }
     }
-    const short8 pa = words_to_short8(pw[0], pw[1], pw[2], pw[3]);
+    __syncthreads();  // B2
 #pragma unroll
-    for (int i = 0; i < 32; i += 2) {
-      const uint32_t a0 = code_pairs(hx, 0, i), a1 = code_pairs(hx, 2, i);
-      const uint32_t a2 = code_pairs(hy, 0, i), a3 = code_pairs(hy, 2, i);
-      const short8 v0 = words_to_short8(fp8x2_to_bf16x2(a0), fp8x2_to_bf16x2(a1), fp8x2_to_bf16x2(a2),
-                                        fp8x2_to_bf16x2(a3));
-      const short8 v1 = words_to_short8(fp8x2_hi_to_bf16x2(a0), fp8x2_hi_to_bf16x2(a1), fp8x2_hi_to_bf16x2(a2),
-                                        fp8x2_hi_to_bf16x2(a3));
-      acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, v0, acc[i], 0, 0, 0);
-      acc[i + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, v1, acc[i + 1], 0, 0, 0);
+    for (int s32 = 0; s32 < 2; ++s32) {  // two 32-token steps
+      const short8 pa = *reinterpret_cast<const short8*>(&sm.prob[n * kRowPr + (32 * s32 + 8 * kg) * 2]);
+      uint2 vr[8];  // codes 128w + 8n .. +8 of rows 32 s32 + 8kg + e
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        vr[e] = *reinterpret_cast<const uint2*>(&tb.ckv[(32 * s32 + 8 * kg + e) * kRowC + 128 * w + 8 * n]);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int i2 = 0; i2 < 2; ++i2) {
+          // codes i = 4h + 2 i2 and i + 1 of rows (2 e2, 2 e2 + 1), interleaved
+          const uint32_t sel = i2 ? 0x07030602u : 0x05010400u;
+          uint32_t q[4];
+#pragma unroll
+          for (int e2 = 0; e2 < 4; ++e2)
+            q[e2] = __builtin_amdgcn_perm(h ? vr[2 * e2 + 1].y : vr[2 * e2 + 1].x, h ? vr[2 * e2].y : vr[2 * e2].x, sel);
+          const int i = 4 * h + 2 * i2;
+          const short8 b0 = words_to_short8(fp8x2_to_bf16x2(q[0]), fp8x2_to_bf16x2(q[1]), fp8x2_to_bf16x2(q[2]),
+                                            fp8x2_to_bf16x2(q[3]));
+          const short8 b1 = words_to_short8(fp8x2_hi_to_bf16x2(q[0]), fp8x2_hi_to_bf16x2(q[1]),
+                                            fp8x2_hi_to_bf16x2(q[2]), fp8x2_hi_to_bf16x2(q[3]));
+          acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, b0, acc[i], 0, 0, 0);
+          acc[i + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, b1, acc[i + 1], 0, 0, 0);
+        }
+      }
     }
-    if (more) {
-      load_v_half(p, nx < 0 ? 0 : nx, nx < 0 ? 0 : nox, lane, hx);
-      load_v_half(p, ny < 0 ? 0 : ny, ny < 0 ? 0 : noy, lane, hy);
-    }
-    px = nx;
-    ox = nox;
-    py = ny;
-    oy = noy;
   }
 
-  // Combine the four waves.  Head h's max and sums sit in lanes h, h + 16,
-  // h + 32, h + 48 of the score layout (the same value after the reductions);
-  // acc[i][j] holds O[head 4kg + j][32n + i].
+  // Final sums over the compute waves (each summed its own tokens; all share m).
   const float ls = sum4(lsum), le = sum4(lsum_e);
-  if (lane < kMlaHeads) {
-    s_m[wave][lane] = m;
-    s_l[wave][lane] = ls;
-    s_le[wave][lane] = le;
+  if (kg == 0) {
+    sm.red[w][n] = ls;
+    sm.red2[w][n] = le;
   }
-  __syncthreads();
+  __syncthreads();  // final sums (the load waves join it)
+  const bool whole = nparts == 1;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int h = 4 * kg + j;
-    float M = s_m[0][h];
-#pragma unroll
-    for (int w = 1; w < kMlaWaves; ++w) M = fmaxf(M, s_m[w][h]);
-    const float f = fast_exp2(s_m[wave][h] - (M == -INFINITY ? 0.f : M));
+    const float L = (sm.red[0][h] + sm.red[1][h]) + (sm.red[2][h] + sm.red[3][h]);
+    const float Le = (sm.red2[0][h] + sm.red2[1][h]) + (sm.red2[2][h] + sm.red2[3][h]);
+    const float mh = __shfl(m, h);
     if (h < H) {
-      float* dst = &sm.m.acc[wave][h][n][0];
+      const float inv = L > 0.f ? s_ckv / L : 0.f;
+      const int64_t orow = (int64_t)b * H + h;
+      const int col = 128 * w + 8 * n;
+      const float lse = Le > 0.f ? (mh + fast_log2(Le)) * kLn2 : -INFINITY;
+      if (whole) {
+        uint32_t o[4];
 #pragma unroll
-      for (int i = 0; i < 32; i += 4)
-        *reinterpret_cast<float4*>(dst + i) =
-            make_float4(acc[i][j] * f, acc[i + 1][j] * f, acc[i + 2][j] * f, acc[i + 3][j] * f);
-    }
-  }
-  __syncthreads();
-  const bool whole = nparts == 1;
-  for (int e = threadIdx.x; e < H * (kDL / 2); e += kDecodeThreads) {  // two elements each
-    const int h = e / (kDL / 2);
-    const int d = 2 * (e - h * (kDL / 2));
-    float M = s_m[0][h];
-#pragma unroll
-    for (int w = 1; w < kMlaWaves; ++w) M = fmaxf(M, s_m[w][h]);
-    const float Ms = M == -INFINITY ? 0.f : M;
-    float L = 0.f, Le = 0.f, o0 = 0.f, o1 = 0.f;
-#pragma unroll
-    for (int w = 0; w < kMlaWaves; ++w) {
-      const float f = fast_exp2(s_m[w][h] - Ms);
-      L = fmaf(s_l[w][h], f, L);
-      Le = fmaf(s_le[w][h], f, Le);
-      const float2 v = *reinterpret_cast<const float2*>(&sm.m.acc[w][h][d >> 5][d & 31]);
-      o0 += v.x;
-      o1 += v.y;
-    }
-    const float inv = L > 0.f ? s_ckv / L : 0.f;
-    const int64_t orow = (int64_t)b * H + h;
-    const float lse = Le > 0.f ? (M + fast_log2(Le)) * kLn2 : -INFINITY;
-    if (whole) {
-      uint16_t* dst = static_cast<uint16_t*>(p.out) + orow * kDL + d;
-      *reinterpret_cast<uint32_t*>(dst) = (uint32_t)f32_to_bf16_rne(o0 * inv) | ((uint32_t)f32_to_bf16_rne(o1 * inv) << 16);
-      if (d == 0 && p.out_lse) p.out_lse[orow] = lse;
-    } else {
-      const int64_t prow = orow * p.max_partitions + part;
-      *reinterpret_cast<float2*>(p.part_out + prow * kDL + d) = make_float2(o0 * inv, o1 * inv);
-      if (d == 0) p.part_lse[prow] = lse;
+        for (int e = 0; e < 4; ++e)
+          o[e] = (uint32_t)f32_to_bf16_rne(acc[2 * e][j] * inv) |
+                 ((uint32_t)f32_to_bf16_rne(acc[2 * e + 1][j] * inv) << 16);
+        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.out) + orow * kDL + col) = make_uint4(o[0], o[1], o[2], o[3]);
+        if (w == 0 && n == 0 && p.out_lse) p.out_lse[orow] = lse;
+      } else {
+        const int64_t prow = orow * p.max_partitions + part;
+        float* dst = p.part_out + prow * kDL + col;
+        *reinterpret_cast<float4*>(dst) = make_float4(acc[0][j] * inv, acc[1][j] * inv, acc[2][j] * inv, acc[3][j] * inv);
+        *reinterpret_cast<float4*>(dst + 4) =
+            make_float4(acc[4][j] * inv, acc[5][j] * inv, acc[6][j] * inv, acc[7][j] * inv);
+        if (w == 0 && n == 0) p.part_lse[prow] = lse;
+      }
     }
   }
 }
@@ -341,11 +372,11 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void paged_mla_kernel(MlaArgs p)
 
 bool mla_supported(lgm_dtype ckv, int latent_dim, int rope_dim, int num_heads, int block_size) {
   return ckv == LGM_FP8_E4M3 && latent_dim == kDL && rope_dim == kDR && num_heads >= 1 && num_heads <= kMlaHeads &&
-         block_size >= 16 && block_size % 16 == 0;
+         block_size >= 1 && (block_size & (block_size - 1)) == 0;
 }
 
 hipError_t launch_paged_mla(const MlaArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(paged_mla_kernel, dim3(a.max_partitions, a.dims.num_seqs), dim3(kDecodeThreads), 0, s, a);
+  hipLaunchKernelGGL(paged_mla_kernel, dim3(a.max_partitions, a.dims.num_seqs), dim3(kMlaThreads), 0, s, a);
   return hipGetLastError();
 }
 

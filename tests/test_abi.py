@@ -332,7 +332,7 @@ MLA_BAD = [
     (dict(dims=mla_dims(rope_dim=32)), UNS, "rope_dim"),
     (dict(dims=mla_dims(num_heads=17)), UNS, "num_heads"),
     (dict(dims=mla_dims(num_heads=0)), INV, "num_heads"),
-    (dict(dims=mla_dims(block_size=8, max_blocks_per_seq=6400)), UNS, "block_size"),
+    (dict(dims=mla_dims(block_size=48, max_blocks_per_seq=1100)), UNS, "block_size"),
     (dict(dims=mla_dims(block_size=24, max_blocks_per_seq=3000)), UNS, "block_size"),
     (dict(dims=mla_dims(num_seqs=-1)), INV, "num_seqs"),
     (dict(dims=mla_dims(num_seqs=70000)), UNS, "num_seqs"),

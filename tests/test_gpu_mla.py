@@ -71,7 +71,7 @@ def _check(w, out, lse, seqs=None):
 
 
 @pytest.mark.parametrize("ps", [0, 32, 96, 832, 4096])
-@pytest.mark.parametrize("bs", [64, 16])
+@pytest.mark.parametrize("bs", [64, 16, 1])
 def test_ragged_page_and_split_edges(ps, bs):
     """Contexts around page ends (block_size +-1) and partitions that end
     inside pages (96 with pages of 64, 832 = 13 pages, 32 inside pages of 64)."""
