@@ -7,11 +7,12 @@
 // Every query head attends to the same latent rows.  One workgroup takes one
 // (sequence, partition) and walks it in 64-token tiles held in LDS.  Its
 // eight waves have two roles:
-//   load waves (4..7) gather the tiles through the block table into
-//           registers and store them into one of three LDS tile buffers,
-//           two tiles ahead of the compute waves, so that HBM reads overlap
-//           the matrix work; invalid rows (past the partition, or behind an
-//           out-of-range table entry) are stored as zeros and masked.
+//   load waves (4..7) gather the tiles through the block table into three
+//           register stages and store them into one of three LDS tile
+//           buffers two tiles ahead of the compute waves (loads are issued
+//           five tiles ahead), so that HBM reads overlap the matrix work;
+//           invalid rows (past the partition, or behind an out-of-range table
+//           entry) are stored as zeros and masked.
 //   compute waves (0..3), v_mfma_f32_16x16x32_bf16, lane l = 16 kg + n:
 //     scores  wave w scores tokens 16w .. 16w+15 for all heads (up to 16,
 //             the MFMA columns): S^T[token][head] = K[token][576] Q^T, 16
@@ -76,10 +77,6 @@ struct MlaStage {
   u32x4 r[2];
   int ok;  // bit k: latent row k valid; bit 8 + k: positional row k valid
 };
-struct MlaRows {
-  int e[10];  // table entries of those rows (latent 0..7, positional 8..9)
-};
-
 __device__ __forceinline__ int lat_row(int k, int v, int lane) { return 8 * k + 2 * v + (lane >> 5); }
 __device__ __forceinline__ int pos_row(int k, int v, int lane) { return 32 * k + 8 * v + (lane >> 3); }
 
@@ -87,31 +84,30 @@ __device__ __forceinline__ u32x4 ld_nt(const uint8_t* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 
-// Table entries of this lane's rows of the tile starting at token ts.
-// Reads are clamped to the partition's last token (t1 - 1), so they stay
-// within the entries of the context; the values are first used by the tile's
-// loads, one tile later.
-__device__ __forceinline__ void load_entries(const int32_t* bt, int ts, int t1, int bs_log2, int v, int lane,
-                                             MlaRows& e) {
-#pragma unroll
-  for (int k = 0; k < 8; ++k) e.e[k] = bt[min(ts + lat_row(k, v, lane), t1 - 1) >> bs_log2];
-#pragma unroll
-  for (int k = 0; k < 2; ++k) e.e[8 + k] = bt[min(ts + pos_row(k, v, lane), t1 - 1) >> bs_log2];
+// Table entry of row `lane` of the tile starting at token ts (one load per
+// lane; the rows a lane gathers take theirs from the lane of that row).  The
+// read is clamped to the partition's last token (t1 - 1), so it stays within
+// the entries of the context; the value is first used one tile later.
+__device__ __forceinline__ int load_entry(const int32_t* bt, int ts, int t1, int bs_log2, int lane) {
+  return bt[min(ts + lane, t1 - 1) >> bs_log2];
 }
 
 // Loads of this lane's share of the tile starting at ts; a row past the
 // partition end t1 or behind an out-of-range entry reads block 0, row 0.
-__device__ __forceinline__ void stage_load(const MlaArgs& p, int ts, int t1, int bs_log2, const MlaRows& e, int v,
-                                           int lane, MlaStage& st) {
+__device__ __forceinline__ void stage_load(const MlaArgs& p, int ts, int t1, int bs_log2, int entry, int v, int lane,
+                                           MlaStage& st) {
   const unsigned nb = (unsigned)p.dims.num_blocks;
   const uint8_t* ckv = static_cast<const uint8_t*>(p.ckv);
   const uint8_t* kpe = static_cast<const uint8_t*>(p.kpe);
+  int e[10];  // every row's entry first: one LDS round trip for all ten
+#pragma unroll
+  for (int k = 0; k < 10; ++k) e[k] = __shfl(entry, k < 8 ? lat_row(k, v, lane) : pos_row(k - 8, v, lane));
   int ok = 0;
 #pragma unroll
   for (int k = 0; k < 10; ++k) {
     const int tok = ts + (k < 8 ? lat_row(k, v, lane) : pos_row(k - 8, v, lane));
-    const bool good = tok < t1 && (unsigned)e.e[k] < nb;
-    const int64_t row = good ? ((int64_t)e.e[k] << bs_log2) + (tok & ((1 << bs_log2) - 1)) : 0;
+    const bool good = tok < t1 && (unsigned)e[k] < nb;
+    const int64_t row = good ? ((int64_t)e[k] << bs_log2) + (tok & ((1 << bs_log2) - 1)) : 0;
     if (k < 8)
       st.c[k] = ld_nt(ckv + row * kDL + 16 * (lane & 31));
     else
@@ -124,67 +120,72 @@ __device__ __forceinline__ void stage_load(const MlaArgs& p, int ts, int t1, int
 __device__ __forceinline__ void stage_store(const MlaStage& st, MlaTileBuf& tb, int v, int lane) {
   const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const bool good = (st.ok >> k) & 1;
-    const int r = lat_row(k, v, lane);
-    *reinterpret_cast<u32x4*>(&tb.ckv[r * kRowC + 16 * (lane & 31)]) = good ? st.c[k] : z;
-    if ((lane & 31) == 0) tb.valid[r] = good;
-  }
+  for (int k = 0; k < 8; ++k)
+    *reinterpret_cast<u32x4*>(&tb.ckv[lat_row(k, v, lane) * kRowC + 16 * (lane & 31)]) =
+        ((st.ok >> k) & 1) ? st.c[k] : z;
 #pragma unroll
   for (int k = 0; k < 2; ++k)
     *reinterpret_cast<u32x4*>(&tb.kpe[pos_row(k, v, lane) * kRowP + 16 * (lane & 7)]) =
         ((st.ok >> (8 + k)) & 1) ? st.r[k] : z;
+  if ((lane & 31) == 0) {  // one lane per latent row writes its flag
+#pragma unroll
+    for (int k = 0; k < 8; ++k) tb.valid[lat_row(k, v, lane)] = (st.ok >> k) & 1;
+  }
 }
 
 __device__ __forceinline__ short8 fp8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
   return words_to_short8(fp8x2_to_bf16x2(w0), fp8x2_hi_to_bf16x2(w0), fp8x2_to_bf16x2(w1), fp8x2_hi_to_bf16x2(w1));
 }
 
-// Load waves: tiles 0 and 1 before the first barrier, then after each
-// tile's B2 the tile two ahead into the buffer the previous tile used (its
-// readers finished before this tile's B1) and a new load four ahead.  Tile
-// k sits in stage sa for even k, sb for odd k; entries run one tile ahead of
-// the loads that use them (ea even tiles, eb odd).  Tile starts past the
-// partition are clamped to its last token (their rows are invalid and read
-// block 0, row 0), so every load is unconditional and the memory counters
-// carried around the loop are exact.
+// Load waves: tiles 0 and 1 in LDS before the first barrier, then after
+// each tile's B2 the tile two ahead into the buffer the previous tile used
+// (its readers finished before this tile's B1), and a new load five ahead.
+// Tile k sits in register stage k % 3; the table entries of its rows (one
+// per lane) are loaded one step before the tile.  Tile starts past the partition are
+// clamped to its last token (their rows are invalid and read block 0, row
+// 0), so every load is unconditional and the memory counters carried around
+// the loop are exact.
 __device__ __forceinline__ void load_role(const MlaArgs& p, MlaSmem& sm, const int32_t* bt, int t0, int t1, int ntiles,
                                           int bsl, int v, int lane) {
   auto tile_start = [&](int k) { return min(t0 + k * kT, t1 - 1); };
-  MlaStage sa, sb;
-  MlaRows ea, eb;
-  load_entries(bt, tile_start(0), t1, bsl, v, lane, ea);
-  load_entries(bt, tile_start(1), t1, bsl, v, lane, eb);
-  stage_load(p, tile_start(0), t1, bsl, ea, v, lane, sa);
-  load_entries(bt, tile_start(2), t1, bsl, v, lane, ea);
+  MlaStage s0, s1, s2;
+  int e0 = load_entry(bt, tile_start(0), t1, bsl, lane);
+  int e1 = load_entry(bt, tile_start(1), t1, bsl, lane);
+  int e2 = load_entry(bt, tile_start(2), t1, bsl, lane);
+  stage_load(p, tile_start(0), t1, bsl, e0, v, lane, s0);
+  e0 = load_entry(bt, tile_start(3), t1, bsl, lane);
   __builtin_amdgcn_sched_barrier(0);
-  stage_load(p, tile_start(1), t1, bsl, eb, v, lane, sb);
-  load_entries(bt, tile_start(3), t1, bsl, v, lane, eb);
+  stage_load(p, tile_start(1), t1, bsl, e1, v, lane, s1);
+  e1 = load_entry(bt, tile_start(4), t1, bsl, lane);
   __builtin_amdgcn_sched_barrier(0);
-  stage_store(sa, sm.tile[0], v, lane);
-  stage_load(p, tile_start(2), t1, bsl, ea, v, lane, sa);
-  load_entries(bt, tile_start(4), t1, bsl, v, lane, ea);
+  stage_load(p, tile_start(2), t1, bsl, e2, v, lane, s2);
+  e2 = load_entry(bt, tile_start(5), t1, bsl, lane);
   __builtin_amdgcn_sched_barrier(0);
-  stage_store(sb, sm.tile[1], v, lane);
-  stage_load(p, tile_start(3), t1, bsl, eb, v, lane, sb);
-  load_entries(bt, tile_start(5), t1, bsl, v, lane, eb);
+  stage_store(s0, sm.tile[0], v, lane);
+  stage_load(p, tile_start(3), t1, bsl, e0, v, lane, s0);
+  __builtin_amdgcn_sched_barrier(0);
+  stage_store(s1, sm.tile[1], v, lane);
+  stage_load(p, tile_start(4), t1, bsl, e1, v, lane, s1);
   __syncthreads();  // tiles 0 and 1 in LDS
 
-  auto step = [&](int tau, MlaStage& st, MlaRows& et) {
+  // Step tau: stage st holds tile tau+2 and entry eu that of tile tau+5;
+  // el (free) takes that of tile tau+6.
+  auto step = [&](int tau, MlaStage& st, int& eu, int& el) {
     __syncthreads();  // B1
     __syncthreads();  // B2
     stage_store(st, sm.tile[(tau + 2) % kBufs], v, lane);
-    MlaRows cur = et;
-    load_entries(bt, tile_start(tau + 6), t1, bsl, v, lane, et);
-    __builtin_amdgcn_sched_barrier(0);  // entry loads ahead of the tile loads (counter order)
-    stage_load(p, tile_start(tau + 4), t1, bsl, cur, v, lane, st);
+    el = load_entry(bt, tile_start(tau + 6), t1, bsl, lane);
+    __builtin_amdgcn_sched_barrier(0);  // entry load ahead of the tile loads (counter order)
+    stage_load(p, tile_start(tau + 5), t1, bsl, eu, v, lane, st);
   };
   int tau = 0;
-  for (; tau + 1 < ntiles; tau += 2) {
-    step(tau, sa, ea);
-    step(tau + 1, sb, eb);
+  for (; tau + 2 < ntiles; tau += 3) {
+    step(tau, s2, e2, e0);
+    step(tau + 1, s0, e0, e1);
+    step(tau + 2, s1, e1, e2);
   }
-  if (tau < ntiles) step(tau, sa, ea);
+  if (tau < ntiles) step(tau, s2, e2, e0);
+  if (tau + 1 < ntiles) step(tau + 1, s0, e0, e1);
   __syncthreads();  // final sums
   __builtin_amdgcn_s_waitcnt(0);  // drain the prefetches past the end before leaving
 }
