@@ -111,6 +111,16 @@ def test_full_size_every_latent_window(ps):
     assert win.shape == (64,) and np.all(win <= TOL)
 
 
+def test_full_size_batch_sampled():
+    """The 16-sequence serving workload in the benchmark's launch
+    configuration; the oracle checks the first and the last sequence."""
+    w = W.make_mla_workload(W.MLA_CONFIGS["mla_b16_51k"])
+    d = _dev(w)
+    out, lse = _gpu(w, d, 0)
+    torch.cuda.synchronize()
+    _check(w, out, lse, seqs=[0, w.cfg.num_seqs - 1])
+
+
 def test_poisoned_unused_slots_and_entries_are_bitwise_identical():
     """Slots past each context (NaN codes 0x7F, bf16 NaN in kpe), unused
     pool blocks and table entries past each context (out-of-range ids) do

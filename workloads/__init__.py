@@ -390,6 +390,10 @@ MLA_CONFIGS = {
         "mla_kimi_tp8", seed=7, num_seqs=1, num_heads=8, ctx=51200, partition_size=832,
         description="MLA latent decode: 8 heads (one GPU's share of 64 under TP8), 51,200 tokens in 800 pages "
                     "of 64, FP8 E4M3 ckv 512 + bf16 kpe 64, split-K into 62 partitions of 832 tokens"),
+    "mla_b16_51k": MlaConfig(
+        "mla_b16_51k", seed=8, num_seqs=16, num_heads=8, ctx=51200, partition_size=0,
+        description="MLA latent decode at a serving batch: 16 sequences of the same 51,200-token shape, "
+                    "library-chosen partitions"),
 }
 
 
