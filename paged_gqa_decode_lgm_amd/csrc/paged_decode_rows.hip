@@ -49,8 +49,8 @@ __device__ __forceinline__ int clamped_ctx(const DecodeArgs& p, int b) {
 }
 
 // Fills sm.pre for sequences b0 .. b0 + kChunk - 1 (nhg streams of
-// ceil(ctx / unit) work units per sequence: 32-token tiles, or partitions,
-// where an empty context still counts one) and returns the chunk's total.
+// ceil(ctx / unit) work units per sequence: 32-token tiles, or partitions;
+// an empty context still counts one) and returns the chunk's total.
 // Called by every thread of the NT-thread workgroup (it synchronises).
 template <int NT>
 __device__ int scan_chunk(const DecodeArgs& p, RowsSmem& sm, int b0, int nhg, int unit, int min_units) {
@@ -299,7 +299,7 @@ __global__ __launch_bounds__(NT, 1) void paged_decode_rows_kernel(DecodeArgs p, 
   const bool parts = r.part_tiles > 0;
   const int upt = parts ? r.part_tiles : 1;   // tiles per unit
   const int unit = kTile * upt;               // tokens per unit
-  const int min_units = parts ? 1 : 0;        // an empty context still writes out = 0, lse = -inf
+  const int min_units = 1;                    // an empty context still writes out = 0, lse = -inf
 
   int total = scan_chunk<NT>(p, sm, 0, nhg, unit, min_units);
   for (int c0 = kChunk; c0 < B; c0 += kChunk) total += scan_chunk<NT>(p, sm, c0, nhg, unit, min_units);
@@ -482,6 +482,10 @@ hipError_t launch_group(const DecodeArgs& a, const RowsArgs& r, hipStream_t s) {
                        s, a, r);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || r.part_tiles > 0) return e;  // partition records are merged by lse_merge
+  // Short contexts: when every context fits one tile, no stream is split
+  // (each, an empty one included, is one unit written by the decode kernel),
+  // so the call is a single launch.
+  if (a.max_context_len <= kTile) return e;
   const int merge_rows = a.dims.num_seqs * a.dims.num_q_heads;
   hipLaunchKernelGGL(rows_merge_kernel, dim3((merge_rows + kMergeRows - 1) / kMergeRows), dim3(kMergeThreads), 0, s, a,
                      r);

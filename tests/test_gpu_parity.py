@@ -379,6 +379,20 @@ def test_row_plan_ragged_edges(cache, hkv, G):
     _run_and_check(cfg)
 
 
+@pytest.mark.parametrize("cache", ["bf16", "fp8", "fp4"])
+def test_row_plan_short_contexts_single_launch(cache):
+    """Every context within one 32-token tile (max_context_len 32): no stream
+    can be split, so the call is the decode launch alone, and the decode
+    kernel itself writes the empty contexts (out = 0, lse = -inf)."""
+    ctx = (0, 1, 5, 16, 17, 31, 32, 0, 2, 32)
+    cfg = W.Config(f"rows_short_{cache}", seed=15, num_seqs=len(ctx), num_q_heads=32, num_kv_heads=8, head_dim=128,
+                   block_size=16, act="bf16", cache=cache, ctx=0, rope_theta=5e5, partition_size=0, append=True,
+                   ctx_list=ctx)
+    w, d, out, lse = _run_and_check(cfg)
+    assert torch.count_nonzero(out[0]).item() == 0 and torch.count_nonzero(out[7]).item() == 0
+    assert bool(torch.isneginf(lse[0]).all()) and bool(torch.isneginf(lse[7]).all())
+
+
 def test_row_plan_more_workgroups_than_tiles():
     """The range count follows the longest context, so one long sequence among
     many one-token ones leaves most ranges empty, between non-empty ones."""
