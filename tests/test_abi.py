@@ -37,6 +37,12 @@ def test_library_loads_and_exports_every_header_function():
     assert L.lgm_abi_version() == 4
 
 
+def test_build_entry_abi_check_matches_header():
+    import __graft_entry__
+
+    __graft_entry__.check_abi()
+
+
 # ------------------------------------------------------------------ append
 def _append(**over):
     a = dict(qkv=addr(0), qkv_row_stride=(32 + 16) * 128, q_out=addr(1), k_cache=addr(2), v_cache=addr(3),
