@@ -465,22 +465,24 @@ def main() -> int:
     ps = ops.partition_size(q, k_pool, bt, max_ctx, cfg.partition_size)
     stream = torch.cuda.current_stream()
 
+    # Two events per step, around the attention call.  The append of step i
+    # runs between the end of step i-1's call and the start of step i's, so
+    # that interval times it (with the launch gaps around it) without a third
+    # event per step.
     def step(ev=None):
         if cfg.append:
-            if ev:
-                ev[0].record(stream)
             ops.rope_kv_append(qkv, k_pool, v_pool, bt, ctx, cfg.rope_theta, Hq, ks, vs, q_out=q)
         if ev:
-            ev[1].record(stream)
+            ev[0].record(stream)
         ops.paged_decode_attn(q, k_pool, v_pool, bt, ctx, max_ctx, softmax_scale=cfg.softmax_scale,
                               partition_size=cfg.partition_size, k_scale=ks, v_scale=vs, out=out, out_lse=lse,
                               workspace=ws)
         if ev:
-            ev[2].record(stream)
+            ev[1].record(stream)
 
     for _ in range(args.warmup):
         step()
-    events = [[TimingEvent() for _ in range(3)] for _ in range(args.steps)]
+    events = [[TimingEvent() for _ in range(2)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -507,8 +509,9 @@ def main() -> int:
         cold_ms.append(a.elapsed_time(b))
     del scratch
 
-    attn_ms = [e[1].elapsed_time(e[2]) for e in events]
-    append_ms = [e[0].elapsed_time(e[1]) for e in events] if cfg.append else []
+    attn_ms = [e[0].elapsed_time(e[1]) for e in events]
+    # (step 0's append follows an idle GPU and its launch latency: left out)
+    append_ms = [events[i - 1][1].elapsed_time(events[i][0]) for i in range(1, len(events))] if cfg.append else []
     ms_per_step = wall * 1e3 / args.steps
     kv = w.kv_bytes()
     attn_avg_s = statistics.mean(attn_ms) / 1e3
