@@ -429,9 +429,9 @@ def main() -> int:
     if args.copy_probe:
         return copy_probe(args.copy_probe, max(args.steps, 1))
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (this build has no "
-              "multi-GPU path: the decode step shards by kv heads or sequence blocks, see DESIGN.md).",
-              file=sys.stderr)
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported: the library has no "
+              "multi-GPU path (the decode step would shard by kv heads, or by sequence blocks with one "
+              "exchange of LSE records before lgm_lse_merge).", file=sys.stderr)
         return 2
 
     import torch
