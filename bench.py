@@ -406,6 +406,45 @@ def run_mla(args, torch, W) -> int:
     return 0 if mismatches == 0 else 1
 
 
+def graph_replay(torch, step, stream, steps: int, outputs) -> dict:
+    """The step captured once in a HIP graph and replayed back to back, with
+    events around each replay: the GPU time of a step without the host's
+    launch overhead (what bounds latency-bound shapes when run eagerly).
+    Checked replays, with host synchronisations between them, must equal the
+    eager step's outputs bitwise."""
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in outputs]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for _ in range(5):
+        graph.replay()
+    events = [(TimingEvent(), TimingEvent()) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for a, b in events:
+        a.record(stream)
+        graph.replay()
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in events]
+    equal = True
+    for _ in range(3):
+        for t in outputs:
+            t.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        equal &= all(torch.equal(t.view(torch.uint8), r.view(torch.uint8)) for t, r in zip(outputs, ref))
+    return {"step_avg_ms": round(statistics.mean(ms), 5), "step_median_ms": round(statistics.median(ms), 5),
+            "step_p10_ms": round(_quantile(ms, 0.1), 5), "replays": steps,
+            "replays_bitwise_equal_to_eager": bool(equal)}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -414,6 +453,8 @@ def main() -> int:
     ap.add_argument("--workload", default="llama3_8b_gqa")
     ap.add_argument("--partition-size", type=int, default=None, help="override the workload's partition size")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step replayed from a HIP graph (reported under 'graph')")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the read-only streaming ceiling probe")
     ap.add_argument("--cold", type=int, default=10, help="extra attention calls timed after a cache-evicting write")
     ap.add_argument("--copy-probe", type=int, default=None, metavar="BYTES",
@@ -490,6 +531,8 @@ def main() -> int:
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
+    graph_rec = graph_replay(torch, step, stream, args.steps, (q, out, lse)) if args.graph else None
+
     # Cold calls: reading 1 GiB between calls (outside the event pair) evicts
     # the previous call's lines from L2 and the 256 MB Infinity Cache.  A read,
     # not a write: evicting a write's dirty lines would charge the next call
@@ -554,6 +597,8 @@ def main() -> int:
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
     }
+    if graph_rec is not None:
+        rec["graph"] = graph_rec
     if not args.no_ceiling:
         ceil = read_ceiling(torch)
         ceil["attention_pct_of_ceiling"] = round(100.0 * achieved / ceil["gbs"], 2)
