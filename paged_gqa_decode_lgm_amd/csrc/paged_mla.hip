@@ -107,7 +107,8 @@ __device__ __forceinline__ void stage_load(const MlaArgs& p, int ts, int t1, int
   for (int k = 0; k < 10; ++k) {
     const int tok = ts + (k < 8 ? lat_row(k, v, lane) : pos_row(k - 8, v, lane));
     const bool good = tok < t1 && (unsigned)e[k] < nb;
-    const int64_t row = good ? ((int64_t)e[k] << bs_log2) + (tok & ((1 << bs_log2) - 1)) : 0;
+    // an invalid row reads block 0, row 0 (one line for all of them) and is zeroed after its store
+    const int64_t row = ((int64_t)(good ? e[k] : 0) << bs_log2) + (good ? tok & ((1 << bs_log2) - 1) : 0);
     if (k < 8)
       st.c[k] = ld_nt(ckv + row * kDL + 16 * (lane & 31));
     else
@@ -117,16 +118,26 @@ __device__ __forceinline__ void stage_load(const MlaArgs& p, int ts, int t1, int
   st.ok = ok;
 }
 
+// The rows go to LDS as loaded; only when a row of this wave's share is
+// invalid (the partition's last tile, or an out-of-range table entry) are
+// those rows overwritten with zeros (later LDS stores of one wave land later).
 __device__ __forceinline__ void stage_store(const MlaStage& st, MlaTileBuf& tb, int v, int lane) {
-  const u32x4 z = {0u, 0u, 0u, 0u};
+  constexpr int kAll = (1 << 10) - 1;
 #pragma unroll
   for (int k = 0; k < 8; ++k)
-    *reinterpret_cast<u32x4*>(&tb.ckv[lat_row(k, v, lane) * kRowC + 16 * (lane & 31)]) =
-        ((st.ok >> k) & 1) ? st.c[k] : z;
+    *reinterpret_cast<u32x4*>(&tb.ckv[lat_row(k, v, lane) * kRowC + 16 * (lane & 31)]) = st.c[k];
 #pragma unroll
   for (int k = 0; k < 2; ++k)
-    *reinterpret_cast<u32x4*>(&tb.kpe[pos_row(k, v, lane) * kRowP + 16 * (lane & 7)]) =
-        ((st.ok >> (8 + k)) & 1) ? st.r[k] : z;
+    *reinterpret_cast<u32x4*>(&tb.kpe[pos_row(k, v, lane) * kRowP + 16 * (lane & 7)]) = st.r[k];
+  if (__builtin_expect(__any(st.ok != kAll), 0)) {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (!((st.ok >> k) & 1)) *reinterpret_cast<u32x4*>(&tb.ckv[lat_row(k, v, lane) * kRowC + 16 * (lane & 31)]) = z;
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+      if (!((st.ok >> (8 + k)) & 1)) *reinterpret_cast<u32x4*>(&tb.kpe[pos_row(k, v, lane) * kRowP + 16 * (lane & 7)]) = z;
+  }
   if ((lane & 31) == 0) {  // one lane per latent row writes its flag
 #pragma unroll
     for (int k = 0; k < 8; ++k) tb.valid[lat_row(k, v, lane)] = (st.ok >> k) & 1;
@@ -173,7 +184,7 @@ __device__ __forceinline__ void load_role(const MlaArgs& p, MlaSmem& sm, const i
   auto step = [&](int tau, MlaStage& st, int& eu, int& el) {
     __syncthreads();  // B1
     __syncthreads();  // B2
-    stage_store(st, sm.tile[(tau + 2) % kBufs], v, lane);
+    if (tau + 2 < ntiles) stage_store(st, sm.tile[(tau + 2) % kBufs], v, lane);  // a tile past the end is never read
     el = load_entry(bt, tile_start(tau + 6), t1, bsl, lane);
     __builtin_amdgcn_sched_barrier(0);  // entry load ahead of the tile loads (counter order)
     stage_load(p, tile_start(tau + 5), t1, bsl, eu, v, lane, st);
