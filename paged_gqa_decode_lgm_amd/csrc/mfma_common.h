@@ -178,12 +178,14 @@ struct MfmaBF16 {
   }
   // A operand of score MFMA c.
   __device__ static short8 k_operand(const KBlock& r, int c) { return __builtin_bit_cast(short8, r.k[c]); }
-  // V element i (0..7) of row jj packed with the same element of row jj+1 -> bf16x2.
-  __device__ static uint32_t v_pair(const VBlock& r, int jj, int i) {
+  // V elements i and i+1 (i even) of row jj, each packed with the same
+  // element of row jj+1 -> two bf16x2 words (one byte permute each).
+  __device__ static void v_pairs2(const VBlock& r, int jj, int i, uint32_t& lo, uint32_t& hi) {
     const uint32_t* a = reinterpret_cast<const uint32_t*>(&r.v[jj]);
     const uint32_t* b = reinterpret_cast<const uint32_t*>(&r.v[jj + 1]);
     const uint32_t x = a[i >> 1], y = b[i >> 1];
-    return (i & 1) ? ((y & 0xffff0000u) | (x >> 16)) : ((y << 16) | (x & 0xffffu));
+    lo = __builtin_amdgcn_perm(y, x, 0x05040100u);  // x.lo16 | y.lo16 << 16
+    hi = __builtin_amdgcn_perm(y, x, 0x07060302u);  // x.hi16 | y.hi16 << 16
   }
   __device__ static void zero_v_row(VBlock& r, int jj) { r.v[jj] = make_uint4(0, 0, 0, 0); }
 };
@@ -225,10 +227,15 @@ struct MfmaFP8 {
     return words_to_short8(fp8x2_to_bf16x2(w0), fp8x2_hi_to_bf16x2(w0), fp8x2_to_bf16x2(w1),
                            fp8x2_hi_to_bf16x2(w1));
   }
-  __device__ static uint32_t v_pair(const VBlock& r, int jj, int i) {
-    const uint32_t x = (i < 4 ? r.v[jj].x : r.v[jj].y) >> (8 * (i & 3));
-    const uint32_t y = (i < 4 ? r.v[jj + 1].x : r.v[jj + 1].y) >> (8 * (i & 3));
-    return fp8x2_to_bf16x2((x & 0xffu) | ((y & 0xffu) << 8));
+  // Codes i and i+1 (i even) of rows jj and jj+1: one byte permute gathers
+  // [row jj code i, row jj+1 code i, row jj code i+1, row jj+1 code i+1] and
+  // the two halves convert to the two bf16x2 words.
+  __device__ static void v_pairs2(const VBlock& r, int jj, int i, uint32_t& lo, uint32_t& hi) {
+    const uint32_t x = i < 4 ? r.v[jj].x : r.v[jj].y;
+    const uint32_t y = i < 4 ? r.v[jj + 1].x : r.v[jj + 1].y;
+    const uint32_t q = __builtin_amdgcn_perm(y, x, (i & 3) == 0 ? 0x05010400u : 0x07030602u);
+    lo = fp8x2_to_bf16x2(q);
+    hi = fp8x2_hi_to_bf16x2(q);
   }
   __device__ static void zero_v_row(VBlock& r, int jj) { r.v[jj] = make_uint2(0, 0); }
 };
@@ -281,9 +288,10 @@ struct MfmaFP4 {
     return words_to_short8(fp4x2_to_bf16x2<0>(w, sc), fp4x2_to_bf16x2<1>(w, sc), fp4x2_to_bf16x2<2>(w, sc),
                            fp4x2_to_bf16x2<3>(w, sc));
   }
-  // Rows jj and jj+1, element i: convert the byte holding element i of each
-  // row with the row's own scale, then pair the two halves.
-  __device__ static uint32_t v_pair(const VBlock& r, int jj, int i) {
+  // Rows jj and jj+1, elements i and i+1 (i even, one byte of each row):
+  // convert that byte of each row with the row's own scale, then pair the
+  // halves.
+  __device__ static void v_pairs2(const VBlock& r, int jj, int i, uint32_t& lo, uint32_t& hi) {
     uint32_t x, y;
     const float sx = e8m0_to_f32(r.s[jj]), sy = e8m0_to_f32(r.s[jj + 1]);
     switch (i >> 1) {
@@ -292,7 +300,8 @@ struct MfmaFP4 {
       case 2: x = fp4x2_to_bf16x2<2>(r.v[jj], sx); y = fp4x2_to_bf16x2<2>(r.v[jj + 1], sy); break;
       default: x = fp4x2_to_bf16x2<3>(r.v[jj], sx); y = fp4x2_to_bf16x2<3>(r.v[jj + 1], sy); break;
     }
-    return (i & 1) ? ((y & 0xffff0000u) | (x >> 16)) : ((y << 16) | (x & 0xffffu));
+    lo = __builtin_amdgcn_perm(y, x, 0x05040100u);  // element i of both rows
+    hi = __builtin_amdgcn_perm(y, x, 0x07060302u);  // element i+1 of both rows
   }
   // A masked row: zero codes and a finite scale, so the row contributes
   // exactly zero whatever its stored scale byte held.
@@ -436,10 +445,14 @@ __device__ __forceinline__ void tile_update(WaveState& st, TileRegs<C>& r, const
   // P operand: head n, tokens x rows 4kg..4kg+3 then y rows 4kg..4kg+3.
   const short8 pa = words_to_short8(pw[0], pw[1], pw[2], pw[3]);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const short8 vb = words_to_short8(C::v_pair(r.vx, 0, i), C::v_pair(r.vx, 2, i), C::v_pair(r.vy, 0, i),
-                                      C::v_pair(r.vy, 2, i));
-    st.acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, st.acc[i], 0, 0, 0);
+  for (int i = 0; i < 8; i += 2) {
+    uint32_t a0, a1, b0, b1, c0, c1, d0, d1;
+    C::v_pairs2(r.vx, 0, i, a0, a1);
+    C::v_pairs2(r.vx, 2, i, b0, b1);
+    C::v_pairs2(r.vy, 0, i, c0, c1);
+    C::v_pairs2(r.vy, 2, i, d0, d1);
+    st.acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, words_to_short8(a0, b0, c0, d0), st.acc[i], 0, 0, 0);
+    st.acc[i + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, words_to_short8(a1, b1, c1, d1), st.acc[i + 1], 0, 0, 0);
   }
 }
 
