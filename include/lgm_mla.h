@@ -54,7 +54,8 @@ typedef struct lgm_mla_dims {
  * partition_size itself (capped to max_context_len rounded up to 32) when
  * positive, else one that gives about one workgroup per compute unit (256)
  * at max_context_len over the batch: ceil(B * max_context_len / 256)
- * rounded up to a multiple of 32, at least 128.  Returns -1 (and sets
+ * rounded up to a multiple of 64 (the kernel's tile), at least 128, and
+ * capped as above.  Returns -1 (and sets
  * lgm_last_error) on invalid arguments.
  */
 int32_t lgm_paged_mla_partition_size(lgm_mla_dims dims, int32_t max_context_len, int32_t partition_size);

@@ -312,6 +312,7 @@ lgm_status check_decode_common(const char* fn, const lgm_paged_dims& d, int32_t 
 // unit of MI355X at max_context_len, and at least one tile per wave.
 constexpr int64_t kMlaTargetWorkgroups = 256;
 constexpr int32_t kMlaTile = 32;
+constexpr int32_t kMlaAutoStep = 64;  // the kernel's tile: a partition's last tile costs a whole tile
 constexpr int32_t kMlaMinAutoPartition = 128;
 
 lgm_status check_mla_dims(const char* fn, const lgm_mla_dims& d, int32_t max_ctx) {
@@ -358,7 +359,7 @@ lgm_status plan_mla(const char* fn, const lgm_mla_dims& d, int32_t max_ctx, int3
   if (p == 0) {
     const int64_t tokens = (int64_t)(d.num_seqs > 0 ? d.num_seqs : 1) * max_ctx;
     p = (tokens + kMlaTargetWorkgroups - 1) / kMlaTargetWorkgroups;
-    p = (p + kMlaTile - 1) / kMlaTile * kMlaTile;
+    p = (p + kMlaAutoStep - 1) / kMlaAutoStep * kMlaAutoStep;
     p = p < kMlaMinAutoPartition ? kMlaMinAutoPartition : p;
   }
   pl.ps = (int32_t)(p < cap ? p : cap);

@@ -382,7 +382,9 @@ def test_mla_empty_batch_is_a_noop():
 
 @pytest.mark.parametrize("B,max_ctx,ps,want", [
     (1, 51200, 832, 832),      # explicit: kept
-    (1, 51200, 0, 224),        # ceil(51200 / 256) = 200 -> 224 (whole tiles)
+    (1, 51200, 0, 256),        # ceil(51200 / 256) = 200 -> 256 (whole 64-token tiles)
+    (2, 51200, 0, 448),        # ceil(102400 / 256) = 400 -> 448
+    (16, 51200, 0, 3200),      # already whole tiles
     (64, 4096, 0, 1024),       # 64 * 4096 / 256
     (1, 1000, 0, 128),         # at least one tile per wave
     (1, 100, 0, 128),          # capped to the context rounded up to 32
