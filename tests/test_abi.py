@@ -396,6 +396,22 @@ def test_mla_partition_plan(B, max_ctx, ps, want):
     assert L.lgm_paged_mla_partition_size(mla_dims(num_seqs=B), max_ctx, ps) == want
 
 
+@pytest.mark.parametrize("B", [1, 2, 3, 7, 16, 64, 300])
+@pytest.mark.parametrize("max_ctx", [1, 31, 129, 1000, 4097, 51200, 131072])
+def test_mla_auto_partition_properties(B, max_ctx):
+    """Library-chosen partitions are whole 64-token tiles of at least 128
+    tokens, unless one partition covers the context (then the context rounded
+    up to 32); a batch spreads over about one workgroup per compute unit."""
+    d = mla_dims(num_seqs=B, max_blocks_per_seq=-(-max_ctx // 64) + 1)
+    ps = L.lgm_paged_mla_partition_size(d, max_ctx, 0)
+    cap = -(-max_ctx // 32) * 32
+    assert 0 < ps <= cap
+    if ps < cap:
+        assert ps % 64 == 0 and ps >= 128
+        # one 64-token tile fewer per partition would need more than 256 workgroups
+        assert ps == 128 or B * max_ctx > 256 * (ps - 64)
+
+
 @pytest.mark.parametrize("B,H,max_ctx,ps", [(1, 8, 51200, 832), (1, 8, 51200, 0), (4, 16, 3000, 96),
                                             (2, 1, 100, 0), (5, 8, 64, 64)])
 def test_mla_workspace_formula(B, H, max_ctx, ps):
