@@ -89,7 +89,7 @@ typedef enum lgm_status {
 
 /* Element types.  LGM_FP8_E4M3 is OCP e4m3fn ([mainarch]): bias 7, largest
  * finite 448, 0x7F/0xFF NaN, no infinities.  LGM_FP4_E2M1 is a cache type
- * only ([mainarch]: 4-bit E2M1 KV with E8M0 block scales), in the OCP
+ * only ([mainarch] names an E2M1 KV cache with E8M0 block scales), in the OCP
  * Microscaling form: E2M1 codes (magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6), one
  * E8M0 scale byte 2^(byte - 127) per 32 consecutive head_dim elements of a
  * (token, kv head) row; see "FP4 cache blocks" above. */
@@ -182,27 +182,40 @@ lgm_status lgm_rope_kv_append(const void* qkv, int64_t qkv_row_stride, void* q_o
  *    tokens that still gives 2048 (sequence, partition, kv head) work items
  *    at max_context_len;
  *  - other shapes: a size that gives about 8192 workgroups.
- * With partitions, when max_context_len exceeds the partition size each
- * context is cut into floor(L / partition) full partitions followed by
- * partitions of half that size (at least block_size) over the rest, which
- * are processed last.  Returns -1 (and sets lgm_last_error) on invalid
- * arguments.
+ * How contexts are cut into partitions:
+ *  - the whole-row partition plan, taken when the matrix-core shapes have
+ *    num_kv_heads divisible by 4 and an explicit partition_size that is a
+ *    multiple of 32 and at least 256 tokens, max_context_len holds at least
+ *    64 partitions and the batch at least 256 (sequence, head group of 8 or
+ *    4 kv heads, partition) units: plain ceil(L / partition) partitions, run
+ *    in equal numbers of whole partitions per workgroup (256 workgroups of
+ *    whole KV rows);
+ *  - every other partitioned plan: when max_context_len exceeds the
+ *    partition size, each context is cut into floor(L / partition) full
+ *    partitions followed by partitions of half that size (at least
+ *    block_size) over the rest, which are processed last.
+ * Returns -1 (and sets lgm_last_error) on invalid arguments.
  */
 int32_t lgm_paged_decode_partition_size(lgm_paged_dims dims, int32_t max_context_len,
                                         int32_t partition_size, lgm_dtype cache_dtype);
 
 /*
  * Bytes of device workspace lgm_paged_decode_attn needs for these
- * arguments (each region 256-byte aligned):
+ * arguments, 0 when the plan needs none.  A nonzero workspace always starts
+ * with the same 256-byte slot: two int32 work counters that only the
+ * work-queue plan uses (it needs them zero on entry and leaves them zero);
+ * no other plan reads or writes that slot.  After it come the plan's own
+ * regions, each 256-byte aligned:
  *  - equal ranges (see lgm_paged_decode_partition_size): two records per
  *    range (fp32 outputs of the head group's Hq * 8 / Hkv or Hq * 4 / Hkv
  *    query heads, D each, and their natural-log LSEs), then int32 range
  *    and context bookkeeping (one per range, two per context and head group);
- *  - partitions on the matrix-core shapes: 256 bytes holding two int32 work
- *    counters, then, when contexts are split, fp32 partial outputs
- *    [B][Hq][P][D] and LSEs [B][Hq][P], P = the most partitions any context
- *    up to max_context_len is cut into;
- *  - partitions on other shapes: the partials only (0 without a split).
+ *  - partitions (the whole-row partition plan, the work-queue plan on the
+ *    other matrix-core shapes, the vector-ALU plan on the rest): when
+ *    contexts are split, fp32 partial outputs [B][Hq][P][D] and LSEs
+ *    [B][Hq][P], P = the most partitions any context up to max_context_len
+ *    is cut into.  Without a split the work-queue plan needs the slot alone
+ *    and the other two plans need no workspace.
  * Returns 0 and sets lgm_last_error on invalid arguments (check it when 0
  * is unexpected).
  */
@@ -239,12 +252,12 @@ size_t lgm_paged_decode_workspace_size(lgm_paged_dims dims, int32_t max_context_
  *   max_context_len upper bound on context_lens, 0..max_blocks_per_seq*block_size
  *   workspace      device buffer of at least lgm_paged_decode_workspace_size()
  *                  bytes, 256-byte aligned (NULL allowed when that size is 0).
- *                  With partitions on the matrix-core shapes its first 256
- *                  bytes (the work counters) must be zero before the first
- *                  call on it; every completed call leaves them zero again.
- *                  Zero-fill it again after a call on it failed to complete.
- *                  Calls sharing a workspace must not overlap in time (one
- *                  per stream).
+ *                  Its first 256 bytes (the work counters) must be zero
+ *                  before the first call on it; every completed call, on any
+ *                  plan, leaves them zero, so one buffer may serve calls with
+ *                  different shapes and plans in turn.  Zero-fill it again
+ *                  after a call on it failed to complete.  Calls sharing a
+ *                  workspace must not overlap in time (one per stream).
  *   flags          LGM_CACHE_HND | LGM_SCALE_PER_TENSOR (the latter for FP8
  *                  caches only); LGM_ROPE_INTERLEAVED is rejected here
  * Supported: (act, cache) in {(F32, F32), (BF16, BF16), (BF16, FP8_E4M3)},
@@ -268,8 +281,10 @@ lgm_status lgm_paged_decode_attn(void* out, float* out_lse, const void* q, int64
  * n = num_partitions[b] (clamped to [0, max_partitions]; NULL = all):
  *   M = max_p lse_p,  w_p = exp(lse_p - M),
  *   out[b][h] = sum_p w_p o_p / sum_p w_p,  out_lse[b][h] = M + log(sum_p w_p);
- * records with lse = -inf weigh 0; n = 0 or all -inf gives out = 0,
- * out_lse = -inf.  Summation order is fixed (bitwise reproducible).
+ * records with lse = -inf weigh 0 and their partial_out rows are not
+ * used (they may hold anything, NaN or Inf included); n = 0 or all -inf
+ * gives out = 0, out_lse = -inf.  Summation order is fixed (bitwise
+ * reproducible).
  *
  *   out            [B][H][D] out_dtype (LGM_F32 or LGM_BF16), dense
  *   out_lse        optional fp32 [B][H]

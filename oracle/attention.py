@@ -165,7 +165,16 @@ def paged_decode_partials(q, k_pool, v_pool, block_tables, context_lens, softmax
 
 def lse_merge(o_p, lse_p, num_parts=None):
     """Merge partition records [B, H, P, D] / [B, H, P] by log-sum-exp.
-    ``num_parts`` [B] limits each sequence to its first P_b records."""
+    ``num_parts`` [B] limits each sequence to its first P_b records.
+
+    A record whose lse is -inf is an empty partition (its softmax sums over
+    no token): it is left out of the merge altogether, so whatever its
+    output row holds (zeros, or NaN/Inf in memory nobody wrote) has no
+    effect.  That is the reading taken of "an empty partition weighs zero"
+    (the combine of split partials in the mainarch README's decode-attention
+    section; the local split-K/LSE merge of the Loom Kernels README, row
+    "Attention"): its weight exp(-inf) is exactly 0, and 0 times its row is
+    taken as 0 even where IEEE arithmetic would give NaN."""
     o_p = np.asarray(o_p, dtype=np.float64)
     lse_p = np.asarray(lse_p, dtype=np.float64)
     B, H, P, D = o_p.shape
@@ -175,10 +184,12 @@ def lse_merge(o_p, lse_p, num_parts=None):
         n = P if num_parts is None else int(num_parts[b])
         for h in range(H):
             ls = lse_p[b, h, :n]
-            if n == 0 or not np.any(np.isfinite(ls)):
+            live = ls > -np.inf
+            if not live.any():
                 continue
+            ls = ls[live]
             M = ls.max()
             w = np.exp(ls - M)
-            out[b, h] = (w[:, None] * o_p[b, h, :n]).sum(axis=0) / w.sum()
+            out[b, h] = (w[:, None] * o_p[b, h, :n][live]).sum(axis=0) / w.sum()
             lse[b, h] = M + np.log(w.sum())
     return out, lse

@@ -1,9 +1,10 @@
 """NeoX (split-half) and interleaved rotary position embedding (oracle only).
 
-The pages name the operation but print no formula: Loom Kernels lists
-"NeoX/interleaved RoPE + native/static-FP8 paged-KV write" among its
-supported operator paths, and microLLM-rocm's ledger calls the same layout
-"split-half RoPE".  The textbook split-half rotary embedding is taken: for a
+The pages name the operation but print no formula: Loom Kernels lists a
+NeoX or interleaved RoPE fused with the native or static-FP8 paged-KV write
+among its supported operator paths (row «Position and KV»), and
+microLLM-rocm's ledger names the same layout as the split-half form.  The
+textbook split-half rotary embedding is taken: for a
 head vector x of even length D, pair i (0 <= i < D/2) is (x[i], x[i + D/2]),
 rotated by the angle pos * w_i with w_i = theta ** (-2i/D):
 

@@ -1,7 +1,8 @@
 // C-ABI host layer: validates every host-visible argument before any HIP
 // call, resolves the partition plan, and launches the kernels on the
-// caller's stream.  "Accept the exact contract or return an error" (Loom
-// Kernels README, "Architecture"); error text names the function, the
+// caller's stream.  A call either meets its full contract or returns an
+// error and does nothing (Loom Kernels README, «Architecture»); error text
+// names the function, the
 // argument and what was expected (the span check of mainarch's VA guard,
 // troubleshooting section, is the model).  Nothing here allocates device or
 // host memory.
@@ -179,11 +180,13 @@ int32_t resolve_partition(const char* fn, const lgm_paged_dims& d, int32_t max_c
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+constexpr size_t kCounterSlot = 256;  // the work-queue counters at the start of every workspace
 
-// Launch plan of one attention call, a function of host-visible arguments only:
-// partitions of `ps` tokens; workspace = the persistent kernel's two work
-// counters (matrix-core shapes, one 256-byte slot), then the partial outputs
-// and LSEs (none when every sequence fits one partition).
+// Launch plan of one attention call, a function of host-visible arguments only.
+// Every plan that needs a workspace lays it out the same way at the start:
+// a 256-byte slot holding the work-queue kernel's two counters, which only
+// that kernel writes (it leaves them zero), then the plan's own regions.  So
+// one zero-filled workspace may serve calls on any plan in turn.
 struct Plan {
   bool rows;        // whole-row kernel (Hkv % 4 == 0): equal tile ranges (partition_size 0) ...
   bool rows_parts;  // ... or equal runs of whole partitions (an explicit partition_size of whole tiles)
@@ -238,11 +241,12 @@ lgm_status plan_decode(const char* fn, const lgm_paged_dims& d, int32_t max_ctx,
     W = W < 1 ? 1 : (W > kRowsWorkgroups ? kRowsWorkgroups : W);
     pl.W = (int32_t)W;
     const size_t rows_per_rec = (size_t)pl.HG * G;
+    pl.counters_bytes = kCounterSlot;
     pl.rec_out_bytes = align256((size_t)W * 2 * rows_per_rec * d.head_dim * sizeof(float));
     pl.rec_lse_bytes = align256((size_t)W * 2 * rows_per_rec * sizeof(float));
     pl.first_bytes = align256((size_t)W * sizeof(int32_t));
     pl.stream_bytes = align256((size_t)streams * sizeof(int32_t));
-    pl.total = pl.rec_out_bytes + pl.rec_lse_bytes + pl.first_bytes + 2 * pl.stream_bytes;
+    pl.total = pl.counters_bytes + pl.rec_out_bytes + pl.rec_lse_bytes + pl.first_bytes + 2 * pl.stream_bytes;
     return LGM_OK;
   }
   pl.ps = resolve_partition(fn, d, max_ctx, ps_arg, persistent);
@@ -263,10 +267,11 @@ lgm_status plan_decode(const char* fn, const lgm_paged_dims& d, int32_t max_ctx,
       return fail(LGM_ERR_UNSUPPORTED, fn, "num_seqs * head groups * partitions = %lld: too many", (long long)units);
     pl.W = (int32_t)(units < 1 ? 1 : (units > kRowsWorkgroups ? kRowsWorkgroups : units));
     if (pl.P > 1) {
+      pl.counters_bytes = kCounterSlot;
       pl.part_out_bytes = align256((size_t)d.num_seqs * d.num_q_heads * pl.P * d.head_dim * sizeof(float));
       pl.part_lse_bytes = align256((size_t)d.num_seqs * d.num_q_heads * pl.P * sizeof(float));
     }
-    pl.total = pl.part_out_bytes + pl.part_lse_bytes;
+    pl.total = pl.counters_bytes + pl.part_out_bytes + pl.part_lse_bytes;
     return LGM_OK;
   }
   // When contexts are split, the tokens past a context's last full partition
@@ -286,7 +291,7 @@ lgm_status plan_decode(const char* fn, const lgm_paged_dims& d, int32_t max_ctx,
   if (persistent && (int64_t)d.num_seqs * d.num_kv_heads * pl.P > (int64_t)INT32_MAX - (1 << 20))
     return fail(LGM_ERR_UNSUPPORTED, fn, "num_seqs * num_kv_heads * partitions = %lld work items: too many",
                 (long long)d.num_seqs * d.num_kv_heads * pl.P);
-  if (persistent) pl.counters_bytes = 256;
+  if (persistent || pl.P > 1) pl.counters_bytes = kCounterSlot;
   if (pl.P > 1) {
     pl.part_out_bytes = align256((size_t)d.num_seqs * d.num_q_heads * pl.P * d.head_dim * sizeof(float));
     pl.part_lse_bytes = align256((size_t)d.num_seqs * d.num_q_heads * pl.P * sizeof(float));
@@ -531,8 +536,8 @@ lgm_status lgm_paged_decode_attn(void* out, float* out_lse, const void* q, int64
 
   char* wsb = static_cast<char*>(workspace);
   if (pl.rows_parts) {
-    float* part_out = pl.P > 1 ? reinterpret_cast<float*>(wsb) : nullptr;
-    float* part_lse = pl.P > 1 ? reinterpret_cast<float*>(wsb + pl.part_out_bytes) : nullptr;
+    float* part_out = pl.P > 1 ? reinterpret_cast<float*>(wsb + pl.counters_bytes) : nullptr;
+    float* part_lse = pl.P > 1 ? reinterpret_cast<float*>(wsb + pl.counters_bytes + pl.part_out_bytes) : nullptr;
     lgm::DecodeArgs a{out, out_lse, q, q_seq_stride, k_cache, v_cache, block_tables, context_lens, k_scale, v_scale,
                       part_out, part_lse, nullptr, softmax_scale, pl.parts, max_context_len, pl.P, dims, flags};
     lgm::RowsArgs r{};
@@ -553,7 +558,7 @@ lgm_status lgm_paged_decode_attn(void* out, float* out_lse, const void* q, int64
     lgm::DecodeArgs a{out, out_lse, q, q_seq_stride, k_cache, v_cache, block_tables, context_lens, k_scale, v_scale,
                       nullptr, nullptr, nullptr, softmax_scale, lgm::PartitionPlan{1, 1}, max_context_len, 0, dims,
                       flags};
-    char* w = wsb;
+    char* w = wsb + pl.counters_bytes;
     lgm::RowsArgs r{};
     r.num_wg = pl.W;
     r.head_group = pl.HG;
@@ -570,7 +575,10 @@ lgm_status lgm_paged_decode_attn(void* out, float* out_lse, const void* q, int64
     if (e != hipSuccess) return fail(LGM_ERR_HIP, fn, "row kernel launch failed: %s", hipGetErrorString(e));
     return LGM_OK;
   }
-  int32_t* counters = pl.counters_bytes ? reinterpret_cast<int32_t*>(wsb) : nullptr;
+  int32_t* counters = pl.counters_bytes && lgm::decode_mfma_supported(act_dtype, cache_dtype, dims.head_dim, G,
+                                                                     dims.block_size)
+                          ? reinterpret_cast<int32_t*>(wsb)
+                          : nullptr;
   float* part_out = pl.P > 1 ? reinterpret_cast<float*>(wsb + pl.counters_bytes) : nullptr;
   float* part_lse = pl.P > 1 ? reinterpret_cast<float*>(wsb + pl.counters_bytes + pl.part_out_bytes) : nullptr;
   lgm::DecodeArgs a{out, out_lse, q, q_seq_stride, k_cache, v_cache, block_tables, context_lens, k_scale, v_scale,

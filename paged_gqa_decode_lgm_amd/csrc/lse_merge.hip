@@ -90,12 +90,15 @@ __global__ __launch_bounds__(kThreads) void lse_merge_kernel(MergeArgs p) {
   float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll 4
   for (int i = pg; i < n; i += PG) {
+    // A record of weight zero (lse = -inf: an empty partition) is left out
+    // by a select, so its row may hold anything, NaN included.
     const float w = expf(lse[i] - ms);
     const float4 v = reinterpret_cast<const float4*>(po + (int64_t)i * D)[td];
-    a.x = fmaf(w, v.x, a.x);
-    a.y = fmaf(w, v.y, a.y);
-    a.z = fmaf(w, v.z, a.z);
-    a.w = fmaf(w, v.w, a.w);
+    const bool live = w != 0.f;
+    a.x = live ? fmaf(w, v.x, a.x) : a.x;
+    a.y = live ? fmaf(w, v.y, a.y) : a.y;
+    a.z = live ? fmaf(w, v.z, a.z) : a.z;
+    a.w = live ? fmaf(w, v.w, a.w) : a.w;
   }
   s_acc[pg][td * 4 + 0] = a.x;
   s_acc[pg][td * 4 + 1] = a.y;

@@ -77,8 +77,8 @@ __device__ __forceinline__ void cursor_locate(const DecodeArgs& p, CursorSmem& c
   int base_b = __builtin_amdgcn_readfirstlane(cs.base_b);
   int base_item = __builtin_amdgcn_readfirstlane(cs.base_item);
   int total = __builtin_amdgcn_readfirstlane(cs.total);
-  bool found = true;
-  while (item >= base_item + total) {
+  bool found = item >= 0;  // a negative item (counters not zero on entry) is no item
+  while (found && item >= base_item + total) {
     base_item += total;
     if (base_b + kWaveSize < p.dims.num_seqs) {
       base_b += kWaveSize;

@@ -194,12 +194,12 @@ def partitions_brute_force(max_ctx, ps, tps):
 def test_workspace_size_formula():
     al = lambda x: (x + 255) // 256 * 256
     # whole-row partition plan: Hkv % 4 == 0, whole-tile partitions of >= 256 tokens, >= 64 of them at the
-    # longest context and >= 256 units in the batch; plain ceil(L / ps) partitions, no counters
+    # longest context and >= 256 units in the batch; plain ceil(L / ps) partitions after the counter slot
     long = dims(num_seqs=4, max_blocks_per_seq=8192)
     assert L.lgm_paged_decode_workspace_size(long, 131072, 512, L.LGM_BF16) == (
-        al(4 * 32 * 256 * 128 * 4) + al(4 * 32 * 256 * 4))
+        256 + al(4 * 32 * 256 * 128 * 4) + al(4 * 32 * 256 * 4))
     assert L.lgm_paged_decode_workspace_size(long, 131072, 2048, L.LGM_FP8_E4M3) == (
-        al(4 * 32 * 64 * 128 * 4) + al(4 * 32 * 64 * 4))
+        256 + al(4 * 32 * 64 * 128 * 4) + al(4 * 32 * 64 * 4))
     d = dims()                                     # 16 partitions at the longest context: work-queue kernel
     assert L.lgm_paged_decode_workspace_size(d, 8192, 8192, L.LGM_BF16) == 256     # one partition
     assert L.lgm_paged_decode_workspace_size(d, 8192, 8192, L.LGM_FP8_E4M3) == 256
@@ -215,9 +215,10 @@ def test_workspace_size_formula():
     assert L.lgm_paged_decode_workspace_size(d, 8192, 64, L.LGM_BF16) == (
         256 + al(64 * 32 * P64 * 128 * 4) + al(64 * 32 * P64 * 4))
     lse_b = 64 * 32 * P * 4
-    v = dims(head_dim=64)                          # vector-ALU shape: partials only
+    v = dims(head_dim=64)                          # vector-ALU shape: the counter slot, then the partials
     assert L.lgm_paged_decode_workspace_size(v, 8192, 8192, L.LGM_BF16) == 0
-    assert L.lgm_paged_decode_workspace_size(v, 8192, 512, L.LGM_BF16) == al(64 * 32 * P * 64 * 4) + al(lse_b)
+    assert L.lgm_paged_decode_workspace_size(v, 8192, 512, L.LGM_BF16) == (
+        256 + al(64 * 32 * P * 64 * 4) + al(lse_b))
 
 
 @pytest.mark.parametrize("max_ctx,ps", [(100, 16), (100, 64), (1000, 96), (3000, 512), (4096, 1024), (17, 16),
@@ -228,7 +229,7 @@ def test_partition_count_bound(max_ctx, ps):
     P = partitions_brute_force(max_ctx, ps, tps)
     d = dims(head_dim=64, max_blocks_per_seq=(max_ctx + 15) // 16)
     al = lambda x: (x + 255) // 256 * 256
-    want = 0 if P == 1 else al(64 * 32 * P * 64 * 4) + al(64 * 32 * P * 4)
+    want = 0 if P == 1 else 256 + al(64 * 32 * P * 64 * 4) + al(64 * 32 * P * 4)
     assert L.lgm_paged_decode_workspace_size(d, max_ctx, ps, L.LGM_BF16) == want
     assert L.lgm_last_error() == ""
     with pytest.raises(L.LgmError):
@@ -239,14 +240,14 @@ def test_row_plan_workspace_formula():
     al = lambda x: (x + 255) // 256 * 256
     d = dims()                                     # 8 kv heads per workgroup, 64 streams of 256 tiles
     W, rows = 256, 8 * 4
-    want = al(W * 2 * rows * 128 * 4) + al(W * 2 * rows * 4) + al(W * 4) + 2 * al(64 * 4)
+    want = 256 + al(W * 2 * rows * 128 * 4) + al(W * 2 * rows * 4) + al(W * 4) + 2 * al(64 * 4)
     assert L.lgm_paged_decode_workspace_size(d, 8192, 0, L.LGM_BF16) == want
     assert L.lgm_paged_decode_workspace_size(d, 8192, 0, L.LGM_FP8_E4M3) == want
     assert L.lgm_paged_decode_workspace_size(d, 8192, 0, L.LGM_FP4_E2M1) == want
     small = dims(num_seqs=2, num_q_heads=16, num_kv_heads=4, max_blocks_per_seq=8)  # 2 x 4 tiles: one range
     W, rows = 1, 4 * 4
     assert L.lgm_paged_decode_workspace_size(small, 100, 0, L.LGM_BF16) == (
-        al(W * 2 * rows * 128 * 4) + al(W * 2 * rows * 4) + al(W * 4) + 2 * al(2 * 4))
+        256 + al(W * 2 * rows * 128 * 4) + al(W * 2 * rows * 4) + al(W * 4) + 2 * al(2 * 4))
 
 
 def test_too_many_partitions_is_unsupported():

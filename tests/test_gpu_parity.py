@@ -297,6 +297,12 @@ def test_lse_merge_standalone(out_dtype):
     pl = (rng.standard_normal((B, H, P)) * 6).astype(np.float32)
     pl[1, :, 3] = -np.inf
     pl[2] = -np.inf                     # a sequence whose records are all empty
+    # empty records weigh exactly zero whatever their rows hold
+    po[1, :, 3] = np.nan
+    po[2, :, ::2] = np.inf
+    po[2, :, 1::2] = np.nan
+    pl[4, :, 0] = -np.inf               # n = 1 and that record empty
+    po[4, :, 0, :7] = -np.inf
     n = np.array([37, 5, 37, 0, 1], np.int32)
     announce("lse_merge", out_dtype)
     out, lse = ops.lse_merge(torch.from_numpy(po).cuda(), torch.from_numpy(pl).cuda(),
@@ -305,6 +311,7 @@ def test_lse_merge_standalone(out_dtype):
     r_out, r_lse = OA.lse_merge(po, pl, n)
     g = out.float().cpu().numpy().astype(np.float64)
     tol = 1e-5 if out_dtype == torch.float32 else 2e-2
+    assert np.isfinite(g).all() and np.isfinite(r_out).all()
     assert np.abs(g - r_out).max() <= tol
     _lse_check(lse.cpu().numpy(), r_lse)
     # without counts: every record is used
@@ -353,6 +360,34 @@ def test_persistent_workspace_is_reusable_and_left_zeroed(name, ps):
     r_out, r_lse = oracle_attention(w, act_raw(w, q_from_qkv(w)), pool_raw(w, w.k_pool), pool_raw(w, w.v_pool))
     assert max_abs(out_values(cfg, outs[0][0]), r_out) <= TOL["bf16"]
     _lse_check(outs[0][1].cpu().numpy(), r_lse)
+
+
+@pytest.mark.parametrize("name", ["llama3_8b_gqa", "fp8_kv"])
+def test_one_workspace_serves_every_plan(name):
+    """One zero-filled workspace shared by calls on different plans in turn:
+    equal ranges (partition_size 0), the whole-row partition plan, the work
+    queue (partitions of 64) and equal ranges again.  No plan but the work
+    queue touches the counter slot at its start, and the work queue leaves it
+    zero, so every call matches the oracle and the slot ends at zero."""
+    cfg = W.CONFIGS[name].with_(num_seqs=12, ctx=(1, 20000), num_blocks=None, append=False)
+    w = W.make_workload(cfg)
+    d = to_device(w)
+    q = q_from_qkv(w).cuda()
+    mc = d.max_ctx
+    plans = [0, 256, 64, 0, 64]
+    assert ops.partition_size(q, d.k_pool, d.block_tables, mc, 0) == 0  # equal ranges
+    nbytes = max(ops.workspace_bytes(q, d.k_pool, d.block_tables, mc, ps) for ps in plans)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    announce("shared workspace across plans", name, plans, nbytes)
+    r_out, r_lse = oracle_attention(w, act_raw(w, q_from_qkv(w)), pool_raw(w, w.k_pool), pool_raw(w, w.v_pool))
+    for ps in plans:
+        o, l = ops.paged_decode_attn(q, d.k_pool, d.v_pool, d.block_tables, d.context_lens, mc,
+                                     softmax_scale=cfg.softmax_scale, partition_size=ps, k_scale=d.k_scale,
+                                     v_scale=d.v_scale, workspace=ws)
+        torch.cuda.synchronize()
+        assert int(ws[:256].view(torch.int32).abs().sum()) == 0, ps
+        assert max_abs(out_values(cfg, o), r_out) <= TOL["bf16"], ps
+        _lse_check(l.cpu().numpy(), r_lse)
 
 
 @pytest.mark.parametrize("ps", [0, 16, 32])

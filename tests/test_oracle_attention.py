@@ -179,6 +179,17 @@ def test_merge_identity_order_and_empty_partition():
     keep = [0, 1, 3, 4]
     d, dl = A.lse_merge(o[:, :, keep], l[:, :, keep])
     assert np.abs(c - d).max() <= 1e-14 and np.abs(cl - dl).max() <= 1e-14
+    # an empty record weighs exactly zero whatever its row holds: memory
+    # nobody wrote may be NaN or Inf
+    o2 = o.copy()
+    o2[0, :, 2] = np.nan
+    o2[1, :, 2] = np.inf
+    o2[1, 0, 2, ::2] = -np.inf
+    c2, cl2 = A.lse_merge(o2, l2)
+    assert np.array_equal(c2, c) and np.array_equal(cl2, cl)
+    # all records empty: out = 0 and lse = -inf, even over NaN rows
+    z, zl = A.lse_merge(np.full((1, 2, 3, 4), np.nan), np.full((1, 2, 3), -np.inf))
+    assert np.array_equal(z, np.zeros((1, 2, 4))) and np.isneginf(zl).all()
     # counts limit each sequence to its first P_b records
     e, el = A.lse_merge(o, l, np.array([2, 5]))
     f, fl = A.lse_merge(o[:1, :, :2], l[:1, :, :2])

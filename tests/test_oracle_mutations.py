@@ -111,6 +111,25 @@ def test_merge_without_normalisation_is_caught(monkeypatch):
     _fails(T_A.test_merge_closed_form_two_partitions)
 
 
+def test_merge_reading_empty_rows_is_caught(monkeypatch):
+    def bad(o_p, lse_p, num_parts=None):
+        o_p, lse_p = np.asarray(o_p, np.float64), np.asarray(lse_p, np.float64)
+        B, H, P, D = o_p.shape
+        out, lse = np.zeros((B, H, D)), np.full((B, H), -np.inf)
+        for b in range(B):
+            n = P if num_parts is None else int(num_parts[b])
+            for h in range(H):
+                ls = lse_p[b, h, :n]
+                if n == 0 or not np.isfinite(ls).any():
+                    continue
+                w = np.exp(ls - ls.max())  # 0 for an empty record, then 0 * NaN = NaN
+                out[b, h] = (w[:, None] * o_p[b, h, :n]).sum(0) / w.sum()
+                lse[b, h] = ls.max() + np.log(w.sum())
+        return out, lse
+    monkeypatch.setattr(A, "lse_merge", bad)
+    _fails(T_A.test_merge_identity_order_and_empty_partition)
+
+
 def test_append_at_wrong_position_is_caught(monkeypatch):
     orig = AP.rope_kv_append
     def bad(qkv, context_lens, *a, **k):
