@@ -261,7 +261,7 @@ def traffic_summary(workload: str, fetch_csv: str, write_csv: str, copy_fetch_cs
     write = _counter_means(write_csv, "WRITE_SIZE")
     kernels = {}
     for name in fetch:
-        if any(k in name for k in ATTN_KERNELS):
+        if any(k in name for k in ATTN_KERNELS + ("paged_mla",)):
             kernels[name] = {"fetch_bytes": fetch[name] * 1024.0 * f_fetch,
                              "write_bytes": write.get(name, 0.0) * 1024.0 * f_write}
     total = sum(v["fetch_bytes"] + v["write_bytes"] for v in kernels.values())
@@ -273,6 +273,82 @@ def traffic_summary(workload: str, fetch_csv: str, write_csv: str, copy_fetch_cs
     with open(os.path.join(ROOT, "profiles", f"traffic_{workload}.json"), "w") as fh:
         json.dump(rec, fh, indent=1)
     print(json.dumps(rec, indent=1))
+    return 0
+
+
+# MI355X: 256 compute units of 4 SIMDs in 8 XCDs (GRBM_GUI_ACTIVE is counted once per XCD).
+NUM_CU, SIMD_PER_CU, NUM_XCD = 256, 4, 8
+
+
+def _dispatch_counters(paths):
+    """{kernel: {counter: [value per dispatch]}} from rocprofv3 counter_collection.csv files; the rows of
+    one dispatch and counter (one per hardware instance, or one already summed) are added."""
+    import csv
+    import collections
+
+    per = collections.defaultdict(float)
+    names = {}
+    for path in paths:
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                key = (path, r["Dispatch_Id"], r["Counter_Name"])
+                per[key] += float(r["Counter_Value"])
+                names[(path, r["Dispatch_Id"])] = r["Kernel_Name"]
+    out = collections.defaultdict(lambda: collections.defaultdict(list))
+    for (path, disp, counter), v in per.items():
+        out[names[(path, disp)]][counter].append(v)
+    return out
+
+
+def counter_summary(workload: str, paths, commands: list) -> int:
+    """Per-kernel means of the SQ/GRBM counters of rocprofv3 --pmc runs of the bench, and the shares they
+    give (wave-lifetime shares of VALU issue, memory issue and waiting; MFMA busy per SIMD-cycle of the
+    kernel's span); writes profiles/counters_<workload>.json."""
+    data = _dispatch_counters(paths)
+    kernels = {}
+    for name, cs in data.items():
+        if not any(k in name for k in ATTN_KERNELS + ("paged_mla", "rope_kv_append")):
+            continue
+        mean = {c: sum(v) / len(v) for c, v in cs.items()}
+        rec = {"dispatches": max(len(v) for v in cs.values()), "counters": mean}
+        wave = mean.get("SQ_WAVE_CYCLES")
+        gui = mean.get("GRBM_GUI_ACTIVE")
+        derived = {}
+        if wave:
+            for c, label in (("SQ_ACTIVE_INST_VALU", "valu_active_share_of_wave_cycles"),
+                             ("SQ_ACTIVE_INST_VMEM", "vmem_issue_share_of_wave_cycles"),
+                             ("SQ_WAIT_INST_ANY", "wait_inst_any_share_of_wave_cycles"),
+                             ("SQ_WAIT_ANY", "wait_any_share_of_wave_cycles"),
+                             ("SQ_ACTIVE_INST_ANY", "any_issue_share_of_wave_cycles")):
+                if c in mean:
+                    derived[label] = round(mean[c] / wave, 4)
+        if gui:
+            span = gui / NUM_XCD  # cycles of the kernel's span, per XCD
+            derived["span_cycles_per_xcd"] = round(span, 1)
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in mean:
+                derived["mfma_busy_pct"] = round(100.0 * mean["SQ_VALU_MFMA_BUSY_CYCLES"] /
+                                                 (span * NUM_CU * SIMD_PER_CU), 2)
+            if "SQ_ACTIVE_INST_VALU" in mean:
+                derived["valu_busy_pct"] = round(100.0 * mean["SQ_ACTIVE_INST_VALU"] / NUM_CU / span, 2)
+            if "SQ_BUSY_CYCLES" in mean:
+                derived["sq_busy_cycles_per_xcd"] = round(mean["SQ_BUSY_CYCLES"] / NUM_XCD, 1)
+        if "SQ_WAVES" in mean and mean["SQ_WAVES"]:
+            for c in ("SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_VMEM_RD", "SQ_INSTS_SALU", "SQ_INSTS_VALU_CVT",
+                      "SQ_INSTS_VALU_TRANS_F32", "SQ_INSTS_LDS"):
+                if c in mean:
+                    derived[c.lower().replace("sq_insts_", "insts_per_wave_")] = round(mean[c] / mean["SQ_WAVES"], 1)
+        rec["derived"] = derived
+        kernels[name] = rec
+    out = {"workload": workload, "kernel_source_hash": kernel_source_hash(), "kernels": kernels,
+           "commands": commands,
+           "notes": "counters summed over hardware instances per dispatch, then averaged over dispatches; "
+                    "SQ_WAVE_CYCLES, SQ_ACTIVE_INST_*, SQ_WAIT_* in the same (quad-cycle) units; "
+                    f"MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / {NUM_XCD} * {NUM_CU * SIMD_PER_CU} "
+                    f"SIMDs); VALU busy = SQ_ACTIVE_INST_VALU / {NUM_CU} CUs / (GRBM_GUI_ACTIVE / {NUM_XCD})"}
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(os.path.join(ROOT, "profiles", f"counters_{workload}.json"), "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps(out, indent=1))
     return 0
 
 
@@ -491,8 +567,12 @@ def main() -> int:
     ap.add_argument("--traffic-summary", nargs=5, default=None,
                     metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV", "COPY_BYTES"),
                     help="write profiles/traffic_<workload>.json from rocprofv3 counter_collection.csv files")
+    ap.add_argument("--counter-summary", nargs="+", default=None, metavar="CSV",
+                    help="write profiles/counters_<workload>.json from rocprofv3 counter_collection.csv files")
     ap.add_argument("--commands", nargs="*", default=[], help="the profiling command lines, recorded with the summary")
     args = ap.parse_args()
+    if args.counter_summary:
+        return counter_summary(args.workload, args.counter_summary, args.commands)
     if args.traffic_summary:
         f, w_, cf, cw, cb = args.traffic_summary
         return traffic_summary(args.workload, f, w_, cf, cw, int(cb), args.commands)

@@ -32,7 +32,10 @@ UNITS = {
     "rope_kv_append.hip": ["-ffp-contract=off"],
     "paged_decode.hip": [],
     "paged_decode_mfma.hip": [],
-    "paged_decode_rows.hip": [],
+    # MFMA accumulators in VGPRs: the whole-row step loop then keeps them in
+    # the registers its MFMAs use instead of copying them between register
+    # files around every step.
+    "paged_decode_rows.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "lse_merge.hip": [],
     "stream_probe.hip": [],
     "paged_mla.hip": [],

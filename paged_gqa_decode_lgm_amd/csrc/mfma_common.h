@@ -77,10 +77,13 @@ __device__ __forceinline__ float sum4(float x) {
 // intrinsic calls, which the compiler keeps where the software pipeline puts
 // them (plain loads carried around the tile loop get merged into a single
 // load at the loop head, right before their use).
+// An absent block (pb < 0: past the segment, or an out-of-range table
+// entry) gets a descriptor of size zero at the pool's start: every load
+// through it returns zeros without touching memory, and the step masks it.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const void* pool, int64_t block_bytes, int pb) {
   return __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<char*>(static_cast<const char*>(pool) + (int64_t)pb * block_bytes), (short)0, (int)block_bytes,
-      0x00020000);
+      const_cast<char*>(static_cast<const char*>(pool) + (int64_t)max(pb, 0) * block_bytes), (short)0,
+      pb >= 0 ? (int)block_bytes : 0, 0x00020000);
 }
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t span_rsrc(const void* base, int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
@@ -149,6 +152,7 @@ __device__ __forceinline__ uint32_t fp4x2_to_bf16x2(uint32_t w, float scale) {
 
 struct MfmaBF16 {
   static constexpr bool kFp8 = false;
+  static constexpr int kStepBlocks = 2;  // see step_blocks
   using elem_t = uint16_t;
   static constexpr int kRowBytes = kD * 2;  // one (token, kv head) row
   static constexpr int kScaleRowBytes = 0;
@@ -192,6 +196,7 @@ struct MfmaBF16 {
 
 struct MfmaFP8 {
   static constexpr bool kFp8 = true;
+  static constexpr int kStepBlocks = 2;
   using elem_t = uint8_t;
   static constexpr int kRowBytes = kD;
   static constexpr int kScaleRowBytes = 0;
@@ -244,6 +249,7 @@ struct MfmaFP8 {
 // first), then scales [16][Hkv][4 bytes] (E8M0, one per 32 head-dim elements).
 struct MfmaFP4 {
   static constexpr bool kFp8 = false;
+  static constexpr int kStepBlocks = 2;
   using elem_t = uint8_t;
   static constexpr int kRowBytes = kD / 2;        // codes of one (token, kv head) row
   static constexpr int kScaleRowBytes = kD / 32;  // its scales
@@ -317,10 +323,6 @@ __device__ __forceinline__ int score_d(int c, int kg, int j) {
   return C::score_d(c, kg, j);
 }
 
-
-// Query rows of a head group as the B operand of the score MFMAs (bf16 bit
-// patterns; zero for n >= G).  qrow points at head 0 of the group; 16-byte
-// loads when the rows are 16-byte aligned, element loads otherwise.
 // Query rows of a head group as the B operand of the score MFMAs (bf16 bit
 // patterns; zero for n >= G).  qrow points at head 0 of the group.  Aligned
 // rows are read with 16-byte buffer loads (the same kind of load as the K/V
@@ -352,108 +354,183 @@ __device__ __forceinline__ void load_q_operand(short8 (&qb)[4], const uint16_t* 
   }
 }
 
-// Online-softmax state of one wave for one (sequence, kv head): running max
-// m of head n (log2 units, the same in its four lanes), this lane's shares of
-// the sums of rounded (lsum) and unrounded (lsum_e) probabilities, and the
-// output accumulator acc[i][j] = O[head 4kg + j][8n + i].
+// The score scale in log2 units (softmax_scale * log2(e), times the FP8 K
+// scale), made positive so that max(scale * s) = scale * max(s): a negative
+// scale flips the sign bits of the query operand instead, which is exact in
+// bf16.  A zero scale becomes the smallest normal float, so that a masked
+// score (-inf) still maps to -inf; every live score then maps to ~0, as it
+// would with a zero scale.
+__device__ __forceinline__ float fold_score_scale(float c, short8 (&qb)[4]) {
+  if (c < 0.f) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      uint4 u = __builtin_bit_cast(uint4, qb[k]);
+      u.x ^= 0x80008000u;
+      u.y ^= 0x80008000u;
+      u.z ^= 0x80008000u;
+      u.w ^= 0x80008000u;
+      qb[k] = __builtin_bit_cast(short8, u);
+    }
+  }
+  const float a = fabsf(c);
+  return a == 0.f ? 1.17549435e-38f : a;
+}
+
+// Online-softmax state of one wave for one (sequence, kv head), against a
+// lazily moved reference: m is the reference of head n in log2 units (the
+// same in its four lanes; -inf until the head has a live score) and ms the
+// offset the exponentials use (m, or 0 while m is -inf).  The reference moves
+// only when a step's maximum passes it by more than kRescaleGap, so
+// probabilities stay below 2^kRescaleGap and the accumulators are rescaled a
+// handful of times per context instead of at every new maximum; any
+// reference gives the same normalised output and log-sum-exp.
+//   lsum_e  this lane's share of the sum of the fp32 probabilities (the LSE)
+//   psum    sums of the bf16-rounded probabilities of heads 4kg .. 4kg+3
+//           (from an MFMA against a column of ones; every column holds the
+//           same sum): the output is normalised by the sum of the rounded
+//           values it was built from, an exact convex combination of V rows
+//   acc     acc[i][j] = O[head 4kg + j][8n + i]
+constexpr float kRescaleGap = 8.f;
+
 struct WaveState {
-  float m, lsum, lsum_e;
+  float m, ms, lsum_e;
+  float4v psum;
   float4v acc[8];
   __device__ __forceinline__ void reset() {
     m = -INFINITY;
-    lsum = 0.f;
+    ms = 0.f;
     lsum_e = 0.f;
+    psum = (float4v){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = (float4v){0.f, 0.f, 0.f, 0.f};
   }
 };
 
-// Registers of one 32-token tile (blocks x and y).
+// Blocks of 16 tokens a wave takes per step (every format: 2, one 32-token
+// tile).  The step code takes any even count.  Steps of 64 tokens for FP8
+// (16 KB of K and V per step, the bytes of a bf16 step) halved the vector
+// instructions per byte but made the FP8 call slower (136 against 127 us on
+// 128 contexts of 1024..4096 tokens): a copy of the kernel that only loads
+// reached 118.6 us with 32-token steps and 120.9 us with 64-token steps, so
+// the FP8 call is bound by how the memory system serves the reads, not by
+// the bytes each wave keeps in flight; the larger steps only added register
+// pressure (SGPR spills).  FP4's eight-wave kernel spilled to scratch with
+// 64-token steps.
 template <class C>
-struct TileRegs {
-  typename C::KBlock kx, ky;
-  typename C::VBlock vx, vy;
+constexpr int step_blocks() {
+  return C::kStepBlocks;
+}
+
+// Registers of one step: NB consecutive 16-token blocks of one kv head.
+template <class C, int NB>
+struct StepRegs {
+  typename C::KBlock k[NB];
+  typename C::VBlock v[NB];
 };
 
-template <class C>
-__device__ __forceinline__ void tile_scores(const TileRegs<C>& r, const short8 (&qb)[4], float4v& sx, float4v& sy) {
-  sx = (float4v){0.f, 0.f, 0.f, 0.f};
-  sy = (float4v){0.f, 0.f, 0.f, 0.f};
+// Raw scores of a step: s[b][j] = <q_n, K[token 4kg + j of block b]>.
+template <class C, int NB>
+__device__ __forceinline__ void step_scores(const StepRegs<C, NB>& r, const short8 (&qb)[4], float4v (&s)[NB]) {
+#pragma unroll
+  for (int b = 0; b < NB; ++b) s[b] = (float4v){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
-    sx = __builtin_amdgcn_mfma_f32_16x16x32_bf16(C::k_operand(r.kx, c), qb[c], sx, 0, 0, 0);
-    sy = __builtin_amdgcn_mfma_f32_16x16x32_bf16(C::k_operand(r.ky, c), qb[c], sy, 0, 0, 0);
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+      s[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(C::k_operand(r.k[b], c), qb[c], s[b], 0, 0, 0);
   }
 }
 
-// Softmax update and output MFMAs for one tile whose scores are sx / sy.
-// xval / yval: the blocks are present with valid table entries; tok0: first
-// token of the tile, end: one past the last valid token (same origin).
-// Masked rows get -inf scores and zeroed V rows (V there may hold anything,
-// even NaN, and a zero probability must contribute exactly zero).
-template <class C>
-__device__ __forceinline__ void tile_update(WaveState& st, TileRegs<C>& r, const float4v& sx, const float4v& sy,
-                                            float sscale, bool xval, bool yval, int tok0, int end, int kg) {
-  float s[8];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    s[j] = xval ? sx[j] * sscale : -INFINITY;
-    s[4 + j] = yval ? sy[j] * sscale : -INFINITY;
-  }
-  if (!xval || !yval || tok0 + kTile > end) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (tok0 + 4 * kg + j >= end) s[j] = -INFINITY;
-      if (tok0 + kBS + 4 * kg + j >= end) s[4 + j] = -INFINITY;
-      if (!xval || tok0 + 4 * kg + j >= end) C::zero_v_row(r.vx, j);
-      if (!yval || tok0 + kBS + 4 * kg + j >= end) C::zero_v_row(r.vy, j);
-    }
-  }
-  float tmax = s[0];
-#pragma unroll
-  for (int j = 1; j < 8; ++j) tmax = fmaxf(tmax, s[j]);
-  tmax = max4(tmax);
-  const float mn = fmaxf(st.m, tmax);
+// Moves the reference of every head of the wave to max(m, ts) and rescales
+// the sums and accumulators by 2^(m_old - m_new): row j of lane group kg is
+// head 4kg + j, whose factor sits in lane 4kg + j.  Taken rarely; the
+// rescaled accumulators go back through an MFMA with zero operands, so that
+// outside this branch they stay in the registers the MFMAs use (a plain
+// multiply made the compiler copy every accumulator out and back around the
+// branch on every step).
+__device__ __forceinline__ void rescale(WaveState& st, float ts, int kg) {
+  const float mn = fmaxf(st.m, ts);
   const float ms = mn == -INFINITY ? 0.f : mn;
-  const float alpha = fast_exp2(st.m - ms);
+  const float alpha = fast_exp2(st.m - ms);  // 0 before the first live score
   st.m = mn;
-  // Probabilities, rounded to bf16 once for the output MFMAs; the output is
-  // normalised by the sum of those rounded values (an exact convex
-  // combination of V rows) and the log-sum-exp uses the unrounded sum.
-  uint32_t pw[4];
-  float psum = 0.f, psum_e = 0.f;
+  st.ms = ms;
+  st.lsum_e *= alpha;
+  float4v a4;
 #pragma unroll
-  for (int t2 = 0; t2 < 4; ++t2) {
-    const float p0 = fast_exp2(s[2 * t2] - ms);
-    const float p1 = fast_exp2(s[2 * t2 + 1] - ms);
-    pw[t2] = pack_bf16(p0, p1);
-    psum += bf16_lo(pw[t2]) + bf16_hi(pw[t2]);
-    psum_e += p0 + p1;
-  }
-  st.lsum = st.lsum * alpha + psum;
-  st.lsum_e = st.lsum_e * alpha + psum_e;
-  // Rescale the accumulator rows: row j of lane group kg is head 4kg + j,
-  // whose alpha sits in lane 4kg + j.
-  if (__any(alpha != 1.f)) {
+  for (int j = 0; j < 4; ++j) a4[j] = __shfl(alpha, 4 * kg + j);
+  const short8 z = {0, 0, 0, 0, 0, 0, 0, 0};
+  st.psum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(z, z, st.psum * a4, 0, 0, 0);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float aj = __shfl(alpha, 4 * kg + j);
+  for (int i = 0; i < 8; ++i) st.acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(z, z, st.acc[i] * a4, 0, 0, 0);
+}
+
+// Softmax update and output MFMAs of one step whose raw scores are s.
+// csc: the positive score scale (fold_score_scale); valid: bit b set when
+// block b is present with a valid table entry (uniform); tok0: first token
+// of the step; end: one past the last valid token (same origin).  On an edge
+// step (a block absent, or the context ending inside the step) masked rows
+// get -inf scores and zeroed V rows: V there may hold anything, even NaN,
+// and a zero probability must contribute exactly zero.
+template <class C, int NB>
+__device__ __forceinline__ void step_update(WaveState& st, StepRegs<C, NB>& r, float4v (&s)[NB], float csc,
+                                            uint32_t valid, int tok0, int end, int kg) {
+  static_assert(NB % 2 == 0, "steps are whole 32-token tiles");
+  constexpr uint32_t kAll = (1u << NB) - 1u;
+  if (__builtin_expect(valid != kAll || tok0 + NB * kBS > end, 0)) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) st.acc[i][j] *= aj;
+    for (int b = 0; b < NB; ++b) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (!((valid >> b) & 1u) || tok0 + kBS * b + 4 * kg + j >= end) {
+          s[b][j] = -INFINITY;
+          C::zero_v_row(r.v[b], j);
+        }
+      }
     }
   }
-  // P operand: head n, tokens x rows 4kg..4kg+3 then y rows 4kg..4kg+3.
-  const short8 pa = words_to_short8(pw[0], pw[1], pw[2], pw[3]);
+  float tmax = s[0][0];
 #pragma unroll
-  for (int i = 0; i < 8; i += 2) {
-    uint32_t a0, a1, b0, b1, c0, c1, d0, d1;
-    C::v_pairs2(r.vx, 0, i, a0, a1);
-    C::v_pairs2(r.vx, 2, i, b0, b1);
-    C::v_pairs2(r.vy, 0, i, c0, c1);
-    C::v_pairs2(r.vy, 2, i, d0, d1);
-    st.acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, words_to_short8(a0, b0, c0, d0), st.acc[i], 0, 0, 0);
-    st.acc[i + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, words_to_short8(a1, b1, c1, d1), st.acc[i + 1], 0, 0, 0);
+  for (int b = 0; b < NB; ++b) {
+#pragma unroll
+    for (int j = (b == 0 ? 1 : 0); j < 4; ++j) tmax = fmaxf(tmax, s[b][j]);
   }
+  tmax = max4(tmax);
+  const float ts = tmax == -INFINITY ? -INFINITY : tmax * csc;
+  if (__builtin_expect(__any(ts > st.m + kRescaleGap), 0)) rescale(st, ts, kg);
+  // Probabilities 2^(csc * s - ms), rounded to bf16 once for the output
+  // MFMAs.  P operand of block pair q: head n, tokens rows 4kg..4kg+3 of
+  // block 2q then of block 2q+1, exactly as the score MFMAs left them.
+  const float nms = -st.ms;
+  const short8 ones = {0x3F80, 0x3F80, 0x3F80, 0x3F80, 0x3F80, 0x3F80, 0x3F80, 0x3F80};  // bf16 1.0
+  float pe = 0.f;
+#pragma unroll
+  for (int q = 0; q < NB / 2; ++q) {
+    uint32_t pw[4];
+#pragma unroll
+    for (int t2 = 0; t2 < 4; ++t2) {
+      const float4v& sb = s[2 * q + (t2 >> 1)];
+      const float p0 = fast_exp2(fmaf(sb[2 * (t2 & 1)], csc, nms));
+      const float p1 = fast_exp2(fmaf(sb[2 * (t2 & 1) + 1], csc, nms));
+      pw[t2] = pack_bf16(p0, p1);
+      pe += p0 + p1;
+    }
+    const short8 pa = words_to_short8(pw[0], pw[1], pw[2], pw[3]);
+    st.psum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, ones, st.psum, 0, 0, 0);
+    const typename C::VBlock& vx = r.v[2 * q];
+    const typename C::VBlock& vy = r.v[2 * q + 1];
+#pragma unroll
+    for (int i = 0; i < 8; i += 2) {
+      uint32_t a0, a1, b0, b1, c0, c1, d0, d1;
+      C::v_pairs2(vx, 0, i, a0, a1);
+      C::v_pairs2(vx, 2, i, b0, b1);
+      C::v_pairs2(vy, 0, i, c0, c1);
+      C::v_pairs2(vy, 2, i, d0, d1);
+      st.acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, words_to_short8(a0, b0, c0, d0), st.acc[i], 0, 0, 0);
+      st.acc[i + 1] =
+          __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, words_to_short8(a1, b1, c1, d1), st.acc[i + 1], 0, 0, 0);
+    }
+  }
+  st.lsum_e += pe;
 }
 
 }  // namespace mfma

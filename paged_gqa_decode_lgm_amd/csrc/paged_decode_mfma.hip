@@ -130,10 +130,12 @@ struct DecodeSmem {
 
 // One item's values, uniform across the workgroup.
 struct Item {
-  int b, g, part, nparts, start, end, ntiles;
+  int b, g, part, nparts, start, end, nsteps;
 };
 
+template <class C>
 __device__ __forceinline__ Item read_item(const DecodeArgs& p, const ItemSlot& sl) {
+  constexpr int kStepTokens = step_blocks<C>() * kBS;
   Item it;
   it.b = __builtin_amdgcn_readfirstlane(sl.b);
   it.g = __builtin_amdgcn_readfirstlane(sl.g);
@@ -141,124 +143,139 @@ __device__ __forceinline__ Item read_item(const DecodeArgs& p, const ItemSlot& s
   const int ctx = __builtin_amdgcn_readfirstlane(sl.ctx);
   it.nparts = p.parts.count(ctx);
   p.parts.range(ctx, it.part, it.start, it.end);
-  it.ntiles = (it.end - it.start + kTile - 1) / kTile;
+  it.nsteps = (it.end - it.start + kStepTokens - 1) / kStepTokens;
   return it;
 }
 
-// Tiles of the item this wave takes: wave, wave + 4, ...
-__device__ __forceinline__ int wave_tiles(const Item& it, int wave) {
-  return it.ntiles > wave ? (it.ntiles - wave + kNW - 1) / kNW : 0;
+// Steps of the item this wave takes: wave, wave + 4, ...
+__device__ __forceinline__ int wave_steps(const Item& it, int wave) {
+  return it.nsteps > wave ? (it.nsteps - wave + kNW - 1) / kNW : 0;
 }
 
-// Block ids of this wave's tiles k0 .. k0 + 31 of the item, one per lane
-// (lane 2k + h holds block h of the wave's tile k0 + k), read back with
-// readlane so no table load sits between a tile and its K/V loads.  -1 marks
-// an absent block (past the end) or an out-of-range table entry.
+// Block ids of this wave's steps k0 .. k0 + 64/NB - 1 of the item, one per
+// lane (lane NB*k + h holds block h of the wave's step k0 + k), read back
+// with readlane so no table load sits between a step and its K/V loads.  -1
+// marks an absent block (past the end) or an out-of-range table entry.
+template <int NB>
 __device__ __forceinline__ int preload_ids(const DecodeArgs& p, const Item& it, int k0, int lane, int wave) {
   const int MB = p.dims.max_blocks_per_seq;
   const __amdgpu_buffer_rsrc_t bt_rs = span_rsrc(p.block_tables + (int64_t)it.b * MB, MB * 4);
-  const int t = wave + kNW * (k0 + (lane >> 1));
-  const int lb = it.start / kBS + 2 * t + (lane & 1);
+  const int t = wave + kNW * (k0 + lane / NB);
+  const int lb = it.start / kBS + NB * t + lane % NB;
   const int lb_end = (it.end + kBS - 1) / kBS;
   const int id = buf_load4(bt_rs, 4 * (lb < MB ? lb : 0));
-  return (t < it.ntiles && lb < lb_end && (unsigned)id < (unsigned)p.dims.num_blocks) ? id : -1;
+  return (t < it.nsteps && lb < lb_end && (unsigned)id < (unsigned)p.dims.num_blocks) ? id : -1;
 }
 
-// Every tile issues the same loads: an absent or invalid block reads the
-// tile's other block (or block 0) instead and is masked, so the load count
-// per tile is fixed and the compiler can wait for K without waiting for V.
-template <class C>
-__device__ __forceinline__ void load_tile_k(const DecodeArgs& p, int g, int px, int py, int lane, TileRegs<C>& tr) {
+// Every step issues the same loads: an absent block's loads return zeros
+// without touching memory (block_rsrc) and the step masks it, so the load
+// count per step is fixed and the compiler can wait for K without waiting
+// for V.
+template <class C, int NB>
+__device__ __forceinline__ void load_step_k(const DecodeArgs& p, int g, const int (&id)[NB], int lane,
+                                            StepRegs<C, NB>& sr) {
   const KVLayout L = kv_layout<C>(p.flags, p.dims.num_kv_heads);
   const int off = C::k_lane_off(L, g, lane & 15, lane >> 4);
   const int soff = C::k_scale_off(L, g, lane & 15, lane >> 4);
-  const int ex = px >= 0 ? px : 0, ey = py >= 0 ? py : ex;
-  C::load_k(tr.kx, block_rsrc(p.k_cache, L.block, ex), off, L, soff);
-  C::load_k(tr.ky, block_rsrc(p.k_cache, L.block, ey), off, L, soff);
+#pragma unroll
+  for (int b = 0; b < NB; ++b) C::load_k(sr.k[b], block_rsrc(p.k_cache, L.block, id[b]), off, L, soff);
 }
-template <class C>
-__device__ __forceinline__ void load_tile_v(const DecodeArgs& p, int g, int px, int py, int lane, TileRegs<C>& tr) {
+template <class C, int NB>
+__device__ __forceinline__ void load_step_v(const DecodeArgs& p, int g, const int (&id)[NB], int lane,
+                                            StepRegs<C, NB>& sr) {
   const KVLayout L = kv_layout<C>(p.flags, p.dims.num_kv_heads);
   const int off = C::v_lane_off(L, g, lane & 15, lane >> 4);
   const int soff = C::v_scale_off(L, g, lane & 15, lane >> 4);
-  const int ex = px >= 0 ? px : 0, ey = py >= 0 ? py : ex;
-  C::load_v(tr.vx, block_rsrc(p.v_cache, L.block, ex), off, L, soff);
-  C::load_v(tr.vy, block_rsrc(p.v_cache, L.block, ey), off, L, soff);
+#pragma unroll
+  for (int b = 0; b < NB; ++b) C::load_v(sr.v[b], block_rsrc(p.v_cache, L.block, id[b]), off, L, soff);
 }
 
-// Starts an item for this wave: the query operand, the block ids of its
-// first 32 tiles and the K/V loads of its first tile are issued here, so
-// that they are in flight while the previous item is merged and stored.
+// Starts an item for this wave: the query operand (with the score scale's
+// sign folded in; the positive scale is returned), the block ids of its first
+// steps and the K/V loads of its first step are issued here, so that they are
+// in flight while the previous item is merged and stored.
 template <class C, int G>
-__device__ __forceinline__ void begin_item(const DecodeArgs& p, const Item& it, int lane, int wave, short8 (&qb)[4],
-                                           int& ids, int& px, int& py, TileRegs<C>& tr) {
+__device__ __forceinline__ float begin_item(const DecodeArgs& p, const Item& it, int lane, int wave, short8 (&qb)[4],
+                                            int& ids, int (&pid)[step_blocks<C>()],
+                                            StepRegs<C, step_blocks<C>()>& sr) {
+  constexpr int NB = step_blocks<C>();
   const bool qvec = ((uintptr_t)p.q % 16 == 0) && (p.q_seq_stride % 8 == 0);
   const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + (int64_t)it.b * p.q_seq_stride + (int64_t)it.g * G * kD;
   load_q_operand<C, G>(qb, qrow, qvec, lane & 15, lane >> 4);
-  if (wave_tiles(it, wave) > 0) {
-    ids = preload_ids(p, it, 0, lane, wave);
-    px = __builtin_amdgcn_readlane(ids, 0);
-    py = __builtin_amdgcn_readlane(ids, 1);
-    load_tile_k<C>(p, it.g, px, py, lane, tr);
-    __builtin_amdgcn_sched_barrier(0);  // K before V, as inside the tile loop
-    load_tile_v<C>(p, it.g, px, py, lane, tr);
+  float c = p.softmax_scale * kLog2e;
+  if constexpr (C::kFp8) c *= kv_scale(p.k_scale, p.flags, it.g);
+  const float csc = fold_score_scale(c, qb);
+  if (wave_steps(it, wave) > 0) {
+    ids = preload_ids<NB>(p, it, 0, lane, wave);
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb) pid[bb] = __builtin_amdgcn_readlane(ids, bb);
+    load_step_k<C, NB>(p, it.g, pid, lane, sr);
+    __builtin_amdgcn_sched_barrier(0);  // K before V, as inside the step loop
+    load_step_v<C, NB>(p, it.g, pid, lane, sr);
   }
+  return csc;
 }
 
-// The wave's tiles of an item into st.  One register set per operand: the
-// next tile's K loads are issued as soon as the score MFMAs have consumed the
+// The wave's steps of an item into st.  One register set per operand: the
+// next step's K loads are issued as soon as the score MFMAs have consumed the
 // current K, and its V loads as soon as the output MFMAs have consumed the
-// current V, so loads stay in flight through all of a tile's arithmetic.
-// Wave 0's lane 0 claims the workgroup's next item two tiles before the end
+// current V, so loads stay in flight through all of a step's arithmetic.
+// Wave 0's lane 0 claims the workgroup's next item two steps before the end
 // (into `next`): late enough that items are claimed in about the order they
 // start, early enough that the claim is back before the merge needs it.
 template <class C, int G>
-__device__ __forceinline__ void run_tiles(const DecodeArgs& p, const Item& it, int lane, int wave,
-                                          const short8 (&qb)[4], int ids, int px, int py, TileRegs<C>& tr,
-                                          WaveState& st, int& next) {
-  float sscale = p.softmax_scale * kLog2e;
-  if constexpr (C::kFp8) sscale *= kv_scale(p.k_scale, p.flags, it.g);
-  const int my_tiles = wave_tiles(it, wave);
-  const int claim_at = my_tiles > 2 ? my_tiles - 2 : 0;
+__device__ __forceinline__ void run_steps(const DecodeArgs& p, const Item& it, int lane, int wave,
+                                          const short8 (&qb)[4], float csc, int ids, int (&pid)[step_blocks<C>()],
+                                          StepRegs<C, step_blocks<C>()>& sr, WaveState& st, int& next) {
+  constexpr int NB = step_blocks<C>();
+  constexpr int SPW = kWaveSize / NB;  // steps per window of block ids
+  const int my_steps = wave_steps(it, wave);
+  const int claim_at = my_steps > 2 ? my_steps - 2 : 0;
   const bool claimer = wave == 0;
-  if (claimer && my_tiles == 0 && lane == 0) next = (int)gridDim.x + atomicAdd(p.work_counters, 1);
-  for (int k = 0; k < my_tiles; ++k) {
+  if (claimer && my_steps == 0 && lane == 0) next = (int)gridDim.x + atomicAdd(p.work_counters, 1);
+  for (int k = 0; k < my_steps; ++k) {
     if (claimer && k == claim_at && lane == 0) next = (int)gridDim.x + atomicAdd(p.work_counters, 1);
     const int t = wave + kNW * k;
-    float4v sx, sy;
-    tile_scores<C>(tr, qb, sx, sy);
-    // Next tile's K.  After the last tile the current blocks are read again
-    // (cache hits, results unused) so that every iteration issues the same
-    // loads in the same order and the compiler can wait for K alone.
-    int nx = px, ny = py;
-    if (k + 1 < my_tiles) {
-      if (((k + 1) & 31) == 0) ids = preload_ids(p, it, k + 1, lane, wave);
-      nx = __builtin_amdgcn_readlane(ids, 2 * ((k + 1) & 31));
-      ny = __builtin_amdgcn_readlane(ids, 2 * ((k + 1) & 31) + 1);
+    float4v s[NB];
+    step_scores<C, NB>(sr, qb, s);
+    // Next step's K.  After the last step the blocks are absent, so every
+    // iteration issues the same loads in the same order and the compiler can
+    // wait for K alone.
+    int nid[NB];
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb) nid[bb] = -1;
+    if (k + 1 < my_steps) {
+      if (((k + 1) % SPW) == 0) ids = preload_ids<NB>(p, it, k + 1, lane, wave);
+#pragma unroll
+      for (int bb = 0; bb < NB; ++bb) nid[bb] = __builtin_amdgcn_readlane(ids, NB * ((k + 1) % SPW) + bb);
     }
-    load_tile_k<C>(p, it.g, nx, ny, lane, tr);
-    tile_update<C>(st, tr, sx, sy, sscale, px >= 0, py >= 0, it.start + kTile * t, it.end, lane >> 4);
-    load_tile_v<C>(p, it.g, nx, ny, lane, tr);
-    px = nx;
-    py = ny;
+    load_step_k<C, NB>(p, it.g, nid, lane, sr);
+    uint32_t valid = 0;
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb) valid |= (pid[bb] >= 0 ? 1u : 0u) << bb;
+    step_update<C, NB>(st, sr, s, csc, valid, it.start + NB * kBS * t, it.end, lane >> 4);
+    load_step_v<C, NB>(p, it.g, nid, lane, sr);
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb) pid[bb] = nid[bb];
   }
 }
 
 // Wave epilogue: complete the denominators and publish this wave's state.
+// The rounded-probability sum of head 4kg + j sits in psum[j] of lane group
+// kg; the reference and the fp32 sum of head n in lane n.
 template <int G>
 __device__ __forceinline__ void publish_state(DecodeSmem<G>& sm, int buf, const WaveState& st, int lane, int wave) {
   const int n = lane & 15, kg = lane >> 4;
-  const float lsum = sum4(st.lsum);
   const float lsum_e = sum4(st.lsum_e);
   if (kg == 0 && n < G) {
     sm.m[buf][wave][n] = st.m;
-    sm.l[buf][wave][n] = lsum;
     sm.le[buf][wave][n] = lsum_e;
   }
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int h = 4 * kg + j;
     if (h < G) {
+      if (n == 0) sm.l[buf][wave][h] = st.psum[j];
 #pragma unroll
       for (int i = 0; i < 8; ++i) sm.acc[buf][wave][h][8 * n + i] = st.acc[i][j];
     }
@@ -328,26 +345,28 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void paged_decode_mfma_kernel(De
     cursor_locate(p, sm.cursor, blockIdx.x, lane, sm.slot[0]);
   }
   __syncthreads();
-  Item it = read_item(p, sm.slot[0]);
+  constexpr int NB = step_blocks<C>();
+  Item it = read_item<C>(p, sm.slot[0]);
   short8 qb[4];
-  TileRegs<C> tr;
-  int ids = 0, px = -1, py = -1;
-  if (it.b >= 0) begin_item<C, G>(p, it, lane, wave, qb, ids, px, py, tr);
+  StepRegs<C, NB> sr;
+  int ids = 0, pid[NB];
+  float csc = 1.f;
+  if (it.b >= 0) csc = begin_item<C, G>(p, it, lane, wave, qb, ids, pid, sr);
   for (int k = 0; it.b >= 0; ++k) {
     // Lane-derived addresses are loop-invariant; recomputing them per item
-    // (instead of keeping them live across every tile) keeps the tile loop
+    // (instead of keeping them live across every step) keeps the step loop
     // within its register budget.
     int lane_i = lane, tid_i = threadIdx.x;
     asm volatile("" : "+v"(lane_i), "+v"(tid_i));
     WaveState st;
     st.reset();
     int next = 0;
-    run_tiles<C, G>(p, it, lane_i, wave, qb, ids, px, py, tr, st, next);
+    run_steps<C, G>(p, it, lane_i, wave, qb, csc, ids, pid, sr, st, next);
     publish_state<G>(sm, k & 1, st, lane_i, wave);
     if (wave == 0) cursor_locate(p, sm.cursor, __builtin_amdgcn_readlane(next, 0), lane_i, sm.slot[(k + 1) & 1]);
     __syncthreads();
-    const Item nx = read_item(p, sm.slot[(k + 1) & 1]);
-    if (nx.b >= 0) begin_item<C, G>(p, nx, lane_i, wave, qb, ids, px, py, tr);
+    const Item nx = read_item<C>(p, sm.slot[(k + 1) & 1]);
+    if (nx.b >= 0) csc = begin_item<C, G>(p, nx, lane_i, wave, qb, ids, pid, sr);
     merge_and_store<C, G>(p, sm, k & 1, it, tid_i);
     it = nx;
   }

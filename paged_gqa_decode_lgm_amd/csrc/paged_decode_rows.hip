@@ -110,23 +110,25 @@ constexpr int row_policy() {
   return std::is_same<C, MfmaFP4>::value ? kDefaultPolicy : kStreamPolicy;
 }
 
-template <class C>
-__device__ __forceinline__ void row_load_k(const DecodeArgs& p, int g, int px, int py, int lane, TileRegs<C>& tr) {
+template <class C, int NB>
+__device__ __forceinline__ void row_load_k(const DecodeArgs& p, int g, const int (&id)[NB], int lane,
+                                           StepRegs<C, NB>& sr) {
   const KVLayout L = kv_layout<C>(p.flags, p.dims.num_kv_heads);
   const int off = C::k_lane_off(L, g, lane & 15, lane >> 4);
   const int soff = C::k_scale_off(L, g, lane & 15, lane >> 4);
-  const int ex = px >= 0 ? px : 0, ey = py >= 0 ? py : ex;
-  C::template load_k<row_policy<C>()>(tr.kx, block_rsrc(p.k_cache, L.block, ex), off, L, soff);
-  C::template load_k<row_policy<C>()>(tr.ky, block_rsrc(p.k_cache, L.block, ey), off, L, soff);
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+    C::template load_k<row_policy<C>()>(sr.k[b], block_rsrc(p.k_cache, L.block, id[b]), off, L, soff);
 }
-template <class C>
-__device__ __forceinline__ void row_load_v(const DecodeArgs& p, int g, int px, int py, int lane, TileRegs<C>& tr) {
+template <class C, int NB>
+__device__ __forceinline__ void row_load_v(const DecodeArgs& p, int g, const int (&id)[NB], int lane,
+                                           StepRegs<C, NB>& sr) {
   const KVLayout L = kv_layout<C>(p.flags, p.dims.num_kv_heads);
   const int off = C::v_lane_off(L, g, lane & 15, lane >> 4);
   const int soff = C::v_scale_off(L, g, lane & 15, lane >> 4);
-  const int ex = px >= 0 ? px : 0, ey = py >= 0 ? py : ex;
-  C::template load_v<row_policy<C>()>(tr.vx, block_rsrc(p.v_cache, L.block, ex), off, L, soff);
-  C::template load_v<row_policy<C>()>(tr.vy, block_rsrc(p.v_cache, L.block, ey), off, L, soff);
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+    C::template load_v<row_policy<C>()>(sr.v[b], block_rsrc(p.v_cache, L.block, id[b]), off, L, soff);
 }
 
 // Writes one head's result of a segment: the final output (bf16, normalised)
@@ -137,18 +139,17 @@ template <class C, int G>
 __device__ __forceinline__ void write_head(const DecodeArgs& p, const RowsArgs& r, const WaveState& st, int b, int g,
                                            bool whole, int rec, int lane) {
   const int n = lane & 15, kg = lane >> 4;
-  const float lsum = sum4(st.lsum);
   const float lsum_e = sum4(st.lsum_e);
   const float vscale = C::kFp8 ? kv_scale(p.v_scale, p.flags, g) : 1.f;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int row = 4 * kg + j;
-    const float L = __shfl(lsum, row);
+    const float L = st.psum[j];  // rounded-probability sum of head `row`
     const float Le = __shfl(lsum_e, row);
-    const float m = __shfl(st.m, row);
+    const float ms = __shfl(st.ms, row);
     if (row < G) {
       const float inv = L > 0.f ? vscale / L : 0.f;
-      const float lse = Le > 0.f ? (m + fast_log2(Le)) * kLn2 : -INFINITY;
+      const float lse = Le > 0.f ? (ms + fast_log2(Le)) * kLn2 : -INFINITY;
       const int64_t orow = (int64_t)b * p.dims.num_q_heads + g * G + row;
       if (whole) {
         uint32_t w[4];
@@ -180,98 +181,108 @@ __device__ __forceinline__ void write_head(const DecodeArgs& p, const RowsArgs& 
   }
 }
 
-// Register sets per wave: how many (tile, head) steps of loads a wave keeps
-// in flight.  Two cover HBM latency at one wave per SIMD for bf16 tiles
-// (16 KB per kv head).  The FP8 and FP4 tiles are smaller, but four or six
-// sets made those kernels slower (more register traffic, no more bandwidth:
-// they are bound by their per-tile instruction stream, not by loads in
-// flight), so every format uses two.
+// Register sets per wave: how many (step, head) pairs of loads a wave keeps
+// in flight.  Two cover HBM latency at one wave per SIMD (a bf16 set holds
+// 16 KB of one kv head's K and V, an FP8 set 8 KB; more sets or larger steps
+// gave FP8 no more bandwidth, see step_blocks).
 constexpr int kRowSets = 2;
 
 // One segment for this wave: tiles lt .. et - 1 of sequence b (context ctx)
-// for kv heads g0 .. g0 + HPW - 1.  The wave walks steps s = (tile s / HPW,
-// head s % HPW) with NS register sets: set j always holds steps j, j + NS,
-// j + 2NS, ... (one head, every NS/HPW-th tile).  A set's next step is loaded
-// as soon as its current step's MFMAs have consumed the registers (K after
-// the scores, V after P V), so while one set is computed the other sets'
-// loads and this set's next loads are in flight: NS steps of loads per wave,
-// which with one wave per SIMD keeps HBM busy.  Steps past the segment (and
-// the dummy loads after the last one) use absent blocks: they read block 0
-// and are masked, so every iteration issues the same loads in the same order.
+// for kv heads g0 .. g0 + HPW - 1, in steps of NB 16-token blocks (NB / 2
+// tiles).  The wave walks pairs s = (step s / HPW, head s % HPW) with NS
+// register sets: set j always holds pairs j, j + NS, j + 2NS, ... (one head,
+// every NS/HPW-th step).  A set's next step is loaded as soon as its current
+// step's MFMAs have consumed the registers (K after the scores, V after
+// P V), so while one set is computed the other sets' loads and this set's
+// next loads are in flight.  Blocks past the segment are absent: their loads
+// return zeros without touching memory and the step masks them, so every
+// iteration issues the same loads in the same order.
 template <class C, int G, int HPW>
 __device__ __forceinline__ void run_segment(const DecodeArgs& p, const RowsArgs& r, int b, int ctx, int lt, int et,
                                             int g0, bool whole, int rec, int lane) {
+  constexpr int NB = step_blocks<C>();
+  constexpr int ST = NB / 2;  // tiles per step
   constexpr int NS = kRowSets;
   static_assert(NS % HPW == 0, "each set must stay on one head");
-  constexpr int kAdvance = NS / HPW;  // tiles a set moves per iteration
+  static_assert(32 % ST == 0, "a step's tiles share one window of block ids");
+  constexpr int kAdvance = NS / HPW;  // steps a set moves per iteration
+  const int kg = lane >> 4;
   short8 qb[HPW][4];
   WaveState st[HPW];
+  float csc[HPW];
   const bool qvec = ((uintptr_t)p.q % 16 == 0) && (p.q_seq_stride % 8 == 0);
 #pragma unroll
   for (int hh = 0; hh < HPW; ++hh) {
     const uint16_t* qrow =
         static_cast<const uint16_t*>(p.q) + (int64_t)b * p.q_seq_stride + (int64_t)(g0 + hh) * G * kD;
-    load_q_operand<C, G>(qb[hh], qrow, qvec, lane & 15, lane >> 4);
+    load_q_operand<C, G>(qb[hh], qrow, qvec, lane & 15, kg);
     st[hh].reset();
-  }
-  float sscale[HPW];
-#pragma unroll
-  for (int hh = 0; hh < HPW; ++hh) {
-    sscale[hh] = p.softmax_scale * kLog2e;
-    if constexpr (C::kFp8) sscale[hh] *= kv_scale(p.k_scale, p.flags, g0 + hh);
+    float c = p.softmax_scale * kLog2e;
+    if constexpr (C::kFp8) c *= kv_scale(p.k_scale, p.flags, g0 + hh);
+    csc[hh] = fold_score_scale(c, qb[hh]);
   }
 
   const int lb_end = (ctx + kBS - 1) / kBS;
   int win = 0;
   int ids = preload_row_ids(p, b, lt, et, lb_end, 0, lane);
-  // Block ids of tile lt + k (-1 when absent), from the 32-tile window of ids.
-  auto tile_id = [&](int k, int& x, int& y) {
-    if ((k >> 5) != win) {
-      win = k >> 5;
+  // Block ids of step k (-1 when absent), from the 32-tile window of ids.
+  auto step_ids = [&](int k, int (&id)[NB]) {
+    const int kt = ST * k;
+    if ((kt >> 5) != win) {
+      win = kt >> 5;
       ids = preload_row_ids(p, b, lt, et, lb_end, 32 * win, lane);
     }
-    x = __builtin_amdgcn_readlane(ids, 2 * (k & 31));
-    y = __builtin_amdgcn_readlane(ids, 2 * (k & 31) + 1);
+#pragma unroll
+    for (int t = 0; t < ST; ++t) {
+      id[2 * t] = __builtin_amdgcn_readlane(ids, 2 * ((kt + t) & 31));
+      id[2 * t + 1] = __builtin_amdgcn_readlane(ids, 2 * ((kt + t) & 31) + 1);
+    }
   };
-  TileRegs<C> ts[NS];
-  int px[NS], py[NS];
+  auto valid_bits = [](const int (&id)[NB]) {
+    uint32_t v = 0;
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb) v |= (id[bb] >= 0 ? 1u : 0u) << bb;
+    return v;
+  };
+  StepRegs<C, NB> sr[NS];
+  int pid[NS][NB];
 #pragma unroll
   for (int j = 0; j < NS; ++j) {
     if (j % HPW == 0) {
-      tile_id(j / HPW, px[j], py[j]);
+      step_ids(j / HPW, pid[j]);
     } else {
-      px[j] = px[j - j % HPW];
-      py[j] = py[j - j % HPW];
+#pragma unroll
+      for (int bb = 0; bb < NB; ++bb) pid[j][bb] = pid[j - j % HPW][bb];
     }
   }
 #pragma unroll
   for (int j = 0; j < NS; ++j) {  // the loop's load order: K, V of each set in turn
-    row_load_k<C>(p, g0 + j % HPW, px[j], py[j], lane, ts[j]);
+    row_load_k<C, NB>(p, g0 + j % HPW, pid[j], lane, sr[j]);
     __builtin_amdgcn_sched_barrier(0);
-    row_load_v<C>(p, g0 + j % HPW, px[j], py[j], lane, ts[j]);
+    row_load_v<C, NB>(p, g0 + j % HPW, pid[j], lane, sr[j]);
     __builtin_amdgcn_sched_barrier(0);
   }
-  const int ntiles = et - lt;
-  const int iters = (ntiles + kAdvance - 1) / kAdvance;
+  const int nsteps = (et - lt + ST - 1) / ST;
+  const int iters = (nsteps + kAdvance - 1) / kAdvance;
   for (int it = 0; it < iters; ++it) {
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
       const int h = j % HPW;
-      const int k = it * kAdvance + j / HPW;  // this set's tile
-      int nx, ny;
+      const int k = it * kAdvance + j / HPW;  // this set's step
+      int nid[NB];
       if (h == 0) {
-        tile_id(k + kAdvance, nx, ny);
+        step_ids(k + kAdvance, nid);
       } else {
-        nx = px[j - h];  // the head-0 set of the same tile has just looked it up
-        ny = py[j - h];
+#pragma unroll
+        for (int bb = 0; bb < NB; ++bb) nid[bb] = pid[j - h][bb];  // the head-0 set of the same step looked it up
       }
-      float4v sx, sy;
-      tile_scores<C>(ts[j], qb[h], sx, sy);
-      row_load_k<C>(p, g0 + h, nx, ny, lane, ts[j]);
-      tile_update<C>(st[h], ts[j], sx, sy, sscale[h], px[j] >= 0, py[j] >= 0, kTile * (lt + k), ctx, lane >> 4);
-      row_load_v<C>(p, g0 + h, nx, ny, lane, ts[j]);
-      px[j] = nx;
-      py[j] = ny;
+      float4v s[NB];
+      step_scores<C, NB>(sr[j], qb[h], s);
+      row_load_k<C, NB>(p, g0 + h, nid, lane, sr[j]);
+      step_update<C, NB>(st[h], sr[j], s, csc[h], valid_bits(pid[j]), kTile * (lt + ST * k), ctx, kg);
+      row_load_v<C, NB>(p, g0 + h, nid, lane, sr[j]);
+#pragma unroll
+      for (int bb = 0; bb < NB; ++bb) pid[j][bb] = nid[bb];
     }
   }
 #pragma unroll

@@ -169,15 +169,12 @@ def test_config_parity(name):
 
 
 @pytest.mark.parametrize("name", ["llama3_8b_gqa", "long_ctx_splitk", "fp8_kv", "fp4_kv"])
-def test_full_size_sampled(name):
-    """Full-size workload in the launch configuration the benchmark times;
-    the oracle checks a sample of sequences (first, shortest, longest, last)."""
-    cfg = W.CONFIGS[name]
-    ctx = W.draw_context_lens(cfg)
-    sample = sorted({0, int(np.argmin(ctx)), int(np.argmax(ctx)), cfg.num_seqs - 1})
-    if name == "long_ctx_splitk":
-        sample = [0, cfg.num_seqs - 1]
-    _run_and_check(cfg, sample=sample)
+def test_full_size_every_sequence(name):
+    """Full-size workload in the launch configuration the benchmark times
+    (the append, then attention with the workload's partition size): every
+    output element of every sequence against the oracle, so every split
+    point of the equal tile ranges and every partition boundary is covered."""
+    _run_and_check(W.CONFIGS[name])
 
 
 EDGE_CTX = (0, 1, 15, 16, 17, 63, 64, 65, 200, 513)
