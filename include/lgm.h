@@ -77,7 +77,7 @@
 extern "C" {
 #endif
 
-#define LGM_ABI_VERSION 4
+#define LGM_ABI_VERSION 5
 
 typedef enum lgm_status {
   LGM_OK = 0,
@@ -274,6 +274,35 @@ lgm_status lgm_paged_decode_attn(void* out, float* out_lse, const void* q, int64
                                  int32_t partition_size, int32_t max_context_len, void* workspace,
                                  size_t workspace_bytes, lgm_paged_dims dims, lgm_dtype act_dtype,
                                  lgm_dtype cache_dtype, uint32_t flags, void* stream);
+
+/*
+ * lgm_paged_decode_attn without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  It computes exactly what
+ * lgm_paged_decode_attn computes (same plans, same kernels, bitwise the same
+ * results) and allocates nothing: its workspace is a device-resident array
+ * of LGM_STATIC_SCRATCH_BYTES inside the library, one per GPU it runs on,
+ * held until the process ends.
+ *   - The first call on a device looks the array up on that device and
+ *     clears its work-counter slot with a kernel on `stream`; every
+ *     completed call leaves that slot zero again.
+ *   - Calls whose lgm_paged_decode_workspace_size exceeds
+ *     LGM_STATIC_SCRATCH_BYTES return LGM_ERR_WORKSPACE_TOO_SMALL and
+ *     launch nothing (use lgm_paged_decode_attn with a workspace instead).
+ *   - Every call on a GPU shares that GPU's array: calls that overlap in
+ *     time on one GPU (on different streams, or from different threads
+ *     without ordering) race and give wrong results.  Order them, e.g. on
+ *     one stream.
+ * Arguments, layouts, validation and errors are those of
+ * lgm_paged_decode_attn, less workspace and workspace_bytes.
+ */
+#define LGM_STATIC_SCRATCH_BYTES (32u << 20)
+lgm_status lgm_paged_decode_attn_static(void* out, float* out_lse, const void* q, int64_t q_seq_stride,
+                                        const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                                        const int32_t* context_lens, const float* k_scale, const float* v_scale,
+                                        float softmax_scale, int32_t partition_size, int32_t max_context_len,
+                                        lgm_paged_dims dims, lgm_dtype act_dtype, lgm_dtype cache_dtype,
+                                        uint32_t flags, void* stream);
 
 /*
  * Log-sum-exp merge of split-K records ([mainarch] combine of split

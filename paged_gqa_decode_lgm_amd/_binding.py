@@ -69,6 +69,9 @@ def lib() -> ctypes.CDLL:
         L.lgm_paged_decode_attn.argtypes = [vp, vp, vp, i64, vp, vp, vp, vp, vp, vp, f32, i32, i32, vp, sz,
                                             lgm_paged_dims, i32, i32, u32, vp]
         L.lgm_paged_decode_attn.restype = i32
+        L.lgm_paged_decode_attn_static.argtypes = [vp, vp, vp, i64, vp, vp, vp, vp, vp, vp, f32, i32, i32,
+                                                   lgm_paged_dims, i32, i32, u32, vp]
+        L.lgm_paged_decode_attn_static.restype = i32
         L.lgm_lse_merge.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
         L.lgm_lse_merge.restype = i32
         L.lgm_last_error.argtypes = []
@@ -154,6 +157,15 @@ def lgm_paged_decode_attn(out, out_lse, q, q_seq_stride, k_cache, v_cache, block
                                        _ptr(v_scale), softmax_scale, partition_size, max_context_len,
                                        _ptr(workspace), workspace_bytes, dims, act_dtype, cache_dtype, flags,
                                        _stream(stream)))
+
+
+def lgm_paged_decode_attn_static(out, out_lse, q, q_seq_stride, k_cache, v_cache, block_tables, context_lens,
+                                 k_scale, v_scale, softmax_scale, partition_size, max_context_len, dims, act_dtype,
+                                 cache_dtype, flags=0, stream=None):
+    _check(lib().lgm_paged_decode_attn_static(_ptr(out), _ptr(out_lse), _ptr(q), q_seq_stride, _ptr(k_cache),
+                                              _ptr(v_cache), _ptr(block_tables), _ptr(context_lens), _ptr(k_scale),
+                                              _ptr(v_scale), softmax_scale, partition_size, max_context_len, dims,
+                                              act_dtype, cache_dtype, flags, _stream(stream)))
 
 
 def lgm_lse_merge(out, out_lse, partial_out, partial_lse, num_partitions, num_seqs, num_q_heads, head_dim,

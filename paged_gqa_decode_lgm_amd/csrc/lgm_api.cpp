@@ -10,6 +10,7 @@
 #include <stdio.h>
 
 #include <cmath>
+#include <mutex>
 #include <string>
 
 #include "lgm_internal.h"
@@ -466,14 +467,28 @@ size_t lgm_paged_decode_workspace_size(lgm_paged_dims dims, int32_t max_context_
   return pl.total;
 }
 
-lgm_status lgm_paged_decode_attn(void* out, float* out_lse, const void* q, int64_t q_seq_stride, const void* k_cache,
-                                 const void* v_cache, const int32_t* block_tables, const int32_t* context_lens,
-                                 const float* k_scale, const float* v_scale, float softmax_scale,
-                                 int32_t partition_size, int32_t max_context_len, void* workspace,
-                                 size_t workspace_bytes, lgm_paged_dims dims, lgm_dtype act_dtype,
-                                 lgm_dtype cache_dtype, uint32_t flags, void* stream) {
-  const char* fn = "lgm_paged_decode_attn";
-  g_err.clear();
+}  // extern "C"
+
+namespace {
+
+// Where lgm_paged_decode_attn_static finds its workspace.
+struct StaticWorkspace {
+  void* ptr;
+  size_t bytes;
+};
+constexpr size_t kStaticScratchBytes = LGM_STATIC_SCRATCH_BYTES;
+using ScratchResolver = lgm_status (*)(const char* fn, hipStream_t stream, StaticWorkspace& sw);
+
+// The attention call of both entry points.  resolve_static is NULL for
+// lgm_paged_decode_attn (the caller's workspace is checked and used);
+// lgm_paged_decode_attn_static passes the resolver of the device-resident
+// scratch array, called only after every other argument has been validated.
+lgm_status decode_attn_impl(const char* fn, void* out, float* out_lse, const void* q, int64_t q_seq_stride,
+                            const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                            const int32_t* context_lens, const float* k_scale, const float* v_scale,
+                            float softmax_scale, int32_t partition_size, int32_t max_context_len, void* workspace,
+                            size_t workspace_bytes, lgm_paged_dims dims, lgm_dtype act_dtype, lgm_dtype cache_dtype,
+                            uint32_t flags, void* stream, ScratchResolver resolve_static) {
   lgm_status st = check_decode_common(fn, dims, max_context_len, cache_dtype);
   if (st != LGM_OK) return st;
   if (!dtype_valid(act_dtype)) return fail(LGM_ERR_INVALID_ARGUMENT, fn, "act_dtype = %d is not an lgm_dtype", (int)act_dtype);
@@ -501,7 +516,12 @@ lgm_status lgm_paged_decode_attn(void* out, float* out_lse, const void* q, int64
   struct {
     size_t total;
   } ws{pl.total};
-  if (ws.total > 0) {
+  if (resolve_static && ws.total > kStaticScratchBytes)
+    return fail(LGM_ERR_WORKSPACE_TOO_SMALL, fn,
+                "these arguments need %zu bytes of workspace, more than the %zu bytes of the device-resident scratch "
+                "array (LGM_STATIC_SCRATCH_BYTES); call lgm_paged_decode_attn with a workspace instead",
+                ws.total, (size_t)kStaticScratchBytes);
+  if (ws.total > 0 && !resolve_static) {
     if (!workspace)
       return fail(LGM_ERR_WORKSPACE_TOO_SMALL, fn, "workspace is NULL but %zu bytes are needed", ws.total);
     if (workspace_bytes < ws.total)
@@ -534,6 +554,12 @@ lgm_status lgm_paged_decode_attn(void* out, float* out_lse, const void* q, int64
                       {"v_scale", (uintptr_t)v_scale, scale_bytes(v_scale, dims, flags)}};
   if ((st = check_no_alias(fn, outs, 3, ins, 7)) != LGM_OK) return st;
 
+  if (resolve_static) {
+    StaticWorkspace sw{};
+    if ((st = resolve_static(fn, (hipStream_t)stream, sw)) != LGM_OK) return st;
+    workspace = sw.ptr;
+    workspace_bytes = sw.bytes;
+  }
   char* wsb = static_cast<char*>(workspace);
   if (pl.rows_parts) {
     float* part_out = pl.P > 1 ? reinterpret_cast<float*>(wsb + pl.counters_bytes) : nullptr;
@@ -592,6 +618,93 @@ lgm_status lgm_paged_decode_attn(void* out, float* out_lse, const void* q, int64
     if (e != hipSuccess) return fail(LGM_ERR_HIP, fn, "merge kernel launch failed: %s", hipGetErrorString(e));
   }
   return LGM_OK;
+}
+
+// ---- the device-resident scratch array of lgm_paged_decode_attn_static -----------
+// One copy per GPU the library runs on, held until the process ends.  Host code
+// never uses the array's name as an address: each device's address comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+constexpr size_t kStaticScratchWords = kStaticScratchBytes / 4;
+static __device__ __align__(256) uint32_t scratch[kStaticScratchWords];
+
+__global__ void zero_words_kernel(uint32_t* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+constexpr int kMaxDevices = 64;
+struct ScratchSlot {
+  std::once_flag once;
+  hipError_t err;
+  void* ptr;
+};
+ScratchSlot g_scratch[kMaxDevices];
+
+// The scratch array of the device `stream` runs on.  The first call on a
+// device looks its address up (with that device current) and clears the
+// work-counter slot at its start with a small kernel on `stream` (a kernel,
+// not a memset, so that a caller capturing a graph records an ordinary
+// node); every completed call leaves that slot zero again.
+lgm_status resolve_scratch(const char* fn, hipStream_t stream, StaticWorkspace& sw) {
+  int dev = 0;
+  if (stream == nullptr || hipStreamGetDevice(stream, &dev) != hipSuccess) {
+    if (hipGetDevice(&dev) != hipSuccess) return fail(LGM_ERR_HIP, fn, "hipGetDevice failed");
+  }
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(LGM_ERR_UNSUPPORTED, fn, "device %d: the scratch array is kept for devices 0..%d", dev,
+                kMaxDevices - 1);
+  ScratchSlot& slot = g_scratch[dev];
+  std::call_once(slot.once, [&] {
+    int cur = -1;
+    slot.err = hipGetDevice(&cur);
+    if (slot.err != hipSuccess) return;
+    if (cur != dev && (slot.err = hipSetDevice(dev)) != hipSuccess) return;
+    void* p = nullptr;
+    slot.err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (slot.err == hipSuccess) {
+      slot.ptr = p;
+      hipLaunchKernelGGL(zero_words_kernel, dim3(1), dim3(64), 0, stream, static_cast<uint32_t*>(p), 64);
+      slot.err = hipGetLastError();
+    }
+    if (cur != dev) {
+      const hipError_t e = hipSetDevice(cur);
+      if (slot.err == hipSuccess) slot.err = e;
+    }
+  });
+  if (slot.err != hipSuccess || slot.ptr == nullptr)
+    return fail(LGM_ERR_HIP, fn, "device %d: the scratch array's address could not be taken: %s", dev,
+                hipGetErrorString(slot.err));
+  sw.ptr = slot.ptr;
+  sw.bytes = kStaticScratchBytes;
+  return LGM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+lgm_status lgm_paged_decode_attn(void* out, float* out_lse, const void* q, int64_t q_seq_stride, const void* k_cache,
+                                 const void* v_cache, const int32_t* block_tables, const int32_t* context_lens,
+                                 const float* k_scale, const float* v_scale, float softmax_scale,
+                                 int32_t partition_size, int32_t max_context_len, void* workspace,
+                                 size_t workspace_bytes, lgm_paged_dims dims, lgm_dtype act_dtype,
+                                 lgm_dtype cache_dtype, uint32_t flags, void* stream) {
+  g_err.clear();
+  return decode_attn_impl("lgm_paged_decode_attn", out, out_lse, q, q_seq_stride, k_cache, v_cache, block_tables,
+                          context_lens, k_scale, v_scale, softmax_scale, partition_size, max_context_len, workspace,
+                          workspace_bytes, dims, act_dtype, cache_dtype, flags, stream, nullptr);
+}
+
+lgm_status lgm_paged_decode_attn_static(void* out, float* out_lse, const void* q, int64_t q_seq_stride,
+                                        const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                                        const int32_t* context_lens, const float* k_scale, const float* v_scale,
+                                        float softmax_scale, int32_t partition_size, int32_t max_context_len,
+                                        lgm_paged_dims dims, lgm_dtype act_dtype, lgm_dtype cache_dtype,
+                                        uint32_t flags, void* stream) {
+  g_err.clear();
+  return decode_attn_impl("lgm_paged_decode_attn_static", out, out_lse, q, q_seq_stride, k_cache, v_cache,
+                          block_tables, context_lens, k_scale, v_scale, softmax_scale, partition_size,
+                          max_context_len, nullptr, 0, dims, act_dtype, cache_dtype, flags, stream, resolve_scratch);
 }
 
 lgm_status lgm_lse_merge(void* out, float* out_lse, const float* partial_out, const float* partial_lse,

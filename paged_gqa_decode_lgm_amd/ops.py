@@ -129,6 +129,29 @@ def paged_decode_attn(q, k_cache, v_cache, block_tables, context_lens, max_conte
     return out, out_lse
 
 
+def paged_decode_attn_static(q, k_cache, v_cache, block_tables, context_lens, max_context_len: int,
+                             softmax_scale: Optional[float] = None, partition_size: int = 0, k_scale=None,
+                             v_scale=None, out=None, out_lse=None, want_lse: bool = True, stream=None,
+                             layout: str = "nhd") -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """paged_decode_attn on the library's device-resident scratch array
+    (lgm_paged_decode_attn_static): no workspace is passed or allocated."""
+    bsz, hq, d = q.shape
+    if q.stride(2) != 1 or q.stride(1) != d:
+        raise ValueError("q must be [B, Hq, D] with heads dense (only the sequence stride may differ)")
+    dims = dims_for(bsz, hq, k_cache, block_tables, layout)
+    flags = variant_flags(layout, "neox", k_scale, dims.num_kv_heads)
+    if softmax_scale is None:
+        softmax_scale = float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32))
+    if out is None:
+        out = torch.empty((bsz, hq, d), dtype=q.dtype, device=q.device)
+    if out_lse is None and want_lse:
+        out_lse = torch.empty((bsz, hq), dtype=torch.float32, device=q.device)
+    B.lgm_paged_decode_attn_static(out, out_lse, q, q.stride(0), k_cache, v_cache, block_tables, context_lens,
+                                   k_scale, v_scale, float(softmax_scale), partition_size, int(max_context_len), dims,
+                                   lgm_dtype(q), lgm_dtype(k_cache), flags=flags, stream=stream)
+    return out, out_lse
+
+
 def lse_merge(partial_out, partial_lse, num_partitions=None, out_dtype=torch.float32, out=None, out_lse=None,
               stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Merge records partial_out [B, H, P, D] / partial_lse [B, H, P]."""

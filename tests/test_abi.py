@@ -29,12 +29,12 @@ def test_library_loads_and_exports_every_header_function():
     lib = L.lib()
     names = L.header_functions()
     assert set(names) == {"lgm_rope_kv_append", "lgm_paged_decode_partition_size", "lgm_paged_decode_workspace_size",
-                          "lgm_paged_decode_attn", "lgm_lse_merge", "lgm_last_error", "lgm_abi_version",
-                          "lgm_stream_read_probe", "lgm_paged_mla_partition_size", "lgm_paged_mla_workspace_size",
-                          "lgm_paged_mla_decode"}
+                          "lgm_paged_decode_attn", "lgm_paged_decode_attn_static", "lgm_lse_merge", "lgm_last_error",
+                          "lgm_abi_version", "lgm_stream_read_probe", "lgm_paged_mla_partition_size",
+                          "lgm_paged_mla_workspace_size", "lgm_paged_mla_decode"}
     for n in names:
         assert hasattr(lib, n), n
-    assert L.lgm_abi_version() == 4
+    assert L.lgm_abi_version() == 5
 
 
 def test_build_entry_abi_check_matches_header():
@@ -163,6 +163,53 @@ def test_attention_rejects(over, status, word):
 
 def test_attention_empty_batch_is_a_noop():
     _attn(dims=dims(num_seqs=0), out=None, q=None)
+
+
+# ------------------------------------------------------------------ attention without a workspace
+def _attn_static(**over):
+    a = dict(out=addr(0), out_lse=addr(1), q=addr(2), q_seq_stride=32 * 128, k_cache=addr(3), v_cache=addr(4),
+             block_tables=addr(5), context_lens=addr(6), k_scale=None, v_scale=None, softmax_scale=0.0883883,
+             partition_size=512, max_context_len=8192, dims=dims(), act_dtype=L.LGM_BF16, cache_dtype=L.LGM_BF16,
+             stream=0)
+    a.update(over)
+    return L.lgm_paged_decode_attn_static(**a)
+
+
+STATIC_BAD = [(over, status, word) for over, status, word in ATTN_BAD if not any(k.startswith("workspace") for k in over)] + [
+    # C4-shaped long contexts in partitions of 64 need 66 MB of partial records: more than the array holds
+    (dict(dims=dims(num_seqs=4, max_blocks_per_seq=8192), max_context_len=131072, partition_size=64), WS,
+     "LGM_STATIC_SCRATCH_BYTES"),
+]
+
+
+@pytest.mark.parametrize("over,status,word", STATIC_BAD)
+def test_attention_static_rejects(over, status, word):
+    """The allocation-free entry point validates exactly as the workspace one
+    does, and refuses plans whose workspace exceeds its device array, before
+    any HIP call."""
+    with pytest.raises(L.LgmError) as e:
+        _attn_static(**over)
+    assert e.value.status == status
+    assert e.value.message.startswith("lgm_paged_decode_attn_static:")
+    assert word in e.value.message
+
+
+def test_attention_static_capacity_covers_the_workloads():
+    """The array holds the workspace of every benchmarked shape: 64 contexts
+    of up to 8192 tokens in equal ranges, 128 FP8 or FP4 contexts of up to
+    4096, and four 131072-token contexts in partitions of 512."""
+    cap = 32 << 20
+    assert L.lgm_paged_decode_workspace_size(dims(), 8192, 0, L.LGM_BF16) <= cap
+    for cache in (L.LGM_FP8_E4M3, L.LGM_FP4_E2M1):
+        assert L.lgm_paged_decode_workspace_size(dims(num_seqs=128, max_blocks_per_seq=256), 4096, 0, cache) <= cap
+    assert L.lgm_paged_decode_workspace_size(dims(num_seqs=4, max_blocks_per_seq=8192), 131072, 512,
+                                             L.LGM_BF16) <= cap
+    too_big = L.lgm_paged_decode_workspace_size(dims(num_seqs=4, max_blocks_per_seq=8192), 131072, 64, L.LGM_BF16)
+    assert too_big > cap
+
+
+def test_attention_static_empty_batch_is_a_noop():
+    _attn_static(dims=dims(num_seqs=0), out=None, q=None)
 
 
 # ------------------------------------------------------------------ plan queries
