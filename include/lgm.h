@@ -77,7 +77,7 @@
 extern "C" {
 #endif
 
-#define LGM_ABI_VERSION 5
+#define LGM_ABI_VERSION 6
 
 typedef enum lgm_status {
   LGM_OK = 0,
@@ -93,7 +93,15 @@ typedef enum lgm_status {
  * Microscaling form: E2M1 codes (magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6), one
  * E8M0 scale byte 2^(byte - 127) per 32 consecutive head_dim elements of a
  * (token, kv head) row; see "FP4 cache blocks" above. */
+/* A C caller may pass any int here; every call rejects values that are not
+ * listed.  C++ sees the enum with a fixed 32-bit underlying type, so such a
+ * value is an ordinary value of the type there too (without one, loading it
+ * would be undefined behaviour in C++); the size and passing are the same. */
+#ifdef __cplusplus
+typedef enum lgm_dtype : int32_t { LGM_F32 = 0, LGM_BF16 = 1, LGM_FP8_E4M3 = 2, LGM_FP4_E2M1 = 3 } lgm_dtype;
+#else
 typedef enum lgm_dtype { LGM_F32 = 0, LGM_BF16 = 1, LGM_FP8_E4M3 = 2, LGM_FP4_E2M1 = 3 } lgm_dtype;
+#endif
 
 /* Contract-variant flags ([Loom] "Position and KV": NeoX/interleaved RoPE,
  * NHD/HND cache views, static per-tensor/per-head FP8 scales), OR-ed into
@@ -326,6 +334,32 @@ lgm_status lgm_lse_merge(void* out, float* out_lse, const float* partial_out,
                          const float* partial_lse, const int32_t* num_partitions,
                          int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                          int32_t max_partitions, lgm_dtype out_dtype, void* stream);
+
+/*
+ * Opt-in check of the block tables and context lengths (the debug check of
+ * the paged-KV contract; the span check of the mainarch README's
+ * troubleshooting section is its model).  The attention and append kernels
+ * never dereference a table entry outside [0, num_blocks) and clamp context
+ * lengths, silently; enqueued on the same stream before or after them, this
+ * call reads the same device-resident entries with the same clamping and
+ * raises counters in `status` where they would mask or clamp:
+ *   status[0] += table entries of logical blocks < ceil(ctx / block_size)
+ *                (ctx clamped to [0, max_blocks_per_seq * block_size]) that
+ *                lie outside [0, num_blocks)
+ *   status[1] += sequences whose context_lens[b] exceeds
+ *                max_blocks_per_seq * block_size or max_context_len
+ *   status[2]  = the largest 0x7FFFFFFF - (b * max_blocks_per_seq + lb) over
+ *                bad entries: the first bad (sequence b, logical block lb) is
+ *                0x7FFFFFFF - status[2] when status[0] > 0
+ *   status[3]  unused (left as is)
+ * status is int32 [4] device memory the caller zero-fills before the first
+ * check; later checks only add to it.  Read it after synchronising.
+ *   block_tables   int32 [B][max_blocks_per_seq];  context_lens  int32 [B]
+ *   max_context_len the value the attention call is given (0..capacity)
+ * dims.num_seqs <= 65535.  Nothing else is read or written.
+ */
+lgm_status lgm_check_block_tables(const int32_t* block_tables, const int32_t* context_lens, lgm_paged_dims dims,
+                                  int32_t max_context_len, int32_t* status, void* stream);
 
 /* Message of the last failed lgm_* call on this thread ("" if none).  Valid
  * until the next lgm_* call on the same thread. */

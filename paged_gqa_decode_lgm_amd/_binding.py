@@ -13,7 +13,8 @@ import ctypes
 import os
 import re
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblgm.so")
+# LGM_LIBRARY selects another build of the library (e.g. the sanitizer build).
+LIB_PATH = os.environ.get("LGM_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblgm.so")
 INCLUDE = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
 HEADER = os.path.join(INCLUDE, "lgm.h")
 
@@ -72,6 +73,8 @@ def lib() -> ctypes.CDLL:
         L.lgm_paged_decode_attn_static.argtypes = [vp, vp, vp, i64, vp, vp, vp, vp, vp, vp, f32, i32, i32,
                                                    lgm_paged_dims, i32, i32, u32, vp]
         L.lgm_paged_decode_attn_static.restype = i32
+        L.lgm_check_block_tables.argtypes = [vp, vp, lgm_paged_dims, i32, vp, vp]
+        L.lgm_check_block_tables.restype = i32
         L.lgm_lse_merge.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
         L.lgm_lse_merge.restype = i32
         L.lgm_last_error.argtypes = []
@@ -166,6 +169,11 @@ def lgm_paged_decode_attn_static(out, out_lse, q, q_seq_stride, k_cache, v_cache
                                               _ptr(v_cache), _ptr(block_tables), _ptr(context_lens), _ptr(k_scale),
                                               _ptr(v_scale), softmax_scale, partition_size, max_context_len, dims,
                                               act_dtype, cache_dtype, flags, _stream(stream)))
+
+
+def lgm_check_block_tables(block_tables, context_lens, dims, max_context_len, status, stream=None):
+    _check(lib().lgm_check_block_tables(_ptr(block_tables), _ptr(context_lens), dims, max_context_len, _ptr(status),
+                                        _stream(stream)))
 
 
 def lgm_lse_merge(out, out_lse, partial_out, partial_lse, num_partitions, num_seqs, num_q_heads, head_dim,

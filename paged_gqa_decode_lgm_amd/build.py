@@ -1,11 +1,21 @@
 """Build liblgm.so in-tree with hipcc for gfx950.
 
-    python -m paged_gqa_decode_lgm_amd.build [--verbose]
+    python -m paged_gqa_decode_lgm_amd.build [--verbose] [--sanitize]
 
 Each translation unit is compiled separately (the RoPE/append unit with
 -ffp-contract=off so no multiply-add is fused) and linked into
 paged_gqa_decode_lgm_amd/liblgm.so.  Packed-fp32 VALU ops are disabled for all
 device code.
+
+--sanitize builds liblgm_san.so instead, with the host code of every unit
+(argument validation, plans, launches) under AddressSanitizer and
+UndefinedBehaviorSanitizer; device code is built as usual.  Load it with
+LGM_LIBRARY pointing at it and the ASan runtime preloaded, e.g.
+
+    LGM_LIBRARY=$PWD/paged_gqa_decode_lgm_amd/liblgm_san.so \
+    LD_PRELOAD=$(hipcc -print-file-name=libclang_rt.asan-x86_64.so) \
+    ASAN_OPTIONS=detect_leaks=0 UBSAN_OPTIONS=halt_on_error=1:print_stacktrace=1 \
+    python -m pytest tests/test_abi.py
 """
 from __future__ import annotations
 
@@ -37,6 +47,7 @@ UNITS = {
     # files around every step.
     "paged_decode_rows.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "lse_merge.hip": [],
+    "table_check.hip": [],
     "stream_probe.hip": [],
     "paged_mla.hip": [],
 }
@@ -52,22 +63,32 @@ def _run(cmd, verbose):
     return r
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+# Host-only sanitizers: each -fsanitize= applies to the host pass alone.
+SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=undefined"]
+SAN_LIB = os.path.join(PKG, "liblgm_san.so")
+
+
+def build(verbose: bool = False, sanitize: bool = False) -> str:
+    bdir = BUILD + ("_san" if sanitize else "")
+    lib = SAN_LIB if sanitize else LIB
+    san = SANITIZE if sanitize else []
+    os.makedirs(bdir, exist_ok=True)
 
     def compile_one(item):
         src, extra = item
-        obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-        _run([HIPCC, *COMMON, *extra, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
+        obj = os.path.join(bdir, os.path.splitext(src)[0] + ".o")
+        _run([HIPCC, *COMMON, *san, *extra, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
         return obj
 
     with ThreadPoolExecutor(min(len(UNITS), os.cpu_count() or 1)) as ex:
         objs = list(ex.map(compile_one, UNITS.items()))
-    tmp = LIB + ".tmp"
-    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
-    os.replace(tmp, LIB)
-    return LIB
+    tmp = lib + ".tmp"
+    link_san = ["-shared-libasan", "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined"] if sanitize else []
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *link_san, *objs, "-o", tmp], verbose)
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
-    print(build(verbose="--verbose" in sys.argv))
+    print(build(verbose="--verbose" in sys.argv, sanitize="--sanitize" in sys.argv))

@@ -707,6 +707,34 @@ lgm_status lgm_paged_decode_attn_static(void* out, float* out_lse, const void* q
                           max_context_len, nullptr, 0, dims, act_dtype, cache_dtype, flags, stream, resolve_scratch);
 }
 
+lgm_status lgm_check_block_tables(const int32_t* block_tables, const int32_t* context_lens, lgm_paged_dims dims,
+                                  int32_t max_context_len, int32_t* status, void* stream) {
+  const char* fn = "lgm_check_block_tables";
+  g_err.clear();
+  lgm_status st = check_dims(fn, dims);
+  if (st != LGM_OK) return st;
+  const int64_t cap = (int64_t)dims.max_blocks_per_seq * dims.block_size;
+  if (max_context_len < 0 || max_context_len > cap)
+    return fail(LGM_ERR_INVALID_ARGUMENT, fn,
+                "max_context_len = %d must be in [0, max_blocks_per_seq * block_size = %lld]", max_context_len,
+                (long long)cap);
+  if (dims.num_seqs > 65535) return fail(LGM_ERR_UNSUPPORTED, fn, "dims.num_seqs = %d: at most 65535", dims.num_seqs);
+  if (dims.num_seqs == 0) return LGM_OK;
+  if (!block_tables) return fail(LGM_ERR_INVALID_ARGUMENT, fn, "block_tables is NULL");
+  if (!context_lens) return fail(LGM_ERR_INVALID_ARGUMENT, fn, "context_lens is NULL");
+  if (!status) return fail(LGM_ERR_INVALID_ARGUMENT, fn, "status is NULL");
+  if ((uintptr_t)status % 4 != 0) return fail(LGM_ERR_INVALID_ARGUMENT, fn, "status %p must be 4-byte aligned", (void*)status);
+  const int64_t B = dims.num_seqs;
+  const Span outs[] = {{"status", (uintptr_t)status, 16}};
+  const Span ins[] = {{"block_tables", (uintptr_t)block_tables, B * dims.max_blocks_per_seq * 4},
+                      {"context_lens", (uintptr_t)context_lens, B * 4}};
+  if ((st = check_no_alias(fn, outs, 1, ins, 2)) != LGM_OK) return st;
+  const hipError_t e =
+      lgm::launch_table_check(block_tables, context_lens, dims, max_context_len, status, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(LGM_ERR_HIP, fn, "kernel launch failed: %s", hipGetErrorString(e));
+  return LGM_OK;
+}
+
 lgm_status lgm_lse_merge(void* out, float* out_lse, const float* partial_out, const float* partial_lse,
                          const int32_t* num_partitions, int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                          int32_t max_partitions, lgm_dtype out_dtype, void* stream) {

@@ -130,6 +130,8 @@ hipError_t launch_stream_read_probe(const void* src, int64_t bytes, int num_wg, 
                                     hipStream_t s);
 hipError_t launch_paged_decode(const DecodeArgs& a, lgm_dtype act, lgm_dtype cache, hipStream_t s);
 hipError_t launch_lse_merge(const MergeArgs& a, lgm_dtype out_dtype, hipStream_t s);
+hipError_t launch_table_check(const int32_t* block_tables, const int32_t* context_lens, const lgm_paged_dims& d,
+                              int32_t max_context_len, int32_t* status, hipStream_t s);
 
 // Matrix-core decode for bf16 activations with bf16 / FP8 caches, head_dim 128.
 hipError_t launch_paged_decode_mfma(const DecodeArgs& a, lgm_dtype cache, hipStream_t s);

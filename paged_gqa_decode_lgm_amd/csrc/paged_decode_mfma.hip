@@ -25,6 +25,8 @@
 // partitions first and the shorter tail partitions last; every workgroup
 // walks the context lengths 64 sequences at a time with a wave prefix sum to
 // turn an item number into its triple.
+#include <mutex>
+
 #include "mfma_common.h"
 
 namespace lgm {
@@ -415,20 +417,22 @@ hipError_t dispatch(const DecodeArgs& a, int G, int compute_units, hipStream_t s
   }
 }
 
-// Compute units of the device a stream runs on, queried once per device.
+// Compute units of the device a stream runs on, queried once per device
+// (std::call_once, so threads making their first calls together agree).
 int compute_units_of(hipStream_t s) {
   constexpr int kMaxDevices = 64;
-  static int cache[kMaxDevices] = {};
+  static std::once_flag once[kMaxDevices];
+  static int cache[kMaxDevices];
   int dev = 0;
   if (s == nullptr || hipStreamGetDevice(s, &dev) != hipSuccess) {
     if (hipGetDevice(&dev) != hipSuccess) dev = 0;
   }
   if (dev < 0 || dev >= kMaxDevices) dev = 0;
-  if (cache[dev] == 0) {
+  std::call_once(once[dev], [dev] {
     int n = 0;
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) n = 1;
     cache[dev] = n;
-  }
+  });
   return cache[dev];
 }
 

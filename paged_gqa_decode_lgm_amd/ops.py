@@ -152,6 +152,18 @@ def paged_decode_attn_static(q, k_cache, v_cache, block_tables, context_lens, ma
     return out, out_lse
 
 
+def check_block_tables(k_cache, block_tables, context_lens, max_context_len: int, status=None, stream=None,
+                       layout: str = "nhd") -> torch.Tensor:
+    """Enqueues lgm_check_block_tables; returns its int32 [4] status words
+    (zero-filled here when not given; read them after synchronising)."""
+    dims = dims_for(block_tables.shape[0], 1, k_cache, block_tables, layout)
+    dims.num_q_heads = dims.num_kv_heads  # the check reads no query
+    if status is None:
+        status = torch.zeros(4, dtype=torch.int32, device=block_tables.device)
+    B.lgm_check_block_tables(block_tables, context_lens, dims, int(max_context_len), status, stream)
+    return status
+
+
 def lse_merge(partial_out, partial_lse, num_partitions=None, out_dtype=torch.float32, out=None, out_lse=None,
               stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Merge records partial_out [B, H, P, D] / partial_lse [B, H, P]."""

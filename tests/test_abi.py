@@ -29,12 +29,13 @@ def test_library_loads_and_exports_every_header_function():
     lib = L.lib()
     names = L.header_functions()
     assert set(names) == {"lgm_rope_kv_append", "lgm_paged_decode_partition_size", "lgm_paged_decode_workspace_size",
-                          "lgm_paged_decode_attn", "lgm_paged_decode_attn_static", "lgm_lse_merge", "lgm_last_error",
+                          "lgm_paged_decode_attn", "lgm_paged_decode_attn_static", "lgm_check_block_tables",
+                          "lgm_lse_merge", "lgm_last_error",
                           "lgm_abi_version", "lgm_stream_read_probe", "lgm_paged_mla_partition_size",
                           "lgm_paged_mla_workspace_size", "lgm_paged_mla_decode"}
     for n in names:
         assert hasattr(lib, n), n
-    assert L.lgm_abi_version() == 5
+    assert L.lgm_abi_version() == 6
 
 
 def test_build_entry_abi_check_matches_header():
@@ -163,6 +164,40 @@ def test_attention_rejects(over, status, word):
 
 def test_attention_empty_batch_is_a_noop():
     _attn(dims=dims(num_seqs=0), out=None, q=None)
+
+
+# ------------------------------------------------------------------ block-table check
+def _tcheck(**over):
+    a = dict(block_tables=addr(5), context_lens=addr(6), dims=dims(), max_context_len=8192, status=addr(7), stream=0)
+    a.update(over)
+    return L.lgm_check_block_tables(**a)
+
+
+TCHECK_BAD = [
+    (dict(dims=dims(num_q_heads=30)), INV, "num_q_heads"),
+    (dict(dims=dims(num_blocks=0)), INV, "num_blocks"),
+    (dict(max_context_len=8193), INV, "max_context_len"),
+    (dict(max_context_len=-1), INV, "max_context_len"),
+    (dict(dims=dims(num_seqs=70000)), UNS, "num_seqs"),
+    (dict(block_tables=None), INV, "block_tables"),
+    (dict(context_lens=None), INV, "context_lens"),
+    (dict(status=None), INV, "status"),
+    (dict(status=addr(7) + 2), INV, "aligned"),
+    (dict(status=addr(5) + 64), INV, "'status' overlaps input 'block_tables'"),
+]
+
+
+@pytest.mark.parametrize("over,status,word", TCHECK_BAD)
+def test_table_check_rejects(over, status, word):
+    with pytest.raises(L.LgmError) as e:
+        _tcheck(**over)
+    assert e.value.status == status
+    assert e.value.message.startswith("lgm_check_block_tables:")
+    assert word in e.value.message
+
+
+def test_table_check_empty_batch_is_a_noop():
+    _tcheck(dims=dims(num_seqs=0), block_tables=None, context_lens=None, status=None)
 
 
 # ------------------------------------------------------------------ attention without a workspace
