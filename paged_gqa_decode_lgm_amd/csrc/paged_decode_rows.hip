@@ -37,10 +37,50 @@ using namespace mfma;
 
 constexpr int kChunk = 1024;       // sequences per scan step
 constexpr int kMaxRowWaves = 8;    // waves of the widest row workgroup
+constexpr int kWin = 32;           // tiles per window of block ids (two ids per tile: one per lane)
+constexpr int kStageWin = 4;       // windows of block ids staged in LDS per segment (128 tiles)
 
+// A segment: the tiles lt .. et - 1 of one stream (sequence b, head group
+// hg) that a range holds, and where its result goes.
+struct SegDesc {
+  int b, ctx, lt, et, hg, rec, whole, pad;
+};
+
+// Segments are processed in batches staged in LDS: their descriptors, the
+// first window of their block ids, their query rows and (FP8) their kv-head
+// scales, all loaded by the workgroup together, so that moving from one
+// segment to the next costs no memory round trip; and their results, which
+// the workgroup writes out together after the batch's last step.  (Results
+// stored to global memory as each segment ended held up the loads issued
+// after them, which wait for those stores to complete: 4-5 us per segment
+// on 128 FP8 contexts of 1024..4096 tokens, measured with per-workgroup
+// timestamps.)  A batch holds as many segments as ~140 KB of LDS allow.
+template <int G, int HG>
+struct Batch {
+  static constexpr int kQRow = kD + 8;  // bf16 per staged query row; the pad spreads rows over LDS banks
+  static constexpr int kPerSeg = HG * G * (kQRow * 2 + kD * 4 + 12) + kStageWin * 2 * kWin * 4 + 2 * HG * 4 + 32;
+  static constexpr int kFit = 140000 / kPerSeg;
+  static constexpr int kMax = kFit > 16 ? 16 : (kFit < 1 ? 1 : kFit);
+};
+
+template <int G, int HG>
 struct RowsSmem {
+  using B = Batch<G, HG>;
   int pre[kChunk + 1];  // tiles of the streams of sequences b0 .. b0 + j - 1
   int wave_sum[kMaxRowWaves];
+  SegDesc seg[B::kMax];
+  int ids[B::kMax][kStageWin][2 * kWin];  // block ids of the segment's tiles lt .. lt + 127 (-1: absent)
+  float kscale[B::kMax][HG];
+  float vscale[B::kMax][HG];
+  uint16_t q[B::kMax][HG * G][B::kQRow];
+  // Results, row = local kv head * G + query head of the group: the
+  // accumulators and, per row, the rounded-probability sum (psum), the fp32
+  // sum (le) and the reference (ms) they are relative to; the flush
+  // normalises them.
+  float out[B::kMax][HG * G][kD];
+  float psum[B::kMax][HG * G];
+  float le[B::kMax][HG * G];
+  float ms[B::kMax][HG * G];
 };
 
 __device__ __forceinline__ int clamped_ctx(const DecodeArgs& p, int b) {
@@ -52,8 +92,8 @@ __device__ __forceinline__ int clamped_ctx(const DecodeArgs& p, int b) {
 // ceil(ctx / unit) work units per sequence: 32-token tiles, or partitions;
 // an empty context still counts one) and returns the chunk's total.
 // Called by every thread of the NT-thread workgroup (it synchronises).
-template <int NT>
-__device__ int scan_chunk(const DecodeArgs& p, RowsSmem& sm, int b0, int nhg, int unit, int min_units) {
+template <int NT, class SM>
+__device__ int scan_chunk(const DecodeArgs& p, SM& sm, int b0, int nhg, int unit, int min_units) {
   constexpr int SPT = kChunk / NT;  // sequences per thread
   static_assert(SPT * NT == kChunk && NT / kWaveSize <= kMaxRowWaves, "scan layout");
   const int tid = threadIdx.x, lane = tid & (kWaveSize - 1), wave = tid / kWaveSize;
@@ -131,51 +171,90 @@ __device__ __forceinline__ void row_load_v(const DecodeArgs& p, int g, const int
     C::template load_v<row_policy<C>()>(sr.v[b], block_rsrc(p.v_cache, L.block, id[b]), off, L, soff);
 }
 
-// Writes one head's result of a segment: the final output (bf16, normalised)
-// when the segment is the whole stream, else a record (fp32 normalised output
-// and natural-log LSE).  acc[i][j] holds O[row 4kg + j][8n + i]; the row's
-// max and sums sit in lane `row` of the score layout.
-template <class C, int G>
-__device__ __forceinline__ void write_head(const DecodeArgs& p, const RowsArgs& r, const WaveState& st, int b, int g,
-                                           bool whole, int rec, int lane) {
+// Stages one head's result of a segment in LDS: its accumulators (acc[i][j]
+// holds O[row 4kg + j][8n + i], rows 0 .. G - 1 of local kv head hl), the
+// rounded-probability sums (psum[j] of lane group kg: row 4kg + j), and the
+// fp32 sum and reference of head n (lane n).  No lane exchange is needed.
+template <int G, int HG>
+__device__ __forceinline__ void stage_head(RowsSmem<G, HG>& sm, int s, int hl, const WaveState& st, int lane) {
   const int n = lane & 15, kg = lane >> 4;
   const float lsum_e = sum4(st.lsum_e);
-  const float vscale = C::kFp8 ? kv_scale(p.v_scale, p.flags, g) : 1.f;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int row = 4 * kg + j;
-    const float L = st.psum[j];  // rounded-probability sum of head `row`
-    const float Le = __shfl(lsum_e, row);
-    const float ms = __shfl(st.ms, row);
     if (row < G) {
-      const float inv = L > 0.f ? vscale / L : 0.f;
-      const float lse = Le > 0.f ? (ms + fast_log2(Le)) * kLn2 : -INFINITY;
-      const int64_t orow = (int64_t)b * p.dims.num_q_heads + g * G + row;
-      if (whole) {
-        uint32_t w[4];
+      float* dst = &sm.out[s][hl * G + row][8 * n];
+      *reinterpret_cast<float4*>(dst) = make_float4(st.acc[0][j], st.acc[1][j], st.acc[2][j], st.acc[3][j]);
+      *reinterpret_cast<float4*>(dst + 4) = make_float4(st.acc[4][j], st.acc[5][j], st.acc[6][j], st.acc[7][j]);
+      if (n == 0) sm.psum[s][hl * G + row] = st.psum[j];
+    }
+  }
+  if (kg == 0 && n < G) {
+    sm.le[s][hl * G + n] = lsum_e;
+    sm.ms[s][hl * G + n] = st.ms;
+  }
+}
+
+// Writes a batch's staged results, one wave per segment: each of its
+// HG * G rows is normalised (scaled by vscale / the rounded-probability sum;
+// LSE = ms + log2(le), in natural log) and goes to the final output (bf16)
+// and out_lse when the segment is its whole stream, else to its record: a
+// split-K partition record ([B][Hq][P][D], [B][Hq][P]) in partition mode, or
+// the range's record slot.  Eight columns per lane; a wave reads all its
+// rows of a pass from LDS before it stores any.
+template <class C, int G, int HG, int NT>
+__device__ __forceinline__ void flush_batch(const DecodeArgs& p, const RowsArgs& r, const RowsSmem<G, HG>& sm,
+                                            int nseg, int wave, int lane) {
+  constexpr int kRows = HG * G;
+  constexpr int kCh = kD / 8;
+  constexpr int kItems = kRows * kCh;               // 8-column pieces per segment
+  constexpr int kPass = 8;                          // pieces per lane per pass
+  constexpr int kPerPass = kPass * kWaveSize;
+  for (int s = wave; s < nseg; s += NT / kWaveSize) {
+    const SegDesc d = read_seg(sm, s);
+    for (int i0 = 0; i0 < kItems; i0 += kPerPass) {
+      float4 v0[kPass], v1[kPass];
+      float L[kPass], Le[kPass], M[kPass], vsc[kPass];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          w[i] = (uint32_t)f32_to_bf16_rne(st.acc[2 * i][j] * inv) |
-                 ((uint32_t)f32_to_bf16_rne(st.acc[2 * i + 1][j] * inv) << 16);
-        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.out) + orow * kD + 8 * n) = make_uint4(w[0], w[1], w[2], w[3]);
-        if (n == 0 && p.out_lse) p.out_lse[orow] = lse;
-      } else if (r.part_tiles > 0) {
-        // split-K record of partition `rec`: [B][Hq][P][D] and [B][Hq][P]
-        const int64_t prow = orow * p.max_partitions + rec;
-        float* dst = p.part_out + prow * kD + 8 * n;
-        *reinterpret_cast<float4*>(dst) =
-            make_float4(st.acc[0][j] * inv, st.acc[1][j] * inv, st.acc[2][j] * inv, st.acc[3][j] * inv);
-        *reinterpret_cast<float4*>(dst + 4) =
-            make_float4(st.acc[4][j] * inv, st.acc[5][j] * inv, st.acc[6][j] * inv, st.acc[7][j] * inv);
-        if (n == 0) p.part_lse[prow] = lse;
-      } else {
-        const int hrow = (g % r.head_group) * G + row;  // row inside the head group
-        float* dst = r.rec_out + ((int64_t)rec * r.head_group * G + hrow) * kD + 8 * n;
-        *reinterpret_cast<float4*>(dst) =
-            make_float4(st.acc[0][j] * inv, st.acc[1][j] * inv, st.acc[2][j] * inv, st.acc[3][j] * inv);
-        *reinterpret_cast<float4*>(dst + 4) =
-            make_float4(st.acc[4][j] * inv, st.acc[5][j] * inv, st.acc[6][j] * inv, st.acc[7][j] * inv);
-        if (n == 0) r.rec_lse[(int64_t)rec * r.head_group * G + hrow] = lse;
+      for (int k = 0; k < kPass; ++k) {
+        const int i = i0 + k * kWaveSize + lane;
+        const int row = (i < kItems ? i : 0) / kCh, c = (i < kItems ? i : 0) % kCh;
+        v0[k] = *reinterpret_cast<const float4*>(&sm.out[s][row][8 * c]);
+        v1[k] = *reinterpret_cast<const float4*>(&sm.out[s][row][8 * c + 4]);
+        L[k] = sm.psum[s][row];
+        Le[k] = sm.le[s][row];
+        M[k] = sm.ms[s][row];
+        vsc[k] = C::kFp8 ? sm.vscale[s][row / G] : 1.f;
+      }
+#pragma unroll
+      for (int k = 0; k < kPass; ++k) {
+        const int i = i0 + k * kWaveSize + lane;
+        if (i >= kItems) continue;
+        const int row = i / kCh, c = i % kCh;
+        const float inv = L[k] > 0.f ? vsc[k] / L[k] : 0.f;
+        const float4 a = make_float4(v0[k].x * inv, v0[k].y * inv, v0[k].z * inv, v0[k].w * inv);
+        const float4 b = make_float4(v1[k].x * inv, v1[k].y * inv, v1[k].z * inv, v1[k].w * inv);
+        const float ls = Le[k] > 0.f ? (M[k] + fast_log2(Le[k])) * kLn2 : -INFINITY;
+        const int64_t orow = (int64_t)d.b * p.dims.num_q_heads + (int64_t)d.hg * kRows + row;
+        if (d.whole) {
+          const uint32_t w0 = (uint32_t)f32_to_bf16_rne(a.x) | ((uint32_t)f32_to_bf16_rne(a.y) << 16);
+          const uint32_t w1 = (uint32_t)f32_to_bf16_rne(a.z) | ((uint32_t)f32_to_bf16_rne(a.w) << 16);
+          const uint32_t w2 = (uint32_t)f32_to_bf16_rne(b.x) | ((uint32_t)f32_to_bf16_rne(b.y) << 16);
+          const uint32_t w3 = (uint32_t)f32_to_bf16_rne(b.z) | ((uint32_t)f32_to_bf16_rne(b.w) << 16);
+          *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.out) + orow * kD + 8 * c) = make_uint4(w0, w1, w2, w3);
+          if (c == 0 && p.out_lse) p.out_lse[orow] = ls;
+        } else if (r.part_tiles > 0) {
+          const int64_t prow = orow * p.max_partitions + d.rec;
+          float* dst = p.part_out + prow * kD + 8 * c;
+          *reinterpret_cast<float4*>(dst) = a;
+          *reinterpret_cast<float4*>(dst + 4) = b;
+          if (c == 0) p.part_lse[prow] = ls;
+        } else {
+          float* dst = r.rec_out + ((int64_t)d.rec * kRows + row) * kD + 8 * c;
+          *reinterpret_cast<float4*>(dst) = a;
+          *reinterpret_cast<float4*>(dst + 4) = b;
+          if (c == 0) r.rec_lse[(int64_t)d.rec * kRows + row] = ls;
+        }
       }
     }
   }
@@ -187,55 +266,177 @@ __device__ __forceinline__ void write_head(const DecodeArgs& p, const RowsArgs& 
 // gave FP8 no more bandwidth, see step_blocks).
 constexpr int kRowSets = 2;
 
-// One segment for this wave: tiles lt .. et - 1 of sequence b (context ctx)
-// for kv heads g0 .. g0 + HPW - 1, in steps of NB 16-token blocks (NB / 2
-// tiles).  The wave walks pairs s = (step s / HPW, head s % HPW) with NS
-// register sets: set j always holds pairs j, j + NS, j + 2NS, ... (one head,
-// every NS/HPW-th step).  A set's next step is loaded as soon as its current
-// step's MFMAs have consumed the registers (K after the scores, V after
-// P V), so while one set is computed the other sets' loads and this set's
-// next loads are in flight.  Blocks past the segment are absent: their loads
-// return zeros without touching memory and the step masks them, so every
-// iteration issues the same loads in the same order.
-template <class C, int G, int HPW>
-__device__ __forceinline__ void run_segment(const DecodeArgs& p, const RowsArgs& r, int b, int ctx, int lt, int et,
-                                            int g0, bool whole, int rec, int lane) {
+template <int G, int HG>
+__device__ __forceinline__ SegDesc read_seg(const RowsSmem<G, HG>& sm, int s) {
+  SegDesc d;
+  d.b = __builtin_amdgcn_readfirstlane(sm.seg[s].b);
+  d.ctx = __builtin_amdgcn_readfirstlane(sm.seg[s].ctx);
+  d.lt = __builtin_amdgcn_readfirstlane(sm.seg[s].lt);
+  d.et = __builtin_amdgcn_readfirstlane(sm.seg[s].et);
+  d.hg = __builtin_amdgcn_readfirstlane(sm.seg[s].hg);
+  d.rec = __builtin_amdgcn_readfirstlane(sm.seg[s].rec);
+  d.whole = __builtin_amdgcn_readfirstlane(sm.seg[s].whole);
+  d.pad = 0;
+  return d;
+}
+
+// The workgroup stages a batch of nseg segments (descriptors already in
+// sm.seg), one wave per segment: the first kStageWin windows of the
+// segment's block ids, its query rows and, for FP8, the head group's K and V
+// scales.  A wave issues all its loads before it stores any of them to LDS,
+// so the batch costs one memory round trip.
+template <class C, int G, int HG, int NT>
+__device__ __forceinline__ void stage_batch(const DecodeArgs& p, RowsSmem<G, HG>& sm, int nseg, int wave, int lane) {
+  constexpr int kIdsPer = kStageWin * 2 * kWin / kWaveSize;  // ids per lane
+  constexpr int kRows = HG * G;
+  constexpr int kQCh = kRows * (kD / 8);                     // 16-byte query chunks per segment
+  constexpr int kQPass = 8;                                  // chunks per lane per pass
+  const int MB = p.dims.max_blocks_per_seq;
+  const bool qvec = ((uintptr_t)p.q % 16 == 0) && (p.q_seq_stride % 8 == 0);
+  for (int s = wave; s < nseg; s += NT / kWaveSize) {
+    const SegDesc d = read_seg(sm, s);
+    const int lb_end = (d.ctx + kBS - 1) / kBS;  // <= MB: contexts are clamped to the table's capacity
+    const int32_t* bt = p.block_tables + (int64_t)d.b * MB;
+    int idv[kIdsPer];
+#pragma unroll
+    for (int k = 0; k < kIdsPer; ++k) {
+      const int e = k * kWaveSize + lane;
+      const int tile = d.lt + (e >> 1);
+      const int lb = 2 * tile + (e & 1);
+      idv[k] = (tile < d.et && lb < lb_end) ? bt[lb] : -1;
+    }
+    float ks = 1.f, vs = 1.f;
+    if constexpr (C::kFp8) {
+      if (lane < HG) {
+        ks = kv_scale(p.k_scale, p.flags, d.hg * HG + lane);
+        vs = kv_scale(p.v_scale, p.flags, d.hg * HG + lane);
+      }
+    }
+    const uint16_t* qbase = static_cast<const uint16_t*>(p.q) + (int64_t)d.b * p.q_seq_stride + (int64_t)d.hg * kRows * kD;
+    for (int c0 = 0; c0 < kQCh; c0 += kQPass * kWaveSize) {
+      uint4 qv[kQPass];
+#pragma unroll
+      for (int k = 0; k < kQPass; ++k) {
+        const int c = c0 + k * kWaveSize + lane;
+        qv[k] = make_uint4(0, 0, 0, 0);
+        if (c < kQCh) {
+          const uint16_t* src = qbase + (c / (kD / 8)) * kD + 8 * (c % (kD / 8));
+          if (qvec) {
+            qv[k] = *reinterpret_cast<const uint4*>(src);
+          } else {
+            uint32_t w[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) w[t] = (uint32_t)src[2 * t] | ((uint32_t)src[2 * t + 1] << 16);
+            qv[k] = make_uint4(w[0], w[1], w[2], w[3]);
+          }
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < kQPass; ++k) {
+        const int c = c0 + k * kWaveSize + lane;
+        if (c < kQCh) *reinterpret_cast<uint4*>(&sm.q[s][c / (kD / 8)][8 * (c % (kD / 8))]) = qv[k];
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kIdsPer; ++k) {
+      const int e = k * kWaveSize + lane;
+      const int id = idv[k];
+      sm.ids[s][e / (2 * kWin)][e % (2 * kWin)] = (unsigned)id < (unsigned)p.dims.num_blocks ? id : -1;
+    }
+    if constexpr (C::kFp8) {
+      if (lane < HG) {
+        sm.kscale[s][lane] = ks;
+        sm.vscale[s][lane] = vs;
+      }
+    }
+  }
+}
+
+// Query rows of kv head `hl` (inside the head group) of staged segment s as
+// the B operand of the score MFMAs (zero for n >= G).
+template <class C, int G, int HG>
+__device__ __forceinline__ void lds_q_operand(const RowsSmem<G, HG>& sm, int s, int hl, short8 (&qb)[4], int n,
+                                              int kg) {
+  const uint16_t* row = sm.q[s][hl * G + (n < G ? n : 0)];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    uint4 v = *reinterpret_cast<const uint4*>(row + score_d<C>(c, kg, 0));
+    if (n >= G) v = make_uint4(0, 0, 0, 0);
+    qb[c] = __builtin_bit_cast(short8, v);
+  }
+}
+
+// One wave's work on a batch of segments: a continuous pipeline over the
+// sequence of (step, head) pairs of all the batch's segments, in steps of NB
+// 16-token blocks (NB / 2 tiles).  The wave owns kv heads wave * HPW ..
+// + HPW - 1 of each segment's head group.  NS register sets hold pairs
+// j, j + NS, j + 2NS, ...: a set's next pair is loaded as soon as its
+// current one's MFMAs have consumed the registers (K after the scores, V
+// after P V), and when the next pair lies in the next segment its loads go
+// out before the current segment ends, so moving to a new segment costs no
+// wait for memory.  A load cursor runs NS / HPW steps ahead of the compute
+// cursor; block ids come from the staged first window of a segment, later
+// windows are read from the table one window ahead.  At each segment's end
+// the wave writes its heads' results and takes the next segment's query rows
+// from LDS.  Segments without tiles (empty contexts) write out = 0 and
+// lse = -inf.  Pairs past the batch are absent: their loads return zeros
+// without touching memory.
+template <class C, int G, int HG, int HPW>
+__device__ __forceinline__ void run_batch(const DecodeArgs& p, RowsSmem<G, HG>& sm, int nseg, int wave, int lane) {
   constexpr int NB = step_blocks<C>();
   constexpr int ST = NB / 2;  // tiles per step
   constexpr int NS = kRowSets;
-  static_assert(NS % HPW == 0, "each set must stay on one head");
-  static_assert(32 % ST == 0, "a step's tiles share one window of block ids");
-  constexpr int kAdvance = NS / HPW;  // steps a set moves per iteration
-  const int kg = lane >> 4;
-  short8 qb[HPW][4];
-  WaveState st[HPW];
-  float csc[HPW];
-  const bool qvec = ((uintptr_t)p.q % 16 == 0) && (p.q_seq_stride % 8 == 0);
-#pragma unroll
-  for (int hh = 0; hh < HPW; ++hh) {
-    const uint16_t* qrow =
-        static_cast<const uint16_t*>(p.q) + (int64_t)b * p.q_seq_stride + (int64_t)(g0 + hh) * G * kD;
-    load_q_operand<C, G>(qb[hh], qrow, qvec, lane & 15, kg);
-    st[hh].reset();
-    float c = p.softmax_scale * kLog2e;
-    if constexpr (C::kFp8) c *= kv_scale(p.k_scale, p.flags, g0 + hh);
-    csc[hh] = fold_score_scale(c, qb[hh]);
-  }
+  static_assert(NS % HPW == 0, "a set must stay on one head");
+  static_assert(kWin % ST == 0, "a step's tiles share one window of block ids");
+  const int n = lane & 15, kg = lane >> 4;
+  auto nsteps_of = [&](int s) {
+    return __builtin_amdgcn_readfirstlane((sm.seg[s].et - sm.seg[s].lt + ST - 1) / ST);
+  };
 
-  const int lb_end = (ctx + kBS - 1) / kBS;
-  int win = 0;
-  int ids = preload_row_ids(p, b, lt, et, lb_end, 0, lane);
-  // Block ids of step k (-1 when absent), from the 32-tile window of ids.
-  auto step_ids = [&](int k, int (&id)[NB]) {
-    const int kt = ST * k;
-    if ((kt >> 5) != win) {
-      win = kt >> 5;
-      ids = preload_row_ids(p, b, lt, et, lb_end, 32 * win, lane);
+  // ---- load cursor: segment ls, step lk (ls == nseg: past the batch) ----
+  int ls = 0, lk = 0, lwin = 0, l_nsteps = 0, l_b = 0, l_lt = 0, l_et = 0, l_lbend = 0, l_g0 = wave * HPW;
+  int lids = -1, lnext = -1;
+  // Windows 0 .. kStageWin - 1 come from LDS; a longer segment's later
+  // windows are read from the table one window ahead.
+  auto l_window = [&](int w) {
+    if (w < kStageWin) {
+      lids = sm.ids[ls][w][lane];
+    } else {
+      lids = lnext;
     }
+    if (w + 1 >= kStageWin && l_lt + kWin * (w + 1) < l_et)
+      lnext = preload_row_ids(p, l_b, l_lt, l_et, l_lbend, kWin * (w + 1), lane);
+  };
+  auto l_enter = [&](int s) {
+    const SegDesc d = read_seg(sm, s);
+    ls = s;
+    lk = 0;
+    lwin = 0;
+    l_nsteps = nsteps_of(s);
+    l_b = d.b;
+    l_lt = d.lt;
+    l_et = d.et;
+    l_lbend = (d.ctx + kBS - 1) / kBS;
+    l_g0 = d.hg * HG + wave * HPW;
+    l_window(0);
+  };
+  auto l_advance = [&]() {
+    if (ls >= nseg) return;
+    if (++lk < l_nsteps) {
+      if ((ST * lk) / kWin != lwin) l_window(++lwin);
+      return;
+    }
+    int s = ls + 1;
+    while (s < nseg && nsteps_of(s) == 0) ++s;
+    if (s < nseg) l_enter(s);
+    else ls = nseg;
+  };
+  auto l_ids = [&](int (&id)[NB]) {
+    const int kt = ST * lk - kWin * lwin;  // first tile of the step inside its window
 #pragma unroll
     for (int t = 0; t < ST; ++t) {
-      id[2 * t] = __builtin_amdgcn_readlane(ids, 2 * ((kt + t) & 31));
-      id[2 * t + 1] = __builtin_amdgcn_readlane(ids, 2 * ((kt + t) & 31) + 1);
+      id[2 * t] = ls < nseg ? __builtin_amdgcn_readlane(lids, 2 * (kt + t)) : -1;
+      id[2 * t + 1] = ls < nseg ? __builtin_amdgcn_readlane(lids, 2 * (kt + t) + 1) : -1;
     }
   };
   auto valid_bits = [](const int (&id)[NB]) {
@@ -244,49 +445,78 @@ __device__ __forceinline__ void run_segment(const DecodeArgs& p, const RowsArgs&
     for (int bb = 0; bb < NB; ++bb) v |= (id[bb] >= 0 ? 1u : 0u) << bb;
     return v;
   };
+
+  // ---- compute cursor: segment cs, step ck ----
+  int cs = 0, ck = 0, c_nsteps = 0, c_lt = 0, c_ctx = 0;
+  short8 qb[HPW][4];
+  float csc[HPW];
+  WaveState st[HPW];
+  auto write_empty = [&](int s) {  // a segment without tiles (an empty context): out = 0, lse = -inf
+    WaveState e;
+    e.reset();
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh) stage_head<G, HG>(sm, s, wave * HPW + hh, e, lane);
+  };
+  auto c_enter = [&](int s) {
+    const SegDesc d = read_seg(sm, s);
+    cs = s;
+    ck = 0;
+    c_nsteps = nsteps_of(s);
+    c_lt = d.lt;
+    c_ctx = d.ctx;
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh) {
+      lds_q_operand<C, G, HG>(sm, s, wave * HPW + hh, qb[hh], n, kg);
+      float c = p.softmax_scale * kLog2e;
+      if constexpr (C::kFp8) c *= sm.kscale[s][wave * HPW + hh];
+      csc[hh] = fold_score_scale(c, qb[hh]);
+      st[hh].reset();
+    }
+  };
+  int s0 = 0;
+  while (s0 < nseg && nsteps_of(s0) == 0) write_empty(s0++);
+  if (s0 >= nseg) return;
+  c_enter(s0);
+  l_enter(s0);
+
   StepRegs<C, NB> sr[NS];
   int pid[NS][NB];
 #pragma unroll
-  for (int j = 0; j < NS; ++j) {
-    if (j % HPW == 0) {
-      step_ids(j / HPW, pid[j]);
-    } else {
-#pragma unroll
-      for (int bb = 0; bb < NB; ++bb) pid[j][bb] = pid[j - j % HPW][bb];
-    }
-  }
-#pragma unroll
   for (int j = 0; j < NS; ++j) {  // the loop's load order: K, V of each set in turn
-    row_load_k<C, NB>(p, g0 + j % HPW, pid[j], lane, sr[j]);
+    if (j % HPW == 0 && j > 0) l_advance();
+    l_ids(pid[j]);
+    row_load_k<C, NB>(p, l_g0 + j % HPW, pid[j], lane, sr[j]);
     __builtin_amdgcn_sched_barrier(0);
-    row_load_v<C, NB>(p, g0 + j % HPW, pid[j], lane, sr[j]);
+    row_load_v<C, NB>(p, l_g0 + j % HPW, pid[j], lane, sr[j]);
     __builtin_amdgcn_sched_barrier(0);
   }
-  const int nsteps = (et - lt + ST - 1) / ST;
-  const int iters = (nsteps + kAdvance - 1) / kAdvance;
-  for (int it = 0; it < iters; ++it) {
+  bool done = false;
+  while (!done) {
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
       const int h = j % HPW;
-      const int k = it * kAdvance + j / HPW;  // this set's step
+      if (j > 0 && done) break;  // (one head per wave: the batch may end between two sets)
+      if (h == 0) l_advance();
       int nid[NB];
-      if (h == 0) {
-        step_ids(k + kAdvance, nid);
-      } else {
-#pragma unroll
-        for (int bb = 0; bb < NB; ++bb) nid[bb] = pid[j - h][bb];  // the head-0 set of the same step looked it up
-      }
-      float4v s[NB];
-      step_scores<C, NB>(sr[j], qb[h], s);
-      row_load_k<C, NB>(p, g0 + h, nid, lane, sr[j]);
-      step_update<C, NB>(st[h], sr[j], s, csc[h], valid_bits(pid[j]), kTile * (lt + ST * k), ctx, kg);
-      row_load_v<C, NB>(p, g0 + h, nid, lane, sr[j]);
+      l_ids(nid);
+      const int lg = l_g0 + h;
+      float4v sc[NB];
+      step_scores<C, NB>(sr[j], qb[h], sc);
+      row_load_k<C, NB>(p, lg, nid, lane, sr[j]);
+      step_update<C, NB>(st[h], sr[j], sc, csc[h], valid_bits(pid[j]), kTile * (c_lt + ST * ck), c_ctx, kg);
+      row_load_v<C, NB>(p, lg, nid, lane, sr[j]);
 #pragma unroll
       for (int bb = 0; bb < NB; ++bb) pid[j][bb] = nid[bb];
+      if (h == HPW - 1 && ++ck == c_nsteps) {  // the segment is done: write it, move to the next
+#pragma unroll
+        for (int hh = 0; hh < HPW; ++hh) stage_head<G, HG>(sm, cs, wave * HPW + hh, st[hh], lane);
+        int s = cs + 1;
+        while (s < nseg && nsteps_of(s) == 0) write_empty(s++);
+        if (s >= nseg) done = true;
+        else c_enter(s);
+      }
     }
   }
-#pragma unroll
-  for (int hh = 0; hh < HPW; ++hh) write_head<C, G>(p, r, st[hh], b, g0 + hh, whole, rec, lane);
 }
 
 // One workgroup per equal range of the flattened list of work units: the
@@ -297,10 +527,12 @@ __device__ __forceinline__ void run_segment(const DecodeArgs& p, const RowsArgs&
 // and last tiles.  Record slot 2w holds the range's first stream when split,
 // slot 2w + 1 its last one (when that is another stream).  In partition mode
 // every partition of a split context writes its own record, at its index.
+// The range's segments are located, staged and run in batches.
 template <class C, int G, int HPW, int NT>
 __global__ __launch_bounds__(NT, 1) void paged_decode_rows_kernel(DecodeArgs p, RowsArgs r) {
-  __shared__ RowsSmem sm;
   constexpr int HG = NT / kWaveSize * HPW;
+  using Bt = Batch<G, HG>;
+  __shared__ RowsSmem<G, HG> sm;
   const int lane = threadIdx.x & (kWaveSize - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWaveSize);
   const int B = p.dims.num_seqs;
@@ -323,40 +555,52 @@ __global__ __launch_bounds__(NT, 1) void paged_decode_rows_kernel(DecodeArgs p, 
   bool first = true;
   if (!parts && threadIdx.x == 0 && t_lo >= t_hi) r.first_stream[wg] = -1;
   while (pos < t_hi) {
-    int rel = pos - base;
-    while (rel >= __builtin_amdgcn_readfirstlane(sm.pre[kChunk])) {  // uniform: every thread moves on together
-      base += __builtin_amdgcn_readfirstlane(sm.pre[kChunk]);
-      b0 += kChunk;
-      scan_chunk<NT>(p, sm, b0, nhg, unit, min_units);
-      rel = pos - base;
+    int nseg = 0;
+    while (pos < t_hi && nseg < Bt::kMax) {
+      int rel = pos - base;
+      while (rel >= __builtin_amdgcn_readfirstlane(sm.pre[kChunk])) {  // uniform: every thread moves on together
+        base += __builtin_amdgcn_readfirstlane(sm.pre[kChunk]);
+        b0 += kChunk;
+        scan_chunk<NT>(p, sm, b0, nhg, unit, min_units);
+        rel = pos - base;
+      }
+      int lo = 0, hi = kChunk;  // sm.pre[lo] <= rel < sm.pre[hi]
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (__builtin_amdgcn_readfirstlane(sm.pre[mid]) <= rel) lo = mid;
+        else hi = mid;
+      }
+      const int b = b0 + lo;
+      const int ctx = __builtin_amdgcn_readfirstlane(clamped_ctx(p, b));
+      const int ntb = (ctx + kTile - 1) / kTile;                      // tiles of the stream
+      const int ntu = max((ctx + unit - 1) / unit, min_units);        // units of the stream
+      const int off = rel - __builtin_amdgcn_readfirstlane(sm.pre[lo]);
+      const int hg = off / ntu;
+      const int lu = off - hg * ntu;
+      const int eu = parts ? lu + 1 : min(ntu, lu + (t_hi - pos));
+      const int lt = lu * upt;
+      const int et = min(ntb, eu * upt);
+      const int u = b * nhg + hg;
+      const bool whole = parts ? ntu == 1 : (lu == 0 && eu == ntu);
+      if (threadIdx.x == 0) {
+        if (!parts) {
+          if (first) r.first_stream[wg] = u;
+          if (lt == 0) r.wg_first[u] = wg;
+          if (et == ntb) r.wg_last[u] = wg;
+        }
+        sm.seg[nseg] = SegDesc{b, ctx, lt, et, hg, parts ? lu : 2 * wg + (first ? 0 : 1), whole ? 1 : 0, 0};
+      }
+      pos += eu - lu;
+      first = false;
+      ++nseg;
     }
-    int lo = 0, hi = kChunk;  // sm.pre[lo] <= rel < sm.pre[hi]
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (__builtin_amdgcn_readfirstlane(sm.pre[mid]) <= rel) lo = mid;
-      else hi = mid;
-    }
-    const int b = b0 + lo;
-    const int ctx = __builtin_amdgcn_readfirstlane(clamped_ctx(p, b));
-    const int ntb = (ctx + kTile - 1) / kTile;                      // tiles of the stream
-    const int ntu = max((ctx + unit - 1) / unit, min_units);        // units of the stream
-    const int off = rel - __builtin_amdgcn_readfirstlane(sm.pre[lo]);
-    const int hg = off / ntu;
-    const int lu = off - hg * ntu;
-    const int eu = parts ? lu + 1 : min(ntu, lu + (t_hi - pos));
-    const int lt = lu * upt;
-    const int et = min(ntb, eu * upt);
-    const int u = b * nhg + hg;
-    const bool whole = parts ? ntu == 1 : (lu == 0 && eu == ntu);
-    if (!parts && threadIdx.x == 0) {
-      if (first) r.first_stream[wg] = u;
-      if (lt == 0) r.wg_first[u] = wg;
-      if (et == ntb) r.wg_last[u] = wg;
-    }
-    run_segment<C, G, HPW>(p, r, b, ctx, lt, et, hg * HG + wave * HPW, whole,
-                           parts ? lu : 2 * wg + (first ? 0 : 1), lane);
-    pos += eu - lu;
-    first = false;
+    __syncthreads();  // the batch's descriptors
+    stage_batch<C, G, HG, NT>(p, sm, nseg, wave, lane);
+    __syncthreads();  // the batch's ids, query rows and scales
+    run_batch<C, G, HG, HPW>(p, sm, nseg, wave, lane);
+    __syncthreads();  // every wave has staged its results
+    flush_batch<C, G, HG, NT>(p, r, sm, nseg, wave, lane);
+    __syncthreads();  // the batch is written before the next one is staged
   }
 }
 
