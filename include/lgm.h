@@ -216,8 +216,8 @@ int32_t lgm_paged_decode_partition_size(lgm_paged_dims dims, int32_t max_context
  * regions, each 256-byte aligned:
  *  - equal ranges (see lgm_paged_decode_partition_size): two records per
  *    range (fp32 outputs of the head group's Hq * 8 / Hkv or Hq * 4 / Hkv
- *    query heads, D each, and their natural-log LSEs), then int32 range
- *    and context bookkeeping (one per range, two per context and head group);
+ *    query heads, D each, and their natural-log LSEs), then int32 context
+ *    bookkeeping (two per context and head group);
  *  - partitions (the whole-row partition plan, the work-queue plan on the
  *    other matrix-core shapes, the vector-ALU plan on the rest): when
  *    contexts are split, fp32 partial outputs [B][Hq][P][D] and LSEs

@@ -195,7 +195,7 @@ struct Plan {
   int32_t ps, P;
   size_t counters_bytes, part_out_bytes, part_lse_bytes;
   int32_t W, HG;  // rows: workgroups (ranges), kv heads per workgroup
-  size_t rec_out_bytes, rec_lse_bytes, first_bytes, stream_bytes;
+  size_t rec_out_bytes, rec_lse_bytes, stream_bytes;
   size_t total;
 };
 
@@ -245,9 +245,8 @@ lgm_status plan_decode(const char* fn, const lgm_paged_dims& d, int32_t max_ctx,
     pl.counters_bytes = kCounterSlot;
     pl.rec_out_bytes = align256((size_t)W * 2 * rows_per_rec * d.head_dim * sizeof(float));
     pl.rec_lse_bytes = align256((size_t)W * 2 * rows_per_rec * sizeof(float));
-    pl.first_bytes = align256((size_t)W * sizeof(int32_t));
     pl.stream_bytes = align256((size_t)streams * sizeof(int32_t));
-    pl.total = pl.counters_bytes + pl.rec_out_bytes + pl.rec_lse_bytes + pl.first_bytes + 2 * pl.stream_bytes;
+    pl.total = pl.counters_bytes + pl.rec_out_bytes + pl.rec_lse_bytes + 2 * pl.stream_bytes;
     return LGM_OK;
   }
   pl.ps = resolve_partition(fn, d, max_ctx, ps_arg, persistent);
@@ -592,8 +591,6 @@ lgm_status decode_attn_impl(const char* fn, void* out, float* out_lse, const voi
     w += pl.rec_out_bytes;
     r.rec_lse = reinterpret_cast<float*>(w);
     w += pl.rec_lse_bytes;
-    r.first_stream = reinterpret_cast<int32_t*>(w);
-    w += pl.first_bytes;
     r.wg_first = reinterpret_cast<int32_t*>(w);
     w += pl.stream_bytes;
     r.wg_last = reinterpret_cast<int32_t*>(w);

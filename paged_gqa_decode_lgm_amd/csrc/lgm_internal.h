@@ -142,9 +142,8 @@ struct RowsArgs {
   int32_t head_group;     // HG: kv heads per workgroup (8, or 4)
   float* rec_out;         // [W][2][HG * G][D] normalised partial outputs
   float* rec_lse;         // [W][2][HG * G] natural-log LSEs
-  int32_t* first_stream;  // [W] stream each range starts in, -1 for an empty range
-  int32_t* wg_first;      // [B * Hkv / HG] workgroup holding the stream's first tile
-  int32_t* wg_last;       // [B * Hkv / HG] workgroup holding its last tile
+  int32_t* wg_first;  // [B * Hkv / HG] record slot of the stream's first piece (2w or 2w + 1 for range w)
+  int32_t* wg_last;   // [B * Hkv / HG] workgroup holding its last tile
   // > 0: the ranges are cut into split-K partitions of this many 32-token
   // tiles instead (whole partitions per workgroup); each partition's record
   // goes to DecodeArgs::part_out / part_lse and lse_merge combines them.

@@ -521,13 +521,16 @@ __device__ __forceinline__ void run_batch(const DecodeArgs& p, RowsSmem<G, HG>& 
 
 // One workgroup per equal range of the flattened list of work units: the
 // 32-token tiles of all streams, or (partition mode) their split-K
-// partitions, so that a range holds whole partitions.  Metadata for the
-// range merge: first_stream[w] = the stream the range starts in (-1 if
-// empty), wg_first[u] / wg_last[u] = the workgroups holding stream u's first
-// and last tiles.  Record slot 2w holds the range's first stream when split,
-// slot 2w + 1 its last one (when that is another stream).  In partition mode
-// every partition of a split context writes its own record, at its index.
-// The range's segments are located, staged and run in batches.
+// partitions, so that a range holds whole partitions.  Record slot 2w holds
+// range w's first stream when split, slot 2w + 1 its last one (when that is
+// another stream); so piece k >= 1 of a split stream, held by workgroup
+// i0 + k where it is the first stream, is in slot 2(i0 + k), and only its
+// first piece's slot needs recording: wg_first[u] = that slot, wg_last[u] =
+// the workgroup holding the stream's last tile.  An empty range (more
+// workgroups than tiles) writes LSE -inf in slot 2w, so a stream that spans
+// it merges a record of weight zero there.  In partition mode every
+// partition of a split context writes its own record, at its index.  The
+// range's segments are located, staged and run in batches.
 template <class C, int G, int HPW, int NT>
 __global__ __launch_bounds__(NT, 1) void paged_decode_rows_kernel(DecodeArgs p, RowsArgs r) {
   constexpr int HG = NT / kWaveSize * HPW;
@@ -553,7 +556,9 @@ __global__ __launch_bounds__(NT, 1) void paged_decode_rows_kernel(DecodeArgs p, 
 
   int pos = t_lo;
   bool first = true;
-  if (!parts && threadIdx.x == 0 && t_lo >= t_hi) r.first_stream[wg] = -1;
+  if (!parts && t_lo >= t_hi) {  // an empty range: its first record slot weighs nothing in the merge
+    for (int i = threadIdx.x; i < HG * G; i += NT) r.rec_lse[(int64_t)2 * wg * HG * G + i] = -INFINITY;
+  }
   while (pos < t_hi) {
     int nseg = 0;
     while (pos < t_hi && nseg < Bt::kMax) {
@@ -584,8 +589,7 @@ __global__ __launch_bounds__(NT, 1) void paged_decode_rows_kernel(DecodeArgs p, 
       const bool whole = parts ? ntu == 1 : (lu == 0 && eu == ntu);
       if (threadIdx.x == 0) {
         if (!parts) {
-          if (first) r.first_stream[wg] = u;
-          if (lt == 0) r.wg_first[u] = wg;
+          if (lt == 0) r.wg_first[u] = 2 * wg + (first ? 0 : 1);  // the record slot of the stream's first piece
           if (et == ntb) r.wg_last[u] = wg;
         }
         sm.seg[nseg] = SegDesc{b, ctx, lt, et, hg, parts ? lu : 2 * wg + (first ? 0 : 1), whole ? 1 : 0, 0};
@@ -613,12 +617,16 @@ constexpr int kMergeRows = kMergeThreads / kWaveSize;  // one wave per (sequence
 constexpr int kMergeLanes = kD / 8;                    // lanes per record row: eight columns each
 constexpr int kMergeGroups = kWaveSize / kMergeLanes;  // records in flight per wave
 
-// Merge of the records of one output row.  Lane k first holds the record of
-// the k-th workgroup of the stream (64 at a time) and its weight
-// exp(lse - max); the wave then works as four groups of 16 lanes, each group
-// folding every fourth record into eight columns per lane, and the groups are
-// summed by lane shuffles at the end: no LDS, no barrier.
+// Merge of the records of one output row: two memory round trips.  The
+// first reads the row's context length and its stream's first record slot
+// and last workgroup; the second reads, together, the LSE of every piece
+// (lane k holds piece k) and the records of the first 16 pieces (the wave
+// works as four groups of 16 lanes, group q holding pieces q, q + 4, ...,
+// eight columns per lane).  Max and sum are lane shuffles, the groups' sums
+// are added by lane shuffles at the end: no LDS, no barrier.  Streams of
+// more pieces read the rest in a further pass.
 __global__ __launch_bounds__(kMergeThreads) void rows_merge_kernel(DecodeArgs p, RowsArgs r) {
+  constexpr int kPre = 4;  // pieces per group read with the LSEs
   const int lane = threadIdx.x % kWaveSize;
   const int Hq = p.dims.num_q_heads;
   const int orow = blockIdx.x * kMergeRows + threadIdx.x / kWaveSize;
@@ -630,10 +638,10 @@ __global__ __launch_bounds__(kMergeThreads) void rows_merge_kernel(DecodeArgs p,
   const int HG = r.head_group;
   const int nhg = p.dims.num_kv_heads / HG;
   const int u = b * nhg + g / HG;
-  // The context length and the stream's workgroup span do not depend on
-  // each other: both loads are issued before either is used.
+  // The context length and the stream's slots do not depend on each other:
+  // all three loads are issued before any is used.
   const int ctx = clamped_ctx(p, b);
-  const int i0 = r.wg_first[u];
+  const int s0 = r.wg_first[u];
   const int i1 = r.wg_last[u];
   uint16_t* out = static_cast<uint16_t*>(p.out) + (int64_t)orow * kD;
   const int grp = lane / kMergeLanes;
@@ -643,57 +651,67 @@ __global__ __launch_bounds__(kMergeThreads) void rows_merge_kernel(DecodeArgs p,
     if (lane == 0 && p.out_lse) p.out_lse[orow] = -INFINITY;
     return;
   }
+  const int i0 = s0 >> 1;
   if (i0 == i1) return;  // the only workgroup of the stream wrote the row itself
   const int n = i1 - i0 + 1;
   const int64_t rec_rows = (int64_t)HG * G;
   const int hrow = (g % HG) * G + h % G;
-  // Record of the k-th workgroup from i0, or -1 for a workgroup whose range
-  // is empty (there are more workgroups than tiles).
-  auto rec_of = [&](int k) -> int {
-    const int w = i0 + k;
-    const int f = r.first_stream[w];
-    return f < 0 ? -1 : 2 * w + (f == u ? 0 : 1);
+  auto slot = [&](int k) -> int64_t { return k == 0 ? s0 : 2 * (int64_t)(i0 + k); };
+  auto lse_of = [&](int k) -> float { return r.rec_lse[slot(k) * rec_rows + hrow]; };
+  auto rec_ptr = [&](int k) -> const float4* {
+    return reinterpret_cast<const float4*>(r.rec_out + (slot(k) * rec_rows + hrow) * kD) + 2 * c;
   };
-  auto lse_of = [&](int rec) -> float { return rec < 0 ? -INFINITY : r.rec_lse[rec * rec_rows + hrow]; };
 
-  // The first 64 records stay in registers; longer spans reload the rest.
-  const int rc0 = lane < n ? rec_of(lane) : -1;
-  const float ls0 = lse_of(rc0);
+  const float ls0 = lane < n ? lse_of(lane) : -INFINITY;
+  float4 pa[kPre], pb[kPre];
+#pragma unroll
+  for (int m = 0; m < kPre; ++m) {
+    const int k = grp + kMergeGroups * m;
+    const float4* src = rec_ptr(k < n ? k : 0);
+    pa[m] = src[0];
+    pb[m] = src[1];
+  }
   float mx = ls0;
-  for (int k = lane + kWaveSize; k < n; k += kWaveSize) mx = fmaxf(mx, lse_of(rec_of(k)));
+  for (int k = lane + kWaveSize; k < n; k += kWaveSize) mx = fmaxf(mx, lse_of(k));
 #pragma unroll
   for (int o = 1; o < kWaveSize; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
   const float ms = mx == -INFINITY ? 0.f : mx;
-  const float w0 = rc0 < 0 ? 0.f : expf(ls0 - ms);
+  const float w0 = ls0 == -INFINITY ? 0.f : expf(ls0 - ms);
   float sw = w0;
   for (int k = lane + kWaveSize; k < n; k += kWaveSize) {
-    const int rc = rec_of(k);
-    sw += rc < 0 ? 0.f : expf(lse_of(rc) - ms);
+    const float l = lse_of(k);
+    sw += l == -INFINITY ? 0.f : expf(l - ms);
   }
   const float S = group_sum<kWaveSize>(sw);
 
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  // A record that is absent reads record 0 (always in the workspace) and is
-  // dropped by a select, so unwritten workspace bytes never reach the sum.
-  auto fold = [&](int rk, float wk) {
-    const bool ok = rk >= 0;
-    const float4* src = reinterpret_cast<const float4*>(r.rec_out + ((ok ? rk : 0) * rec_rows + hrow) * kD) + 2 * c;
-    const float4 v0 = src[0];
-    const float4 v1 = src[1];
+  // A piece of weight zero (an empty range, or past the stream) is left out
+  // by a select, so its record's bytes never reach the sum.
+  auto fold = [&](float wk, const float4& v0, const float4& v1) {
     const float x[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = fmaf(wk, ok ? x[e] : 0.f, acc[e]);
+    for (int e = 0; e < 8; ++e) acc[e] = wk == 0.f ? acc[e] : fmaf(wk, x[e], acc[e]);
   };
-  const int n0 = n < kWaveSize ? n : kWaveSize;
-#pragma unroll 4
-  for (int k0 = 0; k0 < n0; k0 += kMergeGroups) {
-    const int k = k0 + grp;  // below 64; lanes at or past n hold record -1
-    fold(__shfl(rc0, k), __shfl(w0, k));
+#pragma unroll
+  for (int m = 0; m < kPre; ++m) {
+    const int k = grp + kMergeGroups * m;  // below 64: lanes at or past n have weight 0
+    const float wk = __shfl(w0, k);        // every lane takes part in the shuffle
+    fold(k < n ? wk : 0.f, pa[m], pb[m]);
   }
-  for (int k0 = kWaveSize; k0 < n; k0 += kMergeGroups) {
+  for (int k0 = kMergeGroups * kPre; k0 < n; k0 += kMergeGroups) {  // n is the same across the wave
     const int k = k0 + grp;
-    const int rk = k < n ? rec_of(k) : -1;
-    fold(rk, rk < 0 ? 0.f : expf(lse_of(rk) - ms));
+    const float wl = __shfl(w0, k % kWaveSize);
+    float wk = 0.f;
+    if (k < n) {
+      if (k < kWaveSize) {
+        wk = wl;
+      } else {
+        const float l = lse_of(k);
+        wk = l == -INFINITY ? 0.f : expf(l - ms);
+      }
+    }
+    const float4* src = rec_ptr(k < n ? k : 0);
+    fold(wk, src[0], src[1]);
   }
 #pragma unroll
   for (int e = 0; e < 8; ++e) {

@@ -322,14 +322,14 @@ def test_row_plan_workspace_formula():
     al = lambda x: (x + 255) // 256 * 256
     d = dims()                                     # 8 kv heads per workgroup, 64 streams of 256 tiles
     W, rows = 256, 8 * 4
-    want = 256 + al(W * 2 * rows * 128 * 4) + al(W * 2 * rows * 4) + al(W * 4) + 2 * al(64 * 4)
+    want = 256 + al(W * 2 * rows * 128 * 4) + al(W * 2 * rows * 4) + 2 * al(64 * 4)
     assert L.lgm_paged_decode_workspace_size(d, 8192, 0, L.LGM_BF16) == want
     assert L.lgm_paged_decode_workspace_size(d, 8192, 0, L.LGM_FP8_E4M3) == want
     assert L.lgm_paged_decode_workspace_size(d, 8192, 0, L.LGM_FP4_E2M1) == want
     small = dims(num_seqs=2, num_q_heads=16, num_kv_heads=4, max_blocks_per_seq=8)  # 2 x 4 tiles: one range
     W, rows = 1, 4 * 4
     assert L.lgm_paged_decode_workspace_size(small, 100, 0, L.LGM_BF16) == (
-        256 + al(W * 2 * rows * 128 * 4) + al(W * 2 * rows * 4) + al(W * 4) + 2 * al(2 * 4))
+        256 + al(W * 2 * rows * 128 * 4) + al(W * 2 * rows * 4) + 2 * al(2 * 4))
 
 
 def test_too_many_partitions_is_unsupported():
