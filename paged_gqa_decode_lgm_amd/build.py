@@ -42,6 +42,7 @@ UNITS = {
     "rope_kv_append.hip": ["-ffp-contract=off"],
     "paged_decode.hip": [],
     "paged_decode_mfma.hip": [],
+    "paged_decode_fused.hip": [],
     # MFMA accumulators in VGPRs: the whole-row step loop then keeps them in
     # the registers its MFMAs use instead of copying them between register
     # files around every step.

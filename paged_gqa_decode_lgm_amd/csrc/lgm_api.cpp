@@ -189,12 +189,14 @@ constexpr size_t kCounterSlot = 256;  // the work-queue counters at the start of
 // that kernel writes (it leaves them zero), then the plan's own regions.  So
 // one zero-filled workspace may serve calls on any plan in turn.
 struct Plan {
+  bool fused;       // single-launch split kernel (small jobs): partitions of ps tokens, merged in the launch
   bool rows;        // whole-row kernel (Hkv % 4 == 0): equal tile ranges (partition_size 0) ...
   bool rows_parts;  // ... or equal runs of whole partitions (an explicit partition_size of whole tiles)
   lgm::PartitionPlan parts;
   int32_t ps, P;
   size_t counters_bytes, part_out_bytes, part_lse_bytes;
   int32_t W, HG;  // rows: workgroups (ranges), kv heads per workgroup
+  int32_t chunk_steps, nchunks;  // fused: 32-token steps per wave per partition, partitions per context
   size_t rec_out_bytes, rec_lse_bytes, stream_bytes;
   size_t total;
 };
@@ -222,12 +224,50 @@ constexpr int64_t kRowsTile = 32;
 constexpr int32_t kRowsMinPartition = LGM_ROWS_MIN_PARTITION;
 constexpr int32_t kRowsMinPartitions = 64;
 
+// Single-launch split plan: taken with partition_size 0 on the matrix-core
+// shapes when the job is small, at most kFusedMaxStreams (sequence, kv head)
+// streams and kFusedMaxTiles 32-token tiles over them at max_context_len.
+// Such a job takes a few microseconds of memory traffic, and a separate
+// merge launch would cost as much again.  Partitions are whole steps of the
+// four waves (128 tokens), sized for about kFusedTargetWorkgroups
+// workgroups and at most kFusedMaxChunks per context.
+#ifndef LGM_FUSED_MAX_TILES
+#define LGM_FUSED_MAX_TILES 2048
+#endif
+constexpr int64_t kFusedMaxTiles = LGM_FUSED_MAX_TILES;
+constexpr int64_t kFusedTargetWorkgroups = 256;
+constexpr int64_t kFusedPartStep = 128;
+
 lgm_status plan_decode(const char* fn, const lgm_paged_dims& d, int32_t max_ctx, int32_t ps_arg, lgm_dtype cache,
                        Plan& pl) {
   pl = Plan{};
   const int G = d.num_q_heads / d.num_kv_heads;
   const lgm_dtype act = cache == LGM_F32 ? LGM_F32 : LGM_BF16;  // the only supported pairings
   const bool persistent = lgm::decode_mfma_supported(act, cache, d.head_dim, G, d.block_size);
+  if (ps_arg == 0 && persistent) {
+    const int64_t streams = (int64_t)d.num_seqs * d.num_kv_heads;
+    const int64_t tiles = streams * (((int64_t)max_ctx + kRowsTile - 1) / kRowsTile);
+    int64_t part = (streams * max_ctx + kFusedTargetWorkgroups - 1) / kFusedTargetWorkgroups;
+    const int64_t least = ((int64_t)max_ctx + lgm::kFusedMaxChunks - 1) / lgm::kFusedMaxChunks;
+    part = part > least ? part : least;
+    part = (part + kFusedPartStep - 1) / kFusedPartStep * kFusedPartStep;
+    part = part < kFusedPartStep ? kFusedPartStep : part;
+    if (streams <= lgm::kFusedMaxStreams && tiles <= kFusedMaxTiles && part / kFusedPartStep <= 32) {
+      pl.fused = true;
+      pl.ps = (int32_t)part;
+      pl.chunk_steps = (int32_t)(part / kFusedPartStep);
+      pl.nchunks = (int32_t)(((int64_t)max_ctx + part - 1) / part);
+      pl.nchunks = pl.nchunks < 1 ? 1 : pl.nchunks;
+      pl.P = pl.nchunks;
+      pl.counters_bytes = kCounterSlot;
+      if (pl.nchunks > 1) {
+        pl.rec_out_bytes = align256((size_t)streams * pl.nchunks * G * d.head_dim * sizeof(float));
+        pl.rec_lse_bytes = align256((size_t)streams * pl.nchunks * G * sizeof(float));
+      }
+      pl.total = pl.counters_bytes + pl.rec_out_bytes + pl.rec_lse_bytes;
+      return LGM_OK;
+    }
+  }
   if (ps_arg == 0 && lgm::decode_rows_supported(act, cache, d.head_dim, d.num_kv_heads, G, d.block_size)) {
     pl.rows = true;
     pl.HG = d.num_kv_heads % 8 == 0 ? 8 : 4;
@@ -560,6 +600,22 @@ lgm_status decode_attn_impl(const char* fn, void* out, float* out_lse, const voi
     workspace_bytes = sw.bytes;
   }
   char* wsb = static_cast<char*>(workspace);
+  if (pl.fused) {
+    lgm::DecodeArgs a{out, out_lse, q, q_seq_stride, k_cache, v_cache, block_tables, context_lens, k_scale, v_scale,
+                      nullptr, nullptr, nullptr, softmax_scale, lgm::PartitionPlan{pl.ps, pl.ps}, max_context_len,
+                      pl.P, dims, flags};
+    lgm::FusedArgs f{};
+    f.chunk_steps = pl.chunk_steps;
+    f.nchunks = pl.nchunks;
+    f.rec_out = pl.rec_out_bytes ? reinterpret_cast<float*>(wsb + pl.counters_bytes) : nullptr;
+    f.rec_lse = pl.rec_lse_bytes ? reinterpret_cast<float*>(wsb + pl.counters_bytes + pl.rec_out_bytes) : nullptr;
+    f.rec_out_bytes = (int32_t)pl.rec_out_bytes;
+    f.rec_lse_bytes = (int32_t)pl.rec_lse_bytes;
+    f.arrivals = reinterpret_cast<int32_t*>(wsb) + 2;
+    const hipError_t e = lgm::launch_paged_decode_fused(a, f, cache_dtype, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(LGM_ERR_HIP, fn, "single-launch kernel launch failed: %s", hipGetErrorString(e));
+    return LGM_OK;
+  }
   if (pl.rows_parts) {
     float* part_out = pl.P > 1 ? reinterpret_cast<float*>(wsb + pl.counters_bytes) : nullptr;
     float* part_lse = pl.P > 1 ? reinterpret_cast<float*>(wsb + pl.counters_bytes + pl.part_out_bytes) : nullptr;

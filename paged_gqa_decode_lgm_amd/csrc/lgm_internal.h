@@ -153,6 +153,22 @@ hipError_t launch_paged_decode_rows(const DecodeArgs& a, const RowsArgs& r, lgm_
 bool decode_rows_supported(lgm_dtype act, lgm_dtype cache, int head_dim, int num_kv_heads, int group,
                            int block_size);
 
+// Single-launch split-K decode for small jobs (matrix-core shapes): one
+// workgroup per (sequence, kv head, partition), the last workgroup to finish
+// one of a context's partitions merges its records.  The arrival counters
+// sit in the workspace's counter slot, after the work-queue kernel's two.
+constexpr int kFusedMaxChunks = 64;   // partitions per context
+constexpr int kFusedMaxStreams = 62;  // (sequence, kv head) streams: counter words 2 .. 63 of the slot
+struct FusedArgs {
+  int32_t chunk_steps;  // a partition is 4 waves x chunk_steps x 32 tokens (chunk_steps <= 32)
+  int32_t nchunks;      // partitions per context at max_context_len; grid B * Hkv * nchunks
+  float* rec_out;       // [B * Hkv][nchunks][G][D] normalised partial outputs
+  float* rec_lse;       // [B * Hkv][nchunks][G] natural-log LSEs
+  int32_t rec_out_bytes, rec_lse_bytes;
+  int32_t* arrivals;    // [B * Hkv] zero on entry, left zero on completion
+};
+hipError_t launch_paged_decode_fused(const DecodeArgs& a, const FusedArgs& f, lgm_dtype cache, hipStream_t s);
+
 // Upper bound on the persistent matrix-core kernel's workgroups per compute
 // unit (the grid is compute units x min(this, resident capacity)).
 #ifndef LGM_PERSISTENT_MAX_PER_CU

@@ -428,6 +428,29 @@ struct StepRegs {
   typename C::VBlock v[NB];
 };
 
+// Every step issues the same loads: an absent block's loads return zeros
+// without touching memory (block_rsrc) and the step masks it, so the load
+// count per step is fixed and the compiler can wait for K without waiting
+// for V.
+template <class C, int NB>
+__device__ __forceinline__ void load_step_k(const DecodeArgs& p, int g, const int (&id)[NB], int lane,
+                                            StepRegs<C, NB>& sr) {
+  const KVLayout L = kv_layout<C>(p.flags, p.dims.num_kv_heads);
+  const int off = C::k_lane_off(L, g, lane & 15, lane >> 4);
+  const int soff = C::k_scale_off(L, g, lane & 15, lane >> 4);
+#pragma unroll
+  for (int b = 0; b < NB; ++b) C::load_k(sr.k[b], block_rsrc(p.k_cache, L.block, id[b]), off, L, soff);
+}
+template <class C, int NB>
+__device__ __forceinline__ void load_step_v(const DecodeArgs& p, int g, const int (&id)[NB], int lane,
+                                            StepRegs<C, NB>& sr) {
+  const KVLayout L = kv_layout<C>(p.flags, p.dims.num_kv_heads);
+  const int off = C::v_lane_off(L, g, lane & 15, lane >> 4);
+  const int soff = C::v_scale_off(L, g, lane & 15, lane >> 4);
+#pragma unroll
+  for (int b = 0; b < NB; ++b) C::load_v(sr.v[b], block_rsrc(p.v_cache, L.block, id[b]), off, L, soff);
+}
+
 // Raw scores of a step: s[b][j] = <q_n, K[token 4kg + j of block b]>.
 template <class C, int NB>
 __device__ __forceinline__ void step_scores(const StepRegs<C, NB>& r, const short8 (&qb)[4], float4v (&s)[NB]) {

@@ -169,29 +169,6 @@ __device__ __forceinline__ int preload_ids(const DecodeArgs& p, const Item& it, 
   return (t < it.nsteps && lb < lb_end && (unsigned)id < (unsigned)p.dims.num_blocks) ? id : -1;
 }
 
-// Every step issues the same loads: an absent block's loads return zeros
-// without touching memory (block_rsrc) and the step masks it, so the load
-// count per step is fixed and the compiler can wait for K without waiting
-// for V.
-template <class C, int NB>
-__device__ __forceinline__ void load_step_k(const DecodeArgs& p, int g, const int (&id)[NB], int lane,
-                                            StepRegs<C, NB>& sr) {
-  const KVLayout L = kv_layout<C>(p.flags, p.dims.num_kv_heads);
-  const int off = C::k_lane_off(L, g, lane & 15, lane >> 4);
-  const int soff = C::k_scale_off(L, g, lane & 15, lane >> 4);
-#pragma unroll
-  for (int b = 0; b < NB; ++b) C::load_k(sr.k[b], block_rsrc(p.k_cache, L.block, id[b]), off, L, soff);
-}
-template <class C, int NB>
-__device__ __forceinline__ void load_step_v(const DecodeArgs& p, int g, const int (&id)[NB], int lane,
-                                            StepRegs<C, NB>& sr) {
-  const KVLayout L = kv_layout<C>(p.flags, p.dims.num_kv_heads);
-  const int off = C::v_lane_off(L, g, lane & 15, lane >> 4);
-  const int soff = C::v_scale_off(L, g, lane & 15, lane >> 4);
-#pragma unroll
-  for (int b = 0; b < NB; ++b) C::load_v(sr.v[b], block_rsrc(p.v_cache, L.block, id[b]), off, L, soff);
-}
-
 // Starts an item for this wave: the query operand (with the score scale's
 // sign folded in; the positive scale is returned), the block ids of its first
 // steps and the K/V loads of its first step are issued here, so that they are

@@ -255,7 +255,13 @@ def test_attention_static_empty_batch_is_a_noop():
     (dims(num_q_heads=16, num_kv_heads=2), 8192, 0, 512),                 # work queue: >= 2048 items
     (dims(num_q_heads=24, num_kv_heads=6), 8192, 0, 1024),
     (dims(num_seqs=256, num_q_heads=16, num_kv_heads=2), 8192, 0, 2048),
-    (dims(num_seqs=2, num_q_heads=12, num_kv_heads=2, max_blocks_per_seq=128), 2048, 0, 64),
+    # single launch (<= 62 streams, <= 2048 tiles): partitions for ~256 workgroups, whole 128-token steps
+    (dims(num_seqs=2, num_q_heads=12, num_kv_heads=2, max_blocks_per_seq=128), 2048, 0, 128),
+    (dims(num_seqs=1, max_blocks_per_seq=512), 8192, 0, 256),             # 8 streams x 256 tiles
+    (dims(num_seqs=1, num_q_heads=4, num_kv_heads=1, max_blocks_per_seq=4096), 65536, 0, 1024),  # <= 64 per context
+    (dims(num_seqs=62, num_q_heads=16, num_kv_heads=1, max_blocks_per_seq=8), 100, 0, 128),
+    (dims(num_seqs=63, num_q_heads=16, num_kv_heads=1, max_blocks_per_seq=8), 100, 0, 64),  # 63 streams: work queue
+    (dims(num_seqs=1, max_blocks_per_seq=528), 8448, 0, 0),               # 2112 tiles: whole-row ranges
     (dims(head_dim=64), 8192, 0, 512),                                    # vector-ALU shape
     (dims(num_seqs=2, num_q_heads=12, num_kv_heads=2, head_dim=64, max_blocks_per_seq=128), 2048, 0, 64),
     (dims(num_seqs=4, max_blocks_per_seq=8192), 131072, 512, 512),         # explicit
@@ -326,10 +332,22 @@ def test_row_plan_workspace_formula():
     assert L.lgm_paged_decode_workspace_size(d, 8192, 0, L.LGM_BF16) == want
     assert L.lgm_paged_decode_workspace_size(d, 8192, 0, L.LGM_FP8_E4M3) == want
     assert L.lgm_paged_decode_workspace_size(d, 8192, 0, L.LGM_FP4_E2M1) == want
-    small = dims(num_seqs=2, num_q_heads=16, num_kv_heads=4, max_blocks_per_seq=8)  # 2 x 4 tiles: one range
-    W, rows = 1, 4 * 4
+    # 64 (sequence, kv head) streams, too many for the single-launch plan: 16 head groups x 4 tiles, 8 ranges
+    small = dims(num_seqs=16, num_q_heads=16, num_kv_heads=4, max_blocks_per_seq=8)
+    W, rows = 8, 4 * 4
     assert L.lgm_paged_decode_workspace_size(small, 100, 0, L.LGM_BF16) == (
-        256 + al(W * 2 * rows * 128 * 4) + al(W * 2 * rows * 4) + 2 * al(2 * 4))
+        256 + al(W * 2 * rows * 128 * 4) + al(W * 2 * rows * 4) + 2 * al(16 * 4))
+
+
+def test_single_launch_workspace_formula():
+    """The counter slot (its words 2.. are the arrival counters), then one
+    record per (stream, partition): G fp32 rows of D, then G LSEs."""
+    al = lambda x: (x + 255) // 256 * 256
+    c2 = dims(num_seqs=2, num_q_heads=12, num_kv_heads=2, max_blocks_per_seq=128)  # 4 streams x 16 partitions
+    for cache in (L.LGM_BF16, L.LGM_FP8_E4M3, L.LGM_FP4_E2M1):
+        assert L.lgm_paged_decode_workspace_size(c2, 2048, 0, cache) == 256 + al(4 * 16 * 6 * 128 * 4) + al(4 * 16 * 6 * 4)
+    assert L.lgm_paged_decode_workspace_size(c2, 100, 0, L.LGM_BF16) == 256    # one partition: no records
+    assert L.lgm_paged_decode_workspace_size(c2, 0, 0, L.LGM_BF16) == 256
 
 
 def test_too_many_partitions_is_unsupported():

@@ -404,11 +404,101 @@ def test_many_short_sequences_and_empty_ones(ps):
 @pytest.mark.parametrize("hkv,G", [(4, 1), (4, 4), (8, 4), (8, 5), (16, 2), (8, 16)])
 def test_row_plan_ragged_edges(cache, hkv, G):
     """Whole-row ranges (partition_size 0, kv heads divisible by 4): head
-    groups of 4 and 8, empty and one-token contexts, block and tile edges."""
-    cfg = W.Config(f"rows_{cache}_H{hkv}_G{G}", seed=12, num_seqs=len(EDGE_CTX), num_q_heads=hkv * G,
+    groups of 4 and 8, empty and one-token contexts, block and tile edges.
+    The edge contexts twice over: at least 80 (sequence, kv head) streams,
+    past the single-launch plan's 62."""
+    ctx = EDGE_CTX * 2
+    cfg = W.Config(f"rows_{cache}_H{hkv}_G{G}", seed=12, num_seqs=len(ctx), num_q_heads=hkv * G,
                    num_kv_heads=hkv, head_dim=128, block_size=16, act="bf16", cache=cache, ctx=0, rope_theta=1e4,
-                   partition_size=0, append=True, ctx_list=EDGE_CTX)
+                   partition_size=0, append=True, ctx_list=ctx)
+    assert len(ctx) * hkv > 62
     _run_and_check(cfg)
+
+
+# ------------------------------------------------------------------ single-launch plan
+# partition_size 0 with at most 62 (sequence, kv head) streams and at most 2048
+# 32-token tiles over them: one launch, partitions of whole 128-token steps, the
+# last workgroup to finish one of a context's partitions merges its records.
+def _single_launch_cfg(name, cache, hkv, G, ctx, seed=16, append=True):
+    cfg = W.Config(name, seed=seed, num_seqs=len(ctx), num_q_heads=hkv * G, num_kv_heads=hkv, head_dim=128,
+                   block_size=16, act="bf16", cache=cache, ctx=0, rope_theta=1e4, partition_size=0, append=append,
+                   ctx_list=tuple(ctx))
+    streams, tiles = len(ctx) * hkv, len(ctx) * hkv * -(-max(ctx) // 32)
+    assert streams <= 62 and tiles <= 2048, (streams, tiles)
+    return cfg
+
+
+@pytest.mark.parametrize("cache", ["bf16", "fp8", "fp4"])
+@pytest.mark.parametrize("hkv,G", [(1, 16), (2, 6), (4, 1), (1, 8), (3, 5)])
+def test_single_launch_ragged_edges(cache, hkv, G):
+    """Empty, one-token, block-edge and step-edge contexts next to ones of
+    several partitions: contexts written directly (one partition) and merged
+    ones (up to 5 partitions) in one grid."""
+    ctx = EDGE_CTX + (128, 129, 640, 383)
+    _run_and_check(_single_launch_cfg(f"single_{cache}_H{hkv}_G{G}", cache, hkv, G, ctx))
+
+
+@pytest.mark.parametrize("hkv,ctx", [(1, 65536), (2, 32768), (1, 65535), (2, 20001)])
+def test_single_launch_many_partitions_and_steps(hkv, ctx):
+    """Up to 64 partitions per context (the most the plan makes), of 4 to 8
+    steps per wave: the merge reads its records in several batches."""
+    cfg = _single_launch_cfg(f"single_long_H{hkv}_{ctx}", "bf16", hkv, 8, (ctx,), seed=17, append=False)
+    _run_and_check(cfg)
+
+
+def test_single_launch_counters_left_zero_and_workspace_shared():
+    """The arrival counters (the counter slot's words 2..) come back zero
+    after every call, so calls repeat bitwise, and the work-queue plan may
+    use the same workspace in between."""
+    cfg = W.CONFIGS["qwen2.5_1.5b_gqa"].with_(num_seqs=3, ctx_list=(2048, 700, 1), num_blocks=None, append=False)
+    w = W.make_workload(cfg)
+    d = to_device(w)
+    q = q_from_qkv(w).cuda()
+    nbytes = max(ops.workspace_bytes(q, d.k_pool, d.block_tables, d.max_ctx, ps) for ps in (0, 64))
+    ws = torch.zeros((nbytes,), dtype=torch.uint8, device="cuda")
+    announce("single-launch counters", nbytes)
+    outs = []
+    for ps in (0, 0, 64, 0, 64, 0):
+        o, l = ops.paged_decode_attn(q, d.k_pool, d.v_pool, d.block_tables, d.context_lens, d.max_ctx,
+                                     softmax_scale=cfg.softmax_scale, partition_size=ps, workspace=ws)
+        torch.cuda.synchronize()
+        assert int(ws[:256].view(torch.int32).abs().sum()) == 0, ps
+        outs.append((ps, o.clone(), l.clone()))
+    ref = [x for x in outs if x[0] == 0][0]
+    for ps, o, l in outs:
+        if ps == 0:
+            assert torch.equal(o.view(torch.int16), ref[1].view(torch.int16)) and torch.equal(l, ref[2])
+    r_out, r_lse = oracle_attention(w, act_raw(w, q_from_qkv(w)), pool_raw(w, w.k_pool), pool_raw(w, w.v_pool))
+    for ps, o, l in outs:
+        assert max_abs(out_values(cfg, o), r_out) <= TOL["bf16"], ps
+        _lse_check(l.cpu().numpy(), r_lse)
+
+
+def test_single_launch_back_to_back_different_inputs():
+    """Calls with different queries, caches and context lengths on one
+    workspace, no host sync between them: each call's merges see its own
+    records and arrival counts."""
+    cfgs = [W.CONFIGS["qwen2.5_1.5b_gqa"].with_(seed=50 + i, num_seqs=2, ctx_list=c, num_blocks=None, append=False)
+            for i, c in enumerate([(2048, 2048), (1000, 2047), (129, 1920)])]
+    ws_list = [W.make_workload(c) for c in cfgs]
+    devs = [to_device(w) for w in ws_list]
+    qs = [q_from_qkv(w).cuda() for w in ws_list]
+    nbytes = max(ops.workspace_bytes(q, d.k_pool, d.block_tables, d.max_ctx, 0) for q, d in zip(qs, devs))
+    ws = torch.zeros((nbytes,), dtype=torch.uint8, device="cuda")
+    announce("single-launch back-to-back", nbytes)
+    outs = []
+    for rep in range(3):
+        for q, d, c in zip(qs, devs, cfgs):
+            outs.append(ops.paged_decode_attn(q, d.k_pool, d.v_pool, d.block_tables, d.context_lens, d.max_ctx,
+                                              softmax_scale=c.softmax_scale, partition_size=0, workspace=ws))
+    torch.cuda.synchronize()
+    assert int(ws[:256].view(torch.int32).abs().sum()) == 0
+    for i, (w, c) in enumerate(zip(ws_list, cfgs)):
+        r_out, r_lse = oracle_attention(w, act_raw(w, q_from_qkv(w)), pool_raw(w, w.k_pool), pool_raw(w, w.v_pool))
+        for rep in range(3):
+            o, l = outs[rep * len(cfgs) + i]
+            assert max_abs(out_values(c, o), r_out) <= TOL["bf16"]
+            _lse_check(l.cpu().numpy(), r_lse)
 
 
 @pytest.mark.parametrize("cache", ["bf16", "fp8", "fp4"])
