@@ -77,7 +77,11 @@
 extern "C" {
 #endif
 
-#define LGM_ABI_VERSION 6
+#define LGM_ABI_VERSION 7
+
+/* Bytes of int32 counters at the start of every nonzero attention workspace
+ * (see lgm_paged_decode_workspace_size): zero on entry, left zero. */
+#define LGM_COUNTER_SLOT_BYTES 4096u
 
 typedef enum lgm_status {
   LGM_OK = 0,
@@ -180,13 +184,21 @@ lgm_status lgm_rope_kv_append(const void* qkv, int64_t qkv_row_stride, void* q_o
  * A positive partition_size must be a multiple of block_size and is returned
  * as is (clamped to the rounded-up max_context_len).  partition_size 0 lets
  * the library choose from the shapes alone (deterministic, no device query):
- *  - matrix-core shapes (bf16 activations, bf16 / FP8 / FP4 caches, head_dim 128)
- *    with num_kv_heads divisible by 4: returns 0.  The 32-token tiles of all
+ *  - small jobs on the matrix-core shapes (bf16 activations, bf16 / FP8 /
+ *    FP4 caches, head_dim 128): at most 1022 (sequence, kv head) streams and
+ *    at most 16384 32-token tiles over them at max_context_len (32768 for
+ *    FP8 caches).  One launch: plain ceil(L / partition) partitions of a
+ *    multiple of 128 tokens (at most 64 per context, at most 1024 tokens per
+ *    wave), the size that best balances the (sequence, kv head, partition)
+ *    workgroups over 256 compute units, counting a fixed cost of 128 tokens
+ *    per workgroup; the workgroup that finishes a context's last partition
+ *    merges that context by log-sum-exp.  Returns the partition;
+ *  - other matrix-core shapes with num_kv_heads divisible by 4: returns 0.  The 32-token tiles of all
  *    contexts (per group of 8, or 4, kv heads) are cut into equal ranges, one
- *    per compute unit (256, fewer when a range would hold under 8 tiles);
+ *    per compute unit (256, fewer when a range would hold under 2 tiles);
  *    each workgroup reads whole KV rows of its head group, and contexts split
  *    between ranges are merged by log-sum-exp;
- *  - other matrix-core shapes: the largest power of two from 64 to 4096
+ *  - the remaining matrix-core shapes: the largest power of two from 64 to 4096
  *    tokens that still gives 2048 (sequence, partition, kv head) work items
  *    at max_context_len;
  *  - other shapes: a size that gives about 8192 workgroups.
@@ -210,10 +222,14 @@ int32_t lgm_paged_decode_partition_size(lgm_paged_dims dims, int32_t max_context
 /*
  * Bytes of device workspace lgm_paged_decode_attn needs for these
  * arguments, 0 when the plan needs none.  A nonzero workspace always starts
- * with the same 256-byte slot: two int32 work counters that only the
- * work-queue plan uses (it needs them zero on entry and leaves them zero);
- * no other plan reads or writes that slot.  After it come the plan's own
+ * with the same slot of LGM_COUNTER_SLOT_BYTES (1024 int32 counters), which
+ * must be zero on entry and which every plan leaves zero: the work-queue plan
+ * uses words 0 and 1, the single-launch plan one arrival counter per
+ * (sequence, kv head) stream from word 2 on, the other plans none.  After it come the plan's own
  * regions, each 256-byte aligned:
+ *  - single launch (small jobs, see lgm_paged_decode_partition_size): when
+ *    contexts are split, one record per (sequence, kv head, partition):
+ *    fp32 outputs [B * Hkv][P][G][D], then natural-log LSEs [B * Hkv][P][G];
  *  - equal ranges (see lgm_paged_decode_partition_size): two records per
  *    range (fp32 outputs of the head group's Hq * 8 / Hkv or Hq * 4 / Hkv
  *    query heads, D each, and their natural-log LSEs), then int32 context
@@ -243,9 +259,11 @@ size_t lgm_paged_decode_workspace_size(lgm_paged_dims dims, int32_t max_context_
  * cut into partitions (see lgm_paged_decode_partition_size) processed in
  * parallel; partial results are merged by log-sum-exp (as lgm_lse_merge) on
  * the same stream, within this call.  A sequence that fits one partition is
- * written directly.  The matrix-core kernel runs as many workgroups as the
- * device keeps resident, each taking (sequence, partition, kv head) items
- * from the workspace's work counters until none is left.
+ * written directly.  Small jobs take one launch, whose workgroups merge the
+ * contexts they finish; the whole-row plan cuts equal tile ranges; the
+ * work-queue plan runs as many workgroups as the device keeps resident, each
+ * taking (sequence, partition, kv head) items from the workspace's work
+ * counters until none is left.
  *
  *   out            [B][Hq][D] act dtype (dense)
  *   out_lse        optional fp32 [B][Hq] (NULL = not written)
@@ -260,7 +278,7 @@ size_t lgm_paged_decode_workspace_size(lgm_paged_dims dims, int32_t max_context_
  *   max_context_len upper bound on context_lens, 0..max_blocks_per_seq*block_size
  *   workspace      device buffer of at least lgm_paged_decode_workspace_size()
  *                  bytes, 256-byte aligned (NULL allowed when that size is 0).
- *                  Its first 256 bytes (the work counters) must be zero
+ *                  Its first LGM_COUNTER_SLOT_BYTES (the counters) must be zero
  *                  before the first call on it; every completed call, on any
  *                  plan, leaves them zero, so one buffer may serve calls with
  *                  different shapes and plans in turn.  Zero-fill it again

@@ -181,13 +181,15 @@ int32_t resolve_partition(const char* fn, const lgm_paged_dims& d, int32_t max_c
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
-constexpr size_t kCounterSlot = 256;  // the work-queue counters at the start of every workspace
+constexpr size_t kCounterSlot = LGM_COUNTER_SLOT_BYTES;  // the counters at the start of every workspace
 
 // Launch plan of one attention call, a function of host-visible arguments only.
 // Every plan that needs a workspace lays it out the same way at the start:
-// a 256-byte slot holding the work-queue kernel's two counters, which only
-// that kernel writes (it leaves them zero), then the plan's own regions.  So
-// one zero-filled workspace may serve calls on any plan in turn.
+// the counter slot (LGM_COUNTER_SLOT_BYTES): the work-queue kernel's two
+// counters, then the single-launch kernel's arrival counters, one per
+// (sequence, kv head) stream.  Each kernel leaves the counters it uses zero,
+// and no plan puts anything else there, so one zero-filled workspace may
+// serve calls on any plan in turn.  The plan's own regions follow.
 struct Plan {
   bool fused;       // single-launch split kernel (small jobs): partitions of ps tokens, merged in the launch
   bool rows;        // whole-row kernel (Hkv % 4 == 0): equal tile ranges (partition_size 0) ...
@@ -208,7 +210,10 @@ struct Plan {
 #define LGM_ROWS_WORKGROUPS 256
 #endif
 constexpr int64_t kRowsWorkgroups = LGM_ROWS_WORKGROUPS;
-constexpr int64_t kRowsMinTiles = 8;
+#ifndef LGM_ROWS_MIN_TILES
+#define LGM_ROWS_MIN_TILES 2
+#endif
+constexpr int64_t kRowsMinTiles = LGM_ROWS_MIN_TILES;
 constexpr int64_t kRowsTile = 32;
 // Whole-row partition plan: explicit partition sizes of at least this many
 // tokens (and whole 32-token tiles), when the longest context holds at least
@@ -225,18 +230,54 @@ constexpr int32_t kRowsMinPartition = LGM_ROWS_MIN_PARTITION;
 constexpr int32_t kRowsMinPartitions = 64;
 
 // Single-launch split plan: taken with partition_size 0 on the matrix-core
-// shapes when the job is small, at most kFusedMaxStreams (sequence, kv head)
-// streams and kFusedMaxTiles 32-token tiles over them at max_context_len.
-// Such a job takes a few microseconds of memory traffic, and a separate
-// merge launch would cost as much again.  Partitions are whole steps of the
-// four waves (128 tokens), sized for about kFusedTargetWorkgroups
-// workgroups and at most kFusedMaxChunks per context.
+// shapes when the job is small or middling: at most kFusedMaxStreams
+// (sequence, kv head) streams and at most kFusedMaxTiles 32-token tiles over
+// them at max_context_len (twice that for FP8 caches, whose tiles are half
+// the bytes).  Measured on MI355X (uniform contexts, partition_size 0, call
+// times): the whole-row and work-queue plans pay a fixed cost that dominates
+// such jobs (8 x 8 kv heads x 2048 tokens: 15.5 us single launch against 26.5
+// us whole-row; 128 x 2 x 2048: 41.8 against 57.0 us work queue), while from
+// about 28672 bf16 tiles the whole-row plan streams faster (7 x 8 x 16384:
+// 86 against 93 us; 32 x 8 x 8192: 172 against 192 us; FP8 64 x 8 x 4096:
+// 99 against 109 us).
 #ifndef LGM_FUSED_MAX_TILES
-#define LGM_FUSED_MAX_TILES 2048
+#define LGM_FUSED_MAX_TILES 16384
 #endif
 constexpr int64_t kFusedMaxTiles = LGM_FUSED_MAX_TILES;
-constexpr int64_t kFusedTargetWorkgroups = 256;
+#ifndef LGM_FUSED_TARGET_WORKGROUPS
+#define LGM_FUSED_TARGET_WORKGROUPS 256
+#endif
+constexpr int64_t kFusedTargetWorkgroups = LGM_FUSED_TARGET_WORKGROUPS;
 constexpr int64_t kFusedPartStep = 128;
+constexpr int64_t kFusedMaxSteps = 32;  // 32-token steps per wave in one partition
+#ifndef LGM_FUSED_WG_OVERHEAD
+#define LGM_FUSED_WG_OVERHEAD 128
+#endif
+constexpr int64_t kFusedWorkgroupOverhead = LGM_FUSED_WG_OVERHEAD;  // tokens' worth of fixed latency per workgroup
+
+// Partition of the single-launch plan: over 1..kFusedMaxChunks partitions per
+// context (whole 128-token steps, at most kFusedMaxSteps per wave), the one
+// whose slowest compute unit has the least to read when the
+// streams * partitions workgroups are spread kFusedTargetWorkgroups at a
+// time: rounds * partition tokens.  Ties go to fewer partitions (fewer
+// records to merge).  0 if no partition fits.
+int64_t fused_partition(int64_t streams, int64_t max_ctx) {
+  int64_t best = 0, best_cost = 0;
+  for (int64_t n = 1; n <= lgm::kFusedMaxChunks; ++n) {
+    int64_t part = (max_ctx + n - 1) / n;
+    part = (part + kFusedPartStep - 1) / kFusedPartStep * kFusedPartStep;
+    part = part < kFusedPartStep ? kFusedPartStep : part;
+    if (part / kFusedPartStep > kFusedMaxSteps) continue;
+    const int64_t used = (max_ctx + part - 1) / part;
+    const int64_t rounds = (streams * (used < 1 ? 1 : used) + kFusedTargetWorkgroups - 1) / kFusedTargetWorkgroups;
+    const int64_t cost = rounds * (part + kFusedWorkgroupOverhead);
+    if (best == 0 || cost < best_cost) {
+      best = part;
+      best_cost = cost;
+    }
+  }
+  return best;
+}
 
 lgm_status plan_decode(const char* fn, const lgm_paged_dims& d, int32_t max_ctx, int32_t ps_arg, lgm_dtype cache,
                        Plan& pl) {
@@ -247,12 +288,9 @@ lgm_status plan_decode(const char* fn, const lgm_paged_dims& d, int32_t max_ctx,
   if (ps_arg == 0 && persistent) {
     const int64_t streams = (int64_t)d.num_seqs * d.num_kv_heads;
     const int64_t tiles = streams * (((int64_t)max_ctx + kRowsTile - 1) / kRowsTile);
-    int64_t part = (streams * max_ctx + kFusedTargetWorkgroups - 1) / kFusedTargetWorkgroups;
-    const int64_t least = ((int64_t)max_ctx + lgm::kFusedMaxChunks - 1) / lgm::kFusedMaxChunks;
-    part = part > least ? part : least;
-    part = (part + kFusedPartStep - 1) / kFusedPartStep * kFusedPartStep;
-    part = part < kFusedPartStep ? kFusedPartStep : part;
-    if (streams <= lgm::kFusedMaxStreams && tiles <= kFusedMaxTiles && part / kFusedPartStep <= 32) {
+    const int64_t max_tiles = cache == LGM_FP8_E4M3 ? 2 * kFusedMaxTiles : kFusedMaxTiles;
+    const int64_t part = streams <= lgm::kFusedMaxStreams && tiles <= max_tiles ? fused_partition(streams, max_ctx) : 0;
+    if (part > 0) {
       pl.fused = true;
       pl.ps = (int32_t)part;
       pl.chunk_steps = (int32_t)(part / kFusedPartStep);
@@ -716,7 +754,9 @@ lgm_status resolve_scratch(const char* fn, hipStream_t stream, StaticWorkspace& 
     slot.err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
     if (slot.err == hipSuccess) {
       slot.ptr = p;
-      hipLaunchKernelGGL(zero_words_kernel, dim3(1), dim3(64), 0, stream, static_cast<uint32_t*>(p), 64);
+      constexpr int kWords = (int)(kCounterSlot / 4);
+      hipLaunchKernelGGL(zero_words_kernel, dim3((kWords + 255) / 256), dim3(256), 0, stream,
+                         static_cast<uint32_t*>(p), kWords);
       slot.err = hipGetLastError();
     }
     if (cur != dev) {

@@ -158,7 +158,7 @@ bool decode_rows_supported(lgm_dtype act, lgm_dtype cache, int head_dim, int num
 // one of a context's partitions merges its records.  The arrival counters
 // sit in the workspace's counter slot, after the work-queue kernel's two.
 constexpr int kFusedMaxChunks = 64;   // partitions per context
-constexpr int kFusedMaxStreams = 62;  // (sequence, kv head) streams: counter words 2 .. 63 of the slot
+constexpr int kFusedMaxStreams = (int)(LGM_COUNTER_SLOT_BYTES / 4) - 2;  // arrival counters: slot words 2 ..
 struct FusedArgs {
   int32_t chunk_steps;  // a partition is 4 waves x chunk_steps x 32 tokens (chunk_steps <= 32)
   int32_t nchunks;      // partitions per context at max_context_len; grid B * Hkv * nchunks

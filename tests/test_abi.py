@@ -18,6 +18,16 @@ def addr(i):
     return A * (i + 1)
 
 
+SLOT = 4096  # LGM_COUNTER_SLOT_BYTES: the counters at the start of every nonzero attention workspace
+
+
+def test_counter_slot_constant():
+    import re
+    from pathlib import Path
+    text = (Path(L.__file__).resolve().parents[1] / "include" / "lgm.h").read_text()
+    assert int(re.search(r"#define\s+LGM_COUNTER_SLOT_BYTES\s+(\d+)u", text).group(1)) == SLOT
+
+
 def dims(**kw):
     d = dict(num_seqs=64, num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16, num_blocks=1000,
              max_blocks_per_seq=512)
@@ -35,7 +45,7 @@ def test_library_loads_and_exports_every_header_function():
                           "lgm_paged_mla_workspace_size", "lgm_paged_mla_decode"}
     for n in names:
         assert hasattr(lib, n), n
-    assert L.lgm_abi_version() == 6
+    assert L.lgm_abi_version() == 7
 
 
 def test_build_entry_abi_check_matches_header():
@@ -255,13 +265,14 @@ def test_attention_static_empty_batch_is_a_noop():
     (dims(num_q_heads=16, num_kv_heads=2), 8192, 0, 512),                 # work queue: >= 2048 items
     (dims(num_q_heads=24, num_kv_heads=6), 8192, 0, 1024),
     (dims(num_seqs=256, num_q_heads=16, num_kv_heads=2), 8192, 0, 2048),
-    # single launch (<= 62 streams, <= 2048 tiles): partitions for ~256 workgroups, whole 128-token steps
+    # single launch (<= 1022 streams, <= 16384 tiles): partitions that balance the workgroups, 128-token steps
     (dims(num_seqs=2, num_q_heads=12, num_kv_heads=2, max_blocks_per_seq=128), 2048, 0, 128),
     (dims(num_seqs=1, max_blocks_per_seq=512), 8192, 0, 256),             # 8 streams x 256 tiles
     (dims(num_seqs=1, num_q_heads=4, num_kv_heads=1, max_blocks_per_seq=4096), 65536, 0, 1024),  # <= 64 per context
-    (dims(num_seqs=62, num_q_heads=16, num_kv_heads=1, max_blocks_per_seq=8), 100, 0, 128),
-    (dims(num_seqs=63, num_q_heads=16, num_kv_heads=1, max_blocks_per_seq=8), 100, 0, 64),  # 63 streams: work queue
-    (dims(num_seqs=1, max_blocks_per_seq=528), 8448, 0, 0),               # 2112 tiles: whole-row ranges
+    (dims(num_seqs=1022, num_q_heads=16, num_kv_heads=1, max_blocks_per_seq=8), 100, 0, 128),
+    (dims(num_seqs=1023, num_q_heads=16, num_kv_heads=1, max_blocks_per_seq=8), 100, 0, 64),  # 1023 streams: work queue
+    (dims(num_seqs=1, max_blocks_per_seq=4096), 65536, 0, 2048),          # 8 x 2048 = 16384 tiles
+    (dims(num_seqs=1, max_blocks_per_seq=4098), 65537, 0, 0),             # 8 x 2049 tiles: whole-row ranges
     (dims(head_dim=64), 8192, 0, 512),                                    # vector-ALU shape
     (dims(num_seqs=2, num_q_heads=12, num_kv_heads=2, head_dim=64, max_blocks_per_seq=128), 2048, 0, 64),
     (dims(num_seqs=4, max_blocks_per_seq=8192), 131072, 512, 512),         # explicit
@@ -271,6 +282,12 @@ def test_attention_static_empty_batch_is_a_noop():
 ])
 def test_partition_plan(d, max_ctx, ps, want):
     assert L.lgm_paged_decode_partition_size(d, max_ctx, ps, L.LGM_BF16) == want
+
+
+@pytest.mark.parametrize("cache,want", [(L.LGM_BF16, 0), (L.LGM_FP4_E2M1, 0), (L.LGM_FP8_E4M3, 4096)])
+def test_single_launch_tile_cap_by_cache(cache, want):
+    """8 streams x 4096 tiles = 32768: within the FP8 cap (half the bytes per tile) only."""
+    assert L.lgm_paged_decode_partition_size(dims(num_seqs=1, max_blocks_per_seq=8192), 131072, 0, cache) == want
 
 
 def partitions_brute_force(max_ctx, ps, tps):
@@ -285,28 +302,28 @@ def test_workspace_size_formula():
     # longest context and >= 256 units in the batch; plain ceil(L / ps) partitions after the counter slot
     long = dims(num_seqs=4, max_blocks_per_seq=8192)
     assert L.lgm_paged_decode_workspace_size(long, 131072, 512, L.LGM_BF16) == (
-        256 + al(4 * 32 * 256 * 128 * 4) + al(4 * 32 * 256 * 4))
+        SLOT + al(4 * 32 * 256 * 128 * 4) + al(4 * 32 * 256 * 4))
     assert L.lgm_paged_decode_workspace_size(long, 131072, 2048, L.LGM_FP8_E4M3) == (
-        256 + al(4 * 32 * 64 * 128 * 4) + al(4 * 32 * 64 * 4))
+        SLOT + al(4 * 32 * 64 * 128 * 4) + al(4 * 32 * 64 * 4))
     d = dims()                                     # 16 partitions at the longest context: work-queue kernel
-    assert L.lgm_paged_decode_workspace_size(d, 8192, 8192, L.LGM_BF16) == 256     # one partition
-    assert L.lgm_paged_decode_workspace_size(d, 8192, 8192, L.LGM_FP8_E4M3) == 256
+    assert L.lgm_paged_decode_workspace_size(d, 8192, 8192, L.LGM_BF16) == SLOT    # one partition
+    assert L.lgm_paged_decode_workspace_size(d, 8192, 8192, L.LGM_FP8_E4M3) == SLOT
     d2 = dims(num_q_heads=16, num_kv_heads=2)      # work-queue shape: 256 bytes of work counters first
-    assert L.lgm_paged_decode_workspace_size(d2, 8192, 8192, L.LGM_BF16) == 256    # one partition
+    assert L.lgm_paged_decode_workspace_size(d2, 8192, 8192, L.LGM_BF16) == SLOT    # one partition
     P = partitions_brute_force(8192, 512, 256)     # tails in half partitions
     assert P == 17
     out_b = 64 * 16 * P * 128 * 4
     lse_b = 64 * 16 * P * 4
-    assert L.lgm_paged_decode_workspace_size(d2, 8192, 512, L.LGM_BF16) == 256 + al(out_b) + al(lse_b)
+    assert L.lgm_paged_decode_workspace_size(d2, 8192, 512, L.LGM_BF16) == SLOT + al(out_b) + al(lse_b)
     # below the whole-row partition minimum: the work-queue kernel, tails included
     P64 = partitions_brute_force(8192, 64, 32)
     assert L.lgm_paged_decode_workspace_size(d, 8192, 64, L.LGM_BF16) == (
-        256 + al(64 * 32 * P64 * 128 * 4) + al(64 * 32 * P64 * 4))
+        SLOT + al(64 * 32 * P64 * 128 * 4) + al(64 * 32 * P64 * 4))
     lse_b = 64 * 32 * P * 4
     v = dims(head_dim=64)                          # vector-ALU shape: the counter slot, then the partials
     assert L.lgm_paged_decode_workspace_size(v, 8192, 8192, L.LGM_BF16) == 0
     assert L.lgm_paged_decode_workspace_size(v, 8192, 512, L.LGM_BF16) == (
-        256 + al(64 * 32 * P * 64 * 4) + al(lse_b))
+        SLOT + al(64 * 32 * P * 64 * 4) + al(lse_b))
 
 
 @pytest.mark.parametrize("max_ctx,ps", [(100, 16), (100, 64), (1000, 96), (3000, 512), (4096, 1024), (17, 16),
@@ -317,7 +334,7 @@ def test_partition_count_bound(max_ctx, ps):
     P = partitions_brute_force(max_ctx, ps, tps)
     d = dims(head_dim=64, max_blocks_per_seq=(max_ctx + 15) // 16)
     al = lambda x: (x + 255) // 256 * 256
-    want = 0 if P == 1 else 256 + al(64 * 32 * P * 64 * 4) + al(64 * 32 * P * 4)
+    want = 0 if P == 1 else SLOT + al(64 * 32 * P * 64 * 4) + al(64 * 32 * P * 4)
     assert L.lgm_paged_decode_workspace_size(d, max_ctx, ps, L.LGM_BF16) == want
     assert L.lgm_last_error() == ""
     with pytest.raises(L.LgmError):
@@ -328,15 +345,20 @@ def test_row_plan_workspace_formula():
     al = lambda x: (x + 255) // 256 * 256
     d = dims()                                     # 8 kv heads per workgroup, 64 streams of 256 tiles
     W, rows = 256, 8 * 4
-    want = 256 + al(W * 2 * rows * 128 * 4) + al(W * 2 * rows * 4) + 2 * al(64 * 4)
+    want = SLOT + al(W * 2 * rows * 128 * 4) + al(W * 2 * rows * 4) + 2 * al(64 * 4)
     assert L.lgm_paged_decode_workspace_size(d, 8192, 0, L.LGM_BF16) == want
     assert L.lgm_paged_decode_workspace_size(d, 8192, 0, L.LGM_FP8_E4M3) == want
     assert L.lgm_paged_decode_workspace_size(d, 8192, 0, L.LGM_FP4_E2M1) == want
-    # 64 (sequence, kv head) streams, too many for the single-launch plan: 16 head groups x 4 tiles, 8 ranges
-    small = dims(num_seqs=16, num_q_heads=16, num_kv_heads=4, max_blocks_per_seq=8)
-    W, rows = 8, 4 * 4
-    assert L.lgm_paged_decode_workspace_size(small, 100, 0, L.LGM_BF16) == (
-        256 + al(W * 2 * rows * 128 * 4) + al(W * 2 * rows * 4) + 2 * al(16 * 4))
+    # 8 streams x 4096 tiles, past the single-launch cap: 2 head groups of 4 x 4096 tiles, two a range
+    long = dims(num_seqs=2, num_q_heads=16, num_kv_heads=4, max_blocks_per_seq=8192)
+    W, rows = 256, 4 * 4
+    assert L.lgm_paged_decode_workspace_size(long, 131072, 0, L.LGM_BF16) == (
+        SLOT + al(W * 2 * rows * 128 * 4) + al(W * 2 * rows * 4) + 2 * al(2 * 4))
+    few = dims(num_seqs=1100, num_q_heads=16, num_kv_heads=4, max_blocks_per_seq=1)  # 4400 streams of one tile
+    W = 1100 // 2
+    W = 256 if W > 256 else W
+    assert L.lgm_paged_decode_workspace_size(few, 16, 0, L.LGM_BF16) == (
+        SLOT + al(W * 2 * rows * 128 * 4) + al(W * 2 * rows * 4) + 2 * al(1100 * 4))
 
 
 def test_single_launch_workspace_formula():
@@ -345,9 +367,9 @@ def test_single_launch_workspace_formula():
     al = lambda x: (x + 255) // 256 * 256
     c2 = dims(num_seqs=2, num_q_heads=12, num_kv_heads=2, max_blocks_per_seq=128)  # 4 streams x 16 partitions
     for cache in (L.LGM_BF16, L.LGM_FP8_E4M3, L.LGM_FP4_E2M1):
-        assert L.lgm_paged_decode_workspace_size(c2, 2048, 0, cache) == 256 + al(4 * 16 * 6 * 128 * 4) + al(4 * 16 * 6 * 4)
-    assert L.lgm_paged_decode_workspace_size(c2, 100, 0, L.LGM_BF16) == 256    # one partition: no records
-    assert L.lgm_paged_decode_workspace_size(c2, 0, 0, L.LGM_BF16) == 256
+        assert L.lgm_paged_decode_workspace_size(c2, 2048, 0, cache) == SLOT + al(4 * 16 * 6 * 128 * 4) + al(4 * 16 * 6 * 4)
+    assert L.lgm_paged_decode_workspace_size(c2, 100, 0, L.LGM_BF16) == SLOT    # one partition: no records
+    assert L.lgm_paged_decode_workspace_size(c2, 0, 0, L.LGM_BF16) == SLOT
 
 
 def test_too_many_partitions_is_unsupported():

@@ -353,7 +353,7 @@ def test_persistent_workspace_is_reusable_and_left_zeroed(name, ps):
     torch.cuda.synchronize()
     for o, l in outs[1:]:
         assert torch.equal(o.view(torch.int16), outs[0][0].view(torch.int16)) and torch.equal(l, outs[0][1])
-    assert int(ws[:256].view(torch.int32).abs().sum()) == 0
+    assert int(ws[:4096].view(torch.int32).abs().sum()) == 0
     r_out, r_lse = oracle_attention(w, act_raw(w, q_from_qkv(w)), pool_raw(w, w.k_pool), pool_raw(w, w.v_pool))
     assert max_abs(out_values(cfg, outs[0][0]), r_out) <= TOL["bf16"]
     _lse_check(outs[0][1].cpu().numpy(), r_lse)
@@ -363,9 +363,11 @@ def test_persistent_workspace_is_reusable_and_left_zeroed(name, ps):
 def test_one_workspace_serves_every_plan(name):
     """One zero-filled workspace shared by calls on different plans in turn:
     equal ranges (partition_size 0), the whole-row partition plan, the work
-    queue (partitions of 64) and equal ranges again.  No plan but the work
-    queue touches the counter slot at its start, and the work queue leaves it
-    zero, so every call matches the oracle and the slot ends at zero."""
+    queue (partitions of 64) and equal ranges again.  Of these plans only
+    the work queue touches the counter slot at its start, and it leaves the
+    slot zero, so every call matches the oracle and the slot ends at zero
+    (the single-launch plan, which also counts there, is covered with the
+    work queue below)."""
     cfg = W.CONFIGS[name].with_(num_seqs=12, ctx=(1, 20000), num_blocks=None, append=False)
     w = W.make_workload(cfg)
     d = to_device(w)
@@ -382,7 +384,7 @@ def test_one_workspace_serves_every_plan(name):
                                      softmax_scale=cfg.softmax_scale, partition_size=ps, k_scale=d.k_scale,
                                      v_scale=d.v_scale, workspace=ws)
         torch.cuda.synchronize()
-        assert int(ws[:256].view(torch.int32).abs().sum()) == 0, ps
+        assert int(ws[:4096].view(torch.int32).abs().sum()) == 0, ps
         assert max_abs(out_values(cfg, o), r_out) <= TOL["bf16"], ps
         _lse_check(l.cpu().numpy(), r_lse)
 
@@ -405,26 +407,27 @@ def test_many_short_sequences_and_empty_ones(ps):
 def test_row_plan_ragged_edges(cache, hkv, G):
     """Whole-row ranges (partition_size 0, kv heads divisible by 4): head
     groups of 4 and 8, empty and one-token contexts, block and tile edges.
-    The edge contexts twice over: at least 80 (sequence, kv head) streams,
-    past the single-launch plan's 62."""
-    ctx = EDGE_CTX * 2
+    The edge contexts twice over and one 16384-token context: past the
+    single-launch plan's tile cap (16384 tiles, 32768 for FP8)."""
+    ctx = EDGE_CTX * 2 + (16384,)
     cfg = W.Config(f"rows_{cache}_H{hkv}_G{G}", seed=12, num_seqs=len(ctx), num_q_heads=hkv * G,
                    num_kv_heads=hkv, head_dim=128, block_size=16, act="bf16", cache=cache, ctx=0, rope_theta=1e4,
                    partition_size=0, append=True, ctx_list=ctx)
-    assert len(ctx) * hkv > 62
+    assert len(ctx) * hkv * 16384 // 32 > 32768
     _run_and_check(cfg)
 
 
 # ------------------------------------------------------------------ single-launch plan
-# partition_size 0 with at most 62 (sequence, kv head) streams and at most 2048
-# 32-token tiles over them: one launch, partitions of whole 128-token steps, the
-# last workgroup to finish one of a context's partitions merges its records.
+# partition_size 0 with at most 1022 (sequence, kv head) streams and at most 16384
+# 32-token tiles over them (32768 for FP8): one launch, partitions of whole
+# 128-token steps, the last workgroup to finish one of a context's partitions
+# merges its records.
 def _single_launch_cfg(name, cache, hkv, G, ctx, seed=16, append=True):
     cfg = W.Config(name, seed=seed, num_seqs=len(ctx), num_q_heads=hkv * G, num_kv_heads=hkv, head_dim=128,
                    block_size=16, act="bf16", cache=cache, ctx=0, rope_theta=1e4, partition_size=0, append=append,
                    ctx_list=tuple(ctx))
     streams, tiles = len(ctx) * hkv, len(ctx) * hkv * -(-max(ctx) // 32)
-    assert streams <= 62 and tiles <= 2048, (streams, tiles)
+    assert streams <= 1022 and tiles <= 16384, (streams, tiles)
     return cfg
 
 
@@ -462,7 +465,7 @@ def test_single_launch_counters_left_zero_and_workspace_shared():
         o, l = ops.paged_decode_attn(q, d.k_pool, d.v_pool, d.block_tables, d.context_lens, d.max_ctx,
                                      softmax_scale=cfg.softmax_scale, partition_size=ps, workspace=ws)
         torch.cuda.synchronize()
-        assert int(ws[:256].view(torch.int32).abs().sum()) == 0, ps
+        assert int(ws[:4096].view(torch.int32).abs().sum()) == 0, ps
         outs.append((ps, o.clone(), l.clone()))
     ref = [x for x in outs if x[0] == 0][0]
     for ps, o, l in outs:
@@ -492,7 +495,7 @@ def test_single_launch_back_to_back_different_inputs():
             outs.append(ops.paged_decode_attn(q, d.k_pool, d.v_pool, d.block_tables, d.context_lens, d.max_ctx,
                                               softmax_scale=c.softmax_scale, partition_size=0, workspace=ws))
     torch.cuda.synchronize()
-    assert int(ws[:256].view(torch.int32).abs().sum()) == 0
+    assert int(ws[:4096].view(torch.int32).abs().sum()) == 0
     for i, (w, c) in enumerate(zip(ws_list, cfgs)):
         r_out, r_lse = oracle_attention(w, act_raw(w, q_from_qkv(w)), pool_raw(w, w.k_pool), pool_raw(w, w.v_pool))
         for rep in range(3):
@@ -505,8 +508,9 @@ def test_single_launch_back_to_back_different_inputs():
 def test_row_plan_short_contexts_single_launch(cache):
     """Every context within one 32-token tile (max_context_len 32): no stream
     can be split, so the call is the decode launch alone, and the decode
-    kernel itself writes the empty contexts (out = 0, lse = -inf)."""
-    ctx = (0, 1, 5, 16, 17, 31, 32, 0, 2, 32)
+    kernel itself writes the empty contexts (out = 0, lse = -inf).  130
+    sequences x 8 kv heads: past the single-launch plan's 1022 streams."""
+    ctx = (0, 1, 5, 16, 17, 31, 32, 0, 2, 32) * 13
     cfg = W.Config(f"rows_short_{cache}", seed=15, num_seqs=len(ctx), num_q_heads=32, num_kv_heads=8, head_dim=128,
                    block_size=16, act="bf16", cache=cache, ctx=0, rope_theta=5e5, partition_size=0, append=True,
                    ctx_list=ctx)
@@ -535,12 +539,15 @@ def test_row_plan_many_sequences_scan_chunks():
 def test_row_plan_workspace_reuse():
     """The row plan needs no zeroed workspace (every entry it reads is written
     earlier in the same call): a reused, non-zero one gives identical results."""
-    cfg = W.CONFIGS["llama3_8b_gqa"].with_(num_seqs=12, ctx=(1, 3000), num_blocks=None, append=False)
+    ctx = (1, 3000, 6000, 17, 500, 2048, 4095, 33, 5000, 1, 600, 3333)  # 96 streams x 188 tiles: whole-row plan
+    cfg = W.CONFIGS["llama3_8b_gqa"].with_(num_seqs=len(ctx), ctx_list=ctx, num_blocks=None, append=False)
     w = W.make_workload(cfg)
     d = to_device(w)
     q = q_from_qkv(w).cuda()
+    assert ops.partition_size(q, d.k_pool, d.block_tables, d.max_ctx, 0) == 0
     nbytes = ops.workspace_bytes(q, d.k_pool, d.block_tables, d.max_ctx, 0)
     ws = torch.full((nbytes,), 0x7F, dtype=torch.uint8, device="cuda")
+    ws[:4096] = 0  # the counter slot: zero on entry for every plan
     announce("row workspace reuse", nbytes)
     outs = []
     for _ in range(3):
@@ -560,7 +567,8 @@ def test_row_plan_back_to_back_different_inputs(name):
     """Calls with different queries and caches on one workspace, no host sync
     between them: each must see its own split records, not the previous
     call's."""
-    over = dict(num_seqs=10, ctx=(1, 6000)) if name == "llama3_8b_gqa" else dict(num_seqs=2, ctx=20000)
+    # past the single-launch plan's tile cap: the whole-row ranges
+    over = dict(num_seqs=10, ctx=(7000, 16000)) if name == "llama3_8b_gqa" else dict(num_seqs=2, ctx=40000)
     cfgs = [W.CONFIGS[name].with_(seed=40 + i, num_blocks=None, append=False, partition_size=0, **over)
             for i in range(3)]
     ws_list = [W.make_workload(c) for c in cfgs]

@@ -16,7 +16,7 @@ pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not torch.cuda.is_available(),
 
 # (workload, first input, second (smaller) input, partition size)
 CASES = [
-    ("llama3_8b_gqa", dict(num_seqs=16, ctx=(17, 5000)), dict(num_seqs=5, ctx=(1, 900)), 0),       # equal ranges
+    ("llama3_8b_gqa", dict(num_seqs=16, ctx=(4500, 5000)), dict(num_seqs=5, ctx=(1, 900)), 0),     # ranges, then single launch
     ("llama3_8b_gqa", dict(num_seqs=16, ctx=(17, 5000)), dict(num_seqs=5, ctx=(1, 900)), 64),      # work queue
     ("qwen2.5_1.5b_gqa", dict(), dict(num_seqs=1, ctx_list=(700,)), 64),                          # work queue, Hkv 2
     ("qwen2.5_1.5b_gqa", dict(), dict(num_seqs=1, ctx_list=(700,)), 0),                           # single launch
