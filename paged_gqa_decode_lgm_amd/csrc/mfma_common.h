@@ -122,6 +122,26 @@ template <int POL>
 __device__ __forceinline__ uint32_t kv_load1(__amdgpu_buffer_rsrc_t r, int off) {
   return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, off, 0, POL);
 }
+// Device-scope accesses (cache-policy bit sc1) through a buffer descriptor,
+// for records that one workgroup writes and another reads within a launch:
+// each XCD has its own L2, which writes such stores through and does not
+// serve such loads from a stale line, as the memory model's device-scope
+// relaxed stores and loads do.
+constexpr int kDeviceScope = 16;
+__device__ __forceinline__ void store16_device(__amdgpu_buffer_rsrc_t r, int off, float4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) uint32_t, v), r, off, 0,
+                                         kDeviceScope);
+}
+__device__ __forceinline__ void store4_device(__amdgpu_buffer_rsrc_t r, int off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(v), r, off, 0, kDeviceScope);
+}
+__device__ __forceinline__ float4 load16_device(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kDeviceScope));
+}
+__device__ __forceinline__ float load4_device(__amdgpu_buffer_rsrc_t r, int off) {
+  return __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kDeviceScope));
+}
+
 // E8M0 byte -> the fp32 scale 2^(b - 127): the byte is the fp32 exponent
 // field, except 0 (2^-127, an fp32 subnormal) and 0xFF (NaN).
 __device__ __forceinline__ float e8m0_to_f32(uint32_t b) {

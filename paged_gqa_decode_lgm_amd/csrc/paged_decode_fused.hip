@@ -34,8 +34,6 @@ namespace {
 
 using namespace mfma;
 
-constexpr int kDeviceScope = 16;  // buffer cache-policy bit sc1: device-scope access
-
 template <int G>
 struct FusedSmem {
   float acc[kNW][G][kD];
@@ -45,20 +43,6 @@ struct FusedSmem {
   float lse[kFusedMaxChunks * G];  // the merging workgroup's record LSEs, [partition][head]
   int last;
 };
-
-__device__ __forceinline__ void store16_device(__amdgpu_buffer_rsrc_t r, int off, float4 v) {
-  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) uint32_t, v), r, off, 0,
-                                         kDeviceScope);
-}
-__device__ __forceinline__ void store4_device(__amdgpu_buffer_rsrc_t r, int off, float v) {
-  __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(v), r, off, 0, kDeviceScope);
-}
-__device__ __forceinline__ float4 load16_device(__amdgpu_buffer_rsrc_t r, int off) {
-  return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kDeviceScope));
-}
-__device__ __forceinline__ float load4_device(__amdgpu_buffer_rsrc_t r, int off) {
-  return __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kDeviceScope));
-}
 
 __device__ __forceinline__ void store_bf16x4(uint16_t* dst, float a, float b, float c, float d) {
   const uint32_t lo = (uint32_t)f32_to_bf16_rne(a) | ((uint32_t)f32_to_bf16_rne(b) << 16);
