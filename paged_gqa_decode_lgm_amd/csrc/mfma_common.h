@@ -212,6 +212,7 @@ struct MfmaBF16 {
     hi = __builtin_amdgcn_perm(y, x, 0x07060302u);  // x.hi16 | y.hi16 << 16
   }
   __device__ static void zero_v_row(VBlock& r, int jj) { r.v[jj] = make_uint4(0, 0, 0, 0); }
+  __device__ static void prepare_v(VBlock&) {}
 };
 
 struct MfmaFP8 {
@@ -263,7 +264,14 @@ struct MfmaFP8 {
     hi = fp8x2_hi_to_bf16x2(q);
   }
   __device__ static void zero_v_row(VBlock& r, int jj) { r.v[jj] = make_uint2(0, 0); }
+  __device__ static void prepare_v(VBlock&) {}
 };
+
+// Lane x of a wave receives lane (x & ~3) + J's value (a quad broadcast).
+template <int J>
+__device__ __forceinline__ uint32_t quad_bcast(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, J * 0x55, 0xF, 0xF, false);
+}
 
 // FP4 blocks: codes [16][Hkv][64 bytes] (two E2M1 codes a byte, low nibble
 // first), then scales [16][Hkv][4 bytes] (E8M0, one per 32 head-dim elements).
@@ -280,9 +288,17 @@ struct MfmaFP4 {
     uint4 k;     // codes of K[n][32kg .. 32kg+31]
     uint32_t s;  // their scale byte
   };
+  // The V scales of a lane's four rows: lane (kg, 4a + t) loads the four
+  // scale bytes of row 4kg + t, and the rows a lane reads (4kg .. 4kg + 3,
+  // byte a) are then in its own quad: one dword load instead of four byte
+  // loads, each of which costs the load pipeline a whole instruction.
+  // prepare_v takes each row's byte from its quad neighbour once the loads
+  // are in; a masked row keeps a finite scale (bit jj of dead).
   struct VBlock {
     uint32_t v[4];  // codes of V[4kg + jj][8n .. 8n+7]
-    uint32_t s[4];  // their scale bytes
+    uint32_t sw;    // scale bytes of row 4kg + (n & 3)
+    uint32_t dead;  // bit jj: row jj masked
+    float sf[4];    // scales of rows 4kg + jj, head-dim block n / 4 (prepare_v)
   };
   __device__ static int k_lane_off(const KVLayout& L, int g, int n, int kg) { return n * L.tok + g * L.head + 16 * kg; }
   __device__ static int v_lane_off(const KVLayout& L, int g, int n, int kg) {
@@ -294,7 +310,7 @@ struct MfmaFP4 {
     return L.sbase + n * L.stok + g * L.shead + kg;
   }
   __device__ static int v_scale_off(const KVLayout& L, int g, int n, int kg) {
-    return L.sbase + 4 * kg * L.stok + g * L.shead + (n >> 2);
+    return L.sbase + (4 * kg + (n & 3)) * L.stok + g * L.shead;
   }
   template <int POL = kDefaultPolicy>
   __device__ static void load_k(KBlock& r, __amdgpu_buffer_rsrc_t rs, int off, const KVLayout&, int soff) {
@@ -305,8 +321,19 @@ struct MfmaFP4 {
   __device__ static void load_v(VBlock& r, __amdgpu_buffer_rsrc_t rs, int off, const KVLayout& L, int soff) {
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) r.v[jj] = kv_load4<POL>(rs, off + jj * L.tok);
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) r.s[jj] = kv_load1<POL>(rs, soff + jj * L.stok);
+    r.sw = kv_load4<POL>(rs, soff);
+    r.dead = 0;
+  }
+  // Every lane of a quad needs the same head-dim block (n / 4), so each lane
+  // decodes its own row's scale for that block once and the quad shares the
+  // decoded values.
+  __device__ static void prepare_v(VBlock& r) {
+    const uint32_t lane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    const uint32_t own = __float_as_uint(e8m0_to_f32((r.sw >> (8 * ((lane >> 2) & 3))) & 0xFFu));
+    r.sf[0] = (r.dead & 1u) ? 1.f : __uint_as_float(quad_bcast<0>(own));
+    r.sf[1] = (r.dead & 2u) ? 1.f : __uint_as_float(quad_bcast<1>(own));
+    r.sf[2] = (r.dead & 4u) ? 1.f : __uint_as_float(quad_bcast<2>(own));
+    r.sf[3] = (r.dead & 8u) ? 1.f : __uint_as_float(quad_bcast<3>(own));
   }
   __device__ static short8 k_operand(const KBlock& r, int c) {
     const uint32_t w = c == 0 ? r.k.x : (c == 1 ? r.k.y : (c == 2 ? r.k.z : r.k.w));
@@ -319,7 +346,7 @@ struct MfmaFP4 {
   // halves.
   __device__ static void v_pairs2(const VBlock& r, int jj, int i, uint32_t& lo, uint32_t& hi) {
     uint32_t x, y;
-    const float sx = e8m0_to_f32(r.s[jj]), sy = e8m0_to_f32(r.s[jj + 1]);
+    const float sx = r.sf[jj], sy = r.sf[jj + 1];
     switch (i >> 1) {
       case 0: x = fp4x2_to_bf16x2<0>(r.v[jj], sx); y = fp4x2_to_bf16x2<0>(r.v[jj + 1], sy); break;
       case 1: x = fp4x2_to_bf16x2<1>(r.v[jj], sx); y = fp4x2_to_bf16x2<1>(r.v[jj + 1], sy); break;
@@ -329,11 +356,11 @@ struct MfmaFP4 {
     lo = __builtin_amdgcn_perm(y, x, 0x05040100u);  // element i of both rows
     hi = __builtin_amdgcn_perm(y, x, 0x07060302u);  // element i+1 of both rows
   }
-  // A masked row: zero codes and a finite scale, so the row contributes
-  // exactly zero whatever its stored scale byte held.
+  // A masked row: zero codes and (prepare_v) a finite scale, so the row
+  // contributes exactly zero whatever its stored scale byte held.
   __device__ static void zero_v_row(VBlock& r, int jj) {
     r.v[jj] = 0;
-    r.s[jj] = 127;
+    r.dead |= 1u << jj;
   }
 };
 
@@ -559,6 +586,8 @@ __device__ __forceinline__ void step_update(WaveState& st, StepRegs<C, NB>& r, f
     }
     const short8 pa = words_to_short8(pw[0], pw[1], pw[2], pw[3]);
     st.psum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, ones, st.psum, 0, 0, 0);
+    C::prepare_v(r.v[2 * q]);  // (after the exponentials: the first use of this pair's V)
+    C::prepare_v(r.v[2 * q + 1]);
     const typename C::VBlock& vx = r.v[2 * q];
     const typename C::VBlock& vy = r.v[2 * q + 1];
 #pragma unroll

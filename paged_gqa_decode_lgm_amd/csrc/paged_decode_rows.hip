@@ -264,7 +264,20 @@ __device__ __forceinline__ void flush_batch(const DecodeArgs& p, const RowsArgs&
 // in flight.  Two cover HBM latency at one wave per SIMD (a bf16 set holds
 // 16 KB of one kv head's K and V, an FP8 set 8 KB; more sets or larger steps
 // gave FP8 no more bandwidth, see step_blocks).
-constexpr int kRowSets = 2;
+#ifndef LGM_ROW_SETS_BF16
+#define LGM_ROW_SETS_BF16 2
+#endif
+#ifndef LGM_ROW_SETS_FP8
+#define LGM_ROW_SETS_FP8 2
+#endif
+#ifndef LGM_ROW_SETS_FP4
+#define LGM_ROW_SETS_FP4 2
+#endif
+template <class C>
+constexpr int row_sets() {
+  return std::is_same<C, MfmaFP8>::value ? LGM_ROW_SETS_FP8
+                                         : (std::is_same<C, MfmaFP4>::value ? LGM_ROW_SETS_FP4 : LGM_ROW_SETS_BF16);
+}
 
 template <int G, int HG>
 __device__ __forceinline__ SegDesc read_seg(const RowsSmem<G, HG>& sm, int s) {
@@ -385,7 +398,7 @@ template <class C, int G, int HG, int HPW>
 __device__ __forceinline__ void run_batch(const DecodeArgs& p, RowsSmem<G, HG>& sm, int nseg, int wave, int lane) {
   constexpr int NB = step_blocks<C>();
   constexpr int ST = NB / 2;  // tiles per step
-  constexpr int NS = kRowSets;
+  constexpr int NS = row_sets<C>();
   static_assert(NS % HPW == 0, "a set must stay on one head");
   static_assert(kWin % ST == 0, "a step's tiles share one window of block ids");
   const int n = lane & 15, kg = lane >> 4;
@@ -736,9 +749,12 @@ __global__ __launch_bounds__(kMergeThreads) void rows_merge_kernel(DecodeArgs p,
 // each within half the register file.  FP4 moves the fewest bytes per
 // instruction; with one wave per SIMD its dependency stalls were exposed, and
 // eight waves made it ~10% faster, while FP8 was ~2% slower with eight.
+#ifndef LGM_FP4_EIGHT_WAVES
+#define LGM_FP4_EIGHT_WAVES 1
+#endif
 template <class C>
 constexpr bool two_waves_per_simd() {
-  return std::is_same<C, MfmaFP4>::value;
+  return LGM_FP4_EIGHT_WAVES && std::is_same<C, MfmaFP4>::value;
 }
 
 template <class C, int G>
