@@ -114,6 +114,13 @@ template <int POL>
 __device__ __forceinline__ uint2 kv_load8(__amdgpu_buffer_rsrc_t r, int off) {
   return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, POL));
 }
+// 16 bytes per lane from a buffer straight into LDS (buffer_load_dwordx4 ...
+// lds): lane l's bytes land at lds + 16 l.  lds must be the same for the
+// whole wave (it goes to M0).
+template <int POL>
+__device__ __forceinline__ void kv_load16_lds(__amdgpu_buffer_rsrc_t r, void* lds, int off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, off, 0, 0, POL);
+}
 template <int POL>
 __device__ __forceinline__ uint32_t kv_load4(__amdgpu_buffer_rsrc_t r, int off) {
   return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, POL);

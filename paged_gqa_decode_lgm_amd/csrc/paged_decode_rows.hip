@@ -54,12 +54,13 @@ struct SegDesc {
 // stored to global memory as each segment ended held up the loads issued
 // after them, which wait for those stores to complete: 4-5 us per segment
 // on 128 FP8 contexts of 1024..4096 tokens, measured with per-workgroup
-// timestamps.)  A batch holds as many segments as ~140 KB of LDS allow.
+// timestamps.)  A batch holds as many segments as ~108 KB of LDS allow; the
+// FP8 kernel's K staging (32 KB, below) takes part of the rest.
 template <int G, int HG>
 struct Batch {
   static constexpr int kQRow = kD + 8;  // bf16 per staged query row; the pad spreads rows over LDS banks
   static constexpr int kPerSeg = HG * G * (kQRow * 2 + kD * 4 + 12) + kStageWin * 2 * kWin * 4 + 2 * HG * 4 + 32;
-  static constexpr int kFit = 140000 / kPerSeg;
+  static constexpr int kFit = 108000 / kPerSeg;
   static constexpr int kMax = kFit > 16 ? 16 : (kFit < 1 ? 1 : kFit);
 };
 
@@ -160,6 +161,47 @@ __device__ __forceinline__ void row_load_k(const DecodeArgs& p, int g, const int
   for (int b = 0; b < NB; ++b)
     C::template load_k<row_policy<C>()>(sr.k[b], block_rsrc(p.k_cache, L.block, id[b]), off, L, soff);
 }
+// FP8 K tiles go through LDS.  A wave's K loads in the MFMA operand layout
+// read 16 token rows x 64 bytes per instruction; loads that read whole
+// 128-byte rows (eight rows per instruction) made the FP8 call ~4% faster
+// in a timing-only test, and staging the rows in LDS with direct loads keeps
+// that pattern while the operand layout comes from LDS reads (FP8 call
+// 119.6-121.2 against 122.7-129.0 us medians on 128 contexts of
+// 1024..4096 tokens; bf16 gained nothing from whole-row K loads).  Per wave
+// and register set a buffer of NB blocks x 16 rows x 128 bytes: chunk c (16
+// bytes) of row n sits in slot 8n + (c ^ (n >> 1)), so the operand reads of
+// 16 lanes (rows 0..15, one chunk) fall in 16 different groups of four
+// banks.  Load instruction u of a block fills slots 64u .. 64u + 63, one per
+// lane: lane l takes row 8u + l / 8, chunk (l % 8) ^ (row >> 1), whole rows
+// per eight lanes.
+constexpr int kKStageBlock = 16 * 128;  // bytes of one block's K rows of one kv head (FP8)
+template <class C, int NB>
+__device__ __forceinline__ void row_load_k_lds(const DecodeArgs& p, int g, const int (&id)[NB], int lane,
+                                               uint8_t* buf) {
+  const KVLayout L = kv_layout<C>(p.flags, p.dims.num_kv_heads);
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const __amdgpu_buffer_rsrc_t rs = block_rsrc(p.k_cache, L.block, id[b]);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int row = 8 * u + (lane >> 3);
+      const int chunk = (lane & 7) ^ (row >> 1);
+      kv_load16_lds<row_policy<C>()>(rs, buf + b * kKStageBlock + 1024 * u, row * L.tok + g * L.head + 16 * chunk);
+    }
+  }
+}
+// The K operand registers of a step from its LDS buffer: lane (kg, n) takes
+// chunks kg and 4 + kg of row n (head-dim 16kg .. 16kg + 15 and 64 more).
+template <class C, int NB>
+__device__ __forceinline__ void row_read_k_lds(const uint8_t* buf, int lane, StepRegs<C, NB>& sr) {
+  const int n = lane & 15, kg = lane >> 4;
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+      sr.k[b].k[u] = *reinterpret_cast<const uint4*>(buf + b * kKStageBlock + 16 * (8 * n + ((4 * u + kg) ^ (n >> 1))));
+}
+
 template <class C, int NB>
 __device__ __forceinline__ void row_load_v(const DecodeArgs& p, int g, const int (&id)[NB], int lane,
                                            StepRegs<C, NB>& sr) {
@@ -395,7 +437,8 @@ __device__ __forceinline__ void lds_q_operand(const RowsSmem<G, HG>& sm, int s, 
 // lse = -inf.  Pairs past the batch are absent: their loads return zeros
 // without touching memory.
 template <class C, int G, int HG, int HPW>
-__device__ __forceinline__ void run_batch(const DecodeArgs& p, RowsSmem<G, HG>& sm, int nseg, int wave, int lane) {
+__device__ __forceinline__ void run_batch(const DecodeArgs& p, RowsSmem<G, HG>& sm, int nseg, int wave, int lane,
+                                          uint8_t* kst) {
   constexpr int NB = step_blocks<C>();
   constexpr int ST = NB / 2;  // tiles per step
   constexpr int NS = row_sets<C>();
@@ -498,7 +541,8 @@ __device__ __forceinline__ void run_batch(const DecodeArgs& p, RowsSmem<G, HG>& 
   for (int j = 0; j < NS; ++j) {  // the loop's load order: K, V of each set in turn
     if (j % HPW == 0 && j > 0) l_advance();
     l_ids(pid[j]);
-    row_load_k<C, NB>(p, l_g0 + j % HPW, pid[j], lane, sr[j]);
+    if constexpr (C::kFp8) row_load_k_lds<C, NB>(p, l_g0 + j % HPW, pid[j], lane, kst + j * NB * kKStageBlock);
+    else row_load_k<C, NB>(p, l_g0 + j % HPW, pid[j], lane, sr[j]);
     __builtin_amdgcn_sched_barrier(0);
     row_load_v<C, NB>(p, l_g0 + j % HPW, pid[j], lane, sr[j]);
     __builtin_amdgcn_sched_barrier(0);
@@ -514,8 +558,17 @@ __device__ __forceinline__ void run_batch(const DecodeArgs& p, RowsSmem<G, HG>& 
       l_ids(nid);
       const int lg = l_g0 + h;
       float4v sc[NB];
+      if constexpr (C::kFp8) row_read_k_lds<C, NB>(kst + j * NB * kKStageBlock, lane, sr[j]);
       step_scores<C, NB>(sr[j], qb[h], sc);
-      row_load_k<C, NB>(p, lg, nid, lane, sr[j]);
+      if constexpr (C::kFp8) {
+        // The buffer's reads are complete before the next step's loads may
+        // write it (a load of an absent block lands in LDS at once), and no
+        // memory access moves across this point.
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        row_load_k_lds<C, NB>(p, lg, nid, lane, kst + j * NB * kKStageBlock);
+      } else {
+        row_load_k<C, NB>(p, lg, nid, lane, sr[j]);
+      }
       step_update<C, NB>(st[h], sr[j], sc, csc[h], valid_bits(pid[j]), kTile * (c_lt + ST * ck), c_ctx, kg);
       row_load_v<C, NB>(p, lg, nid, lane, sr[j]);
 #pragma unroll
@@ -530,6 +583,10 @@ __device__ __forceinline__ void run_batch(const DecodeArgs& p, RowsSmem<G, HG>& 
       }
     }
   }
+  // The K loads issued past the batch's last step (absent blocks) may still
+  // be in flight; the next batch's first loads fill the same buffers, and
+  // nothing orders two loads' arrival in LDS, so they complete here.
+  if constexpr (C::kFp8) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 // One workgroup per equal range of the flattened list of work units: the
@@ -549,6 +606,8 @@ __global__ __launch_bounds__(NT, 1) void paged_decode_rows_kernel(DecodeArgs p, 
   constexpr int HG = NT / kWaveSize * HPW;
   using Bt = Batch<G, HG>;
   __shared__ RowsSmem<G, HG> sm;
+  constexpr int kKStage = C::kFp8 ? row_sets<C>() * step_blocks<C>() * kKStageBlock : 0;  // per wave
+  __shared__ __attribute__((aligned(16))) uint8_t kst[kKStage > 0 ? NT / kWaveSize * kKStage : 16];
   const int lane = threadIdx.x & (kWaveSize - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWaveSize);
   const int B = p.dims.num_seqs;
@@ -614,7 +673,7 @@ __global__ __launch_bounds__(NT, 1) void paged_decode_rows_kernel(DecodeArgs p, 
     __syncthreads();  // the batch's descriptors
     stage_batch<C, G, HG, NT>(p, sm, nseg, wave, lane);
     __syncthreads();  // the batch's ids, query rows and scales
-    run_batch<C, G, HG, HPW>(p, sm, nseg, wave, lane);
+    run_batch<C, G, HG, HPW>(p, sm, nseg, wave, lane, kst + wave * kKStage);
     __syncthreads();  // every wave has staged its results
     flush_batch<C, G, HG, NT>(p, r, sm, nseg, wave, lane);
     __syncthreads();  // the batch is written before the next one is staged
