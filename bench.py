@@ -332,9 +332,14 @@ def counter_summary(workload: str, paths, commands: list) -> int:
                 derived["valu_busy_pct"] = round(100.0 * mean["SQ_ACTIVE_INST_VALU"] / NUM_CU / span, 2)
             if "SQ_BUSY_CYCLES" in mean:
                 derived["sq_busy_cycles_per_xcd"] = round(mean["SQ_BUSY_CYCLES"] / NUM_XCD, 1)
+        if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in mean:  # 512 flops per MOP (rocprofv3's own derived metrics)
+            derived["mfma_bf16_flops_per_dispatch"] = round(512.0 * mean["SQ_INSTS_VALU_MFMA_MOPS_BF16"], 1)
+        if mean.get("SQ_VALU_MFMA_BUSY_CYCLES") and "SQ_VALU_MFMA_COEXEC_CYCLES" in mean:
+            derived["valu_coexec_share_of_mfma_busy"] = round(mean["SQ_VALU_MFMA_COEXEC_CYCLES"] /
+                                                              mean["SQ_VALU_MFMA_BUSY_CYCLES"], 4)
         if "SQ_WAVES" in mean and mean["SQ_WAVES"]:
-            for c in ("SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_VMEM_RD", "SQ_INSTS_SALU", "SQ_INSTS_VALU_CVT",
-                      "SQ_INSTS_VALU_TRANS_F32", "SQ_INSTS_LDS"):
+            for c in ("SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_VALU_MFMA_BF16", "SQ_INSTS_VMEM_RD", "SQ_INSTS_SALU",
+                      "SQ_INSTS_VALU_CVT", "SQ_INSTS_VALU_TRANS_F32", "SQ_INSTS_LDS"):
                 if c in mean:
                     derived[c.lower().replace("sq_insts_", "insts_per_wave_")] = round(mean[c] / mean["SQ_WAVES"], 1)
         rec["derived"] = derived
