@@ -91,10 +91,12 @@ __device__ __forceinline__ int clamped_ctx(const DecodeArgs& p, int b) {
 
 // Fills sm.pre for sequences b0 .. b0 + kChunk - 1 (nhg streams of
 // ceil(ctx / unit) work units per sequence: 32-token tiles, or partitions;
-// an empty context still counts one) and returns the chunk's total.
-// Called by every thread of the NT-thread workgroup (it synchronises).
+// an empty context still counts one; each stream costs ucost per unit plus
+// scost) and returns the chunk's total cost.  Called by every thread of the
+// NT-thread workgroup (it synchronises).
 template <int NT, class SM>
-__device__ int scan_chunk(const DecodeArgs& p, SM& sm, int b0, int nhg, int unit, int min_units) {
+__device__ int scan_chunk(const DecodeArgs& p, SM& sm, int b0, int nhg, int unit, int min_units, int ucost,
+                          int scost) {
   constexpr int SPT = kChunk / NT;  // sequences per thread
   static_assert(SPT * NT == kChunk && NT / kWaveSize <= kMaxRowWaves, "scan layout");
   const int tid = threadIdx.x, lane = tid & (kWaveSize - 1), wave = tid / kWaveSize;
@@ -102,7 +104,7 @@ __device__ int scan_chunk(const DecodeArgs& p, SM& sm, int b0, int nhg, int unit
 #pragma unroll
   for (int k = 0; k < SPT; ++k) {
     const int b = b0 + SPT * tid + k;
-    t[k] = b < p.dims.num_seqs ? max((clamped_ctx(p, b) + unit - 1) / unit, min_units) * nhg : 0;
+    t[k] = b < p.dims.num_seqs ? (max((clamped_ctx(p, b) + unit - 1) / unit, min_units) * ucost + scost) * nhg : 0;
     s += t[k];
   }
   int incl = s;
@@ -589,6 +591,34 @@ __device__ __forceinline__ void run_batch(const DecodeArgs& p, RowsSmem<G, HG>& 
   if constexpr (C::kFp8) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
+// A segment costs its workgroup more than its tiles (entering it, staging its
+// query and writing its result), so ranges are cut in equal cost: kTileCost
+// per tile plus seg_cost<C>() per stream.  Measured with per-workgroup
+// timestamps on equal tile ranges: 128 FP8 contexts of 1024..4096 tokens,
+// ranges holding two segments ended 3-5 us after ranges holding one (a
+// range takes ~100 us; 8% of the workgroups' time idle at the end); bf16
+// (64 contexts of 512..8192): ~1 us.  FP8 call medians by the cost per
+// stream (quarter tiles): 0: 119.0-120.4 us, 3: 117.3-118.1, 6: 116.8-117.4,
+// 10: 116.5-116.7 (16: slower again); bf16 and FP4 moved within noise.
+constexpr int kTileCost = 4;
+#ifndef LGM_ROWS_SEG_COST_BF16
+#define LGM_ROWS_SEG_COST_BF16 1
+#endif
+#ifndef LGM_ROWS_SEG_COST_FP8
+#define LGM_ROWS_SEG_COST_FP8 10
+#endif
+#ifndef LGM_ROWS_SEG_COST_FP4
+#define LGM_ROWS_SEG_COST_FP4 4
+#endif
+static_assert(kTileCost == 4 && LGM_ROWS_SEG_COST_BF16 <= 16 && LGM_ROWS_SEG_COST_FP8 <= 16 &&
+                  LGM_ROWS_SEG_COST_FP4 <= 16,
+              "the host checks the total cost against 4 per tile and 16 per stream");
+template <class C>
+constexpr int seg_cost() {
+  return std::is_same<C, MfmaFP8>::value ? LGM_ROWS_SEG_COST_FP8
+                                         : (std::is_same<C, MfmaFP4>::value ? LGM_ROWS_SEG_COST_FP4 : LGM_ROWS_SEG_COST_BF16);
+}
+
 // One workgroup per equal range of the flattened list of work units: the
 // 32-token tiles of all streams, or (partition mode) their split-K
 // partitions, so that a range holds whole partitions.  Record slot 2w holds
@@ -618,19 +648,20 @@ __global__ __launch_bounds__(NT, 1) void paged_decode_rows_kernel(DecodeArgs p, 
   const int upt = parts ? r.part_tiles : 1;   // tiles per unit
   const int unit = kTile * upt;               // tokens per unit
   const int min_units = 1;                    // an empty context still writes out = 0, lse = -inf
+  // Equal ranges of cost: kTileCost per tile and seg_cost<C>() per stream
+  // (partition mode: one per partition).
+  const int ucost = parts ? 1 : kTileCost;
+  const int scost = parts ? 0 : seg_cost<C>();
 
-  int total = scan_chunk<NT>(p, sm, 0, nhg, unit, min_units);
-  for (int c0 = kChunk; c0 < B; c0 += kChunk) total += scan_chunk<NT>(p, sm, c0, nhg, unit, min_units);
+  int total = scan_chunk<NT>(p, sm, 0, nhg, unit, min_units, ucost, scost);
+  for (int c0 = kChunk; c0 < B; c0 += kChunk) total += scan_chunk<NT>(p, sm, c0, nhg, unit, min_units, ucost, scost);
   const int t_lo = (int)((int64_t)wg * total / W);
   const int t_hi = (int)((int64_t)(wg + 1) * total / W);
   int b0 = 0, base = 0;
-  if (B > kChunk) scan_chunk<NT>(p, sm, 0, nhg, unit, min_units);  // back to the first chunk
+  if (B > kChunk) scan_chunk<NT>(p, sm, 0, nhg, unit, min_units, ucost, scost);  // back to the first chunk
 
   int pos = t_lo;
   bool first = true;
-  if (!parts && t_lo >= t_hi) {  // an empty range: its first record slot weighs nothing in the merge
-    for (int i = threadIdx.x; i < HG * G; i += NT) r.rec_lse[(int64_t)2 * wg * HG * G + i] = -INFINITY;
-  }
   while (pos < t_hi) {
     int nseg = 0;
     while (pos < t_hi && nseg < Bt::kMax) {
@@ -638,7 +669,7 @@ __global__ __launch_bounds__(NT, 1) void paged_decode_rows_kernel(DecodeArgs p, 
       while (rel >= __builtin_amdgcn_readfirstlane(sm.pre[kChunk])) {  // uniform: every thread moves on together
         base += __builtin_amdgcn_readfirstlane(sm.pre[kChunk]);
         b0 += kChunk;
-        scan_chunk<NT>(p, sm, b0, nhg, unit, min_units);
+        scan_chunk<NT>(p, sm, b0, nhg, unit, min_units, ucost, scost);
         rel = pos - base;
       }
       int lo = 0, hi = kChunk;  // sm.pre[lo] <= rel < sm.pre[hi]
@@ -652,9 +683,16 @@ __global__ __launch_bounds__(NT, 1) void paged_decode_rows_kernel(DecodeArgs p, 
       const int ntb = (ctx + kTile - 1) / kTile;                      // tiles of the stream
       const int ntu = max((ctx + unit - 1) / unit, min_units);        // units of the stream
       const int off = rel - __builtin_amdgcn_readfirstlane(sm.pre[lo]);
-      const int hg = off / ntu;
-      const int lu = off - hg * ntu;
-      const int eu = parts ? lu + 1 : min(ntu, lu + (t_hi - pos));
+      const int stream_cost = scost + ucost * ntu;
+      const int hg = off / stream_cost;
+      // The range holds the units whose cost position scost + ucost * j
+      // (the unit's start) lies in [c0, c1), its part of this stream.
+      const int c0 = off - hg * stream_cost;
+      const int c1 = min(stream_cost, c0 + (t_hi - pos));
+      const int lu = c0 <= scost ? 0 : (c0 - scost + ucost - 1) / ucost;
+      const int eu = parts ? lu + 1 : (c1 <= scost ? 0 : min(ntu, (c1 - scost + ucost - 1) / ucost));
+      pos += parts ? 1 : c1 - c0;
+      if (lu >= eu) continue;  // only the stream's fixed cost lies in the range
       const int lt = lu * upt;
       const int et = min(ntb, eu * upt);
       const int u = b * nhg + hg;
@@ -666,7 +704,6 @@ __global__ __launch_bounds__(NT, 1) void paged_decode_rows_kernel(DecodeArgs p, 
         }
         sm.seg[nseg] = SegDesc{b, ctx, lt, et, hg, parts ? lu : 2 * wg + (first ? 0 : 1), whole ? 1 : 0, 0};
       }
-      pos += eu - lu;
       first = false;
       ++nseg;
     }
@@ -677,6 +714,12 @@ __global__ __launch_bounds__(NT, 1) void paged_decode_rows_kernel(DecodeArgs p, 
     __syncthreads();  // every wave has staged its results
     flush_batch<C, G, HG, NT>(p, r, sm, nseg, wave, lane);
     __syncthreads();  // the batch is written before the next one is staged
+  }
+  // A range without a unit (more workgroups than units, or only streams'
+  // fixed costs): its first record slot weighs nothing in the merge of a
+  // stream it lies inside.
+  if (!parts && first) {
+    for (int i = threadIdx.x; i < HG * G; i += NT) r.rec_lse[(int64_t)2 * wg * HG * G + i] = -INFINITY;
   }
 }
 
