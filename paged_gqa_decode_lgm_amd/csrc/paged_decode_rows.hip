@@ -851,18 +851,24 @@ __global__ __launch_bounds__(kMergeThreads) void rows_merge_kernel(DecodeArgs p,
 // each within half the register file.  FP4 moves the fewest bytes per
 // instruction; with one wave per SIMD its dependency stalls were exposed, and
 // eight waves made it ~10% faster, while FP8 was ~2% slower with eight.
+// Groups of more than 11 query heads do not fit half the register file (the
+// eight-wave build spills 8 to 92 bytes per lane to scratch memory at
+// G = 12..16) and keep four waves of two heads: 150 against 154 us at
+// G = 16 (8 kv heads, 128 contexts of 1024..4096 tokens), the same time
+// within noise at G = 12.
 #ifndef LGM_FP4_EIGHT_WAVES
 #define LGM_FP4_EIGHT_WAVES 1
 #endif
-template <class C>
+constexpr int kEightWaveMaxGroup = 11;
+template <class C, int G>
 constexpr bool two_waves_per_simd() {
-  return LGM_FP4_EIGHT_WAVES && std::is_same<C, MfmaFP4>::value;
+  return LGM_FP4_EIGHT_WAVES && std::is_same<C, MfmaFP4>::value && G <= kEightWaveMaxGroup;
 }
 
 template <class C, int G>
 hipError_t launch_group(const DecodeArgs& a, const RowsArgs& r, hipStream_t s) {
   if (r.head_group == 8) {
-    if constexpr (two_waves_per_simd<C>())
+    if constexpr (two_waves_per_simd<C, G>())
       hipLaunchKernelGGL((paged_decode_rows_kernel<C, G, 1, 2 * kDecodeThreads>), dim3(r.num_wg),
                          dim3(2 * kDecodeThreads), 0, s, a, r);
     else

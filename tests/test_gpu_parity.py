@@ -403,10 +403,12 @@ def test_many_short_sequences_and_empty_ones(ps):
 
 
 @pytest.mark.parametrize("cache", ["bf16", "fp8", "fp4"])
-@pytest.mark.parametrize("hkv,G", [(4, 1), (4, 4), (8, 4), (8, 5), (16, 2), (8, 16)])
+@pytest.mark.parametrize("hkv,G", [(4, 1), (4, 4), (8, 4), (8, 5), (16, 2), (8, 11), (8, 12), (8, 16)])
 def test_row_plan_ragged_edges(cache, hkv, G):
     """Whole-row ranges (partition_size 0, kv heads divisible by 4): head
     groups of 4 and 8, empty and one-token contexts, block and tile edges.
+    FP4 at 11 and 12 query heads per kv head: the two sides of the bound on
+    its eight-wave workgroup shape.
     The edge contexts twice over and one 16384-token context: past the
     single-launch plan's tile cap (16384 tiles, 32768 for FP8)."""
     ctx = EDGE_CTX * 2 + (16384,)
