@@ -194,7 +194,8 @@ lgm_status lgm_rope_kv_append(const void* qkv, int64_t qkv_row_stride, void* q_o
  *    per workgroup; the workgroup that finishes a context's last partition
  *    merges that context by log-sum-exp.  Returns the partition;
  *  - other matrix-core shapes with num_kv_heads divisible by 4: returns 0.  The 32-token tiles of all
- *    contexts (per group of 8, or 4, kv heads) are cut into equal ranges, one
+ *    contexts (per group of 8 kv heads when 8 divide num_kv_heads and
+ *    num_q_heads / num_kv_heads is at most 8, else of 4) are cut into equal ranges, one
  *    per compute unit (256, fewer when a range would hold under 2 tiles);
  *    each workgroup reads whole KV rows of its head group, and contexts split
  *    between ranges are merged by log-sum-exp;
@@ -207,7 +208,7 @@ lgm_status lgm_rope_kv_append(const void* qkv, int64_t qkv_row_stride, void* q_o
  *    num_kv_heads divisible by 4 and an explicit partition_size that is a
  *    multiple of 32 and at least 256 tokens, max_context_len holds at least
  *    64 partitions and the batch at least 256 (sequence, head group of 8 or
- *    4 kv heads, partition) units: plain ceil(L / partition) partitions, run
+ *    4 kv heads as above, partition) units: plain ceil(L / partition) partitions, run
  *    in equal numbers of whole partitions per workgroup (256 workgroups of
  *    whole KV rows);
  *  - every other partitioned plan: when max_context_len exceeds the
@@ -232,7 +233,8 @@ int32_t lgm_paged_decode_partition_size(lgm_paged_dims dims, int32_t max_context
  *    fp32 outputs [B * Hkv][P][G][D], then natural-log LSEs [B * Hkv][P][G];
  *  - equal ranges (see lgm_paged_decode_partition_size): two records per
  *    range (fp32 outputs of the head group's Hq * 8 / Hkv or Hq * 4 / Hkv
- *    query heads, D each, and their natural-log LSEs), then int32 context
+ *    query heads, D each, and their natural-log LSEs; head groups as in
+ *    lgm_paged_decode_partition_size), then int32 context
  *    bookkeeping (two per context and head group);
  *  - partitions (the whole-row partition plan, the work-queue plan on the
  *    other matrix-core shapes, the vector-ALU plan on the rest): when

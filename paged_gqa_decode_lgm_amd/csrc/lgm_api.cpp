@@ -190,6 +190,18 @@ constexpr size_t kCounterSlot = LGM_COUNTER_SLOT_BYTES;  // the counters at the 
 // (sequence, kv head) stream.  Each kernel leaves the counters it uses zero,
 // and no plan puts anything else there, so one zero-filled workspace may
 // serve calls on any plan in turn.  The plan's own regions follow.
+// kv heads per whole-row workgroup: 8 (whole NHD rows) when they divide the
+// kv heads and the group has at most 8 query heads per kv head, else 4.  A
+// segment's staged query rows and results grow with G (128 rows of 272 +
+// 512 bytes at G = 16 and 8 heads), and past 8 a batch holds a single
+// segment, so a range's second segment waits for the first one's flush and
+// restarts the load pipeline.  Call medians at G = 16 (8 kv heads, 4 vs 8
+// heads per workgroup): bf16 200 vs 206 us (64 contexts of 512..8192), FP8
+// 139-141 vs 147 us (128 of 1024..4096); at G = 8 FP8 was 1.5% slower with 4.
+static int rows_head_group(int num_kv_heads, int G) {
+  return num_kv_heads % 8 == 0 && G <= LGM_ROWS_HG8_MAX_GROUP ? 8 : 4;
+}
+
 struct Plan {
   bool fused;       // single-launch split kernel (small jobs): partitions of ps tokens, merged in the launch
   bool rows;        // whole-row kernel (Hkv % 4 == 0): equal tile ranges (partition_size 0) ...
@@ -308,7 +320,7 @@ lgm_status plan_decode(const char* fn, const lgm_paged_dims& d, int32_t max_ctx,
   }
   if (ps_arg == 0 && lgm::decode_rows_supported(act, cache, d.head_dim, d.num_kv_heads, G, d.block_size)) {
     pl.rows = true;
-    pl.HG = d.num_kv_heads % 8 == 0 ? 8 : 4;
+    pl.HG = rows_head_group(d.num_kv_heads, G);
     const int64_t streams = (int64_t)d.num_seqs * (d.num_kv_heads / pl.HG);
     const int64_t tiles = streams * ((max_ctx + kRowsTile - 1) / kRowsTile);
     // The kernel cuts its ranges in cost units: 4 per tile and at most 16 per stream.
@@ -331,14 +343,14 @@ lgm_status plan_decode(const char* fn, const lgm_paged_dims& d, int32_t max_ctx,
   pl.ps = resolve_partition(fn, d, max_ctx, ps_arg, persistent);
   if (pl.ps < 0) return LGM_ERR_INVALID_ARGUMENT;
   const int32_t most_parts = (int32_t)(((int64_t)max_ctx + pl.ps - 1) / pl.ps);
-  const int64_t est_units = (int64_t)d.num_seqs * (d.num_kv_heads / (d.num_kv_heads % 8 == 0 ? 8 : 4)) * most_parts;
+  const int64_t est_units = (int64_t)d.num_seqs * (d.num_kv_heads / rows_head_group(d.num_kv_heads, G)) * most_parts;
   if (ps_arg > 0 && pl.ps >= kRowsMinPartition && pl.ps % kRowsTile == 0 && most_parts >= kRowsMinPartitions &&
       est_units >= kRowsWorkgroups &&
       lgm::decode_rows_supported(act, cache, d.head_dim, d.num_kv_heads, G, d.block_size)) {
     // Whole-row kernel over equal runs of whole partitions, plain
     // ceil(L / ps) partitions (the ranges already balance the work).
     pl.rows = pl.rows_parts = true;
-    pl.HG = d.num_kv_heads % 8 == 0 ? 8 : 4;
+    pl.HG = rows_head_group(d.num_kv_heads, G);
     pl.parts = lgm::PartitionPlan{pl.ps, pl.ps};
     pl.P = pl.parts.max_count(max_ctx);
     const int64_t units = (int64_t)d.num_seqs * (d.num_kv_heads / pl.HG) * pl.P;

@@ -137,6 +137,11 @@ hipError_t launch_table_check(const int32_t* block_tables, const int32_t* contex
 hipError_t launch_paged_decode_mfma(const DecodeArgs& a, lgm_dtype cache, hipStream_t s);
 // Whole-row decode (matrix-core shapes with num_kv_heads % 4 == 0): equal
 // static tile ranges, one per workgroup, then a merge of the split streams.
+// Head groups of 8 kv heads only up to this many query heads per kv head
+// (the planner's rule; the kernel builds no 8-head shape past it).
+#ifndef LGM_ROWS_HG8_MAX_GROUP
+#define LGM_ROWS_HG8_MAX_GROUP 8
+#endif
 struct RowsArgs {
   int32_t num_wg;         // W: workgroups, one range each
   int32_t head_group;     // HG: kv heads per workgroup (8, or 4)

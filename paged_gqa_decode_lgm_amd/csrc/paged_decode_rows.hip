@@ -851,11 +851,10 @@ __global__ __launch_bounds__(kMergeThreads) void rows_merge_kernel(DecodeArgs p,
 // each within half the register file.  FP4 moves the fewest bytes per
 // instruction; with one wave per SIMD its dependency stalls were exposed, and
 // eight waves made it ~10% faster, while FP8 was ~2% slower with eight.
-// Groups of more than 11 query heads do not fit half the register file (the
-// eight-wave build spills 8 to 92 bytes per lane to scratch memory at
-// G = 12..16) and keep four waves of two heads: 150 against 154 us at
-// G = 16 (8 kv heads, 128 contexts of 1024..4096 tokens), the same time
-// within noise at G = 12.
+// Groups of more than 11 query heads would not fit half the register file
+// (the eight-wave build spills 8 to 92 bytes per lane to scratch memory at
+// G = 12..16) and keep four waves of two heads, should the head groups of 8
+// be widened past LGM_ROWS_HG8_MAX_GROUP.
 #ifndef LGM_FP4_EIGHT_WAVES
 #define LGM_FP4_EIGHT_WAVES 1
 #endif
@@ -868,7 +867,9 @@ constexpr bool two_waves_per_simd() {
 template <class C, int G>
 hipError_t launch_group(const DecodeArgs& a, const RowsArgs& r, hipStream_t s) {
   if (r.head_group == 8) {
-    if constexpr (two_waves_per_simd<C, G>())
+    if constexpr (G > LGM_ROWS_HG8_MAX_GROUP)
+      return hipErrorInvalidValue;  // the planner takes groups of 4 kv heads there
+    else if constexpr (two_waves_per_simd<C, G>())
       hipLaunchKernelGGL((paged_decode_rows_kernel<C, G, 1, 2 * kDecodeThreads>), dim3(r.num_wg),
                          dim3(2 * kDecodeThreads), 0, s, a, r);
     else

@@ -349,6 +349,13 @@ def test_row_plan_workspace_formula():
     assert L.lgm_paged_decode_workspace_size(d, 8192, 0, L.LGM_BF16) == want
     assert L.lgm_paged_decode_workspace_size(d, 8192, 0, L.LGM_FP8_E4M3) == want
     assert L.lgm_paged_decode_workspace_size(d, 8192, 0, L.LGM_FP4_E2M1) == want
+    # 8 kv heads in groups of 8 up to 8 query heads per kv head, in groups of 4 past that
+    g8 = dims(num_q_heads=64)
+    assert L.lgm_paged_decode_workspace_size(g8, 8192, 0, L.LGM_BF16) == (
+        SLOT + al(256 * 2 * 64 * 128 * 4) + al(256 * 2 * 64 * 4) + 2 * al(64 * 4))
+    g16 = dims(num_q_heads=128)
+    assert L.lgm_paged_decode_workspace_size(g16, 8192, 0, L.LGM_FP8_E4M3) == (
+        SLOT + al(256 * 2 * 64 * 128 * 4) + al(256 * 2 * 64 * 4) + 2 * al(128 * 4))
     # 8 streams x 4096 tiles, past the single-launch cap: 2 head groups of 4 x 4096 tiles, two a range
     long = dims(num_seqs=2, num_q_heads=16, num_kv_heads=4, max_blocks_per_seq=8192)
     W, rows = 256, 4 * 4
