@@ -193,15 +193,15 @@ lgm_status lgm_rope_kv_append(const void* qkv, int64_t qkv_row_stride, void* q_o
  *    workgroups over 256 compute units, counting a fixed cost of 128 tokens
  *    per workgroup; the workgroup that finishes a context's last partition
  *    merges that context by log-sum-exp.  Returns the partition;
- *  - other matrix-core shapes with num_kv_heads divisible by 4: returns 0.  The 32-token tiles of all
- *    contexts (per group of 8 kv heads when 8 divide num_kv_heads and
- *    num_q_heads / num_kv_heads is at most 8, else of 4) are cut into equal ranges, one
- *    per compute unit (256, fewer when a range would hold under 2 tiles);
- *    each workgroup reads whole KV rows of its head group, and contexts split
- *    between ranges are merged by log-sum-exp;
- *  - the remaining matrix-core shapes: the largest power of two from 64 to 4096
- *    tokens that still gives 2048 (sequence, partition, kv head) work items
- *    at max_context_len;
+ *  - larger jobs on the matrix-core shapes: returns 0.  The 32-token tiles
+ *    of all contexts, per head group (8 kv heads when 8 divide num_kv_heads
+ *    and num_q_heads / num_kv_heads is at most 8, else 4 when 4 divide it,
+ *    else 2 when 2 do, else 1), are cut into equal ranges, one per compute
+ *    unit (256, fewer when a range would hold under 2 tiles); each workgroup
+ *    reads whole KV rows of its head group (with a group of 2 or 1 kv heads
+ *    its four waves take each head's tiles in 2 or 4 interleaved slices and
+ *    combine them), and contexts split between ranges are merged by
+ *    log-sum-exp;
  *  - other shapes: a size that gives about 8192 workgroups.
  * How contexts are cut into partitions:
  *  - the whole-row partition plan, taken when the matrix-core shapes have

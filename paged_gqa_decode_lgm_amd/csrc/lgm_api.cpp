@@ -137,16 +137,9 @@ constexpr int kTailDivisor = LGM_TAIL_DIVISOR;
 constexpr int kMinAutoPartitionBlocks = 4;
 
 // Partition plan: returns the partition size in tokens, or -1 after setting the error.
-// Auto plan of the persistent matrix-core kernel: the largest power-of-two
-// partition (64 .. 4096 tokens) that still gives at least kAutoMinItems
-// (sequence, partition, kv head) items at the longest context, four per
-// workgroup of its grid on MI355X (256 CUs x 2): large partitions amortise
-// each item's start and merge, enough items keep the drain short.
-constexpr int64_t kAutoMinItems = 2048;
-constexpr int kAutoMaxPartition = 4096;
-constexpr int kAutoMinPartition = 64;
-
-int32_t resolve_partition(const char* fn, const lgm_paged_dims& d, int32_t max_ctx, int32_t ps, bool persistent) {
+// (partition_size 0 reaches here only for the vector-ALU shapes: the
+// matrix-core shapes take the single-launch or whole-row plan.)
+int32_t resolve_partition(const char* fn, const lgm_paged_dims& d, int32_t max_ctx, int32_t ps) {
   if (ps < 0) {
     fail(LGM_ERR_INVALID_ARGUMENT, fn, "partition_size = %d must be 0 (library chooses) or positive", ps);
     return -1;
@@ -157,16 +150,7 @@ int32_t resolve_partition(const char* fn, const lgm_paged_dims& d, int32_t max_c
     return -1;
   }
   const int64_t cap = ((int64_t)(max_ctx > 0 ? max_ctx : 1) + d.block_size - 1) / d.block_size * d.block_size;
-  if (ps == 0 && persistent) {
-    const int64_t units = (int64_t)(d.num_seqs > 0 ? d.num_seqs : 1) * d.num_kv_heads;
-    ps = kAutoMinPartition;
-    for (int64_t p = kAutoMaxPartition; p > kAutoMinPartition; p /= 2) {
-      if (units * ((cap + p - 1) / p) >= kAutoMinItems) {
-        ps = (int32_t)p;
-        break;
-      }
-    }
-  } else if (ps == 0) {
+  if (ps == 0) {
     // Enough partitions that the grid holds ~kAutoTargetWorkgroups workgroups
     // at the longest context, but never fewer than 4 blocks (one per wave).
     const int64_t units = (int64_t)(d.num_seqs > 0 ? d.num_seqs : 1) * d.num_kv_heads;
@@ -191,7 +175,9 @@ constexpr size_t kCounterSlot = LGM_COUNTER_SLOT_BYTES;  // the counters at the 
 // and no plan puts anything else there, so one zero-filled workspace may
 // serve calls on any plan in turn.  The plan's own regions follow.
 // kv heads per whole-row workgroup: 8 (whole NHD rows) when they divide the
-// kv heads and the group has at most 8 query heads per kv head, else 4.  A
+// kv heads and the group has at most 8 query heads per kv head, else 4, else
+// (2 or 1, whole rows of 2 or 1 kv heads) as many as divide the kv heads,
+// each head's tiles then dealt to 2 or 4 waves in token slices.  A
 // segment's staged query rows and results grow with G (128 rows of 272 +
 // 512 bytes at G = 16 and 8 heads), and past 8 a batch holds a single
 // segment, so a range's second segment waits for the first one's flush and
@@ -199,13 +185,15 @@ constexpr size_t kCounterSlot = LGM_COUNTER_SLOT_BYTES;  // the counters at the 
 // heads per workgroup): bf16 200 vs 206 us (64 contexts of 512..8192), FP8
 // 139-141 vs 147 us (128 of 1024..4096); at G = 8 FP8 was 1.5% slower with 4.
 static int rows_head_group(int num_kv_heads, int G) {
-  return num_kv_heads % 8 == 0 && G <= LGM_ROWS_HG8_MAX_GROUP ? 8 : 4;
+  if (num_kv_heads % 8 == 0 && G <= LGM_ROWS_HG8_MAX_GROUP) return 8;
+  if (num_kv_heads % 4 == 0) return 4;
+  return num_kv_heads % 2 == 0 ? 2 : 1;
 }
 
 struct Plan {
   bool fused;       // single-launch split kernel (small jobs): partitions of ps tokens, merged in the launch
-  bool rows;        // whole-row kernel (Hkv % 4 == 0): equal tile ranges (partition_size 0) ...
-  bool rows_parts;  // ... or equal runs of whole partitions (an explicit partition_size of whole tiles)
+  bool rows;        // whole-row kernel: equal tile ranges (partition_size 0) ...
+  bool rows_parts;  // ... or (Hkv % 4 == 0) equal runs of whole partitions (an explicit partition_size of whole tiles)
   lgm::PartitionPlan parts;
   int32_t ps, P;
   size_t counters_bytes, part_out_bytes, part_lse_bytes;
@@ -340,12 +328,12 @@ lgm_status plan_decode(const char* fn, const lgm_paged_dims& d, int32_t max_ctx,
     pl.total = pl.counters_bytes + pl.rec_out_bytes + pl.rec_lse_bytes + 2 * pl.stream_bytes;
     return LGM_OK;
   }
-  pl.ps = resolve_partition(fn, d, max_ctx, ps_arg, persistent);
+  pl.ps = resolve_partition(fn, d, max_ctx, ps_arg);
   if (pl.ps < 0) return LGM_ERR_INVALID_ARGUMENT;
   const int32_t most_parts = (int32_t)(((int64_t)max_ctx + pl.ps - 1) / pl.ps);
   const int64_t est_units = (int64_t)d.num_seqs * (d.num_kv_heads / rows_head_group(d.num_kv_heads, G)) * most_parts;
   if (ps_arg > 0 && pl.ps >= kRowsMinPartition && pl.ps % kRowsTile == 0 && most_parts >= kRowsMinPartitions &&
-      est_units >= kRowsWorkgroups &&
+      est_units >= kRowsWorkgroups && d.num_kv_heads % 4 == 0 &&
       lgm::decode_rows_supported(act, cache, d.head_dim, d.num_kv_heads, G, d.block_size)) {
     // Whole-row kernel over equal runs of whole partitions, plain
     // ceil(L / ps) partitions (the ranges already balance the work).

@@ -135,8 +135,8 @@ hipError_t launch_table_check(const int32_t* block_tables, const int32_t* contex
 
 // Matrix-core decode for bf16 activations with bf16 / FP8 caches, head_dim 128.
 hipError_t launch_paged_decode_mfma(const DecodeArgs& a, lgm_dtype cache, hipStream_t s);
-// Whole-row decode (matrix-core shapes with num_kv_heads % 4 == 0): equal
-// static tile ranges, one per workgroup, then a merge of the split streams.
+// Whole-row decode (matrix-core shapes): equal static tile ranges, one per
+// workgroup, then a merge of the split streams.
 // Head groups of 8 kv heads only up to this many query heads per kv head
 // (the planner's rule; the kernel builds no 8-head shape past it).
 #ifndef LGM_ROWS_HG8_MAX_GROUP
@@ -144,7 +144,7 @@ hipError_t launch_paged_decode_mfma(const DecodeArgs& a, lgm_dtype cache, hipStr
 #endif
 struct RowsArgs {
   int32_t num_wg;         // W: workgroups, one range each
-  int32_t head_group;     // HG: kv heads per workgroup (8, or 4)
+  int32_t head_group;     // HG: kv heads per workgroup (8 or 4; 2 or 1 with 2 or 4 token slices per head)
   float* rec_out;         // [W][2][HG * G][D] normalised partial outputs
   float* rec_lse;         // [W][2][HG * G] natural-log LSEs
   int32_t* wg_first;  // [B * Hkv / HG] record slot of the stream's first piece (2w or 2w + 1 for range w)

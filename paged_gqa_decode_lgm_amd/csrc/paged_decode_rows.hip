@@ -1,6 +1,6 @@
 // Paged GQA decode attention over whole KV token rows, for gfx950 matrix
 // cores: bf16 activations, bf16, FP8 E4M3 or FP4 E2M1 (E8M0 block scales)
-// caches, head_dim 128, block_size 16, a kv head count divisible by 4.
+// caches, head_dim 128, block_size 16, any kv head count.
 //
 // The split-K method of paged_decode.hip (mainarch README, decode-attention
 // section; Loom Kernels README, "Attention" row) with the work laid out for
@@ -10,7 +10,11 @@
 // every row leave the rest of each DRAM page to other workgroups at other
 // times; here one workgroup covers a group of HG = 8 (or 4) kv heads, its four
 // waves taking 2 (or 1) heads each, so the workgroup reads whole rows and
-// whole blocks.
+// whole blocks.  With 2 or 1 kv heads in all (or a count that 4 does not
+// divide) the group is 2 or 1 heads and each head's steps are dealt to 2 or
+// 4 waves in interleaved token slices (steps slice, slice + SL, ...), whose
+// partial results the workgroup combines by log-sum-exp when it writes them:
+// the workgroup still reads whole rows and the wave's pipeline is the same.
 //
 // The work is the flattened list of 32-token tiles of all streams (a stream
 // is one sequence's tiles for one head group), cut into as many equal ranges
@@ -19,8 +23,8 @@
 // the end of one stream, whole streams, and the start of another; a stream
 // that lies inside one range is written directly, the pieces of a split
 // stream go to two record slots per workgroup and are merged by log-sum-exp
-// afterwards (rows_merge_kernel).  Since each wave owns its heads for the
-// whole range, no wave ever waits for another.
+// afterwards (rows_merge_kernel).  Since each wave owns its heads (and token
+// slice) for the whole range, no wave ever waits for another.
 //
 // Per tile a wave computes scores S^T = K Q^T and O += P V on
 // v_mfma_f32_16x16x32_bf16 exactly as the partition kernel does (operand
@@ -56,17 +60,18 @@ struct SegDesc {
 // on 128 FP8 contexts of 1024..4096 tokens, measured with per-workgroup
 // timestamps.)  A batch holds as many segments as ~108 KB of LDS allow; the
 // FP8 kernel's K staging (32 KB, below) takes part of the rest.
-template <int G, int HG>
+template <int G, int HG, int SL>
 struct Batch {
   static constexpr int kQRow = kD + 8;  // bf16 per staged query row; the pad spreads rows over LDS banks
-  static constexpr int kPerSeg = HG * G * (kQRow * 2 + kD * 4 + 12) + kStageWin * 2 * kWin * 4 + 2 * HG * 4 + 32;
+  static constexpr int kPerSeg =
+      HG * G * kQRow * 2 + SL * HG * G * (kD * 4 + 12) + kStageWin * 2 * kWin * 4 + 2 * HG * 4 + 32;
   static constexpr int kFit = 108000 / kPerSeg;
   static constexpr int kMax = kFit > 16 ? 16 : (kFit < 1 ? 1 : kFit);
 };
 
-template <int G, int HG>
+template <int G, int HG, int SL>
 struct RowsSmem {
-  using B = Batch<G, HG>;
+  using B = Batch<G, HG, SL>;
   int pre[kChunk + 1];  // tiles of the streams of sequences b0 .. b0 + j - 1
   int wave_sum[kMaxRowWaves];
   SegDesc seg[B::kMax];
@@ -74,14 +79,14 @@ struct RowsSmem {
   float kscale[B::kMax][HG];
   float vscale[B::kMax][HG];
   uint16_t q[B::kMax][HG * G][B::kQRow];
-  // Results, row = local kv head * G + query head of the group: the
-  // accumulators and, per row, the rounded-probability sum (psum), the fp32
-  // sum (le) and the reference (ms) they are relative to; the flush
-  // normalises them.
-  float out[B::kMax][HG * G][kD];
-  float psum[B::kMax][HG * G];
-  float le[B::kMax][HG * G];
-  float ms[B::kMax][HG * G];
+  // Results, row = (token slice * HG + local kv head) * G + query head of
+  // the group: the accumulators and, per row, the rounded-probability sum
+  // (psum), the fp32 sum (le) and the reference (ms) they are relative to;
+  // the flush combines a head's slices and normalises them.
+  float out[B::kMax][SL * HG * G][kD];
+  float psum[B::kMax][SL * HG * G];
+  float le[B::kMax][SL * HG * G];
+  float ms[B::kMax][SL * HG * G];
 };
 
 __device__ __forceinline__ int clamped_ctx(const DecodeArgs& p, int b) {
@@ -219,8 +224,8 @@ __device__ __forceinline__ void row_load_v(const DecodeArgs& p, int g, const int
 // holds O[row 4kg + j][8n + i], rows 0 .. G - 1 of local kv head hl), the
 // rounded-probability sums (psum[j] of lane group kg: row 4kg + j), and the
 // fp32 sum and reference of head n (lane n).  No lane exchange is needed.
-template <int G, int HG>
-__device__ __forceinline__ void stage_head(RowsSmem<G, HG>& sm, int s, int hl, const WaveState& st, int lane) {
+template <int G, int HG, int SL>
+__device__ __forceinline__ void stage_head(RowsSmem<G, HG, SL>& sm, int s, int hl, const WaveState& st, int lane) {
   const int n = lane & 15, kg = lane >> 4;
   const float lsum_e = sum4(st.lsum_e);
 #pragma unroll
@@ -245,14 +250,17 @@ __device__ __forceinline__ void stage_head(RowsSmem<G, HG>& sm, int s, int hl, c
 // and out_lse when the segment is its whole stream, else to its record: a
 // split-K partition record ([B][Hq][P][D], [B][Hq][P]) in partition mode, or
 // the range's record slot.  Eight columns per lane; a wave reads all its
-// rows of a pass from LDS before it stores any.
-template <class C, int G, int HG, int NT>
-__device__ __forceinline__ void flush_batch(const DecodeArgs& p, const RowsArgs& r, const RowsSmem<G, HG>& sm,
+// rows of a pass from LDS before it stores any.  With SL token slices per
+// head a row's SL partial results (each relative to its own reference ms)
+// are first combined by log-sum-exp weights 2^(ms_i - max ms); a slice that
+// saw no token (le = 0) weighs nothing.
+template <class C, int G, int HG, int SL, int NT>
+__device__ __forceinline__ void flush_batch(const DecodeArgs& p, const RowsArgs& r, const RowsSmem<G, HG, SL>& sm,
                                             int nseg, int wave, int lane) {
   constexpr int kRows = HG * G;
   constexpr int kCh = kD / 8;
   constexpr int kItems = kRows * kCh;               // 8-column pieces per segment
-  constexpr int kPass = 8;                          // pieces per lane per pass
+  constexpr int kPass = 8 / SL;                     // pieces per lane per pass
   constexpr int kPerPass = kPass * kWaveSize;
   for (int s = wave; s < nseg; s += NT / kWaveSize) {
     const SegDesc d = read_seg(sm, s);
@@ -263,11 +271,38 @@ __device__ __forceinline__ void flush_batch(const DecodeArgs& p, const RowsArgs&
       for (int k = 0; k < kPass; ++k) {
         const int i = i0 + k * kWaveSize + lane;
         const int row = (i < kItems ? i : 0) / kCh, c = (i < kItems ? i : 0) % kCh;
-        v0[k] = *reinterpret_cast<const float4*>(&sm.out[s][row][8 * c]);
-        v1[k] = *reinterpret_cast<const float4*>(&sm.out[s][row][8 * c + 4]);
-        L[k] = sm.psum[s][row];
-        Le[k] = sm.le[s][row];
-        M[k] = sm.ms[s][row];
+        if constexpr (SL == 1) {
+          v0[k] = *reinterpret_cast<const float4*>(&sm.out[s][row][8 * c]);
+          v1[k] = *reinterpret_cast<const float4*>(&sm.out[s][row][8 * c + 4]);
+          L[k] = sm.psum[s][row];
+          Le[k] = sm.le[s][row];
+          M[k] = sm.ms[s][row];
+        } else {
+          float le[SL], ms[SL], mx = -INFINITY;
+#pragma unroll
+          for (int q = 0; q < SL; ++q) {
+            le[q] = sm.le[s][q * kRows + row];
+            ms[q] = sm.ms[s][q * kRows + row];
+            if (le[q] > 0.f) mx = fmaxf(mx, ms[q]);
+          }
+          float4 a0 = make_float4(0.f, 0.f, 0.f, 0.f), a1 = a0;
+          float ps = 0.f, ls = 0.f;
+#pragma unroll
+          for (int q = 0; q < SL; ++q) {
+            const float w = le[q] > 0.f ? fast_exp2(ms[q] - mx) : 0.f;
+            const float4 x0 = *reinterpret_cast<const float4*>(&sm.out[s][q * kRows + row][8 * c]);
+            const float4 x1 = *reinterpret_cast<const float4*>(&sm.out[s][q * kRows + row][8 * c + 4]);
+            a0 = make_float4(fmaf(w, x0.x, a0.x), fmaf(w, x0.y, a0.y), fmaf(w, x0.z, a0.z), fmaf(w, x0.w, a0.w));
+            a1 = make_float4(fmaf(w, x1.x, a1.x), fmaf(w, x1.y, a1.y), fmaf(w, x1.z, a1.z), fmaf(w, x1.w, a1.w));
+            ps = fmaf(w, sm.psum[s][q * kRows + row], ps);
+            ls = fmaf(w, le[q], ls);
+          }
+          v0[k] = a0;
+          v1[k] = a1;
+          L[k] = ps;
+          Le[k] = ls;
+          M[k] = mx;
+        }
         vsc[k] = C::kFp8 ? sm.vscale[s][row / G] : 1.f;
       }
 #pragma unroll
@@ -323,8 +358,8 @@ constexpr int row_sets() {
                                          : (std::is_same<C, MfmaFP4>::value ? LGM_ROW_SETS_FP4 : LGM_ROW_SETS_BF16);
 }
 
-template <int G, int HG>
-__device__ __forceinline__ SegDesc read_seg(const RowsSmem<G, HG>& sm, int s) {
+template <class SM>
+__device__ __forceinline__ SegDesc read_seg(const SM& sm, int s) {
   SegDesc d;
   d.b = __builtin_amdgcn_readfirstlane(sm.seg[s].b);
   d.ctx = __builtin_amdgcn_readfirstlane(sm.seg[s].ctx);
@@ -342,8 +377,9 @@ __device__ __forceinline__ SegDesc read_seg(const RowsSmem<G, HG>& sm, int s) {
 // segment's block ids, its query rows and, for FP8, the head group's K and V
 // scales.  A wave issues all its loads before it stores any of them to LDS,
 // so the batch costs one memory round trip.
-template <class C, int G, int HG, int NT>
-__device__ __forceinline__ void stage_batch(const DecodeArgs& p, RowsSmem<G, HG>& sm, int nseg, int wave, int lane) {
+template <class C, int G, int HG, int SL, int NT>
+__device__ __forceinline__ void stage_batch(const DecodeArgs& p, RowsSmem<G, HG, SL>& sm, int nseg, int wave,
+                                            int lane) {
   constexpr int kIdsPer = kStageWin * 2 * kWin / kWaveSize;  // ids per lane
   constexpr int kRows = HG * G;
   constexpr int kQCh = kRows * (kD / 8);                     // 16-byte query chunks per segment
@@ -411,8 +447,8 @@ __device__ __forceinline__ void stage_batch(const DecodeArgs& p, RowsSmem<G, HG>
 
 // Query rows of kv head `hl` (inside the head group) of staged segment s as
 // the B operand of the score MFMAs (zero for n >= G).
-template <class C, int G, int HG>
-__device__ __forceinline__ void lds_q_operand(const RowsSmem<G, HG>& sm, int s, int hl, short8 (&qb)[4], int n,
+template <class C, int G, int HG, int SL>
+__device__ __forceinline__ void lds_q_operand(const RowsSmem<G, HG, SL>& sm, int s, int hl, short8 (&qb)[4], int n,
                                               int kg) {
   const uint16_t* row = sm.q[s][hl * G + (n < G ? n : 0)];
 #pragma unroll
@@ -438,21 +474,27 @@ __device__ __forceinline__ void lds_q_operand(const RowsSmem<G, HG>& sm, int s, 
 // from LDS.  Segments without tiles (empty contexts) write out = 0 and
 // lse = -inf.  Pairs past the batch are absent: their loads return zeros
 // without touching memory.
-template <class C, int G, int HG, int HPW>
-__device__ __forceinline__ void run_batch(const DecodeArgs& p, RowsSmem<G, HG>& sm, int nseg, int wave, int lane,
+template <class C, int G, int HG, int HPW, int SL>
+__device__ __forceinline__ void run_batch(const DecodeArgs& p, RowsSmem<G, HG, SL>& sm, int nseg, int wave, int lane,
                                           uint8_t* kst) {
   constexpr int NB = step_blocks<C>();
   constexpr int ST = NB / 2;  // tiles per step
   constexpr int NS = row_sets<C>();
   static_assert(NS % HPW == 0, "a set must stay on one head");
-  static_assert(kWin % ST == 0, "a step's tiles share one window of block ids");
+  static_assert(kWin % ST == 0 && SL * ST <= kWin, "a step's tiles share one window of block ids");
+  static_assert(SL == 1 || HPW == 1, "token slices take one head per wave");
   const int n = lane & 15, kg = lane >> 4;
+  // The wave's heads (hl0 .. hl0 + HPW - 1 of the group) and its token
+  // slice: it takes the segment's steps slice, slice + SL, ...
+  const int hl0 = (wave % (HG / HPW)) * HPW;
+  const int slice = wave / (HG / HPW);
   auto nsteps_of = [&](int s) {
-    return __builtin_amdgcn_readfirstlane((sm.seg[s].et - sm.seg[s].lt + ST - 1) / ST);
+    const int all = (sm.seg[s].et - sm.seg[s].lt + ST - 1) / ST;
+    return __builtin_amdgcn_readfirstlane(all > slice ? (all - slice + SL - 1) / SL : 0);
   };
 
   // ---- load cursor: segment ls, step lk (ls == nseg: past the batch) ----
-  int ls = 0, lk = 0, lwin = 0, l_nsteps = 0, l_b = 0, l_lt = 0, l_et = 0, l_lbend = 0, l_g0 = wave * HPW;
+  int ls = 0, lk = 0, lwin = 0, l_nsteps = 0, l_b = 0, l_lt = 0, l_et = 0, l_lbend = 0, l_g0 = hl0;
   int lids = -1, lnext = -1;
   // Windows 0 .. kStageWin - 1 come from LDS; a longer segment's later
   // windows are read from the table one window ahead.
@@ -475,13 +517,13 @@ __device__ __forceinline__ void run_batch(const DecodeArgs& p, RowsSmem<G, HG>& 
     l_lt = d.lt;
     l_et = d.et;
     l_lbend = (d.ctx + kBS - 1) / kBS;
-    l_g0 = d.hg * HG + wave * HPW;
+    l_g0 = d.hg * HG + hl0;
     l_window(0);
   };
   auto l_advance = [&]() {
     if (ls >= nseg) return;
     if (++lk < l_nsteps) {
-      if ((ST * lk) / kWin != lwin) l_window(++lwin);
+      if ((ST * (slice + SL * lk)) / kWin != lwin) l_window(++lwin);
       return;
     }
     int s = ls + 1;
@@ -490,7 +532,7 @@ __device__ __forceinline__ void run_batch(const DecodeArgs& p, RowsSmem<G, HG>& 
     else ls = nseg;
   };
   auto l_ids = [&](int (&id)[NB]) {
-    const int kt = ST * lk - kWin * lwin;  // first tile of the step inside its window
+    const int kt = ST * (slice + SL * lk) - kWin * lwin;  // first tile of the step inside its window
 #pragma unroll
     for (int t = 0; t < ST; ++t) {
       id[2 * t] = ls < nseg ? __builtin_amdgcn_readlane(lids, 2 * (kt + t)) : -1;
@@ -513,7 +555,7 @@ __device__ __forceinline__ void run_batch(const DecodeArgs& p, RowsSmem<G, HG>& 
     WaveState e;
     e.reset();
 #pragma unroll
-    for (int hh = 0; hh < HPW; ++hh) stage_head<G, HG>(sm, s, wave * HPW + hh, e, lane);
+    for (int hh = 0; hh < HPW; ++hh) stage_head<G, HG, SL>(sm, s, wave * HPW + hh, e, lane);
   };
   auto c_enter = [&](int s) {
     const SegDesc d = read_seg(sm, s);
@@ -524,9 +566,9 @@ __device__ __forceinline__ void run_batch(const DecodeArgs& p, RowsSmem<G, HG>& 
     c_ctx = d.ctx;
 #pragma unroll
     for (int hh = 0; hh < HPW; ++hh) {
-      lds_q_operand<C, G, HG>(sm, s, wave * HPW + hh, qb[hh], n, kg);
+      lds_q_operand<C, G, HG, SL>(sm, s, hl0 + hh, qb[hh], n, kg);
       float c = p.softmax_scale * kLog2e;
-      if constexpr (C::kFp8) c *= sm.kscale[s][wave * HPW + hh];
+      if constexpr (C::kFp8) c *= sm.kscale[s][hl0 + hh];
       csc[hh] = fold_score_scale(c, qb[hh]);
       st[hh].reset();
     }
@@ -571,13 +613,14 @@ __device__ __forceinline__ void run_batch(const DecodeArgs& p, RowsSmem<G, HG>& 
       } else {
         row_load_k<C, NB>(p, lg, nid, lane, sr[j]);
       }
-      step_update<C, NB>(st[h], sr[j], sc, csc[h], valid_bits(pid[j]), kTile * (c_lt + ST * ck), c_ctx, kg);
+      step_update<C, NB>(st[h], sr[j], sc, csc[h], valid_bits(pid[j]), kTile * (c_lt + ST * (slice + SL * ck)),
+                         c_ctx, kg);
       row_load_v<C, NB>(p, lg, nid, lane, sr[j]);
 #pragma unroll
       for (int bb = 0; bb < NB; ++bb) pid[j][bb] = nid[bb];
       if (h == HPW - 1 && ++ck == c_nsteps) {  // the segment is done: write it, move to the next
 #pragma unroll
-        for (int hh = 0; hh < HPW; ++hh) stage_head<G, HG>(sm, cs, wave * HPW + hh, st[hh], lane);
+        for (int hh = 0; hh < HPW; ++hh) stage_head<G, HG, SL>(sm, cs, wave * HPW + hh, st[hh], lane);
         int s = cs + 1;
         while (s < nseg && nsteps_of(s) == 0) write_empty(s++);
         if (s >= nseg) done = true;
@@ -631,11 +674,12 @@ constexpr int seg_cost() {
 // it merges a record of weight zero there.  In partition mode every
 // partition of a split context writes its own record, at its index.  The
 // range's segments are located, staged and run in batches.
-template <class C, int G, int HPW, int NT>
+template <class C, int G, int HPW, int NT, int SL = 1>
 __global__ __launch_bounds__(NT, 1) void paged_decode_rows_kernel(DecodeArgs p, RowsArgs r) {
-  constexpr int HG = NT / kWaveSize * HPW;
-  using Bt = Batch<G, HG>;
-  __shared__ RowsSmem<G, HG> sm;
+  constexpr int HG = NT / kWaveSize * HPW / SL;
+  static_assert(HG * SL == NT / kWaveSize * HPW, "whole waves per token slice");
+  using Bt = Batch<G, HG, SL>;
+  __shared__ RowsSmem<G, HG, SL> sm;
   constexpr int kKStage = C::kFp8 ? row_sets<C>() * step_blocks<C>() * kKStageBlock : 0;  // per wave
   __shared__ __attribute__((aligned(16))) uint8_t kst[kKStage > 0 ? NT / kWaveSize * kKStage : 16];
   const int lane = threadIdx.x & (kWaveSize - 1);
@@ -708,11 +752,11 @@ __global__ __launch_bounds__(NT, 1) void paged_decode_rows_kernel(DecodeArgs p, 
       ++nseg;
     }
     __syncthreads();  // the batch's descriptors
-    stage_batch<C, G, HG, NT>(p, sm, nseg, wave, lane);
+    stage_batch<C, G, HG, SL, NT>(p, sm, nseg, wave, lane);
     __syncthreads();  // the batch's ids, query rows and scales
-    run_batch<C, G, HG, HPW>(p, sm, nseg, wave, lane, kst + wave * kKStage);
+    run_batch<C, G, HG, HPW, SL>(p, sm, nseg, wave, lane, kst + wave * kKStage);
     __syncthreads();  // every wave has staged its results
-    flush_batch<C, G, HG, NT>(p, r, sm, nseg, wave, lane);
+    flush_batch<C, G, HG, SL, NT>(p, r, sm, nseg, wave, lane);
     __syncthreads();  // the batch is written before the next one is staged
   }
   // A range without a unit (more workgroups than units, or only streams'
@@ -875,9 +919,18 @@ hipError_t launch_group(const DecodeArgs& a, const RowsArgs& r, hipStream_t s) {
     else
       hipLaunchKernelGGL((paged_decode_rows_kernel<C, G, 2, kDecodeThreads>), dim3(r.num_wg), dim3(kDecodeThreads),
                          0, s, a, r);
-  } else
+  } else if (r.head_group == 4) {
     hipLaunchKernelGGL((paged_decode_rows_kernel<C, G, 1, kDecodeThreads>), dim3(r.num_wg), dim3(kDecodeThreads), 0,
                        s, a, r);
+  } else if (r.head_group == 2) {  // two token slices per head
+    hipLaunchKernelGGL((paged_decode_rows_kernel<C, G, 1, kDecodeThreads, 2>), dim3(r.num_wg), dim3(kDecodeThreads),
+                       0, s, a, r);
+  } else if (r.head_group == 1) {  // four token slices
+    hipLaunchKernelGGL((paged_decode_rows_kernel<C, G, 1, kDecodeThreads, 4>), dim3(r.num_wg), dim3(kDecodeThreads),
+                       0, s, a, r);
+  } else {
+    return hipErrorInvalidValue;
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || r.part_tiles > 0) return e;  // partition records are merged by lse_merge
   // Short contexts: when every context fits one tile, no stream is split
@@ -908,7 +961,7 @@ hipError_t dispatch(const DecodeArgs& a, const RowsArgs& r, int G, hipStream_t s
 
 bool decode_rows_supported(lgm_dtype act, lgm_dtype cache, int head_dim, int num_kv_heads, int group,
                            int block_size) {
-  return decode_mfma_supported(act, cache, head_dim, group, block_size) && num_kv_heads % 4 == 0;
+  return decode_mfma_supported(act, cache, head_dim, group, block_size) && num_kv_heads >= 1;
 }
 
 hipError_t launch_paged_decode_rows(const DecodeArgs& a, const RowsArgs& r, lgm_dtype cache, hipStream_t s) {

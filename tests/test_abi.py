@@ -259,18 +259,19 @@ def test_attention_static_empty_batch_is_a_noop():
 
 # ------------------------------------------------------------------ plan queries
 @pytest.mark.parametrize("d,max_ctx,ps,want", [
-    (dims(), 8192, 0, 0),                                                 # whole-row ranges (Hkv % 4 == 0)
+    (dims(), 8192, 0, 0),                                                 # whole-row ranges
     (dims(num_seqs=128, max_blocks_per_seq=256), 4096, 0, 0),
     (dims(num_seqs=4, max_blocks_per_seq=8192), 131072, 0, 0),
-    (dims(num_q_heads=16, num_kv_heads=2), 8192, 0, 512),                 # work queue: >= 2048 items
-    (dims(num_q_heads=24, num_kv_heads=6), 8192, 0, 1024),
-    (dims(num_seqs=256, num_q_heads=16, num_kv_heads=2), 8192, 0, 2048),
+    (dims(num_q_heads=16, num_kv_heads=2), 8192, 0, 0),                   # head groups of 2: token slices
+    (dims(num_q_heads=24, num_kv_heads=6), 8192, 0, 0),
+    (dims(num_seqs=256, num_q_heads=16, num_kv_heads=2), 8192, 0, 0),
+    (dims(num_seqs=128, num_q_heads=8, num_kv_heads=1), 8192, 0, 0),      # head groups of 1
     # single launch (<= 1022 streams, <= 16384 tiles): partitions that balance the workgroups, 128-token steps
     (dims(num_seqs=2, num_q_heads=12, num_kv_heads=2, max_blocks_per_seq=128), 2048, 0, 128),
     (dims(num_seqs=1, max_blocks_per_seq=512), 8192, 0, 256),             # 8 streams x 256 tiles
     (dims(num_seqs=1, num_q_heads=4, num_kv_heads=1, max_blocks_per_seq=4096), 65536, 0, 1024),  # <= 64 per context
     (dims(num_seqs=1022, num_q_heads=16, num_kv_heads=1, max_blocks_per_seq=8), 100, 0, 128),
-    (dims(num_seqs=1023, num_q_heads=16, num_kv_heads=1, max_blocks_per_seq=8), 100, 0, 64),  # 1023 streams: work queue
+    (dims(num_seqs=1023, num_q_heads=16, num_kv_heads=1, max_blocks_per_seq=8), 100, 0, 0),  # 1023 streams: ranges
     (dims(num_seqs=1, max_blocks_per_seq=4096), 65536, 0, 2048),          # 8 x 2048 = 16384 tiles
     (dims(num_seqs=1, max_blocks_per_seq=4098), 65537, 0, 0),             # 8 x 2049 tiles: whole-row ranges
     (dims(head_dim=64), 8192, 0, 512),                                    # vector-ALU shape
@@ -349,6 +350,13 @@ def test_row_plan_workspace_formula():
     assert L.lgm_paged_decode_workspace_size(d, 8192, 0, L.LGM_BF16) == want
     assert L.lgm_paged_decode_workspace_size(d, 8192, 0, L.LGM_FP8_E4M3) == want
     assert L.lgm_paged_decode_workspace_size(d, 8192, 0, L.LGM_FP4_E2M1) == want
+    # 2 and 1 kv heads: head groups of 2 and 1 (HG * G rows per record)
+    h2 = dims(num_q_heads=16, num_kv_heads=2)
+    assert L.lgm_paged_decode_workspace_size(h2, 8192, 0, L.LGM_BF16) == (
+        SLOT + al(256 * 2 * 16 * 128 * 4) + al(256 * 2 * 16 * 4) + 2 * al(64 * 4))
+    h1 = dims(num_seqs=128, num_q_heads=8, num_kv_heads=1)
+    assert L.lgm_paged_decode_workspace_size(h1, 8192, 0, L.LGM_FP4_E2M1) == (
+        SLOT + al(256 * 2 * 8 * 128 * 4) + al(256 * 2 * 8 * 4) + 2 * al(128 * 4))
     # 8 kv heads in groups of 8 up to 8 query heads per kv head, in groups of 4 past that
     g8 = dims(num_q_heads=64)
     assert L.lgm_paged_decode_workspace_size(g8, 8192, 0, L.LGM_BF16) == (

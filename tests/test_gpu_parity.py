@@ -419,6 +419,23 @@ def test_row_plan_ragged_edges(cache, hkv, G):
     _run_and_check(cfg)
 
 
+@pytest.mark.parametrize("cache", ["bf16", "fp8", "fp4"])
+@pytest.mark.parametrize("hkv,G", [(2, 6), (1, 8), (6, 4), (1, 16), (2, 1), (3, 5)])
+def test_row_plan_token_slices(cache, hkv, G):
+    """Whole-row ranges over head groups of 2 and 1 kv heads (num_kv_heads
+    not divisible by 4): each head's steps are dealt to 2 or 4 waves in
+    interleaved token slices whose partial results the flush combines.
+    Contexts shorter than the slices (slices that see no token), step counts
+    that are no multiple of the slice count, and a long context split across
+    ranges; enough sequences to pass the single-launch caps."""
+    ctx = EDGE_CTX * 7 + (16384,)
+    cfg = W.Config(f"slices_{cache}_H{hkv}_G{G}", seed=18, num_seqs=len(ctx), num_q_heads=hkv * G,
+                   num_kv_heads=hkv, head_dim=128, block_size=16, act="bf16", cache=cache, ctx=0, rope_theta=1e4,
+                   partition_size=0, append=True, ctx_list=ctx)
+    assert len(ctx) * hkv * 16384 // 32 > 32768
+    _run_and_check(cfg)
+
+
 # ------------------------------------------------------------------ single-launch plan
 # partition_size 0 with at most 1022 (sequence, kv head) streams and at most 16384
 # 32-token tiles over them (32768 for FP8): one launch, partitions of whole
@@ -766,7 +783,7 @@ def test_contract_variants(cache, layout, rope_style, per_tensor, ps, hkv, G):
 
 # ------------------------------------------------------------------ whole-row partition plan
 @pytest.mark.parametrize("cache", ["bf16", "fp8", "fp4"])
-@pytest.mark.parametrize("hkv,G,ps", [(8, 4, 256), (4, 4, 256), (16, 2, 512)])
+@pytest.mark.parametrize("hkv,G,ps", [(8, 4, 256), (4, 4, 256), (16, 2, 512), (8, 16, 256)])
 def test_row_partition_plan_ragged_edges(cache, hkv, G, ps):
     """Explicit partition sizes of whole tiles (>= 256 tokens) on whole-row
     shapes with a long context (>= 64 partitions) in the batch: equal runs of
