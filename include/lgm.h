@@ -205,10 +205,10 @@ lgm_status lgm_rope_kv_append(const void* qkv, int64_t qkv_row_stride, void* q_o
  *  - other shapes: a size that gives about 8192 workgroups.
  * How contexts are cut into partitions:
  *  - the whole-row partition plan, taken when the matrix-core shapes have
- *    num_kv_heads divisible by 4 and an explicit partition_size that is a
+ *    an even num_kv_heads and an explicit partition_size that is a
  *    multiple of 32 and at least 256 tokens, max_context_len holds at least
- *    64 partitions and the batch at least 256 (sequence, head group of 8 or
- *    4 kv heads as above, partition) units: plain ceil(L / partition) partitions, run
+ *    64 partitions and the batch at least 256 (sequence, head group as
+ *    above, partition) units: plain ceil(L / partition) partitions, run
  *    in equal numbers of whole partitions per workgroup (256 workgroups of
  *    whole KV rows);
  *  - every other partitioned plan: when max_context_len exceeds the
@@ -232,8 +232,8 @@ int32_t lgm_paged_decode_partition_size(lgm_paged_dims dims, int32_t max_context
  *    contexts are split, one record per (sequence, kv head, partition):
  *    fp32 outputs [B * Hkv][P][G][D], then natural-log LSEs [B * Hkv][P][G];
  *  - equal ranges (see lgm_paged_decode_partition_size): two records per
- *    range (fp32 outputs of the head group's Hq * 8 / Hkv or Hq * 4 / Hkv
- *    query heads, D each, and their natural-log LSEs; head groups as in
+ *    range (fp32 outputs of the head group's HG * Hq / Hkv query heads, D
+ *    each, and their natural-log LSEs; HG = 8, 4, 2 or 1 kv heads as in
  *    lgm_paged_decode_partition_size), then int32 context
  *    bookkeeping (two per context and head group);
  *  - partitions (the whole-row partition plan, the work-queue plan on the

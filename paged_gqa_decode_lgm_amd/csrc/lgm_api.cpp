@@ -193,7 +193,8 @@ static int rows_head_group(int num_kv_heads, int G) {
 struct Plan {
   bool fused;       // single-launch split kernel (small jobs): partitions of ps tokens, merged in the launch
   bool rows;        // whole-row kernel: equal tile ranges (partition_size 0) ...
-  bool rows_parts;  // ... or (Hkv % 4 == 0) equal runs of whole partitions (an explicit partition_size of whole tiles)
+  bool rows_parts;  // ... or equal runs of whole partitions (an explicit partition_size of whole tiles; an
+                    // even Hkv: four slices of one head's partition held up the 1-kv-head shape, 60 vs 54 us)
   lgm::PartitionPlan parts;
   int32_t ps, P;
   size_t counters_bytes, part_out_bytes, part_lse_bytes;
@@ -333,7 +334,7 @@ lgm_status plan_decode(const char* fn, const lgm_paged_dims& d, int32_t max_ctx,
   const int32_t most_parts = (int32_t)(((int64_t)max_ctx + pl.ps - 1) / pl.ps);
   const int64_t est_units = (int64_t)d.num_seqs * (d.num_kv_heads / rows_head_group(d.num_kv_heads, G)) * most_parts;
   if (ps_arg > 0 && pl.ps >= kRowsMinPartition && pl.ps % kRowsTile == 0 && most_parts >= kRowsMinPartitions &&
-      est_units >= kRowsWorkgroups && d.num_kv_heads % 4 == 0 &&
+      est_units >= kRowsWorkgroups && rows_head_group(d.num_kv_heads, G) >= 2 &&
       lgm::decode_rows_supported(act, cache, d.head_dim, d.num_kv_heads, G, d.block_size)) {
     // Whole-row kernel over equal runs of whole partitions, plain
     // ceil(L / ps) partitions (the ranges already balance the work).

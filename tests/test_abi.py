@@ -299,9 +299,17 @@ def partitions_brute_force(max_ctx, ps, tps):
 
 def test_workspace_size_formula():
     al = lambda x: (x + 255) // 256 * 256
-    # whole-row partition plan: Hkv % 4 == 0, whole-tile partitions of >= 256 tokens, >= 64 of them at the
-    # longest context and >= 256 units in the batch; plain ceil(L / ps) partitions after the counter slot
+    # whole-row partition plan: whole-tile partitions of >= 256 tokens, >= 64 of them at the longest
+    # context and >= 256 units in the batch; plain ceil(L / ps) partitions after the counter slot
     long = dims(num_seqs=4, max_blocks_per_seq=8192)
+    long2 = dims(num_seqs=4, num_q_heads=12, num_kv_heads=2, max_blocks_per_seq=8192)   # head groups of 2
+    assert L.lgm_paged_decode_workspace_size(long2, 131072, 512, L.LGM_BF16) == (
+        SLOT + al(4 * 12 * 256 * 128 * 4) + al(4 * 12 * 256 * 4))
+    long1 = dims(num_seqs=4, num_q_heads=8, num_kv_heads=1, max_blocks_per_seq=8192)  # one kv head: work queue
+    P1 = partitions_brute_force(131072, 512, 256)
+    assert P1 == 257
+    assert L.lgm_paged_decode_workspace_size(long1, 131072, 512, L.LGM_BF16) == (
+        SLOT + al(4 * 8 * P1 * 128 * 4) + al(4 * 8 * P1 * 4))
     assert L.lgm_paged_decode_workspace_size(long, 131072, 512, L.LGM_BF16) == (
         SLOT + al(4 * 32 * 256 * 128 * 4) + al(4 * 32 * 256 * 4))
     assert L.lgm_paged_decode_workspace_size(long, 131072, 2048, L.LGM_FP8_E4M3) == (

@@ -783,7 +783,7 @@ def test_contract_variants(cache, layout, rope_style, per_tensor, ps, hkv, G):
 
 # ------------------------------------------------------------------ whole-row partition plan
 @pytest.mark.parametrize("cache", ["bf16", "fp8", "fp4"])
-@pytest.mark.parametrize("hkv,G,ps", [(8, 4, 256), (4, 4, 256), (16, 2, 512), (8, 16, 256)])
+@pytest.mark.parametrize("hkv,G,ps", [(8, 4, 256), (4, 4, 256), (16, 2, 512), (8, 16, 256), (2, 6, 256), (6, 2, 512)])
 def test_row_partition_plan_ragged_edges(cache, hkv, G, ps):
     """Explicit partition sizes of whole tiles (>= 256 tokens) on whole-row
     shapes with a long context (>= 64 partitions) in the batch: equal runs of
