@@ -436,6 +436,19 @@ def test_row_plan_token_slices(cache, hkv, G):
     _run_and_check(cfg)
 
 
+@pytest.mark.parametrize("cache", ["bf16", "fp8"])
+@pytest.mark.parametrize("hkv,G,B", [(2, 6, 320), (1, 8, 640)])
+def test_row_plan_token_slices_full_size(cache, hkv, G, B):
+    """Token slices past the single-launch caps at the shapes timed for them
+    (Qwen2.5-1.5B-shaped 12/2 and an MQA 8/1, 2048-token contexts; 256 and
+    512 sequences reach the FP8 cap exactly, so a few more): every output
+    element of every sequence against the oracle."""
+    cfg = W.CONFIGS["qwen2.5_1.5b_gqa"].with_(name=f"slices_full_{cache}_H{hkv}_G{G}", num_seqs=B, num_kv_heads=hkv,
+                                              num_q_heads=hkv * G, cache=cache, num_blocks=None)
+    assert B * hkv * 2048 // 32 > 32768  # past the single-launch caps (16384 tiles, 32768 for FP8)
+    _run_and_check(cfg)
+
+
 # ------------------------------------------------------------------ single-launch plan
 # partition_size 0 with at most 1022 (sequence, kv head) streams and at most 16384
 # 32-token tiles over them (32768 for FP8): one launch, partitions of whole
