@@ -784,13 +784,21 @@ constexpr int kMergeGroups = kWaveSize / kMergeLanes;  // records in flight per 
 // Merge of the records of one output row: two memory round trips.  The
 // first reads the row's context length and its stream's first record slot
 // and last workgroup; the second reads, together, the LSE of every piece
-// (lane k holds piece k) and the records of the first 16 pieces (the wave
+// (lane k holds piece k) and the records of the first 8 pieces (the wave
 // works as four groups of 16 lanes, group q holding pieces q, q + 4, ...,
 // eight columns per lane).  Max and sum are lane shuffles, the groups' sums
 // are added by lane shuffles at the end: no LDS, no barrier.  Streams of
 // more pieces read the rest in a further pass.
 __global__ __launch_bounds__(kMergeThreads) void rows_merge_kernel(DecodeArgs p, RowsArgs r) {
-  constexpr int kPre = 4;  // pieces per group read with the LSEs
+  // Pieces per group read with the LSEs.  Two (the first 8 pieces) keep the
+  // kernel at 48 VGPRs, 8 waves per SIMD; four took 66 VGPRs (7 waves), and
+  // rows past what fits waited for a second round.  Merge times (rocprofv3,
+  // C3 / C5 / FP8 and bf16 at G = 8): 4.62 / 6.03 / 8.86 / 5.91 us with two,
+  // 5.16 / 6.48 / 10.22 / 6.36 with four, 5.32 / 5.81 / 8.26 / 6.16 with one.
+#ifndef LGM_ROWS_MERGE_PRE
+#define LGM_ROWS_MERGE_PRE 2
+#endif
+  constexpr int kPre = LGM_ROWS_MERGE_PRE;
   const int lane = threadIdx.x % kWaveSize;
   const int Hq = p.dims.num_q_heads;
   const int orow = blockIdx.x * kMergeRows + threadIdx.x / kWaveSize;
