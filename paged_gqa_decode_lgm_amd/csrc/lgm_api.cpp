@@ -167,13 +167,6 @@ int32_t resolve_partition(const char* fn, const lgm_paged_dims& d, int32_t max_c
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 constexpr size_t kCounterSlot = LGM_COUNTER_SLOT_BYTES;  // the counters at the start of every workspace
 
-// Launch plan of one attention call, a function of host-visible arguments only.
-// Every plan that needs a workspace lays it out the same way at the start:
-// the counter slot (LGM_COUNTER_SLOT_BYTES): the work-queue kernel's two
-// counters, then the single-launch kernel's arrival counters, one per
-// (sequence, kv head) stream.  Each kernel leaves the counters it uses zero,
-// and no plan puts anything else there, so one zero-filled workspace may
-// serve calls on any plan in turn.  The plan's own regions follow.
 // kv heads per whole-row workgroup: 8 (whole NHD rows) when they divide the
 // kv heads and the group has at most 8 query heads per kv head, else 4, else
 // (2 or 1, whole rows of 2 or 1 kv heads) as many as divide the kv heads,
@@ -190,6 +183,13 @@ static int rows_head_group(int num_kv_heads, int G) {
   return num_kv_heads % 2 == 0 ? 2 : 1;
 }
 
+// Launch plan of one attention call, a function of host-visible arguments only.
+// Every plan that needs a workspace lays it out the same way at the start:
+// the counter slot (LGM_COUNTER_SLOT_BYTES): the work-queue kernel's two
+// counters, then the single-launch kernel's arrival counters, one per
+// (sequence, kv head) stream.  Each kernel leaves the counters it uses zero,
+// and no plan puts anything else there, so one zero-filled workspace may
+// serve calls on any plan in turn.  The plan's own regions follow.
 struct Plan {
   bool fused;       // single-launch split kernel (small jobs): partitions of ps tokens, merged in the launch
   bool rows;        // whole-row kernel: equal tile ranges (partition_size 0) ...
