@@ -935,12 +935,20 @@ hipError_t launch_group(const DecodeArgs& a, const RowsArgs& r, hipStream_t s) {
   } else if (r.head_group == 4) {
     hipLaunchKernelGGL((paged_decode_rows_kernel<C, G, 1, kDecodeThreads>), dim3(r.num_wg), dim3(kDecodeThreads), 0,
                        s, a, r);
-  } else if (r.head_group == 2) {  // two token slices per head
-    hipLaunchKernelGGL((paged_decode_rows_kernel<C, G, 1, kDecodeThreads, 2>), dim3(r.num_wg), dim3(kDecodeThreads),
-                       0, s, a, r);
-  } else if (r.head_group == 1) {  // four token slices
-    hipLaunchKernelGGL((paged_decode_rows_kernel<C, G, 1, kDecodeThreads, 4>), dim3(r.num_wg), dim3(kDecodeThreads),
-                       0, s, a, r);
+  } else if (r.head_group == 2) {  // two token slices per head (FP4: four, over eight waves)
+    if constexpr (two_waves_per_simd<C, G>())
+      hipLaunchKernelGGL((paged_decode_rows_kernel<C, G, 1, 2 * kDecodeThreads, 4>), dim3(r.num_wg),
+                         dim3(2 * kDecodeThreads), 0, s, a, r);
+    else
+      hipLaunchKernelGGL((paged_decode_rows_kernel<C, G, 1, kDecodeThreads, 2>), dim3(r.num_wg), dim3(kDecodeThreads),
+                         0, s, a, r);
+  } else if (r.head_group == 1) {  // four token slices (FP4: eight)
+    if constexpr (two_waves_per_simd<C, G>())
+      hipLaunchKernelGGL((paged_decode_rows_kernel<C, G, 1, 2 * kDecodeThreads, 8>), dim3(r.num_wg),
+                         dim3(2 * kDecodeThreads), 0, s, a, r);
+    else
+      hipLaunchKernelGGL((paged_decode_rows_kernel<C, G, 1, kDecodeThreads, 4>), dim3(r.num_wg), dim3(kDecodeThreads),
+                         0, s, a, r);
   } else {
     return hipErrorInvalidValue;
   }
