@@ -932,9 +932,14 @@ hipError_t launch_group(const DecodeArgs& a, const RowsArgs& r, hipStream_t s) {
     else
       hipLaunchKernelGGL((paged_decode_rows_kernel<C, G, 2, kDecodeThreads>), dim3(r.num_wg), dim3(kDecodeThreads),
                          0, s, a, r);
-  } else if (r.head_group == 4) {
-    hipLaunchKernelGGL((paged_decode_rows_kernel<C, G, 1, kDecodeThreads>), dim3(r.num_wg), dim3(kDecodeThreads), 0,
-                       s, a, r);
+  } else if (r.head_group == 4) {  // FP4: two token slices per head over eight waves (at G = 9, 10 that
+                                   // shape spilled to scratch)
+    if constexpr (two_waves_per_simd<C, G>() && G <= 8)
+      hipLaunchKernelGGL((paged_decode_rows_kernel<C, G, 1, 2 * kDecodeThreads, 2>), dim3(r.num_wg),
+                         dim3(2 * kDecodeThreads), 0, s, a, r);
+    else
+      hipLaunchKernelGGL((paged_decode_rows_kernel<C, G, 1, kDecodeThreads>), dim3(r.num_wg), dim3(kDecodeThreads),
+                         0, s, a, r);
   } else if (r.head_group == 2) {  // two token slices per head (FP4: four, over eight waves)
     if constexpr (two_waves_per_simd<C, G>())
       hipLaunchKernelGGL((paged_decode_rows_kernel<C, G, 1, 2 * kDecodeThreads, 4>), dim3(r.num_wg),
