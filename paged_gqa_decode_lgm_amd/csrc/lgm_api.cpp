@@ -312,8 +312,8 @@ lgm_status plan_decode(const char* fn, const lgm_paged_dims& d, int32_t max_ctx,
     pl.HG = rows_head_group(d.num_kv_heads, G);
     const int64_t streams = (int64_t)d.num_seqs * (d.num_kv_heads / pl.HG);
     const int64_t tiles = streams * ((max_ctx + kRowsTile - 1) / kRowsTile);
-    // The kernel cuts its ranges in cost units: 4 per tile and at most 16 per stream.
-    if (4 * tiles + 16 * streams > (int64_t)INT32_MAX)
+    // The kernel cuts its ranges in cost units: 4 per tile and at most 16 * 8 / HG per stream.
+    if (4 * tiles + 128 * streams > (int64_t)INT32_MAX)
       return fail(LGM_ERR_UNSUPPORTED, fn, "num_seqs * head groups * tiles = %lld: too many", (long long)tiles);
     if ((int64_t)d.num_seqs * d.num_q_heads > (int64_t)INT32_MAX - 1024)  // merge rows are int-indexed
       return fail(LGM_ERR_UNSUPPORTED, fn, "num_seqs * num_q_heads = %lld: too many",
