@@ -20,6 +20,7 @@ CASES = [
     ("llama3_8b_gqa", dict(num_seqs=16, ctx=(17, 5000)), dict(num_seqs=5, ctx=(1, 900)), 64),      # work queue
     ("qwen2.5_1.5b_gqa", dict(), dict(num_seqs=1, ctx_list=(700,)), 64),                          # work queue, Hkv 2
     ("qwen2.5_1.5b_gqa", dict(), dict(num_seqs=1, ctx_list=(700,)), 0),                           # single launch
+    ("qwen2.5_1.5b_gqa", dict(num_seqs=320), dict(num_seqs=3, ctx_list=(40, 300, 2048)), 0),       # token slices
     ("fp8_kv", dict(num_seqs=24), dict(num_seqs=3, ctx=(40, 300)), 0),
     ("fp4_kv", dict(num_seqs=24), dict(num_seqs=3, ctx=(40, 300)), 0),
     ("long_ctx_splitk", dict(num_seqs=2, ctx=40000), dict(num_seqs=1, ctx=20000), 512),          # row partitions
